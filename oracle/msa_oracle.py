@@ -1,0 +1,326 @@
+"""Plain fp64 CPU oracle of the MSA (MiniMax Sparse Attention) forward path.
+
+TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module.  It shares no code with the HIP path
+in block_sparse_top_amd/ and neither side imports the other.
+
+Everything is written as the plain definition, in float64, from the exact
+stored bytes (bf16 bits -> float; fp8 e4m3fn bits -> table value x fp32
+per-head scale).  Sources (the pages):
+
+  [README]  "MiniMax-AI/MSA" README (pigsec.cn mirror), section "Usage": a
+            dense proxy pass over a cheap query slice returns a per-block max
+            score; `sparse_topk_select` turns the scores into KV block indexes
+            (`topk` of them, bounded by the number of valid pages); the sparse
+            plan uses the same `topk` as its `kv_block_num`; attention then
+            runs on the selected blocks of the paged K/V.  k_pages.shape[1] is
+            the number of KV heads, so pages are [page, head, slot, dim].
+  [NEWS]    "MSA; MiniMax sparse attention kernels for SM100 GPUs"
+            (news.ditty.ir), the paragraph on the three-step flow: the cheap
+            pass computes the highest score of each block.
+  [FLASH]   "Flash-MSA: open kernels for training sparse-attention models on
+            millions of tokens" (iitog.ru), the paragraph comparing MSA with
+            DSA (128-token blocks picked by max-pooling proxy scores; GQA main
+            attention; each proxy head picks its own blocks for its group) and
+            the paragraph on the forward kernels (each token's local block is
+            always visible, like a sliding window).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * a "score" is the scaled proxy logit proxy_sm_scale * q.k (no softmax);
+  * `topk` counts slots including the forced local block;
+  * ties go to the lower block index; output ascending, padded with -1;
+  * a query row i of a sequence sits at position kv_len - qo_len + i
+    (bottom-right causal alignment); key j is visible iff j <= pos and
+    j < kv_len (the diagonal key counts);
+  * proxy head p drives KV group p; with one proxy-K head it is shared.
+
+Parity pins live in tests/test_oracle_*.py.  Parity unpinned: the absolute
+scale of the exported max scores beyond the scaled-logit reading (only the
+selection is invariant to it) and the 16-versus-17-slot reading of the decode
+workload.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BF16 = "bf16"
+FP8 = "fp8"
+
+
+# ----------------------------------------------------------------------------
+# Storage formats
+# ----------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64: the bf16 value is the float32
+    whose top 16 bits are these and whose low 16 bits are zero."""
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _e4m3fn_value(byte: int) -> float:
+    """OCP 8-bit float E4M3 ("fn": finite, no infinities), from its definition:
+    1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+    subnormal (m/8 * 2^-6); S.1111.111 is NaN; max finite 448."""
+    s = -1.0 if byte & 0x80 else 1.0
+    e = (byte >> 3) & 0xF
+    m = byte & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return s * (m / 8.0) * 2.0 ** (-6)
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3FN_TABLE = np.array([_e4m3fn_value(b) for b in range(256)], dtype=np.float64)
+
+
+def e4m3fn_to_f64(bits: np.ndarray) -> np.ndarray:
+    return E4M3FN_TABLE[np.asarray(bits, dtype=np.uint8)]
+
+
+def dequant(bits: np.ndarray, dtype: str, scale=None, head_axis: int = 1) -> np.ndarray:
+    """Stored bits -> float64 values; fp8 values are multiplied by the fp32
+    per-head scale (in float64)."""
+    if dtype == BF16:
+        return bf16_to_f64(bits)
+    if dtype == FP8:
+        v = e4m3fn_to_f64(bits)
+        shape = [1] * v.ndim
+        shape[head_axis] = -1
+        return v * np.asarray(scale, dtype=np.float32).astype(np.float64).reshape(shape)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# Sequence layout (re-derived here; the HIP path has its own planner)
+# ----------------------------------------------------------------------------
+class Layout:
+    """Row and page bookkeeping of a varlen batch.
+
+    Rows of all sequences are concatenated (sequence s owns rows
+    row_start[s] .. row_start[s] + qo_len[s]); sequence s owns the
+    ceil(kv_len / page_size) entries of the flat page table that start at
+    page_start[s] ([README] "Usage": the page table is one flat list and the
+    plan is built from the per-sequence lengths)."""
+
+    def __init__(self, qo_lens, kv_lens, page_size: int):
+        self.qo = [int(x) for x in qo_lens]
+        self.kv = [int(x) for x in kv_lens]
+        self.B = int(page_size)
+        self.nb = [-(-L // self.B) for L in self.kv]
+        self.row_start = np.concatenate([[0], np.cumsum(self.qo)]).astype(np.int64)
+        self.page_start = np.concatenate([[0], np.cumsum(self.nb)]).astype(np.int64)
+        self.T = int(self.row_start[-1])
+
+    def seq_of_row(self, r: int) -> int:
+        return int(np.searchsorted(self.row_start, r, side="right") - 1)
+
+    def pos(self, r: int) -> int:
+        """Absolute KV position of query row r (bottom-right alignment)."""
+        s = self.seq_of_row(r)
+        i = r - int(self.row_start[s])
+        return self.kv[s] - self.qo[s] + i
+
+    def local(self, r: int) -> int:
+        return self.pos(r) // self.B
+
+
+def gather_rows(pages_bits, dtype, scale, kv_indices, lay: Layout, s: int, head: int, key_idx) -> np.ndarray:
+    """Logical key rows `key_idx` of sequence s, KV head `head` -> float64 [n, d].
+    Key j lives in page kv_indices[page_start[s] + j // B], slot j % B."""
+    key_idx = np.asarray(key_idx, dtype=np.int64)
+    pages = np.asarray(kv_indices, dtype=np.int64)[lay.page_start[s] + key_idx // lay.B]
+    raw = pages_bits[pages, head, key_idx % lay.B, :]
+    if dtype == BF16:
+        return bf16_to_f64(raw)
+    if dtype == FP8:
+        return e4m3fn_to_f64(raw) * np.float64(np.float32(np.asarray(scale)[head]))
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# O1: proxy block max scores
+# ----------------------------------------------------------------------------
+def proxy_block_maxscore(proxy_q, proxy_k_pages, kv_indices, qo_lens, kv_lens, page_size, proxy_sm_scale,
+                         proxy_dtype=BF16, proxy_q_scale=None, proxy_k_scale=None, rows=None):
+    """Per-block max of the scaled proxy logits ([NEWS] three-step flow;
+    [README] "Usage", `output_maxscore`; [FLASH] max-pooling over proxy scores).
+
+      ms[r, p, b] = max over keys j of block b with j <= pos(r), j < kv_len of
+                    proxy_sm_scale * <pq[r, p], pk[j, pk_head(p)]>
+
+    pk_head(p) = p when there are as many proxy-K heads as proxy heads, else 0.
+    Blocks with no visible key give -inf; blocks after the row's local block
+    are not defined and returned as NaN.
+
+    Returns float64 [len(rows), P, nb_max].
+    """
+    lay = Layout(qo_lens, kv_lens, page_size)
+    rows = np.arange(lay.T) if rows is None else np.asarray(rows, dtype=np.int64)
+    T, P, d = proxy_q.shape
+    Pk = proxy_k_pages.shape[1]
+    B = lay.B
+    nb_max = max(lay.nb)
+    out = np.full((rows.size, P, nb_max), np.nan)
+    pq_all = None
+    for s in range(len(lay.kv)):
+        sel = np.nonzero((rows >= lay.row_start[s]) & (rows < lay.row_start[s + 1]))[0]
+        if sel.size == 0:
+            continue
+        L = lay.kv[s]
+        keys = np.arange(L)
+        for p in range(P):
+            ph = p if Pk == P else 0
+            K = gather_rows(proxy_k_pages, proxy_dtype, proxy_k_scale, kv_indices, lay, s, ph, keys)  # [L, d]
+            for c0 in range(0, sel.size, 256):
+                idx = sel[c0:c0 + 256]
+                r = rows[idx]
+                qv = dequant(proxy_q[r, p:p + 1, :], proxy_dtype,
+                             None if proxy_q_scale is None else np.asarray(proxy_q_scale)[p:p + 1])[:, 0, :]
+                S = proxy_sm_scale * (qv @ K.T)                               # [n, L]
+                pos = np.array([lay.pos(int(x)) for x in r])
+                S[keys[None, :] > pos[:, None]] = -np.inf
+                nbs = lay.nb[s]
+                Sp = np.full((idx.size, nbs * B), -np.inf)
+                Sp[:, :L] = S
+                ms = Sp.reshape(idx.size, nbs, B).max(axis=2)                 # [n, nb_s]
+                loc = pos // B
+                ms[np.arange(nbs)[None, :] > loc[:, None]] = np.nan
+                out[idx, p, :nbs] = ms
+    return out
+
+
+# ----------------------------------------------------------------------------
+# O2: top-k block selection
+# ----------------------------------------------------------------------------
+def topk_select_row(scores: np.ndarray, local: int, k: int) -> np.ndarray:
+    """Selection for one (row, group) ([README] "Usage", `sparse_topk_select`
+    with `topk` slots; [FLASH] forward-kernel paragraph: the local block is
+    always kept).
+
+    Competing blocks are the fully visible ones before the local block.  The
+    k - 1 best of them by score (ties: lower block index first) join the
+    local block.  Output ascending, padded with -1 to k entries.
+    """
+    cand = np.arange(local)
+    R = min(k - 1, local)
+    if R > 0:
+        order = np.lexsort((cand, -scores[:local]))     # primary: score desc, then index asc
+        chosen = cand[order[:R]]
+    else:
+        chosen = np.zeros(0, dtype=np.int64)
+    sel = np.sort(np.concatenate([chosen, [local]]))
+    out = np.full(k, -1, dtype=np.int32)
+    out[:sel.size] = sel
+    return out
+
+
+def topk_select(max_score, qo_lens, kv_lens, page_size, topk, rows=None):
+    """Apply topk_select_row to every (row, group).  max_score is indexed
+    [i, p, b] for the i-th entry of `rows` (all rows by default).
+    Returns int32 [len(rows), P, topk]."""
+    lay = Layout(qo_lens, kv_lens, page_size)
+    rows = np.arange(lay.T) if rows is None else np.asarray(rows, dtype=np.int64)
+    n, P, _ = max_score.shape
+    out = np.empty((n, P, topk), dtype=np.int32)
+    for i, r in enumerate(rows):
+        loc = lay.local(int(r))
+        for p in range(P):
+            out[i, p] = topk_select_row(max_score[i, p], loc, topk)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# O3 / O4: block-sparse GQA attention (prefill and decode)
+# ----------------------------------------------------------------------------
+def sparse_attention(q, k_pages, v_pages, kv_indices, kv_block_indexes, qo_lens, kv_lens, page_size, sm_scale,
+                     kv_dtype=BF16, k_scale=None, v_scale=None, rows=None):
+    """Softmax attention of each query row over the keys of its group's
+    selected blocks ([README] "Usage": attention over the selected blocks of
+    the paged K/V; [FLASH] GQA main attention, one block set per group).
+
+    For row r, query head h, group g = h // (H_q / H_kv):
+      K(r, g) = { j : j // B in S(r, g), j <= pos(r), j < kv_len }
+      s_j = sm_scale * <q[r, h], k[j, g]>
+      o   = sum_j exp(s_j - M) v[j, g] / sum_j exp(s_j - M),   M = max_j s_j
+      lse = M + log sum_j exp(s_j - M)
+    S(r, g) is kv_block_indexes[r, g, :] with -1 entries ignored.  A decode
+    step is the case qo_len = 1.
+
+    Returns (out float64 [len(rows), H_q, d], lse float64 [len(rows), H_q]).
+    """
+    lay = Layout(qo_lens, kv_lens, page_size)
+    rows = np.arange(lay.T) if rows is None else np.asarray(rows, dtype=np.int64)
+    T, Hq, d = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    B = lay.B
+    out = np.zeros((rows.size, Hq, d))
+    lse = np.zeros((rows.size, Hq))
+    for i, r in enumerate(rows):
+        r = int(r)
+        s = lay.seq_of_row(r)
+        pos = lay.pos(r)
+        L = lay.kv[s]
+        qv = bf16_to_f64(q[r])                                             # [H_q, d]
+        for g in range(Hkv):
+            blocks = sorted(set(int(b) for b in kv_block_indexes[r, g] if b >= 0))
+            keys = np.concatenate([np.arange(b * B, (b + 1) * B) for b in blocks]) if blocks else np.zeros(0, np.int64)
+            keys = keys[(keys <= pos) & (keys < L)]
+            K = gather_rows(k_pages, kv_dtype, k_scale, kv_indices, lay, s, g, keys)
+            V = gather_rows(v_pages, kv_dtype, v_scale, kv_indices, lay, s, g, keys)
+            for h in range(g * G, (g + 1) * G):
+                sc = sm_scale * (K @ qv[h])
+                M = sc.max()
+                w = np.exp(sc - M)
+                out[i, h] = (w @ V) / w.sum()
+                lse[i, h] = M + np.log(w.sum())
+    return out, lse
+
+
+def sparse_decode(q, k_pages, v_pages, kv_indices, kv_block_indexes, kv_lens, page_size, sm_scale,
+                  kv_dtype=FP8, k_scale=None, v_scale=None, rows=None):
+    """Paged sparse decode ([README] "Stacks": paged FP8 decode wrapper): one
+    new query row per sequence, already in the cache, so pos = kv_len - 1."""
+    return sparse_attention(q, k_pages, v_pages, kv_indices, kv_block_indexes, [1] * len(kv_lens), kv_lens,
+                            page_size, sm_scale, kv_dtype, k_scale, v_scale, rows)
+
+
+# ----------------------------------------------------------------------------
+# Acceptance rule for a selection produced elsewhere
+# ----------------------------------------------------------------------------
+def check_selection_row(sel: np.ndarray, scores: np.ndarray, local: int, k: int, band: float = 1e-3):
+    """Is `sel` an acceptable selection for a row whose fp64 block scores are
+    `scores`?  Returns (ok, reason).
+
+    The local block must be present, the set size must be min(k, local + 1),
+    ids ascending, unique, <= local, -1 padded.  Let s_1 >= s_2 >= ... be the
+    scores of the competing blocks and R = min(k - 1, local).  If
+    s_R - s_{R+1} > band the competing part must equal the oracle's choice;
+    otherwise every chosen competing block must score >= s_R - band.
+    """
+    sel = np.asarray(sel)
+    valid = sel[sel >= 0]
+    n = min(k, local + 1)
+    if valid.size != n or np.any(sel[n:] != -1):
+        return False, f"size {valid.size} != {n} or bad padding"
+    if np.any(np.diff(valid) <= 0):
+        return False, "not strictly ascending"
+    if valid[-1] != local:
+        return False, "local block missing"
+    comp = valid[:-1]
+    R = min(k - 1, local)
+    if R == 0:
+        return True, ""
+    cs = np.sort(scores[:local])[::-1]
+    sR = cs[R - 1]
+    if R < local and cs[R - 1] - cs[R] > band:
+        ref = topk_select_row(scores, local, k)
+        if not np.array_equal(ref, sel):
+            return False, "clear gap but different set"
+        return True, ""
+    if np.any(scores[comp] < sR - band):
+        return False, "a chosen block scores below the band"
+    return True, ""

@@ -1,0 +1,60 @@
+"""Planted mistakes: each test breaks the oracle on the CPU in a plausible way
+and checks that one of the pins catches it (so the pins are not vacuous)."""
+import numpy as np
+import pytest
+
+import oracle.msa_oracle as om
+from tests import test_oracle_attention as ta
+from tests import test_oracle_proxy as tp
+from tests import test_oracle_topk as tt
+
+
+def test_off_by_one_causal_alignment_is_caught(monkeypatch):
+    orig = om.Layout.pos
+    monkeypatch.setattr(om.Layout, "pos", lambda self, r: orig(self, r) - 1 if orig(self, r) > 0 else 0)
+    with pytest.raises(AssertionError):
+        tp.test_positional_closed_form([300], [300], 16, 2)
+    with pytest.raises(AssertionError):
+        ta.test_all_blocks_selected_equals_dense_causal_gqa([200], [200], 32, 4, 2)
+
+
+def test_wrong_kv_head_is_caught(monkeypatch):
+    orig = om.gather_rows
+
+    def bad(pages_bits, dtype, scale, kv_indices, lay, s, head, key_idx):
+        return orig(pages_bits, dtype, scale, kv_indices, lay, s, (head + 1) % pages_bits.shape[1], key_idx)
+    monkeypatch.setattr(om, "gather_rows", bad)
+    with pytest.raises(AssertionError):
+        ta.test_all_blocks_selected_equals_dense_causal_gqa([200], [200], 32, 4, 2)
+    with pytest.raises(AssertionError):
+        tp.test_positional_closed_form([256], [256], 128, 2)
+
+
+def test_ties_to_higher_index_are_caught(monkeypatch):
+    def bad(scores, local, k):
+        cand = np.arange(local)
+        R = min(k - 1, local)
+        order = np.lexsort((-cand, -scores[:local]))
+        sel = np.sort(np.concatenate([cand[order[:R]], [local]]))
+        out = np.full(k, -1, np.int32)
+        out[:sel.size] = sel
+        return out
+    monkeypatch.setattr(tt, "topk_select_row", bad)
+    with pytest.raises(AssertionError):
+        tt.test_hand_worked_cases()
+    with pytest.raises(AssertionError):
+        for seed in range(40):
+            tt.test_brute_force_subsets(seed)
+
+
+def test_dropping_the_local_block_is_caught(monkeypatch):
+    def bad(scores, local, k):
+        cand = np.arange(local + 1)
+        order = np.lexsort((cand, -scores[:local + 1]))
+        sel = np.sort(cand[order[:min(k, local + 1)]])
+        out = np.full(k, -1, np.int32)
+        out[:sel.size] = sel
+        return out
+    monkeypatch.setattr(tt, "topk_select_row", bad)
+    with pytest.raises(AssertionError):
+        tt.test_hand_worked_cases()
