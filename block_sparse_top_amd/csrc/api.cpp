@@ -1,0 +1,343 @@
+// Host side of the MSA C ABI: plan construction, argument validation,
+// workspace layout and dispatch to the kernel launchers.  The plan follows
+// the plan -> run split of the MiniMax-AI/MSA README (section "Usage": the
+// plan is built from qo_lens / kv_lens, head counts, page size and topk).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "msa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status_t fail(msa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+msa_status_t ok() {
+  g_last_error.clear();
+  return MSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+#define MSA_CHECK_PTR(p)                                                                        \
+  do {                                                                                          \
+    if ((p) == nullptr) return fail(MSA_ERR_INVALID_ARG, "%s: `%s` is NULL", __func__, #p);     \
+    if (!aligned16(p)) return fail(MSA_ERR_INVALID_ARG, "%s: `%s` is not 16-byte aligned", __func__, #p); \
+  } while (0)
+
+msa_status_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MSA_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+// Copy the plan metadata into the workspace unless this workspace already
+// holds it.  The copy is ordered on `st` before the kernels that read it.
+msa_status_t upload_meta(msa_plan_s* p, void* ws, hipStream_t st) {
+  if (p->uploaded_to == ws) return MSA_OK;
+  hipError_t e = hipMemcpyAsync(static_cast<char*>(ws) + p->lay.meta, p->meta.data(),
+                                p->meta.size() * sizeof(int32_t), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_status(e, "metadata upload");
+  p->uploaded_to = ws;
+  return MSA_OK;
+}
+
+msa_status_t check_ws(const msa_plan_s* p, void* ws, size_t bytes) {
+  if (ws == nullptr) return fail(MSA_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (bytes < p->lay.total)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu", bytes, p->lay.total);
+  return MSA_OK;
+}
+
+msa_status_t check_rows(const msa_plan_s* p, int64_t row_begin, int64_t row_count, const char* fn) {
+  if (row_count <= 0 || row_begin < 0 || row_begin + row_count > p->T)
+    return fail(MSA_ERR_INVALID_ARG, "%s: row range [%lld, %lld) is empty or outside [0, %d)", fn,
+                (long long)row_begin, (long long)(row_begin + row_count), p->T);
+  if (row_count > p->max_rows)
+    return fail(MSA_ERR_INVALID_ARG, "%s: row_count %lld exceeds the plan's max_rows_per_call %lld", fn,
+                (long long)row_count, (long long)p->max_rows);
+  return MSA_OK;
+}
+
+}  // namespace
+
+namespace msa {
+
+DevMeta dev_meta(const msa_plan_s* p, const void* workspace) {
+  const int32_t* base = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + p->lay.meta);
+  DevMeta m;
+  m.S = p->S;
+  m.T = p->T;
+  m.NB = p->NB;
+  m.nb_max = p->nb_max;
+  m.qo = base;
+  m.kv = base + p->S;
+  m.row_start = base + 2 * p->S;
+  m.page_start = base + 3 * p->S + 1;
+  m.tiles = base + 4 * p->S + 2;
+  return m;
+}
+
+}  // namespace msa
+
+extern "C" {
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* workspace_bytes) {
+  if (!desc || !out || !workspace_bytes) return fail(MSA_ERR_INVALID_ARG, "msa_plan: NULL argument");
+  *out = nullptr;
+  const msa_plan_desc_t& d = *desc;
+  if (d.batch < 1) return fail(MSA_ERR_INVALID_ARG, "msa_plan: batch must be >= 1 (got %d)", d.batch);
+  if (d.mode != MSA_PREFILL && d.mode != MSA_DECODE) return fail(MSA_ERR_INVALID_ARG, "msa_plan: bad mode");
+  if (!d.kv_lens_host) return fail(MSA_ERR_INVALID_ARG, "msa_plan: kv_lens_host is NULL");
+  if (d.mode == MSA_PREFILL && !d.qo_lens_host) return fail(MSA_ERR_INVALID_ARG, "msa_plan: qo_lens_host is NULL");
+  if (d.num_qo_heads < 1 || d.num_kv_heads < 1 || d.num_qo_heads % d.num_kv_heads)
+    return fail(MSA_ERR_INVALID_ARG, "msa_plan: need num_qo_heads %% num_kv_heads == 0 (got %d, %d)",
+                d.num_qo_heads, d.num_kv_heads);
+  const int G = d.num_qo_heads / d.num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_plan: GQA group size %d not in {1,2,4,8,16}", G);
+  if (d.head_dim != 128) return fail(MSA_ERR_UNSUPPORTED, "msa_plan: head_dim %d != 128", d.head_dim);
+  if (d.page_size != 128) return fail(MSA_ERR_UNSUPPORTED, "msa_plan: page_size %d != 128", d.page_size);
+  if (d.topk < 1 || d.topk > 64) return fail(MSA_ERR_INVALID_ARG, "msa_plan: topk %d not in [1, 64]", d.topk);
+  if (d.kv_dtype != MSA_BF16 && d.kv_dtype != MSA_FP8_E4M3) return fail(MSA_ERR_INVALID_ARG, "msa_plan: bad kv_dtype");
+  if (!(d.sm_scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "msa_plan: sm_scale must be > 0");
+  if (d.mode == MSA_PREFILL) {
+    if (d.kv_dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "msa_plan: prefill K/V must be bf16");
+    if (d.proxy_dtype != MSA_BF16 && d.proxy_dtype != MSA_FP8_E4M3)
+      return fail(MSA_ERR_INVALID_ARG, "msa_plan: bad proxy_dtype");
+    if (d.num_proxy_heads != d.num_kv_heads)
+      return fail(MSA_ERR_UNSUPPORTED, "msa_plan: num_proxy_heads (%d) must equal num_kv_heads (%d)",
+                  d.num_proxy_heads, d.num_kv_heads);
+    if (d.num_proxy_kv_heads != 1 && d.num_proxy_kv_heads != d.num_proxy_heads)
+      return fail(MSA_ERR_INVALID_ARG, "msa_plan: num_proxy_kv_heads must be 1 or num_proxy_heads");
+    if (!(d.proxy_sm_scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "msa_plan: proxy_sm_scale must be > 0");
+  }
+  if (d.max_rows_per_call < 0) return fail(MSA_ERR_INVALID_ARG, "msa_plan: max_rows_per_call < 0");
+
+  msa_plan_s* p = new (std::nothrow) msa_plan_s();
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_plan: out of host memory");
+  p->d = d;
+  p->d.qo_lens_host = nullptr;
+  p->d.kv_lens_host = nullptr;
+  p->S = d.batch;
+  p->G = G;
+  int64_t T = 0, NB = 0;
+  p->row_start.push_back(0);
+  p->page_start.push_back(0);
+  for (int s = 0; s < d.batch; ++s) {
+    const int32_t kv = d.kv_lens_host[s];
+    const int32_t qo = d.mode == MSA_DECODE ? 1 : d.qo_lens_host[s];
+    if (d.mode == MSA_DECODE && d.qo_lens_host && d.qo_lens_host[s] != 1) {
+      delete p;
+      return fail(MSA_ERR_INVALID_ARG, "msa_plan: decode plans need qo_len == 1 (sequence %d has %d)", s,
+                  d.qo_lens_host[s]);
+    }
+    if (qo < 1 || kv < qo) {
+      delete p;
+      return fail(MSA_ERR_INVALID_ARG, "msa_plan: sequence %d needs 1 <= qo_len <= kv_len (got %d, %d)", s, qo, kv);
+    }
+    const int32_t nb = (kv + 127) / 128;
+    p->qo.push_back(qo);
+    p->kv.push_back(kv);
+    p->nb.push_back(nb);
+    T += qo;
+    NB += nb;
+    p->nb_max = std::max(p->nb_max, nb);
+    if (T > (int64_t)INT32_MAX / 64 || NB > (int64_t)INT32_MAX / 64) {
+      delete p;
+      return fail(MSA_ERR_UNSUPPORTED, "msa_plan: too many rows or pages");
+    }
+    p->row_start.push_back((int32_t)T);
+    p->page_start.push_back((int32_t)NB);
+  }
+  p->T = (int32_t)T;
+  p->NB = (int32_t)NB;
+  p->max_rows = d.max_rows_per_call > 0 ? std::min<int64_t>(d.max_rows_per_call, T) : std::min<int64_t>(T, 32768);
+
+  // Proxy row tiles: rows of one sequence whose positions fall in one
+  // 256-aligned position window (at most 256 rows).
+  for (int s = 0; s < p->S; ++s) {
+    const int32_t first_pos = p->kv[s] - p->qo[s];
+    int32_t i = 0;
+    while (i < p->qo[s]) {
+      const int32_t pos = first_pos + i;
+      const int32_t end_pos = (pos / 256 + 1) * 256;
+      const int32_t n = std::min(p->qo[s] - i, end_pos - pos);
+      p->tiles.insert(p->tiles.end(), {s, p->row_start[s] + i, n, pos});
+      i += n;
+    }
+  }
+  p->ntiles = (int32_t)(p->tiles.size() / 4);
+
+  // Metadata blob.
+  p->meta.reserve(4 * p->S + 2 + p->tiles.size());
+  p->meta.insert(p->meta.end(), p->qo.begin(), p->qo.end());
+  p->meta.insert(p->meta.end(), p->kv.begin(), p->kv.end());
+  p->meta.insert(p->meta.end(), p->row_start.begin(), p->row_start.end());
+  p->meta.insert(p->meta.end(), p->page_start.begin(), p->page_start.end());
+  p->meta.insert(p->meta.end(), p->tiles.begin(), p->tiles.end());
+
+  // Workspace layout.
+  msa::PlanLayout& L = p->lay;
+  size_t off = 0;
+  L.meta = off;
+  L.meta_bytes = p->meta.size() * sizeof(int32_t);
+  off = align_up(off + L.meta_bytes, 256);
+  const int64_t Hkv = d.num_kv_heads, Hq = d.num_qo_heads, K = d.topk;
+  if (d.mode == MSA_PREFILL) {
+    p->tokens_per_chunk = 128 / G;
+    p->entries_per_item = p->tokens_per_chunk * 4;
+    const int64_t W = p->max_rows;
+    const int64_t nkey = Hkv * NB;
+    L.counts = off; off = align_up(off + nkey * 4, 256);
+    L.cursor = off; off = align_up(off + nkey * 4, 256);
+    L.offsets = off; off = align_up(off + (nkey + 1) * 4, 256);
+    L.max_items = (W * Hkv * K + p->entries_per_item - 1) / p->entries_per_item + nkey;
+    L.items = off; off = align_up(off + L.max_items * 16, 256);
+    L.nitems = off; off = align_up(off + 16, 256);
+    L.entries = off; off = align_up(off + W * Hkv * K * 4, 256);
+    L.part_o = off; off = align_up(off + W * Hq * K * 128 * 2, 256);
+    L.part_lse = off; off = align_up(off + W * Hq * K * 4, 256);
+  } else {
+    p->dec_splits = std::min(4, (int)K);
+    L.dec_o = off; off = align_up(off + (size_t)p->S * Hq * p->dec_splits * 128 * 4, 256);
+    L.dec_ml = off; off = align_up(off + (size_t)p->S * Hq * p->dec_splits * 2 * 4, 256);
+  }
+  L.total = off;
+  *workspace_bytes = L.total;
+  *out = p;
+  return ok();
+}
+
+msa_status_t msa_plan_destroy(msa_plan_t plan) {
+  delete plan;
+  return ok();
+}
+
+msa_status_t msa_plan_info(msa_plan_t p, int64_t* total_rows, int32_t* nb_max, int64_t* max_rows_per_call) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_plan_info: NULL plan");
+  if (total_rows) *total_rows = p->T;
+  if (nb_max) *nb_max = p->nb_max;
+  if (max_rows_per_call) *max_rows_per_call = p->max_rows;
+  return ok();
+}
+
+msa_status_t msa_proxy_block_maxscore(msa_plan_t p, const void* proxy_q, const void* proxy_k_pages,
+                                      const float* proxy_q_scale, const float* proxy_k_scale,
+                                      const int32_t* kv_indices, int64_t row_begin, int64_t row_count,
+                                      float* max_score, void* workspace, size_t workspace_bytes,
+                                      msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_proxy_block_maxscore: NULL plan");
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_proxy_block_maxscore: decode plan");
+  MSA_CHECK_PTR(proxy_q);
+  MSA_CHECK_PTR(proxy_k_pages);
+  MSA_CHECK_PTR(kv_indices);
+  MSA_CHECK_PTR(max_score);
+  const bool fp8 = p->d.proxy_dtype == MSA_FP8_E4M3;
+  if (fp8 != (proxy_q_scale != nullptr) || fp8 != (proxy_k_scale != nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "msa_proxy_block_maxscore: scale pointers must be given iff the proxy dtype is fp8");
+  msa_status_t st = check_rows(p, row_begin, row_count, __func__);
+  if (st != MSA_OK) return st;
+  if ((st = check_ws(p, workspace, workspace_bytes)) != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  // tiles intersecting the row range
+  int32_t lo = 0, hi = p->ntiles;
+  while (lo < p->ntiles && p->tiles[4 * lo + 1] + p->tiles[4 * lo + 2] <= row_begin) ++lo;
+  while (hi > lo && p->tiles[4 * (hi - 1) + 1] >= row_begin + row_count) --hi;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  return hip_status(msa::launch_proxy_maxscore(p, m, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale,
+                                               kv_indices, lo, hi, row_begin, row_count, max_score, hs),
+                    __func__);
+}
+
+msa_status_t msa_topk_select(msa_plan_t p, const float* max_score, int64_t row_begin, int64_t row_count,
+                             int32_t* kv_block_indexes, void* workspace, size_t workspace_bytes,
+                             msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_topk_select: NULL plan");
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_topk_select: decode plan");
+  MSA_CHECK_PTR(max_score);
+  MSA_CHECK_PTR(kv_block_indexes);
+  msa_status_t st = check_rows(p, row_begin, row_count, __func__);
+  if (st != MSA_OK) return st;
+  if ((st = check_ws(p, workspace, workspace_bytes)) != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  return hip_status(msa::launch_topk(p, m, max_score, row_begin, row_count, kv_block_indexes, hs), __func__);
+}
+
+msa_status_t msa_sparse_attn_prefill(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                     const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                     const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill: NULL plan");
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_prefill: decode plan");
+  MSA_CHECK_PTR(q);
+  MSA_CHECK_PTR(k_pages);
+  MSA_CHECK_PTR(v_pages);
+  MSA_CHECK_PTR(kv_indices);
+  MSA_CHECK_PTR(kv_block_indexes);
+  MSA_CHECK_PTR(out);
+  if (lse && !aligned16(lse)) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill: lse not 16-byte aligned");
+  if (k_scale || v_scale) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill: bf16 K/V take no scales");
+  msa_status_t st = check_ws(p, workspace, workspace_bytes);
+  if (st != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  for (int64_t w0 = 0; w0 < p->T; w0 += p->max_rows) {
+    const int32_t w1 = (int32_t)std::min<int64_t>(p->T, w0 + p->max_rows);
+    hipError_t e = msa::launch_prefill_window(p, m, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse,
+                                              static_cast<char*>(workspace), (int32_t)w0, w1, hs);
+    if (e != hipSuccess) return hip_status(e, __func__);
+  }
+  return ok();
+}
+
+msa_status_t msa_sparse_attn_decode(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                    const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                    const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_decode: NULL plan");
+  if (p->d.mode != MSA_DECODE) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_decode: prefill plan");
+  MSA_CHECK_PTR(q);
+  MSA_CHECK_PTR(k_pages);
+  MSA_CHECK_PTR(v_pages);
+  MSA_CHECK_PTR(kv_indices);
+  MSA_CHECK_PTR(kv_block_indexes);
+  MSA_CHECK_PTR(out);
+  if (lse && !aligned16(lse)) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_decode: lse not 16-byte aligned");
+  const bool fp8 = p->d.kv_dtype == MSA_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_decode: scale pointers must be given iff K/V are fp8");
+  msa_status_t st = check_ws(p, workspace, workspace_bytes);
+  if (st != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  return hip_status(msa::launch_decode(p, m, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes,
+                                       out, lse, static_cast<char*>(workspace), hs),
+                    __func__);
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Device helpers shared by the MSA kernels (gfx950 / CDNA4 only).
+//
+// MFMA operand layouts used throughout (checked on hardware):
+//   v_mfma_f32_32x32x16_bf16: A[i][k] in lane (i + 32*(k/8)), element k%8;
+//     B[k][j] in lane (j + 32*(k/8)), element k%8;
+//     C[i][j] in lane (j + 32*((i/4)%2)), register 4*(i/8) + i%4.
+//   v_mfma_f32_16x16x32_bf16: A[i][k] in lane (i + 16*(k/8)), element k%8;
+//     B[k][j] in lane (j + 16*(k/8)), element k%8;
+//     C[i][j] in lane (j + 16*(i/4)), register i%4.
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, unit scales): as 32x32x16 with
+//     32 consecutive k per lane half: A[i][k] in lane (i + 32*(k/32)), byte k%32.
+// Because a contraction is a sum over k, A and B may both use any one
+// permutation of k; the kernels exploit that to load 16- or 32-byte runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+#define MSA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp8 e4m3 x fp8 e4m3, block scales fixed at 2^0 (E8M0 code 127).
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Eight OCP e4m3 codes (two dwords) -> eight bf16, exactly (v_cvt_scalef32_pk_bf16_fp8
+// with unit scale; the last argument picks bytes 0-1 or 2-3).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  const i32x4 r = {__builtin_bit_cast(int, a), __builtin_bit_cast(int, b), __builtin_bit_cast(int, c),
+                   __builtin_bit_cast(int, d)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32); }
+
+// Read 16 bytes from LDS.
+template <typename T>
+__device__ __forceinline__ T lds_load16(const void* p) {
+  return *(const MSA_LDS T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store16(void* p, const T& v) {
+  *(MSA_LDS T*)(p) = v;
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 4 bf16 read by lane 4*e + i/4, for e = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MSA_LDS s16x4*)(p));
+}
+// ds_read_b64_tr_b8: within each group of 16 lanes, lane i receives byte
+// (i % 8) of the 8 bytes read by lane 2*e + i/8, for e = 0..7.
+__device__ __forceinline__ i32x2 lds_read_tr8(const void* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MSA_LDS i32x2*)(p));
+}
+
+// Two transposed 4 x bf16 reads -> one 8 x bf16 MFMA operand (whole-vector
+// casts: element-wise reassembly of these results has been miscompiled).
+__device__ __forceinline__ bf16x8 join_tr16(const s16x4& lo, const s16x4& hi) {
+  const i32x2 a = __builtin_bit_cast(i32x2, lo), b = __builtin_bit_cast(i32x2, hi);
+  const i32x4 r = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int32_t x) {
+  // first index i in [0, n) with a[i] > x (a ascending)
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace msa

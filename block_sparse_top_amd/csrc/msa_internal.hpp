@@ -1,0 +1,72 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "msa.h"
+
+namespace msa {
+
+// Device view of the plan's metadata (lives at the start of the workspace).
+struct DevMeta {
+  const int32_t* qo;          // [S]
+  const int32_t* kv;          // [S]
+  const int32_t* row_start;   // [S+1]
+  const int32_t* page_start;  // [S+1]
+  const int32_t* tiles;       // [ntiles][4] = seq, first row, rows, first position
+  int32_t S, T, NB, nb_max;
+};
+
+struct PlanLayout {
+  size_t meta = 0, meta_bytes = 0;
+  // prefill window scratch
+  size_t counts = 0, cursor = 0, offsets = 0, items = 0, nitems = 0, entries = 0, part_o = 0, part_lse = 0;
+  int64_t max_items = 0;
+  // decode split scratch
+  size_t dec_o = 0, dec_ml = 0;
+  size_t total = 0;
+};
+
+}  // namespace msa
+
+struct msa_plan_s {
+  msa_plan_desc_t d;                 // copy; host pointers cleared
+  std::vector<int32_t> qo, kv, nb, row_start, page_start;
+  int32_t S = 0, T = 0, NB = 0, nb_max = 0, G = 0;
+  int64_t max_rows = 0;              // rows per proxy/top-k call and per prefill window
+  std::vector<int32_t> tiles;        // proxy row tiles (seq, row0, nrows, pos0)
+  int32_t ntiles = 0;
+  std::vector<int32_t> meta;         // uploaded blob
+  msa::PlanLayout lay;
+  // prefill attention schedule
+  int32_t tokens_per_chunk = 0;      // 128 / G query tokens per 128-row chunk
+  int32_t entries_per_item = 0;      // tokens per work item
+  // decode schedule
+  int32_t dec_splits = 1;
+  const void* uploaded_to = nullptr; // last workspace the metadata was copied into
+};
+
+namespace msa {
+
+DevMeta dev_meta(const msa_plan_s* p, const void* workspace);
+
+// Kernel launchers (defined in the .hip files).  They assume validated inputs.
+hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const void* pq, const void* pk,
+                                 const float* qs, const float* ks, const int32_t* kv_indices, int32_t tile_lo,
+                                 int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
+                                 hipStream_t st);
+hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, int64_t row_begin,
+                       int64_t row_count, int32_t* sel, hipStream_t st);
+hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
+                                 const void* vp, const int32_t* kv_indices, const int32_t* sel, void* out,
+                                 float* lse, char* ws, int32_t w0, int32_t w1, hipStream_t st);
+hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
+                         const float* ks, const float* vs, const int32_t* kv_indices, const int32_t* sel,
+                         void* out, float* lse, char* ws, hipStream_t st);
+
+}  // namespace msa

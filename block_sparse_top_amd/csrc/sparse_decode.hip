@@ -1,0 +1,329 @@
+// Stage 3b of MSA: paged sparse decode (MiniMax-AI/MSA README, section
+// "Stacks": paged FP8 decode of the sparse attention).  One new query token
+// per sequence, already the last key of its sequence, attends to the keys of
+// its group's selected 128-key blocks.
+//
+// Design (gfx950), HBM-bound (every selected K/V byte is read once):
+//  * grid = (split, KV group, sequence); a workgroup of 4 waves takes the
+//    valid slots of its split one block per round; wave w owns keys
+//    32w .. 32w+31 of every block, so each round reads one whole block
+//    (K + V: 32 KB in fp8) with 16-byte coalesced loads, and the next
+//    round's loads are issued before the current round's math;
+//  * S^T = K Q^T on bf16 MFMA 16x16x32: the 32 keys are two 16-row tiles
+//    whose rows are interleaved so that each lane ends up holding 8
+//    consecutive keys of one head - exactly the B operand layout of the
+//    following O^T = V^T P^T product;
+//  * fp8 codes are widened to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8);
+//    the per-head fp32 scales multiply the logits and the output;
+//  * V reaches the A operand through LDS with transposing reads
+//    (ds_read_b64_tr_b8 for fp8, ds_read_b64_tr_b16 for bf16);
+//  * online softmax per wave; the 4 waves merge through LDS; with several
+//    splits a small kernel merges the splits by log-sum-exp.
+#include "device_common.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+struct DecodeArgs {
+  const uint8_t* q;     // bf16 [S, Hq, 128]
+  const uint8_t* kp;    // [N, Hkv, 128, 128] fp8 or bf16
+  const uint8_t* vp;
+  const float* ks;      // [Hkv] (fp8)
+  const float* vs;
+  const int32_t* kv_indices;
+  const int32_t* sel;   // [S, Hkv, k]
+  DevMeta m;
+  uint16_t* out;        // bf16 [S, Hq, 128]
+  float* lse;           // [S, Hq] or null
+  float* part_o;        // [S, Hq, nsplit, 128]
+  float* part_ml;       // [S, Hq, nsplit, 2] (lse, unused)
+  int32_t Hq, Hkv, G, k, nsplit;
+  float scale_log2;
+};
+
+template <bool FP8>
+struct DecTraits;
+template <>
+struct DecTraits<true> {
+  static constexpr int kRow = 128;      // bytes per key row
+  static constexpr int kVRow = 144;     // LDS bytes per V row
+  static constexpr int kKLoads = 2;     // 16-byte loads per lane per K tile
+  static constexpr int kVLoads = 4;     // 16-byte loads per lane for the wave's V rows
+};
+template <>
+struct DecTraits<false> {
+  static constexpr int kRow = 256;
+  static constexpr int kVRow = 272;
+  static constexpr int kKLoads = 4;
+  static constexpr int kVLoads = 8;
+};
+
+template <bool FP8>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  using Tr = DecTraits<FP8>;
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[4][32 * Tr::kVRow];
+  __shared__ float red_m[4][16], red_l[4][16];
+  __shared__ float red_o[4][16][129];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q16 = lane >> 4, m16 = lane & 15;
+  const int split = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;
+  const int G = a.G;
+  const int32_t kv_len = a.m.kv[seq];
+  const int32_t pos = kv_len - 1;
+  const int local = pos >> 7;
+  const int32_t* selrow = a.sel + ((int64_t)seq * a.Hkv + g) * a.k;
+  const int32_t* pages = a.kv_indices + a.m.page_start[seq];
+
+  // this split's share of the valid slots
+  int nvalid = 0;
+  for (int j = 0; j < a.k; ++j) nvalid += (selrow[j] >= 0 && selrow[j] <= local) ? 1 : 0;
+  const int per = (nvalid + a.nsplit - 1) / a.nsplit;
+  const int v_lo = split * per, v_hi = min(nvalid, v_lo + per);
+
+  // Q (B operand of S^T): lane -> head m16, d-run 32*q16 .. +32, 8 per k-step
+  bf16x8 qf[4];
+  {
+    const int hh = m16 < G ? m16 : 0;
+    const uint8_t* qrow = a.q + ((int64_t)seq * a.Hq + g * G + hh) * 256 + q16 * 64;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 16);
+      if (m16 >= G) qf[st] = bf16x8{};
+    }
+  }
+  const float kscale = FP8 ? a.ks[g] : 1.f;
+  const float vscale = FP8 ? a.vs[g] : 1.f;
+  const float c = a.scale_log2 * kscale;
+
+  // global loads of one block's K rows (this lane's two interleaved key rows)
+  // and V rows (2 lanes per key row) of this wave's 32 keys
+  i32x4 kreg[2][2 * Tr::kKLoads], vreg[2][Tr::kVLoads];
+  auto issue = [&](int buf, int b) {
+    const int32_t page = pages[b];
+    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * (128 * Tr::kRow) + (int64_t)(32 * wave) * Tr::kRow;
+    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * (128 * Tr::kRow) + (int64_t)(32 * wave) * Tr::kRow;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // tile j row i=m16 holds key 8*(i/4) + 4*j + i%4 of the wave's 32
+      const int key = 8 * (m16 >> 2) + 4 * j + (m16 & 3);
+      const uint8_t* src = kb + key * Tr::kRow + q16 * (Tr::kRow / 4);
+#pragma unroll
+      for (int x = 0; x < Tr::kKLoads; ++x) kreg[buf][j * Tr::kKLoads + x] = *reinterpret_cast<const i32x4*>(src + 16 * x);
+    }
+    const uint8_t* vsrc = vb + (lane >> 1) * Tr::kRow + (lane & 1) * (Tr::kRow / 2);
+#pragma unroll
+    for (int x = 0; x < Tr::kVLoads; ++x) vreg[buf][x] = *reinterpret_cast<const i32x4*>(vsrc + 16 * x);
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{};
+
+  // slot index of the v-th valid entry
+  auto nth_valid = [&](int v) {
+    int seen = 0;
+    for (int j = 0; j < a.k; ++j) {
+      const int b = selrow[j];
+      if (b >= 0 && b <= local) {
+        if (seen == v) return b;
+        ++seen;
+      }
+    }
+    return local;
+  };
+
+  int cur = 0;
+  if (v_lo < v_hi) issue(0, nth_valid(v_lo));
+  for (int v = v_lo; v < v_hi; ++v) {
+    const int b = nth_valid(v);
+    // V of this round -> this wave's LDS tile
+    uint8_t* vt = vlds[wave];
+    // rows past kv_len are page padding (may hold NaN; P = 0 there but 0 * NaN is NaN)
+    const bool vrow_ok = b * 128 + 32 * wave + (lane >> 1) < kv_len;
+#pragma unroll
+    for (int x = 0; x < Tr::kVLoads; ++x)
+      lds_store16<i32x4>(vt + (lane >> 1) * Tr::kVRow + (lane & 1) * (Tr::kRow / 2) + 16 * x,
+                         vrow_ok ? vreg[cur][x] : i32x4{});
+    i32x4 kcur[2 * Tr::kKLoads];
+#pragma unroll
+    for (int x = 0; x < 2 * Tr::kKLoads; ++x) kcur[x] = kreg[cur][x];
+    if (v + 1 < v_hi) issue(cur ^ 1, nth_valid(v + 1));
+    __syncthreads();
+
+    // S^T tiles
+    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bf16x8 af;
+        if constexpr (FP8) {
+          const i32x4 w = kcur[j * Tr::kKLoads + st / 2];
+          af = fp8x8_to_bf16x8((uint32_t)w[(st & 1) * 2], (uint32_t)w[(st & 1) * 2 + 1]);
+        } else {
+          af = __builtin_bit_cast(bf16x8, kcur[j * Tr::kKLoads + st]);
+        }
+        sacc[j] = mfma16x16x32(af, qf[st], sacc[j]);
+      }
+    }
+    // lane holds keys 32*wave + 8*q16 + t, t = 4j + e; mask keys past the position
+    const int lim = pos - (b * 128 + 32 * wave + 8 * q16);
+    float cm = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float s = (4 * j + e) <= lim ? sacc[j][e] : kNegInf;
+        sacc[j][e] = s;
+        cm = fmaxf(cm, s);
+      }
+    }
+    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    const float m_new = fmaxf(m_run, cm);
+    // a wave whose keys so far are all masked keeps m = -inf; use 0 as the
+    // reference then so that no (-inf) - (-inf) appears
+    const float m_ref = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2((m_run - m_ref) * c);
+    bf16x8 pf;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pv = fast_exp2((sacc[j][e] - m_ref) * c);
+        psum += pv;
+        pf[4 * j + e] = (__bf16)pv;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      oacc[dt] *= alpha;
+      bf16x8 vf;
+      if constexpr (FP8) {
+        // lane m16 of group q16 gets bytes V[8*q16 + e][16*dt + m16], e = 0..7
+        const i32x2 w = lds_read_tr8(vt + (8 * q16 + (m16 >> 1)) * Tr::kVRow + 16 * dt + 8 * (m16 & 1));
+        vf = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
+      } else {
+        const s16x4 lo = lds_read_tr16(vt + (8 * q16 + (m16 >> 2)) * Tr::kVRow + (16 * dt + 4 * (m16 & 3)) * 2);
+        const s16x4 hi = lds_read_tr16(vt + (8 * q16 + 4 + (m16 >> 2)) * Tr::kVRow + (16 * dt + 4 * (m16 & 3)) * 2);
+        vf = join_tr16(lo, hi);
+      }
+      oacc[dt] = mfma16x16x32(vf, pf, oacc[dt]);
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+
+  // wave -> LDS: running max, lane-group sums, O^T (lane holds d = 16dt + 4q16 + e of head m16)
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (q16 == 0) {
+    red_m[wave][m16] = m_run;
+    red_l[wave][m16] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red_o[wave][m16][16 * dt + 4 * q16 + e] = oacc[dt][e];
+  __syncthreads();
+
+  // combine the 4 waves: thread -> (head, 8 consecutive d)
+  const int hh = tid >> 4;          // 16 heads
+  const int d0 = (tid & 15) * 8;    // 16 x 8 = 128
+  if (hh < G) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
+    float wsum = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = red_m[w][hh] == kNegInf ? 0.f : fast_exp2((red_m[w][hh] - M) * c);
+      wsum += f * red_l[w][hh];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) o[x] += f * red_o[w][hh][d0 + x];
+    }
+    const int h = g * G + hh;
+    const float lse_v = (wsum > 0.f) ? (M * c + fast_log2(wsum)) * kLn2 : kNegInf;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    if (a.nsplit == 1) {
+      bf16x8 ob;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(o[x] * inv * vscale);
+      *reinterpret_cast<bf16x8*>(a.out + ((int64_t)seq * a.Hq + h) * 128 + d0) = ob;
+      if (a.lse && d0 == 0) a.lse[(int64_t)seq * a.Hq + h] = lse_v;
+    } else {
+      float* po = a.part_o + (((int64_t)seq * a.Hq + h) * a.nsplit + split) * 128 + d0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) po[x] = o[x] * inv * vscale;
+      if (d0 == 0) a.part_ml[(((int64_t)seq * a.Hq + h) * a.nsplit + split) * 2] = lse_v;
+    }
+  }
+}
+
+// Merge decode splits: one wave per (sequence, head), lane -> 2 columns.
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* part_o, const float* part_ml, uint16_t* out,
+                                                           float* lse, int32_t S, int32_t Hq, int32_t nsplit) {
+  const int lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= (int64_t)S * Hq) return;
+  float M = kNegInf;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, part_ml[(idx * nsplit + sp) * 2]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float l = part_ml[(idx * nsplit + sp) * 2];
+    if (l == kNegInf) continue;
+    const float w = fast_exp2((l - M) * kLog2e);
+    const f32x2 v = *reinterpret_cast<const f32x2*>(part_o + (idx * nsplit + sp) * 128 + 2 * lane);
+    L += w;
+    o0 += w * v[0];
+    o1 += w * v[1];
+  }
+  bf16x2 o;
+  o[0] = (__bf16)(o0 / L);
+  o[1] = (__bf16)(o1 / L);
+  *reinterpret_cast<bf16x2*>(out + idx * 128 + 2 * lane) = o;
+  if (lse && lane == 0) lse[idx] = M + fast_log2(L) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
+                         const float* ks, const float* vs, const int32_t* kv_indices, const int32_t* sel,
+                         void* out, float* lse, char* ws, hipStream_t st) {
+  DecodeArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.kp = static_cast<const uint8_t*>(kp);
+  a.vp = static_cast<const uint8_t*>(vp);
+  a.ks = ks;
+  a.vs = vs;
+  a.kv_indices = kv_indices;
+  a.sel = sel;
+  a.m = m;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(ws + p->lay.dec_o);
+  a.part_ml = reinterpret_cast<float*>(ws + p->lay.dec_ml);
+  a.Hq = p->d.num_qo_heads;
+  a.Hkv = p->d.num_kv_heads;
+  a.G = p->G;
+  a.k = p->d.topk;
+  a.nsplit = p->dec_splits;
+  a.scale_log2 = p->d.sm_scale * kLog2e;
+  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)p->S), block(256);
+  if (p->d.kv_dtype == MSA_FP8_E4M3) hipLaunchKernelGGL(decode_kernel<true>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(decode_kernel<false>, grid, block, 0, st, a);
+  if (a.nsplit > 1) {
+    const int64_t nw = (int64_t)p->S * a.Hq;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, a.part_o, a.part_ml,
+                       a.out, lse, p->S, a.Hq, a.nsplit);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

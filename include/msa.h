@@ -1,0 +1,197 @@
+/*
+ * msa.h - C ABI of the MiniMax Sparse Attention (MSA) forward path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The path has three stages, in the order the MiniMax-AI/MSA README (section
+ * "Usage") runs them and the MSA news summary ("MSA; MiniMax sparse attention
+ * kernels for SM100 GPUs", paragraph on the three-step flow) describes:
+ *
+ *   1. msa_proxy_block_maxscore - a cheap dense proxy pass whose only output
+ *      is, per query row, proxy head and 128-token KV block, the largest
+ *      scaled proxy logit in that block (causal).
+ *   2. msa_topk_select          - per (row, KV group) the `topk` best blocks,
+ *      the row's own (local) block always kept (Flash-MSA article, paragraph
+ *      on the forward kernels).
+ *   3. msa_sparse_attn_prefill  - GQA attention over only the selected blocks
+ *      of a paged K/V cache (README "Usage": kv_block_indexes argument),
+ *      msa_sparse_attn_decode   - its one-token-per-sequence paged decode
+ *      form with fp8 or bf16 K/V (README "Stacks": paged FP8 decode wrapper).
+ *
+ * msa_plan turns the per-sequence lengths into a host plan (README "Usage":
+ * the plan is built from qo_lens / kv_lens, heads and page size, then run).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named *_host are host memory; every other tensor pointer is
+ *    device memory on the current HIP device.  All tensors are dense,
+ *    row-major and 16-byte aligned.  The caller owns every buffer.
+ *  - The library allocates no device memory.  Each call is enqueued on the
+ *    caller's `stream` and returns without synchronising; results are ready
+ *    when the stream reaches that point.
+ *  - Rows: the query rows of all sequences are concatenated, T = sum(qo_len).
+ *    Row i of sequence s sits at KV position kv_len[s] - qo_len[s] + i
+ *    (causal, bottom-right aligned).  Key j is visible to it iff j <= that
+ *    position (the diagonal counts) and j < kv_len[s].
+ *  - Pages: page_size = 128 = block size.  kv_indices is one flat int32 list;
+ *    sequence s owns its ceil(kv_len[s]/128) entries starting right after
+ *    those of sequences 0..s-1.  Key j of sequence s is slot j % 128 of page
+ *    kv_indices[start_s + j / 128].  Page pools are
+ *    [num_pages, heads, 128, head_dim] (the README's k_pages.shape[1] is the
+ *    KV head count).  Slots past kv_len in a sequence's last page are never
+ *    read into results (they may hold anything, NaN included).
+ *  - Block ids in kv_block_indexes are logical blocks of the row's sequence
+ *    (0-based), ascending, padded with -1.
+ *  - head_dim = proxy head_dim = 128; page_size = 128.
+ *  - bf16 = IEEE bfloat16; fp8 = OCP E4M3FN.  fp8 tensors carry one fp32
+ *    scale per head (value = code x scale).
+ *  - Every call returns msa_status_t; on failure msa_last_error() gives a
+ *    message (thread-local, valid until the thread's next call).  No C++
+ *    exception crosses this boundary.  Argument errors are detected on the
+ *    host before anything is enqueued.  Device-side data errors (page ids
+ *    outside the pool, block ids beyond the row's local block) are not
+ *    checked and lead to undefined results.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct msa_plan_s* msa_plan_t;
+typedef void* msa_stream_t; /* a hipStream_t; NULL = the null stream */
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1,         /* bad pointer, size, range or combination */
+  MSA_ERR_UNSUPPORTED = 2,         /* valid but not built (head_dim != 128 ...) */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes smaller than the plan's */
+  MSA_ERR_HIP = 4                  /* the HIP runtime reported an error */
+} msa_status_t;
+
+typedef enum { MSA_BF16 = 0, MSA_FP8_E4M3 = 1 } msa_dtype_t;
+typedef enum { MSA_PREFILL = 0, MSA_DECODE = 1 } msa_mode_t;
+
+typedef struct {
+  int32_t batch;               /* number of sequences, >= 1 */
+  const int32_t* qo_lens_host; /* [batch] query rows per sequence (copied) */
+  const int32_t* kv_lens_host; /* [batch] keys per sequence, >= qo_len (copied) */
+  int32_t num_qo_heads;        /* H_q */
+  int32_t num_kv_heads;        /* H_kv; H_q % H_kv == 0, G = H_q / H_kv in {1,2,4,8,16} */
+  int32_t num_proxy_heads;     /* P == H_kv (prefill); proxy head p drives KV group p */
+  int32_t num_proxy_kv_heads;  /* P_k: 1 (shared) or P */
+  int32_t head_dim;            /* 128 */
+  int32_t page_size;           /* 128 */
+  int32_t topk;                /* slots per (row, group), local block included; 1..64 */
+  msa_dtype_t kv_dtype;        /* K/V pages: bf16 (prefill, decode) or fp8 (decode) */
+  msa_dtype_t proxy_dtype;     /* proxy q and proxy k pages: bf16 or fp8 */
+  float sm_scale;              /* main attention logit scale */
+  float proxy_sm_scale;        /* proxy logit scale */
+  msa_mode_t mode;             /* which entry points the plan serves */
+  int64_t max_rows_per_call;   /* prefill: rows per proxy/top-k call and per
+                                  internal attention window; 0 = min(T, 32768) */
+} msa_plan_desc_t;
+
+/* Build a host plan from `desc`.  Validates every field; touches no device.
+ * *workspace_bytes receives the device workspace size the compute calls need
+ * (the caller allocates it; a workspace belongs to one plan).  The plan is
+ * released by msa_plan_destroy. */
+msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* plan, size_t* workspace_bytes);
+
+msa_status_t msa_plan_destroy(msa_plan_t plan);
+
+/* Stage 1: proxy block max scores (README "Usage", proxy pass with
+ * output_maxscore; Flash-MSA article, max-pooling of proxy scores over
+ * 128-token blocks).
+ *
+ * For rows r in [row_begin, row_begin + row_count), proxy head p and block b
+ * of r's sequence with b <= local(r) = position(r) / 128:
+ *   max_score[p][b][r - row_begin] = max over visible keys j of block b of
+ *       proxy_sm_scale * qs[p] * ks[pk(p)] * <proxy_q[r][p], proxy_k[j][pk(p)]>
+ * where pk(p) = p if P_k = P else 0, and qs/ks are the fp8 scales (1 for
+ * bf16).  Entries with b > local(r) are left unspecified (may be written).
+ *
+ *   proxy_q        [T, P, 128]  bf16 or fp8 (desc.proxy_dtype)
+ *   proxy_k_pages  [num_pages, P_k, 128, 128], same dtype
+ *   proxy_q_scale  [P]   fp32, device; NULL iff proxy dtype is bf16
+ *   proxy_k_scale  [P_k] fp32, device; NULL iff proxy dtype is bf16
+ *   kv_indices     int32 flat page table (see conventions)
+ *   max_score      fp32 [P, nb_max, row_count], nb_max = max over sequences
+ *                  of ceil(kv_len / 128); row_count <= plan's max_rows_per_call
+ * Errors: INVALID_ARG for a null pointer, a row range outside [0, T), an
+ * empty range, or a scale pointer that does not match the dtype;
+ * UNSUPPORTED if the plan is a decode plan. */
+msa_status_t msa_proxy_block_maxscore(msa_plan_t plan, const void* proxy_q, const void* proxy_k_pages,
+                                      const float* proxy_q_scale, const float* proxy_k_scale,
+                                      const int32_t* kv_indices, int64_t row_begin, int64_t row_count,
+                                      float* max_score, void* workspace, size_t workspace_bytes,
+                                      msa_stream_t stream);
+
+/* Stage 2: top-k block selection (README "Usage", sparse_topk_select with
+ * `topk` slots; Flash-MSA article: each token's local block always stays
+ * visible, each proxy head selects for its own KV group).
+ *
+ * For each row r in the range and group g (= proxy head g): the local block
+ * plus the topk-1 highest-scoring blocks among 0..local-1 (ties: lower block
+ * id), ascending, -1 padded, written to kv_block_indexes[r][g][0..topk).
+ * When local < topk - 1 every block 0..local is selected.
+ *
+ *   max_score         fp32 [P, nb_max, row_count] as written by stage 1
+ *   kv_block_indexes  int32 [T, H_kv, topk]; only the rows of the range are written
+ * Errors: as stage 1. */
+msa_status_t msa_topk_select(msa_plan_t plan, const float* max_score, int64_t row_begin, int64_t row_count,
+                             int32_t* kv_block_indexes, void* workspace, size_t workspace_bytes,
+                             msa_stream_t stream);
+
+/* Stage 3a: block-sparse GQA prefill attention (README "Usage", attention
+ * run with kv_block_indexes; Flash-MSA article: GQA main attention,
+ * block-sparse flash attention reformulated as variable-length attention).
+ *
+ * For every row r and query head h (group g = h / G):
+ *   keys K = { j : j / 128 in kv_block_indexes[r][g][:], j visible to r }
+ *   out[r][h] = sum_j softmax_j(sm_scale * <q[r][h], k[j][g]>) v[j][g]
+ *   lse[r][h] = natural log of sum_j exp(sm_scale * <q[r][h], k[j][g]>)
+ * Every selection must contain the row's local block (stage 2 guarantees it).
+ *
+ *   q                 bf16 [T, H_q, 128]
+ *   k_pages, v_pages  bf16 [num_pages, H_kv, 128, 128]
+ *   k_scale, v_scale  must be NULL (bf16 K/V)
+ *   kv_block_indexes  int32 [T, H_kv, topk]
+ *   out               bf16 [T, H_q, 128]
+ *   lse               fp32 [T, H_q] or NULL
+ * Errors: INVALID_ARG for null pointers; UNSUPPORTED for a decode plan or
+ * fp8 K/V; WORKSPACE_TOO_SMALL. */
+msa_status_t msa_sparse_attn_prefill(msa_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
+                                     const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                     const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, msa_stream_t stream);
+
+/* Stage 3b: paged sparse decode (README "Stacks": paged FP8 decode).  Stage
+ * 3a with qo_len = 1 for every sequence: the new token is already the last
+ * key of its sequence (position kv_len - 1), so its local block is the last.
+ *
+ *   q                 bf16 [batch, H_q, 128]
+ *   k_pages, v_pages  fp8 or bf16 (desc.kv_dtype) [num_pages, H_kv, 128, 128]
+ *   k_scale, v_scale  fp32 [H_kv] device, NULL iff bf16
+ *   kv_block_indexes  int32 [batch, H_kv, topk]
+ *   out               bf16 [batch, H_q, 128];  lse fp32 [batch, H_q] or NULL
+ * Errors: INVALID_ARG; UNSUPPORTED for a prefill plan; WORKSPACE_TOO_SMALL. */
+msa_status_t msa_sparse_attn_decode(msa_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
+                                    const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                    const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, msa_stream_t stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* msa_last_error(void);
+
+/* Plan introspection (host only): total rows T, max blocks per sequence
+ * nb_max, and the row bound of one proxy / top-k call. */
+msa_status_t msa_plan_info(msa_plan_t plan, int64_t* total_rows, int32_t* nb_max, int64_t* max_rows_per_call);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H_ */

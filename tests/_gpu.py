@@ -1,0 +1,91 @@
+"""Helpers for the GPU parity tests: move synthetic inputs to the device, run
+the HIP path through the binding, compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from synthetic.gen import Inputs, BF16, FP8
+
+BAND = 1e-3          # selection tie band on block scores
+MS_ATOL, MS_RTOL = 1e-4, 1e-5
+BF16_ATOL, BF16_COS = 2e-2, 0.999
+FP8_ATOL, FP8_COS = 6e-2, 0.99
+
+
+def dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def device_inputs(inp: Inputs, device="cuda") -> dict:
+    d = dict(q=dev(inp.q), k_pages=dev(inp.k_pages), v_pages=dev(inp.v_pages), kv_indices=dev(inp.kv_indices))
+    for name in ("k_scale", "v_scale", "proxy_q", "proxy_k_pages", "proxy_q_scale", "proxy_k_scale",
+                 "kv_block_indexes"):
+        v = getattr(inp, name)
+        d[name] = dev(v) if v is not None else None
+    return d
+
+
+def plan_for(msa, inp: Inputs, max_rows_per_call=0, topk=None):
+    w = inp.w
+    if w.mode == "decode":
+        return msa.msa_plan(None, w.kv_lens, w.num_qo_heads, w.num_kv_heads, topk=topk or w.topk,
+                            kv_dtype=w.kv_dtype, mode="decode")
+    return msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                        w.num_proxy_kv_heads, topk=topk or w.topk, kv_dtype=w.kv_dtype, proxy_dtype=w.proxy_dtype,
+                        max_rows_per_call=max_rows_per_call)
+
+
+def bf16_out_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    a = a.ravel()
+    b = b.ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def oracle_scores(inp: Inputs, rows=None):
+    w = inp.w
+    return O.proxy_block_maxscore(inp.proxy_q, inp.proxy_k_pages, inp.kv_indices, w.qo_lens, w.kv_lens,
+                                  w.page_size, w.proxy_sm_scale, w.proxy_dtype, inp.proxy_q_scale,
+                                  inp.proxy_k_scale, rows=rows)
+
+
+def check_max_score(gpu_ms: np.ndarray, ref: np.ndarray, what=""):
+    """gpu_ms [P, nb_max, n] vs ref [n, P, nb_max]; compare defined entries."""
+    g = np.transpose(gpu_ms, (2, 0, 1)).astype(np.float64)
+    m = ~np.isnan(ref)
+    fin = m & np.isfinite(ref)
+    # -inf entries must match exactly
+    assert np.array_equal(np.isneginf(g[m & ~fin]), np.ones(int((m & ~fin).sum()), bool)), what
+    err = np.abs(g[fin] - ref[fin])
+    tol = MS_ATOL + MS_RTOL * np.abs(ref[fin])
+    bad = err > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} max_score entries off (worst {err.max():.3g})"
+
+
+def check_selection(sel: np.ndarray, scores: np.ndarray, locals_: np.ndarray, k: int, what=""):
+    """sel [n, P, k] (GPU) against fp64 oracle scores [n, P, nb]."""
+    n, P, _ = sel.shape
+    bad = []
+    ties = 0
+    for i in range(n):
+        for p in range(P):
+            ok, why = O.check_selection_row(sel[i, p], scores[i, p], int(locals_[i]), k, BAND)
+            if not ok:
+                bad.append((i, p, why))
+    assert not bad, f"{what}: {len(bad)} selections rejected, first {bad[:3]}"
+    return ties
+
+
+def check_output(out: np.ndarray, ref: np.ndarray, atol: float, cos_min: float, what=""):
+    err = np.abs(out - ref).max()
+    c = cosine(out, ref)
+    assert err <= atol and c >= cos_min, f"{what}: max|err| {err:.4g} (tol {atol}), cos {c:.6f} (min {cos_min})"
+    return err, c

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every entry point include/msa.h declares,
+and rejects bad arguments on the host (no GPU needed: no call here reaches
+a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+msa = pytest.importorskip("block_sparse_top_amd.msa", reason="libmsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"msa_plan", "msa_plan_destroy", "msa_proxy_block_maxscore", "msa_topk_select",
+            "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_last_error"} <= set(names)
+    lib = ctypes.CDLL(msa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _plan(**kw):
+    args = dict(qo_lens=[300, 5], kv_lens=[300, 900], num_qo_heads=8, num_kv_heads=2, num_proxy_heads=2,
+                num_proxy_kv_heads=2, topk=4, allocate=False)
+    args.update(kw)
+    return msa.msa_plan(**args)
+
+
+def test_plan_info_and_workspace():
+    p = _plan()
+    assert p.total_rows == 305 and p.nb_max == 8 and p.max_rows_per_call == 305
+    assert p.workspace_bytes > 0
+    p2 = _plan(max_rows_per_call=100)
+    assert p2.max_rows_per_call == 100 and p2.workspace_bytes < p.workspace_bytes
+    d = msa.msa_plan(None, [1000] * 4, 16, 2, topk=17, kv_dtype="fp8", mode="decode", allocate=False)
+    assert d.total_rows == 4 and d.nb_max == 8
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), msa.MSA_ERR_UNSUPPORTED),
+    (dict(page_size=64), msa.MSA_ERR_UNSUPPORTED),
+    (dict(num_qo_heads=6, num_kv_heads=2), msa.MSA_ERR_UNSUPPORTED),        # G = 3
+    (dict(num_qo_heads=7, num_kv_heads=2), msa.MSA_ERR_INVALID_ARG),
+    (dict(topk=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(topk=65), msa.MSA_ERR_INVALID_ARG),
+    (dict(qo_lens=[300, 901]), msa.MSA_ERR_INVALID_ARG),                     # qo > kv
+    (dict(qo_lens=[0, 5]), msa.MSA_ERR_INVALID_ARG),
+    (dict(num_proxy_heads=1), msa.MSA_ERR_UNSUPPORTED),
+    (dict(num_proxy_kv_heads=3), msa.MSA_ERR_INVALID_ARG),
+    (dict(kv_dtype="fp8"), msa.MSA_ERR_UNSUPPORTED),                         # fp8 K/V prefill not built
+    (dict(sm_scale=-1.0), msa.MSA_ERR_INVALID_ARG),
+])
+def test_plan_validation(kw, status):
+    with pytest.raises(msa.MsaError) as e:
+        _plan(**kw)
+    assert e.value.status == status
+    assert msa.lib().msa_last_error().decode()
+
+
+def test_decode_plan_needs_single_query_rows():
+    with pytest.raises(msa.MsaError) as e:
+        msa.msa_plan([2, 1], [100, 100], 8, 2, topk=4, mode="decode", allocate=False)
+    assert e.value.status == msa.MSA_ERR_INVALID_ARG
+
+
+class _Fake:
+    """Stands in for a device tensor: an aligned, never-dereferenced address."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _call(fn, *args):
+    return getattr(msa.lib(), fn)(*args)
+
+
+def test_compute_calls_validate_before_touching_the_device():
+    p = _plan()
+    L = msa.lib()
+    a = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x20000)
+    none = None
+    nb = p.workspace_bytes
+    # null pointer
+    st = L.msa_proxy_block_maxscore(p.handle, none, a, none, none, a, 0, 10, a, ws, nb, none)
+    assert st == msa.MSA_ERR_INVALID_ARG and b"proxy_q" in L.msa_last_error()
+    # misaligned pointer
+    st = L.msa_proxy_block_maxscore(p.handle, ctypes.c_void_p(0x10004), a, none, none, a, 0, 10, a, ws, nb, none)
+    assert st == msa.MSA_ERR_INVALID_ARG
+    # row range outside [0, T) and empty range
+    assert L.msa_proxy_block_maxscore(p.handle, a, a, none, none, a, 300, 10, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_topk_select(p.handle, a, 0, 0, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    # scales given for bf16
+    assert L.msa_proxy_block_maxscore(p.handle, a, a, a, a, a, 0, 10, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    # workspace too small / missing / misaligned
+    assert L.msa_topk_select(p.handle, a, 0, 10, a, ws, nb - 1, none) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    assert L.msa_topk_select(p.handle, a, 0, 10, a, none, nb, none) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_topk_select(p.handle, a, 0, 10, a, ctypes.c_void_p(0x20010), nb, none) == msa.MSA_ERR_INVALID_ARG
+    # wrong mode
+    assert L.msa_sparse_attn_decode(p.handle, a, a, a, none, none, a, a, a, none, ws, nb, none) == msa.MSA_ERR_UNSUPPORTED
+    # prefill takes no scales
+    assert L.msa_sparse_attn_prefill(p.handle, a, a, a, a, a, a, a, a, none, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    d = msa.msa_plan(None, [1000] * 4, 16, 2, topk=17, kv_dtype="fp8", mode="decode", allocate=False)
+    # fp8 decode needs both scales
+    assert L.msa_sparse_attn_decode(d.handle, a, a, a, a, none, a, a, a, none, ws, d.workspace_bytes, none) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_proxy_block_maxscore(d.handle, a, a, none, none, a, 0, 1, a, ws, d.workspace_bytes, none) == msa.MSA_ERR_UNSUPPORTED
+    assert L.msa_plan_destroy(None) == msa.MSA_OK

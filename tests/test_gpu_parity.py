@@ -1,0 +1,137 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle on
+seeded inputs small enough for the oracle, spanning several tiles and ragged
+tails: each stage is checked in turn (max scores, selection, attention), and
+the attention is checked on the selection the GPU produced so that near-ties
+cannot move the output.
+
+Tolerances: max scores |gpu - oracle| <= 1e-4 + 1e-5 |oracle| (fp32
+accumulation of exact bf16/fp8 products); selections by the 1e-3 band rule;
+outputs max-abs <= 2e-2 and cosine >= 0.999 (bf16 K/V) or <= 6e-2 and
+>= 0.99 (fp8 K/V)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synthetic.gen import Workload, make_inputs, workload, seed_of, FP8, BF16
+from tests._gpu import (device_inputs, plan_for, bf16_out_to_f64, oracle_scores, check_max_score, check_selection,
+                        check_output, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS)
+
+pytestmark = pytest.mark.gpu
+
+
+def _msa():
+    from block_sparse_top_amd import msa
+    return msa
+
+
+PREFILL_CASES = {
+    "cfg1": (workload(1), seed_of(1), 0),
+    "cfg1_shared_proxy_k": (workload(1, num_proxy_kv_heads=1, name="cfg1b"), seed_of(1), 0),
+    "varlen_ragged_prefix": (Workload("ragged", [300, 77, 1, 513], [300, 200, 1, 700], 16, 4, 4, 4, topk=5,
+                                      extra_pages=0.25, poison_tail=True), 11, 0),
+    "gqa8": (Workload("gqa8", [640], [640], 16, 2, 2, 2, topk=3), 12, 0),
+    "gqa1_gqa16": (Workload("g1", [384], [384], 2, 2, 2, 2, topk=2), 13, 0),
+    "gqa16": (Workload("g16", [260], [400], 32, 2, 2, 2, topk=3, poison_tail=True), 14, 0),
+    "fp8_proxy": (Workload("fp8p", [700], [700], 8, 2, 2, 2, topk=4, proxy_dtype=FP8), 15, 0),
+    "lowrank": (Workload("lr", [512, 1024], [512, 1024], 16, 2, 2, 2, topk=4, lowrank=8), 16, 0),
+    "chunked_calls": (Workload("chunk", [900, 333], [900, 400], 8, 2, 2, 2, topk=6, poison_tail=True), 17, 200),
+    "topk_exceeds_blocks": (Workload("bigk", [500], [500], 8, 2, 2, 2, topk=9), 18, 0),
+    "topk1_local_only": (Workload("k1", [450], [450], 8, 2, 2, 2, topk=1), 19, 0),
+}
+
+
+def run_prefill_stages(msa, inp, max_rows):
+    w = inp.w
+    d = device_inputs(inp)
+    plan = plan_for(msa, inp, max_rows_per_call=max_rows)
+    T = w.total_rows
+    R = plan.max_rows_per_call
+    ms_all = []
+    sel = torch.full((T, w.num_kv_heads, w.topk), -7, dtype=torch.int32, device="cuda")
+    ms = msa.max_score_buffer(plan)
+    for r0 in range(0, T, R):
+        n = min(R, T - r0)
+        ms.fill_(float("nan"))
+        msa.msa_proxy_block_maxscore(plan, d["proxy_q"], d["proxy_k_pages"], d["proxy_q_scale"], d["proxy_k_scale"],
+                                     d["kv_indices"], r0, n, ms)
+        msa.msa_topk_select(plan, ms, r0, n, sel)
+        ms_all.append(ms[:, :, :n].cpu().numpy().copy())
+    out = torch.full((T, w.num_qo_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, w.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_prefill(plan, d["q"], d["k_pages"], d["v_pages"], d["kv_indices"], sel, out, lse)
+    torch.cuda.synchronize()
+    return np.concatenate(ms_all, axis=2), sel.cpu().numpy(), bf16_out_to_f64(out), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", list(PREFILL_CASES))
+def test_prefill_stages_match_oracle(case):
+    msa = _msa()
+    w, seed, max_rows = PREFILL_CASES[case]
+    inp = make_inputs(w, seed)
+    print(f"[parity] prefill case={case} T={w.total_rows} seed={seed}", flush=True)
+    gms, gsel, gout, glse = run_prefill_stages(msa, inp, max_rows)
+    ref_ms = oracle_scores(inp)
+    check_max_score(gms, ref_ms, case)
+    lay = O.Layout(w.qo_lens, w.kv_lens, w.page_size)
+    locals_ = np.array([lay.local(r) for r in range(w.total_rows)])
+    check_selection(gsel, ref_ms, locals_, w.topk, case)
+    ref_out, ref_lse = O.sparse_attention(inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, gsel, w.qo_lens,
+                                          w.kv_lens, w.page_size, w.sm_scale)
+    check_output(gout, ref_out, BF16_ATOL, BF16_COS, case)
+    assert np.abs(glse - ref_lse).max() < 1e-3, case
+
+
+def test_topk_exact_on_given_scores_with_ties():
+    """The top-k kernel on fp32 scores with many exact ties must equal the
+    oracle's selection bit for bit (same fp32 values, lower id wins)."""
+    msa = _msa()
+    w = Workload("ties", [1500, 40], [1500, 300], 8, 2, 2, 2, topk=6)
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, 8, 2, 2, 2, topk=6, max_rows_per_call=1540)
+    rng = np.random.default_rng(5)
+    T = w.total_rows
+    scores = rng.integers(-3, 4, size=(2, plan.nb_max, T)).astype(np.float32)     # heavy ties
+    scores[:, :, ::7] = rng.standard_normal((2, plan.nb_max, len(range(0, T, 7)))).astype(np.float32)
+    ms = torch.from_numpy(scores).cuda()
+    sel = torch.full((T, 2, 6), -7, dtype=torch.int32, device="cuda")
+    msa.msa_topk_select(plan, ms, 0, T, sel)
+    got = sel.cpu().numpy()
+    lay = O.Layout(w.qo_lens, w.kv_lens, 128)
+    for r in range(T):
+        for p in range(2):
+            exp = O.topk_select_row(scores[p, :, r].astype(np.float64), lay.local(r), 6)
+            assert np.array_equal(got[r, p], exp), (r, p, got[r, p], exp)
+
+
+DECODE_CASES = {
+    "fp8_g8": (Workload("dec", [1] * 4, [1000, 128, 2000, 5000], 16, 2, topk=17, kv_dtype=FP8, mode="decode",
+                        extra_pages=0.2, poison_tail=True), 21),
+    "bf16_g8": (Workload("decb", [1] * 3, [129, 4000, 777], 16, 2, topk=9, kv_dtype=BF16, mode="decode",
+                         poison_tail=True), 22),
+    "fp8_g16": (Workload("dec16", [1] * 2, [3000, 300], 32, 2, topk=5, kv_dtype=FP8, mode="decode"), 23),
+    "fp8_g4_local_only": (Workload("dec1", [1] * 5, [50, 128, 129, 255, 1000], 8, 2, topk=1, kv_dtype=FP8,
+                                   mode="decode", poison_tail=True), 24),
+    "fp8_g1": (Workload("decg1", [1] * 2, [640, 1500], 4, 4, topk=3, kv_dtype=FP8, mode="decode"), 25),
+}
+
+
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_matches_oracle(case):
+    msa = _msa()
+    w, seed = DECODE_CASES[case]
+    inp = make_inputs(w, seed)
+    print(f"[parity] decode case={case} B={w.num_seqs} seed={seed}", flush=True)
+    d = device_inputs(inp)
+    plan = plan_for(msa, inp)
+    out = torch.full((w.num_seqs, w.num_qo_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((w.num_seqs, w.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_decode(plan, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"],
+                               d["kv_indices"], d["kv_block_indexes"], out, lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.sparse_decode(inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, inp.kv_block_indexes, w.kv_lens,
+                                   w.page_size, w.sm_scale, w.kv_dtype, inp.k_scale, inp.v_scale)
+    atol, cmin = (FP8_ATOL, FP8_COS) if w.kv_dtype == FP8 else (BF16_ATOL, BF16_COS)
+    check_output(bf16_out_to_f64(out), ref, atol, cmin, case)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-3, case
