@@ -95,9 +95,73 @@ DevMeta dev_meta(const msa_plan_s* p, const void* workspace) {
   return m;
 }
 
+namespace {
+hipEvent_t take_event(msa::Profiler& pr) {
+  if (!pr.pool.empty()) {
+    hipEvent_t e = pr.pool.back();
+    pr.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "csr", "partial_attn", "merge", "decode",
+                                    "decode_merge"};
+}  // namespace
+
+ProfScope::ProfScope(const msa_plan_s* p, const char* name, hipStream_t st) : p_(p), st_(st) {
+  if (p->prof.kernel.empty() || p->prof.kernel != name) return;
+  hipEvent_t start = take_event(p->prof);
+  stop_ = take_event(p->prof);
+  if (!start || !stop_) {
+    stop_ = nullptr;
+    return;
+  }
+  (void)hipEventRecord(start, st);
+  p->prof.pending.emplace_back(start, stop_);
+}
+
+ProfScope::~ProfScope() {
+  if (stop_) (void)hipEventRecord(stop_, st_);
+}
+
 }  // namespace msa
 
 extern "C" {
+
+msa_status_t msa_profile_kernel(msa_plan_t p, const char* kernel) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_profile_kernel: NULL plan");
+  if (!kernel) {
+    p->prof.kernel.clear();
+    return ok();
+  }
+  for (const char* n : msa::kKernelNames)
+    if (std::strcmp(n, kernel) == 0) {
+      p->prof.kernel = kernel;
+      return ok();
+    }
+  return fail(MSA_ERR_INVALID_ARG, "msa_profile_kernel: unknown kernel '%s'", kernel);
+}
+
+msa_status_t msa_profile_read(msa_plan_t p, double* total_ms, int64_t* launches) {
+  if (!p || !total_ms || !launches) return fail(MSA_ERR_INVALID_ARG, "msa_profile_read: NULL argument");
+  double tot = 0.0;
+  msa_status_t st = MSA_OK;
+  for (auto& pr : p->prof.pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess && st == MSA_OK) st = hip_status(e, "msa_profile_read");
+    tot += ms;
+    p->prof.pool.push_back(pr.first);
+    p->prof.pool.push_back(pr.second);
+  }
+  *launches = (int64_t)p->prof.pending.size();
+  *total_ms = tot;
+  p->prof.pending.clear();
+  return st == MSA_OK ? ok() : st;
+}
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
@@ -132,6 +196,7 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     if (!(d.proxy_sm_scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "msa_plan: proxy_sm_scale must be > 0");
   }
   if (d.max_rows_per_call < 0) return fail(MSA_ERR_INVALID_ARG, "msa_plan: max_rows_per_call < 0");
+  if (d.attn_window_rows < 0) return fail(MSA_ERR_INVALID_ARG, "msa_plan: attn_window_rows < 0");
 
   msa_plan_s* p = new (std::nothrow) msa_plan_s();
   if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_plan: out of host memory");
@@ -205,8 +270,14 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
   const int64_t Hkv = d.num_kv_heads, Hq = d.num_qo_heads, K = d.topk;
   if (d.mode == MSA_PREFILL) {
     p->tokens_per_chunk = 128 / G;
-    p->entries_per_item = p->tokens_per_chunk * 4;
-    const int64_t W = p->max_rows;
+    p->entries_per_item = p->tokens_per_chunk * 16;  // 16 chunks of 128 query rows per K/V load
+    // attention window: rows whose partials live at once.  Larger windows
+    // give each (block, group) more rows per K/V load and fewer launches;
+    // by default up to 32768 rows, capped at 16 GiB of partials.
+    const int64_t per_row = Hq * K * (128 * 2 + 4);
+    const int64_t auto_w = std::max<int64_t>(256, std::min<int64_t>(32768, ((int64_t)16 << 30) / per_row));
+    p->attn_window = std::min<int64_t>(T, d.attn_window_rows > 0 ? d.attn_window_rows : auto_w);
+    const int64_t W = p->attn_window;
     const int64_t nkey = Hkv * NB;
     L.counts = off; off = align_up(off + nkey * 4, 256);
     L.cursor = off; off = align_up(off + nkey * 4, 256);
@@ -218,7 +289,11 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     L.part_o = off; off = align_up(off + W * Hq * K * 128 * 2, 256);
     L.part_lse = off; off = align_up(off + W * Hq * K * 4, 256);
   } else {
-    p->dec_splits = std::min(4, (int)K);
+    // one workgroup per (sequence, group) when that fills the GPU; otherwise
+    // split each pair's 32-key slices over up to 8 workgroups
+    const int64_t pairs = (int64_t)p->S * Hkv;
+    p->dec_splits = (int)std::max<int64_t>(1, std::min<int64_t>(8, (512 + pairs - 1) / pairs));
+    if (pairs >= 192) p->dec_splits = 1;
     L.dec_o = off; off = align_up(off + (size_t)p->S * Hq * p->dec_splits * 128 * 4, 256);
     L.dec_ml = off; off = align_up(off + (size_t)p->S * Hq * p->dec_splits * 2 * 4, 256);
   }
@@ -229,6 +304,13 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
 }
 
 msa_status_t msa_plan_destroy(msa_plan_t plan) {
+  if (plan) {
+    for (auto& pr : plan->prof.pending) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+    for (hipEvent_t e : plan->prof.pool) (void)hipEventDestroy(e);
+  }
   delete plan;
   return ok();
 }
@@ -305,8 +387,8 @@ msa_status_t msa_sparse_attn_prefill(msa_plan_t p, const void* q, const void* k_
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
   const msa::DevMeta m = msa::dev_meta(p, workspace);
-  for (int64_t w0 = 0; w0 < p->T; w0 += p->max_rows) {
-    const int32_t w1 = (int32_t)std::min<int64_t>(p->T, w0 + p->max_rows);
+  for (int64_t w0 = 0; w0 < p->T; w0 += p->attn_window) {
+    const int32_t w1 = (int32_t)std::min<int64_t>(p->T, w0 + p->attn_window);
     hipError_t e = msa::launch_prefill_window(p, m, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse,
                                               static_cast<char*>(workspace), (int32_t)w0, w1, hs);
     if (e != hipSuccess) return hip_status(e, __func__);

@@ -22,6 +22,13 @@ struct DevMeta {
   int32_t S, T, NB, nb_max;
 };
 
+// Optional event bracketing of one named internal kernel (msa_profile_kernel).
+struct Profiler {
+  std::string kernel;                                   // empty = off
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  std::vector<hipEvent_t> pool;
+};
+
 struct PlanLayout {
   size_t meta = 0, meta_bytes = 0;
   // prefill window scratch
@@ -38,7 +45,8 @@ struct msa_plan_s {
   msa_plan_desc_t d;                 // copy; host pointers cleared
   std::vector<int32_t> qo, kv, nb, row_start, page_start;
   int32_t S = 0, T = 0, NB = 0, nb_max = 0, G = 0;
-  int64_t max_rows = 0;              // rows per proxy/top-k call and per prefill window
+  int64_t max_rows = 0;              // rows per proxy/top-k call
+  int64_t attn_window = 0;           // rows per prefill attention window
   std::vector<int32_t> tiles;        // proxy row tiles (seq, row0, nrows, pos0)
   int32_t ntiles = 0;
   std::vector<int32_t> meta;         // uploaded blob
@@ -49,11 +57,24 @@ struct msa_plan_s {
   // decode schedule
   int32_t dec_splits = 1;
   const void* uploaded_to = nullptr; // last workspace the metadata was copied into
+  mutable msa::Profiler prof;
 };
 
 namespace msa {
 
 DevMeta dev_meta(const msa_plan_s* p, const void* workspace);
+
+// Brackets one kernel launch with HIP events when the plan profiles `name`.
+class ProfScope {
+ public:
+  ProfScope(const msa_plan_s* p, const char* name, hipStream_t st);
+  ~ProfScope();
+
+ private:
+  const msa_plan_s* p_;
+  hipStream_t st_;
+  hipEvent_t stop_ = nullptr;
+};
 
 // Kernel launchers (defined in the .hip files).  They assume validated inputs.
 hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const void* pq, const void* pk,

@@ -4,21 +4,25 @@
 // its group's selected 128-key blocks.
 //
 // Design (gfx950), HBM-bound (every selected K/V byte is read once):
-//  * grid = (split, KV group, sequence); a workgroup of 4 waves takes the
-//    valid slots of its split one block per round; wave w owns keys
-//    32w .. 32w+31 of every block, so each round reads one whole block
-//    (K + V: 32 KB in fp8) with 16-byte coalesced loads, and the next
-//    round's loads are issued before the current round's math;
+//  * grid = (split, KV group, sequence), 8 waves per workgroup; the valid
+//    selected blocks are listed once per workgroup (one ballot), and each
+//    block is cut into four 32-key slices dealt round-robin to the waves, so
+//    the waves stay balanced (17 blocks = 68 slices over 8 waves) and each
+//    wave streams its slices independently, with the next slice's loads in
+//    flight while the current one is computed (no workgroup barrier in the
+//    loop).  Splits are only used when (sequence, group) pairs are too few to
+//    fill the GPU; a small kernel then merges them by log-sum-exp;
 //  * S^T = K Q^T on bf16 MFMA 16x16x32: the 32 keys are two 16-row tiles
 //    whose rows are interleaved so that each lane ends up holding 8
 //    consecutive keys of one head - exactly the B operand layout of the
 //    following O^T = V^T P^T product;
 //  * fp8 codes are widened to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8);
 //    the per-head fp32 scales multiply the logits and the output;
-//  * V reaches the A operand through LDS with transposing reads
-//    (ds_read_b64_tr_b8 for fp8, ds_read_b64_tr_b16 for bf16);
-//  * online softmax per wave; the 4 waves merge through LDS; with several
-//    splits a small kernel merges the splits by log-sum-exp.
+//  * V reaches the A operand through a wave-private, double-buffered LDS
+//    tile with transposing reads (ds_read_b64_tr_b8 for fp8,
+//    ds_read_b64_tr_b16 for bf16); LDS operations of one wave execute in
+//    order, so the wave needs no barrier between its write and its reads;
+//  * online softmax per wave; the 8 waves merge through LDS at the end.
 #include "device_common.hpp"
 #include "msa_internal.hpp"
 
@@ -49,7 +53,7 @@ struct DecTraits<true> {
   static constexpr int kRow = 128;      // bytes per key row
   static constexpr int kVRow = 144;     // LDS bytes per V row
   static constexpr int kKLoads = 2;     // 16-byte loads per lane per K tile
-  static constexpr int kVLoads = 4;     // 16-byte loads per lane for the wave's V rows
+  static constexpr int kVLoads = 4;     // 16-byte loads per lane for the slice's V rows
 };
 template <>
 struct DecTraits<false> {
@@ -59,12 +63,23 @@ struct DecTraits<false> {
   static constexpr int kVLoads = 8;
 };
 
+constexpr int kDecWaves = 8;
+
 template <bool FP8>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+struct SliceRegs {
+  i32x4 k[2 * DecTraits<FP8>::kKLoads];
+  i32x4 v[DecTraits<FP8>::kVLoads];
+};
+
+template <bool FP8>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   using Tr = DecTraits<FP8>;
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[4][32 * Tr::kVRow];
-  __shared__ float red_m[4][16], red_l[4][16];
-  __shared__ float red_o[4][16][129];
+  constexpr int kVTile = 32 * Tr::kVRow;
+  constexpr int kRedBytes = kDecWaves * 16 * (129 + 2) * 4;
+  constexpr int kVBytes = kDecWaves * 2 * kVTile;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kVBytes > kRedBytes ? kVBytes : kRedBytes];
+  __shared__ int32_t blist[64];
+  __shared__ int32_t s_nvalid;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q16 = lane >> 4, m16 = lane & 15;
@@ -76,11 +91,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int32_t* selrow = a.sel + ((int64_t)seq * a.Hkv + g) * a.k;
   const int32_t* pages = a.kv_indices + a.m.page_start[seq];
 
-  // this split's share of the valid slots
-  int nvalid = 0;
-  for (int j = 0; j < a.k; ++j) nvalid += (selrow[j] >= 0 && selrow[j] <= local) ? 1 : 0;
-  const int per = (nvalid + a.nsplit - 1) / a.nsplit;
-  const int v_lo = split * per, v_hi = min(nvalid, v_lo + per);
+  // valid selected blocks, in slot order (k <= 64: one wave)
+  if (wave == 0) {
+    const int b = lane < a.k ? selrow[lane] : -1;
+    const bool ok = b >= 0 && b <= local;
+    const uint64_t mask = __ballot(ok);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (ok) blist[before] = b;
+    if (lane == 0) s_nvalid = __popcll(mask);
+  }
+  __syncthreads();
+  const int nslices = 4 * s_nvalid;
+  const int per = (nslices + a.nsplit - 1) / a.nsplit;
+  const int s_lo = split * per, s_hi = min(nslices, s_lo + per);
 
   // Q (B operand of S^T): lane -> head m16, d-run 32*q16 .. +32, 8 per k-step
   bf16x8 qf[4];
@@ -97,24 +120,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const float vscale = FP8 ? a.vs[g] : 1.f;
   const float c = a.scale_log2 * kscale;
 
-  // global loads of one block's K rows (this lane's two interleaved key rows)
-  // and V rows (2 lanes per key row) of this wave's 32 keys
-  i32x4 kreg[2][2 * Tr::kKLoads], vreg[2][Tr::kVLoads];
-  auto issue = [&](int buf, int b) {
+  // global loads of one 32-key slice: this lane's two interleaved K rows and
+  // half a V row (two lanes per V row)
+  auto issue = [&](SliceRegs<FP8>& R, int sl) {
+    const int b = blist[sl >> 2];
+    const int key0 = 32 * (sl & 3);
     const int32_t page = pages[b];
-    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * (128 * Tr::kRow) + (int64_t)(32 * wave) * Tr::kRow;
-    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * (128 * Tr::kRow) + (int64_t)(32 * wave) * Tr::kRow;
+    const int64_t blk = ((int64_t)page * a.Hkv + g) * (128 * Tr::kRow);
+    const uint8_t* kb = a.kp + blk + (int64_t)key0 * Tr::kRow;
+    const uint8_t* vb = a.vp + blk + (int64_t)key0 * Tr::kRow;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      // tile j row i=m16 holds key 8*(i/4) + 4*j + i%4 of the wave's 32
+      // tile j row i=m16 holds key 8*(i/4) + 4*j + i%4 of the slice
       const int key = 8 * (m16 >> 2) + 4 * j + (m16 & 3);
       const uint8_t* src = kb + key * Tr::kRow + q16 * (Tr::kRow / 4);
 #pragma unroll
-      for (int x = 0; x < Tr::kKLoads; ++x) kreg[buf][j * Tr::kKLoads + x] = *reinterpret_cast<const i32x4*>(src + 16 * x);
+      for (int x = 0; x < Tr::kKLoads; ++x) R.k[j * Tr::kKLoads + x] = *reinterpret_cast<const i32x4*>(src + 16 * x);
     }
     const uint8_t* vsrc = vb + (lane >> 1) * Tr::kRow + (lane & 1) * (Tr::kRow / 2);
 #pragma unroll
-    for (int x = 0; x < Tr::kVLoads; ++x) vreg[buf][x] = *reinterpret_cast<const i32x4*>(vsrc + 16 * x);
+    for (int x = 0; x < Tr::kVLoads; ++x) R.v[x] = *reinterpret_cast<const i32x4*>(vsrc + 16 * x);
   };
 
   float m_run = kNegInf, l_run = 0.f;
@@ -122,37 +147,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{};
 
-  // slot index of the v-th valid entry
-  auto nth_valid = [&](int v) {
-    int seen = 0;
-    for (int j = 0; j < a.k; ++j) {
-      const int b = selrow[j];
-      if (b >= 0 && b <= local) {
-        if (seen == v) return b;
-        ++seen;
-      }
-    }
-    return local;
-  };
-
-  int cur = 0;
-  if (v_lo < v_hi) issue(0, nth_valid(v_lo));
-  for (int v = v_lo; v < v_hi; ++v) {
-    const int b = nth_valid(v);
-    // V of this round -> this wave's LDS tile
-    uint8_t* vt = vlds[wave];
-    // rows past kv_len are page padding (may hold NaN; P = 0 there but 0 * NaN is NaN)
-    const bool vrow_ok = b * 128 + 32 * wave + (lane >> 1) < kv_len;
+  auto compute = [&](const SliceRegs<FP8>& R, int sl, uint8_t* vt) {
+    const int b = blist[sl >> 2];
+    const int key0 = 32 * (sl & 3);
+    // V slice -> LDS; rows past kv_len are page padding (may hold NaN, and
+    // P = 0 there but 0 * NaN is NaN)
+    const bool vrow_ok = b * 128 + key0 + (lane >> 1) < kv_len;
 #pragma unroll
     for (int x = 0; x < Tr::kVLoads; ++x)
       lds_store16<i32x4>(vt + (lane >> 1) * Tr::kVRow + (lane & 1) * (Tr::kRow / 2) + 16 * x,
-                         vrow_ok ? vreg[cur][x] : i32x4{});
-    i32x4 kcur[2 * Tr::kKLoads];
-#pragma unroll
-    for (int x = 0; x < 2 * Tr::kKLoads; ++x) kcur[x] = kreg[cur][x];
-    if (v + 1 < v_hi) issue(cur ^ 1, nth_valid(v + 1));
-    __syncthreads();
-
+                         vrow_ok ? R.v[x] : i32x4{});
     // S^T tiles
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
@@ -161,24 +165,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       for (int st = 0; st < 4; ++st) {
         bf16x8 af;
         if constexpr (FP8) {
-          const i32x4 w = kcur[j * Tr::kKLoads + st / 2];
+          const i32x4 w = R.k[j * Tr::kKLoads + st / 2];
           af = fp8x8_to_bf16x8((uint32_t)w[(st & 1) * 2], (uint32_t)w[(st & 1) * 2 + 1]);
         } else {
-          af = __builtin_bit_cast(bf16x8, kcur[j * Tr::kKLoads + st]);
+          af = __builtin_bit_cast(bf16x8, R.k[j * Tr::kKLoads + st]);
         }
         sacc[j] = mfma16x16x32(af, qf[st], sacc[j]);
       }
     }
-    // lane holds keys 32*wave + 8*q16 + t, t = 4j + e; mask keys past the position
-    const int lim = pos - (b * 128 + 32 * wave + 8 * q16);
+    // lane holds keys key0 + 8*q16 + t, t = 4j + e; mask keys past the position
+    const int lim = pos - (b * 128 + key0 + 8 * q16);
     float cm = kNegInf;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float s = (4 * j + e) <= lim ? sacc[j][e] : kNegInf;
-        sacc[j][e] = s;
-        cm = fmaxf(cm, s);
+        const float sv = (4 * j + e) <= lim ? sacc[j][e] : kNegInf;
+        sacc[j][e] = sv;
+        cm = fmaxf(cm, sv);
       }
     }
     cm = fmaxf(cm, __shfl_xor(cm, 16));
@@ -188,17 +192,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // reference then so that no (-inf) - (-inf) appears
     const float m_ref = m_new == kNegInf ? 0.f : m_new;
     const float alpha = fast_exp2((m_run - m_ref) * c);
-    bf16x8 pf;
     float psum = 0.f;
+    float pv[8];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pv = fast_exp2((sacc[j][e] - m_ref) * c);
-        psum += pv;
-        pf[4 * j + e] = (__bf16)pv;
+        pv[4 * j + e] = fast_exp2((sacc[j][e] - m_ref) * c);
+        psum += pv[4 * j + e];
       }
     }
+    i32x4 pw;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x2 two = {(__bf16)pv[2 * t], (__bf16)pv[2 * t + 1]};
+      pw[t] = __builtin_bit_cast(int, two);
+    }
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
@@ -216,51 +226,72 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       oacc[dt] = mfma16x16x32(vf, pf, oacc[dt]);
     }
-    cur ^= 1;
-    __syncthreads();
+  };
+
+  // this wave's slices: s_lo + wave, + 8, ...; two register buffers, two LDS tiles
+  uint8_t* vt0 = smem + (2 * wave) * kVTile;
+  uint8_t* vt1 = vt0 + kVTile;
+  SliceRegs<FP8> r0, r1;
+  int sl = s_lo + wave;
+  if (sl < s_hi) issue(r0, sl);
+  while (sl < s_hi) {
+    const int sl1 = sl + kDecWaves;
+    if (sl1 < s_hi) issue(r1, sl1);
+    compute(r0, sl, vt0);
+    if (sl1 >= s_hi) break;
+    const int sl2 = sl1 + kDecWaves;
+    if (sl2 < s_hi) issue(r0, sl2);
+    compute(r1, sl1, vt1);
+    sl = sl2;
   }
 
-  // wave -> LDS: running max, lane-group sums, O^T (lane holds d = 16dt + 4q16 + e of head m16)
+  // waves -> LDS: running max, lane-group sums, O^T (lane holds d = 16dt + 4q16 + e of head m16)
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  __syncthreads();  // every wave is done with its V tiles; reuse smem
+  float* red = reinterpret_cast<float*>(smem);  // [wave][head][131]: o[128], m, l
+  float* mine = red + (wave * 16 + m16) * 131;
   if (q16 == 0) {
-    red_m[wave][m16] = m_run;
-    red_l[wave][m16] = l_run;
+    mine[128] = m_run;
+    mine[129] = l_run;
   }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red_o[wave][m16][16 * dt + 4 * q16 + e] = oacc[dt][e];
+    for (int e = 0; e < 4; ++e) mine[16 * dt + 4 * q16 + e] = oacc[dt][e];
   __syncthreads();
 
-  // combine the 4 waves: thread -> (head, 8 consecutive d)
-  const int hh = tid >> 4;          // 16 heads
-  const int d0 = (tid & 15) * 8;    // 16 x 8 = 128
+  // combine the waves: thread -> (head, 4 consecutive d) for 16 heads x 128 d
+  const int hh = tid >> 5;          // 16 heads
+  const int d0 = (tid & 31) * 4;    // 32 x 4 = 128
   if (hh < G) {
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
-    float wsum = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red[(w * 16 + hh) * 131 + 128]);
+    float wsum = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = red_m[w][hh] == kNegInf ? 0.f : fast_exp2((red_m[w][hh] - M) * c);
-      wsum += f * red_l[w][hh];
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float* rw = red + (w * 16 + hh) * 131;
+      const float f = rw[128] == kNegInf ? 0.f : fast_exp2((rw[128] - M) * c);
+      wsum += f * rw[129];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) o[x] += f * red_o[w][hh][d0 + x];
+      for (int x = 0; x < 4; ++x) o[x] += f * rw[d0 + x];
     }
     const int h = g * G + hh;
     const float lse_v = (wsum > 0.f) ? (M * c + fast_log2(wsum)) * kLn2 : kNegInf;
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     if (a.nsplit == 1) {
-      bf16x8 ob;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(o[x] * inv * vscale);
-      *reinterpret_cast<bf16x8*>(a.out + ((int64_t)seq * a.Hq + h) * 128 + d0) = ob;
+      bf16x4 ob;
+      const bf16x2 lo2 = {(__bf16)(o[0] * inv * vscale), (__bf16)(o[1] * inv * vscale)};
+      const bf16x2 hi2 = {(__bf16)(o[2] * inv * vscale), (__bf16)(o[3] * inv * vscale)};
+      const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+      ob = __builtin_bit_cast(bf16x4, pk);
+      *reinterpret_cast<bf16x4*>(a.out + ((int64_t)seq * a.Hq + h) * 128 + d0) = ob;
       if (a.lse && d0 == 0) a.lse[(int64_t)seq * a.Hq + h] = lse_v;
     } else {
       float* po = a.part_o + (((int64_t)seq * a.Hq + h) * a.nsplit + split) * 128 + d0;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) po[x] = o[x] * inv * vscale;
+      for (int x = 0; x < 4; ++x) po[x] = o[x] * inv * vscale;
       if (d0 == 0) a.part_ml[(((int64_t)seq * a.Hq + h) * a.nsplit + split) * 2] = lse_v;
     }
   }
@@ -315,11 +346,12 @@ hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, c
   a.k = p->d.topk;
   a.nsplit = p->dec_splits;
   a.scale_log2 = p->d.sm_scale * kLog2e;
-  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)p->S), block(256);
-  if (p->d.kv_dtype == MSA_FP8_E4M3) hipLaunchKernelGGL(decode_kernel<true>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(decode_kernel<false>, grid, block, 0, st, a);
+  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)p->S), block(64 * kDecWaves);
+  if (p->d.kv_dtype == MSA_FP8_E4M3) { ProfScope ps_(p, "decode", st); hipLaunchKernelGGL(decode_kernel<true>, grid, block, 0, st, a); }
+  else { ProfScope ps_(p, "decode", st); hipLaunchKernelGGL(decode_kernel<false>, grid, block, 0, st, a); }
   if (a.nsplit > 1) {
     const int64_t nw = (int64_t)p->S * a.Hq;
+    ProfScope ps_(p, "decode_merge", st);
     hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, a.part_o, a.part_ml,
                        a.out, lse, p->S, a.Hq, a.nsplit);
   }

@@ -43,30 +43,61 @@ struct CsrArgs {
   int32_t w0, w1, Hkv, k;
 };
 
-// One thread per (row, group): visit the row's valid slots (0 <= b <= local).
-template <bool FILL>
+// One thread per row of one group (grid.y = group); a row's valid slots are
+// those with 0 <= b <= local.  With LDS_HIST the workgroup first histograms
+// its 256 rows' blocks in LDS, so global memory sees one atomic per touched
+// (group, block) bin per workgroup instead of one per entry.
+constexpr int kMaxLdsBins = 16384;
+
+template <bool FILL, bool LDS_HIST>
 __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nrows = a.w1 - a.w0;
-  if (idx >= nrows * a.Hkv) return;
-  const int32_t rl = (int32_t)(idx / a.Hkv);
-  const int g = (int)(idx % a.Hkv);
-  const int32_t r = a.w0 + rl;
+  extern __shared__ int32_t hist[];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.y;
+  const int32_t nrows = a.w1 - a.w0;
+  const int32_t rl = (int32_t)blockIdx.x * 256 + tid;
+  const bool valid = rl < nrows;
+  const int32_t r = a.w0 + (valid ? rl : 0);
   const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
   const int32_t pos = a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s]);
   const int local = pos >> 7;
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   const int32_t pb = a.m.page_start[s];
-  for (int slot = 0; slot < a.k; ++slot) {
-    const int b = row[slot];
-    if (b < 0 || b > local) continue;
-    const int key = g * a.m.NB + pb + b;
-    if (!FILL) {
-      atomicAdd(&a.counts[key], 1);
-    } else {
-      const int at = atomicAdd(&a.cursor[key], 1);
-      a.entries[a.offsets[key] + at] = rl * a.k + slot;
+  const int NB = a.m.NB;
+  int32_t* counts = a.counts + (int64_t)g * NB;
+  int32_t* cursor = a.cursor + (int64_t)g * NB;
+  const int32_t* offsets = a.offsets + (int64_t)g * NB;
+  if constexpr (!LDS_HIST) {
+    if (!valid) return;
+    for (int slot = 0; slot < a.k; ++slot) {
+      const int b = row[slot];
+      if (b < 0 || b > local) continue;
+      if (!FILL) atomicAdd(&counts[pb + b], 1);
+      else a.entries[offsets[pb + b] + atomicAdd(&cursor[pb + b], 1)] = rl * a.k + slot;
     }
+    return;
+  } else {
+    for (int i = tid; i < NB; i += 256) hist[i] = 0;
+    __syncthreads();
+    if (valid)
+      for (int slot = 0; slot < a.k; ++slot) {
+        const int b = row[slot];
+        if (b >= 0 && b <= local) atomicAdd(&hist[pb + b], 1);
+      }
+    __syncthreads();
+    for (int i = tid; i < NB; i += 256) {
+      const int c = hist[i];
+      if (c == 0) continue;
+      if (!FILL) atomicAdd(&counts[i], c);
+      else hist[i] = offsets[i] + atomicAdd(&cursor[i], c);  // this workgroup's range in bin i
+    }
+    if (!FILL) return;
+    __syncthreads();
+    if (valid)
+      for (int slot = 0; slot < a.k; ++slot) {
+        const int b = row[slot];
+        if (b >= 0 && b <= local) a.entries[atomicAdd(&hist[pb + b], 1)] = rl * a.k + slot;
+      }
   }
 }
 
@@ -122,9 +153,12 @@ struct PartialArgs {
   float scale_log2;      // sm_scale * log2(e)
 };
 
+constexpr int kMaxItemEntries = 2048;  // entries_per_item = 16 chunks of 128 / G tokens
+
 __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * kKRow];
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * kVRow];
+  __shared__ int32_t ent_s[kMaxItemEntries];
   const int item = blockIdx.x;
   if (item >= *a.nitems) return;
   const int4 it = a.items[item];
@@ -135,8 +169,9 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   const int32_t page = a.kv_indices[gb];
   const int32_t first_pos = a.m.kv[s] - a.m.qo[s];
   const int32_t rs = a.m.row_start[s];
+  const int n_ent = e1 - e0;
 
-  {  // K and V block -> LDS (coalesced 16-byte chunks)
+  {  // K and V block -> LDS (coalesced 16-byte chunks); this item's entries -> LDS
     const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * 32768;
     const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * 32768;
     i32x4 kr[8], vr[8];
@@ -146,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       kr[i] = *reinterpret_cast<const i32x4*>(kb + c * 16);
       vr[i] = *reinterpret_cast<const i32x4*>(vb + c * 16);
     }
+    for (int i = tid; i < n_ent; i += 256) ent_s[i] = a.entries[e0 + i];
     const int kv_in_block = a.m.kv[s] - b * 128;  // V rows at or past this are page padding
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -159,22 +195,33 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
 
   const int G = a.G;
   const int MT = 128 / G;                      // tokens per 128-row chunk
-  const int qr = 32 * wave + (lane & 31);      // this lane's query row within the chunk
+  const int qr = 32 * wave + (lane & 31);      // this lane's query row within a chunk
   const int half = lane >> 5;
   const int q16 = lane >> 4, m16 = lane & 15;
-  for (int c0 = e0; c0 < e1; c0 += MT) {
-    const int e = c0 + qr / G;
-    const bool valid = e < e1;
-    const int ent = a.entries[valid ? e : e0];
-    const int rl = ent / a.k, slot = ent % a.k;
-    const int32_t r = a.w0 + rl;
-    const int h = g * G + qr % G;
-    const int32_t pos = first_pos + (r - rs);
+  const int hh = qr % G, tok = qr / G;
+  const int h = g * G + hh;
+  const int nchunks = (n_ent + MT - 1) / MT;
 
-    bf16x8 qf[8];
-    const uint8_t* qrow = a.q + ((int64_t)r * a.Hq + h) * 256;
+  // Q fragments (B operand) of a chunk's row for this lane: gathered rows
+  auto load_q = [&](bf16x8 (&qf)[8], int chunk) {
+    const int e = min(chunk * MT + tok, n_ent - 1);
+    const int32_t r = a.w0 + ent_s[e] / a.k;
+    const uint8_t* qrow = a.q + ((int64_t)r * a.Hq + h) * 256 + half * 16;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 32 + half * 16);
+    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
+  };
+
+  bf16x8 qn[8];
+  load_q(qn, 0);
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    bf16x8 qf[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qf[st] = qn[st];
+    const int e = chunk * MT + tok;
+    const bool valid = e < n_ent;
+    const int ent = ent_s[valid ? e : 0];
+    const int rl = ent / a.k, slot = ent % a.k;
+    const int32_t pos = first_pos + (a.w0 + rl - rs);
 
     // S^T = K Q^T: 4 key tiles of 32
     f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
@@ -185,7 +232,11 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
         const bf16x8 af = lds_load16<bf16x8>(&ks[(32 * kt + (lane & 31)) * kKRow + st * 32 + half * 16]);
         acc[kt] = mfma32x32x16(af, qf[st], acc[kt]);
       }
+      if (st & 1) __builtin_amdgcn_sched_barrier(0);
     }
+    // the next chunk's gathered Q rows are in flight during softmax and P.V
+    if (chunk + 1 < nchunks) load_q(qn, chunk + 1);
+
     // causal mask (keys past the row's position), row max
     const int lim = pos - b * 128 - 4 * half;
     float mx = kNegInf;
@@ -201,13 +252,21 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     }
     mx = fmaxf(mx, wave_xor32(mx));
     float sum = 0.f;
+    bf16x8 pf[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2((acc[kt][i] - mx) * a.scale_log2);
-        acc[kt][i] = pv;
-        sum += pv;
+      for (int u = 0; u < 2; ++u) {
+        i32x4 pw;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float p0 = fast_exp2((acc[kt][8 * u + 2 * t] - mx) * a.scale_log2);
+          const float p1 = fast_exp2((acc[kt][8 * u + 2 * t + 1] - mx) * a.scale_log2);
+          sum += p0 + p1;
+          const bf16x2 two = {(__bf16)p0, (__bf16)p1};
+          pw[t] = __builtin_bit_cast(int, two);
+        }
+        pf[kt][u] = __builtin_bit_cast(bf16x8, pw);
       }
     }
     sum += wave_xor32(sum);
@@ -218,19 +277,16 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        bf16x8 pf;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pf[t] = (__bf16)acc[kt][8 * u + t];
         const int key0 = 32 * kt + 16 * u + 4 * (q16 >> 1);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int d0 = 32 * dt + 16 * (q16 & 1);
           const s16x4 lo = lds_read_tr16(&vs[(key0 + (m16 >> 2)) * kVRow + (d0 + 4 * (m16 & 3)) * 2]);
           const s16x4 hi = lds_read_tr16(&vs[(key0 + 8 + (m16 >> 2)) * kVRow + (d0 + 4 * (m16 & 3)) * 2]);
-          const bf16x8 vf = join_tr16(lo, hi);
-          oacc[dt] = mfma32x32x16(vf, pf, oacc[dt]);
+          oacc[dt] = mfma32x32x16(join_tr16(lo, hi), pf[kt][u], oacc[dt]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of transposed reads
     }
     if (valid) {
       const float inv = 1.f / sum;
@@ -240,10 +296,10 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          bf16x4 o;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) o[t] = (__bf16)(oacc[dt][4 * gq + t] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * gq + 4 * half) = o;
+          const bf16x2 lo2 = {(__bf16)(oacc[dt][4 * gq] * inv), (__bf16)(oacc[dt][4 * gq + 1] * inv)};
+          const bf16x2 hi2 = {(__bf16)(oacc[dt][4 * gq + 2] * inv), (__bf16)(oacc[dt][4 * gq + 3] * inv)};
+          const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+          *reinterpret_cast<i32x2*>(orow + 32 * dt + 8 * gq + 4 * half) = pk;
         }
       }
       if (half == 0) a.part_lse[pi] = (mx * a.scale_log2 + fast_log2(sum)) * kLn2;
@@ -261,40 +317,71 @@ struct MergeArgs {
   int32_t Hq, Hkv, G, k, w0, w1;
 };
 
-// One wave per (row, head); lane l owns output columns 2l, 2l+1.
+// 16 lanes per (row, head), 8 output columns per lane.  Lane j of the 16
+// reads slot j's block id and log-sum-exp (coalesced), the group's max and
+// weights move by shuffles, and every partial row is read as 16-byte loads
+// (one 256-byte segment per 16 lanes), 16 slots at a time.  topk <= 64.
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (idx >= (int64_t)(a.w1 - a.w0) * a.Hq) return;
-  const int32_t rl = (int32_t)(idx / a.Hq);
-  const int h = (int)(idx % a.Hq);
+  const int sub = threadIdx.x & 15;
+  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = idx < (int64_t)(a.w1 - a.w0) * a.Hq;   // shuffles need every lane
+  const int64_t id = live ? idx : 0;
+  const int32_t rl = (int32_t)(id / a.Hq);
+  const int h = (int)(id % a.Hq);
   const int g = h / a.G;
   const int32_t r = a.w0 + rl;
   const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
   const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
+  const int ngroups = (a.k + 15) >> 4;
+  float lse_g[4];
   float M = kNegInf;
-  for (int slot = 0; slot < a.k; ++slot) {
-    const int b = row[slot];
-    if (b >= 0 && b <= local) M = fmaxf(M, a.part_lse[base + slot]);
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const int slot = 16 * gi + sub;
+    float l = kNegInf;
+    if (gi < ngroups && slot < a.k) {
+      const int b = row[slot];
+      if (b >= 0 && b <= local) l = a.part_lse[base + slot];
+    }
+    lse_g[gi] = l;
+    M = fmaxf(M, l);
   }
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int slot = 0; slot < a.k; ++slot) {
-    const int b = row[slot];
-    if (b < 0 || b > local) continue;
-    const float w = fast_exp2((a.part_lse[base + slot] - M) * kLog2e);
-    const uint32_t two = *reinterpret_cast<const uint32_t*>(a.part_o + (base + slot) * 128 + 2 * lane);
-    L += w;
-    o0 += w * __builtin_bit_cast(float, two << 16);
-    o1 += w * __builtin_bit_cast(float, two & 0xffff0000u);
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+  float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int gi = 0; gi < ngroups; ++gi) {
+    const float wl = lse_g[gi] == kNegInf ? 0.f : fast_exp2((lse_g[gi] - M) * kLog2e);
+    i32x4 v[16];
+    float w[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      w[j] = __shfl(wl, j, 16);
+      const int slot = min(16 * gi + j, a.k - 1);
+      v[j] = *reinterpret_cast<const i32x4*>(a.part_o + (base + slot) * 128 + 8 * sub);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (w[j] == 0.f) continue;  // invalid slots: never written, never read into the result
+      L += w[j];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        o[2 * x] += w[j] * __builtin_bit_cast(float, (uint32_t)v[j][x] << 16);
+        o[2 * x + 1] += w[j] * __builtin_bit_cast(float, (uint32_t)v[j][x] & 0xffff0000u);
+      }
+    }
   }
+  if (!live) return;
   const float inv = 1.f / L;
-  bf16x2 o;
-  o[0] = (__bf16)(o0 * inv);
-  o[1] = (__bf16)(o1 * inv);
-  *reinterpret_cast<bf16x2*>(a.out + ((int64_t)r * a.Hq + h) * 128 + 2 * lane) = o;
-  if (a.lse && lane == 0) a.lse[(int64_t)r * a.Hq + h] = M + fast_log2(L) * kLn2;
+  i32x4 packed;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x2 t = {(__bf16)(o[2 * j] * inv), (__bf16)(o[2 * j + 1] * inv)};
+    packed[j] = __builtin_bit_cast(int, t);
+  }
+  *reinterpret_cast<i32x4*>(a.out + ((int64_t)r * a.Hq + h) * 128 + 8 * sub) = packed;
+  if (a.lse && sub == 0) a.lse[(int64_t)r * a.Hq + h] = M + fast_log2(L) * kLn2;
 }
 
 }  // namespace
@@ -313,6 +400,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   int32_t* entries = reinterpret_cast<int32_t*>(ws + L.entries);
   // counts and cursor are adjacent 256-aligned segments: clear both
   const int64_t nclear = (int64_t)(L.offsets - L.counts) / 4;
+  {
+  ProfScope ps_(p, "csr", st);
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(1024, (nclear + 255) / 256)), dim3(256), 0, st,
                      counts, nclear, 0);
   CsrArgs c;
@@ -326,12 +415,16 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   c.w1 = w1;
   c.Hkv = Hkv;
   c.k = k;
-  const int64_t nthreads = (int64_t)(w1 - w0) * Hkv;
-  const dim3 cgrid((unsigned)((nthreads + 255) / 256));
-  hipLaunchKernelGGL(csr_pass_kernel<false>, cgrid, dim3(256), 0, st, c);
+  const dim3 cgrid((unsigned)((w1 - w0 + 255) / 256), (unsigned)Hkv);
+  const bool lds_hist = p->NB <= kMaxLdsBins;
+  const size_t hist_bytes = lds_hist ? (size_t)p->NB * 4 : 0;
+  if (lds_hist) hipLaunchKernelGGL((csr_pass_kernel<false, true>), cgrid, dim3(256), hist_bytes, st, c);
+  else hipLaunchKernelGGL((csr_pass_kernel<false, false>), cgrid, dim3(256), 0, st, c);
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, counts, offsets, items, nitems, nkey,
                      p->NB, p->entries_per_item);
-  hipLaunchKernelGGL(csr_pass_kernel<true>, cgrid, dim3(256), 0, st, c);
+  if (lds_hist) hipLaunchKernelGGL((csr_pass_kernel<true, true>), cgrid, dim3(256), hist_bytes, st, c);
+  else hipLaunchKernelGGL((csr_pass_kernel<true, false>), cgrid, dim3(256), 0, st, c);
+  }
 
   PartialArgs a;
   a.q = static_cast<const uint8_t*>(q);
@@ -352,7 +445,10 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   a.scale_log2 = p->d.sm_scale * kLog2e;
   // upper bound on the number of work items of this window
   const int64_t max_items = ((int64_t)(w1 - w0) * Hkv * k + p->entries_per_item - 1) / p->entries_per_item + nkey;
-  hipLaunchKernelGGL(partial_attn_kernel, dim3((unsigned)max_items), dim3(256), 0, st, a);
+  {
+    ProfScope ps_(p, "partial_attn", st);
+    hipLaunchKernelGGL(partial_attn_kernel, dim3((unsigned)max_items), dim3(256), 0, st, a);
+  }
 
   MergeArgs mg;
   mg.sel = sel;
@@ -367,8 +463,11 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   mg.k = k;
   mg.w0 = w0;
   mg.w1 = w1;
-  const int64_t nwaves = (int64_t)(w1 - w0) * Hq;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((nwaves + 3) / 4)), dim3(256), 0, st, mg);
+  const int64_t npairs = (int64_t)(w1 - w0) * Hq;
+  {
+    ProfScope ps_(p, "merge", st);
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, mg);
+  }
   return hipGetLastError();
 }
 

@@ -12,23 +12,25 @@
 //  * max_score is [P][nb_max][rows] (rows fastest), so at every block index
 //    the 64 lanes of a wave read 64 consecutive floats: every load is one
 //    coalesced 256-byte line;
-//  * pass 1 folds the row into NG group maxima (block b -> group b % NG,
-//    NG >= topk-1).  Their minimum tau is a lower bound of the (topk-1)-th
-//    largest score, because the NG maxima are distinct blocks;
-//  * pass 2 compacts the ids of blocks scoring >= tau (typically 30-60) into
-//    a per-thread LDS list, in ascending block order;
+//  * pass 1 folds the row into NG = 2*KS group maxima (block b -> group
+//    b % NG).  The group maxima are distinct blocks, so their R-th largest
+//    (R = topk-1 competing slots) is a lower bound tau of the row's R-th
+//    largest score; found by a register insertion sort of the NG maxima;
+//  * pass 2 compacts (score, id) of the blocks scoring >= tau (about 19 on
+//    average for random scores, rarely above 34) into a per-thread LDS list,
+//    in ascending block order;
 //  * pass 3 runs a register insertion sort of those scores to find the exact
-//    (topk-1)-th value tau* and how many scores equal to it are taken, and
-//    pass 4 emits the chosen ids in ascending order (ties: lowest ids first).
-//    If the list overflows (heavy ties), passes 3-4 stream the row instead.
+//    R-th value tau* and how many scores equal to it are taken, and pass 4
+//    emits the chosen ids in ascending order (ties: lowest ids first).  If
+//    the list overflows (heavy exact ties), passes 3-4 stream the row.
 #include "device_common.hpp"
 #include "msa_internal.hpp"
 
 namespace msa {
 namespace {
 
-constexpr int kTopkThreads = 256;
-constexpr int kCap = 96;  // per-thread candidate list length
+constexpr int kTopkThreads = 128;
+constexpr int kCap = 48;  // per-thread candidate list length
 
 struct TopkArgs {
   const float* ms;          // [P, nb_max, row_count]
@@ -38,9 +40,30 @@ struct TopkArgs {
   int32_t P, k;
 };
 
-template <int NG>
+// Insert v into the descending list top[0..KS).
+template <int KS>
+__device__ __forceinline__ void insert_desc(float (&top)[KS], float v) {
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const float hi = fmaxf(top[j], v);
+    v = fminf(top[j], v);
+    top[j] = hi;
+  }
+}
+
+template <int KS>
+__device__ __forceinline__ float pick(const float (&top)[KS], int i) {
+  float r = top[0];
+#pragma unroll
+  for (int j = 1; j < KS; ++j) r = (j == i) ? top[j] : r;
+  return r;
+}
+
+template <int KS>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ uint16_t cand[kCap][kTopkThreads];
+  constexpr int NG = 2 * KS;
+  __shared__ float cval[kCap][kTopkThreads];
+  __shared__ uint16_t cid[kCap][kTopkThreads];
   const int tid = threadIdx.x;
   const int p = blockIdx.y;
   const int64_t i = (int64_t)blockIdx.x * kTopkThreads + tid;
@@ -60,63 +83,70 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     return;
   }
 
-  // pass 1: group maxima
+  // pass 1: group maxima, then tau = R-th largest of them
   float gm[NG];
 #pragma unroll
   for (int j = 0; j < NG; ++j) gm[j] = kNegInf;
+  // loads use clamped addresses (always in bounds, issued back to back);
+  // entries past the competing range are masked to -inf, never duplicated,
+  // so that the group maxima stay maxima of disjoint sets
   for (int b0 = 0; b0 < local; b0 += NG) {
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const int b = b0 + j;
-      if (b < local) gm[j] = fmaxf(gm[j], col[(int64_t)b * stride]);
+      const float v = col[(int64_t)min(b, local - 1) * stride];
+      gm[j] = fmaxf(gm[j], b < local ? v : kNegInf);
     }
   }
-  float tau = gm[0];
+  float top[KS];
 #pragma unroll
-  for (int j = 1; j < NG; ++j) tau = fminf(tau, gm[j]);
+  for (int j = 0; j < KS; ++j) top[j] = kNegInf;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) insert_desc<KS>(top, gm[j]);
+  const float tau = pick<KS>(top, R - 1);
 
-  // pass 2: compact candidate ids
+  // pass 2: compact candidates (score, id)
   int cnt = 0;
-  for (int b = 0; b < local; ++b) {
-    const float v = col[(int64_t)b * stride];
-    if (v >= tau) {
-      if (cnt < kCap) cand[cnt][tid] = (uint16_t)b;
-      ++cnt;
+  for (int b0 = 0; b0 < local; b0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = col[(int64_t)min(b0 + j, local - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (b0 + j < local && v[j] >= tau) {
+        if (cnt < kCap) {
+          cval[cnt][tid] = v[j];
+          cid[cnt][tid] = (uint16_t)(b0 + j);
+        }
+        ++cnt;
+      }
     }
   }
   const bool listed = cnt <= kCap;
-  const int n = listed ? cnt : local;
 
-  // pass 3: insertion sort of the candidate scores (descending, NG slots)
-  float top[NG];
+  // pass 3: exact R-th value among the candidates
 #pragma unroll
-  for (int j = 0; j < NG; ++j) top[j] = kNegInf;
-  for (int c = 0; c < n; ++c) {
-    const int b = listed ? (int)cand[c][tid] : c;
-    float v = col[(int64_t)b * stride];
-    if (!listed && v < tau) continue;
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      const float hi = fmaxf(top[j], v);
-      v = fminf(top[j], v);
-      top[j] = hi;
+  for (int j = 0; j < KS; ++j) top[j] = kNegInf;
+  if (listed) {
+    for (int c = 0; c < cnt; ++c) insert_desc<KS>(top, cval[c][tid]);
+  } else {
+    for (int b = 0; b < local; ++b) {
+      const float v = col[(int64_t)b * stride];
+      if (v >= tau) insert_desc<KS>(top, v);
     }
   }
-  float tstar = top[0];
+  const float tstar = pick<KS>(top, R - 1);
   int gt = 0;
 #pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    if (j == R - 1) tstar = top[j];
-  }
-#pragma unroll
-  for (int j = 0; j < NG; ++j) gt += (j < R && top[j] > tstar) ? 1 : 0;
+  for (int j = 0; j < KS; ++j) gt += (j < R && top[j] > tstar) ? 1 : 0;
   int need_eq = R - gt;
 
   // pass 4: emit ascending ids
   int w = 0;
+  const int n = listed ? cnt : local;
   for (int c = 0; c < n; ++c) {
-    const int b = listed ? (int)cand[c][tid] : c;
-    const float v = col[(int64_t)b * stride];
+    const float v = listed ? cval[c][tid] : col[(int64_t)c * stride];
+    const int b = listed ? (int)cid[c][tid] : c;
     bool take = v > tstar;
     if (!take && v == tstar && need_eq > 0) {
       take = true;
@@ -142,9 +172,9 @@ hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_s
   a.k = p->d.topk;
   const dim3 grid((unsigned)((row_count + kTopkThreads - 1) / kTopkThreads), (unsigned)a.P), block(kTopkThreads);
   const int need = a.k - 1;
-  if (need <= 16) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, a);
-  else if (need <= 32) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, st, a);
+  if (need <= 16) { ProfScope ps_(p, "topk_select", st); hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, a); }
+  else if (need <= 32) { ProfScope ps_(p, "topk_select", st); hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, st, a); }
+  else { ProfScope ps_(p, "topk_select", st); hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, st, a); }
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ MSA_BF16, MSA_FP8_E4M3 = 0, 1
 MSA_PREFILL, MSA_DECODE = 0, 1
 
 ENTRY_POINTS = ("msa_plan", "msa_plan_destroy", "msa_plan_info", "msa_proxy_block_maxscore", "msa_topk_select",
-                "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_last_error")
+                "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_last_error", "msa_profile_kernel",
+                "msa_profile_read")
 
 
 class MsaError(RuntimeError):
@@ -50,6 +51,7 @@ class PlanDesc(ctypes.Structure):
         ("proxy_sm_scale", ctypes.c_float),
         ("mode", ctypes.c_int),
         ("max_rows_per_call", ctypes.c_int64),
+        ("attn_window_rows", ctypes.c_int64),
     ]
 
 
@@ -68,6 +70,8 @@ def _load() -> ctypes.CDLL:
     lib.msa_topk_select.argtypes = [P, FP, I64, I64, IP, VP, SZ, P]
     lib.msa_sparse_attn_prefill.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
     lib.msa_sparse_attn_decode.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
+    lib.msa_profile_kernel.argtypes = [P, ctypes.c_char_p]
+    lib.msa_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.msa_last_error.restype = ctypes.c_char_p
     for name in ENTRY_POINTS:
         if name != "msa_last_error":
@@ -132,7 +136,7 @@ def msa_plan(qo_lens: Sequence[int], kv_lens: Sequence[int], num_qo_heads: int, 
              num_proxy_heads: int = 0, num_proxy_kv_heads: int = 0, topk: int = 16, kv_dtype: str = "bf16",
              proxy_dtype: str = "bf16", sm_scale: Optional[float] = None, proxy_sm_scale: Optional[float] = None,
              mode: str = "prefill", max_rows_per_call: int = 0, head_dim: int = 128, page_size: int = 128,
-             device=None, allocate: bool = True) -> Plan:
+             device=None, allocate: bool = True, attn_window_rows: int = 0) -> Plan:
     n = len(kv_lens)
     qo = (ctypes.c_int32 * n)(*[int(x) for x in qo_lens]) if qo_lens is not None else None
     kv = (ctypes.c_int32 * n)(*[int(x) for x in kv_lens])
@@ -148,6 +152,7 @@ def msa_plan(qo_lens: Sequence[int], kv_lens: Sequence[int], num_qo_heads: int, 
     d.proxy_sm_scale = proxy_sm_scale if proxy_sm_scale is not None else 1.0 / math.sqrt(head_dim)
     d.mode = {"prefill": MSA_PREFILL, "decode": MSA_DECODE}[mode]
     d.max_rows_per_call = max_rows_per_call
+    d.attn_window_rows = attn_window_rows
     return Plan(d, qo, kv, device=device, allocate=allocate)
 
 
@@ -179,6 +184,18 @@ def msa_sparse_attn_decode(plan: Plan, q, k_pages, v_pages, k_scale, v_scale, kv
                                        _ptr(v_scale), _ptr(kv_indices), _ptr(kv_block_indexes), _ptr(out),
                                        _ptr(lse), _ptr(plan.workspace), plan.workspace_bytes, _stream()))
     return out, lse
+
+
+def msa_profile_kernel(plan: Plan, kernel: Optional[str]):
+    """Bracket every later launch of one internal kernel with HIP events."""
+    _check(_lib.msa_profile_kernel(plan.handle, kernel.encode() if kernel else None))
+
+
+def msa_profile_read(plan: Plan):
+    """(summed milliseconds, launches) of the profiled kernel since the last read."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(_lib.msa_profile_read(plan.handle, ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
 
 
 def max_score_buffer(plan: Plan, device=None) -> torch.Tensor:

@@ -91,8 +91,9 @@ typedef struct {
   float sm_scale;              /* main attention logit scale */
   float proxy_sm_scale;        /* proxy logit scale */
   msa_mode_t mode;             /* which entry points the plan serves */
-  int64_t max_rows_per_call;   /* prefill: rows per proxy/top-k call and per
-                                  internal attention window; 0 = min(T, 32768) */
+  int64_t max_rows_per_call;   /* prefill: rows per proxy/top-k call; 0 = min(T, 32768) */
+  int64_t attn_window_rows;    /* prefill: rows whose attention partials are live at
+                                  once (workspace scales with it); 0 = automatic */
 } msa_plan_desc_t;
 
 /* Build a host plan from `desc`.  Validates every field; touches no device.
@@ -190,6 +191,17 @@ const char* msa_last_error(void);
 /* Plan introspection (host only): total rows T, max blocks per sequence
  * nb_max, and the row bound of one proxy / top-k call. */
 msa_status_t msa_plan_info(msa_plan_t plan, int64_t* total_rows, int32_t* nb_max, int64_t* max_rows_per_call);
+
+/* Diagnostics, not part of the path.  When `kernel` names one of the
+ * library's internal kernels ("proxy_maxscore", "topk_select", "csr",
+ * "partial_attn", "merge", "decode", "decode_merge"), each later launch of it
+ * for this plan is bracketed by two HIP events recorded on the call's stream
+ * (events are created on first use and reused; no device memory).  NULL
+ * switches it off.  msa_profile_read waits for the recorded events, returns
+ * the summed kernel time in milliseconds and the number of launches, and
+ * clears the record.  Errors: INVALID_ARG for an unknown name; HIP. */
+msa_status_t msa_profile_kernel(msa_plan_t plan, const char* kernel);
+msa_status_t msa_profile_read(msa_plan_t plan, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }
