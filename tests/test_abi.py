@@ -40,7 +40,9 @@ def test_plan_info_and_workspace():
     assert p.total_rows == 305 and p.nb_max == 8 and p.max_rows_per_call == 305
     assert p.workspace_bytes > 0
     p2 = _plan(max_rows_per_call=100)
-    assert p2.max_rows_per_call == 100 and p2.workspace_bytes < p.workspace_bytes
+    assert p2.max_rows_per_call == 100
+    p3 = _plan(attn_window_rows=100)          # attention partials scale with the window
+    assert p3.workspace_bytes < p.workspace_bytes
     d = msa.msa_plan(None, [1000] * 4, 16, 2, topk=17, kv_dtype="fp8", mode="decode", allocate=False)
     assert d.total_rows == 4 and d.nb_max == 8
 
@@ -58,6 +60,7 @@ def test_plan_info_and_workspace():
     (dict(num_proxy_kv_heads=3), msa.MSA_ERR_INVALID_ARG),
     (dict(kv_dtype="fp8"), msa.MSA_ERR_UNSUPPORTED),                         # fp8 K/V prefill not built
     (dict(sm_scale=-1.0), msa.MSA_ERR_INVALID_ARG),
+    (dict(attn_window_rows=-1), msa.MSA_ERR_INVALID_ARG),
 ])
 def test_plan_validation(kw, status):
     with pytest.raises(msa.MsaError) as e:
