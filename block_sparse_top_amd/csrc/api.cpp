@@ -239,13 +239,14 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
   p->max_rows = d.max_rows_per_call > 0 ? std::min<int64_t>(d.max_rows_per_call, T) : std::min<int64_t>(T, 32768);
 
   // Proxy row tiles: rows of one sequence whose positions fall in one
-  // 256-aligned position window (at most 256 rows).
+  // 512-aligned position window (at most 512 rows, one per lane of the proxy
+  // kernel's 8 waves x 64 rows).
   for (int s = 0; s < p->S; ++s) {
     const int32_t first_pos = p->kv[s] - p->qo[s];
     int32_t i = 0;
     while (i < p->qo[s]) {
       const int32_t pos = first_pos + i;
-      const int32_t end_pos = (pos / 256 + 1) * 256;
+      const int32_t end_pos = (pos / 512 + 1) * 512;
       const int32_t n = std::min(p->qo[s] - i, end_pos - pos);
       p->tiles.insert(p->tiles.end(), {s, p->row_start[s] + i, n, pos});
       i += n;

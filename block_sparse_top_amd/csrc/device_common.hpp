@@ -75,6 +75,22 @@ __device__ __forceinline__ void lds_store16(void* p, const T& v) {
   *(MSA_LDS T*)(p) = v;
 }
 
+// global_load_lds_dwordx4: each lane's 16 bytes at `g` land at LDS
+// `l + 16 * lane` (l is wave-uniform; it goes through M0).  The body exists
+// only in the device pass (the builtin has no host meaning).
+__device__ __forceinline__ void global_load_lds16(const void* g, MSA_LDS void* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+#endif
+}
+
+// Wait for every outstanding memory counter (vector memory, LDS, exports).
+__device__ __forceinline__ void wait_all_mem() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // (i % 4) of the 4 bf16 read by lane 4*e + i/4, for e = 0..3.
 __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {

@@ -7,16 +7,18 @@
 // every causally visible 128-key block.
 //
 // Design (gfx950):
-//  * one workgroup = 256 threads = 4 waves, one proxy head, one row tile of
-//    up to 256 rows whose positions share a 256-aligned window; wave w owns
-//    rows 64w .. 64w+63 as two 32-row MFMA column tiles;
+//  * one workgroup = 512 threads = 8 waves, one proxy head, one row tile of
+//    up to 512 rows whose positions share a 512-aligned window; wave w owns
+//    rows 64w .. 64w+63 as two 32-row MFMA column tiles, so each K tile
+//    staged in LDS feeds 512 rows;
 //  * S^T = K Q^T on MFMA (bf16 32x32x16 or fp8 32x32x64): keys are the MFMA
 //    rows, queries the columns, so each lane holds one query row and the
 //    max over keys is an in-register reduction plus one lane swap;
 //  * the tile's proxy Q stays in registers for the whole key loop; each K
-//    block (one page of one head, 32 KB bf16 / 16 KB fp8) is loaded with
-//    coalesced 16-byte loads into a double-buffered LDS tile; every A
-//    fragment read from LDS feeds two MFMAs (the wave's two row tiles);
+//    block (one page of one head, 32 KB bf16 / 16 KB fp8) goes straight from
+//    global memory into one of two LDS tiles (global_load_lds_dwordx4, no
+//    registers) while the other is being read; every A fragment read from
+//    LDS feeds two MFMAs (the wave's two row tiles);
 //  * only blocks up to the tile's last local block are visited; the two
 //    boundary blocks apply the per-row causal mask; scales are applied after
 //    the max (they are positive);
@@ -47,20 +49,23 @@ struct ProxyArgs {
 template <bool FP8>
 struct ProxyTraits;
 
+// K tiles live in LDS unpadded, with the 16-byte chunks of each row permuted
+// (physical chunk = logical chunk ^ swz(row)) so that the 16 rows read by a
+// fragment load hit 16 distinct bank groups.
 template <>
 struct ProxyTraits<false> {
   static constexpr int kElem = 2;             // bytes per element
   static constexpr int kRowBytes = 256;       // one key row
-  static constexpr int kLdsRow = 272;         // padded LDS row (bank spread)
   static constexpr int kSteps = 8;            // MFMA k-steps over d = 128
+  __device__ static int swz(int row) { return row & 15; }
   typedef bf16x8 Frag;
 };
 template <>
 struct ProxyTraits<true> {
   static constexpr int kElem = 1;
   static constexpr int kRowBytes = 128;
-  static constexpr int kLdsRow = 144;
   static constexpr int kSteps = 2;
+  __device__ static int swz(int row) { return (row >> 1) & 7; }
   typedef i32x8 Frag;
 };
 
@@ -78,17 +83,20 @@ __device__ __forceinline__ typename ProxyTraits<FP8>::Frag load_frag_global(cons
   }
 }
 
+// A fragment of key row `row`, logical 16-byte chunk `c` (and c+1 for fp8).
 template <bool FP8>
-__device__ __forceinline__ typename ProxyTraits<FP8>::Frag load_frag_lds(const uint8_t* p) {
+__device__ __forceinline__ typename ProxyTraits<FP8>::Frag load_frag_lds(const uint8_t* tile, int row, int c) {
+  using Tr = ProxyTraits<FP8>;
+  const uint8_t* base = tile + row * Tr::kRowBytes;
   if constexpr (FP8) {
-    i32x4 a = lds_load16<i32x4>(p);
-    i32x4 b = lds_load16<i32x4>(p + 16);
+    i32x4 a = lds_load16<i32x4>(base + ((c ^ Tr::swz(row)) << 4));
+    i32x4 b = lds_load16<i32x4>(base + (((c + 1) ^ Tr::swz(row)) << 4));
     i32x8 r;
     r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
     r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
     return r;
   } else {
-    return lds_load16<bf16x8>(p);
+    return lds_load16<bf16x8>(base + ((c ^ Tr::swz(row)) << 4));
   }
 }
 
@@ -99,15 +107,22 @@ __device__ __forceinline__ f32x16 mma(const typename ProxyTraits<FP8>::Frag& a,
   else return mfma32x32x16(a, b, c);
 }
 
+constexpr int kProxyWaves = 8;
+
 template <bool FP8>
-__global__ __launch_bounds__(256) void proxy_maxscore_kernel(ProxyArgs a) {
+__global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyArgs a) {
   using Tr = ProxyTraits<FP8>;
   using Frag = typename Tr::Frag;
   constexpr int kBlockBytes = 128 * Tr::kRowBytes;        // one K block in global memory
-  constexpr int kChunks = kBlockBytes / 16 / 256;         // 16-byte chunks per thread
+  constexpr int kLoads = kBlockBytes / 1024 / kProxyWaves;  // 1 KB direct-to-LDS loads per wave
   constexpr int kChunksPerRow = Tr::kRowBytes / 16;
+  constexpr int kRowsPerKB = 1024 / Tr::kRowBytes;
   constexpr int kStepBytes = Tr::kRowBytes / Tr::kSteps;  // bytes of d per MFMA k-step
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][128 * Tr::kLdsRow];
+  // two distinct tile objects (not one array indexed by a runtime buffer
+  // number): the loads in flight into one are then provably disjoint from
+  // the reads of the other
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBlockBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBlockBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -138,18 +153,18 @@ __global__ __launch_bounds__(256) void proxy_maxscore_kernel(ProxyArgs a) {
     }
   }
 
-  // Cooperative K block load: thread -> chunks tid + 256*i (coalesced).
-  i32x4 stage[kChunks];
-  auto gload = [&](int b) {
-    const uint8_t* src = a.pk + ((int64_t)pages[b] * a.Pk + ph) * kBlockBytes;
+  // K block -> LDS without registers: each wave issues kLoads direct 1 KB
+  // loads (global_load_lds_dwordx4: lane i fills bytes 16i..16i+15 of the
+  // KB), fetching for each lane the global chunk its swizzled slot holds.
+  auto kload = [&](int32_t page, uint8_t* tile) {
+    const uint8_t* src = a.pk + ((int64_t)page * a.Pk + ph) * kBlockBytes;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) stage[i] = *reinterpret_cast<const i32x4*>(src + (int64_t)(tid + 256 * i) * 16);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + 256 * i;
-      lds_store16<i32x4>(&lds[buf][(c / kChunksPerRow) * Tr::kLdsRow + (c % kChunksPerRow) * 16], stage[i]);
+    for (int i = 0; i < kLoads; ++i) {
+      const int kb = wave + kProxyWaves * i;             // which KB of the tile
+      const int row = kb * kRowsPerKB + lane / kChunksPerRow;
+      const int pc = lane % kChunksPerRow;               // physical chunk written by this lane
+      const int lc = pc ^ Tr::swz(row);                  // logical chunk it must hold
+      global_load_lds16(src + row * Tr::kRowBytes + lc * 16, (MSA_LDS void*)(tile + kb * 1024));
     }
   };
 
@@ -161,48 +176,110 @@ __global__ __launch_bounds__(256) void proxy_maxscore_kernel(ProxyArgs a) {
   const bool writes = my_row < nrows && my_grow >= a.row_begin && my_grow < a.row_end;
   float* outp = a.out + (int64_t)p * a.nb_max * a.row_count + (my_grow - a.row_begin);
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int b = 0; b <= b_last; ++b) {
-    const int buf = b & 1;
-    if (b < b_last) gload(b + 1);
-    if (wave_active) {
-      float m[2] = {kNegInf, kNegInf};
-      const bool masked = b >= b_full;
+  const int chunk0 = ((lane >> 5) * (kStepBytes / 2)) >> 4;
+  // one block against this wave's 64 rows: key tiles in two halves of two
+  // (4 independent accumulator chains each), fragments one k-step ahead,
+  // then the (masked) max into the running block max of each row tile
+  auto block_max = [&](const uint8_t* tile, int b, float (&m)[2]) {
+    m[0] = m[1] = kNegInf;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        f32x16 acc[2] = {f32x16{}, f32x16{}};
-        const uint8_t* arow = &lds[buf][(32 * kt + (lane & 31)) * Tr::kLdsRow + (lane >> 5) * (kStepBytes / 2)];
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 acc[2][2];
 #pragma unroll
-        for (int s = 0; s < Tr::kSteps; ++s) {
-          const Frag af = load_frag_lds<FP8>(arow + s * kStepBytes);
-          acc[0] = mma<FP8>(af, qf[0][s], acc[0]);
-          acc[1] = mma<FP8>(af, qf[1][s], acc[1]);
+      for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = f32x16{};
+      Frag fr[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fr[0][j] = load_frag_lds<FP8>(tile, 32 * (2 * hf + j) + (lane & 31), chunk0);
+#pragma unroll
+      for (int st = 0; st < Tr::kSteps; ++st) {
+        if (st + 1 < Tr::kSteps) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            fr[(st + 1) & 1][j] = load_frag_lds<FP8>(tile, 32 * (2 * hf + j) + (lane & 31),
+                                                     chunk0 + (((st + 1) * kStepBytes) >> 4));
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[j][0] = mma<FP8>(fr[st & 1][j], qf[0][st], acc[j][0]);
+          acc[j][1] = mma<FP8>(fr[st & 1][j], qf[1][st], acc[j][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep LDS fragment reads one k-step ahead at most
+      }
+      if (b >= b_full) {
+        // boundary block: key (32kt + 8(i/4) + 4(lane/32) + i%4) is visible to
+        // this lane's row iff its position does not exceed the row's
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          if (masked) {
-            const int rpos = pos0 + 64 * wave + 32 * sub + (lane & 31);
-            const int lim = rpos - (b * 128 + 32 * kt + 4 * (lane >> 5));  // key offset bound
+          const int lim = pos0 + 64 * wave + 32 * sub + (lane & 31) - (b * 128 + 4 * (lane >> 5));
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int koff = 8 * (i >> 2) + (i & 3);
-              const float v = koff <= lim ? acc[sub][i] : kNegInf;
-              m[sub] = fmaxf(m[sub], v);
-            }
-          } else {
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m[sub] = fmaxf(m[sub], acc[sub][i]);
-          }
+            for (int i = 0; i < 16; ++i)
+              m[sub] = fmaxf(m[sub], (32 * (2 * hf + j) + 8 * (i >> 2) + (i & 3)) <= lim ? acc[j][sub][i] : kNegInf);
         }
+      } else {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2)
+              m[sub] = __builtin_fmaxf(m[sub], __builtin_fmaxf(acc[j][sub][i], acc[j][sub][i + 1]));
       }
-      m[0] = fmaxf(m[0], wave_xor32(m[0]));
-      m[1] = fmaxf(m[1], wave_xor32(m[1]));
-      if (writes) outp[(int64_t)b * a.row_count] = (lane < 32 ? m[0] : m[1]) * scale;
     }
-    if (b < b_last) lstore(buf ^ 1);
-    __syncthreads();
+  };
+  auto finish = [&](int b, float (&m)[2]) {
+    m[0] = fmaxf(m[0], wave_xor32(m[0]));
+    m[1] = fmaxf(m[1], wave_xor32(m[1]));
+    if (writes) outp[(int64_t)b * a.row_count] = (lane < 32 ? m[0] : m[1]) * scale;
+  };
+
+  // Page ids: lane i holds page (64*w + i) of window w; the next window is
+  // loaded a whole window ahead, and the id of a block is picked with a
+  // uniform-index lane read, so no page-table latency sits in the loop.
+  int pw_cur = lane <= b_last ? pages[lane] : 0;
+  int pw_next = 64 + lane <= b_last ? pages[64 + lane] : 0;
+  int cur_w = 0;
+  auto page_of = [&](int x) -> int32_t {
+    return __builtin_amdgcn_readlane((x >> 6) == cur_w ? pw_cur : pw_next, x & 63);
+  };
+  auto advance = [&](int x) {  // x: the block about to be computed
+    if ((x & 63) == 0 && (x >> 6) != cur_w) {
+      pw_cur = pw_next;
+      cur_w = x >> 6;
+      const int nx = 64 * (cur_w + 1) + lane;
+      pw_next = nx <= b_last ? pages[nx] : 0;
+    }
+  };
+
+  // block loop unrolled by two over the two tiles: block b computes from one
+  // tile while block b+1 streams into the other
+  kload(page_of(0), lds0);
+  wait_all_mem();
+  __syncthreads();
+  for (int b = 0; b <= b_last; b += 2) {
+    {
+      advance(b);
+      if (b + 1 <= b_last) kload(page_of(b + 1), lds1);
+      float m[2];
+      if (wave_active) {
+        block_max(lds0, b, m);
+        finish(b, m);
+      }
+      wait_all_mem();
+      __syncthreads();
+    }
+    if (b + 1 <= b_last) {
+      advance(b + 1);
+      if (b + 2 <= b_last) kload(page_of(b + 2), lds0);
+      float m[2];
+      if (wave_active) {
+        block_max(lds1, b + 1, m);
+        finish(b + 1, m);
+      }
+      wait_all_mem();
+      __syncthreads();
+    }
   }
 }
 
@@ -231,7 +308,7 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
   a.row_count = row_count;
   a.out = max_score;
   a.scale = p->d.proxy_sm_scale;
-  const dim3 grid((unsigned)(a.ntiles * a.P)), block(256);
+  const dim3 grid((unsigned)(a.ntiles * a.P)), block(64 * kProxyWaves);
   if (p->d.proxy_dtype == MSA_FP8_E4M3) {
     { ProfScope ps_(p, "proxy_maxscore", st); hipLaunchKernelGGL(proxy_maxscore_kernel<true>, grid, block, 0, st, a); }
   } else {
