@@ -57,7 +57,40 @@ def oracle_scores(inp: Inputs, rows=None):
                                   inp.proxy_k_scale, rows=rows)
 
 
-def check_max_score(gpu_ms: np.ndarray, ref: np.ndarray, what=""):
+# fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) does not accumulate exactly:
+# measured on random e4m3 operands, a length-128 dot product is off by up to
+# 2^-12.5 of the sum of its absolute products (median 2^-16).  fp8 proxy
+# scores are therefore compared within 2^-12 of that magnitude.
+FP8_ACC_REL = 2.0 ** -12
+
+
+def fp8_score_bound(inp, rows, scale):
+    """Per (row, head, block): 2^-12 * scale * max over the block's visible
+    keys of sum_d |q_d k_d| (dequantised values), for fp8 proxy tolerances."""
+    w = inp.w
+    lay = O.Layout(w.qo_lens, w.kv_lens, w.page_size)
+    P, Pk = w.num_proxy_heads, w.num_proxy_kv_heads
+    out = np.zeros((len(rows), P, max(lay.nb)))
+    for s in range(len(lay.kv)):
+        idx = [i for i, r in enumerate(rows) if lay.row_start[s] <= r < lay.row_start[s + 1]]
+        if not idx:
+            continue
+        L = lay.kv[s]
+        for p in range(P):
+            ph = p if Pk == P else 0
+            K = np.abs(O.gather_rows(inp.proxy_k_pages, FP8, inp.proxy_k_scale, inp.kv_indices, lay, s, ph, np.arange(L)))
+            q = np.abs(O.dequant(inp.proxy_q[np.asarray(rows)[idx], p:p + 1, :], FP8, inp.proxy_q_scale[p:p + 1]))[:, 0]
+            S = q @ K.T
+            pos = np.array([lay.pos(int(rows[i])) for i in idx])
+            S[np.arange(L)[None, :] > pos[:, None]] = 0.0
+            nb = lay.nb[s]
+            Sp = np.zeros((len(idx), nb * lay.B))
+            Sp[:, :L] = S
+            out[idx, p, :nb] = Sp.reshape(len(idx), nb, lay.B).max(axis=2)
+    return FP8_ACC_REL * scale * out
+
+
+def check_max_score(gpu_ms: np.ndarray, ref: np.ndarray, what="", extra_tol=None):
     """gpu_ms [P, nb_max, n] vs ref [n, P, nb_max]; compare defined entries."""
     g = np.transpose(gpu_ms, (2, 0, 1)).astype(np.float64)
     m = ~np.isnan(ref)
@@ -66,6 +99,8 @@ def check_max_score(gpu_ms: np.ndarray, ref: np.ndarray, what=""):
     assert np.array_equal(np.isneginf(g[m & ~fin]), np.ones(int((m & ~fin).sum()), bool)), what
     err = np.abs(g[fin] - ref[fin])
     tol = MS_ATOL + MS_RTOL * np.abs(ref[fin])
+    if extra_tol is not None:
+        tol = tol + extra_tol[fin]
     bad = err > tol
     assert not bad.any(), f"{what}: {int(bad.sum())} max_score entries off (worst {err.max():.3g})"
 

@@ -1,0 +1,134 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration
+bench.py times (default plan: 32768-row proxy/top-k chunks and attention
+windows).  The oracle computes sampled rows one by one: evenly spaced rows
+plus the edge rows of every sequence (first, last, and the rows around the
+first 128- and 1920-key boundaries).  The decode workload is checked on every
+output.  Inputs come from the seeded device generator (the same recipe as the
+CPU generator, drawn on the GPU).
+
+Tolerances as in test_gpu_parity: max scores 1e-4 + 1e-5|x| (plus the fp8
+accumulation bound for fp8 proxy scores), the 1e-3 band
+rule for selections, outputs max-abs 2e-2 / cosine 0.999 (bf16 K/V) or
+6e-2 / 0.99 (fp8 K/V)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synthetic.gen import workload, seed_of, FP8
+from synthetic.device_gen import make_inputs_device, to_host
+from tests._gpu import (bf16_out_to_f64, check_max_score, check_selection, check_output, fp8_score_bound,
+                        BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(w, n_even, seed):
+    T = w.total_rows
+    rows = set(np.linspace(0, T - 1, n_even).astype(np.int64).tolist())
+    r0 = 0
+    for qo in w.qo_lens:
+        for i in (0, 1, 127, 128, 129, 1919, 1920, qo - 1):
+            if 0 <= i < qo:
+                rows.add(r0 + i)
+        r0 += qo
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, T, size=8).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _prefill_case(n_cfg, n_even):
+    from block_sparse_top_amd import msa
+    w = workload(n_cfg)
+    print(f"[fullsize] prefill workload={w.name} T={w.total_rows}", flush=True)
+    inp = make_inputs_device(w, seed_of(n_cfg))
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                        w.num_proxy_kv_heads, topk=w.topk, kv_dtype=w.kv_dtype, proxy_dtype=w.proxy_dtype)
+    T, R = w.total_rows, plan.max_rows_per_call
+    rows = _sample_rows(w, n_even, seed_of(n_cfg))
+    sel = torch.full((T, w.num_kv_heads, w.topk), -7, dtype=torch.int32, device="cuda")
+    ms = msa.max_score_buffer(plan)
+    got_ms = np.full((w.num_proxy_heads, plan.nb_max, rows.size), np.nan, np.float32)
+    for r0 in range(0, T, R):
+        n = min(R, T - r0)
+        msa.msa_proxy_block_maxscore(plan, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale,
+                                     inp.kv_indices, r0, n, ms)
+        msa.msa_topk_select(plan, ms, r0, n, sel)
+        here = np.nonzero((rows >= r0) & (rows < r0 + n))[0]
+        if here.size:
+            got_ms[:, :, here] = ms[:, :, torch.from_numpy(rows[here] - r0).cuda()].cpu().numpy()
+    out = torch.empty((T, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, w.num_qo_heads), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_prefill(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, lse)
+    torch.cuda.synchronize()
+    gsel = sel.cpu().numpy()
+    gout = bf16_out_to_f64(out[torch.from_numpy(rows).cuda()])
+    glse = lse[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del out, lse, ms
+    h = {k: to_host(getattr(inp, k)) for k in ("q", "k_pages", "v_pages", "kv_indices", "proxy_q", "proxy_k_pages",
+                                                "proxy_q_scale", "proxy_k_scale")}
+    del inp
+    torch.cuda.empty_cache()
+    ref_ms = O.proxy_block_maxscore(h["proxy_q"], h["proxy_k_pages"], h["kv_indices"], w.qo_lens, w.kv_lens, 128,
+                                    w.proxy_sm_scale, w.proxy_dtype, h["proxy_q_scale"], h["proxy_k_scale"], rows=rows)
+    extra = None
+    if w.proxy_dtype == FP8:
+        from synthetic.gen import Inputs
+        hi = Inputs(w, h["kv_indices"], h["q"], h["k_pages"], h["v_pages"], proxy_q=h["proxy_q"],
+                    proxy_k_pages=h["proxy_k_pages"], proxy_q_scale=h["proxy_q_scale"],
+                    proxy_k_scale=h["proxy_k_scale"])
+        extra = fp8_score_bound(hi, rows, w.proxy_sm_scale)
+    check_max_score(got_ms, ref_ms, w.name, extra)
+    lay = O.Layout(w.qo_lens, w.kv_lens, 128)
+    check_selection(gsel[rows], ref_ms, np.array([lay.local(int(r)) for r in rows]), w.topk, w.name)
+    # every row: local block present, ascending, valid padding
+    loc_all = np.concatenate([(np.arange(kv - qo, kv) // 128) for qo, kv in zip(w.qo_lens, w.kv_lens)])
+    valid = gsel >= 0
+    assert np.all(valid[:, :, 0]), "every row selects at least its local block"
+    last = np.where(valid, gsel, -1).max(axis=2)
+    assert np.array_equal(last, np.broadcast_to(loc_all[:, None], last.shape)), "local block missing somewhere"
+    ref_out, ref_lse = O.sparse_attention(h["q"], h["k_pages"], h["v_pages"], h["kv_indices"], gsel, w.qo_lens,
+                                          w.kv_lens, 128, w.sm_scale, rows=rows)
+    check_output(gout, ref_out, BF16_ATOL, BF16_COS, w.name)
+    assert np.abs(glse - ref_lse).max() < 1e-3, w.name
+
+
+def test_prefill_32k_sampled_rows():
+    _prefill_case(2, 48)
+
+
+def test_prefill_varlen_128k_sampled_rows():
+    _prefill_case(3, 48)
+
+
+@pytest.mark.slow
+def test_prefill_1m_fp8_proxy_sampled_rows():
+    _prefill_case(5, 12)
+
+
+def test_decode_fp8_b32_131k_all_outputs():
+    from block_sparse_top_amd import msa
+    w = workload(4)
+    print(f"[fullsize] decode workload={w.name}", flush=True)
+    inp = make_inputs_device(w, seed_of(4))
+    plan = msa.msa_plan(None, w.kv_lens, w.num_qo_heads, w.num_kv_heads, topk=w.topk, kv_dtype="fp8", mode="decode")
+    out = torch.empty((w.num_seqs, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.num_seqs, w.num_qo_heads), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_decode(plan, inp.q, inp.k_pages, inp.v_pages, inp.k_scale, inp.v_scale, inp.kv_indices,
+                               inp.kv_block_indexes, out, lse)
+    torch.cuda.synchronize()
+    # the oracle only needs the selected pages: gather them (a plain copy) and renumber
+    sel = to_host(inp.kv_block_indexes)
+    kvi = to_host(inp.kv_indices)
+    lay = O.Layout([1] * w.num_seqs, w.kv_lens, 128)
+    need = sorted({int(kvi[lay.page_start[s] + b]) for s in range(w.num_seqs) for b in sel[s].ravel() if b >= 0})
+    remap = np.full(inp.k_pages.shape[0], -1, np.int64)
+    remap[need] = np.arange(len(need))
+    idx = torch.tensor(need, device="cuda")
+    kp = to_host(inp.k_pages[idx])
+    vp = to_host(inp.v_pages[idx])
+    kvi2 = np.where(remap[kvi] >= 0, remap[kvi], 0).astype(np.int32)
+    ref, ref_lse = O.sparse_decode(to_host(inp.q), kp, vp, kvi2, sel, w.kv_lens, 128, w.sm_scale, FP8,
+                                   to_host(inp.k_scale), to_host(inp.v_scale))
+    check_output(bf16_out_to_f64(out), ref, FP8_ATOL, FP8_COS, w.name)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-3

@@ -5,7 +5,10 @@ the attention is checked on the selection the GPU produced so that near-ties
 cannot move the output.
 
 Tolerances: max scores |gpu - oracle| <= 1e-4 + 1e-5 |oracle| (fp32
-accumulation of exact bf16/fp8 products); selections by the 1e-3 band rule;
+accumulation of exact bf16 products), plus 2^-12 * scale * max_key sum_d |q_d k_d|
+for fp8 proxy scores (the fp8 matrix cores do not accumulate exactly: the
+measured worst case is 2^-12.5 of the absolute product sum); selections by the
+1e-3 band rule;
 outputs max-abs <= 2e-2 and cosine >= 0.999 (bf16 K/V) or <= 6e-2 and
 >= 0.99 (fp8 K/V)."""
 import dataclasses
@@ -17,7 +20,7 @@ import torch
 import oracle as O
 from synthetic.gen import Workload, make_inputs, workload, seed_of, FP8, BF16
 from tests._gpu import (device_inputs, plan_for, bf16_out_to_f64, oracle_scores, check_max_score, check_selection,
-                        check_output, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS)
+                        check_output, fp8_score_bound, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +77,8 @@ def test_prefill_stages_match_oracle(case):
     print(f"[parity] prefill case={case} T={w.total_rows} seed={seed}", flush=True)
     gms, gsel, gout, glse = run_prefill_stages(msa, inp, max_rows)
     ref_ms = oracle_scores(inp)
-    check_max_score(gms, ref_ms, case)
+    extra = fp8_score_bound(inp, np.arange(w.total_rows), w.proxy_sm_scale) if w.proxy_dtype == FP8 else None
+    check_max_score(gms, ref_ms, case, extra)
     lay = O.Layout(w.qo_lens, w.kv_lens, w.page_size)
     locals_ = np.array([lay.local(r) for r in range(w.total_rows)])
     check_selection(gsel, ref_ms, locals_, w.topk, case)
