@@ -49,14 +49,166 @@ def source_hash(kernel: str) -> str:
 
 def traffic_from_profiles(kernel: str, workload: str):
     """Counter-measured HBM bytes per launch, if a committed summary for the
-    current kernel source exists (null otherwise)."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__traffic.json")
+    current kernel source exists (null otherwise).  The summary's last line
+    is a JSON object."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__traffic.txt")
     if not os.path.exists(p):
         return None
-    d = json.load(open(p))
+    last = [ln for ln in open(p).read().splitlines() if ln.startswith("{")][-1]
+    d = json.loads(last)
     if d.get("source_hash") != source_hash(kernel):
         return None
     return d.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# rocprofv3 summaries (run on the host from the CSV files rocprofv3 wrote)
+# ----------------------------------------------------------------------------
+COPY_BYTES = 1 << 30           # calibration copy: bytes read and bytes written per launch
+PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --extra decode_131k --copy-calibration"
+PMC_CMDS = {
+    "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o f -- python bench.py {PMC_ARGS}",
+    "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o w -- python bench.py {PMC_ARGS}",
+}
+TRACE_CMD = "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/kt -o kt -- python bench.py"
+SECTION_OF_KERNEL = {"decode": "decode_fp8_b32_131k", "decode_merge": "decode_fp8_b32_131k"}
+
+
+def _short_kernel(name: str):
+    import re
+    if "bitwise_not" in name:
+        return "copy"
+    m = re.search(r"msa::\(anonymous namespace\)::(\w+?)(_kernel)?[<(]", name)
+    return m.group(1) if m else None
+
+
+def summarize_counters(fetch_csv: str, write_csv: str):
+    """Per-launch HBM bytes of every library kernel from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch), each scaled by the factor that makes
+    the same counter read the known size of the calibration copy."""
+    import collections
+    import csv
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(dict)          # kernel -> dispatch -> KiB
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _short_kernel(r["Kernel_Name"])
+            if k is not None:
+                acc[k][int(r["Dispatch_Id"])] = acc[k].get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+        return {k: (sum(v.values()) / len(v), len(v)) for k, v in acc.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    f_fac = COPY_BYTES / (fetch["copy"][0] * 1024.0)
+    w_fac = COPY_BYTES / (write["copy"][0] * 1024.0)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    written = []
+    for k in sorted(set(fetch) & set(write)):
+        if k == "copy" or k not in KERNEL_SOURCES:
+            continue
+        wl = SECTION_OF_KERNEL.get(k, "prefill_32k_gqa4")
+        fb = fetch[k][0] * 1024.0 * f_fac
+        wb = write[k][0] * 1024.0 * w_fac
+        d = {"kernel": k, "workload": wl, "bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
+             "fetch_kib_raw": fetch[k][0], "write_kib_raw": write[k][0], "dispatches": fetch[k][1],
+             "fetch_factor": f_fac, "write_factor": w_fac, "source_hash": source_hash(k)}
+        txt = (f"# HBM traffic of {k} on {wl} (rocprofv3 counters, per dispatch)\n"
+               f"# fetch: {PMC_CMDS['FETCH_SIZE']}\n# write: {PMC_CMDS['WRITE_SIZE']}\n"
+               f"# summary: python bench.py --summarize-counters gpurun_out/pmc_fetch/f_counter_collection.csv "
+               f"gpurun_out/pmc_write/w_counter_collection.csv\n"
+               f"# calibration: a streaming int32 copy reading and writing {COPY_BYTES} B per launch reads "
+               f"FETCH_SIZE {fetch['copy'][0]:.0f} KiB and WRITE_SIZE {write['copy'][0]:.0f} KiB, "
+               f"factors {f_fac:.4f} and {w_fac:.4f}\n"
+               f"# {k}: {fetch[k][1]} dispatches, FETCH_SIZE {fetch[k][0]:.0f} KiB, WRITE_SIZE {write[k][0]:.0f} KiB "
+               f"-> {fb / 1e9:.3f} GB read + {wb / 1e9:.3f} GB written = {(fb + wb) / 1e9:.3f} GB per launch\n"
+               + json.dumps(d) + "\n")
+        path = os.path.join(ROOT, "profiles", f"{k}__{wl}__traffic.txt")
+        open(path, "w").write(txt)
+        written.append(path)
+    return written
+
+
+def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
+    """Kernel durations from a rocprofv3 kernel trace, per workload, next to
+    the per-launch averages that bench.py measured with HIP events in the same
+    run.  The prefill workloads run one after another and every step ends
+    with the attention and merge kernels, so a prefill dispatch belongs to the
+    workload of the next partial_attn dispatch, a merge to that of the one
+    before it; workloads are named in the order bench.py runs them."""
+    import collections
+    import csv
+    line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
+    b = json.loads(line)
+    ev = [(b["config"]["workload"], b["roofline"])]
+    for name, r in (b.get("extra") or {}).items():
+        ev.append((r["workload"], r["roofline"]))
+    prefill_names = [wl for wl, _ in ev if wl.startswith("prefill")]
+    rows = []
+    for r in sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"])):
+        k = _short_kernel(r["Kernel_Name"])
+        if k is None or k == "copy":
+            continue
+        grid = "x".join(r[f"Grid_Size_{a}"] for a in "XYZ")
+        rows.append((k, grid, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6))
+    # partial_attn grid -> workload by order of first appearance
+    grids = []
+    for k, grid, _ in rows:
+        if k == "partial_attn" and grid not in grids:
+            grids.append(grid)
+    label_of_grid = {gr: (prefill_names[i] if i < len(prefill_names) else f"prefill grid {gr}")
+                     for i, gr in enumerate(grids)}
+    section = [None] * len(rows)
+    nxt = None
+    for i in range(len(rows) - 1, -1, -1):
+        k, grid, _ = rows[i]
+        if k == "partial_attn":
+            nxt = label_of_grid[grid]
+        section[i] = nxt
+    last = None
+    for i, (k, grid, _) in enumerate(rows):
+        if k.startswith("decode"):
+            section[i] = SECTION_OF_KERNEL["decode"]
+        elif k == "merge" or section[i] is None:
+            section[i] = last
+        if k == "partial_attn":
+            last = label_of_grid[grid]
+    g = collections.OrderedDict()
+    for (k, grid, ms), sec in zip(rows, section):
+        g.setdefault((sec, k, grid), []).append(ms)
+    out = [f"# Kernel durations, rocprofv3 kernel trace of the default benchmark run",
+           f"# command: {TRACE_CMD}",
+           f"# summary: python bench.py --summarize-trace gpurun_out/kt/kt_kernel_trace.csv <bench stdout> {out_name}",
+           "", "| workload | kernel | grid | calls | avg ms | min ms | max ms | total ms |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (sec, k, grid), v in sorted(g.items(), key=lambda kv: str(kv[0][0])):
+        out.append(f"| {sec} | {k} | {grid} | {len(v)} | {np.mean(v):.4f} | {min(v):.4f} | {max(v):.4f} | "
+                   f"{sum(v):.3f} |")
+    out += ["", "HIP-event averages that bench.py reported for the dominant kernel of each workload in this run:", ""]
+    for wl, r in ev:
+        tr = np.mean(g.get((wl, r["kernel"], next((gr for (s2, k2, gr) in g if s2 == wl and k2 == r["kernel"]), "")),
+                           [float("nan")]))
+        out.append(f"- {wl}: {r['kernel']} {r['avg_launch_ms']:.4f} ms per launch by HIP events, {tr:.4f} ms in the "
+                   f"trace ({r['launches_per_step']} launches per step); {r['achieved']:.1f} {r['unit']} "
+                   f"= {100 * r['frac']:.1f}% of {r['peak']:.0f}")
+    out += ["", "bench.py line of this run:", "", "```", line, "```", ""]
+    path = os.path.join(ROOT, "profiles", out_name)
+    open(path, "w").write("\n".join(out))
+    return path
+
+
+def copy_calibration(reps=3):
+    """A plain streaming copy of known size (int32 bitwise not: COPY_BYTES read
+    and COPY_BYTES written per launch), profiled beside the library kernels to
+    scale the HBM byte counters."""
+    import torch
+    src = torch.arange(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 # ----------------------------------------------------------------------------
@@ -264,9 +416,24 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode entries")
+    ap.add_argument("--extra", default="prefill_128k,decode_131k",
+                    help="comma-separated extra entries: prefill_128k, decode_131k (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a streaming copy of known size (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: write profiles/<kernel>__<workload>__traffic.txt from two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "BENCH_STDOUT", "OUT_NAME"),
+                    help="host only: write a kernel-duration summary under profiles/ from a rocprofv3 kernel trace")
     args = ap.parse_args()
+    if args.summarize_counters:
+        for p in summarize_counters(*args.summarize_counters):
+            print(p)
+        return
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (see the design notes on "
               "sharding); run with --gpus 1", file=sys.stderr)
@@ -274,13 +441,21 @@ def main():
     import torch
     from block_sparse_top_amd import msa
     torch.cuda.set_device(0)
+    extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
+    for e in extras:
+        if e not in ("prefill_128k", "decode_131k"):
+            ap.error(f"unknown extra entry {e}")
+    if args.copy_calibration:
+        print("[bench] calibration copy", file=sys.stderr, flush=True)
+        copy_calibration()
     print("[bench] prefill 32k", file=sys.stderr, flush=True)
     main_res, (w, inp, sel) = prefill_bench(msa, 2, args.steps, args.warmup)
     extra = {}
-    if not args.no_extra:
+    if "prefill_128k" in extras:
         print("[bench] prefill 128k varlen", file=sys.stderr, flush=True)
         r3, _ = prefill_bench(msa, 3, max(2, args.steps // 2), 1)
         extra["prefill_128k"] = r3
+    if "decode_131k" in extras:
         print("[bench] decode 131k fp8", file=sys.stderr, flush=True)
         extra["decode_131k"] = decode_bench(msa, max(50, args.steps * 10), 10)
     cpu = None

@@ -110,20 +110,17 @@ const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "csr", "par
                                     "decode_merge"};
 }  // namespace
 
-ProfScope::ProfScope(const msa_plan_s* p, const char* name, hipStream_t st) : p_(p), st_(st) {
+ProfEvents::ProfEvents(const msa_plan_s* p, const char* name) {
   if (p->prof.kernel.empty() || p->prof.kernel != name) return;
-  hipEvent_t start = take_event(p->prof);
-  stop_ = take_event(p->prof);
-  if (!start || !stop_) {
-    stop_ = nullptr;
+  start = take_event(p->prof);
+  stop = take_event(p->prof);
+  if (!start || !stop) {
+    if (start) p->prof.pool.push_back(start);
+    if (stop) p->prof.pool.push_back(stop);
+    start = stop = nullptr;
     return;
   }
-  (void)hipEventRecord(start, st);
-  p->prof.pending.emplace_back(start, stop_);
-}
-
-ProfScope::~ProfScope() {
-  if (stop_) (void)hipEventRecord(stop_, st_);
+  p->prof.pending.emplace_back(start, stop);
 }
 
 }  // namespace msa

@@ -1,6 +1,7 @@
 // Internal declarations shared by the host API and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -64,16 +65,13 @@ namespace msa {
 
 DevMeta dev_meta(const msa_plan_s* p, const void* workspace);
 
-// Brackets one kernel launch with HIP events when the plan profiles `name`.
-class ProfScope {
- public:
-  ProfScope(const msa_plan_s* p, const char* name, hipStream_t st);
-  ~ProfScope();
-
- private:
-  const msa_plan_s* p_;
-  hipStream_t st_;
-  hipEvent_t stop_ = nullptr;
+// Start/stop events for one stage when the plan profiles `name` (both null
+// otherwise).  They are handed to hipExtLaunchKernelGGL, which stamps them
+// with the dispatch's own begin and end: `start` on a stage's first kernel,
+// `stop` on its last.
+struct ProfEvents {
+  ProfEvents(const msa_plan_s* p, const char* name);
+  hipEvent_t start = nullptr, stop = nullptr;
 };
 
 // Kernel launchers (defined in the .hip files).  They assume validated inputs.

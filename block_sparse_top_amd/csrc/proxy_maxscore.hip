@@ -310,9 +310,9 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
   a.scale = p->d.proxy_sm_scale;
   const dim3 grid((unsigned)(a.ntiles * a.P)), block(64 * kProxyWaves);
   if (p->d.proxy_dtype == MSA_FP8_E4M3) {
-    { ProfScope ps_(p, "proxy_maxscore", st); hipLaunchKernelGGL(proxy_maxscore_kernel<true>, grid, block, 0, st, a); }
+    { ProfEvents pe(p, "proxy_maxscore"); hipExtLaunchKernelGGL(proxy_maxscore_kernel<true>, grid, block, 0, st, pe.start, pe.stop, 0, a); }
   } else {
-    { ProfScope ps_(p, "proxy_maxscore", st); hipLaunchKernelGGL(proxy_maxscore_kernel<false>, grid, block, 0, st, a); }
+    { ProfEvents pe(p, "proxy_maxscore"); hipExtLaunchKernelGGL(proxy_maxscore_kernel<false>, grid, block, 0, st, pe.start, pe.stop, 0, a); }
   }
   return hipGetLastError();
 }

@@ -347,13 +347,18 @@ hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, c
   a.nsplit = p->dec_splits;
   a.scale_log2 = p->d.sm_scale * kLog2e;
   const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)p->S), block(64 * kDecWaves);
-  if (p->d.kv_dtype == MSA_FP8_E4M3) { ProfScope ps_(p, "decode", st); hipLaunchKernelGGL(decode_kernel<true>, grid, block, 0, st, a); }
-  else { ProfScope ps_(p, "decode", st); hipLaunchKernelGGL(decode_kernel<false>, grid, block, 0, st, a); }
+  {
+    ProfEvents pe(p, "decode");
+    if (p->d.kv_dtype == MSA_FP8_E4M3)
+      hipExtLaunchKernelGGL(decode_kernel<true>, grid, block, 0, st, pe.start, pe.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(decode_kernel<false>, grid, block, 0, st, pe.start, pe.stop, 0, a);
+  }
   if (a.nsplit > 1) {
     const int64_t nw = (int64_t)p->S * a.Hq;
-    ProfScope ps_(p, "decode_merge", st);
-    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, a.part_o, a.part_ml,
-                       a.out, lse, p->S, a.Hq, a.nsplit);
+    ProfEvents pe(p, "decode_merge");
+    hipExtLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, pe.start, pe.stop, 0,
+                          a.part_o, a.part_ml, a.out, lse, p->S, a.Hq, a.nsplit);
   }
   return hipGetLastError();
 }

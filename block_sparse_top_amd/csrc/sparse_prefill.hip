@@ -401,9 +401,9 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   // counts and cursor are adjacent 256-aligned segments: clear both
   const int64_t nclear = (int64_t)(L.offsets - L.counts) / 4;
   {
-  ProfScope ps_(p, "csr", st);
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(1024, (nclear + 255) / 256)), dim3(256), 0, st,
-                     counts, nclear, 0);
+  ProfEvents pe(p, "csr");
+  hipExtLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(1024, (nclear + 255) / 256)), dim3(256), 0,
+                        st, pe.start, nullptr, 0, counts, nclear, 0);
   CsrArgs c;
   c.sel = sel;
   c.m = m;
@@ -422,8 +422,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   else hipLaunchKernelGGL((csr_pass_kernel<false, false>), cgrid, dim3(256), 0, st, c);
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, counts, offsets, items, nitems, nkey,
                      p->NB, p->entries_per_item);
-  if (lds_hist) hipLaunchKernelGGL((csr_pass_kernel<true, true>), cgrid, dim3(256), hist_bytes, st, c);
-  else hipLaunchKernelGGL((csr_pass_kernel<true, false>), cgrid, dim3(256), 0, st, c);
+  if (lds_hist) hipExtLaunchKernelGGL((csr_pass_kernel<true, true>), cgrid, dim3(256), hist_bytes, st, nullptr, pe.stop, 0, c);
+  else hipExtLaunchKernelGGL((csr_pass_kernel<true, false>), cgrid, dim3(256), 0, st, nullptr, pe.stop, 0, c);
   }
 
   PartialArgs a;
@@ -446,8 +446,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   // upper bound on the number of work items of this window
   const int64_t max_items = ((int64_t)(w1 - w0) * Hkv * k + p->entries_per_item - 1) / p->entries_per_item + nkey;
   {
-    ProfScope ps_(p, "partial_attn", st);
-    hipLaunchKernelGGL(partial_attn_kernel, dim3((unsigned)max_items), dim3(256), 0, st, a);
+    ProfEvents pe(p, "partial_attn");
+    hipExtLaunchKernelGGL(partial_attn_kernel, dim3((unsigned)max_items), dim3(256), 0, st, pe.start, pe.stop, 0, a);
   }
 
   MergeArgs mg;
@@ -465,8 +465,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   mg.w1 = w1;
   const int64_t npairs = (int64_t)(w1 - w0) * Hq;
   {
-    ProfScope ps_(p, "merge", st);
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, mg);
+    ProfEvents pe(p, "merge");
+    hipExtLaunchKernelGGL(merge_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, pe.start, pe.stop, 0, mg);
   }
   return hipGetLastError();
 }

@@ -172,9 +172,9 @@ hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_s
   a.k = p->d.topk;
   const dim3 grid((unsigned)((row_count + kTopkThreads - 1) / kTopkThreads), (unsigned)a.P), block(kTopkThreads);
   const int need = a.k - 1;
-  if (need <= 16) { ProfScope ps_(p, "topk_select", st); hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, a); }
-  else if (need <= 32) { ProfScope ps_(p, "topk_select", st); hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, st, a); }
-  else { ProfScope ps_(p, "topk_select", st); hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, st, a); }
+  if (need <= 16) { ProfEvents pe(p, "topk_select"); hipExtLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, pe.start, pe.stop, 0, a); }
+  else if (need <= 32) { ProfEvents pe(p, "topk_select"); hipExtLaunchKernelGGL(topk_kernel<32>, grid, block, 0, st, pe.start, pe.stop, 0, a); }
+  else { ProfEvents pe(p, "topk_select"); hipExtLaunchKernelGGL(topk_kernel<64>, grid, block, 0, st, pe.start, pe.stop, 0, a); }
   return hipGetLastError();
 }
 
