@@ -268,7 +268,8 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
   const int64_t Hkv = d.num_kv_heads, Hq = d.num_qo_heads, K = d.topk;
   if (d.mode == MSA_PREFILL) {
     p->tokens_per_chunk = 128 / G;
-    p->entries_per_item = p->tokens_per_chunk * 16;  // 16 chunks of 128 query rows per K/V load
+    // up to 16 chunks of 128 query rows per K/V load, at most 512 entries (LDS staging)
+    p->entries_per_item = std::min(512, p->tokens_per_chunk * 16);
     // attention window: rows whose partials live at once.  Larger windows
     // give each (block, group) more rows per K/V load and fewer launches;
     // by default up to 32768 rows, capped at 16 GiB of partials.

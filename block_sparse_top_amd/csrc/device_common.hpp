@@ -75,6 +75,17 @@ __device__ __forceinline__ void lds_store16(void* p, const T& v) {
   *(MSA_LDS T*)(p) = v;
 }
 
+__device__ __forceinline__ void lds_store8(void* p, const i32x2& v) { *(MSA_LDS i32x2*)(p) = v; }
+
+// Order one wave's LDS writes before its following LDS reads of other lanes'
+// data (a wave executes in lockstep and its LDS operations complete in order;
+// the fences keep the compiler from moving accesses across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // global_load_lds_dwordx4: each lane's 16 bytes at `g` land at LDS
 // `l + 16 * lane` (l is wave-uniform; it goes through M0).  The body exists
 // only in the device pass (the builtin has no host meaning).

@@ -26,8 +26,15 @@
 namespace msa {
 namespace {
 
-constexpr int kKRow = 272;  // LDS bytes per K row (256 + 16: spreads 16-byte reads over banks)
-constexpr int kVRow = 320;  // LDS bytes per V row (256 + 64: spreads transposed 8-byte reads)
+// K and V sit in LDS as unpadded 256-byte rows whose 16-byte chunks are
+// XOR-swizzled by row.  K: chunk c of row r at c ^ (r & 15), so each 16 lanes
+// of an MFMA operand read (16 rows, one column chunk) hit 16 distinct chunk
+// positions.  V: chunk c at c ^ 4 (r & 3), so the 8 rows x 4 chunks of a
+// transposed read cover every bank exactly twice.  The per-lane part of each
+// read address is computed once (8 K bases, one per 32-byte column step; 4 V
+// bases, one per 32-column tile) and the row offsets become immediates.
+__device__ __forceinline__ int k_swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int v_swz(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 2)) << 4); }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
@@ -153,11 +160,13 @@ struct PartialArgs {
   float scale_log2;      // sm_scale * log2(e)
 };
 
-constexpr int kMaxItemEntries = 2048;  // entries_per_item = 16 chunks of 128 / G tokens
+constexpr int kMaxItemEntries = 512;   // entries_per_item = min(512, 16 chunks of 128 / G tokens)
+constexpr int kOStage = 32 * 64;       // output staging per wave: 32 rows x 32 bf16 columns
 
 __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * kKRow];
-  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * kVRow];
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
   __shared__ int32_t ent_s[kMaxItemEntries];
   const int item = blockIdx.x;
   if (item >= *a.nitems) return;
@@ -186,9 +195,9 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + 256 * i;
-      lds_store16<i32x4>(&ks[(c >> 4) * kKRow + (c & 15) * 16], kr[i]);
+      lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], kr[i]);
       // padding may hold anything; P is 0 there but 0 * NaN is NaN
-      lds_store16<i32x4>(&vs[(c >> 4) * kVRow + (c & 15) * 16], (c >> 4) < kv_in_block ? vr[i] : i32x4{});
+      lds_store16<i32x4>(&vs[v_swz(c >> 4, c & 15)], (c >> 4) < kv_in_block ? vr[i] : i32x4{});
     }
   }
   __syncthreads();
@@ -201,6 +210,18 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   const int hh = qr % G, tok = qr / G;
   const int h = g * G + hh;
   const int nchunks = (n_ent + MT - 1) / MT;
+  // K row 32 kt + (lane & 31), column chunk 2 st + half: kbase[st] + 8192 kt
+  int kbase[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) kbase[st] = (lane & 31) * 256 + (((2 * st + half) ^ (lane & 15)) << 4);
+  // V row 32 kt + 16 u + 4 (q16 >> 1) + (m16 >> 2) (+ 8), bytes 64 dt + 32 (q16 & 1)
+  // + 8 (m16 & 3): vbase[dt] + 256 (32 kt + 16 u) (+ 2048)
+  int vbase[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
+                ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  uint8_t* ow = ost + wave * kOStage;
 
   // Q fragments (B operand) of a chunk's row for this lane: gathered rows
   auto load_q = [&](bf16x8 (&qf)[8], int chunk) {
@@ -211,12 +232,9 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
   };
 
-  bf16x8 qn[8];
-  load_q(qn, 0);
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    bf16x8 qf[8];
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = qn[st];
+  // One 128-row chunk: S^T = K Q^T, causal mask, softmax, O^T = V^T P^T,
+  // normalised bf16 partial and log-sum-exp out.
+  auto process = [&](const bf16x8 (&qf)[8], int chunk) __attribute__((always_inline)) {
     const int e = chunk * MT + tok;
     const bool valid = e < n_ent;
     const int ent = ent_s[valid ? e : 0];
@@ -229,13 +247,11 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     for (int st = 0; st < 8; ++st) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 af = lds_load16<bf16x8>(&ks[(32 * kt + (lane & 31)) * kKRow + st * 32 + half * 16]);
+        const bf16x8 af = lds_load16<bf16x8>(&ks[kbase[st] + 8192 * kt]);
         acc[kt] = mfma32x32x16(af, qf[st], acc[kt]);
       }
       if (st & 1) __builtin_amdgcn_sched_barrier(0);
     }
-    // the next chunk's gathered Q rows are in flight during softmax and P.V
-    if (chunk + 1 < nchunks) load_q(qn, chunk + 1);
 
     // causal mask (keys past the row's position), row max
     const int lim = pos - b * 128 - 4 * half;
@@ -277,33 +293,70 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int key0 = 32 * kt + 16 * u + 4 * (q16 >> 1);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const int d0 = 32 * dt + 16 * (q16 & 1);
-          const s16x4 lo = lds_read_tr16(&vs[(key0 + (m16 >> 2)) * kVRow + (d0 + 4 * (m16 & 3)) * 2]);
-          const s16x4 hi = lds_read_tr16(&vs[(key0 + 8 + (m16 >> 2)) * kVRow + (d0 + 4 * (m16 & 3)) * 2]);
+          const s16x4 lo = lds_read_tr16(&vs[vbase[dt] + 256 * (32 * kt + 16 * u)]);
+          const s16x4 hi = lds_read_tr16(&vs[vbase[dt] + 256 * (32 * kt + 16 * u + 8)]);
           oacc[dt] = mfma32x32x16(join_tr16(lo, hi), pf[kt][u], oacc[dt]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of transposed reads
     }
-    if (valid) {
-      const float inv = 1.f / sum;
-      const int64_t pi = ((int64_t)rl * a.Hq + h) * a.k + slot;
-      uint16_t* orow = a.part_o + pi * 128;
+    // Output: each 32 x 32 tile of O (this wave's rows, 32 columns) goes
+    // through the wave's LDS staging area so that every store instruction
+    // writes 16 rows x 64 contiguous bytes.  Staged row j holds its 4 16-byte
+    // chunks at c ^ ((j >> 2) & 3): the 8-byte writes of a tile land on every
+    // bank exactly twice.
+    const float inv = 1.f / sum;
+    int64_t spi[2];
+    bool sval[2];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const bf16x2 lo2 = {(__bf16)(oacc[dt][4 * gq] * inv), (__bf16)(oacc[dt][4 * gq + 1] * inv)};
-          const bf16x2 hi2 = {(__bf16)(oacc[dt][4 * gq + 2] * inv), (__bf16)(oacc[dt][4 * gq + 3] * inv)};
-          const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
-          *reinterpret_cast<i32x2*>(orow + 32 * dt + 8 * gq + 4 * half) = pk;
-        }
-      }
-      if (half == 0) a.part_lse[pi] = (mx * a.scale_log2 + fast_log2(sum)) * kLn2;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int srow = 32 * wave + 16 * pass + (lane >> 2);
+      const int se = chunk * MT + srow / G;
+      sval[pass] = se < n_ent;
+      const int sent = ent_s[sval[pass] ? se : 0];
+      spi[pass] = ((int64_t)(sent / a.k) * a.Hq + g * G + srow % G) * a.k + sent % a.k;
     }
+    const int jrow = lane & 31;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const bf16x2 lo2 = {(__bf16)(oacc[dt][4 * gq] * inv), (__bf16)(oacc[dt][4 * gq + 1] * inv)};
+        const bf16x2 hi2 = {(__bf16)(oacc[dt][4 * gq + 2] * inv), (__bf16)(oacc[dt][4 * gq + 3] * inv)};
+        const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+        lds_store8(&ow[jrow * 64 + ((gq ^ ((jrow >> 2) & 3)) << 4) + 8 * half], pk);
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int r = 16 * pass + (lane >> 2), c = lane & 3;
+        const i32x4 v = lds_load16<i32x4>(&ow[r * 64 + ((c ^ ((r >> 2) & 3)) << 4)]);
+        if (sval[pass]) *reinterpret_cast<i32x4*>(a.part_o + spi[pass] * 128 + 32 * dt + 8 * c) = v;
+      }
+      wave_lds_sync();
+    }
+    if (valid && half == 0) {
+      const int64_t pi = ((int64_t)rl * a.Hq + h) * a.k + slot;
+      a.part_lse[pi] = (mx * a.scale_log2 + fast_log2(sum)) * kLn2;
+    }
+  };
+
+  // Two register buffers of gathered Q rows: the next chunk's loads are
+  // issued before the current chunk's work, a whole chunk ahead of their use.
+  bf16x8 qa[8], qb[8];
+  load_q(qa, 0);
+  for (int chunk = 0; chunk < nchunks; chunk += 2) {
+    if (chunk + 1 < nchunks) load_q(qb, chunk + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    process(qa, chunk);
+    __builtin_amdgcn_sched_barrier(0);
+    if (chunk + 1 >= nchunks) break;
+    if (chunk + 2 < nchunks) load_q(qa, chunk + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    process(qb, chunk + 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
