@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
       const int b = row[slot];
       if (b < 0 || b > local) continue;
       if (!FILL) atomicAdd(&counts[pb + b], 1);
-      else a.entries[offsets[pb + b] + atomicAdd(&cursor[pb + b], 1)] = rl * a.k + slot;
+      else a.entries[offsets[pb + b] + atomicAdd(&cursor[pb + b], 1)] = (rl << 6) | slot;
     }
     return;
   } else {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
     if (valid)
       for (int slot = 0; slot < a.k; ++slot) {
         const int b = row[slot];
-        if (b >= 0 && b <= local) a.entries[atomicAdd(&hist[pb + b], 1)] = rl * a.k + slot;
+        if (b >= 0 && b <= local) a.entries[atomicAdd(&hist[pb + b], 1)] = (rl << 6) | slot;
       }
   }
 }
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   // Q fragments (B operand) of a chunk's row for this lane: gathered rows
   auto load_q = [&](bf16x8 (&qf)[8], int chunk) {
     const int e = min(chunk * MT + tok, n_ent - 1);
-    const int32_t r = a.w0 + ent_s[e] / a.k;
+    const int32_t r = a.w0 + (ent_s[e] >> 6);
     const uint8_t* qrow = a.q + ((int64_t)r * a.Hq + h) * 256 + half * 16;
 #pragma unroll
     for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     const int e = chunk * MT + tok;
     const bool valid = e < n_ent;
     const int ent = ent_s[valid ? e : 0];
-    const int rl = ent / a.k, slot = ent % a.k;
+    const int rl = ent >> 6, slot = ent & 63;
     const int32_t pos = first_pos + (a.w0 + rl - rs);
 
     // S^T = K Q^T: 4 key tiles of 32
@@ -253,18 +253,29 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       if (st & 1) __builtin_amdgcn_sched_barrier(0);
     }
 
-    // causal mask (keys past the row's position), row max
-    const int lim = pos - b * 128 - 4 * half;
+    // Scores scaled first (products are canonical, so the max needs no NaN
+    // quieting).  Only a row's own (diagonal) block needs the causal mask:
+    // tiles whose every row sees the whole block take the branch without it.
+    const int lim = pos - b * 128 - 4 * half;  // last visible key offset, minus this lane's 4-key shift
+    float sc[4][16];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[kt][i] = acc[kt][i] * a.scale_log2;
     float mx = kNegInf;
+    if (__builtin_amdgcn_ballot_w64(lim < 124) == 0) {  // 124 + 3: the last key offset a lane holds
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int koff = 32 * kt + 8 * (i >> 2) + (i & 3);
-        const float v = koff <= lim ? acc[kt][i] : kNegInf;
-        acc[kt][i] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[kt][i], sc[kt][i + 1]));
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) sc[kt][i] = kNegInf;
+          mx = fmaxf(mx, sc[kt][i]);
+        }
     }
     mx = fmaxf(mx, wave_xor32(mx));
     float sum = 0.f;
@@ -276,8 +287,8 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
         i32x4 pw;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float p0 = fast_exp2((acc[kt][8 * u + 2 * t] - mx) * a.scale_log2);
-          const float p1 = fast_exp2((acc[kt][8 * u + 2 * t + 1] - mx) * a.scale_log2);
+          const float p0 = fast_exp2(sc[kt][8 * u + 2 * t] - mx);
+          const float p1 = fast_exp2(sc[kt][8 * u + 2 * t + 1] - mx);
           sum += p0 + p1;
           const bf16x2 two = {(__bf16)p0, (__bf16)p1};
           pw[t] = __builtin_bit_cast(int, two);
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       const int se = chunk * MT + srow / G;
       sval[pass] = se < n_ent;
       const int sent = ent_s[sval[pass] ? se : 0];
-      spi[pass] = ((int64_t)(sent / a.k) * a.Hq + g * G + srow % G) * a.k + sent % a.k;
+      spi[pass] = ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63);
     }
     const int jrow = lane & 31;
 #pragma unroll
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     }
     if (valid && half == 0) {
       const int64_t pi = ((int64_t)rl * a.Hq + h) * a.k + slot;
-      a.part_lse[pi] = (mx * a.scale_log2 + fast_log2(sum)) * kLn2;
+      a.part_lse[pi] = (mx + fast_log2(sum)) * kLn2;  // mx is already scaled
     }
   };
 
