@@ -1,7 +1,8 @@
 """Benchmark of the MSA forward path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-for prefill, proxy block max scores and top-k selection over every row chunk,
+for prefill, the block selection (the fused proxy + top-k pass when topk <= 17,
+else proxy block max scores and top-k over every row chunk),
 then the block-sparse attention; for decode, one sparse decode call.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ...]
@@ -33,7 +34,8 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
-    "proxy_maxscore": "proxy_maxscore.hip", "topk_select": "topk_select.hip", "csr": "sparse_prefill.hip",
+    "proxy_maxscore": "proxy_maxscore.hip", "topk_select": "topk_select.hip", "proxy_topk": "proxy_maxscore.hip",
+    "csr": "sparse_prefill.hip",
     "partial_attn": "sparse_prefill.hip", "merge": "sparse_prefill.hip", "decode": "sparse_decode.hip",
     "decode_merge": "sparse_decode.hip",
 }
@@ -298,7 +300,8 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
 
     step()
     torch.cuda.synchronize()
-    per_kernel = kernel_profile(msa, plan, step, ["proxy_maxscore", "topk_select", "csr", "partial_attn", "merge"])
+    stages = (["proxy_topk"] if w.topk <= 17 else ["proxy_maxscore", "topk_select"]) + ["csr", "partial_attn", "merge"]
+    per_kernel = kernel_profile(msa, plan, step, stages)
     dominant = max(per_kernel, key=lambda n: per_kernel[n][0])
     ms_step, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, dominant)
     launches_per_step = launches // steps
@@ -308,7 +311,7 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
     f_proxy = proxy_flops(w.qo_lens, w.kv_lens, w.num_proxy_heads)
     proxy_peak = PEAK_FP8_TFLOPS if w.proxy_dtype == "fp8" else PEAK_BF16_TFLOPS
     # work per launch of the dominant kernel (launches cover equal shares of a step)
-    if dominant == "proxy_maxscore":
+    if dominant in ("proxy_maxscore", "proxy_topk"):
         work, peak, unit, bound = f_proxy / launches_per_step, proxy_peak, "TFLOP/s", "mfma"
     elif dominant == "partial_attn":
         work, peak, unit, bound = f_main / launches_per_step, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"

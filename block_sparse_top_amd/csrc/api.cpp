@@ -106,8 +106,8 @@ hipEvent_t take_event(msa::Profiler& pr) {
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
 }
-const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "csr", "partial_attn", "merge", "decode",
-                                    "decode_merge"};
+const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "proxy_topk", "csr", "partial_attn", "merge",
+                                    "decode", "decode_merge"};
 }  // namespace
 
 ProfEvents::ProfEvents(const msa_plan_s* p, const char* name) {
@@ -347,7 +347,41 @@ msa_status_t msa_proxy_block_maxscore(msa_plan_t p, const void* proxy_q, const v
   while (hi > lo && p->tiles[4 * (hi - 1) + 1] >= row_begin + row_count) --hi;
   const msa::DevMeta m = msa::dev_meta(p, workspace);
   return hip_status(msa::launch_proxy_maxscore(p, m, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale,
-                                               kv_indices, lo, hi, row_begin, row_count, max_score, hs),
+                                               kv_indices, lo, hi, row_begin, row_count, max_score, nullptr, hs),
+                    __func__);
+}
+
+msa_status_t msa_proxy_topk_select(msa_plan_t p, const void* proxy_q, const void* proxy_k_pages,
+                                   const float* proxy_q_scale, const float* proxy_k_scale,
+                                   const int32_t* kv_indices, int64_t row_begin, int64_t row_count,
+                                   int32_t* kv_block_indexes, void* workspace, size_t workspace_bytes,
+                                   msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_proxy_topk_select: NULL plan");
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_proxy_topk_select: decode plan");
+  if (p->d.topk > 17)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_proxy_topk_select: topk %d > 17; use msa_proxy_block_maxscore + msa_topk_select",
+                p->d.topk);
+  MSA_CHECK_PTR(proxy_q);
+  MSA_CHECK_PTR(proxy_k_pages);
+  MSA_CHECK_PTR(kv_indices);
+  MSA_CHECK_PTR(kv_block_indexes);
+  const bool fp8 = p->d.proxy_dtype == MSA_FP8_E4M3;
+  if (fp8 != (proxy_q_scale != nullptr) || fp8 != (proxy_k_scale != nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "msa_proxy_topk_select: scale pointers must be given iff the proxy dtype is fp8");
+  if (row_count < 1 || row_begin < 0 || row_begin + row_count > p->T)
+    return fail(MSA_ERR_INVALID_ARG, "msa_proxy_topk_select: rows [%lld, %lld) outside [0, %lld)", (long long)row_begin,
+                (long long)(row_begin + row_count), (long long)p->T);
+  msa_status_t st = check_ws(p, workspace, workspace_bytes);
+  if (st != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  int32_t lo = 0, hi = p->ntiles;
+  while (lo < p->ntiles && p->tiles[4 * lo + 1] + p->tiles[4 * lo + 2] <= row_begin) ++lo;
+  while (hi > lo && p->tiles[4 * (hi - 1) + 1] >= row_begin + row_count) --hi;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  return hip_status(msa::launch_proxy_maxscore(p, m, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale,
+                                               kv_indices, lo, hi, row_begin, row_count, nullptr, kv_block_indexes,
+                                               hs),
                     __func__);
 }
 

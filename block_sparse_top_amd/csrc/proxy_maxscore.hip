@@ -1,4 +1,5 @@
-// Stage 1 of MSA: proxy block max scores.
+// Stage 1 of MSA: proxy block max scores, and optionally the top-k block
+// selection fused into the same pass.
 //
 // The proxy pass of the MiniMax-AI/MSA README (section "Usage": dense pass,
 // output_o off, output_maxscore on) and the max-pooling of proxy scores over
@@ -42,9 +43,17 @@ struct ProxyArgs {
   int32_t tile_lo, ntiles;
   int32_t P, Pk, nb_max;
   int64_t row_begin, row_end, row_count;
-  float* out;                // [P, nb_max, row_count]
+  float* out;                // [P, nb_max, row_count] (block max scores) or null
+  int32_t* sel;              // [T, P, k] selections when fused with top-k, else null
+  int32_t k;                 // slots per (row, group), local block included (fused path)
   float scale;
 };
+
+// Fused selection: each lane keeps its row's best kSelCap (score, block)
+// pairs in descending score order.  Blocks arrive in ascending order and an
+// equal score never displaces a listed one, so ties go to the lower block,
+// exactly as in the separate top-k over the same fp32 scores.
+constexpr int kSelCap = 16;
 
 template <bool FP8>
 struct ProxyTraits;
@@ -109,7 +118,7 @@ __device__ __forceinline__ f32x16 mma(const typename ProxyTraits<FP8>::Frag& a,
 
 constexpr int kProxyWaves = 8;
 
-template <bool FP8>
+template <bool FP8, bool TOPK>
 __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyArgs a) {
   using Tr = ProxyTraits<FP8>;
   using Frag = typename Tr::Frag;
@@ -228,10 +237,42 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
       }
     }
   };
+  const int my_local = (pos0 + my_row) >> 7;   // this lane's row's local block
+  float tv[TOPK ? kSelCap : 1];
+  int ti[TOPK ? kSelCap : 1];
+#pragma unroll
+  for (int j = 0; j < (TOPK ? kSelCap : 1); ++j) {
+    tv[j] = kNegInf;
+    ti[j] = -1;
+  }
   auto finish = [&](int b, float (&m)[2]) {
     m[0] = fmaxf(m[0], wave_xor32(m[0]));
     m[1] = fmaxf(m[1], wave_xor32(m[1]));
-    if (writes) outp[(int64_t)b * a.row_count] = (lane < 32 ? m[0] : m[1]) * scale;
+    const float v = (lane < 32 ? m[0] : m[1]) * scale;
+    if constexpr (TOPK) {
+      // blocks before the local one compete (the local block is forced)
+      if (b < my_local) {
+        // insert before the first strictly smaller score, then shift the
+        // rest down one slot unconditionally (a displaced entry must not be
+        // compared again: it would pass an equal score with a larger id)
+        float cv = v;
+        int ci = b;
+        bool shifting = false;
+#pragma unroll
+        for (int j = 0; j < kSelCap; ++j) {
+          const bool mv = shifting || cv > tv[j];
+          const float ov = tv[j];
+          const int oi = ti[j];
+          tv[j] = mv ? cv : ov;
+          ti[j] = mv ? ci : oi;
+          cv = mv ? ov : cv;
+          ci = mv ? oi : ci;
+          shifting = mv;
+        }
+      }
+    } else {
+      if (writes) outp[(int64_t)b * a.row_count] = v;
+    }
   };
 
   // Page ids: lane i holds page (64*w + i) of window w; the next window is
@@ -281,6 +322,31 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
       __syncthreads();
     }
   }
+
+  if constexpr (TOPK) {
+    // the R = min(k - 1, local) best earlier blocks and the local block, ascending, -1 padded
+    if (writes) {
+      const int R = min(a.k - 1, my_local);
+#pragma unroll
+      for (int j = 0; j < kSelCap; ++j)
+        if (j >= R) ti[j] = 0x7fffffff;
+#pragma unroll
+      for (int rnd = 0; rnd < kSelCap; ++rnd)  // odd-even transposition sort by block id
+#pragma unroll
+        for (int j = rnd & 1; j + 1 < kSelCap; j += 2) {
+          const int x = ti[j], y = ti[j + 1];
+          ti[j] = min(x, y);
+          ti[j + 1] = max(x, y);
+        }
+      int32_t* dst = a.sel + ((int64_t)my_grow * a.P + p) * a.k;
+#pragma unroll
+      for (int j = 0; j <= kSelCap; ++j) {
+        if (j >= a.k) break;
+        const int v = j < R ? ti[j < kSelCap ? j : 0] : (j == R ? my_local : -1);
+        dst[j] = v;
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -288,7 +354,7 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
 hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const void* pq, const void* pk,
                                  const float* qs, const float* ks, const int32_t* kv_indices, int32_t tile_lo,
                                  int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
-                                 hipStream_t st) {
+                                 int32_t* sel, hipStream_t st) {
   if (tile_hi <= tile_lo) return hipSuccess;
   ProxyArgs a;
   a.pq = static_cast<const uint8_t*>(pq);
@@ -307,12 +373,19 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
   a.row_end = row_begin + row_count;
   a.row_count = row_count;
   a.out = max_score;
+  a.sel = sel;
+  a.k = p->d.topk;
   a.scale = p->d.proxy_sm_scale;
   const dim3 grid((unsigned)(a.ntiles * a.P)), block(64 * kProxyWaves);
-  if (p->d.proxy_dtype == MSA_FP8_E4M3) {
-    { ProfEvents pe(p, "proxy_maxscore"); hipExtLaunchKernelGGL(proxy_maxscore_kernel<true>, grid, block, 0, st, pe.start, pe.stop, 0, a); }
+  const bool fp8 = p->d.proxy_dtype == MSA_FP8_E4M3;
+  if (sel) {
+    ProfEvents pe(p, "proxy_topk");
+    if (fp8) hipExtLaunchKernelGGL((proxy_maxscore_kernel<true, true>), grid, block, 0, st, pe.start, pe.stop, 0, a);
+    else hipExtLaunchKernelGGL((proxy_maxscore_kernel<false, true>), grid, block, 0, st, pe.start, pe.stop, 0, a);
   } else {
-    { ProfEvents pe(p, "proxy_maxscore"); hipExtLaunchKernelGGL(proxy_maxscore_kernel<false>, grid, block, 0, st, pe.start, pe.stop, 0, a); }
+    ProfEvents pe(p, "proxy_maxscore");
+    if (fp8) hipExtLaunchKernelGGL((proxy_maxscore_kernel<true, false>), grid, block, 0, st, pe.start, pe.stop, 0, a);
+    else hipExtLaunchKernelGGL((proxy_maxscore_kernel<false, false>), grid, block, 0, st, pe.start, pe.stop, 0, a);
   }
   return hipGetLastError();
 }

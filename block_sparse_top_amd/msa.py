@@ -23,6 +23,7 @@ MSA_BF16, MSA_FP8_E4M3 = 0, 1
 MSA_PREFILL, MSA_DECODE = 0, 1
 
 ENTRY_POINTS = ("msa_plan", "msa_plan_destroy", "msa_plan_info", "msa_proxy_block_maxscore", "msa_topk_select",
+               "msa_proxy_topk_select",
                 "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_last_error", "msa_profile_kernel",
                 "msa_profile_read")
 
@@ -68,6 +69,7 @@ def _load() -> ctypes.CDLL:
                                   ctypes.POINTER(ctypes.c_int64)]
     lib.msa_proxy_block_maxscore.argtypes = [P, VP, VP, FP, FP, IP, I64, I64, FP, VP, SZ, P]
     lib.msa_topk_select.argtypes = [P, FP, I64, I64, IP, VP, SZ, P]
+    lib.msa_proxy_topk_select.argtypes = [P, VP, VP, FP, FP, IP, I64, I64, IP, VP, SZ, P]
     lib.msa_sparse_attn_prefill.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
     lib.msa_sparse_attn_decode.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
     lib.msa_profile_kernel.argtypes = [P, ctypes.c_char_p]
@@ -170,6 +172,14 @@ def msa_topk_select(plan: Plan, max_score, row_begin: int, row_count: int, kv_bl
     return kv_block_indexes
 
 
+def msa_proxy_topk_select(plan: Plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale, kv_indices,
+                          row_begin: int, row_count: int, kv_block_indexes) -> torch.Tensor:
+    _check(_lib.msa_proxy_topk_select(plan.handle, _ptr(proxy_q), _ptr(proxy_k_pages), _ptr(proxy_q_scale),
+                                      _ptr(proxy_k_scale), _ptr(kv_indices), row_begin, row_count,
+                                      _ptr(kv_block_indexes), _ptr(plan.workspace), plan.workspace_bytes, _stream()))
+    return kv_block_indexes
+
+
 def msa_sparse_attn_prefill(plan: Plan, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse=None,
                             k_scale=None, v_scale=None):
     _check(_lib.msa_sparse_attn_prefill(plan.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
@@ -205,10 +215,18 @@ def max_score_buffer(plan: Plan, device=None) -> torch.Tensor:
 
 
 def run_prefill(plan: Plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale, q, k_pages, v_pages, kv_indices,
-                kv_block_indexes, out, lse=None, max_score=None):
-    """The whole prefill path: proxy block max scores and top-k selection
-    chunk by chunk of rows, then the sparse attention."""
+                kv_block_indexes, out, lse=None, max_score=None, fused=None):
+    """The whole prefill path: the block selection (the fused proxy + top-k
+    pass when topk <= 17, else proxy max scores and top-k chunk by chunk of
+    rows), then the sparse attention."""
     T, R = plan.total_rows, plan.max_rows_per_call
+    if fused is None:
+        fused = plan.desc.topk <= 17
+    if fused:
+        msa_proxy_topk_select(plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale, kv_indices, 0, T,
+                              kv_block_indexes)
+        msa_sparse_attn_prefill(plan, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse)
+        return out, lse
     if max_score is None:
         max_score = max_score_buffer(plan, q.device)
     for r0 in range(0, T, R):

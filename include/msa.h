@@ -12,6 +12,8 @@
  *   2. msa_topk_select          - per (row, KV group) the `topk` best blocks,
  *      the row's own (local) block always kept (Flash-MSA article, paragraph
  *      on the forward kernels).
+ *      msa_proxy_topk_select runs 1 and 2 as one pass, keeping each row's
+ *      best blocks in registers instead of writing max_score.
  *   3. msa_sparse_attn_prefill  - GQA attention over only the selected blocks
  *      of a paged K/V cache (README "Usage": kv_block_indexes argument),
  *      msa_sparse_attn_decode   - its one-token-per-sequence paged decode
@@ -147,6 +149,24 @@ msa_status_t msa_topk_select(msa_plan_t plan, const float* max_score, int64_t ro
                              int32_t* kv_block_indexes, void* workspace, size_t workspace_bytes,
                              msa_stream_t stream);
 
+/* Stages 1 and 2 fused: the proxy pass keeps each row's best blocks as it
+ * goes and writes the selection directly, with no max_score round trip (the
+ * streaming selection with an in-register insertion sort that the Flash-MSA
+ * article describes for its proxy attention, paragraph on the forward
+ * kernels).  The result equals msa_proxy_block_maxscore followed by
+ * msa_topk_select on the same inputs, bit for bit (same fp32 scores, same
+ * tie rule).
+ *
+ * Arguments as in stages 1 and 2; rows [row_begin, row_begin + row_count)
+ * may span the whole batch (no max_rows_per_call limit: nothing is staged).
+ * Errors: as stage 1; UNSUPPORTED if the plan's topk exceeds 17 (at most 16
+ * competing blocks are kept per row; use the two separate calls then). */
+msa_status_t msa_proxy_topk_select(msa_plan_t plan, const void* proxy_q, const void* proxy_k_pages,
+                                   const float* proxy_q_scale, const float* proxy_k_scale,
+                                   const int32_t* kv_indices, int64_t row_begin, int64_t row_count,
+                                   int32_t* kv_block_indexes, void* workspace, size_t workspace_bytes,
+                                   msa_stream_t stream);
+
 /* Stage 3a: block-sparse GQA prefill attention (README "Usage", attention
  * run with kv_block_indexes; Flash-MSA article: GQA main attention,
  * block-sparse flash attention reformulated as variable-length attention).
@@ -193,10 +213,11 @@ const char* msa_last_error(void);
 msa_status_t msa_plan_info(msa_plan_t plan, int64_t* total_rows, int32_t* nb_max, int64_t* max_rows_per_call);
 
 /* Diagnostics, not part of the path.  When `kernel` names one of the
- * library's internal kernels ("proxy_maxscore", "topk_select", "csr",
+ * library's internal kernels ("proxy_maxscore", "topk_select", "proxy_topk", "csr",
  * "partial_attn", "merge", "decode", "decode_merge"), each later launch of it
- * for this plan is bracketed by two HIP events recorded on the call's stream
- * (events are created on first use and reused; no device memory).  NULL
+ * for this plan carries two HIP events that the runtime stamps with the
+ * dispatch's begin and end (events are created on first use and reused; no
+ * device memory).  NULL
  * switches it off.  msa_profile_read waits for the recorded events, returns
  * the summed kernel time in milliseconds and the number of launches, and
  * clears the record.  Errors: INVALID_ARG for an unknown name; HIP. */

@@ -126,4 +126,16 @@ def test_compute_calls_validate_before_touching_the_device():
     # fp8 decode needs both scales
     assert L.msa_sparse_attn_decode(d.handle, a, a, a, a, none, a, a, a, none, ws, d.workspace_bytes, none) == msa.MSA_ERR_INVALID_ARG
     assert L.msa_proxy_block_maxscore(d.handle, a, a, none, none, a, 0, 1, a, ws, d.workspace_bytes, none) == msa.MSA_ERR_UNSUPPORTED
+    # fused proxy + top-k: the same checks, no row-chunk bound, topk <= 17
+    T = p.total_rows
+    assert L.msa_proxy_topk_select(p.handle, a, a, none, none, a, 0, 10, none, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_proxy_topk_select(p.handle, a, a, none, none, a, T - 5, 10, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_proxy_topk_select(p.handle, a, a, a, a, a, 0, 10, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_proxy_topk_select(p.handle, a, a, none, none, a, 0, 10, a, ws, nb - 1, none) == \
+        msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    assert L.msa_proxy_topk_select(d.handle, a, a, none, none, a, 0, 1, a, ws, d.workspace_bytes, none) == \
+        msa.MSA_ERR_UNSUPPORTED
+    big = msa.msa_plan([100], [100], 8, 2, 2, 2, topk=18, allocate=False)
+    assert L.msa_proxy_topk_select(big.handle, a, a, none, none, a, 0, 10, a, ws, big.workspace_bytes, none) == \
+        msa.MSA_ERR_UNSUPPORTED and b"topk" in L.msa_last_error()
     assert L.msa_plan_destroy(None) == msa.MSA_OK

@@ -57,6 +57,12 @@ def _prefill_case(n_cfg, n_even):
         here = np.nonzero((rows >= r0) & (rows < r0 + n))[0]
         if here.size:
             got_ms[:, :, here] = ms[:, :, torch.from_numpy(rows[here] - r0).cuda()].cpu().numpy()
+    if w.topk <= 17:  # the fused pass (what run_prefill uses) selects exactly the same blocks, every row
+        fsel = torch.full_like(sel, -7)
+        msa.msa_proxy_topk_select(plan, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale,
+                                  inp.kv_indices, 0, T, fsel)
+        assert torch.equal(fsel, sel), f"{w.name}: fused selection differs in {int((fsel != sel).any(dim=2).sum())} rows"
+        del fsel
     out = torch.empty((T, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((T, w.num_qo_heads), dtype=torch.float32, device="cuda")
     msa.msa_sparse_attn_prefill(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, lse)

@@ -88,6 +88,35 @@ def test_prefill_stages_match_oracle(case):
     assert np.abs(glse - ref_lse).max() < 1e-3, case
 
 
+@pytest.mark.parametrize("case", list(PREFILL_CASES))
+def test_fused_proxy_topk_equals_separate_calls(case):
+    """msa_proxy_topk_select must give, bit for bit, the selection of
+    msa_proxy_block_maxscore + msa_topk_select (same fp32 scores, same tie
+    rule), and that selection passes the band rule against the oracle."""
+    msa = _msa()
+    w, seed, max_rows = PREFILL_CASES[case]
+    inp = make_inputs(w, seed)
+    print(f"[parity] fused proxy+topk case={case} T={w.total_rows} seed={seed}", flush=True)
+    gms, gsel, _, _ = run_prefill_stages(msa, inp, max_rows)
+    d = device_inputs(inp)
+    plan = plan_for(msa, inp, max_rows_per_call=max_rows)
+    T = w.total_rows
+    sel = torch.full((T, w.num_kv_heads, w.topk), -7, dtype=torch.int32, device="cuda")
+    msa.msa_proxy_topk_select(plan, d["proxy_q"], d["proxy_k_pages"], d["proxy_q_scale"], d["proxy_k_scale"],
+                              d["kv_indices"], 0, T, sel)
+    fsel = sel.cpu().numpy()
+    assert np.array_equal(fsel, gsel), f"{case}: {int((fsel != gsel).any(axis=2).sum())} (row, group) differ"
+    # a sub-range writes only its rows
+    if T > 3:
+        r0, n = T // 3, max(1, T // 3)
+        sel2 = torch.full_like(sel, -7)
+        msa.msa_proxy_topk_select(plan, d["proxy_q"], d["proxy_k_pages"], d["proxy_q_scale"], d["proxy_k_scale"],
+                                  d["kv_indices"], r0, n, sel2)
+        s2 = sel2.cpu().numpy()
+        assert np.array_equal(s2[r0:r0 + n], gsel[r0:r0 + n]), case
+        assert (s2[:r0] == -7).all() and (s2[r0 + n:] == -7).all(), case
+
+
 def test_topk_exact_on_given_scores_with_ties():
     """The top-k kernel on fp32 scores with many exact ties must equal the
     oracle's selection bit for bit (same fp32 values, lower id wins)."""
