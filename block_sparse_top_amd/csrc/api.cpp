@@ -285,8 +285,9 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     L.items = off; off = align_up(off + L.max_items * 16, 256);
     L.nitems = off; off = align_up(off + 16, 256);
     L.entries = off; off = align_up(off + W * Hkv * K * 4, 256);
-    L.part_o = off; off = align_up(off + W * Hq * K * 128 * 2, 256);
-    L.part_lse = off; off = align_up(off + W * Hq * K * 4, 256);
+    // one extra slot at index W * Hq * K takes the stores of padding rows
+    L.part_o = off; off = align_up(off + (W * Hq * K + 1) * 128 * 2, 256);
+    L.part_lse = off; off = align_up(off + (W * Hq * K + 1) * 4, 256);
   } else {
     // one workgroup per (sequence, group) when that fills the GPU; otherwise
     // split each pair's 32-key slices over up to 8 workgroups

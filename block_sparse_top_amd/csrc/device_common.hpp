@@ -34,6 +34,7 @@ constexpr int kBlock = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_huge_valf();
 
 #define MSA_LDS __attribute__((address_space(3)))
 
@@ -65,6 +66,19 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32); }
 
+// max(a, b, c) as one v_max3_f32.  Written as an instruction because the
+// compiler otherwise quiets every operand it cannot prove canonical (one
+// extra v_max per matrix-core result); the operands here are finite or -inf.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+#else
+  return fmaxf(a, fmaxf(b, c));
+#endif
+}
+
 // Read 16 bytes from LDS.
 template <typename T>
 __device__ __forceinline__ T lds_load16(const void* p) {
@@ -92,6 +106,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ void global_load_lds16(const void* g, MSA_LDS void* l) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+#endif
+}
+
+// Wait for all outstanding vector memory operations only (loads and stores;
+// on this architecture one counter covers both, in issue order).
+__device__ __forceinline__ void wait_vmem() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // simm16: vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt [11:8] = 15 (no wait)
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 #endif
 }
 

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave branches stay scalar
   const int p = blockIdx.x % a.P;
   const int t = a.tile_lo + (a.ntiles - 1 - (int)(blockIdx.x / a.P));
   const int seq = a.tiles[4 * t + 0];
@@ -185,10 +185,44 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
   const bool writes = my_row < nrows && my_grow >= a.row_begin && my_grow < a.row_end;
   float* outp = a.out + (int64_t)p * a.nb_max * a.row_count + (my_grow - a.row_begin);
 
+  const int my_local = (pos0 + my_row) >> 7;   // this lane's row's local block
+  float tv[TOPK ? kSelCap : 1];
+  int ti[TOPK ? kSelCap : 1];
+#pragma unroll
+  for (int j = 0; j < (TOPK ? kSelCap : 1); ++j) {
+    tv[j] = kNegInf;
+    ti[j] = -1;
+  }
   const int chunk0 = ((lane >> 5) * (kStepBytes / 2)) >> 4;
-  // one block against this wave's 64 rows: key tiles in two halves of two
-  // (4 independent accumulator chains each), fragments one k-step ahead,
-  // then the (masked) max into the running block max of each row tile
+
+  // Fused selection: after each block, its score is inserted into the row's
+  // list, sorted by descending score with equal scores in ascending block
+  // order.  A new block has a larger id than every listed one, so inserting
+  // score v is a slot-parallel update (slots rewritten from the last to the
+  // first): slot j takes med3(old[j-1], v, old[j]) as its score, and keeps its
+  // block if v <= old[j], takes the new block if old[j-1] >= v > old[j], else
+  // the block of slot j-1 (strict compares: an equal listed score stays
+  // ahead, so ties keep the lower block id).
+  float pend_v = 0.f, cv = kNegInf;
+  int pend_b = 0, ci = 0;
+  bool pend_ok = false;
+  auto ins_begin = [&]() {
+    cv = pend_ok ? pend_v : kNegInf;  // -inf changes nothing
+    ci = pend_b;
+  };
+  auto ins_steps = [&](int r) {  // slots 15 - 4r down to 12 - 4r
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = kSelCap - 1 - (4 * r + jj);
+      const bool gj = cv > tv[j];
+      const bool gp = j > 0 ? cv > tv[j > 0 ? j - 1 : 0] : false;
+      const float up = j > 0 ? tv[j > 0 ? j - 1 : 0] : kPosInf;
+      const int upi = j > 0 ? ti[j > 0 ? j - 1 : 0] : 0;
+      ti[j] = gj ? (gp ? upi : ci) : ti[j];
+      tv[j] = __builtin_amdgcn_fmed3f(up, cv, tv[j]);
+    }
+  };
+
   auto block_max = [&](const uint8_t* tile, int b, float (&m)[2]) {
     m[0] = m[1] = kNegInf;
 #pragma unroll
@@ -223,8 +257,9 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              m[sub] = fmaxf(m[sub], (32 * (2 * hf + j) + 8 * (i >> 2) + (i & 3)) <= lim ? acc[j][sub][i] : kNegInf);
+            for (int i = 0; i < 16; i += 2)
+              m[sub] = max3f(m[sub], (32 * (2 * hf + j) + 8 * (i >> 2) + (i & 3)) <= lim ? acc[j][sub][i] : kNegInf,
+                             (32 * (2 * hf + j) + 8 * (i >> 2) + (i & 3) + 1) <= lim ? acc[j][sub][i + 1] : kNegInf);
         }
       } else {
 #pragma unroll
@@ -232,44 +267,23 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 16; i += 2)
-              m[sub] = __builtin_fmaxf(m[sub], __builtin_fmaxf(acc[j][sub][i], acc[j][sub][i + 1]));
+            for (int i = 0; i < 16; i += 2) m[sub] = max3f(m[sub], acc[j][sub][i], acc[j][sub][i + 1]);
       }
     }
   };
-  const int my_local = (pos0 + my_row) >> 7;   // this lane's row's local block
-  float tv[TOPK ? kSelCap : 1];
-  int ti[TOPK ? kSelCap : 1];
-#pragma unroll
-  for (int j = 0; j < (TOPK ? kSelCap : 1); ++j) {
-    tv[j] = kNegInf;
-    ti[j] = -1;
-  }
   auto finish = [&](int b, float (&m)[2]) {
     m[0] = fmaxf(m[0], wave_xor32(m[0]));
     m[1] = fmaxf(m[1], wave_xor32(m[1]));
     const float v = (lane < 32 ? m[0] : m[1]) * scale;
     if constexpr (TOPK) {
-      // blocks before the local one compete (the local block is forced)
-      if (b < my_local) {
-        // insert before the first strictly smaller score, then shift the
-        // rest down one slot unconditionally (a displaced entry must not be
-        // compared again: it would pass an equal score with a larger id)
-        float cv = v;
-        int ci = b;
-        bool shifting = false;
+      // blocks before the local one compete (the local block is forced);
+      // inserted during the next block
+      pend_v = v;
+      pend_b = b;
+      pend_ok = b < my_local;
+      ins_begin();
 #pragma unroll
-        for (int j = 0; j < kSelCap; ++j) {
-          const bool mv = shifting || cv > tv[j];
-          const float ov = tv[j];
-          const int oi = ti[j];
-          tv[j] = mv ? cv : ov;
-          ti[j] = mv ? ci : oi;
-          cv = mv ? ov : cv;
-          ci = mv ? oi : ci;
-          shifting = mv;
-        }
-      }
+      for (int r = 0; r < kSelCap / 4; ++r) ins_steps(r);
     } else {
       if (writes) outp[(int64_t)b * a.row_count] = v;
     }
@@ -294,34 +308,29 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
   };
 
   // block loop unrolled by two over the two tiles: block b computes from one
-  // tile while block b+1 streams into the other
+  // tile while block b+1 streams into the other; pairs run unconditionally
+  // and an odd last block follows the loop (no branch inside the loop body
+  // that the per-row selection state has to flow through)
+  auto step = [&](int b, const uint8_t* tile, uint8_t* next_tile) __attribute__((always_inline)) {
+    advance(b);
+    if (b + 1 <= b_last) kload(page_of(b + 1), next_tile);
+    float m[2];
+    if (wave_active) {
+      block_max(tile, b, m);
+      finish(b, m);
+    }
+    wait_all_mem();
+    __syncthreads();
+  };
   kload(page_of(0), lds0);
   wait_all_mem();
   __syncthreads();
-  for (int b = 0; b <= b_last; b += 2) {
-    {
-      advance(b);
-      if (b + 1 <= b_last) kload(page_of(b + 1), lds1);
-      float m[2];
-      if (wave_active) {
-        block_max(lds0, b, m);
-        finish(b, m);
-      }
-      wait_all_mem();
-      __syncthreads();
-    }
-    if (b + 1 <= b_last) {
-      advance(b + 1);
-      if (b + 2 <= b_last) kload(page_of(b + 2), lds0);
-      float m[2];
-      if (wave_active) {
-        block_max(lds1, b + 1, m);
-        finish(b + 1, m);
-      }
-      wait_all_mem();
-      __syncthreads();
-    }
+  int b = 0;
+  for (; b + 1 <= b_last; b += 2) {
+    step(b, lds0, lds1);
+    step(b + 1, lds1, lds0);
   }
+  if (b <= b_last) step(b, lds0, lds1);
 
   if constexpr (TOPK) {
     // the R = min(k - 1, local) best earlier blocks and the local block, ascending, -1 padded

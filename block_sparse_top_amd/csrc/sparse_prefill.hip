@@ -154,8 +154,9 @@ struct PartialArgs {
   const int4* items;
   const int32_t* nitems;
   DevMeta m;
-  uint16_t* part_o;      // [rows, Hq, k, 128] bf16
-  float* part_lse;       // [rows, Hq, k]
+  uint16_t* part_o;      // [rows, Hq, k, 128] bf16, then one trash slot
+  float* part_lse;       // [rows, Hq, k], then one trash slot
+  int64_t trash;         // index of the trash slot (rows * Hq * k)
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2;      // sm_scale * log2(e)
 };
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       const int se = chunk * MT + srow / G;
       sval[pass] = se < n_ent;
       const int sent = ent_s[sval[pass] ? se : 0];
-      spi[pass] = ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63);
+      spi[pass] = sval[pass] ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
     }
     const int jrow = lane & 31;
 #pragma unroll
@@ -344,27 +345,31 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       for (int pass = 0; pass < 2; ++pass) {
         const int r = 16 * pass + (lane >> 2), c = lane & 3;
         const i32x4 v = lds_load16<i32x4>(&ow[r * 64 + ((c ^ ((r >> 2) & 3)) << 4)]);
-        if (sval[pass]) *reinterpret_cast<i32x4*>(a.part_o + spi[pass] * 128 + 32 * dt + 8 * c) = v;
+        *reinterpret_cast<i32x4*>(a.part_o + spi[pass] * 128 + 32 * dt + 8 * c) = v;
       }
       wave_lds_sync();
     }
-    if (valid && half == 0) {
-      const int64_t pi = ((int64_t)rl * a.Hq + h) * a.k + slot;
+    {  // both halves hold the row's max and sum and store the same value
+      const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : a.trash;
       a.part_lse[pi] = (mx + fast_log2(sum)) * kLn2;  // mx is already scaled
     }
   };
 
   // Two register buffers of gathered Q rows: the next chunk's loads are
   // issued before the current chunk's work, a whole chunk ahead of their use.
+  // Every chunk issues the same loads (past the end they repeat the last
+  // chunk) and the same stores (padding rows go to the trash slot), so the
+  // compiler's wait counts stay exact and never wait for the prefetch.
   bf16x8 qa[8], qb[8];
   load_q(qa, 0);
+  wait_vmem();  // nothing in flight on entering the loop
   for (int chunk = 0; chunk < nchunks; chunk += 2) {
-    if (chunk + 1 < nchunks) load_q(qb, chunk + 1);
+    load_q(qb, min(chunk + 1, nchunks - 1));
     __builtin_amdgcn_sched_barrier(0);
     process(qa, chunk);
     __builtin_amdgcn_sched_barrier(0);
     if (chunk + 1 >= nchunks) break;
-    if (chunk + 2 < nchunks) load_q(qa, chunk + 2);
+    load_q(qa, min(chunk + 2, nchunks - 1));
     __builtin_amdgcn_sched_barrier(0);
     process(qb, chunk + 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -501,6 +506,7 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   a.m = m;
   a.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o);
   a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  a.trash = p->attn_window * Hq * k;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = p->G;
