@@ -254,31 +254,26 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       if (st & 1) __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Scores scaled first (products are canonical, so the max needs no NaN
-    // quieting).  Only a row's own (diagonal) block needs the causal mask:
-    // tiles whose every row sees the whole block take the branch without it.
+    // Row max on the raw scores with v_max3 (two scores per instruction),
+    // then p = exp2(s * scale - max * scale) as one FMA and one exp2.  Only a
+    // row's own (diagonal) block needs the causal mask: tiles whose every row
+    // sees the whole block take the branch without it; the masked branch sets
+    // hidden scores to -inf in place (exp2 then gives 0).
     const int lim = pos - b * 128 - 4 * half;  // last visible key offset, minus this lane's 4-key shift
-    float sc[4][16];
+    if (__builtin_amdgcn_ballot_w64(lim < 124) != 0) {  // 124 + 3: the last key offset a lane holds
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) acc[kt][i] = kNegInf;
+    }
+    float mraw = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[kt][i] = acc[kt][i] * a.scale_log2;
-    float mx = kNegInf;
-    if (__builtin_amdgcn_ballot_w64(lim < 124) == 0) {  // 124 + 3: the last key offset a lane holds
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[kt][i], sc[kt][i + 1]));
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) sc[kt][i] = kNegInf;
-          mx = fmaxf(mx, sc[kt][i]);
-        }
-    }
-    mx = fmaxf(mx, wave_xor32(mx));
+      for (int i = 0; i < 16; i += 2) mraw = max3f(mraw, acc[kt][i], acc[kt][i + 1]);
+    mraw = fmaxf(mraw, wave_xor32(mraw));
+    const float mx = mraw * a.scale_log2;  // scaled row max (log2 domain)
     float sum = 0.f;
     bf16x8 pf[4][2];
 #pragma unroll
@@ -288,8 +283,8 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
         i32x4 pw;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float p0 = fast_exp2(sc[kt][8 * u + 2 * t] - mx);
-          const float p1 = fast_exp2(sc[kt][8 * u + 2 * t + 1] - mx);
+          const float p0 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * t], a.scale_log2, -mx));
+          const float p1 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * t + 1], a.scale_log2, -mx));
           sum += p0 + p1;
           const bf16x2 two = {(__bf16)p0, (__bf16)p1};
           pw[t] = __builtin_bit_cast(int, two);
