@@ -9,7 +9,8 @@ then the block-sparse attention; for decode, one sparse decode call.
 
 Prints one JSON line.  The headline workload is the 32K causal sparse prefill
 (32 query heads, 8 KV heads, top-k 16); the 128K varlen prefill and the
-32 x 131072 fp8 paged decode are reported under "extra".  Throughput is
+32 x 131072 fp8 paged decode (with the workload's fixed selections, and as a
+whole step with its own indexer pass) are reported under "extra".  Throughput is
 measured with inputs resident in HBM, between a synchronize on both sides of
 exactly K timed steps.  The roofline entry times the dominant kernel with HIP
 events recorded by the library on the stream it launches on.
@@ -384,6 +385,63 @@ def decode_bench(msa, steps, warmup, sets=4):
     }
 
 
+def decode_step_bench(msa, steps, warmup, sets=4):
+    """A whole decode step at 32 x 131072: the indexer pass (fused proxy +
+    top-k on a one-query-row plan; 8 fp8 proxy heads sharing one proxy-K
+    head) and the fp8 sparse decode on its selection.  Four independent
+    (proxy q, q) sets are rotated per step."""
+    import torch
+    from synthetic.gen import workload, seed_of
+    from synthetic.device_gen import make_inputs_device
+    w = workload(6)
+    S = w.num_seqs
+    inp = make_inputs_device(w, seed_of(6))
+    pqs, qs = [inp.proxy_q], [inp.q]
+    for j in range(1, sets):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed_of(6) * 100 + j)
+        pq = torch.randn(inp.proxy_q.shape, generator=g, device="cuda") / inp.proxy_q_scale[None, :, None]
+        pqs.append(pq.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8))
+        qs.append(torch.randn(inp.q.shape, generator=g, device="cuda").to(torch.bfloat16))
+    ip = msa.msa_plan([1] * S, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads, w.num_proxy_kv_heads,
+                      topk=w.topk, proxy_dtype="fp8")
+    dp = msa.msa_plan(None, w.kv_lens, w.num_qo_heads, w.num_kv_heads, topk=w.topk, kv_dtype="fp8", mode="decode")
+    sel = torch.empty((S, w.num_kv_heads, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((S, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    it = [0]
+
+    def step():
+        j = it[0] % sets
+        it[0] += 1
+        msa.msa_proxy_topk_select(ip, pqs[j], inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale, inp.kv_indices,
+                                  0, S, sel)
+        msa.msa_sparse_attn_decode(dp, qs[j], inp.k_pages, inp.v_pages, inp.k_scale, inp.v_scale, inp.kv_indices, sel,
+                                   out)
+
+    step()
+    torch.cuda.synchronize()
+    stage = {}
+    for plan, names in ((ip, ["proxy_topk", "topk_select"]), (dp, ["decode"])):
+        for n, v in kernel_profile(msa, plan, step, names).items():
+            stage[n] = v[0]
+    ms_step, k_ms, launches = timed_with_kernel(msa, ip, step, steps, warmup, "proxy_topk")
+    # compulsory bytes of one indexer launch: every visible proxy-K block (fp8) + proxy q
+    nb = sum(-(-L // 128) for L in w.kv_lens)
+    work = nb * w.num_proxy_kv_heads * 128 * 128 + S * w.num_proxy_heads * 128
+    achieved = work / (k_ms * 1e-3) / 1e9
+    roof = {"kernel": "proxy_onerow", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": k_ms,
+            "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "B"}
+    return {
+        "workload": w.name, "tok_per_s": S / (ms_step * 1e-3), "ms_per_step": ms_step, "stage_ms": stage,
+        "roofline": roof,
+        "config": {"workload": w.name, "batch": S, "kv_len": w.kv_lens[0], "num_qo_heads": w.num_qo_heads,
+                   "num_kv_heads": w.num_kv_heads, "num_proxy_heads": w.num_proxy_heads,
+                   "num_proxy_kv_heads": w.num_proxy_kv_heads, "proxy_dtype": "fp8", "kv_dtype": "fp8",
+                   "slots": w.topk, "rotated_sets": sets},
+    }
+
+
 def cpu_baseline(w, inp, sel, rows=256):
     """The fp64 oracle as it stands, on a bounded sample of rows of the same
     workload: proxy scores, selection and attention for `rows` rows spread
@@ -419,8 +477,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode entries")
-    ap.add_argument("--extra", default="prefill_128k,decode_131k",
-                    help="comma-separated extra entries: prefill_128k, decode_131k (or none)")
+    ap.add_argument("--extra", default="prefill_128k,decode_131k,decode_step_131k",
+                    help="comma-separated extra entries: prefill_128k, decode_131k, decode_step_131k (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -446,7 +504,7 @@ def main():
     torch.cuda.set_device(0)
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
-        if e not in ("prefill_128k", "decode_131k"):
+        if e not in ("prefill_128k", "decode_131k", "decode_step_131k"):
             ap.error(f"unknown extra entry {e}")
     if args.copy_calibration:
         print("[bench] calibration copy", file=sys.stderr, flush=True)
@@ -461,6 +519,9 @@ def main():
     if "decode_131k" in extras:
         print("[bench] decode 131k fp8", file=sys.stderr, flush=True)
         extra["decode_131k"] = decode_bench(msa, max(50, args.steps * 10), 10)
+    if "decode_step_131k" in extras:
+        print("[bench] decode step (indexer + decode) 131k fp8", file=sys.stderr, flush=True)
+        extra["decode_step_131k"] = decode_step_bench(msa, max(50, args.steps * 10), 10)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

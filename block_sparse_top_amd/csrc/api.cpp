@@ -202,6 +202,12 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
   p->d.kv_lens_host = nullptr;
   p->S = d.batch;
   p->G = G;
+  {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+      p->num_cu = ncu;
+  }
   int64_t T = 0, NB = 0;
   p->row_start.push_back(0);
   p->page_start.push_back(0);
@@ -288,6 +294,14 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     // one extra slot at index W * Hq * K takes the stores of padding rows
     L.part_o = off; off = align_up(off + (W * Hq * K + 1) * 128 * 2, 256);
     L.part_lse = off; off = align_up(off + (W * Hq * K + 1) * 4, 256);
+    // one query row per sequence (a decode step's indexer pass): the proxy
+    // pass uses the one-row kernel, and the fused selection keeps its block
+    // scores here
+    p->one_row = std::all_of(p->qo.begin(), p->qo.end(), [](int32_t q) { return q == 1; });
+    if (p->one_row) {
+      L.dms = off;
+      off = align_up(off + (int64_t)d.num_proxy_heads * p->nb_max * T * 4, 256);
+    }
   } else {
     // one workgroup per (sequence, group) when that fills the GPU; otherwise
     // split each pair's 32-key slices over up to 8 workgroups
@@ -348,7 +362,7 @@ msa_status_t msa_proxy_block_maxscore(msa_plan_t p, const void* proxy_q, const v
   while (hi > lo && p->tiles[4 * (hi - 1) + 1] >= row_begin + row_count) --hi;
   const msa::DevMeta m = msa::dev_meta(p, workspace);
   return hip_status(msa::launch_proxy_maxscore(p, m, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale,
-                                               kv_indices, lo, hi, row_begin, row_count, max_score, nullptr, hs),
+                                               kv_indices, lo, hi, row_begin, row_count, max_score, nullptr, nullptr, hs),
                     __func__);
 }
 
@@ -382,6 +396,8 @@ msa_status_t msa_proxy_topk_select(msa_plan_t p, const void* proxy_q, const void
   const msa::DevMeta m = msa::dev_meta(p, workspace);
   return hip_status(msa::launch_proxy_maxscore(p, m, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale,
                                                kv_indices, lo, hi, row_begin, row_count, nullptr, kv_block_indexes,
+                                               p->one_row ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p->lay.dms)
+                                                          : nullptr,
                                                hs),
                     __func__);
 }

@@ -37,6 +37,8 @@ struct PlanLayout {
   int64_t max_items = 0;
   // decode split scratch
   size_t dec_o = 0, dec_ml = 0;
+  // block scores of the fused selection on one-query-row plans
+  size_t dms = 0;
   size_t total = 0;
 };
 
@@ -57,6 +59,8 @@ struct msa_plan_s {
   int32_t entries_per_item = 0;      // tokens per work item
   // decode schedule
   int32_t dec_splits = 1;
+  bool one_row = false;              // prefill plan whose every sequence has one query row
+  int32_t num_cu = 256;              // compute units of the device the plan was made on
   const void* uploaded_to = nullptr; // last workspace the metadata was copied into
   mutable msa::Profiler prof;
 };
@@ -78,7 +82,7 @@ struct ProfEvents {
 hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const void* pq, const void* pk,
                                  const float* qs, const float* ks, const int32_t* kv_indices, int32_t tile_lo,
                                  int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
-                                 int32_t* sel, hipStream_t st);
+                                 int32_t* sel, float* scratch, hipStream_t st);
 hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, int64_t row_begin,
                        int64_t row_count, int32_t* sel, hipStream_t st);
 hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,

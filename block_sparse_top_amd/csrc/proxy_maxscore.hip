@@ -358,12 +358,131 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
   }
 }
 
+// One query row per sequence (the indexer pass of a decode step): the row
+// tiles above would leave 511 of 512 rows idle, so this kernel streams each
+// sequence's proxy-K blocks straight from global memory into MFMA A
+// operands instead, and one MFMA serves every proxy head that shares the K
+// head (keys are the MFMA rows, those heads its columns).  Grid: (block
+// chunk, K head used, sequence); wave w of a workgroup takes the chunk's
+// blocks w, w+4, ...; each 32-key tile's loads are in flight while the
+// previous tile is multiplied.  Output: block maxima in the max_score layout.
+struct ProxyRowArgs {
+  const uint8_t* pq;
+  const uint8_t* pk;
+  const float* qs;
+  const float* ks;
+  const int32_t* kv_indices;
+  DevMeta m;
+  int32_t P, Pk, nb_max, blocks_per_wg;
+  int64_t row_begin, row_count;
+  float* out;  // [P, nb_max, row_count]
+  float scale;
+};
+
+constexpr int kRowWaves = 4;
+
+template <bool FP8>
+__global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowArgs a) {
+  using Tr = ProxyTraits<FP8>;
+  using Frag = typename Tr::Frag;
+  constexpr int kStepBytes = Tr::kRowBytes / Tr::kSteps;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rl = blockIdx.z;              // row within the call's range
+  const int seq = (int)(a.row_begin + rl);    // one row per sequence: row index = sequence index
+  const int kh = blockIdx.y;                  // K head
+  const int32_t kv_len = a.m.kv[seq];
+  const int nb = (kv_len + 127) >> 7;
+  const int b0 = blockIdx.x * a.blocks_per_wg, b1 = min(nb, b0 + a.blocks_per_wg);
+  if (b0 >= nb) return;
+  const int ncols = a.Pk == 1 ? a.P : 1;      // query heads this K head serves
+  const int j = lane & 31, hsel = lane >> 5;
+  const bool col_ok = j < ncols;
+  const int head = a.Pk == 1 ? (col_ok ? j : 0) : kh;
+  // B operand: the served heads' proxy q rows (zero columns past ncols)
+  Frag qf[Tr::kSteps];
+  {
+    const uint8_t* src = a.pq + ((int64_t)seq * a.P + head) * (128 * Tr::kElem) + hsel * (kStepBytes / 2);
+#pragma unroll
+    for (int st = 0; st < Tr::kSteps; ++st) {
+      qf[st] = load_frag_global<FP8>(src + st * kStepBytes);
+      if (!col_ok) qf[st] = Frag{};
+    }
+  }
+  float scale = a.scale;
+  if constexpr (FP8) scale *= a.qs[head] * a.ks[kh];
+  const int32_t* pages = a.kv_indices + a.m.page_start[seq];
+  auto load_tile = [&](Frag (&f)[Tr::kSteps], int32_t page, int t) {
+    const uint8_t* src = a.pk + ((int64_t)page * a.Pk + kh) * (128 * Tr::kRowBytes) + (32 * t + j) * Tr::kRowBytes +
+                         hsel * (kStepBytes / 2);
+#pragma unroll
+    for (int st = 0; st < Tr::kSteps; ++st) f[st] = load_frag_global<FP8>(src + st * kStepBytes);
+  };
+  for (int b = b0 + wave; b < b1; b += kRowWaves) {
+    const int32_t page = pages[b];
+    Frag fa[Tr::kSteps], fb[Tr::kSteps];
+    load_tile(fa, page, 0);
+    float m = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      Frag(&cur)[Tr::kSteps] = (t & 1) ? fb : fa;
+      Frag(&nxt)[Tr::kSteps] = (t & 1) ? fa : fb;
+      if (t + 1 < 4) load_tile(nxt, page, t + 1);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int st = 0; st < Tr::kSteps; ++st) acc = mma<FP8>(cur[st], qf[st], acc);
+      // C[i][j]: key 32t + 8(r/4) + 4 hsel + r%4 of register r; keys at or
+      // past kv_len are page padding
+      const int lim = kv_len - 1 - (b * 128 + 32 * t + 4 * hsel);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        m = max3f(m, (8 * (r >> 2) + (r & 3)) <= lim ? acc[r] : kNegInf,
+                  (8 * (r >> 2) + (r & 3) + 1) <= lim ? acc[r + 1] : kNegInf);
+    }
+    m = fmaxf(m, wave_xor32(m));
+    if (lane < ncols) a.out[((int64_t)head * a.nb_max + b) * a.row_count + rl] = m * scale;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const void* pq, const void* pk,
                                  const float* qs, const float* ks, const int32_t* kv_indices, int32_t tile_lo,
                                  int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
-                                 int32_t* sel, hipStream_t st) {
+                                 int32_t* sel, float* scratch, hipStream_t st) {
+  if (p->one_row) {
+    // indexer pass of a decode step: block maxima by the one-row kernel (into
+    // the workspace when the selection is fused), then the top-k kernel
+    ProxyRowArgs r;
+    r.pq = static_cast<const uint8_t*>(pq);
+    r.pk = static_cast<const uint8_t*>(pk);
+    r.qs = qs;
+    r.ks = ks;
+    r.kv_indices = kv_indices;
+    r.m = m;
+    r.P = p->d.num_proxy_heads;
+    r.Pk = p->d.num_proxy_kv_heads;
+    r.nb_max = p->nb_max;
+    r.row_begin = row_begin;
+    r.row_count = row_count;
+    r.out = sel ? scratch : max_score;
+    r.scale = p->d.proxy_sm_scale;
+    const int khs = r.Pk == 1 ? 1 : r.P;
+    // about four workgroups per CU over (sequence, K head, block chunk)
+    const int64_t units = row_count * khs;
+    const int64_t want = 4LL * p->num_cu;
+    r.blocks_per_wg = (int32_t)std::max<int64_t>(kRowWaves, (p->nb_max * units + want - 1) / want);
+    const dim3 grid((unsigned)((p->nb_max + r.blocks_per_wg - 1) / r.blocks_per_wg), (unsigned)khs,
+                    (unsigned)row_count);
+    const bool fp8 = p->d.proxy_dtype == MSA_FP8_E4M3;
+    {
+      ProfEvents pe(p, sel ? "proxy_topk" : "proxy_maxscore");
+      if (fp8) hipExtLaunchKernelGGL(proxy_onerow_kernel<true>, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
+      else hipExtLaunchKernelGGL(proxy_onerow_kernel<false>, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
+    }
+    if (sel) return launch_topk(p, m, scratch, row_begin, row_count, sel, st);
+    return hipGetLastError();
+  }
   if (tile_hi <= tile_lo) return hipSuccess;
   ProxyArgs a;
   a.pq = static_cast<const uint8_t*>(pq);

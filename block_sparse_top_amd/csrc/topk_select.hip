@@ -8,7 +8,8 @@
 // and -1 padded.  The README credits its indexer to a histogram step plus an
 // insertion sort; the same two ideas appear here in a per-thread form.
 //
-// Design (gfx950), one thread per (row, group):
+// Design (gfx950), one thread per (row, group) (plans with one query row per
+// sequence use the wave-per-row kernel further down):
 //  * max_score is [P][nb_max][rows] (rows fastest), so at every block index
 //    the 64 lanes of a wave read 64 consecutive floats: every load is one
 //    coalesced 256-byte line;
@@ -158,6 +159,65 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   for (; w < k; ++w) out[w] = -1;
 }
 
+
+// Few rows with long score rows (the indexer pass of a decode step: one row
+// per sequence, up to thousands of blocks): one wave per (row, group), each
+// lane holding VPL scores (block b at lane b % 64, register b / 64).  Each of
+// the R = min(topk - 1, local) rounds takes the best remaining score across
+// the wave (ties: the lower block id) and retires it; the chosen ids and the
+// local block are then written in ascending order by rank, -1 padded.
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.row_count * a.P) return;  // wave-uniform
+  const int64_t rl = pair / a.P;
+  const int p = (int)(pair % a.P);
+  const int32_t r = (int32_t)(a.row_begin + rl);
+  const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
+  const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
+  const int R = min(a.k - 1, local);
+  const float* col = a.ms + (int64_t)p * a.m.nb_max * a.row_count + rl;
+  float v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int b = 64 * i + lane;
+    v[i] = b < local ? col[(int64_t)b * a.row_count] : kNegInf;
+  }
+  int mine = 0x7fffffff;  // lane j < R keeps round j's block
+  for (int round = 0; round < R; ++round) {
+    float bv = kNegInf;
+    int bb = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {  // ascending ids: strict > keeps the lower id on ties
+      const bool better = v[i] > bv;
+      bv = better ? v[i] : bv;
+      bb = better ? 64 * i + lane : bb;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int ob = __shfl_xor(bb, off);
+      const bool better = ov > bv || (ov == bv && ob < bb);
+      bv = better ? ov : bv;
+      bb = better ? ob : bb;
+    }
+    if (lane == round) mine = bb;
+    if ((bb & 63) == lane) {  // retire it
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (64 * i + lane == bb) v[i] = kNegInf;
+    }
+  }
+  if (lane == R) mine = local;
+  // rank of each chosen id among the R + 1 (all distinct)
+  int rank = 0;
+  for (int j = 0; j <= R; ++j) rank += __shfl(mine, j) < mine ? 1 : 0;
+  int32_t* dst = a.sel + ((int64_t)r * a.P + p) * a.k;
+  if (lane <= R) dst[rank] = mine;
+  else if (lane < a.k) dst[lane] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, int64_t row_begin,
@@ -170,6 +230,17 @@ hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_s
   a.row_count = row_count;
   a.P = p->d.num_proxy_heads;
   a.k = p->d.topk;
+  if (p->one_row && p->nb_max <= 64 * 32 && a.k <= 64) {
+    // one wave per (row, group): these plans have few rows and long score rows
+    const unsigned grid = (unsigned)((row_count * a.P + 3) / 4);
+    const int vpl = (p->nb_max + 63) / 64;
+    ProfEvents pe(p, "topk_select");
+    if (vpl <= 4) hipExtLaunchKernelGGL(topk_wave_kernel<4>, dim3(grid), dim3(256), 0, st, pe.start, pe.stop, 0, a);
+    else if (vpl <= 8) hipExtLaunchKernelGGL(topk_wave_kernel<8>, dim3(grid), dim3(256), 0, st, pe.start, pe.stop, 0, a);
+    else if (vpl <= 16) hipExtLaunchKernelGGL(topk_wave_kernel<16>, dim3(grid), dim3(256), 0, st, pe.start, pe.stop, 0, a);
+    else hipExtLaunchKernelGGL(topk_wave_kernel<32>, dim3(grid), dim3(256), 0, st, pe.start, pe.stop, 0, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((row_count + kTopkThreads - 1) / kTopkThreads), (unsigned)a.P), block(kTopkThreads);
   const int need = a.k - 1;
   if (need <= 16) { ProfEvents pe(p, "topk_select"); hipExtLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, pe.start, pe.stop, 0, a); }

@@ -123,7 +123,7 @@ def make_inputs_device(w: Workload, seed: int, device="cuda", picks_sets: int = 
     v_pages = _scatter(vrows, w, kv_indices, num_pages, device)
     del vrows
     inp = DeviceInputs(w, kv_indices, q, k_pages, v_pages, ks, vs)
-    if w.mode == "prefill":
+    if w.num_proxy_heads > 0:  # prefill, or a decode step that runs its own indexer pass
         P, Pk = w.num_proxy_heads, w.num_proxy_kv_heads
         add_q = add_k = None
         if w.lowrank:
@@ -148,7 +148,7 @@ def make_inputs_device(w: Workload, seed: int, device="cuda", picks_sets: int = 
         pk_rows, pks = _store_rows(w, seed, STREAM_PK, Pk, w.proxy_dtype, device, lens, add_k)
         inp.proxy_k_pages = _scatter(pk_rows, w, kv_indices, num_pages, device)
         inp.proxy_k_scale = pks
-    else:
+    if w.mode == "decode":
         inp.kv_block_indexes = torch.from_numpy(decode_picks(w, seed)).to(device)
     return inp
 

@@ -115,7 +115,9 @@ class Workload:
         return [-(-int(L) // self.page_size) for L in self.kv_lens]
 
 
-# The five workloads the benchmark and the parity tests are built on.
+# The workloads the benchmark and the parity tests are built on (1-5: the
+# configurations the measurements are quoted on; 6: a decode step with its
+# indexer pass).
 def workload(n: int, **over) -> Workload:
     if n == 1:
         w = Workload("prefill_1k_gqa4", [1024], [1024], 8, 2, 2, 2, topk=4, page_table="identity")
@@ -129,6 +131,12 @@ def workload(n: int, **over) -> Workload:
                      kv_dtype=FP8, mode="decode")
     elif n == 5:
         w = Workload("prefill_1m_fp8proxy", [1048576], [1048576], 32, 8, 8, 8, topk=16, proxy_dtype=FP8)
+    elif n == 6:
+        # a whole decode step: the 32 x 131072 fp8 decode plus its own indexer
+        # pass (8 proxy heads, one shared fp8 proxy-K head, low-rank component
+        # for a clear top-k)
+        w = Workload("decode_step_b32_131k", [1] * 32, [131072] * 32, 64, 8, 8, 1, topk=17, kv_dtype=FP8,
+                     proxy_dtype=FP8, lowrank=8, mode="decode")
     else:
         raise ValueError(n)
     return dataclasses.replace(w, **over)
@@ -224,7 +232,7 @@ def make_inputs(w: Workload, seed: int) -> Inputs:
     v_pages, v_scale = paged(STREAM_V, w.num_kv_heads, w.kv_dtype)
     inp = Inputs(w, kv_indices, q, k_pages, v_pages, k_scale, v_scale)
 
-    if w.mode == "prefill":
+    if w.num_proxy_heads > 0:  # prefill, or a decode step that runs its own indexer pass
         P, Pk = w.num_proxy_heads, w.num_proxy_kv_heads
         pq32 = _normals(rng(seed, STREAM_PQ), (T, P, d))
         pk_rows = kv_rows(STREAM_PK, Pk)
@@ -256,7 +264,7 @@ def make_inputs(w: Workload, seed: int) -> Inputs:
         inp.proxy_q, inp.proxy_q_scale = pq_bits, pq_scale
         inp.proxy_k_pages = _scatter_pages(pk_bits, w, kv_indices, num_pages, nanv, npdt)
         inp.proxy_k_scale = pk_scale
-    else:
+    if w.mode == "decode":
         inp.kv_block_indexes = decode_picks(w, seed)
     return inp
 

@@ -76,14 +76,17 @@ def fp8_score_bound(inp, rows, scale):
         if not idx:
             continue
         L = lay.kv[s]
+        pos = np.array([lay.pos(int(rows[i])) for i in idx])
+        nb = lay.nb[s]
+        Kc = {}
         for p in range(P):
             ph = p if Pk == P else 0
-            K = np.abs(O.gather_rows(inp.proxy_k_pages, FP8, inp.proxy_k_scale, inp.kv_indices, lay, s, ph, np.arange(L)))
+            if ph not in Kc:
+                Kc[ph] = np.abs(O.gather_rows(inp.proxy_k_pages, FP8, inp.proxy_k_scale, inp.kv_indices, lay, s, ph,
+                                              np.arange(L)))
             q = np.abs(O.dequant(inp.proxy_q[np.asarray(rows)[idx], p:p + 1, :], FP8, inp.proxy_q_scale[p:p + 1]))[:, 0]
-            S = q @ K.T
-            pos = np.array([lay.pos(int(rows[i])) for i in idx])
+            S = q @ Kc[ph].T
             S[np.arange(L)[None, :] > pos[:, None]] = 0.0
-            nb = lay.nb[s]
             Sp = np.zeros((len(idx), nb * lay.B))
             Sp[:, :L] = S
             out[idx, p, :nb] = Sp.reshape(len(idx), nb, lay.B).max(axis=2)

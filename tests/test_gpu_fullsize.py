@@ -138,3 +138,60 @@ def test_decode_fp8_b32_131k_all_outputs():
                                    to_host(inp.k_scale), to_host(inp.v_scale))
     check_output(bf16_out_to_f64(out), ref, FP8_ATOL, FP8_COS, w.name)
     assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-3
+
+
+def test_decode_step_indexer_and_decode_b32_131k():
+    """A whole decode step at 32 x 131072: the indexer pass (8 fp8 proxy
+    heads sharing one proxy-K head, on a one-query-row plan) selects 16 + 1
+    blocks per (sequence, group), then the fp8 sparse decode runs on that
+    selection.  Fused and separate indexer calls agree bit for bit; block
+    scores, selections and outputs are checked against the oracle for every
+    sequence."""
+    from block_sparse_top_amd import msa
+    from synthetic.gen import Inputs
+    w = workload(6)
+    S = w.num_seqs
+    print(f"[fullsize] decode step workload={w.name}", flush=True)
+    inp = make_inputs_device(w, seed_of(6))
+    ip = msa.msa_plan([1] * S, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads, w.num_proxy_kv_heads,
+                      topk=w.topk, proxy_dtype="fp8")
+    dp = msa.msa_plan(None, w.kv_lens, w.num_qo_heads, w.num_kv_heads, topk=w.topk, kv_dtype="fp8", mode="decode")
+    sel = torch.full((S, w.num_kv_heads, w.topk), -7, dtype=torch.int32, device="cuda")
+    msa.msa_proxy_topk_select(ip, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale,
+                              inp.kv_indices, 0, S, sel)
+    ms = msa.max_score_buffer(ip)
+    sel2 = torch.full_like(sel, -7)
+    msa.msa_proxy_block_maxscore(ip, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale,
+                                 inp.kv_indices, 0, S, ms)
+    msa.msa_topk_select(ip, ms, 0, S, sel2)
+    out = torch.empty((S, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((S, w.num_qo_heads), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_decode(dp, inp.q, inp.k_pages, inp.v_pages, inp.k_scale, inp.v_scale, inp.kv_indices, sel,
+                               out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2), "fused indexer selection differs from the separate calls"
+    gms = ms[:, :, :S].cpu().numpy()
+    gsel = sel.cpu().numpy()
+    rows = np.arange(S)
+    h = {k: to_host(getattr(inp, k)) for k in ("q", "kv_indices", "proxy_q", "proxy_k_pages", "proxy_q_scale",
+                                                "proxy_k_scale", "k_scale", "v_scale")}
+    ref_ms = O.proxy_block_maxscore(h["proxy_q"], h["proxy_k_pages"], h["kv_indices"], [1] * S, w.kv_lens, 128,
+                                    w.proxy_sm_scale, FP8, h["proxy_q_scale"], h["proxy_k_scale"])
+    hi = Inputs(w, h["kv_indices"], h["q"], None, None, proxy_q=h["proxy_q"], proxy_k_pages=h["proxy_k_pages"],
+                proxy_q_scale=h["proxy_q_scale"], proxy_k_scale=h["proxy_k_scale"])
+    check_max_score(gms, ref_ms, w.name, fp8_score_bound(hi, rows, w.proxy_sm_scale))
+    lay = O.Layout([1] * S, w.kv_lens, 128)
+    check_selection(gsel, ref_ms, np.array([lay.local(int(r)) for r in rows]), w.topk, w.name)
+    # the decode on the indexer's selection: the oracle reads only the selected pages
+    kvi = h["kv_indices"]
+    need = sorted({int(kvi[lay.page_start[s] + b]) for s in range(S) for b in gsel[s].ravel() if b >= 0})
+    remap = np.full(inp.k_pages.shape[0], -1, np.int64)
+    remap[need] = np.arange(len(need))
+    idx = torch.tensor(need, device="cuda")
+    kp = to_host(inp.k_pages[idx])
+    vp = to_host(inp.v_pages[idx])
+    kvi2 = np.where(remap[kvi] >= 0, remap[kvi], 0).astype(np.int32)
+    ref, ref_lse = O.sparse_decode(h["q"], kp, vp, kvi2, gsel, w.kv_lens, 128, w.sm_scale, FP8, h["k_scale"],
+                                   h["v_scale"])
+    check_output(bf16_out_to_f64(out), ref, FP8_ATOL, FP8_COS, w.name)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-3

@@ -43,6 +43,11 @@ PREFILL_CASES = {
     "chunked_calls": (Workload("chunk", [900, 333], [900, 400], 8, 2, 2, 2, topk=6, poison_tail=True), 17, 200),
     "topk_exceeds_blocks": (Workload("bigk", [500], [500], 8, 2, 2, 2, topk=9), 18, 0),
     "topk1_local_only": (Workload("k1", [450], [450], 8, 2, 2, 2, topk=1), 19, 0),
+    # one query row per sequence (a decode step's indexer pass; the one-row proxy kernel)
+    "onerow_fp8_shared_proxy_k": (Workload("row1a", [1] * 6, [1000, 128, 129, 2000, 5000, 131], 16, 2, 2, 1, topk=17,
+                                           proxy_dtype=FP8, extra_pages=0.1, poison_tail=True), 26, 0),
+    "onerow_bf16_per_head_proxy_k": (Workload("row1b", [1] * 5, [300, 7000, 256, 1, 4000], 8, 2, 2, 2, topk=5,
+                                              poison_tail=True), 27, 0),
 }
 
 
