@@ -364,8 +364,9 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
 // operands instead, and one MFMA serves every proxy head that shares the K
 // head (keys are the MFMA rows, those heads its columns).  Grid: (block
 // chunk, K head used, sequence); wave w of a workgroup takes the chunk's
-// blocks w, w+4, ...; each 32-key tile's loads are in flight while the
-// previous tile is multiplied.  Output: block maxima in the max_score layout.
+// blocks w, w+4, ... (about one workgroup per CU, each wave streaming a long
+// run of blocks, measured faster than more, shorter workgroups).  Output:
+// block maxima in the max_score layout.
 struct ProxyRowArgs {
   const uint8_t* pq;
   const uint8_t* pk;
@@ -418,19 +419,24 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
 #pragma unroll
     for (int st = 0; st < Tr::kSteps; ++st) f[st] = load_frag_global<FP8>(src + st * kStepBytes);
   };
-  for (int b = b0 + wave; b < b1; b += kRowWaves) {
-    const int32_t page = pages[b];
-    Frag fa[Tr::kSteps], fb[Tr::kSteps];
-    load_tile(fa, page, 0);
+  // Software pipeline over whole blocks: block b + 4's sixteen KB (fp8: 64
+  // VGPRs per buffer) is in flight while block b is multiplied.
+  int b = b0 + wave;
+  if (b >= b1) return;
+  Frag fa[4][Tr::kSteps], fb[4][Tr::kSteps];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) load_tile(fa[t], pages[b], t);
+  auto step = [&](Frag (&cur)[4][Tr::kSteps], Frag (&nxt)[4][Tr::kSteps], int b) {
+    const int bn = min(b + kRowWaves, b1 - 1);  // past the chunk's end: reload its last block (unused)
+    const int32_t pn = pages[bn];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) load_tile(nxt[t], pn, t);
     float m = kNegInf;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      Frag(&cur)[Tr::kSteps] = (t & 1) ? fb : fa;
-      Frag(&nxt)[Tr::kSteps] = (t & 1) ? fa : fb;
-      if (t + 1 < 4) load_tile(nxt, page, t + 1);
       f32x16 acc = f32x16{};
 #pragma unroll
-      for (int st = 0; st < Tr::kSteps; ++st) acc = mma<FP8>(cur[st], qf[st], acc);
+      for (int st = 0; st < Tr::kSteps; ++st) acc = mma<FP8>(cur[t][st], qf[st], acc);
       // C[i][j]: key 32t + 8(r/4) + 4 hsel + r%4 of register r; keys at or
       // past kv_len are page padding
       const int lim = kv_len - 1 - (b * 128 + 32 * t + 4 * hsel);
@@ -441,7 +447,12 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
     }
     m = fmaxf(m, wave_xor32(m));
     if (lane < ncols) a.out[((int64_t)head * a.nb_max + b) * a.row_count + rl] = m * scale;
+  };
+  for (; b + kRowWaves < b1; b += 2 * kRowWaves) {
+    step(fa, fb, b);
+    step(fb, fa, b + kRowWaves);
   }
+  if (b < b1) step(fa, fb, b);
 }
 
 }  // namespace
@@ -468,9 +479,9 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
     r.out = sel ? scratch : max_score;
     r.scale = p->d.proxy_sm_scale;
     const int khs = r.Pk == 1 ? 1 : r.P;
-    // about four workgroups per CU over (sequence, K head, block chunk)
+    // about one workgroup per CU over (sequence, K head, block chunk)
     const int64_t units = row_count * khs;
-    const int64_t want = 4LL * p->num_cu;
+    const int64_t want = p->num_cu;
     r.blocks_per_wg = (int32_t)std::max<int64_t>(kRowWaves, (p->nb_max * units + want - 1) / want);
     const dim3 grid((unsigned)((p->nb_max + r.blocks_per_wg - 1) / r.blocks_per_wg), (unsigned)khs,
                     (unsigned)row_count);

@@ -160,59 +160,74 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 }
 
 
-// Few rows with long score rows (the indexer pass of a decode step: one row
-// per sequence, up to thousands of blocks): one wave per (row, group), each
+// Wave-uniform max: 16-lane row reductions by DPP (quad_perm xor 1,
+// xor 2, then row_ror 4, 8), then the four row results read by readlane.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = fmaxf(v, __int_as_float(dpp<0xB1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<0x4E>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<0x124>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<0x128>(__float_as_int(v))));
+  const int x = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(x, 0)), __int_as_float(__builtin_amdgcn_readlane(x, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(x, 32)), __int_as_float(__builtin_amdgcn_readlane(x, 48))));
+}
+
+// Plans with one query row per sequence (the indexer pass of a decode step:
+// few rows, up to thousands of blocks each): one wave per (row, group), each
 // lane holding VPL scores (block b at lane b % 64, register b / 64).  Each of
-// the R = min(topk - 1, local) rounds takes the best remaining score across
-// the wave (ties: the lower block id) and retires it; the chosen ids and the
-// local block are then written in ascending order by rank, -1 padded.
+// the R = min(topk - 1, local) rounds takes the wave's best remaining score,
+// finds the lowest block holding it (register by register, ballot, lowest
+// lane) and retires it (NaN marks a retired entry or a block outside the
+// competing range: max ignores it and it equals nothing); the chosen ids and
+// the local block are then written in ascending order by rank, -1 padded.
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
+  constexpr int kNone = 0x7fffffff;
   const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= a.row_count * a.P) return;  // wave-uniform
+  const int64_t pair = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (pair >= a.row_count * a.P) return;
   const int64_t rl = pair / a.P;
   const int p = (int)(pair % a.P);
-  const int32_t r = (int32_t)(a.row_begin + rl);
-  const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
-  const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
+  const int32_t r = (int32_t)(a.row_begin + rl);  // = its sequence: one query row each
+  const int local = __builtin_amdgcn_readfirstlane((a.m.kv[r] - 1) >> 7);
   const int R = min(a.k - 1, local);
   const float* col = a.ms + (int64_t)p * a.m.nb_max * a.row_count + rl;
   float v[VPL];
+  const int last = max(local - 1, 0);  // clamped loads: issued back to back, always in bounds
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int b = 64 * i + lane;
-    v[i] = b < local ? col[(int64_t)b * a.row_count] : kNegInf;
+    const float x = col[(int64_t)min(b, last) * a.row_count];
+    v[i] = b < local ? x : __builtin_nanf("");
   }
-  int mine = 0x7fffffff;  // lane j < R keeps round j's block
+  int mine = kNone;  // lane j < R keeps round j's block
   for (int round = 0; round < R; ++round) {
-    float bv = kNegInf;
-    int bb = 0x7fffffff;
+    float lm = v[0];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {  // ascending ids: strict > keeps the lower id on ties
-      const bool better = v[i] > bv;
-      bv = better ? v[i] : bv;
-      bb = better ? 64 * i + lane : bb;
-    }
+    for (int i = 1; i < VPL; ++i) lm = fmaxf(lm, v[i]);  // NaN (retired) is ignored
+    const float wm = wave_max_uniform(lm);
+    // lowest block holding the maximum: the first register with a match,
+    // its lowest matching lane
+    int wb = kNone;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int ob = __shfl_xor(bb, off);
-      const bool better = ov > bv || (ov == bv && ob < bb);
-      bv = better ? ov : bv;
-      bb = better ? ob : bb;
+    for (int i = VPL - 1; i >= 0; --i) {
+      const uint64_t hit = __ballot(v[i] == wm);
+      if (hit) wb = 64 * i + (int)__builtin_ctzll(hit);
     }
-    if (lane == round) mine = bb;
-    if ((bb & 63) == lane) {  // retire it
+    if (lane == round) mine = wb;
+    const bool own = lane == (wb & 63);
 #pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (64 * i + lane == bb) v[i] = kNegInf;
-    }
+    for (int i = 0; i < VPL; ++i)
+      if (i == (wb >> 6) && own) v[i] = __builtin_nanf("");  // retire it
   }
   if (lane == R) mine = local;
   // rank of each chosen id among the R + 1 (all distinct)
   int rank = 0;
-  for (int j = 0; j <= R; ++j) rank += __shfl(mine, j) < mine ? 1 : 0;
+  for (int j = 0; j <= R; ++j) rank += __builtin_amdgcn_readlane(mine, j) < mine ? 1 : 0;
   int32_t* dst = a.sel + ((int64_t)r * a.P + p) * a.k;
   if (lane <= R) dst[rank] = mine;
   else if (lane < a.k) dst[lane] = -1;

@@ -122,25 +122,37 @@ def test_fused_proxy_topk_equals_separate_calls(case):
         assert (s2[:r0] == -7).all() and (s2[r0 + n:] == -7).all(), case
 
 
-def test_topk_exact_on_given_scores_with_ties():
-    """The top-k kernel on fp32 scores with many exact ties must equal the
-    oracle's selection bit for bit (same fp32 values, lower id wins)."""
+TIE_CASES = {
+    # many query rows per sequence: the thread-per-row kernel
+    "multi_row": (Workload("ties", [1500, 40], [1500, 300], 8, 2, 2, 2, topk=6), 5),
+    # one query row per sequence, rows up to 2048 blocks: the wave-per-row kernel
+    "one_row_k17": (Workload("ties1", [1] * 6, [262144, 70000, 5000, 129, 128, 1], 8, 2, 2, 2, topk=17), 6),
+    "one_row_k64": (Workload("ties2", [1] * 3, [200000, 9000, 8193], 8, 2, 2, 2, topk=64), 7),
+}
+
+
+@pytest.mark.parametrize("case", list(TIE_CASES))
+def test_topk_exact_on_given_scores_with_ties(case):
+    """The top-k kernel on fp32 scores with many exact ties (and some -inf)
+    must equal the oracle's selection bit for bit (same fp32 values, lower id
+    wins)."""
     msa = _msa()
-    w = Workload("ties", [1500, 40], [1500, 300], 8, 2, 2, 2, topk=6)
-    plan = msa.msa_plan(w.qo_lens, w.kv_lens, 8, 2, 2, 2, topk=6, max_rows_per_call=1540)
-    rng = np.random.default_rng(5)
+    w, seed = TIE_CASES[case]
     T = w.total_rows
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, 8, 2, 2, 2, topk=w.topk, max_rows_per_call=T)
+    rng = np.random.default_rng(seed)
     scores = rng.integers(-3, 4, size=(2, plan.nb_max, T)).astype(np.float32)     # heavy ties
     scores[:, :, ::7] = rng.standard_normal((2, plan.nb_max, len(range(0, T, 7)))).astype(np.float32)
+    scores[rng.random(scores.shape) < 0.01] = -np.inf
     ms = torch.from_numpy(scores).cuda()
-    sel = torch.full((T, 2, 6), -7, dtype=torch.int32, device="cuda")
+    sel = torch.full((T, 2, w.topk), -7, dtype=torch.int32, device="cuda")
     msa.msa_topk_select(plan, ms, 0, T, sel)
     got = sel.cpu().numpy()
     lay = O.Layout(w.qo_lens, w.kv_lens, 128)
     for r in range(T):
         for p in range(2):
-            exp = O.topk_select_row(scores[p, :, r].astype(np.float64), lay.local(r), 6)
-            assert np.array_equal(got[r, p], exp), (r, p, got[r, p], exp)
+            exp = O.topk_select_row(scores[p, :, r].astype(np.float64), lay.local(r), w.topk)
+            assert np.array_equal(got[r, p], exp), (case, r, p, got[r, p], exp)
 
 
 DECODE_CASES = {
