@@ -38,7 +38,7 @@ KERNEL_SOURCES = {
     "proxy_maxscore": "proxy_maxscore.hip", "topk_select": "topk_select.hip", "proxy_topk": "proxy_maxscore.hip",
     "csr": "sparse_prefill.hip",
     "partial_attn": "sparse_prefill.hip", "merge": "sparse_prefill.hip", "decode": "sparse_decode.hip",
-    "decode_merge": "sparse_decode.hip",
+    "decode_merge": "sparse_decode.hip", "proxy_onerow": "proxy_maxscore.hip", "topk_wave": "topk_select.hip",
 }
 
 
@@ -68,13 +68,15 @@ def traffic_from_profiles(kernel: str, workload: str):
 # rocprofv3 summaries (run on the host from the CSV files rocprofv3 wrote)
 # ----------------------------------------------------------------------------
 COPY_BYTES = 1 << 30           # calibration copy: bytes read and bytes written per launch
-PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --extra decode_131k --copy-calibration"
+PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --extra decode_131k,decode_step_131k --copy-calibration"
 PMC_CMDS = {
     "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o f -- python bench.py {PMC_ARGS}",
     "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o w -- python bench.py {PMC_ARGS}",
 }
 TRACE_CMD = "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/kt -o kt -- python bench.py"
-SECTION_OF_KERNEL = {"decode": "decode_fp8_b32_131k", "decode_merge": "decode_fp8_b32_131k"}
+SECTION_OF_KERNEL = {"decode": "decode_fp8_b32_131k", "decode_merge": "decode_fp8_b32_131k",
+                     "proxy_onerow": "decode_step_b32_131k", "topk_wave": "decode_step_b32_131k"}
+DECODE_STEP_WORKLOAD = "decode_step_b32_131k"
 
 
 def _short_kernel(name: str):
@@ -170,8 +172,11 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
             nxt = label_of_grid[grid]
         section[i] = nxt
     last = None
+    step_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow"), len(rows))
     for i, (k, grid, _) in enumerate(rows):
-        if k.startswith("decode"):
+        if i >= step_from:      # the decode-step workload runs last
+            section[i] = DECODE_STEP_WORKLOAD
+        elif k.startswith("decode"):
             section[i] = SECTION_OF_KERNEL["decode"]
         elif k == "merge" or section[i] is None:
             section[i] = last
@@ -430,7 +435,7 @@ def decode_step_bench(msa, steps, warmup, sets=4):
     work = nb * w.num_proxy_kv_heads * 128 * 128 + S * w.num_proxy_heads * 128
     achieved = work / (k_ms * 1e-3) / 1e9
     roof = {"kernel": "proxy_onerow", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": k_ms,
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles("proxy_onerow", w.name), "avg_launch_ms": k_ms,
             "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "B"}
     return {
         "workload": w.name, "tok_per_s": S / (ms_step * 1e-3), "ms_per_step": ms_step, "stage_ms": stage,
