@@ -6,7 +6,7 @@ in block_sparse_top_amd/ and neither side imports the other.
 
 Everything is written as the plain definition, in float64, from the exact
 stored bytes (bf16 bits -> float; fp8 e4m3fn bits -> table value x fp32
-per-head scale).  Sources (the pages):
+per-head scale; MXFP4 records -> E2M1 table value x E8M0 block scale).  Sources (the pages):
 
   [README]  "MiniMax-AI/MSA" README (pigsec.cn mirror), section "Usage": a
             dense proxy pass over a cheap query slice returns a per-block max
@@ -46,6 +46,11 @@ import numpy as np
 
 BF16 = "bf16"
 FP8 = "fp8"
+# Proxy pair with an MXFP4 proxy K (the low-precision block-score indexer of
+# the README's "Stacks" / package list, in the microscaling FP4 format that
+# gfx950 matrix cores consume): proxy q is fp8 e4m3fn with per-head scales,
+# proxy K pages hold MXFP4 records (see mxfp4_record_rows).
+MXFP4 = "mxfp4"
 
 
 # ----------------------------------------------------------------------------
@@ -78,6 +83,53 @@ E4M3FN_TABLE = np.array([_e4m3fn_value(b) for b in range(256)], dtype=np.float64
 
 def e4m3fn_to_f64(bits: np.ndarray) -> np.ndarray:
     return E4M3FN_TABLE[np.asarray(bits, dtype=np.uint8)]
+
+
+def _e2m1_value(code: int) -> float:
+    """OCP MX 4-bit float E2M1, from its definition: 1 sign bit (bit 3), 2
+    exponent bits with bias 1, 1 mantissa bit; exponent 0 is subnormal
+    (m/2 * 2^0); no infinities or NaN; largest magnitude 6."""
+    s = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return s * (m / 2.0)
+    return s * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e8m0_to_f64(bits: np.ndarray) -> np.ndarray:
+    """OCP MX shared scale E8M0: an unsigned biased exponent, 2^(code - 127);
+    code 255 is NaN."""
+    b = np.asarray(bits, dtype=np.int64)
+    return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
+MXFP4_BLOCK = 32            # elements sharing one E8M0 scale
+
+
+def mxfp4_record_rows(rec: np.ndarray, slots) -> np.ndarray:
+    """Decode key rows from MXFP4 page records (one record per page and head).
+
+    A record of a 128-slot page with head dim d holds first 128 * d/2 bytes of
+    E2M1 codes, slot-major, element 2i of a row in the low nibble of its byte
+    i and element 2i+1 in the high nibble; then 128 * d/32 E8M0 scale bytes,
+    slot-major, byte c scaling elements 32c .. 32c+31 of that slot.  rec is
+    uint8 [n, record bytes] (one record per requested slot), slots [n];
+    returns float64 [n, d]: code value x 2^(scale - 127)."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    slots = np.asarray(slots, dtype=np.int64)
+    n = rec.shape[0]
+    d = rec.shape[1] * 32 // (128 * 17)           # record = 128 * (d/2 + d/32) bytes
+    cb, sb = d // 2, d // MXFP4_BLOCK
+    codes = rec[:, :128 * cb].reshape(n, 128, cb)[np.arange(n), slots]          # [n, d/2]
+    scales = rec[:, 128 * cb:128 * (cb + sb)].reshape(n, 128, sb)[np.arange(n), slots]  # [n, d/32]
+    nib = np.empty((n, d), dtype=np.uint8)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    return E2M1_TABLE[nib] * np.repeat(e8m0_to_f64(scales), MXFP4_BLOCK, axis=1)
 
 
 def dequant(bits: np.ndarray, dtype: str, scale=None, head_axis: int = 1) -> np.ndarray:
@@ -132,6 +184,8 @@ def gather_rows(pages_bits, dtype, scale, kv_indices, lay: Layout, s: int, head:
     Key j lives in page kv_indices[page_start[s] + j // B], slot j % B."""
     key_idx = np.asarray(key_idx, dtype=np.int64)
     pages = np.asarray(kv_indices, dtype=np.int64)[lay.page_start[s] + key_idx // lay.B]
+    if dtype == MXFP4:      # pool [N, heads, record bytes]; no per-head scale
+        return mxfp4_record_rows(pages_bits[pages, head], key_idx % lay.B)
     raw = pages_bits[pages, head, key_idx % lay.B, :]
     if dtype == BF16:
         return bf16_to_f64(raw)
@@ -153,7 +207,9 @@ def proxy_block_maxscore(proxy_q, proxy_k_pages, kv_indices, qo_lens, kv_lens, p
 
     pk_head(p) = p when there are as many proxy-K heads as proxy heads, else 0.
     Blocks with no visible key give -inf; blocks after the row's local block
-    are not defined and returned as NaN.
+    are not defined and returned as NaN.  With proxy_dtype MXFP4 the proxy q
+    is fp8 (scaled by proxy_q_scale) and the proxy K rows are decoded from
+    MXFP4 records (proxy_k_scale unused).
 
     Returns float64 [len(rows), P, nb_max].
     """
@@ -161,6 +217,7 @@ def proxy_block_maxscore(proxy_q, proxy_k_pages, kv_indices, qo_lens, kv_lens, p
     rows = np.arange(lay.T) if rows is None else np.asarray(rows, dtype=np.int64)
     T, P, d = proxy_q.shape
     Pk = proxy_k_pages.shape[1]
+    q_dtype = FP8 if proxy_dtype == MXFP4 else proxy_dtype
     B = lay.B
     nb_max = max(lay.nb)
     out = np.full((rows.size, P, nb_max), np.nan)
@@ -177,7 +234,7 @@ def proxy_block_maxscore(proxy_q, proxy_k_pages, kv_indices, qo_lens, kv_lens, p
             for c0 in range(0, sel.size, 256):
                 idx = sel[c0:c0 + 256]
                 r = rows[idx]
-                qv = dequant(proxy_q[r, p:p + 1, :], proxy_dtype,
+                qv = dequant(proxy_q[r, p:p + 1, :], q_dtype,
                              None if proxy_q_scale is None else np.asarray(proxy_q_scale)[p:p + 1])[:, 0, :]
                 S = proxy_sm_scale * (qv @ K.T)                               # [n, L]
                 pos = np.array([lay.pos(int(x)) for x in r])

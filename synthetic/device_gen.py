@@ -16,7 +16,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from .gen import (Workload, STREAM_Q, STREAM_K, STREAM_V, STREAM_PQ, STREAM_PK, STREAM_LOWRANK, BF16, FP8,
+from .gen import (Workload, STREAM_Q, STREAM_K, STREAM_V, STREAM_PQ, STREAM_PK, STREAM_LOWRANK, BF16, FP8, MXFP4,
+                  E2M1_MAGNITUDES,
                   rng as np_rng, decode_picks, _page_table)
 
 CHUNK = 1 << 24  # elements per generation chunk
@@ -88,6 +89,41 @@ def _store_rows(w: Workload, seed: int, stream: int, H: int, dtype: str, device,
     return out, scale
 
 
+def _mxfp4_rows(x: torch.Tensor) -> torch.Tensor:
+    """float32 [n, H, d] -> uint8 [n, H, d/2 + d/32], the MXFP4 row format of
+    synthetic.gen.to_mxfp4_rows (same conversion, on the device)."""
+    n, H, d = x.shape
+    blk = x.reshape(n, H, d // 32, 32)
+    amax = blk.abs().amax(dim=-1)
+    X = torch.where(amax > 0, torch.frexp(amax)[1].to(torch.int32) - 3, torch.zeros_like(amax, dtype=torch.int32))
+    X = X.clamp(-127, 127)
+    y = torch.ldexp(blk, (-X).to(torch.float32)[..., None])
+    mag = y.abs()
+    grid = torch.tensor(E2M1_MAGNITUDES, dtype=torch.float32, device=x.device)
+    lo = (torch.searchsorted(grid, mag.contiguous(), right=True) - 1).clamp(0, 7)
+    hi = (lo + 1).clamp(max=7)
+    dlo = mag - grid[lo]
+    dhi = grid[hi] - mag
+    code = torch.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo)
+    code = torch.where(mag >= 6.0, torch.full_like(code, 7), code)
+    code = code | (((y < 0) & (code != 0)).to(code.dtype) << 3)
+    code = code.to(torch.uint8).reshape(n, H, d)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return torch.cat([packed, (X + 127).to(torch.uint8)], dim=-1)
+
+
+def _store_mxfp4_rows(w: Workload, seed: int, stream: int, H: int, device, rows_per_seq, extra=None):
+    d = w.head_dim
+    g = _gen(seed, stream, device)
+    out = []
+    for s, L in enumerate(rows_per_seq):
+        t = torch.empty((L, H, d // 2 + d // 32), dtype=torch.uint8, device=device)
+        for r0, x in _randn_rows(g, L, H, d, device, None if extra is None else (lambda r0, x, s=s: extra(s, r0, x))):
+            t[r0:r0 + x.shape[0]] = _mxfp4_rows(x)
+        out.append(t)
+    return out
+
+
 def _scatter(rows, w: Workload, kv_indices: torch.Tensor, num_pages: int, device):
     H, d = rows[0].shape[1], rows[0].shape[2]
     B = w.page_size
@@ -143,10 +179,21 @@ def make_inputs_device(w: Workload, seed: int, device="cuda", picks_sets: int = 
                 n = x.shape[0]
                 blk = (torch.arange(r0, r0 + n, device=device) // B)
                 x += c * torch.einsum("pdr,tpr->tpd", basis[:Pk], wb[s][blk])
-        pq_rows, pqs = _store_rows(w, seed, STREAM_PQ, P, w.proxy_dtype, device, [T], add_q)
+        pq_rows, pqs = _store_rows(w, seed, STREAM_PQ, P, FP8 if w.proxy_dtype == MXFP4 else w.proxy_dtype, device,
+                                   [T], add_q)
         inp.proxy_q, inp.proxy_q_scale = pq_rows[0], pqs
-        pk_rows, pks = _store_rows(w, seed, STREAM_PK, Pk, w.proxy_dtype, device, lens, add_k)
-        inp.proxy_k_pages = _scatter(pk_rows, w, kv_indices, num_pages, device)
+        if w.proxy_dtype == MXFP4:
+            pk_rows = _store_mxfp4_rows(w, seed, STREAM_PK, Pk, device, lens, add_k)
+            pool = _scatter(pk_rows, w, kv_indices, num_pages, device)          # [N, Pk, B, d/2 + d/32]
+            N, _, B, wd = pool.shape
+            cb = wd * 16 // 17
+            inp.proxy_k_pages = torch.cat([pool[..., :cb].reshape(N, Pk, B * cb),
+                                           pool[..., cb:].reshape(N, Pk, B * (wd - cb))], dim=-1).contiguous()
+            del pool
+            pks = None
+        else:
+            pk_rows, pks = _store_rows(w, seed, STREAM_PK, Pk, w.proxy_dtype, device, lens, add_k)
+            inp.proxy_k_pages = _scatter(pk_rows, w, kv_indices, num_pages, device)
         inp.proxy_k_scale = pks
     if w.mode == "decode":
         inp.kv_block_indexes = torch.from_numpy(decode_picks(w, seed)).to(device)

@@ -15,6 +15,13 @@ Recipe (the same for every workload):
   * bf16: round-to-nearest-even from float32.
   * fp8 e4m3fn: per-head scale = amax|x| / 448 over that head's whole tensor,
     round-to-nearest-even, saturate at +-448.
+  * MXFP4 (proxy K of the "mxfp4" proxy pair; its proxy q is fp8): per key row
+    and run of 32 dims a shared E8M0 exponent X = floor(log2 amax) - 2 (2 is
+    the largest E2M1 exponent), elements x / 2^X rounded to the nearest E2M1
+    value (ties to the even code), saturating at +-6 -- the conversion the
+    OCP microscaling specification gives.  Stored per (page, head) as one
+    record: 128 rows of packed codes (even element in the low nibble), then
+    128 rows of scale bytes.
   * the page table is a seeded permutation of the pool (or the identity);
     pool pages not used by any sequence, and page slots past kv_len in a
     sequence's last page, can be filled with NaN to catch stray reads.
@@ -32,6 +39,7 @@ STREAM_Q, STREAM_K, STREAM_V, STREAM_PQ, STREAM_PK, STREAM_PAGES, STREAM_LOWRANK
 
 BF16 = "bf16"
 FP8 = "fp8"
+MXFP4 = "mxfp4"
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -61,6 +69,40 @@ def to_e4m3fn_bits(x: np.ndarray, head_axis: int) -> tuple[np.ndarray, np.ndarra
     return bits, scale
 
 
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)   # codes 0..7
+
+
+def to_mxfp4_rows(x: np.ndarray) -> np.ndarray:
+    """float32 [..., d] -> uint8 [..., d/2 + d/32]: d/2 bytes of packed E2M1
+    codes (element 2i in the low nibble of byte i), then d/32 E8M0 scales."""
+    x = np.asarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    blk = x.reshape(x.shape[:-1] + (d // 32, 32)).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    e = np.frexp(amax)[1].astype(np.int64)           # amax = m 2^e, m in [0.5, 1): floor(log2 amax) = e - 1
+    X = np.clip(np.where(amax > 0, e - 1 - 2, 0), -127, 127)
+    y = blk / np.ldexp(1.0, X)[..., None]
+    mag = np.abs(y)
+    lo = np.clip(np.searchsorted(E2M1_MAGNITUDES, mag, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    dlo = mag - E2M1_MAGNITUDES[lo]
+    dhi = E2M1_MAGNITUDES[hi] - mag
+    code = np.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(mag >= 6.0, 7, code).astype(np.uint8)
+    code |= ((y < 0) & (code != 0)).astype(np.uint8) << 3
+    code = code.reshape(x.shape[:-1] + (d,))
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return np.concatenate([packed, (X + 127).astype(np.uint8)], axis=-1)
+
+
+def mxfp4_pool_to_records(pool: np.ndarray) -> np.ndarray:
+    """[N, H, B, d/2 + d/32] per-row MXFP4 bytes -> [N, H, B*(d/2) + B*(d/32)]
+    page records: all rows' codes, then all rows' scales."""
+    N, H, B, w = pool.shape
+    cb = w * 16 // 17
+    return np.concatenate([pool[..., :cb].reshape(N, H, B * cb), pool[..., cb:].reshape(N, H, B * (w - cb))], axis=-1)
+
+
 def store(x: np.ndarray, dtype: str, head_axis: int):
     if dtype == BF16:
         return to_bf16_bits(x), None
@@ -71,6 +113,7 @@ def store(x: np.ndarray, dtype: str, head_axis: int):
 
 NAN_BF16 = np.uint16(0x7FC0)
 NAN_E4M3 = np.uint8(0x7F)
+NAN_MXFP4 = np.uint8(0xFF)         # as a scale byte: E8M0 NaN
 
 
 @dataclasses.dataclass
@@ -156,7 +199,7 @@ class Inputs:
     k_scale: Optional[np.ndarray] = None        # float32 [H_kv] (fp8)
     v_scale: Optional[np.ndarray] = None
     proxy_q: Optional[np.ndarray] = None        # [T, P, d]
-    proxy_k_pages: Optional[np.ndarray] = None  # [N, P_k, B, d]
+    proxy_k_pages: Optional[np.ndarray] = None  # [N, P_k, B, d]; MXFP4: [N, P_k, record bytes]
     proxy_q_scale: Optional[np.ndarray] = None  # float32 [P]
     proxy_k_scale: Optional[np.ndarray] = None  # float32 [P_k]
     kv_block_indexes: Optional[np.ndarray] = None  # int32 [T, H_kv, k] (decode picks)
@@ -250,9 +293,12 @@ def make_inputs(w: Workload, seed: int) -> Inputs:
                 comp = c * np.einsum("pdr,bpr->bpd", basis[:Pk], wb)          # [nb, Pk, d]
                 tok = np.repeat(comp, B, axis=0)[:int(L)]                      # [L, Pk, d]
                 pk_rows[s] += tok
-        pq_bits, pq_scale = store(pq32, w.proxy_dtype, head_axis=1)
+        pq_bits, pq_scale = store(pq32, FP8 if w.proxy_dtype == MXFP4 else w.proxy_dtype, head_axis=1)
         del pq32
-        if w.proxy_dtype == BF16:
+        if w.proxy_dtype == MXFP4:
+            pk_bits = [to_mxfp4_rows(r) for r in pk_rows]
+            pk_scale, nanv, npdt = None, NAN_MXFP4, np.uint8
+        elif w.proxy_dtype == BF16:
             pk_bits = [to_bf16_bits(r) for r in pk_rows]
             pk_scale, nanv, npdt = None, NAN_BF16, np.uint16
         else:
@@ -263,6 +309,8 @@ def make_inputs(w: Workload, seed: int) -> Inputs:
             nanv, npdt = NAN_E4M3, np.uint8
         inp.proxy_q, inp.proxy_q_scale = pq_bits, pq_scale
         inp.proxy_k_pages = _scatter_pages(pk_bits, w, kv_indices, num_pages, nanv, npdt)
+        if w.proxy_dtype == MXFP4:
+            inp.proxy_k_pages = mxfp4_pool_to_records(inp.proxy_k_pages)
         inp.proxy_k_scale = pk_scale
     if w.mode == "decode":
         inp.kv_block_indexes = decode_picks(w, seed)

@@ -58,3 +58,39 @@ def test_dropping_the_local_block_is_caught(monkeypatch):
     monkeypatch.setattr(tt, "topk_select_row", bad)
     with pytest.raises(AssertionError):
         tt.test_hand_worked_cases()
+
+
+def test_swapped_mxfp4_nibbles_are_caught(monkeypatch):
+    """Odd elements in the low nibble instead of the high one."""
+    from tests import test_oracle_formats as tf
+    orig = om.mxfp4_record_rows
+
+    def bad(rec, slots):
+        rec = np.asarray(rec, dtype=np.uint8)
+        cb = 128 * 64
+        sw = rec.copy()
+        sw[:, :cb] = (rec[:, :cb] >> 4) | (rec[:, :cb] << 4)
+        return orig(sw, slots)
+    monkeypatch.setattr(om, "mxfp4_record_rows", bad)
+    with pytest.raises(AssertionError):
+        tp.test_mxfp4_proxy_k_equals_bf16_path_on_the_same_values()
+    monkeypatch.setattr(tf, "mxfp4_record_rows", bad, raising=False)
+    import oracle
+    monkeypatch.setattr(oracle, "mxfp4_record_rows", bad)
+    with pytest.raises(AssertionError):
+        tf.test_mxfp4_record_layout_by_hand()
+
+
+def test_mxfp4_scale_group_off_by_one_is_caught(monkeypatch):
+    """Each 32-element group scaled by its neighbour's scale byte."""
+    orig = om.mxfp4_record_rows
+
+    def bad(rec, slots):
+        rec = np.asarray(rec, dtype=np.uint8).copy()
+        cb = 128 * 64
+        sc = rec[:, cb:].reshape(rec.shape[0], 128, 4)
+        rec[:, cb:] = np.roll(sc, 1, axis=2).reshape(rec.shape[0], -1)
+        return orig(rec, slots)
+    monkeypatch.setattr(om, "mxfp4_record_rows", bad)
+    with pytest.raises(AssertionError):
+        tp.test_mxfp4_proxy_k_equals_bf16_path_on_the_same_values()

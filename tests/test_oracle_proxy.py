@@ -161,3 +161,32 @@ def test_rows_subset_matches_full():
     sub = [0, 49, 50, 51, 109]
     part = proxy_block_maxscore(pq, pool, kvi, qo, kv, B, 0.25, rows=sub)
     assert np.array_equal(np.nan_to_num(part, nan=7.0), np.nan_to_num(full[sub], nan=7.0))
+
+
+def test_mxfp4_proxy_k_equals_bf16_path_on_the_same_values():
+    """With an MXFP4 proxy K the oracle decodes the records and scores with an
+    fp8 proxy q; on values that bf16 and e4m3 hold exactly (E2M1 x 2^X, e4m3
+    codes with unit scale) the result must equal the bf16 path bit for bit."""
+    from oracle import MXFP4, E2M1_TABLE
+    from synthetic.gen import to_mxfp4_rows, mxfp4_pool_to_records, to_bf16_bits
+    rng = np.random.default_rng(11)
+    qo, kv, B, P, Pk = [1, 3], [700, 300], 128, 2, 1
+    T = sum(qo)
+    nbs = [-(-L // B) for L in kv]
+    N = sum(nbs) + 1
+    kvi = rng.permutation(N)[:sum(nbs)].astype(np.int32)
+    codes = rng.integers(0, 16, size=(N, Pk, B, 128))
+    codes[..., ::32] = rng.choice([6, 7, 14, 15], size=(N, Pk, B, 4))
+    X = rng.integers(-3, 3, size=(N, Pk, B, 4))
+    kvals = E2M1_TABLE[codes] * np.repeat(np.ldexp(1.0, X), 32, axis=-1)
+    rec = mxfp4_pool_to_records(to_mxfp4_rows(kvals.astype(np.float32)))
+    q8 = rng.integers(0, 256, size=(T, P, 128)).astype(np.uint8)
+    q8[(q8 & 0x7F) == 0x7F] = 0x10                       # no NaN codes
+    one = np.ones(P, np.float32)
+    from oracle import e4m3fn_to_f64
+    qbits = to_bf16_bits(e4m3fn_to_f64(q8).astype(np.float32))
+    kbits = to_bf16_bits(kvals.astype(np.float32))
+    a = proxy_block_maxscore(q8, rec, kvi, qo, kv, B, 0.125, MXFP4, one, None)
+    b = proxy_block_maxscore(qbits, kbits, kvi, qo, kv, B, 0.125, BF16)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
