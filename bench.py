@@ -38,7 +38,8 @@ KERNEL_SOURCES = {
     "proxy_maxscore": "proxy_maxscore.hip", "topk_select": "topk_select.hip", "proxy_topk": "proxy_maxscore.hip",
     "csr": "sparse_prefill.hip",
     "partial_attn": "sparse_prefill.hip", "merge": "sparse_prefill.hip", "decode": "sparse_decode.hip",
-    "decode_merge": "sparse_decode.hip", "proxy_onerow": "proxy_maxscore.hip", "topk_wave": "topk_select.hip",
+    "decode_merge": "sparse_decode.hip", "proxy_onerow": "proxy_maxscore.hip",
+    "proxy_onerow_mxfp4": "proxy_maxscore.hip", "topk_wave": "topk_select.hip",
 }
 
 
@@ -68,15 +69,18 @@ def traffic_from_profiles(kernel: str, workload: str):
 # rocprofv3 summaries (run on the host from the CSV files rocprofv3 wrote)
 # ----------------------------------------------------------------------------
 COPY_BYTES = 1 << 30           # calibration copy: bytes read and bytes written per launch
-PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --extra decode_131k,decode_step_131k --copy-calibration"
+PMC_ARGS = ("--steps 2 --warmup 1 --no-cpu-baseline --extra decode_131k,decode_step_131k,decode_step_mxfp4_131k "
+            "--copy-calibration")
 PMC_CMDS = {
     "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o f -- python bench.py {PMC_ARGS}",
     "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o w -- python bench.py {PMC_ARGS}",
 }
 TRACE_CMD = "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/kt -o kt -- python bench.py"
 SECTION_OF_KERNEL = {"decode": "decode_fp8_b32_131k", "decode_merge": "decode_fp8_b32_131k",
-                     "proxy_onerow": "decode_step_b32_131k", "topk_wave": "decode_step_b32_131k"}
+                     "proxy_onerow": "decode_step_b32_131k", "topk_wave": "decode_step_b32_131k",
+                     "proxy_onerow_mxfp4": "decode_step_mxfp4_b32_131k"}
 DECODE_STEP_WORKLOAD = "decode_step_b32_131k"
+DECODE_STEP_MXFP4_WORKLOAD = "decode_step_mxfp4_b32_131k"
 
 
 def _short_kernel(name: str):
@@ -173,8 +177,11 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
         section[i] = nxt
     last = None
     step_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow"), len(rows))
+    mx_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow_mxfp4"), len(rows))
     for i, (k, grid, _) in enumerate(rows):
-        if i >= step_from:      # the decode-step workload runs last
+        if i >= mx_from:        # the decode-step workloads run last, fp8 then MXFP4
+            section[i] = DECODE_STEP_MXFP4_WORKLOAD
+        elif i >= step_from:
             section[i] = DECODE_STEP_WORKLOAD
         elif k.startswith("decode"):
             section[i] = SECTION_OF_KERNEL["decode"]
@@ -390,26 +397,26 @@ def decode_bench(msa, steps, warmup, sets=4):
     }
 
 
-def decode_step_bench(msa, steps, warmup, sets=4):
+def decode_step_bench(msa, steps, warmup, sets=4, wn=6):
     """A whole decode step at 32 x 131072: the indexer pass (fused proxy +
-    top-k on a one-query-row plan; 8 fp8 proxy heads sharing one proxy-K
-    head) and the fp8 sparse decode on its selection.  Four independent
-    (proxy q, q) sets are rotated per step."""
+    top-k on a one-query-row plan; 8 fp8 proxy heads sharing one fp8 (workload
+    6) or MXFP4 (workload 7) proxy-K head) and the fp8 sparse decode on its
+    selection.  Four independent (proxy q, q) sets are rotated per step."""
     import torch
     from synthetic.gen import workload, seed_of
     from synthetic.device_gen import make_inputs_device
-    w = workload(6)
+    w = workload(wn)
     S = w.num_seqs
-    inp = make_inputs_device(w, seed_of(6))
+    inp = make_inputs_device(w, seed_of(wn))
     pqs, qs = [inp.proxy_q], [inp.q]
     for j in range(1, sets):
         g = torch.Generator(device="cuda")
-        g.manual_seed(seed_of(6) * 100 + j)
+        g.manual_seed(seed_of(wn) * 100 + j)
         pq = torch.randn(inp.proxy_q.shape, generator=g, device="cuda") / inp.proxy_q_scale[None, :, None]
         pqs.append(pq.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8))
         qs.append(torch.randn(inp.q.shape, generator=g, device="cuda").to(torch.bfloat16))
     ip = msa.msa_plan([1] * S, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads, w.num_proxy_kv_heads,
-                      topk=w.topk, proxy_dtype="fp8")
+                      topk=w.topk, proxy_dtype=w.proxy_dtype)
     dp = msa.msa_plan(None, w.kv_lens, w.num_qo_heads, w.num_kv_heads, topk=w.topk, kv_dtype="fp8", mode="decode")
     sel = torch.empty((S, w.num_kv_heads, w.topk), dtype=torch.int32, device="cuda")
     out = torch.empty((S, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
@@ -430,19 +437,22 @@ def decode_step_bench(msa, steps, warmup, sets=4):
         for n, v in kernel_profile(msa, plan, step, names).items():
             stage[n] = v[0]
     ms_step, k_ms, launches = timed_with_kernel(msa, ip, step, steps, warmup, "proxy_topk")
-    # compulsory bytes of one indexer launch: every visible proxy-K block (fp8) + proxy q
+    # compulsory bytes of one indexer launch: every visible proxy-K block
+    # (fp8: 128 x 128 B; MXFP4: 128 x (64 + 4) B) + the fp8 proxy q
     nb = sum(-(-L // 128) for L in w.kv_lens)
-    work = nb * w.num_proxy_kv_heads * 128 * 128 + S * w.num_proxy_heads * 128
+    kblock = 128 * 128 if w.proxy_dtype == "fp8" else 128 * (64 + 4)
+    work = nb * w.num_proxy_kv_heads * kblock + S * w.num_proxy_heads * 128
     achieved = work / (k_ms * 1e-3) / 1e9
-    roof = {"kernel": "proxy_onerow", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles("proxy_onerow", w.name), "avg_launch_ms": k_ms,
+    kname = "proxy_onerow" if w.proxy_dtype == "fp8" else "proxy_onerow_mxfp4"
+    roof = {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles(kname, w.name), "avg_launch_ms": k_ms,
             "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "B"}
     return {
         "workload": w.name, "tok_per_s": S / (ms_step * 1e-3), "ms_per_step": ms_step, "stage_ms": stage,
         "roofline": roof,
         "config": {"workload": w.name, "batch": S, "kv_len": w.kv_lens[0], "num_qo_heads": w.num_qo_heads,
                    "num_kv_heads": w.num_kv_heads, "num_proxy_heads": w.num_proxy_heads,
-                   "num_proxy_kv_heads": w.num_proxy_kv_heads, "proxy_dtype": "fp8", "kv_dtype": "fp8",
+                   "num_proxy_kv_heads": w.num_proxy_kv_heads, "proxy_dtype": w.proxy_dtype, "kv_dtype": "fp8",
                    "slots": w.topk, "rotated_sets": sets},
     }
 
@@ -482,8 +492,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode entries")
-    ap.add_argument("--extra", default="prefill_128k,decode_131k,decode_step_131k",
-                    help="comma-separated extra entries: prefill_128k, decode_131k, decode_step_131k (or none)")
+    ap.add_argument("--extra", default="prefill_128k,decode_131k,decode_step_131k,decode_step_mxfp4_131k",
+                    help="comma-separated extra entries: prefill_128k, decode_131k, decode_step_131k, "
+                         "decode_step_mxfp4_131k (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -509,7 +520,7 @@ def main():
     torch.cuda.set_device(0)
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
-        if e not in ("prefill_128k", "decode_131k", "decode_step_131k"):
+        if e not in ("prefill_128k", "decode_131k", "decode_step_131k", "decode_step_mxfp4_131k"):
             ap.error(f"unknown extra entry {e}")
     if args.copy_calibration:
         print("[bench] calibration copy", file=sys.stderr, flush=True)
@@ -527,6 +538,9 @@ def main():
     if "decode_step_131k" in extras:
         print("[bench] decode step (indexer + decode) 131k fp8", file=sys.stderr, flush=True)
         extra["decode_step_131k"] = decode_step_bench(msa, max(50, args.steps * 10), 10)
+    if "decode_step_mxfp4_131k" in extras:
+        print("[bench] decode step (indexer + decode) 131k, MXFP4 proxy K", file=sys.stderr, flush=True)
+        extra["decode_step_mxfp4_131k"] = decode_step_bench(msa, max(50, args.steps * 10), 10, wn=7)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

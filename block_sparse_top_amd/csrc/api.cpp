@@ -66,6 +66,17 @@ msa_status_t check_ws(const msa_plan_s* p, void* ws, size_t bytes) {
   return MSA_OK;
 }
 
+// bf16: no scales; fp8: both per-head scales; MXFP4: the fp8 proxy q's
+// scales only (proxy-K scales live in the page records)
+msa_status_t check_proxy_scales(const msa_plan_s* p, const float* qs, const float* ks, const char* fn) {
+  const msa_dtype_t dt = p->d.proxy_dtype;
+  const bool want_q = dt != MSA_BF16, want_k = dt == MSA_FP8_E4M3;
+  if (want_q != (qs != nullptr) || want_k != (ks != nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "%s: proxy_q_scale must be given iff the proxy dtype is fp8 or MXFP4, proxy_k_scale "
+                "iff it is fp8", fn);
+  return MSA_OK;
+}
+
 msa_status_t check_rows(const msa_plan_s* p, int64_t row_begin, int64_t row_count, const char* fn) {
   if (row_count <= 0 || row_begin < 0 || row_begin + row_count > p->T)
     return fail(MSA_ERR_INVALID_ARG, "%s: row range [%lld, %lld) is empty or outside [0, %d)", fn,
@@ -183,8 +194,11 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
   if (!(d.sm_scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "msa_plan: sm_scale must be > 0");
   if (d.mode == MSA_PREFILL) {
     if (d.kv_dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "msa_plan: prefill K/V must be bf16");
-    if (d.proxy_dtype != MSA_BF16 && d.proxy_dtype != MSA_FP8_E4M3)
+    if (d.proxy_dtype != MSA_BF16 && d.proxy_dtype != MSA_FP8_E4M3 && d.proxy_dtype != MSA_MXFP4)
       return fail(MSA_ERR_INVALID_ARG, "msa_plan: bad proxy_dtype");
+    if (d.proxy_dtype == MSA_MXFP4 && d.batch >= 1 &&
+        !std::all_of(d.qo_lens_host, d.qo_lens_host + d.batch, [](int32_t q) { return q == 1; }))
+      return fail(MSA_ERR_UNSUPPORTED, "msa_plan: an MXFP4 proxy K is built for plans with one query row per sequence");
     if (d.num_proxy_heads != d.num_kv_heads)
       return fail(MSA_ERR_UNSUPPORTED, "msa_plan: num_proxy_heads (%d) must equal num_kv_heads (%d)",
                   d.num_proxy_heads, d.num_kv_heads);
@@ -348,11 +362,9 @@ msa_status_t msa_proxy_block_maxscore(msa_plan_t p, const void* proxy_q, const v
   MSA_CHECK_PTR(proxy_k_pages);
   MSA_CHECK_PTR(kv_indices);
   MSA_CHECK_PTR(max_score);
-  const bool fp8 = p->d.proxy_dtype == MSA_FP8_E4M3;
-  if (fp8 != (proxy_q_scale != nullptr) || fp8 != (proxy_k_scale != nullptr))
-    return fail(MSA_ERR_INVALID_ARG, "msa_proxy_block_maxscore: scale pointers must be given iff the proxy dtype is fp8");
-  msa_status_t st = check_rows(p, row_begin, row_count, __func__);
+  msa_status_t st = check_proxy_scales(p, proxy_q_scale, proxy_k_scale, __func__);
   if (st != MSA_OK) return st;
+  if ((st = check_rows(p, row_begin, row_count, __func__)) != MSA_OK) return st;
   if ((st = check_ws(p, workspace, workspace_bytes)) != MSA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
@@ -380,14 +392,12 @@ msa_status_t msa_proxy_topk_select(msa_plan_t p, const void* proxy_q, const void
   MSA_CHECK_PTR(proxy_k_pages);
   MSA_CHECK_PTR(kv_indices);
   MSA_CHECK_PTR(kv_block_indexes);
-  const bool fp8 = p->d.proxy_dtype == MSA_FP8_E4M3;
-  if (fp8 != (proxy_q_scale != nullptr) || fp8 != (proxy_k_scale != nullptr))
-    return fail(MSA_ERR_INVALID_ARG, "msa_proxy_topk_select: scale pointers must be given iff the proxy dtype is fp8");
+  msa_status_t st = check_proxy_scales(p, proxy_q_scale, proxy_k_scale, __func__);
+  if (st != MSA_OK) return st;
   if (row_count < 1 || row_begin < 0 || row_begin + row_count > p->T)
     return fail(MSA_ERR_INVALID_ARG, "msa_proxy_topk_select: rows [%lld, %lld) outside [0, %lld)", (long long)row_begin,
                 (long long)(row_begin + row_count), (long long)p->T);
-  msa_status_t st = check_ws(p, workspace, workspace_bytes);
-  if (st != MSA_OK) return st;
+  if ((st = check_ws(p, workspace, workspace_bytes)) != MSA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
   int32_t lo = 0, hi = p->ntiles;

@@ -9,6 +9,10 @@
 //     C[i][j] in lane (j + 16*(i/4)), register i%4.
 //   v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, unit scales): as 32x32x16 with
 //     32 consecutive k per lane half: A[i][k] in lane (i + 32*(k/32)), byte k%32.
+//     With an E2M1 (FP4) A operand (4 registers) lane (i + 32h) instead holds
+//     k = 16h..16h+15 as codes 0-15 and k = 32+16h..47+16h as codes 16-31
+//     (code n in bits 4n..4n+3), and its own E8M0 scale byte (op_sel) scales
+//     all 32 of them.
 // Because a contraction is a sum over k, A and B may both use any one
 // permutation of k; the kernels exploit that to load 16- or 32-byte runs.
 #pragma once

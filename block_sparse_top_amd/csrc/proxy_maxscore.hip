@@ -455,6 +455,101 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
   if (b < b1) step(fa, fb, b);
 }
 
+// MXFP4 proxy K, one query row per sequence.  A page record of one proxy-K
+// head holds 128 key rows of E2M1 codes (64 B each, element 2i in the low
+// nibble of byte i), then 128 rows of E8M0 scales (4 B each, byte c scaling
+// dims 32c..32c+31).  The scaled f8f6f4 MFMA takes the codes as its FP4 A
+// operand and the fp8 proxy q as its B operand (unit scale), so every product
+// is exact.  FP4 A layout of v_mfma_scale_f32_32x32x64_f8f6f4 (probed): lane
+// (row i, half h) holds 32 codes, codes 0-15 at k = 16h..16h+15 and codes
+// 16-31 at k = 32+16h..47+16h, and its own scale byte (picked by op_sel)
+// scales all 32.  So a lane takes one whole MX block: at k-step st, lane
+// (key j, h) holds block 2st + h (the 16 code bytes at 32st + 16h of the key
+// row) with that block's scale byte (the key's scale word shifted right by
+// 8h, op_sel 2st), and the q fragment of lane (column, h') pairs with it:
+// dims 64st + 16h' .. +15 then 64st + 32 + 16h' .. +15.  Schedule as in the
+// fp8/bf16 kernel above: whole blocks, the next one in flight.
+constexpr int kMxRowCodeBytes = 64;                          // 128 dims x 4 bits
+constexpr int kMxRecordBytes = 128 * kMxRowCodeBytes + 128 * 4;
+
+struct MxTile {
+  i32x4 c[2];  // MX blocks h and 2 + h of key j (k-steps 0 and 1)
+  int32_t sc;  // the key's four scale bytes >> 8h
+};
+
+template <int ST>
+__device__ __forceinline__ f32x16 mma_fp4_fp8(const i32x4& a, const i32x8& b, int32_t sa, const f32x16& c) {
+  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  // format codes: A = 4 (E2M1), B = 0 (E4M3); A's scale is byte 2 ST of sa, B's 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, c, 4, 0, 2 * ST, sa, 0, 127);
+}
+
+__global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(ProxyRowArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rl = blockIdx.z;
+  const int seq = (int)(a.row_begin + rl);
+  const int kh = blockIdx.y;
+  const int32_t kv_len = a.m.kv[seq];
+  const int nb = (kv_len + 127) >> 7;
+  const int b0 = blockIdx.x * a.blocks_per_wg, b1 = min(nb, b0 + a.blocks_per_wg);
+  if (b0 >= nb) return;
+  const int ncols = a.Pk == 1 ? a.P : 1;
+  const int j = lane & 31, hsel = lane >> 5;
+  const bool col_ok = j < ncols;
+  const int head = a.Pk == 1 ? (col_ok ? j : 0) : kh;
+  i32x8 qf[2];
+  {
+    const uint8_t* src = a.pq + ((int64_t)seq * a.P + head) * 128 + hsel * 16;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const i32x4 x = *reinterpret_cast<const i32x4*>(src + 64 * st);
+      const i32x4 y = *reinterpret_cast<const i32x4*>(src + 64 * st + 32);
+      qf[st] = col_ok ? i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]} : i32x8{};
+    }
+  }
+  const float scale = a.scale * a.qs[head];
+  const int32_t* pages = a.kv_indices + a.m.page_start[seq];
+  auto load_tile = [&](MxTile& f, int32_t page, int t) {
+    const uint8_t* rec = a.pk + ((int64_t)page * a.Pk + kh) * kMxRecordBytes;
+    const int key = 32 * t + j;
+    const uint8_t* cp = rec + key * kMxRowCodeBytes + hsel * 16;
+    f.c[0] = *reinterpret_cast<const i32x4*>(cp);
+    f.c[1] = *reinterpret_cast<const i32x4*>(cp + 32);
+    f.sc = (int32_t)(*reinterpret_cast<const uint32_t*>(rec + 128 * kMxRowCodeBytes + key * 4) >> (8 * hsel));
+  };
+  int b = b0 + wave;
+  if (b >= b1) return;
+  MxTile fa[4], fb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) load_tile(fa[t], pages[b], t);
+  auto step = [&](MxTile (&cur)[4], MxTile (&nxt)[4], int b) {
+    const int bn = min(b + kRowWaves, b1 - 1);  // past the chunk's end: reload its last block (unused)
+    const int32_t pn = pages[bn];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) load_tile(nxt[t], pn, t);
+    float m = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x16 acc = f32x16{};
+      acc = mma_fp4_fp8<0>(cur[t].c[0], qf[0], cur[t].sc, acc);
+      acc = mma_fp4_fp8<1>(cur[t].c[1], qf[1], cur[t].sc, acc);
+      const int lim = kv_len - 1 - (b * 128 + 32 * t + 4 * hsel);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        m = max3f(m, (8 * (r >> 2) + (r & 3)) <= lim ? acc[r] : kNegInf,
+                  (8 * (r >> 2) + (r & 3) + 1) <= lim ? acc[r + 1] : kNegInf);
+    }
+    m = fmaxf(m, wave_xor32(m));
+    if (lane < ncols) a.out[((int64_t)head * a.nb_max + b) * a.row_count + rl] = m * scale;
+  };
+  for (; b + kRowWaves < b1; b += 2 * kRowWaves) {
+    step(fa, fb, b);
+    step(fb, fa, b + kRowWaves);
+  }
+  if (b < b1) step(fa, fb, b);
+}
+
 }  // namespace
 
 hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const void* pq, const void* pk,
@@ -485,11 +580,14 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
     r.blocks_per_wg = (int32_t)std::max<int64_t>(kRowWaves, (p->nb_max * units + want - 1) / want);
     const dim3 grid((unsigned)((p->nb_max + r.blocks_per_wg - 1) / r.blocks_per_wg), (unsigned)khs,
                     (unsigned)row_count);
-    const bool fp8 = p->d.proxy_dtype == MSA_FP8_E4M3;
     {
       ProfEvents pe(p, sel ? "proxy_topk" : "proxy_maxscore");
-      if (fp8) hipExtLaunchKernelGGL(proxy_onerow_kernel<true>, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
-      else hipExtLaunchKernelGGL(proxy_onerow_kernel<false>, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
+      if (p->d.proxy_dtype == MSA_MXFP4)
+        hipExtLaunchKernelGGL(proxy_onerow_mxfp4_kernel, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
+      else if (p->d.proxy_dtype == MSA_FP8_E4M3)
+        hipExtLaunchKernelGGL(proxy_onerow_kernel<true>, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
+      else
+        hipExtLaunchKernelGGL(proxy_onerow_kernel<false>, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
     }
     if (sel) return launch_topk(p, m, scratch, row_begin, row_count, sel, st);
     return hipGetLastError();

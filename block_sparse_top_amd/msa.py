@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_HIP = range(5)
-MSA_BF16, MSA_FP8_E4M3 = 0, 1
+MSA_BF16, MSA_FP8_E4M3, MSA_MXFP4 = 0, 1, 2
 MSA_PREFILL, MSA_DECODE = 0, 1
 
 ENTRY_POINTS = ("msa_plan", "msa_plan_destroy", "msa_plan_info", "msa_proxy_block_maxscore", "msa_topk_select",
@@ -106,7 +106,7 @@ def _stream():
 
 
 def _dtype_code(name: str) -> int:
-    return {"bf16": MSA_BF16, "fp8": MSA_FP8_E4M3}[name]
+    return {"bf16": MSA_BF16, "fp8": MSA_FP8_E4M3, "mxfp4": MSA_MXFP4}[name]
 
 
 class Plan:

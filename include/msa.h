@@ -74,7 +74,16 @@ typedef enum {
   MSA_ERR_HIP = 4                  /* the HIP runtime reported an error */
 } msa_status_t;
 
-typedef enum { MSA_BF16 = 0, MSA_FP8_E4M3 = 1 } msa_dtype_t;
+/* MSA_MXFP4 is a proxy dtype only (desc.proxy_dtype, plans whose every
+ * sequence has one query row): proxy q is fp8 e4m3 with per-head scales, and
+ * each proxy-K page of one head is an MXFP4 record (OCP microscaling FP4:
+ * E2M1 codes, one E8M0 scale per 32 dims) of 128 * 64 bytes of codes
+ * (slot-major; element 2i of a row in the low nibble of byte i) followed by
+ * 128 * 4 scale bytes (slot-major; byte c scales dims 32c..32c+31): value =
+ * e2m1(code) * 2^(scale - 127).  This is the low-precision block-score
+ * indexer of the README's "Stacks" list, in the FP4 format gfx950 matrix
+ * cores consume. */
+typedef enum { MSA_BF16 = 0, MSA_FP8_E4M3 = 1, MSA_MXFP4 = 2 } msa_dtype_t;
 typedef enum { MSA_PREFILL = 0, MSA_DECODE = 1 } msa_mode_t;
 
 typedef struct {
@@ -89,7 +98,8 @@ typedef struct {
   int32_t page_size;           /* 128 */
   int32_t topk;                /* slots per (row, group), local block included; 1..64 */
   msa_dtype_t kv_dtype;        /* K/V pages: bf16 (prefill, decode) or fp8 (decode) */
-  msa_dtype_t proxy_dtype;     /* proxy q and proxy k pages: bf16 or fp8 */
+  msa_dtype_t proxy_dtype;     /* proxy q and proxy k pages: bf16 or fp8; or MXFP4
+                                  (fp8 q, MXFP4 K records; one-row plans only) */
   float sm_scale;              /* main attention logit scale */
   float proxy_sm_scale;        /* proxy logit scale */
   msa_mode_t mode;             /* which entry points the plan serves */
@@ -117,13 +127,17 @@ msa_status_t msa_plan_destroy(msa_plan_t plan);
  * where pk(p) = p if P_k = P else 0, and qs/ks are the fp8 scales (1 for
  * bf16).  Entries with b > local(r) are left unspecified (may be written).
  *
- *   proxy_q        [T, P, 128]  bf16 or fp8 (desc.proxy_dtype)
- *   proxy_k_pages  [num_pages, P_k, 128, 128], same dtype
+ *   proxy_q        [T, P, 128]  bf16 or fp8 (desc.proxy_dtype; fp8 for MXFP4)
+ *   proxy_k_pages  [num_pages, P_k, 128, 128], same dtype; MXFP4:
+ *                  [num_pages, P_k, 8704 B] records (see MSA_MXFP4)
  *   proxy_q_scale  [P]   fp32, device; NULL iff proxy dtype is bf16
- *   proxy_k_scale  [P_k] fp32, device; NULL iff proxy dtype is bf16
+ *   proxy_k_scale  [P_k] fp32, device; given iff proxy dtype is fp8
  *   kv_indices     int32 flat page table (see conventions)
  *   max_score      fp32 [P, nb_max, row_count], nb_max = max over sequences
  *                  of ceil(kv_len / 128); row_count <= plan's max_rows_per_call
+ * Plans whose every sequence has exactly one query row (the indexer pass of a
+ * decode step) run a kernel that streams each sequence's proxy-K blocks
+ * once for all proxy heads; the results are the same.
  * Errors: INVALID_ARG for a null pointer, a row range outside [0, T), an
  * empty range, or a scale pointer that does not match the dtype;
  * UNSUPPORTED if the plan is a decode plan. */

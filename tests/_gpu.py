@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 import oracle as O
-from synthetic.gen import Inputs, BF16, FP8
+from synthetic.gen import Inputs, BF16, FP8, MXFP4
 
 BAND = 1e-3          # selection tie band on block scores
 MS_ATOL, MS_RTOL = 1e-4, 1e-5
@@ -60,13 +60,16 @@ def oracle_scores(inp: Inputs, rows=None):
 # fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) does not accumulate exactly:
 # measured on random e4m3 operands, a length-128 dot product is off by up to
 # 2^-12.5 of the sum of its absolute products (median 2^-16).  fp8 proxy
-# scores are therefore compared within 2^-12 of that magnitude.
+# scores (and the fp8 x MXFP4 scores of the same instruction) are therefore
+# compared within 2^-12 of that magnitude.
 FP8_ACC_REL = 2.0 ** -12
+LOW_PRECISION_PROXY = (FP8, MXFP4)
 
 
 def fp8_score_bound(inp, rows, scale):
     """Per (row, head, block): 2^-12 * scale * max over the block's visible
-    keys of sum_d |q_d k_d| (dequantised values), for fp8 proxy tolerances."""
+    keys of sum_d |q_d k_d| (dequantised values), for fp8 / MXFP4 proxy
+    tolerances."""
     w = inp.w
     lay = O.Layout(w.qo_lens, w.kv_lens, w.page_size)
     P, Pk = w.num_proxy_heads, w.num_proxy_kv_heads
@@ -82,8 +85,8 @@ def fp8_score_bound(inp, rows, scale):
         for p in range(P):
             ph = p if Pk == P else 0
             if ph not in Kc:
-                Kc[ph] = np.abs(O.gather_rows(inp.proxy_k_pages, FP8, inp.proxy_k_scale, inp.kv_indices, lay, s, ph,
-                                              np.arange(L)))
+                Kc[ph] = np.abs(O.gather_rows(inp.proxy_k_pages, w.proxy_dtype, inp.proxy_k_scale, inp.kv_indices,
+                                              lay, s, ph, np.arange(L)))
             q = np.abs(O.dequant(inp.proxy_q[np.asarray(rows)[idx], p:p + 1, :], FP8, inp.proxy_q_scale[p:p + 1]))[:, 0]
             S = q @ Kc[ph].T
             S[np.arange(L)[None, :] > pos[:, None]] = 0.0

@@ -140,21 +140,22 @@ def test_decode_fp8_b32_131k_all_outputs():
     assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-3
 
 
-def test_decode_step_indexer_and_decode_b32_131k():
+@pytest.mark.parametrize("wn", [6, 7])
+def test_decode_step_indexer_and_decode_b32_131k(wn):
     """A whole decode step at 32 x 131072: the indexer pass (8 fp8 proxy
-    heads sharing one proxy-K head, on a one-query-row plan) selects 16 + 1
+    heads sharing one fp8 or MXFP4 proxy-K head, on a one-query-row plan) selects 16 + 1
     blocks per (sequence, group), then the fp8 sparse decode runs on that
     selection.  Fused and separate indexer calls agree bit for bit; block
     scores, selections and outputs are checked against the oracle for every
     sequence."""
     from block_sparse_top_amd import msa
     from synthetic.gen import Inputs
-    w = workload(6)
+    w = workload(wn)
     S = w.num_seqs
     print(f"[fullsize] decode step workload={w.name}", flush=True)
-    inp = make_inputs_device(w, seed_of(6))
+    inp = make_inputs_device(w, seed_of(wn))
     ip = msa.msa_plan([1] * S, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads, w.num_proxy_kv_heads,
-                      topk=w.topk, proxy_dtype="fp8")
+                      topk=w.topk, proxy_dtype=w.proxy_dtype)
     dp = msa.msa_plan(None, w.kv_lens, w.num_qo_heads, w.num_kv_heads, topk=w.topk, kv_dtype="fp8", mode="decode")
     sel = torch.full((S, w.num_kv_heads, w.topk), -7, dtype=torch.int32, device="cuda")
     msa.msa_proxy_topk_select(ip, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale,
@@ -176,7 +177,7 @@ def test_decode_step_indexer_and_decode_b32_131k():
     h = {k: to_host(getattr(inp, k)) for k in ("q", "kv_indices", "proxy_q", "proxy_k_pages", "proxy_q_scale",
                                                 "proxy_k_scale", "k_scale", "v_scale")}
     ref_ms = O.proxy_block_maxscore(h["proxy_q"], h["proxy_k_pages"], h["kv_indices"], [1] * S, w.kv_lens, 128,
-                                    w.proxy_sm_scale, FP8, h["proxy_q_scale"], h["proxy_k_scale"])
+                                    w.proxy_sm_scale, w.proxy_dtype, h["proxy_q_scale"], h["proxy_k_scale"])
     hi = Inputs(w, h["kv_indices"], h["q"], None, None, proxy_q=h["proxy_q"], proxy_k_pages=h["proxy_k_pages"],
                 proxy_q_scale=h["proxy_q_scale"], proxy_k_scale=h["proxy_k_scale"])
     check_max_score(gms, ref_ms, w.name, fp8_score_bound(hi, rows, w.proxy_sm_scale))

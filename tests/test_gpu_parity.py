@@ -18,9 +18,9 @@ import pytest
 import torch
 
 import oracle as O
-from synthetic.gen import Workload, make_inputs, workload, seed_of, FP8, BF16
+from synthetic.gen import Workload, make_inputs, workload, seed_of, FP8, BF16, MXFP4
 from tests._gpu import (device_inputs, plan_for, bf16_out_to_f64, oracle_scores, check_max_score, check_selection,
-                        check_output, fp8_score_bound, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS)
+                        check_output, fp8_score_bound, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS, LOW_PRECISION_PROXY)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,11 @@ PREFILL_CASES = {
                                            proxy_dtype=FP8, extra_pages=0.1, poison_tail=True), 26, 0),
     "onerow_bf16_per_head_proxy_k": (Workload("row1b", [1] * 5, [300, 7000, 256, 1, 4000], 8, 2, 2, 2, topk=5,
                                               poison_tail=True), 27, 0),
+    # MXFP4 proxy K (fp8 proxy q): NaN scale bytes in spare pages and page tails
+    "onerow_mxfp4_shared_proxy_k": (Workload("row1c", [1] * 6, [1000, 128, 129, 2000, 5000, 131], 16, 2, 2, 1,
+                                             topk=17, proxy_dtype=MXFP4, extra_pages=0.1, poison_tail=True), 28, 0),
+    "onerow_mxfp4_per_head_proxy_k": (Workload("row1d", [1] * 5, [300, 7000, 256, 1, 4000], 8, 2, 2, 2, topk=5,
+                                               proxy_dtype=MXFP4, lowrank=8, poison_tail=True), 29, 0),
 }
 
 
@@ -82,7 +87,8 @@ def test_prefill_stages_match_oracle(case):
     print(f"[parity] prefill case={case} T={w.total_rows} seed={seed}", flush=True)
     gms, gsel, gout, glse = run_prefill_stages(msa, inp, max_rows)
     ref_ms = oracle_scores(inp)
-    extra = fp8_score_bound(inp, np.arange(w.total_rows), w.proxy_sm_scale) if w.proxy_dtype == FP8 else None
+    extra = (fp8_score_bound(inp, np.arange(w.total_rows), w.proxy_sm_scale) if w.proxy_dtype in LOW_PRECISION_PROXY
+             else None)
     check_max_score(gms, ref_ms, case, extra)
     lay = O.Layout(w.qo_lens, w.kv_lens, w.page_size)
     locals_ = np.array([lay.local(r) for r in range(w.total_rows)])
