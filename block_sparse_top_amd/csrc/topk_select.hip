@@ -160,35 +160,61 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 }
 
 
-// Wave-uniform max: 16-lane row reductions by DPP (quad_perm xor 1,
+// Wave-uniform unsigned max: 16-lane row reductions by DPP (quad_perm xor 1,
 // xor 2, then row_ror 4, 8), then the four row results read by readlane.
 template <int CTRL>
-__device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
-__device__ __forceinline__ float wave_max_uniform(float v) {
-  v = fmaxf(v, __int_as_float(dpp<0xB1>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp<0x4E>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp<0x124>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp<0x128>(__float_as_int(v))));
-  const int x = __float_as_int(v);
-  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(x, 0)), __int_as_float(__builtin_amdgcn_readlane(x, 16))),
-               fmaxf(__int_as_float(__builtin_amdgcn_readlane(x, 32)), __int_as_float(__builtin_amdgcn_readlane(x, 48))));
+__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
+  v = max(v, dpp<0xB1>(v));
+  v = max(v, dpp<0x4E>(v));
+  v = max(v, dpp<0x124>(v));
+  v = max(v, dpp<0x128>(v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The largest t such that at least n lanes have v >= t, i.e. the n-th largest
+// v of the wave (n >= 1), built bit by bit from ballot counts.
+__device__ __forceinline__ uint32_t wave_nth_largest(uint32_t v, int n) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    if (__popcll(__ballot(v >= c)) >= n) t = c;
+  }
+  return t;
 }
 
 // Plans with one query row per sequence (the indexer pass of a decode step:
 // few rows, up to thousands of blocks each): one wave per (row, group), each
-// lane holding VPL scores (block b at lane b % 64, register b / 64).  Each of
-// the R = min(topk - 1, local) rounds takes the wave's best remaining score,
-// finds the lowest block holding it (register by register, ballot, lowest
-// lane) and retires it (NaN marks a retired entry or a block outside the
-// competing range: max ignores it and it equals nothing); the chosen ids and
-// the local block are then written in ascending order by rank, -1 padded.
+// lane holding VPL scores (block b at lane b % 64, register b / 64) as
+// order-preserving unsigned keys (a larger score has a larger key, -0 counts
+// as +0, key 0 marks a block outside the competing range).  With R =
+// min(topk - 1, local) competing slots:
+//  1. t = the R-th largest of the 64 lane maxima: at least R keys are >= t,
+//     so every block of the top R has a key >= t;
+//  2. if at most 64 keys are >= t, they are compacted (register by register,
+//     lane by lane: ascending block id) to one per lane in LDS, tau = their
+//     R-th largest key is found the same way, and the blocks with key > tau
+//     plus the lowest-id ones with key == tau are written in lane order, so
+//     ascending, followed by the local block and -1 padding;
+//  3. otherwise (many equal scores) R rounds each take the wave's largest
+//     key, find its lowest block by one ballot per register and retire it;
+//     ids are then ordered by rank.
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
   constexpr int kNone = 0x7fffffff;
+  __shared__ uint32_t cand_key[4][64];
+  __shared__ int32_t cand_id[4][64];
   const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
   if (pair >= a.row_count * a.P) return;
   const int64_t rl = pair / a.P;
   const int p = (int)(pair % a.P);
@@ -196,41 +222,78 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
   const int local = __builtin_amdgcn_readfirstlane((a.m.kv[r] - 1) >> 7);
   const int R = min(a.k - 1, local);
   const float* col = a.ms + (int64_t)p * a.m.nb_max * a.row_count + rl;
-  float v[VPL];
+  uint32_t key[VPL];
   const int last = max(local - 1, 0);  // clamped loads: issued back to back, always in bounds
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int b = 64 * i + lane;
     const float x = col[(int64_t)min(b, last) * a.row_count];
-    v[i] = b < local ? x : __builtin_nanf("");
+    const uint32_t u = x == 0.f ? 0u : __float_as_uint(x);
+    key[i] = b < local ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
   }
+  int32_t* dst = a.sel + ((int64_t)r * a.P + p) * a.k;
+  if (lane == 0) dst[R] = local;
+  if (lane > R && lane < a.k) dst[lane] = -1;
+  if (R == 0) return;
+
+  uint32_t lm = key[0];
+#pragma unroll
+  for (int i = 1; i < VPL; ++i) lm = max(lm, key[i]);
+  const uint32_t t = wave_nth_largest(lm, R);
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) total += __popcll(__ballot(key[i] >= t));
+
+  if (total <= 64) {
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const bool c = key[i] >= t;
+      const uint64_t m = __ballot(c);
+      if (c) {
+        const int pos = base + lanes_below(m);
+        cand_key[wave][pos] = key[i];
+        cand_id[wave][pos] = 64 * i + lane;
+      }
+      base += __popcll(m);
+    }
+    wave_lds_sync();
+    const uint32_t ck = lane < total ? cand_key[wave][lane] : 0u;
+    const int32_t cid = lane < total ? cand_id[wave][lane] : kNone;
+    const uint32_t tau = wave_nth_largest(ck, R);
+    const uint64_t gt = __ballot(ck > tau);
+    uint64_t eq = __ballot(ck == tau && lane < total);
+    uint64_t take = gt;
+    for (int need = R - __popcll(gt); need > 0; --need) {  // the lowest-id ties
+      const uint64_t low = eq & (~eq + 1);
+      take |= low;
+      eq ^= low;
+    }
+    if ((take >> lane) & 1) dst[lanes_below(take)] = cid;
+    return;
+  }
+
   int mine = kNone;  // lane j < R keeps round j's block
   for (int round = 0; round < R; ++round) {
-    float lm = v[0];
+    uint32_t km = key[0];
 #pragma unroll
-    for (int i = 1; i < VPL; ++i) lm = fmaxf(lm, v[i]);  // NaN (retired) is ignored
-    const float wm = wave_max_uniform(lm);
-    // lowest block holding the maximum: the first register with a match,
-    // its lowest matching lane
+    for (int i = 1; i < VPL; ++i) km = max(km, key[i]);
+    const uint32_t wm = wave_max_u32_uniform(km);
     int wb = kNone;
 #pragma unroll
     for (int i = VPL - 1; i >= 0; --i) {
-      const uint64_t hit = __ballot(v[i] == wm);
+      const uint64_t hit = __ballot(key[i] == wm);
       if (hit) wb = 64 * i + (int)__builtin_ctzll(hit);
     }
     if (lane == round) mine = wb;
     const bool own = lane == (wb & 63);
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-      if (i == (wb >> 6) && own) v[i] = __builtin_nanf("");  // retire it
+      if (i == (wb >> 6) && own) key[i] = 0u;  // retire it
   }
-  if (lane == R) mine = local;
-  // rank of each chosen id among the R + 1 (all distinct)
   int rank = 0;
-  for (int j = 0; j <= R; ++j) rank += __builtin_amdgcn_readlane(mine, j) < mine ? 1 : 0;
-  int32_t* dst = a.sel + ((int64_t)r * a.P + p) * a.k;
-  if (lane <= R) dst[rank] = mine;
-  else if (lane < a.k) dst[lane] = -1;
+  for (int j = 0; j < R; ++j) rank += __builtin_amdgcn_readlane(mine, j) < mine ? 1 : 0;
+  if (lane < R) dst[rank] = mine;
 }
 
 }  // namespace
