@@ -66,14 +66,14 @@ msa_status_t check_ws(const msa_plan_s* p, void* ws, size_t bytes) {
   return MSA_OK;
 }
 
-// bf16: no scales; fp8: both per-head scales; MXFP4: the fp8 proxy q's
-// scales only (proxy-K scales live in the page records)
+// Per-head fp32 scales come with fp8 tensors only: fp8 (both), MXFP4 (its
+// fp8 q); MXFP4 tensors carry their block scales in the data.
 msa_status_t check_proxy_scales(const msa_plan_s* p, const float* qs, const float* ks, const char* fn) {
   const msa_dtype_t dt = p->d.proxy_dtype;
-  const bool want_q = dt != MSA_BF16, want_k = dt == MSA_FP8_E4M3;
+  const bool want_q = dt == MSA_FP8_E4M3 || dt == MSA_MXFP4, want_k = dt == MSA_FP8_E4M3;
   if (want_q != (qs != nullptr) || want_k != (ks != nullptr))
-    return fail(MSA_ERR_INVALID_ARG, "%s: proxy_q_scale must be given iff the proxy dtype is fp8 or MXFP4, proxy_k_scale "
-                "iff it is fp8", fn);
+    return fail(MSA_ERR_INVALID_ARG, "%s: proxy_q_scale must be given iff proxy q is fp8 (fp8, MXFP4), proxy_k_scale "
+                "iff proxy K is fp8", fn);
   return MSA_OK;
 }
 
@@ -194,11 +194,9 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
   if (!(d.sm_scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "msa_plan: sm_scale must be > 0");
   if (d.mode == MSA_PREFILL) {
     if (d.kv_dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "msa_plan: prefill K/V must be bf16");
-    if (d.proxy_dtype != MSA_BF16 && d.proxy_dtype != MSA_FP8_E4M3 && d.proxy_dtype != MSA_MXFP4)
+    if (d.proxy_dtype != MSA_BF16 && d.proxy_dtype != MSA_FP8_E4M3 && d.proxy_dtype != MSA_MXFP4 &&
+        d.proxy_dtype != MSA_MXFP4_QK)
       return fail(MSA_ERR_INVALID_ARG, "msa_plan: bad proxy_dtype");
-    if (d.proxy_dtype == MSA_MXFP4 && d.batch >= 1 &&
-        !std::all_of(d.qo_lens_host, d.qo_lens_host + d.batch, [](int32_t q) { return q == 1; }))
-      return fail(MSA_ERR_UNSUPPORTED, "msa_plan: an MXFP4 proxy K is built for plans with one query row per sequence");
     if (d.num_proxy_heads != d.num_kv_heads)
       return fail(MSA_ERR_UNSUPPORTED, "msa_plan: num_proxy_heads (%d) must equal num_kv_heads (%d)",
                   d.num_proxy_heads, d.num_kv_heads);
@@ -428,32 +426,53 @@ msa_status_t msa_topk_select(msa_plan_t p, const float* max_score, int64_t row_b
   return hip_status(msa::launch_topk(p, m, max_score, row_begin, row_count, kv_block_indexes, hs), __func__);
 }
 
-msa_status_t msa_sparse_attn_prefill(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
-                                     const float* k_scale, const float* v_scale, const int32_t* kv_indices,
-                                     const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
-                                     size_t workspace_bytes, msa_stream_t stream) {
-  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill: NULL plan");
-  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_prefill: decode plan");
+static msa_status_t prefill_rows(const char* fn, msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                 const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                 const int32_t* kv_block_indexes, void* out, float* lse, int64_t row_begin,
+                                 int64_t row_count, void* workspace, size_t workspace_bytes, msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "%s: NULL plan", fn);
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "%s: decode plan", fn);
   MSA_CHECK_PTR(q);
   MSA_CHECK_PTR(k_pages);
   MSA_CHECK_PTR(v_pages);
   MSA_CHECK_PTR(kv_indices);
   MSA_CHECK_PTR(kv_block_indexes);
   MSA_CHECK_PTR(out);
-  if (lse && !aligned16(lse)) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill: lse not 16-byte aligned");
-  if (k_scale || v_scale) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill: bf16 K/V take no scales");
+  if (lse && !aligned16(lse)) return fail(MSA_ERR_INVALID_ARG, "%s: lse not 16-byte aligned", fn);
+  if (k_scale || v_scale) return fail(MSA_ERR_INVALID_ARG, "%s: bf16 K/V take no scales", fn);
+  if (row_count < 1 || row_begin < 0 || row_begin + row_count > p->T)
+    return fail(MSA_ERR_INVALID_ARG, "%s: rows [%lld, %lld) outside [0, %lld)", fn, (long long)row_begin,
+                (long long)(row_begin + row_count), (long long)p->T);
   msa_status_t st = check_ws(p, workspace, workspace_bytes);
   if (st != MSA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
   const msa::DevMeta m = msa::dev_meta(p, workspace);
-  for (int64_t w0 = 0; w0 < p->T; w0 += p->attn_window) {
-    const int32_t w1 = (int32_t)std::min<int64_t>(p->T, w0 + p->attn_window);
+  const int64_t r1 = row_begin + row_count;
+  for (int64_t w0 = row_begin; w0 < r1; w0 += p->attn_window) {
+    const int32_t w1 = (int32_t)std::min<int64_t>(r1, w0 + p->attn_window);
     hipError_t e = msa::launch_prefill_window(p, m, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse,
                                               static_cast<char*>(workspace), (int32_t)w0, w1, hs);
-    if (e != hipSuccess) return hip_status(e, __func__);
+    if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
+}
+
+msa_status_t msa_sparse_attn_prefill(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                     const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                     const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, msa_stream_t stream) {
+  return prefill_rows(__func__, p, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes, out, lse, 0,
+                      p ? p->T : 0, workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_sparse_attn_prefill_rows(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                          const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                          const int32_t* kv_block_indexes, void* out, float* lse, int64_t row_begin,
+                                          int64_t row_count, void* workspace, size_t workspace_bytes,
+                                          msa_stream_t stream) {
+  return prefill_rows(__func__, p, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes, out, lse,
+                      row_begin, row_count, workspace, workspace_bytes, stream);
 }
 
 msa_status_t msa_sparse_attn_decode(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,

@@ -26,6 +26,8 @@
 //  * workgroup order: workgroups of one proxy head are consecutive modulo
 //    the head count, so with 8 proxy heads each XCD streams one head's K
 //    through its own L2; long (late) tiles launch first.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "msa_internal.hpp"
 
@@ -55,31 +57,64 @@ struct ProxyArgs {
 // exactly as in the separate top-k over the same fp32 scores.
 constexpr int kSelCap = 16;
 
-template <bool FP8>
+// Proxy (q, K) formats: bf16 x bf16, fp8 x fp8, fp8 q x MXFP4 K, MXFP4 q x
+// MXFP4 K.  MXFP4 K rows are 64 bytes of E2M1 codes; the block's 128 x 4
+// E8M0 scale bytes follow the codes (page record); an MXFP4 q row is 64 code
+// bytes then its 4 scale bytes.
+enum class Fmt : int { BF16 = 0, FP8 = 1, MX4K = 2, MX4QK = 3 };
+
+template <Fmt F>
 struct ProxyTraits;
 
 // K tiles live in LDS unpadded, with the 16-byte chunks of each row permuted
 // (physical chunk = logical chunk ^ swz(row)) so that the 16 rows read by a
 // fragment load hit 16 distinct bank groups.
 template <>
-struct ProxyTraits<false> {
-  static constexpr int kElem = 2;             // bytes per element
-  static constexpr int kRowBytes = 256;       // one key row
+struct ProxyTraits<Fmt::BF16> {
+  static constexpr int kQRowBytes = 256;      // one proxy q row (one head)
+  static constexpr int kKRowBytes = 256;      // one key row
+  static constexpr int kKBlockBytes = 128 * 256;
   static constexpr int kSteps = 8;            // MFMA k-steps over d = 128
   __device__ static int swz(int row) { return row & 15; }
-  typedef bf16x8 Frag;
+  typedef bf16x8 AFrag;
+  typedef bf16x8 BFrag;
 };
 template <>
-struct ProxyTraits<true> {
-  static constexpr int kElem = 1;
-  static constexpr int kRowBytes = 128;
+struct ProxyTraits<Fmt::FP8> {
+  static constexpr int kQRowBytes = 128;
+  static constexpr int kKRowBytes = 128;
+  static constexpr int kKBlockBytes = 128 * 128;
   static constexpr int kSteps = 2;
   __device__ static int swz(int row) { return (row >> 1) & 7; }
-  typedef i32x8 Frag;
+  typedef i32x8 AFrag;
+  typedef i32x8 BFrag;
+};
+template <>
+struct ProxyTraits<Fmt::MX4K> {
+  static constexpr int kQRowBytes = 128;
+  static constexpr int kKRowBytes = 64;
+  static constexpr int kKBlockBytes = 128 * 64 + 128 * 4;
+  static constexpr int kSteps = 2;
+  __device__ static int swz(int row) { return (row >> 2) & 3; }
+  typedef i32x4 AFrag;
+  typedef i32x8 BFrag;
+};
+template <>
+struct ProxyTraits<Fmt::MX4QK> {
+  static constexpr int kQRowBytes = 68;
+  static constexpr int kKRowBytes = 64;
+  static constexpr int kKBlockBytes = 128 * 64 + 128 * 4;
+  static constexpr int kSteps = 2;
+  __device__ static int swz(int row) { return (row >> 2) & 3; }
+  typedef i32x4 AFrag;
+  typedef i32x4 BFrag;
 };
 
+template <Fmt F>
+constexpr bool kMxK = F == Fmt::MX4K || F == Fmt::MX4QK;
+
 template <bool FP8>
-__device__ __forceinline__ typename ProxyTraits<FP8>::Frag load_frag_global(const uint8_t* p) {
+__device__ __forceinline__ typename std::conditional<FP8, i32x8, bf16x8>::type load_frag_global(const uint8_t* p) {
   if constexpr (FP8) {
     i32x4 a = *reinterpret_cast<const i32x4*>(p);
     i32x4 b = *reinterpret_cast<const i32x4*>(p + 16);
@@ -92,41 +127,84 @@ __device__ __forceinline__ typename ProxyTraits<FP8>::Frag load_frag_global(cons
   }
 }
 
-// A fragment of key row `row`, logical 16-byte chunk `c` (and c+1 for fp8).
-template <bool FP8>
-__device__ __forceinline__ typename ProxyTraits<FP8>::Frag load_frag_lds(const uint8_t* tile, int row, int c) {
-  using Tr = ProxyTraits<FP8>;
-  const uint8_t* base = tile + row * Tr::kRowBytes;
-  if constexpr (FP8) {
-    i32x4 a = lds_load16<i32x4>(base + ((c ^ Tr::swz(row)) << 4));
-    i32x4 b = lds_load16<i32x4>(base + (((c + 1) ^ Tr::swz(row)) << 4));
-    i32x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-    return r;
+// 16 bytes from a 4-byte aligned address (MXFP4 q rows are 68 bytes apart)
+__device__ __forceinline__ i32x4 load16_a4(const uint8_t* p) {
+  const int32_t* q = reinterpret_cast<const int32_t*>(p);
+  return i32x4{q[0], q[1], q[2], q[3]};
+}
+
+// The B fragment (proxy q) of k-step st for lane half h, from a q row in
+// global memory; for MXFP4 q also the lane's scale word (byte 2st + h is
+// picked by op_sel 2st after the shift).  FP4 operands: lane half h holds
+// one whole 32-dim MX block, 2st + h (codes 0-15 at k = 16h.., 16-31 at
+// k = 32 + 16h..); the fp8 q of the (fp8 q, MXFP4 K) pair is gathered in
+// that k order: dims 64st + 16h .. +15, then 64st + 32 + 16h .. +15.
+template <Fmt F>
+__device__ __forceinline__ typename ProxyTraits<F>::BFrag load_q_frag(const uint8_t* row, int st, int h) {
+  using Tr = ProxyTraits<F>;
+  if constexpr (F == Fmt::BF16 || F == Fmt::FP8) {
+    constexpr int kStepBytes = Tr::kQRowBytes / Tr::kSteps;
+    return load_frag_global<F == Fmt::FP8>(row + st * kStepBytes + h * (kStepBytes / 2));
+  } else if constexpr (F == Fmt::MX4K) {
+    const i32x4 x = *reinterpret_cast<const i32x4*>(row + 64 * st + 16 * h);
+    const i32x4 y = *reinterpret_cast<const i32x4*>(row + 64 * st + 32 + 16 * h);
+    return i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
   } else {
-    return lds_load16<bf16x8>(base + ((c ^ Tr::swz(row)) << 4));
+    return load16_a4(row + 16 * (2 * st + h));
   }
 }
 
-template <bool FP8>
-__device__ __forceinline__ f32x16 mma(const typename ProxyTraits<FP8>::Frag& a,
-                                      const typename ProxyTraits<FP8>::Frag& b, const f32x16& c) {
-  if constexpr (FP8) return mfma32x32x64_fp8(a, b, c);
-  else return mfma32x32x16(a, b, c);
+// The A fragment (K) of key row `row`, k-step st, lane half h, from an LDS tile.
+template <Fmt F>
+__device__ __forceinline__ typename ProxyTraits<F>::AFrag load_k_frag(const uint8_t* tile, int row, int st, int h) {
+  using Tr = ProxyTraits<F>;
+  const uint8_t* base = tile + row * Tr::kKRowBytes;
+  if constexpr (F == Fmt::BF16) {
+    return lds_load16<bf16x8>(base + (((h + 2 * st) ^ Tr::swz(row)) << 4));
+  } else if constexpr (F == Fmt::FP8) {
+    const int c = 2 * h + 4 * st;
+    i32x4 a = lds_load16<i32x4>(base + ((c ^ Tr::swz(row)) << 4));
+    i32x4 b = lds_load16<i32x4>(base + (((c + 1) ^ Tr::swz(row)) << 4));
+    return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    return lds_load16<i32x4>(base + (((2 * st + h) ^ Tr::swz(row)) << 4));
+  }
+}
+
+// One k-step of S^T = K Q^T.  sa / sb: the lanes' E8M0 scale words (MXFP4
+// operands), byte 2st picked by op_sel; fp8 operands take scale 2^0.
+template <Fmt F>
+__device__ __forceinline__ f32x16 mma(const typename ProxyTraits<F>::AFrag& a,
+                                      const typename ProxyTraits<F>::BFrag& b, const f32x16& c, int st, int32_t sa,
+                                      int32_t sb) {
+  if constexpr (F == Fmt::BF16) {
+    return mfma32x32x16(a, b, c);
+  } else if constexpr (F == Fmt::FP8) {
+    return mfma32x32x64_fp8(a, b, c);
+  } else if constexpr (F == Fmt::MX4K) {
+    const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    return st == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, c, 4, 0, 0, sa, 0, 127)
+                   : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, c, 4, 0, 2, sa, 0, 127);
+  } else {
+    const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    return st == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb)
+                   : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 2, sa, 2, sb);
+  }
 }
 
 constexpr int kProxyWaves = 8;
 
-template <bool FP8, bool TOPK>
+template <Fmt F, bool TOPK>
 __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyArgs a) {
-  using Tr = ProxyTraits<FP8>;
-  using Frag = typename Tr::Frag;
-  constexpr int kBlockBytes = 128 * Tr::kRowBytes;        // one K block in global memory
-  constexpr int kLoads = kBlockBytes / 1024 / kProxyWaves;  // 1 KB direct-to-LDS loads per wave
-  constexpr int kChunksPerRow = Tr::kRowBytes / 16;
-  constexpr int kRowsPerKB = 1024 / Tr::kRowBytes;
-  constexpr int kStepBytes = Tr::kRowBytes / Tr::kSteps;  // bytes of d per MFMA k-step
+  using Tr = ProxyTraits<F>;
+  using AFrag = typename Tr::AFrag;
+  using BFrag = typename Tr::BFrag;
+  constexpr int kBlockBytes = Tr::kKBlockBytes;           // one K block in global memory
+  constexpr int kCodeBytes = 128 * Tr::kKRowBytes;        // its key rows (MXFP4: the scales follow)
+  constexpr int kLoads = kCodeBytes / 1024 / kProxyWaves;  // 1 KB direct-to-LDS loads per wave
+  constexpr int kChunksPerRow = Tr::kKRowBytes / 16;
+  constexpr int kRowsPerKB = 1024 / Tr::kKRowBytes;
   // two distinct tile objects (not one array indexed by a runtime buffer
   // number): the loads in flight into one are then provably disjoint from
   // the reads of the other
@@ -135,6 +213,7 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int hsel = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave branches stay scalar
   const int p = blockIdx.x % a.P;
   const int t = a.tile_lo + (a.ntiles - 1 - (int)(blockIdx.x / a.P));
@@ -148,23 +227,28 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
   const int b_full = (pos0 + 1) >> 7;  // blocks < b_full are visible to every row of the tile
 
   // Q fragments (B operand): lane -> query column lane%32 of row tile `sub`,
-  // k-run (lane/32) of each k-step.
-  Frag qf[2][Tr::kSteps];
+  // k-run (lane/32) of each k-step; MXFP4 q also a scale word per row.
+  BFrag qf[2][Tr::kSteps];
+  int32_t qsc[2] = {0x7f7f7f7f, 0x7f7f7f7f};
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     const int r = 64 * wave + 32 * sub + (lane & 31);
     const bool valid = r < nrows;
-    const uint8_t* src = a.pq + ((int64_t)(row0 + (valid ? r : 0)) * a.P + p) * (128 * Tr::kElem);
+    const uint8_t* src = a.pq + ((int64_t)(row0 + (valid ? r : 0)) * a.P + p) * Tr::kQRowBytes;
 #pragma unroll
     for (int s = 0; s < Tr::kSteps; ++s) {
-      qf[sub][s] = load_frag_global<FP8>(src + s * kStepBytes + (lane >> 5) * (kStepBytes / 2));
-      if (!valid) qf[sub][s] = Frag{};
+      qf[sub][s] = load_q_frag<F>(src, s, hsel);
+      if (!valid) qf[sub][s] = BFrag{};
+    }
+    if constexpr (F == Fmt::MX4QK) {
+      if (valid) qsc[sub] = (int32_t)(*reinterpret_cast<const uint32_t*>(src + 64) >> (8 * hsel));
     }
   }
 
   // K block -> LDS without registers: each wave issues kLoads direct 1 KB
   // loads (global_load_lds_dwordx4: lane i fills bytes 16i..16i+15 of the
-  // KB), fetching for each lane the global chunk its swizzled slot holds.
+  // KB), fetching for each lane the global chunk its swizzled slot holds;
+  // an MXFP4 block's 512 scale bytes follow unswizzled (the last wave).
   auto kload = [&](int32_t page, uint8_t* tile) {
     const uint8_t* src = a.pk + ((int64_t)page * a.Pk + ph) * kBlockBytes;
 #pragma unroll
@@ -173,12 +257,17 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
       const int row = kb * kRowsPerKB + lane / kChunksPerRow;
       const int pc = lane % kChunksPerRow;               // physical chunk written by this lane
       const int lc = pc ^ Tr::swz(row);                  // logical chunk it must hold
-      global_load_lds16(src + row * Tr::kRowBytes + lc * 16, (MSA_LDS void*)(tile + kb * 1024));
+      global_load_lds16(src + row * Tr::kKRowBytes + lc * 16, (MSA_LDS void*)(tile + kb * 1024));
+    }
+    if constexpr (kMxK<F>) {
+      if (wave == kProxyWaves - 1 && lane < 32)
+        global_load_lds16(src + kCodeBytes + lane * 16, (MSA_LDS void*)(tile + kCodeBytes));
     }
   };
 
   float scale = a.scale;
-  if constexpr (FP8) scale *= a.qs[p] * a.ks[ph];
+  if constexpr (F == Fmt::FP8) scale *= a.qs[p] * a.ks[ph];
+  if constexpr (F == Fmt::MX4K) scale *= a.qs[p];
   const bool wave_active = 64 * wave < nrows;
   const int my_row = 64 * wave + lane;          // row this lane writes
   const int64_t my_grow = row0 + my_row;
@@ -193,7 +282,6 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
     tv[j] = kNegInf;
     ti[j] = -1;
   }
-  const int chunk0 = ((lane >> 5) * (kStepBytes / 2)) >> 4;
 
   // Fused selection: after each block, its score is inserted into the row's
   // list, sorted by descending score with equal scores in ascending block
@@ -230,21 +318,27 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
       f32x16 acc[2][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = f32x16{};
-      Frag fr[2][2];
+      int32_t ksc[2] = {0, 0};
+      if constexpr (kMxK<F>) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fr[0][j] = load_frag_lds<FP8>(tile, 32 * (2 * hf + j) + (lane & 31), chunk0);
+        for (int j = 0; j < 2; ++j)
+          ksc[j] = (int32_t)(lds_load16<uint32_t>(tile + kCodeBytes + 4 * (32 * (2 * hf + j) + (lane & 31))) >>
+                             (8 * hsel));
+      }
+      AFrag fr[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fr[0][j] = load_k_frag<F>(tile, 32 * (2 * hf + j) + (lane & 31), 0, hsel);
 #pragma unroll
       for (int st = 0; st < Tr::kSteps; ++st) {
         if (st + 1 < Tr::kSteps) {
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            fr[(st + 1) & 1][j] = load_frag_lds<FP8>(tile, 32 * (2 * hf + j) + (lane & 31),
-                                                     chunk0 + (((st + 1) * kStepBytes) >> 4));
+            fr[(st + 1) & 1][j] = load_k_frag<F>(tile, 32 * (2 * hf + j) + (lane & 31), st + 1, hsel);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          acc[j][0] = mma<FP8>(fr[st & 1][j], qf[0][st], acc[j][0]);
-          acc[j][1] = mma<FP8>(fr[st & 1][j], qf[1][st], acc[j][1]);
+          acc[j][0] = mma<F>(fr[st & 1][j], qf[0][st], acc[j][0], st, ksc[j], qsc[0]);
+          acc[j][1] = mma<F>(fr[st & 1][j], qf[1][st], acc[j][1], st, ksc[j], qsc[1]);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep LDS fragment reads one k-step ahead at most
       }
@@ -382,11 +476,11 @@ struct ProxyRowArgs {
 
 constexpr int kRowWaves = 4;
 
-template <bool FP8>
+template <Fmt F>
 __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowArgs a) {
-  using Tr = ProxyTraits<FP8>;
-  using Frag = typename Tr::Frag;
-  constexpr int kStepBytes = Tr::kRowBytes / Tr::kSteps;
+  static_assert(F == Fmt::BF16 || F == Fmt::FP8, "MXFP4 K has its own kernel below");
+  using Tr = ProxyTraits<F>;
+  using Frag = typename Tr::AFrag;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rl = blockIdx.z;              // row within the call's range
@@ -403,21 +497,21 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
   // B operand: the served heads' proxy q rows (zero columns past ncols)
   Frag qf[Tr::kSteps];
   {
-    const uint8_t* src = a.pq + ((int64_t)seq * a.P + head) * (128 * Tr::kElem) + hsel * (kStepBytes / 2);
+    const uint8_t* src = a.pq + ((int64_t)seq * a.P + head) * Tr::kQRowBytes;
 #pragma unroll
     for (int st = 0; st < Tr::kSteps; ++st) {
-      qf[st] = load_frag_global<FP8>(src + st * kStepBytes);
+      qf[st] = load_q_frag<F>(src, st, hsel);
       if (!col_ok) qf[st] = Frag{};
     }
   }
   float scale = a.scale;
-  if constexpr (FP8) scale *= a.qs[head] * a.ks[kh];
+  if constexpr (F == Fmt::FP8) scale *= a.qs[head] * a.ks[kh];
   const int32_t* pages = a.kv_indices + a.m.page_start[seq];
+  // a key row in global memory has the q row's layout: same fragment loads
   auto load_tile = [&](Frag (&f)[Tr::kSteps], int32_t page, int t) {
-    const uint8_t* src = a.pk + ((int64_t)page * a.Pk + kh) * (128 * Tr::kRowBytes) + (32 * t + j) * Tr::kRowBytes +
-                         hsel * (kStepBytes / 2);
+    const uint8_t* src = a.pk + ((int64_t)page * a.Pk + kh) * Tr::kKBlockBytes + (32 * t + j) * Tr::kKRowBytes;
 #pragma unroll
-    for (int st = 0; st < Tr::kSteps; ++st) f[st] = load_frag_global<FP8>(src + st * kStepBytes);
+    for (int st = 0; st < Tr::kSteps; ++st) f[st] = load_q_frag<F>(src, st, hsel);
   };
   // Software pipeline over whole blocks: block b + 4's sixteen KB (fp8: 64
   // VGPRs per buffer) is in flight while block b is multiplied.
@@ -436,7 +530,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
     for (int t = 0; t < 4; ++t) {
       f32x16 acc = f32x16{};
 #pragma unroll
-      for (int st = 0; st < Tr::kSteps; ++st) acc = mma<FP8>(cur[t][st], qf[st], acc);
+      for (int st = 0; st < Tr::kSteps; ++st) acc = mma<F>(cur[t][st], qf[st], acc, st, 0, 0);
       // C[i][j]: key 32t + 8(r/4) + 4 hsel + r%4 of register r; keys at or
       // past kv_len are page padding
       const int lim = kv_len - 1 - (b * 128 + 32 * t + 4 * hsel);
@@ -456,35 +550,22 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
 }
 
 // MXFP4 proxy K, one query row per sequence.  A page record of one proxy-K
-// head holds 128 key rows of E2M1 codes (64 B each, element 2i in the low
-// nibble of byte i), then 128 rows of E8M0 scales (4 B each, byte c scaling
-// dims 32c..32c+31).  The scaled f8f6f4 MFMA takes the codes as its FP4 A
-// operand and the fp8 proxy q as its B operand (unit scale), so every product
-// is exact.  FP4 A layout of v_mfma_scale_f32_32x32x64_f8f6f4 (probed): lane
-// (row i, half h) holds 32 codes, codes 0-15 at k = 16h..16h+15 and codes
-// 16-31 at k = 32+16h..47+16h, and its own scale byte (picked by op_sel)
-// scales all 32.  So a lane takes one whole MX block: at k-step st, lane
-// (key j, h) holds block 2st + h (the 16 code bytes at 32st + 16h of the key
-// row) with that block's scale byte (the key's scale word shifted right by
-// 8h, op_sel 2st), and the q fragment of lane (column, h') pairs with it:
-// dims 64st + 16h' .. +15 then 64st + 32 + 16h' .. +15.  Schedule as in the
-// fp8/bf16 kernel above: whole blocks, the next one in flight.
-constexpr int kMxRowCodeBytes = 64;                          // 128 dims x 4 bits
-constexpr int kMxRecordBytes = 128 * kMxRowCodeBytes + 128 * 4;
-
+// head holds 128 key rows of E2M1 codes, then 128 rows of E8M0 scales (the
+// MXFP4 record above).  The scaled f8f6f4 MFMA takes the codes as its FP4 A
+// operand with each lane's own block scale, and the proxy q (fp8, or MXFP4
+// with its own scales) as its B operand, so every product is exact; see
+// load_q_frag for the lane layout.  Schedule as in the fp8/bf16 kernel
+// above: whole blocks, the next one in flight.
 struct MxTile {
   i32x4 c[2];  // MX blocks h and 2 + h of key j (k-steps 0 and 1)
   int32_t sc;  // the key's four scale bytes >> 8h
 };
 
-template <int ST>
-__device__ __forceinline__ f32x16 mma_fp4_fp8(const i32x4& a, const i32x8& b, int32_t sa, const f32x16& c) {
-  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
-  // format codes: A = 4 (E2M1), B = 0 (E4M3); A's scale is byte 2 ST of sa, B's 2^0
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, c, 4, 0, 2 * ST, sa, 0, 127);
-}
-
+template <Fmt F>
 __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(ProxyRowArgs a) {
+  static_assert(kMxK<F>, "MXFP4 K only");
+  using Tr = ProxyTraits<F>;
+  constexpr int kCodeBytes = 128 * Tr::kKRowBytes;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rl = blockIdx.z;
@@ -498,25 +579,26 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(Prox
   const int j = lane & 31, hsel = lane >> 5;
   const bool col_ok = j < ncols;
   const int head = a.Pk == 1 ? (col_ok ? j : 0) : kh;
-  i32x8 qf[2];
+  typename Tr::BFrag qf[2];
+  int32_t qsc = 0x7f7f7f7f;
   {
-    const uint8_t* src = a.pq + ((int64_t)seq * a.P + head) * 128 + hsel * 16;
+    const uint8_t* src = a.pq + ((int64_t)seq * a.P + head) * Tr::kQRowBytes;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const i32x4 x = *reinterpret_cast<const i32x4*>(src + 64 * st);
-      const i32x4 y = *reinterpret_cast<const i32x4*>(src + 64 * st + 32);
-      qf[st] = col_ok ? i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]} : i32x8{};
+    for (int st = 0; st < 2; ++st) qf[st] = col_ok ? load_q_frag<F>(src, st, hsel) : typename Tr::BFrag{};
+    if constexpr (F == Fmt::MX4QK) {
+      if (col_ok) qsc = (int32_t)(*reinterpret_cast<const uint32_t*>(src + 64) >> (8 * hsel));
     }
   }
-  const float scale = a.scale * a.qs[head];
+  float scale = a.scale;
+  if constexpr (F == Fmt::MX4K) scale *= a.qs[head];
   const int32_t* pages = a.kv_indices + a.m.page_start[seq];
   auto load_tile = [&](MxTile& f, int32_t page, int t) {
-    const uint8_t* rec = a.pk + ((int64_t)page * a.Pk + kh) * kMxRecordBytes;
+    const uint8_t* rec = a.pk + ((int64_t)page * a.Pk + kh) * Tr::kKBlockBytes;
     const int key = 32 * t + j;
-    const uint8_t* cp = rec + key * kMxRowCodeBytes + hsel * 16;
+    const uint8_t* cp = rec + key * Tr::kKRowBytes + hsel * 16;
     f.c[0] = *reinterpret_cast<const i32x4*>(cp);
     f.c[1] = *reinterpret_cast<const i32x4*>(cp + 32);
-    f.sc = (int32_t)(*reinterpret_cast<const uint32_t*>(rec + 128 * kMxRowCodeBytes + key * 4) >> (8 * hsel));
+    f.sc = (int32_t)(*reinterpret_cast<const uint32_t*>(rec + kCodeBytes + key * 4) >> (8 * hsel));
   };
   int b = b0 + wave;
   if (b >= b1) return;
@@ -532,8 +614,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(Prox
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x16 acc = f32x16{};
-      acc = mma_fp4_fp8<0>(cur[t].c[0], qf[0], cur[t].sc, acc);
-      acc = mma_fp4_fp8<1>(cur[t].c[1], qf[1], cur[t].sc, acc);
+      acc = mma<F>(cur[t].c[0], qf[0], acc, 0, cur[t].sc, qsc);
+      acc = mma<F>(cur[t].c[1], qf[1], acc, 1, cur[t].sc, qsc);
       const int lim = kv_len - 1 - (b * 128 + 32 * t + 4 * hsel);
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
@@ -582,12 +664,20 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
                     (unsigned)row_count);
     {
       ProfEvents pe(p, sel ? "proxy_topk" : "proxy_maxscore");
-      if (p->d.proxy_dtype == MSA_MXFP4)
-        hipExtLaunchKernelGGL(proxy_onerow_mxfp4_kernel, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
-      else if (p->d.proxy_dtype == MSA_FP8_E4M3)
-        hipExtLaunchKernelGGL(proxy_onerow_kernel<true>, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
-      else
-        hipExtLaunchKernelGGL(proxy_onerow_kernel<false>, grid, dim3(64 * kRowWaves), 0, st, pe.start, pe.stop, 0, r);
+      const dim3 blk(64 * kRowWaves);
+      switch (p->d.proxy_dtype) {
+        case MSA_MXFP4_QK:
+          hipExtLaunchKernelGGL(proxy_onerow_mxfp4_kernel<Fmt::MX4QK>, grid, blk, 0, st, pe.start, pe.stop, 0, r);
+          break;
+        case MSA_MXFP4:
+          hipExtLaunchKernelGGL(proxy_onerow_mxfp4_kernel<Fmt::MX4K>, grid, blk, 0, st, pe.start, pe.stop, 0, r);
+          break;
+        case MSA_FP8_E4M3:
+          hipExtLaunchKernelGGL(proxy_onerow_kernel<Fmt::FP8>, grid, blk, 0, st, pe.start, pe.stop, 0, r);
+          break;
+        default:
+          hipExtLaunchKernelGGL(proxy_onerow_kernel<Fmt::BF16>, grid, blk, 0, st, pe.start, pe.stop, 0, r);
+      }
     }
     if (sel) return launch_topk(p, m, scratch, row_begin, row_count, sel, st);
     return hipGetLastError();
@@ -614,15 +704,13 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
   a.k = p->d.topk;
   a.scale = p->d.proxy_sm_scale;
   const dim3 grid((unsigned)(a.ntiles * a.P)), block(64 * kProxyWaves);
-  const bool fp8 = p->d.proxy_dtype == MSA_FP8_E4M3;
-  if (sel) {
-    ProfEvents pe(p, "proxy_topk");
-    if (fp8) hipExtLaunchKernelGGL((proxy_maxscore_kernel<true, true>), grid, block, 0, st, pe.start, pe.stop, 0, a);
-    else hipExtLaunchKernelGGL((proxy_maxscore_kernel<false, true>), grid, block, 0, st, pe.start, pe.stop, 0, a);
-  } else {
-    ProfEvents pe(p, "proxy_maxscore");
-    if (fp8) hipExtLaunchKernelGGL((proxy_maxscore_kernel<true, false>), grid, block, 0, st, pe.start, pe.stop, 0, a);
-    else hipExtLaunchKernelGGL((proxy_maxscore_kernel<false, false>), grid, block, 0, st, pe.start, pe.stop, 0, a);
+  ProfEvents pe(p, sel ? "proxy_topk" : "proxy_maxscore");
+  auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, grid, block, 0, st, pe.start, pe.stop, 0, a); };
+  switch (p->d.proxy_dtype) {
+    case MSA_MXFP4_QK: sel ? go(proxy_maxscore_kernel<Fmt::MX4QK, true>) : go(proxy_maxscore_kernel<Fmt::MX4QK, false>); break;
+    case MSA_MXFP4: sel ? go(proxy_maxscore_kernel<Fmt::MX4K, true>) : go(proxy_maxscore_kernel<Fmt::MX4K, false>); break;
+    case MSA_FP8_E4M3: sel ? go(proxy_maxscore_kernel<Fmt::FP8, true>) : go(proxy_maxscore_kernel<Fmt::FP8, false>); break;
+    default: sel ? go(proxy_maxscore_kernel<Fmt::BF16, true>) : go(proxy_maxscore_kernel<Fmt::BF16, false>);
   }
   return hipGetLastError();
 }

@@ -19,13 +19,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE_TOO_SMALL, MSA_ERR_HIP = range(5)
-MSA_BF16, MSA_FP8_E4M3, MSA_MXFP4 = 0, 1, 2
+MSA_BF16, MSA_FP8_E4M3, MSA_MXFP4, MSA_MXFP4_QK = 0, 1, 2, 3
 MSA_PREFILL, MSA_DECODE = 0, 1
 
 ENTRY_POINTS = ("msa_plan", "msa_plan_destroy", "msa_plan_info", "msa_proxy_block_maxscore", "msa_topk_select",
-               "msa_proxy_topk_select",
-                "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_last_error", "msa_profile_kernel",
-                "msa_profile_read")
+                "msa_proxy_topk_select", "msa_sparse_attn_prefill", "msa_sparse_attn_prefill_rows",
+                "msa_sparse_attn_decode", "msa_last_error", "msa_profile_kernel", "msa_profile_read")
 
 
 class MsaError(RuntimeError):
@@ -71,6 +70,7 @@ def _load() -> ctypes.CDLL:
     lib.msa_topk_select.argtypes = [P, FP, I64, I64, IP, VP, SZ, P]
     lib.msa_proxy_topk_select.argtypes = [P, VP, VP, FP, FP, IP, I64, I64, IP, VP, SZ, P]
     lib.msa_sparse_attn_prefill.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
+    lib.msa_sparse_attn_prefill_rows.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, I64, I64, VP, SZ, P]
     lib.msa_sparse_attn_decode.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
     lib.msa_profile_kernel.argtypes = [P, ctypes.c_char_p]
     lib.msa_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -106,7 +106,7 @@ def _stream():
 
 
 def _dtype_code(name: str) -> int:
-    return {"bf16": MSA_BF16, "fp8": MSA_FP8_E4M3, "mxfp4": MSA_MXFP4}[name]
+    return {"bf16": MSA_BF16, "fp8": MSA_FP8_E4M3, "mxfp4": MSA_MXFP4, "mxfp4_qk": MSA_MXFP4_QK}[name]
 
 
 class Plan:
@@ -129,8 +129,9 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
-            _lib.msa_plan_destroy(h)
+        lib_ = _lib  # None once the interpreter has torn the module down
+        if h is not None and h.value and lib_ is not None:
+            lib_.msa_plan_destroy(h)
             self.handle = None
 
 
@@ -188,6 +189,15 @@ def msa_sparse_attn_prefill(plan: Plan, q, k_pages, v_pages, kv_indices, kv_bloc
     return out, lse
 
 
+def msa_sparse_attn_prefill_rows(plan: Plan, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, row_begin,
+                                 row_count, lse=None, k_scale=None, v_scale=None):
+    _check(_lib.msa_sparse_attn_prefill_rows(plan.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                             _ptr(v_scale), _ptr(kv_indices), _ptr(kv_block_indexes), _ptr(out),
+                                             _ptr(lse), row_begin, row_count, _ptr(plan.workspace),
+                                             plan.workspace_bytes, _stream()))
+    return out, lse
+
+
 def msa_sparse_attn_decode(plan: Plan, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes, out,
                            lse=None):
     _check(_lib.msa_sparse_attn_decode(plan.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
@@ -212,6 +222,14 @@ def max_score_buffer(plan: Plan, device=None) -> torch.Tensor:
     """fp32 [P, nb_max, max_rows_per_call] buffer for the proxy/top-k chunks."""
     P = plan.desc.num_proxy_heads
     return torch.empty((P, plan.nb_max, plan.max_rows_per_call), dtype=torch.float32, device=device or "cuda")
+
+
+def max_score_rows(max_score: torch.Tensor, plan: Plan, row_count: int) -> torch.Tensor:
+    """The [P, nb_max, row_count] result of a proxy call over row_count rows:
+    the call writes it densely at the start of the buffer (row stride =
+    row_count), so a shorter last chunk is not a slice of the full buffer."""
+    P = plan.desc.num_proxy_heads
+    return max_score.view(-1)[:P * plan.nb_max * row_count].view(P, plan.nb_max, row_count)
 
 
 def run_prefill(plan: Plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale, q, k_pages, v_pages, kv_indices,

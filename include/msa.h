@@ -74,16 +74,19 @@ typedef enum {
   MSA_ERR_HIP = 4                  /* the HIP runtime reported an error */
 } msa_status_t;
 
-/* MSA_MXFP4 is a proxy dtype only (desc.proxy_dtype, plans whose every
- * sequence has one query row): proxy q is fp8 e4m3 with per-head scales, and
- * each proxy-K page of one head is an MXFP4 record (OCP microscaling FP4:
- * E2M1 codes, one E8M0 scale per 32 dims) of 128 * 64 bytes of codes
+/* MSA_MXFP4 and MSA_MXFP4_QK are proxy dtypes only (desc.proxy_dtype): the
+ * low-precision block-score indexer of the README's "Stacks" list, in the FP4
+ * format gfx950 matrix cores consume (OCP microscaling FP4: E2M1 codes, one
+ * E8M0 scale per 32 dims, value = e2m1(code) * 2^(scale - 127)).
+ *   MSA_MXFP4     proxy q fp8 e4m3 with per-head scales, proxy K MXFP4;
+ *   MSA_MXFP4_QK  proxy q and proxy K both MXFP4 (twice the matrix-core rate
+ *                 of fp8 in the prefill proxy pass).
+ * An MXFP4 proxy-K page of one head is a record of 128 * 64 bytes of codes
  * (slot-major; element 2i of a row in the low nibble of byte i) followed by
- * 128 * 4 scale bytes (slot-major; byte c scales dims 32c..32c+31): value =
- * e2m1(code) * 2^(scale - 127).  This is the low-precision block-score
- * indexer of the README's "Stacks" list, in the FP4 format gfx950 matrix
- * cores consume. */
-typedef enum { MSA_BF16 = 0, MSA_FP8_E4M3 = 1, MSA_MXFP4 = 2 } msa_dtype_t;
+ * 128 * 4 scale bytes (slot-major; byte c scales dims 32c..32c+31): 8704
+ * bytes.  An MXFP4 proxy q row (one row, one head) is its 64 code bytes then
+ * its 4 scale bytes: 68 bytes, rows contiguous ([T, P, 68]). */
+typedef enum { MSA_BF16 = 0, MSA_FP8_E4M3 = 1, MSA_MXFP4 = 2, MSA_MXFP4_QK = 3 } msa_dtype_t;
 typedef enum { MSA_PREFILL = 0, MSA_DECODE = 1 } msa_mode_t;
 
 typedef struct {
@@ -98,8 +101,8 @@ typedef struct {
   int32_t page_size;           /* 128 */
   int32_t topk;                /* slots per (row, group), local block included; 1..64 */
   msa_dtype_t kv_dtype;        /* K/V pages: bf16 (prefill, decode) or fp8 (decode) */
-  msa_dtype_t proxy_dtype;     /* proxy q and proxy k pages: bf16 or fp8; or MXFP4
-                                  (fp8 q, MXFP4 K records; one-row plans only) */
+  msa_dtype_t proxy_dtype;     /* proxy q and proxy k pages: bf16, fp8, MXFP4 (fp8 q,
+                                  MXFP4 K) or MXFP4_QK (both MXFP4) */
   float sm_scale;              /* main attention logit scale */
   float proxy_sm_scale;        /* proxy logit scale */
   msa_mode_t mode;             /* which entry points the plan serves */
@@ -127,11 +130,12 @@ msa_status_t msa_plan_destroy(msa_plan_t plan);
  * where pk(p) = p if P_k = P else 0, and qs/ks are the fp8 scales (1 for
  * bf16).  Entries with b > local(r) are left unspecified (may be written).
  *
- *   proxy_q        [T, P, 128]  bf16 or fp8 (desc.proxy_dtype; fp8 for MXFP4)
- *   proxy_k_pages  [num_pages, P_k, 128, 128], same dtype; MXFP4:
- *                  [num_pages, P_k, 8704 B] records (see MSA_MXFP4)
- *   proxy_q_scale  [P]   fp32, device; NULL iff proxy dtype is bf16
- *   proxy_k_scale  [P_k] fp32, device; given iff proxy dtype is fp8
+ *   proxy_q        [T, P, 128]  bf16 or fp8 (desc.proxy_dtype; fp8 for MXFP4);
+ *                  MXFP4_QK: [T, P, 68 B] rows (see MSA_MXFP4)
+ *   proxy_k_pages  [num_pages, P_k, 128, 128], bf16 or fp8; MXFP4 and
+ *                  MXFP4_QK: [num_pages, P_k, 8704 B] records
+ *   proxy_q_scale  [P]   fp32, device; given iff proxy q is fp8 (fp8, MXFP4)
+ *   proxy_k_scale  [P_k] fp32, device; given iff proxy K is fp8
  *   kv_indices     int32 flat page table (see conventions)
  *   max_score      fp32 [P, nb_max, row_count], nb_max = max over sequences
  *                  of ceil(kv_len / 128); row_count <= plan's max_rows_per_call
@@ -203,6 +207,19 @@ msa_status_t msa_sparse_attn_prefill(msa_plan_t plan, const void* q, const void*
                                      const float* k_scale, const float* v_scale, const int32_t* kv_indices,
                                      const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, msa_stream_t stream);
+
+/* Stage 3a on the rows [row_begin, row_begin + row_count) only: the same
+ * results for those rows, nothing else written.  Lets a caller overlap the
+ * attention of one row range with the selection pass of the next (a second
+ * stream); calls sharing one workspace must not overlap each other.
+ * Arguments as in msa_sparse_attn_prefill; out and lse are the full [T, ...]
+ * tensors.  Errors: as msa_sparse_attn_prefill, plus INVALID_ARG for a row
+ * range outside [0, T) or an empty range. */
+msa_status_t msa_sparse_attn_prefill_rows(msa_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
+                                          const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                          const int32_t* kv_block_indexes, void* out, float* lse, int64_t row_begin,
+                                          int64_t row_count, void* workspace, size_t workspace_bytes,
+                                          msa_stream_t stream);
 
 /* Stage 3b: paged sparse decode (README "Stacks": paged FP8 decode).  Stage
  * 3a with qo_len = 1 for every sequence: the new token is already the last

@@ -51,6 +51,9 @@ FP8 = "fp8"
 # gfx950 matrix cores consume): proxy q is fp8 e4m3fn with per-head scales,
 # proxy K pages hold MXFP4 records (see mxfp4_record_rows).
 MXFP4 = "mxfp4"
+# Proxy pair with both proxy q and proxy K in MXFP4 (q rows of 64 code bytes
+# then 4 scale bytes, see mxfp4_q_rows).
+MXFP4_QK = "mxfp4_qk"
 
 
 # ----------------------------------------------------------------------------
@@ -132,6 +135,28 @@ def mxfp4_record_rows(rec: np.ndarray, slots) -> np.ndarray:
     return E2M1_TABLE[nib] * np.repeat(e8m0_to_f64(scales), MXFP4_BLOCK, axis=1)
 
 
+def mxfp4_q_rows(rows: np.ndarray) -> np.ndarray:
+    """Decode MXFP4 proxy q rows: uint8 [..., d/2 + d/32] (the d/2 code bytes,
+    element 2i in the low nibble of byte i, then the d/32 E8M0 scale bytes,
+    byte c scaling elements 32c .. 32c+31) -> float64 [..., d]."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    d = rows.shape[-1] * 32 // 17
+    cb = d // 2
+    codes, scales = rows[..., :cb], rows[..., cb:]
+    nib = np.empty(rows.shape[:-1] + (d,), dtype=np.uint8)
+    nib[..., 0::2] = codes & 0xF
+    nib[..., 1::2] = codes >> 4
+    return E2M1_TABLE[nib] * np.repeat(e8m0_to_f64(scales), MXFP4_BLOCK, axis=-1)
+
+
+def dequant_proxy_q(bits: np.ndarray, proxy_dtype: str, scale=None) -> np.ndarray:
+    """Proxy q [..., P, ...] stored bits -> float64 values for each proxy pair
+    dtype (the MXFP4 pair's q is fp8; MXFP4_QK's q is MXFP4 rows)."""
+    if proxy_dtype == MXFP4_QK:
+        return mxfp4_q_rows(bits)
+    return dequant(bits, FP8 if proxy_dtype == MXFP4 else proxy_dtype, scale, head_axis=1)
+
+
 def dequant(bits: np.ndarray, dtype: str, scale=None, head_axis: int = 1) -> np.ndarray:
     """Stored bits -> float64 values; fp8 values are multiplied by the fp32
     per-head scale (in float64)."""
@@ -184,7 +209,7 @@ def gather_rows(pages_bits, dtype, scale, kv_indices, lay: Layout, s: int, head:
     Key j lives in page kv_indices[page_start[s] + j // B], slot j % B."""
     key_idx = np.asarray(key_idx, dtype=np.int64)
     pages = np.asarray(kv_indices, dtype=np.int64)[lay.page_start[s] + key_idx // lay.B]
-    if dtype == MXFP4:      # pool [N, heads, record bytes]; no per-head scale
+    if dtype in (MXFP4, MXFP4_QK):      # pool [N, heads, record bytes]; no per-head scale
         return mxfp4_record_rows(pages_bits[pages, head], key_idx % lay.B)
     raw = pages_bits[pages, head, key_idx % lay.B, :]
     if dtype == BF16:
@@ -209,7 +234,8 @@ def proxy_block_maxscore(proxy_q, proxy_k_pages, kv_indices, qo_lens, kv_lens, p
     Blocks with no visible key give -inf; blocks after the row's local block
     are not defined and returned as NaN.  With proxy_dtype MXFP4 the proxy q
     is fp8 (scaled by proxy_q_scale) and the proxy K rows are decoded from
-    MXFP4 records (proxy_k_scale unused).
+    MXFP4 records (proxy_k_scale unused); with MXFP4_QK the proxy q rows are
+    MXFP4 too (no per-head scales).
 
     Returns float64 [len(rows), P, nb_max].
     """
@@ -217,7 +243,6 @@ def proxy_block_maxscore(proxy_q, proxy_k_pages, kv_indices, qo_lens, kv_lens, p
     rows = np.arange(lay.T) if rows is None else np.asarray(rows, dtype=np.int64)
     T, P, d = proxy_q.shape
     Pk = proxy_k_pages.shape[1]
-    q_dtype = FP8 if proxy_dtype == MXFP4 else proxy_dtype
     B = lay.B
     nb_max = max(lay.nb)
     out = np.full((rows.size, P, nb_max), np.nan)
@@ -234,8 +259,8 @@ def proxy_block_maxscore(proxy_q, proxy_k_pages, kv_indices, qo_lens, kv_lens, p
             for c0 in range(0, sel.size, 256):
                 idx = sel[c0:c0 + 256]
                 r = rows[idx]
-                qv = dequant(proxy_q[r, p:p + 1, :], q_dtype,
-                             None if proxy_q_scale is None else np.asarray(proxy_q_scale)[p:p + 1])[:, 0, :]
+                qv = dequant_proxy_q(proxy_q[r, p:p + 1, :], proxy_dtype,
+                                     None if proxy_q_scale is None else np.asarray(proxy_q_scale)[p:p + 1])[:, 0, :]
                 S = proxy_sm_scale * (qv @ K.T)                               # [n, L]
                 pos = np.array([lay.pos(int(x)) for x in r])
                 S[keys[None, :] > pos[:, None]] = -np.inf

@@ -16,7 +16,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from .gen import (Workload, STREAM_Q, STREAM_K, STREAM_V, STREAM_PQ, STREAM_PK, STREAM_LOWRANK, BF16, FP8, MXFP4,
+from .gen import (Workload, STREAM_Q, STREAM_K, STREAM_V, STREAM_PQ, STREAM_PK, STREAM_LOWRANK, BF16, FP8, MXFP4, MXFP4_QK,
                   E2M1_MAGNITUDES,
                   rng as np_rng, decode_picks, _page_table)
 
@@ -179,10 +179,13 @@ def make_inputs_device(w: Workload, seed: int, device="cuda", picks_sets: int = 
                 n = x.shape[0]
                 blk = (torch.arange(r0, r0 + n, device=device) // B)
                 x += c * torch.einsum("pdr,tpr->tpd", basis[:Pk], wb[s][blk])
-        pq_rows, pqs = _store_rows(w, seed, STREAM_PQ, P, FP8 if w.proxy_dtype == MXFP4 else w.proxy_dtype, device,
-                                   [T], add_q)
+        if w.proxy_dtype == MXFP4_QK:
+            pq_rows, pqs = _store_mxfp4_rows(w, seed, STREAM_PQ, P, device, [T], add_q), None
+        else:
+            pq_rows, pqs = _store_rows(w, seed, STREAM_PQ, P, FP8 if w.proxy_dtype == MXFP4 else w.proxy_dtype,
+                                       device, [T], add_q)
         inp.proxy_q, inp.proxy_q_scale = pq_rows[0], pqs
-        if w.proxy_dtype == MXFP4:
+        if w.proxy_dtype in (MXFP4, MXFP4_QK):
             pk_rows = _store_mxfp4_rows(w, seed, STREAM_PK, Pk, device, lens, add_k)
             pool = _scatter(pk_rows, w, kv_indices, num_pages, device)          # [N, Pk, B, d/2 + d/32]
             N, _, B, wd = pool.shape

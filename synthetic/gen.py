@@ -39,7 +39,8 @@ STREAM_Q, STREAM_K, STREAM_V, STREAM_PQ, STREAM_PK, STREAM_PAGES, STREAM_LOWRANK
 
 BF16 = "bf16"
 FP8 = "fp8"
-MXFP4 = "mxfp4"
+MXFP4 = "mxfp4"          # proxy pair: fp8 q, MXFP4 K
+MXFP4_QK = "mxfp4_qk"    # proxy pair: MXFP4 q (68-byte rows), MXFP4 K
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -202,7 +203,7 @@ class Inputs:
     v_pages: np.ndarray
     k_scale: Optional[np.ndarray] = None        # float32 [H_kv] (fp8)
     v_scale: Optional[np.ndarray] = None
-    proxy_q: Optional[np.ndarray] = None        # [T, P, d]
+    proxy_q: Optional[np.ndarray] = None        # [T, P, d]; MXFP4_QK: [T, P, d/2 + d/32] bytes
     proxy_k_pages: Optional[np.ndarray] = None  # [N, P_k, B, d]; MXFP4: [N, P_k, record bytes]
     proxy_q_scale: Optional[np.ndarray] = None  # float32 [P]
     proxy_k_scale: Optional[np.ndarray] = None  # float32 [P_k]
@@ -297,9 +298,12 @@ def make_inputs(w: Workload, seed: int) -> Inputs:
                 comp = c * np.einsum("pdr,bpr->bpd", basis[:Pk], wb)          # [nb, Pk, d]
                 tok = np.repeat(comp, B, axis=0)[:int(L)]                      # [L, Pk, d]
                 pk_rows[s] += tok
-        pq_bits, pq_scale = store(pq32, FP8 if w.proxy_dtype == MXFP4 else w.proxy_dtype, head_axis=1)
+        if w.proxy_dtype == MXFP4_QK:
+            pq_bits, pq_scale = to_mxfp4_rows(pq32), None
+        else:
+            pq_bits, pq_scale = store(pq32, FP8 if w.proxy_dtype == MXFP4 else w.proxy_dtype, head_axis=1)
         del pq32
-        if w.proxy_dtype == MXFP4:
+        if w.proxy_dtype in (MXFP4, MXFP4_QK):
             pk_bits = [to_mxfp4_rows(r) for r in pk_rows]
             pk_scale, nanv, npdt = None, NAN_MXFP4, np.uint8
         elif w.proxy_dtype == BF16:
@@ -313,7 +317,7 @@ def make_inputs(w: Workload, seed: int) -> Inputs:
             nanv, npdt = NAN_E4M3, np.uint8
         inp.proxy_q, inp.proxy_q_scale = pq_bits, pq_scale
         inp.proxy_k_pages = _scatter_pages(pk_bits, w, kv_indices, num_pages, nanv, npdt)
-        if w.proxy_dtype == MXFP4:
+        if w.proxy_dtype in (MXFP4, MXFP4_QK):
             inp.proxy_k_pages = mxfp4_pool_to_records(inp.proxy_k_pages)
         inp.proxy_k_scale = pk_scale
     if w.mode == "decode":

@@ -138,20 +138,30 @@ def test_compute_calls_validate_before_touching_the_device():
     big = msa.msa_plan([100], [100], 8, 2, 2, 2, topk=18, allocate=False)
     assert L.msa_proxy_topk_select(big.handle, a, a, none, none, a, 0, 10, a, ws, big.workspace_bytes, none) == \
         msa.MSA_ERR_UNSUPPORTED and b"topk" in L.msa_last_error()
+    # row-range attention: the range must lie in [0, T) and be non-empty
+    assert L.msa_sparse_attn_prefill_rows(p.handle, a, a, a, none, none, a, a, a, none, T - 5, 10, ws, nb, none) == \
+        msa.MSA_ERR_INVALID_ARG
+    assert L.msa_sparse_attn_prefill_rows(p.handle, a, a, a, none, none, a, a, a, none, 0, 0, ws, nb, none) == \
+        msa.MSA_ERR_INVALID_ARG
+    assert L.msa_sparse_attn_prefill_rows(d.handle, a, a, a, none, none, a, a, a, none, 0, 1, ws, nb, none) == \
+        msa.MSA_ERR_UNSUPPORTED
     assert L.msa_plan_destroy(None) == msa.MSA_OK
 
 
 def test_mxfp4_proxy_rules():
-    """MXFP4 proxy K: plans with one query row per sequence only; proxy q
-    (fp8) carries its per-head scales, proxy K none (they are in the records)."""
-    with pytest.raises(msa.MsaError) as e:
-        msa.msa_plan([2, 1], [300, 300], 8, 2, 2, 1, topk=4, proxy_dtype="mxfp4", allocate=False)
-    assert e.value.status == msa.MSA_ERR_UNSUPPORTED and b"MXFP4" in msa.lib().msa_last_error()
-    p = msa.msa_plan([1, 1], [300, 900], 8, 2, 2, 1, topk=4, proxy_dtype="mxfp4", allocate=False)
+    """MXFP4 proxies: fp8 q carries its per-head scales (MXFP4), MXFP4 q and
+    K carry none (their block scales are in the data); any plan shape."""
     L = msa.lib()
-    a, ws, none, nb = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000), None, p.workspace_bytes
-    for fn, out in (("msa_proxy_block_maxscore", a), ("msa_proxy_topk_select", a)):
-        f = getattr(L, fn)
-        assert f(p.handle, a, a, none, none, a, 0, 2, out, ws, nb, none) == msa.MSA_ERR_INVALID_ARG   # q scale missing
-        assert f(p.handle, a, a, a, a, a, 0, 2, out, ws, nb, none) == msa.MSA_ERR_INVALID_ARG         # k scale given
-        assert f(p.handle, a, a, a, none, a, 0, 2, out, ws, nb - 1, none) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    a, ws, none = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000), None
+    for qo in ([1, 1], [300, 5]):
+        p = msa.msa_plan(qo, [300, 900], 8, 2, 2, 1, topk=4, proxy_dtype="mxfp4", allocate=False)
+        pqk = msa.msa_plan(qo, [300, 900], 8, 2, 2, 2, topk=4, proxy_dtype="mxfp4_qk", allocate=False)
+        for fn in ("msa_proxy_block_maxscore", "msa_proxy_topk_select"):
+            f = getattr(L, fn)
+            nb = p.workspace_bytes
+            assert f(p.handle, a, a, none, none, a, 0, 2, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG   # q scale missing
+            assert f(p.handle, a, a, a, a, a, 0, 2, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG         # k scale given
+            assert f(p.handle, a, a, a, none, a, 0, 2, a, ws, nb - 1, none) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+            nb = pqk.workspace_bytes
+            assert f(pqk.handle, a, a, a, none, a, 0, 2, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG   # q scale given
+            assert f(pqk.handle, a, a, none, none, a, 0, 2, a, ws, nb - 1, none) == msa.MSA_ERR_WORKSPACE_TOO_SMALL

@@ -56,7 +56,7 @@ def _prefill_case(n_cfg, n_even):
         msa.msa_topk_select(plan, ms, r0, n, sel)
         here = np.nonzero((rows >= r0) & (rows < r0 + n))[0]
         if here.size:
-            got_ms[:, :, here] = ms[:, :, torch.from_numpy(rows[here] - r0).cuda()].cpu().numpy()
+            got_ms[:, :, here] = msa.max_score_rows(ms, plan, n)[:, :, torch.from_numpy(rows[here] - r0).cuda()].cpu().numpy()
     if w.topk <= 17:  # the fused pass (what run_prefill uses) selects exactly the same blocks, every row
         fsel = torch.full_like(sel, -7)
         msa.msa_proxy_topk_select(plan, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale,
@@ -171,7 +171,7 @@ def test_decode_step_indexer_and_decode_b32_131k(wn):
                                out, lse)
     torch.cuda.synchronize()
     assert torch.equal(sel, sel2), "fused indexer selection differs from the separate calls"
-    gms = ms[:, :, :S].cpu().numpy()
+    gms = msa.max_score_rows(ms, ip, S).cpu().numpy()
     gsel = sel.cpu().numpy()
     rows = np.arange(S)
     h = {k: to_host(getattr(inp, k)) for k in ("q", "kv_indices", "proxy_q", "proxy_k_pages", "proxy_q_scale",

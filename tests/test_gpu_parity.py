@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle as O
-from synthetic.gen import Workload, make_inputs, workload, seed_of, FP8, BF16, MXFP4
+from synthetic.gen import Workload, make_inputs, workload, seed_of, FP8, BF16, MXFP4, MXFP4_QK
 from tests._gpu import (device_inputs, plan_for, bf16_out_to_f64, oracle_scores, check_max_score, check_selection,
                         check_output, fp8_score_bound, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS, LOW_PRECISION_PROXY)
 
@@ -53,6 +53,13 @@ PREFILL_CASES = {
                                              topk=17, proxy_dtype=MXFP4, extra_pages=0.1, poison_tail=True), 28, 0),
     "onerow_mxfp4_per_head_proxy_k": (Workload("row1d", [1] * 5, [300, 7000, 256, 1, 4000], 8, 2, 2, 2, topk=5,
                                                proxy_dtype=MXFP4, lowrank=8, poison_tail=True), 29, 0),
+    "onerow_mxfp4_qk": (Workload("row1e", [1] * 4, [3000, 129, 700, 12000], 16, 2, 2, 1, topk=17,
+                                 proxy_dtype=MXFP4_QK, lowrank=8, poison_tail=True), 30, 0),
+    # multi-row prefill with MXFP4 proxies (several row tiles, ragged, prefix rows)
+    "mxfp4_proxy_k_prefill": (Workload("mxk", [700, 77, 1], [700, 300, 1], 8, 2, 2, 1, topk=6, proxy_dtype=MXFP4,
+                                       extra_pages=0.2, poison_tail=True), 31, 0),
+    "mxfp4_qk_prefill": (Workload("mxqk", [600, 513], [900, 513], 16, 2, 2, 2, topk=5, proxy_dtype=MXFP4_QK,
+                                  lowrank=8, poison_tail=True), 32, 200),
 }
 
 
@@ -71,7 +78,7 @@ def run_prefill_stages(msa, inp, max_rows):
         msa.msa_proxy_block_maxscore(plan, d["proxy_q"], d["proxy_k_pages"], d["proxy_q_scale"], d["proxy_k_scale"],
                                      d["kv_indices"], r0, n, ms)
         msa.msa_topk_select(plan, ms, r0, n, sel)
-        ms_all.append(ms[:, :, :n].cpu().numpy().copy())
+        ms_all.append(msa.max_score_rows(ms, plan, n).cpu().numpy().copy())
     out = torch.full((T, w.num_qo_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((T, w.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
     msa.msa_sparse_attn_prefill(plan, d["q"], d["k_pages"], d["v_pages"], d["kv_indices"], sel, out, lse)
@@ -126,6 +133,33 @@ def test_fused_proxy_topk_equals_separate_calls(case):
         s2 = sel2.cpu().numpy()
         assert np.array_equal(s2[r0:r0 + n], gsel[r0:r0 + n]), case
         assert (s2[:r0] == -7).all() and (s2[r0 + n:] == -7).all(), case
+
+
+def test_row_range_attention_equals_whole_call():
+    """msa_sparse_attn_prefill_rows over consecutive row ranges (ragged, one
+    of them a single row, some crossing sequence boundaries) writes exactly
+    those rows, and together they give the whole call's output bit for bit."""
+    msa = _msa()
+    w, seed, _ = PREFILL_CASES["varlen_ragged_prefix"]
+    inp = make_inputs(w, seed)
+    d = device_inputs(inp)
+    plan = plan_for(msa, inp)
+    T = w.total_rows
+    sel = torch.full((T, w.num_kv_heads, w.topk), -7, dtype=torch.int32, device="cuda")
+    msa.msa_proxy_topk_select(plan, d["proxy_q"], d["proxy_k_pages"], d["proxy_q_scale"], d["proxy_k_scale"],
+                              d["kv_indices"], 0, T, sel)
+    ref = torch.full((T, w.num_qo_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ref_lse = torch.full((T, w.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_prefill(plan, d["q"], d["k_pages"], d["v_pages"], d["kv_indices"], sel, ref, ref_lse)
+    out = torch.full_like(ref, float("nan"))
+    lse = torch.full_like(ref_lse, float("nan"))
+    bounds = [0, 150, 151, 377, 600, T]
+    for r0, r1 in zip(bounds[:-1], bounds[1:]):
+        msa.msa_sparse_attn_prefill_rows(plan, d["q"], d["k_pages"], d["v_pages"], d["kv_indices"], sel, out, r0,
+                                         r1 - r0, lse)
+        torch.cuda.synchronize()
+        assert torch.isnan(out[r1:].float()).all() and torch.isnan(lse[r1:]).all(), (r0, r1)
+    assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
 
 
 TIE_CASES = {

@@ -138,3 +138,17 @@ def test_mxfp4_quantizer_round_trip_and_error_bound():
     bound = np.repeat(np.ldexp(1.0, Xs.astype(int) + 1), 32, axis=1)
     assert (np.abs(got - x) < bound).all()
     assert (np.abs(got) <= np.repeat(6.0 * np.ldexp(1.0, Xs.astype(int)), 32, axis=1)).all()
+
+
+def test_mxfp4_q_row_layout_by_hand():
+    """An MXFP4 proxy q row: 64 code bytes (element 2j in the low nibble of
+    byte j), then the four scale bytes of its 32-element groups."""
+    from oracle import mxfp4_q_rows
+    codes = (np.arange(128) * 7) % 16
+    row = np.concatenate([(codes[0::2] | (codes[1::2] << 4)).astype(np.uint8),
+                          np.array([125, 127, 129, 131], np.uint8)])
+    vals = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    vals = vals + [-v for v in vals]
+    exp = np.array([vals[codes[i]] * [0.25, 1.0, 4.0, 16.0][i // 32] for i in range(128)])
+    got = mxfp4_q_rows(np.stack([row, row])[None])      # [1, 2, 68] -> [1, 2, 128]
+    assert got.shape == (1, 2, 128) and np.array_equal(got[0, 1], exp)

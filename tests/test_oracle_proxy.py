@@ -190,3 +190,31 @@ def test_mxfp4_proxy_k_equals_bf16_path_on_the_same_values():
     b = proxy_block_maxscore(qbits, kbits, kvi, qo, kv, B, 0.125, BF16)
     assert np.array_equal(np.isnan(a), np.isnan(b))
     assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+
+
+def test_mxfp4_q_and_k_equal_bf16_path_on_the_same_values():
+    """MXFP4 proxy q rows and MXFP4 K records decode to values bf16 holds
+    exactly; the scores must equal the bf16 path's bit for bit."""
+    from oracle import MXFP4_QK, E2M1_TABLE
+    from synthetic.gen import to_mxfp4_rows, mxfp4_pool_to_records, to_bf16_bits
+    rng = np.random.default_rng(12)
+    qo, kv, B, P, Pk = [130, 1], [300, 700], 128, 2, 2
+    T = sum(qo)
+    nbs = [-(-L // B) for L in kv]
+    N = sum(nbs)
+    kvi = rng.permutation(N).astype(np.int32)
+
+    def mx_values(shape):
+        codes = rng.integers(0, 16, size=shape + (128,))
+        codes[..., ::32] = rng.choice([6, 7, 14, 15], size=shape + (4,))
+        X = rng.integers(-3, 3, size=shape + (4,))
+        return E2M1_TABLE[codes] * np.repeat(np.ldexp(1.0, X), 32, axis=-1)
+    kvals = mx_values((N, Pk, B))
+    qvals = mx_values((T, P))
+    rec = mxfp4_pool_to_records(to_mxfp4_rows(kvals.astype(np.float32)))
+    qrows = to_mxfp4_rows(qvals.astype(np.float32))
+    a = proxy_block_maxscore(qrows, rec, kvi, qo, kv, B, 0.125, MXFP4_QK)
+    b = proxy_block_maxscore(to_bf16_bits(qvals.astype(np.float32)), to_bf16_bits(kvals.astype(np.float32)), kvi, qo,
+                             kv, B, 0.125, BF16)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
