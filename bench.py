@@ -33,6 +33,9 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse prefill tok/s + MFMA util @32K/128K; paged fp8 decode tok/s @131K"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP4_TFLOPS = 10100.0
+# matrix-core peak of each proxy pair: fp4 x fp8 products run at the fp8 rate
+PROXY_PEAK = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "mxfp4": PEAK_FP8_TFLOPS, "mxfp4_qk": PEAK_FP4_TFLOPS}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "proxy_maxscore": "proxy_maxscore.hip", "topk_select": "topk_select.hip", "proxy_topk": "proxy_maxscore.hip",
@@ -161,19 +164,22 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
             continue
         grid = "x".join(r[f"Grid_Size_{a}"] for a in "XYZ")
         rows.append((k, grid, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6))
-    # partial_attn grid -> workload by order of first appearance
-    grids = []
-    for k, grid, _ in rows:
-        if k == "partial_attn" and grid not in grids:
-            grids.append(grid)
-    label_of_grid = {gr: (prefill_names[i] if i < len(prefill_names) else f"prefill grid {gr}")
-                     for i, gr in enumerate(grids)}
+    # partial_attn dispatches -> workload: the prefill workloads run one after
+    # another, so each run of partial_attn dispatches with one grid is the
+    # next prefill workload in bench order
+    pa_label = {}
+    run, prev = -1, None
+    for i, (k, grid, _) in enumerate(rows):
+        if k == "partial_attn":
+            if grid != prev:
+                run += 1
+                prev = grid
+            pa_label[i] = prefill_names[run] if run < len(prefill_names) else f"prefill grid {grid}"
     section = [None] * len(rows)
     nxt = None
     for i in range(len(rows) - 1, -1, -1):
-        k, grid, _ = rows[i]
-        if k == "partial_attn":
-            nxt = label_of_grid[grid]
+        if rows[i][0] == "partial_attn":
+            nxt = pa_label[i]
         section[i] = nxt
     last = None
     step_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow"), len(rows))
@@ -188,7 +194,7 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
         elif k == "merge" or section[i] is None:
             section[i] = last
         if k == "partial_attn":
-            last = label_of_grid[grid]
+            last = pa_label[i]
     g = collections.OrderedDict()
     for (k, grid, ms), sec in zip(rows, section):
         g.setdefault((sec, k, grid), []).append(ms)
@@ -322,7 +328,7 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
     G = w.num_qo_heads // w.num_kv_heads
     f_main = 4.0 * 128 * float(nvis.sum().item()) * G
     f_proxy = proxy_flops(w.qo_lens, w.kv_lens, w.num_proxy_heads)
-    proxy_peak = PEAK_FP8_TFLOPS if w.proxy_dtype == "fp8" else PEAK_BF16_TFLOPS
+    proxy_peak = PROXY_PEAK[w.proxy_dtype]
     # work per launch of the dominant kernel (launches cover equal shares of a step)
     if dominant in ("proxy_maxscore", "proxy_topk"):
         work, peak, unit, bound = f_proxy / launches_per_step, proxy_peak, "TFLOP/s", "mfma"
@@ -337,11 +343,16 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
             "launches_per_step": launches_per_step,
             "work_per_launch": work, "work_unit": "FLOP" if unit == "TFLOP/s" else "B"}
     stage_ms = {n: v[0] for n, v in per_kernel.items()}
+    pstage = "proxy_topk" if "proxy_topk" in stage_ms else "proxy_maxscore"
+    p_ach = f_proxy / (stage_ms[pstage] * 1e-3) / 1e12
+    proxy_roof = {"kernel": pstage, "proxy_dtype": w.proxy_dtype, "achieved": p_ach, "peak": proxy_peak,
+                  "unit": "TFLOP/s", "frac": p_ach / proxy_peak}
     tflops = (f_main + f_proxy) / (ms_step * 1e-3) / 1e12
     res = {
         "workload": w.name, "tok_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
         "tflops": tflops, "mfma_util": tflops / PEAK_BF16_TFLOPS,
         "flops": {"proxy": f_proxy, "main": f_main}, "stage_ms": stage_ms, "roofline": roof,
+        "proxy_roofline": proxy_roof,
         "config": {"workload": w.name, "qo_lens": w.qo_lens if len(w.qo_lens) <= 8 else None, "total_rows": T,
                    "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
                    "num_proxy_heads": w.num_proxy_heads, "topk": w.topk, "page_size": 128, "head_dim": 128,
@@ -492,9 +503,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode entries")
-    ap.add_argument("--extra", default="prefill_128k,decode_131k,decode_step_131k,decode_step_mxfp4_131k",
-                    help="comma-separated extra entries: prefill_128k, decode_131k, decode_step_131k, "
-                         "decode_step_mxfp4_131k (or none)")
+    ap.add_argument("--extra", default="prefill_128k,prefill_32k_mxfp4,decode_131k,decode_step_131k,"
+                                       "decode_step_mxfp4_131k",
+                    help="comma-separated extra entries: prefill_128k, prefill_32k_mxfp4, decode_131k, "
+                         "decode_step_131k, decode_step_mxfp4_131k (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -520,7 +532,7 @@ def main():
     torch.cuda.set_device(0)
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
-        if e not in ("prefill_128k", "decode_131k", "decode_step_131k", "decode_step_mxfp4_131k"):
+        if e not in ("prefill_128k", "prefill_32k_mxfp4", "decode_131k", "decode_step_131k", "decode_step_mxfp4_131k"):
             ap.error(f"unknown extra entry {e}")
     if args.copy_calibration:
         print("[bench] calibration copy", file=sys.stderr, flush=True)
@@ -532,6 +544,10 @@ def main():
         print("[bench] prefill 128k varlen", file=sys.stderr, flush=True)
         r3, _ = prefill_bench(msa, 3, max(2, args.steps // 2), 1)
         extra["prefill_128k"] = r3
+    if "prefill_32k_mxfp4" in extras:
+        print("[bench] prefill 32k, MXFP4 proxy q and K", file=sys.stderr, flush=True)
+        r8, _ = prefill_bench(msa, 8, args.steps, args.warmup)
+        extra["prefill_32k_mxfp4"] = r8
     if "decode_131k" in extras:
         print("[bench] decode 131k fp8", file=sys.stderr, flush=True)
         extra["decode_131k"] = decode_bench(msa, max(50, args.steps * 10), 10)
@@ -551,7 +567,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), device generator)",
         "config": main_res["config"], "roofline": main_res["roofline"], "cpu_baseline": cpu,
         "mfma_util": main_res["mfma_util"], "tflops": main_res["tflops"], "stage_ms": main_res["stage_ms"],
-        "flops": main_res["flops"], "extra": extra,
+        "flops": main_res["flops"], "proxy_roofline": main_res["proxy_roofline"], "extra": extra,
     }
     print(json.dumps(line), flush=True)
 
