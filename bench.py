@@ -72,8 +72,7 @@ def traffic_from_profiles(kernel: str, workload: str):
 # rocprofv3 summaries (run on the host from the CSV files rocprofv3 wrote)
 # ----------------------------------------------------------------------------
 COPY_BYTES = 1 << 30           # calibration copy: bytes read and bytes written per launch
-PMC_ARGS = ("--steps 2 --warmup 1 --no-cpu-baseline --extra decode_131k,decode_step_131k,decode_step_mxfp4_131k "
-            "--copy-calibration")
+PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --extra decode_131k,decode_step_131k --copy-calibration"
 PMC_CMDS = {
     "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o f -- python bench.py {PMC_ARGS}",
     "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o w -- python bench.py {PMC_ARGS}",
