@@ -314,7 +314,8 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
 
     def step():
         msa.run_prefill(plan, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale, inp.q,
-                        inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, None, ms_buf)
+                        inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, None, ms_buf, k_scale=inp.k_scale,
+                        v_scale=inp.v_scale)
 
     step()
     torch.cuda.synchronize()
@@ -355,7 +356,7 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
         "config": {"workload": w.name, "qo_lens": w.qo_lens if len(w.qo_lens) <= 8 else None, "total_rows": T,
                    "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
                    "num_proxy_heads": w.num_proxy_heads, "topk": w.topk, "page_size": 128, "head_dim": 128,
-                   "proxy_dtype": w.proxy_dtype, "max_rows_per_call": plan.max_rows_per_call},
+                   "proxy_dtype": w.proxy_dtype, "kv_dtype": w.kv_dtype, "max_rows_per_call": plan.max_rows_per_call},
     }
     return res, (w, inp, sel)
 
@@ -544,7 +545,7 @@ def main():
         r3, _ = prefill_bench(msa, 3, max(2, args.steps // 2), 1)
         extra["prefill_128k"] = r3
     if "prefill_32k_mxfp4" in extras:
-        print("[bench] prefill 32k, MXFP4 proxy q and K", file=sys.stderr, flush=True)
+        print("[bench] prefill 32k, MXFP4 proxy q and K, MXFP4 K/V", file=sys.stderr, flush=True)
         r8, _ = prefill_bench(msa, 8, args.steps, args.warmup)
         extra["prefill_32k_mxfp4"] = r8
     if "decode_131k" in extras:

@@ -190,10 +190,12 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
   if (d.head_dim != 128) return fail(MSA_ERR_UNSUPPORTED, "msa_plan: head_dim %d != 128", d.head_dim);
   if (d.page_size != 128) return fail(MSA_ERR_UNSUPPORTED, "msa_plan: page_size %d != 128", d.page_size);
   if (d.topk < 1 || d.topk > 64) return fail(MSA_ERR_INVALID_ARG, "msa_plan: topk %d not in [1, 64]", d.topk);
-  if (d.kv_dtype != MSA_BF16 && d.kv_dtype != MSA_FP8_E4M3) return fail(MSA_ERR_INVALID_ARG, "msa_plan: bad kv_dtype");
+  if (d.kv_dtype != MSA_BF16 && d.kv_dtype != MSA_FP8_E4M3 && d.kv_dtype != MSA_MXFP4)
+    return fail(MSA_ERR_INVALID_ARG, "msa_plan: bad kv_dtype");
+  if (d.mode == MSA_DECODE && d.kv_dtype == MSA_MXFP4)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_plan: MXFP4 K/V are built for prefill");
   if (!(d.sm_scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "msa_plan: sm_scale must be > 0");
   if (d.mode == MSA_PREFILL) {
-    if (d.kv_dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "msa_plan: prefill K/V must be bf16");
     if (d.proxy_dtype != MSA_BF16 && d.proxy_dtype != MSA_FP8_E4M3 && d.proxy_dtype != MSA_MXFP4 &&
         d.proxy_dtype != MSA_MXFP4_QK)
       return fail(MSA_ERR_INVALID_ARG, "msa_plan: bad proxy_dtype");
@@ -439,7 +441,9 @@ static msa_status_t prefill_rows(const char* fn, msa_plan_t p, const void* q, co
   MSA_CHECK_PTR(kv_block_indexes);
   MSA_CHECK_PTR(out);
   if (lse && !aligned16(lse)) return fail(MSA_ERR_INVALID_ARG, "%s: lse not 16-byte aligned", fn);
-  if (k_scale || v_scale) return fail(MSA_ERR_INVALID_ARG, "%s: bf16 K/V take no scales", fn);
+  const bool fp8 = p->d.kv_dtype == MSA_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "%s: k_scale and v_scale must be given iff K/V are fp8", fn);
   if (row_count < 1 || row_begin < 0 || row_begin + row_count > p->T)
     return fail(MSA_ERR_INVALID_ARG, "%s: rows [%lld, %lld) outside [0, %lld)", fn, (long long)row_begin,
                 (long long)(row_begin + row_count), (long long)p->T);
@@ -451,8 +455,9 @@ static msa_status_t prefill_rows(const char* fn, msa_plan_t p, const void* q, co
   const int64_t r1 = row_begin + row_count;
   for (int64_t w0 = row_begin; w0 < r1; w0 += p->attn_window) {
     const int32_t w1 = (int32_t)std::min<int64_t>(r1, w0 + p->attn_window);
-    hipError_t e = msa::launch_prefill_window(p, m, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse,
-                                              static_cast<char*>(workspace), (int32_t)w0, w1, hs);
+    hipError_t e = msa::launch_prefill_window(p, m, q, k_pages, v_pages, k_scale, v_scale, kv_indices,
+                                              kv_block_indexes, out, lse, static_cast<char*>(workspace), (int32_t)w0,
+                                              w1, hs);
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();

@@ -86,8 +86,9 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
 hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, int64_t row_begin,
                        int64_t row_count, int32_t* sel, hipStream_t st);
 hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
-                                 const void* vp, const int32_t* kv_indices, const int32_t* sel, void* out,
-                                 float* lse, char* ws, int32_t w0, int32_t w1, hipStream_t st);
+                                 const void* vp, const float* ks, const float* vs, const int32_t* kv_indices,
+                                 const int32_t* sel, void* out, float* lse, char* ws, int32_t w0, int32_t w1,
+                                 hipStream_t st);
 hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
                          const float* ks, const float* vs, const int32_t* kv_indices, const int32_t* sel,
                          void* out, float* lse, char* ws, hipStream_t st);

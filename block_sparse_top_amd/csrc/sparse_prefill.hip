@@ -145,10 +145,17 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* c
   }
 }
 
+// K/V page formats: bf16; fp8 e4m3 with one fp32 scale per KV head (the
+// codes widen to bf16 exactly, the scales fold into the logit scale and the
+// output); MXFP4 records (codes widen with their E8M0 block scale, exactly).
+enum class KvFmt : int { BF16 = 0, FP8 = 1, MX4 = 2 };
+
 struct PartialArgs {
   const uint8_t* q;      // bf16 [T, Hq, 128]
-  const uint8_t* kp;     // bf16 [N, Hkv, 128, 128]
+  const uint8_t* kp;     // [N, Hkv, 128, 128] bf16 / fp8, or [N, Hkv, 8704 B] MXFP4 records
   const uint8_t* vp;
+  const float* ks;       // fp8: [Hkv] scales, else null
+  const float* vs;
   const int32_t* kv_indices;
   const int32_t* entries;
   const int4* items;
@@ -164,6 +171,27 @@ struct PartialArgs {
 constexpr int kMaxItemEntries = 512;   // entries_per_item = min(512, 16 chunks of 128 / G tokens)
 constexpr int kOStage = 32 * 64;       // output staging per wave: 32 rows x 32 bf16 columns
 
+// Eight K/V elements of key row `row`, dims 8 col .. 8 col + 7, as bf16
+// (exact) from a page of format F.
+template <KvFmt F>
+__device__ __forceinline__ i32x4 load_kv8(const uint8_t* page, int row, int col) {
+  if constexpr (F == KvFmt::BF16) {
+    return *reinterpret_cast<const i32x4*>(page + row * 256 + col * 16);
+  } else if constexpr (F == KvFmt::FP8) {
+    const i32x2 c = *reinterpret_cast<const i32x2*>(page + row * 128 + col * 8);
+    return __builtin_bit_cast(i32x4, fp8x8_to_bf16x8((uint32_t)c[0], (uint32_t)c[1]));
+  } else {
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(page + row * 64 + col * 4);
+    const uint32_t e = (*reinterpret_cast<const uint32_t*>(page + 128 * 64 + row * 4) >> (8 * (col >> 2))) & 0xffu;
+    const float sc = e ? __uint_as_float(e << 23) : 5.877471754111438e-39f;  // 2^(e - 127); e = 0: 2^-127
+    return i32x4{__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0)),
+                 __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1)),
+                 __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2)),
+                 __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3))};
+  }
+}
+
+template <KvFmt F>
 __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];
@@ -181,15 +209,16 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   const int32_t rs = a.m.row_start[s];
   const int n_ent = e1 - e0;
 
-  {  // K and V block -> LDS (coalesced 16-byte chunks); this item's entries -> LDS
-    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * 32768;
-    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * 32768;
+  {  // K and V block -> LDS as bf16 (coalesced loads); this item's entries -> LDS
+    constexpr int64_t kPageBytes = F == KvFmt::BF16 ? 32768 : F == KvFmt::FP8 ? 16384 : 128 * 64 + 128 * 4;
+    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * kPageBytes;
+    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * kPageBytes;
     i32x4 kr[8], vr[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + 256 * i;
-      kr[i] = *reinterpret_cast<const i32x4*>(kb + c * 16);
-      vr[i] = *reinterpret_cast<const i32x4*>(vb + c * 16);
+      kr[i] = load_kv8<F>(kb, c >> 4, c & 15);
+      vr[i] = load_kv8<F>(vb, c >> 4, c & 15);
     }
     for (int i = tid; i < n_ent; i += 256) ent_s[i] = a.entries[e0 + i];
     const int kv_in_block = a.m.kv[s] - b * 128;  // V rows at or past this are page padding
@@ -211,6 +240,9 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   const int hh = qr % G, tok = qr / G;
   const int h = g * G + hh;
   const int nchunks = (n_ent + MT - 1) / MT;
+  // fp8 pages: logits and outputs carry the group's K and V scales
+  const float scale_log2 = F == KvFmt::FP8 ? a.scale_log2 * a.ks[g] : a.scale_log2;
+  const float v_scale = F == KvFmt::FP8 ? a.vs[g] : 1.f;
   // K row 32 kt + (lane & 31), column chunk 2 st + half: kbase[st] + 8192 kt
   int kbase[8];
 #pragma unroll
@@ -273,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mraw = max3f(mraw, acc[kt][i], acc[kt][i + 1]);
     mraw = fmaxf(mraw, wave_xor32(mraw));
-    const float mx = mraw * a.scale_log2;  // scaled row max (log2 domain)
+    const float mx = mraw * scale_log2;  // scaled row max (log2 domain)
     float sum = 0.f;
     bf16x8 pf[4][2];
 #pragma unroll
@@ -283,8 +315,8 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
         i32x4 pw;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float p0 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * t], a.scale_log2, -mx));
-          const float p1 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * t + 1], a.scale_log2, -mx));
+          const float p0 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * t], scale_log2, -mx));
+          const float p1 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * t + 1], scale_log2, -mx));
           sum += p0 + p1;
           const bf16x2 two = {(__bf16)p0, (__bf16)p1};
           pw[t] = __builtin_bit_cast(int, two);
@@ -314,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     // writes 16 rows x 64 contiguous bytes.  Staged row j holds its 4 16-byte
     // chunks at c ^ ((j >> 2) & 3): the 8-byte writes of a tile land on every
     // bank exactly twice.
-    const float inv = 1.f / sum;
+    const float inv = v_scale / sum;
     int64_t spi[2];
     bool sval[2];
 #pragma unroll
@@ -451,8 +483,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }  // namespace
 
 hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
-                                 const void* vp, const int32_t* kv_indices, const int32_t* sel, void* out,
-                                 float* lse, char* ws, int32_t w0, int32_t w1, hipStream_t st) {
+                                 const void* vp, const float* ks, const float* vs, const int32_t* kv_indices,
+                                 const int32_t* sel, void* out, float* lse, char* ws, int32_t w0, int32_t w1,
+                                 hipStream_t st) {
   const PlanLayout& L = p->lay;
   const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
   const int32_t nkey = Hkv * p->NB;
@@ -494,6 +527,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   a.q = static_cast<const uint8_t*>(q);
   a.kp = static_cast<const uint8_t*>(kp);
   a.vp = static_cast<const uint8_t*>(vp);
+  a.ks = ks;
+  a.vs = vs;
   a.kv_indices = kv_indices;
   a.entries = entries;
   a.items = items;
@@ -512,7 +547,13 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   const int64_t max_items = ((int64_t)(w1 - w0) * Hkv * k + p->entries_per_item - 1) / p->entries_per_item + nkey;
   {
     ProfEvents pe(p, "partial_attn");
-    hipExtLaunchKernelGGL(partial_attn_kernel, dim3((unsigned)max_items), dim3(256), 0, st, pe.start, pe.stop, 0, a);
+    const dim3 grid((unsigned)max_items), blk(256);
+    if (p->d.kv_dtype == MSA_MXFP4)
+      hipExtLaunchKernelGGL(partial_attn_kernel<KvFmt::MX4>, grid, blk, 0, st, pe.start, pe.stop, 0, a);
+    else if (p->d.kv_dtype == MSA_FP8_E4M3)
+      hipExtLaunchKernelGGL(partial_attn_kernel<KvFmt::FP8>, grid, blk, 0, st, pe.start, pe.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(partial_attn_kernel<KvFmt::BF16>, grid, blk, 0, st, pe.start, pe.stop, 0, a);
   }
 
   MergeArgs mg;

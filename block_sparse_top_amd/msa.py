@@ -233,7 +233,7 @@ def max_score_rows(max_score: torch.Tensor, plan: Plan, row_count: int) -> torch
 
 
 def run_prefill(plan: Plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale, q, k_pages, v_pages, kv_indices,
-                kv_block_indexes, out, lse=None, max_score=None, fused=None):
+                kv_block_indexes, out, lse=None, max_score=None, fused=None, k_scale=None, v_scale=None):
     """The whole prefill path: the block selection (the fused proxy + top-k
     pass when topk <= 17, else proxy max scores and top-k chunk by chunk of
     rows), then the sparse attention."""
@@ -243,7 +243,7 @@ def run_prefill(plan: Plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale
     if fused:
         msa_proxy_topk_select(plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale, kv_indices, 0, T,
                               kv_block_indexes)
-        msa_sparse_attn_prefill(plan, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse)
+        msa_sparse_attn_prefill(plan, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse, k_scale, v_scale)
         return out, lse
     if max_score is None:
         max_score = max_score_buffer(plan, q.device)
@@ -252,5 +252,5 @@ def run_prefill(plan: Plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale
         msa_proxy_block_maxscore(plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale, kv_indices, r0, n,
                                  max_score)
         msa_topk_select(plan, max_score, r0, n, kv_block_indexes)
-    msa_sparse_attn_prefill(plan, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse)
+    msa_sparse_attn_prefill(plan, q, k_pages, v_pages, kv_indices, kv_block_indexes, out, lse, k_scale, v_scale)
     return out, lse

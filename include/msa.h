@@ -100,7 +100,7 @@ typedef struct {
   int32_t head_dim;            /* 128 */
   int32_t page_size;           /* 128 */
   int32_t topk;                /* slots per (row, group), local block included; 1..64 */
-  msa_dtype_t kv_dtype;        /* K/V pages: bf16 (prefill, decode) or fp8 (decode) */
+  msa_dtype_t kv_dtype;        /* K/V pages: bf16 or fp8 (prefill, decode), MXFP4 (prefill) */
   msa_dtype_t proxy_dtype;     /* proxy q and proxy k pages: bf16, fp8, MXFP4 (fp8 q,
                                   MXFP4 K) or MXFP4_QK (both MXFP4) */
   float sm_scale;              /* main attention logit scale */
@@ -196,13 +196,19 @@ msa_status_t msa_proxy_topk_select(msa_plan_t plan, const void* proxy_q, const v
  * Every selection must contain the row's local block (stage 2 guarantees it).
  *
  *   q                 bf16 [T, H_q, 128]
- *   k_pages, v_pages  bf16 [num_pages, H_kv, 128, 128]
- *   k_scale, v_scale  must be NULL (bf16 K/V)
+ *   k_pages, v_pages  [num_pages, H_kv, 128, 128] bf16 or fp8 (desc.kv_dtype),
+ *                     or MXFP4 records [num_pages, H_kv, 8704 B] (the record
+ *                     layout of MSA_MXFP4 proxy K pages)
+ *   k_scale, v_scale  fp32 [H_kv] device, given iff K/V are fp8 (value = code
+ *                     x scale); NULL for bf16 and MXFP4
  *   kv_block_indexes  int32 [T, H_kv, topk]
  *   out               bf16 [T, H_q, 128]
  *   lse               fp32 [T, H_q] or NULL
- * Errors: INVALID_ARG for null pointers; UNSUPPORTED for a decode plan or
- * fp8 K/V; WORKSPACE_TOO_SMALL. */
+ * fp8 and MXFP4 codes are widened to bf16 exactly (MXFP4 with its block
+ * scale) before the bf16 matrix products; fp8 per-head scales multiply the
+ * logits and the output.
+ * Errors: INVALID_ARG for null pointers or scales that do not match the K/V
+ * dtype; UNSUPPORTED for a decode plan; WORKSPACE_TOO_SMALL. */
 msa_status_t msa_sparse_attn_prefill(msa_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
                                      const float* k_scale, const float* v_scale, const int32_t* kv_indices,
                                      const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,

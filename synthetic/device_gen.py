@@ -124,6 +124,15 @@ def _store_mxfp4_rows(w: Workload, seed: int, stream: int, H: int, device, rows_
     return out
 
 
+def _records(pool: torch.Tensor) -> torch.Tensor:
+    """[N, H, B, d/2 + d/32] per-row MXFP4 bytes -> [N, H, record bytes] page
+    records (all rows' codes, then all rows' scales)."""
+    N, H, B, wd = pool.shape
+    cb = wd * 16 // 17
+    return torch.cat([pool[..., :cb].reshape(N, H, B * cb), pool[..., cb:].reshape(N, H, B * (wd - cb))],
+                     dim=-1).contiguous()
+
+
 def _scatter(rows, w: Workload, kv_indices: torch.Tensor, num_pages: int, device):
     H, d = rows[0].shape[1], rows[0].shape[2]
     B = w.page_size
@@ -152,12 +161,15 @@ def make_inputs_device(w: Workload, seed: int, device="cuda", picks_sets: int = 
     for r0, x in _randn_rows(gq, T, w.num_qo_heads, d, device):
         q[r0:r0 + x.shape[0]] = x.to(torch.bfloat16)
     lens = [int(L) for L in w.kv_lens]
-    krows, ks = _store_rows(w, seed, STREAM_K, w.num_kv_heads, w.kv_dtype, device, lens)
-    k_pages = _scatter(krows, w, kv_indices, num_pages, device)
-    del krows
-    vrows, vs = _store_rows(w, seed, STREAM_V, w.num_kv_heads, w.kv_dtype, device, lens)
-    v_pages = _scatter(vrows, w, kv_indices, num_pages, device)
-    del vrows
+
+    def paged(stream):
+        if w.kv_dtype == MXFP4:
+            rows = _store_mxfp4_rows(w, seed, stream, w.num_kv_heads, device, lens)
+            return _records(_scatter(rows, w, kv_indices, num_pages, device)), None
+        rows, sc = _store_rows(w, seed, stream, w.num_kv_heads, w.kv_dtype, device, lens)
+        return _scatter(rows, w, kv_indices, num_pages, device), sc
+    k_pages, ks = paged(STREAM_K)
+    v_pages, vs = paged(STREAM_V)
     inp = DeviceInputs(w, kv_indices, q, k_pages, v_pages, ks, vs)
     if w.num_proxy_heads > 0:  # prefill, or a decode step that runs its own indexer pass
         P, Pk = w.num_proxy_heads, w.num_proxy_kv_heads
@@ -187,12 +199,7 @@ def make_inputs_device(w: Workload, seed: int, device="cuda", picks_sets: int = 
         inp.proxy_q, inp.proxy_q_scale = pq_rows[0], pqs
         if w.proxy_dtype in (MXFP4, MXFP4_QK):
             pk_rows = _store_mxfp4_rows(w, seed, STREAM_PK, Pk, device, lens, add_k)
-            pool = _scatter(pk_rows, w, kv_indices, num_pages, device)          # [N, Pk, B, d/2 + d/32]
-            N, _, B, wd = pool.shape
-            cb = wd * 16 // 17
-            inp.proxy_k_pages = torch.cat([pool[..., :cb].reshape(N, Pk, B * cb),
-                                           pool[..., cb:].reshape(N, Pk, B * (wd - cb))], dim=-1).contiguous()
-            del pool
+            inp.proxy_k_pages = _records(_scatter(pk_rows, w, kv_indices, num_pages, device))
             pks = None
         else:
             pk_rows, pks = _store_rows(w, seed, STREAM_PK, Pk, w.proxy_dtype, device, lens, add_k)

@@ -161,7 +161,7 @@ class Workload:
 
 # The workloads the benchmark and the parity tests are built on (1-5: the
 # configurations the measurements are quoted on; 6, 7: a decode step with its
-# indexer pass, fp8 or MXFP4 proxy K; 8: the 32K prefill with MXFP4 proxies).
+# indexer pass, fp8 or MXFP4 proxy K; 8: the 32K prefill in MXFP4).
 def workload(n: int, **over) -> Workload:
     if n == 1:
         w = Workload("prefill_1k_gqa4", [1024], [1024], 8, 2, 2, 2, topk=4, page_table="identity")
@@ -186,8 +186,9 @@ def workload(n: int, **over) -> Workload:
         w = Workload("decode_step_mxfp4_b32_131k", [1] * 32, [131072] * 32, 64, 8, 8, 1, topk=17, kv_dtype=FP8,
                      proxy_dtype=MXFP4, lowrank=8, mode="decode")
     elif n == 8:
-        # the 32K prefill with MXFP4 proxy q and K
-        w = Workload("prefill_32k_gqa4_mxfp4proxy", [32768], [32768], 32, 8, 8, 8, topk=16, proxy_dtype=MXFP4_QK)
+        # the 32K prefill in MXFP4: proxy q and K, and the K/V pages
+        w = Workload("prefill_32k_gqa4_mxfp4", [32768], [32768], 32, 8, 8, 8, topk=16, kv_dtype=MXFP4,
+                     proxy_dtype=MXFP4_QK)
     else:
         raise ValueError(n)
     return dataclasses.replace(w, **over)
@@ -267,6 +268,10 @@ def make_inputs(w: Workload, seed: int) -> Inputs:
 
     def paged(stream, H, dtype):
         rows = kv_rows(stream, H)
+        if dtype == MXFP4:
+            bits = [to_mxfp4_rows(r) for r in rows]
+            pool = _scatter_pages(bits, w, kv_indices, num_pages, NAN_MXFP4, np.uint8)
+            return mxfp4_pool_to_records(pool), None
         if dtype == BF16:
             bits = [to_bf16_bits(r) for r in rows]
             scale = None

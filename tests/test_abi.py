@@ -62,7 +62,7 @@ def test_plan_info_and_workspace():
     (dict(qo_lens=[0, 5]), msa.MSA_ERR_INVALID_ARG),
     (dict(num_proxy_heads=1), msa.MSA_ERR_UNSUPPORTED),
     (dict(num_proxy_kv_heads=3), msa.MSA_ERR_INVALID_ARG),
-    (dict(kv_dtype="fp8"), msa.MSA_ERR_UNSUPPORTED),                         # fp8 K/V prefill not built
+    (dict(kv_dtype="mxfp4", mode="decode", qo_lens=None), msa.MSA_ERR_UNSUPPORTED),  # MXFP4 K/V decode not built
     (dict(sm_scale=-1.0), msa.MSA_ERR_INVALID_ARG),
     (dict(attn_window_rows=-1), msa.MSA_ERR_INVALID_ARG),
 ])
@@ -120,8 +120,14 @@ def test_compute_calls_validate_before_touching_the_device():
     assert L.msa_topk_select(p.handle, a, 0, 10, a, ctypes.c_void_p(0x20010), nb, none) == msa.MSA_ERR_INVALID_ARG
     # wrong mode
     assert L.msa_sparse_attn_decode(p.handle, a, a, a, none, none, a, a, a, none, ws, nb, none) == msa.MSA_ERR_UNSUPPORTED
-    # prefill takes no scales
+    # bf16 prefill takes no scales; fp8 prefill needs both; MXFP4 none
     assert L.msa_sparse_attn_prefill(p.handle, a, a, a, a, a, a, a, a, none, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    p8 = _plan(kv_dtype="fp8")
+    assert L.msa_sparse_attn_prefill(p8.handle, a, a, a, a, none, a, a, a, none, ws, p8.workspace_bytes, none) == \
+        msa.MSA_ERR_INVALID_ARG
+    p4 = _plan(kv_dtype="mxfp4")
+    assert L.msa_sparse_attn_prefill(p4.handle, a, a, a, a, a, a, a, a, none, ws, p4.workspace_bytes, none) == \
+        msa.MSA_ERR_INVALID_ARG
     d = msa.msa_plan(None, [1000] * 4, 16, 2, topk=17, kv_dtype="fp8", mode="decode", allocate=False)
     # fp8 decode needs both scales
     assert L.msa_sparse_attn_decode(d.handle, a, a, a, a, none, a, a, a, none, ws, d.workspace_bytes, none) == msa.MSA_ERR_INVALID_ARG

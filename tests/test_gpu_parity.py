@@ -60,6 +60,11 @@ PREFILL_CASES = {
                                        extra_pages=0.2, poison_tail=True), 31, 0),
     "mxfp4_qk_prefill": (Workload("mxqk", [600, 513], [900, 513], 16, 2, 2, 2, topk=5, proxy_dtype=MXFP4_QK,
                                   lowrank=8, poison_tail=True), 32, 200),
+    # fp8 and MXFP4 K/V pages in the sparse prefill attention
+    "fp8_kv_prefill": (Workload("kv8", [700, 77, 1], [700, 300, 1], 16, 4, 4, 4, topk=5, kv_dtype=FP8,
+                                extra_pages=0.2, poison_tail=True), 33, 0),
+    "mxfp4_kv_prefill": (Workload("kv4", [513, 300], [513, 900], 16, 2, 2, 2, topk=6, kv_dtype=MXFP4,
+                                  proxy_dtype=MXFP4_QK, extra_pages=0.2, poison_tail=True), 34, 0),
 }
 
 
@@ -81,7 +86,8 @@ def run_prefill_stages(msa, inp, max_rows):
         ms_all.append(msa.max_score_rows(ms, plan, n).cpu().numpy().copy())
     out = torch.full((T, w.num_qo_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((T, w.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
-    msa.msa_sparse_attn_prefill(plan, d["q"], d["k_pages"], d["v_pages"], d["kv_indices"], sel, out, lse)
+    msa.msa_sparse_attn_prefill(plan, d["q"], d["k_pages"], d["v_pages"], d["kv_indices"], sel, out, lse,
+                                d["k_scale"], d["v_scale"])
     torch.cuda.synchronize()
     return np.concatenate(ms_all, axis=2), sel.cpu().numpy(), bf16_out_to_f64(out), lse.cpu().numpy()
 
@@ -101,7 +107,7 @@ def test_prefill_stages_match_oracle(case):
     locals_ = np.array([lay.local(r) for r in range(w.total_rows)])
     check_selection(gsel, ref_ms, locals_, w.topk, case)
     ref_out, ref_lse = O.sparse_attention(inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, gsel, w.qo_lens,
-                                          w.kv_lens, w.page_size, w.sm_scale)
+                                          w.kv_lens, w.page_size, w.sm_scale, w.kv_dtype, inp.k_scale, inp.v_scale)
     check_output(gout, ref_out, BF16_ATOL, BF16_COS, case)
     assert np.abs(glse - ref_lse).max() < 1e-3, case
 

@@ -213,3 +213,40 @@ def test_decode_all_blocks_equals_dense_and_last_prefill_row():
     # fp8 V scale multiplies the output
     out2, _ = sparse_decode(q, kp, vp, kvi, sel, kv, B, 0.2, FP8, ks, vs * 2)
     assert np.abs(out2 - 2 * out).max() < 1e-12
+
+
+def test_mxfp4_kv_equals_bf16_path_on_the_same_values():
+    """Attention over MXFP4 K/V records equals the bf16 path bit for bit on
+    values both formats hold exactly (E2M1 x 2^X)."""
+    from oracle import MXFP4, E2M1_TABLE, Layout
+    from synthetic.gen import to_mxfp4_rows, mxfp4_pool_to_records, to_bf16_bits
+    rng = np.random.default_rng(21)
+    qo, kv, B, Hq, Hkv, k = [200, 1], [300, 500], 128, 4, 2, 3
+    T = sum(qo)
+    nbs = [-(-L // B) for L in kv]
+    N = sum(nbs)
+    kvi = rng.permutation(N).astype(np.int32)
+
+    def mx_values(shape):
+        codes = rng.integers(0, 16, size=shape + (128,))
+        codes[..., ::32] = rng.choice([6, 7, 14, 15], size=shape + (4,))
+        X = rng.integers(-4, 1, size=shape + (4,))
+        return E2M1_TABLE[codes] * np.repeat(np.ldexp(1.0, X), 32, axis=-1)
+    kvals, vvals = mx_values((N, Hkv, B)), mx_values((N, Hkv, B))
+    q = to_bf16_bits(rng.standard_normal((T, Hq, 128)).astype(np.float32))
+    sel = np.full((T, Hkv, k), -1, np.int32)
+    lay = Layout(qo, kv, B)
+    for r in range(T):
+        loc = lay.local(r)
+        for g in range(Hkv):
+            pick = np.sort(rng.choice(loc + 1, size=min(k, loc + 1), replace=False))
+            if loc not in pick:
+                pick[-1] = loc
+                pick = np.sort(pick)
+            sel[r, g, :pick.size] = pick
+    krec = mxfp4_pool_to_records(to_mxfp4_rows(kvals.astype(np.float32)))
+    vrec = mxfp4_pool_to_records(to_mxfp4_rows(vvals.astype(np.float32)))
+    a, la = sparse_attention(q, krec, vrec, kvi, sel, qo, kv, B, 0.1, MXFP4)
+    b, lb = sparse_attention(q, to_bf16_bits(kvals.astype(np.float32)), to_bf16_bits(vvals.astype(np.float32)), kvi,
+                             sel, qo, kv, B, 0.1)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
