@@ -362,6 +362,61 @@ def sparse_attention(q, k_pages, v_pages, kv_indices, kv_block_indexes, qo_lens,
     return out, lse
 
 
+def sparse_attention_backward(q, k_pages, v_pages, kv_indices, kv_block_indexes, qo_lens, kv_lens, page_size, sm_scale,
+                              dout):
+    """Gradients of the block-sparse attention above ([FLASH] the training
+    kernels: the selection is computed once in the forward pass and reused,
+    so the backward runs over the same cached blocks) for bf16 q, K, V and an
+    upstream gradient dout [T, H_q, d] (bf16 bits).
+
+    For row r, head h, group g and the keys K(r, g) of the forward:
+      p_j  = softmax_j(s_j),  s_j = sm_scale <q[r,h], k_j>,  o = sum_j p_j v_j
+      dv_j += p_j dout[r,h]
+      dp_j  = <dout[r,h], v_j>,   D = <dout[r,h], o>
+      ds_j  = p_j (dp_j - D)
+      dq[r,h] = sm_scale sum_j ds_j k_j
+      dk_j   += sm_scale ds_j q[r,h]
+    dk and dv are accumulated per (page, KV head, slot) of the paged pools.
+
+    Returns (dq float64 [T, H_q, d], dk float64, dv float64 shaped like the
+    page pools); pool slots no row attends to stay 0.
+    """
+    lay = Layout(qo_lens, kv_lens, page_size)
+    T, Hq, d = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    B = lay.B
+    dq = np.zeros((T, Hq, d))
+    dk = np.zeros(k_pages.shape[:2] + (B, d))
+    dv = np.zeros(v_pages.shape[:2] + (B, d))
+    kvi = np.asarray(kv_indices, dtype=np.int64)
+    for r in range(T):
+        s = lay.seq_of_row(r)
+        pos = lay.pos(r)
+        L = lay.kv[s]
+        qv = bf16_to_f64(q[r])
+        dov = bf16_to_f64(dout[r])
+        for g in range(Hkv):
+            blocks = sorted(set(int(b) for b in kv_block_indexes[r, g] if b >= 0))
+            keys = np.concatenate([np.arange(b * B, (b + 1) * B) for b in blocks]) if blocks else np.zeros(0, np.int64)
+            keys = keys[(keys <= pos) & (keys < L)]
+            K = gather_rows(k_pages, BF16, None, kv_indices, lay, s, g, keys)
+            V = gather_rows(v_pages, BF16, None, kv_indices, lay, s, g, keys)
+            pages = kvi[lay.page_start[s] + keys // B]
+            slots = keys % B
+            for h in range(g * G, (g + 1) * G):
+                sc = sm_scale * (K @ qv[h])
+                w = np.exp(sc - sc.max())
+                p = w / w.sum()
+                o = p @ V
+                dp = V @ dov[h]
+                ds = p * (dp - dov[h] @ o)
+                dq[r, h] = sm_scale * (ds @ K)
+                np.add.at(dv, (pages, g, slots), p[:, None] * dov[h][None, :])
+                np.add.at(dk, (pages, g, slots), sm_scale * ds[:, None] * qv[h][None, :])
+    return dq, dk, dv
+
+
 def sparse_decode(q, k_pages, v_pages, kv_indices, kv_block_indexes, kv_lens, page_size, sm_scale,
                   kv_dtype=FP8, k_scale=None, v_scale=None, rows=None):
     """Paged sparse decode ([README] "Stacks": paged FP8 decode wrapper): one

@@ -94,3 +94,36 @@ def test_mxfp4_scale_group_off_by_one_is_caught(monkeypatch):
     monkeypatch.setattr(om, "mxfp4_record_rows", bad)
     with pytest.raises(AssertionError):
         tp.test_mxfp4_proxy_k_equals_bf16_path_on_the_same_values()
+
+
+def test_backward_without_the_rowsum_term_is_caught(monkeypatch):
+    """ds_j = p_j dp_j (dropping the D = <dout, o> term) must fail the pins."""
+    from tests import test_oracle_backward as tb
+    src = om.sparse_attention_backward
+
+    def bad(q, k_pages, v_pages, kv_indices, sel, qo_lens, kv_lens, B, scale, dout):
+        zero_o = {"flag": True}
+        orig_gather = om.gather_rows
+        dq, dk, dv = src(q, k_pages, v_pages, kv_indices, sel, qo_lens, kv_lens, B, scale, dout)
+        # recompute dq with ds = p * dp only
+        lay = om.Layout(qo_lens, kv_lens, B)
+        T, Hq, d = q.shape
+        G = Hq // k_pages.shape[1]
+        for r in range(T):
+            s = lay.seq_of_row(r)
+            pos = lay.pos(r)
+            for g in range(k_pages.shape[1]):
+                blocks = sorted(set(int(b) for b in sel[r, g] if b >= 0))
+                keys = np.concatenate([np.arange(b * B, (b + 1) * B) for b in blocks])
+                keys = keys[(keys <= pos) & (keys < lay.kv[s])]
+                K = orig_gather(k_pages, om.BF16, None, kv_indices, lay, s, g, keys)
+                V = orig_gather(v_pages, om.BF16, None, kv_indices, lay, s, g, keys)
+                for h in range(g * G, (g + 1) * G):
+                    sc = scale * (K @ om.bf16_to_f64(q[r, h]))
+                    p = np.exp(sc - sc.max())
+                    p /= p.sum()
+                    dq[r, h] = scale * ((p * (V @ om.bf16_to_f64(dout[r, h]))) @ K)
+        return dq, dk, dv
+    monkeypatch.setattr(tb, "sparse_attention_backward", bad)
+    with pytest.raises(AssertionError):
+        tb.test_backward_matches_finite_differences_of_the_forward()
