@@ -117,8 +117,9 @@ hipEvent_t take_event(msa::Profiler& pr) {
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
 }
-const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "proxy_topk", "csr", "partial_attn", "merge",
-                                    "decode", "decode_merge"};
+const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "proxy_topk", "csr",        "partial_attn",
+                                    "merge",          "decode",      "decode_merge", "bwd_dq", "bwd_dq_sum",
+                                    "bwd_dkv"};
 }  // namespace
 
 ProfEvents::ProfEvents(const msa_plan_s* p, const char* name) {
@@ -478,6 +479,41 @@ msa_status_t msa_sparse_attn_prefill_rows(msa_plan_t p, const void* q, const voi
                                           msa_stream_t stream) {
   return prefill_rows(__func__, p, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes, out, lse,
                       row_begin, row_count, workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_sparse_attn_prefill_backward(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                              const int32_t* kv_indices, const int32_t* kv_block_indexes,
+                                              const void* out, const float* lse, const void* dout, float* dq,
+                                              float* dk_pages, float* dv_pages, void* workspace, size_t workspace_bytes,
+                                              msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill_backward: NULL plan");
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_prefill_backward: decode plan");
+  if (p->d.kv_dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_prefill_backward: the backward is built for bf16 K/V");
+  MSA_CHECK_PTR(q);
+  MSA_CHECK_PTR(k_pages);
+  MSA_CHECK_PTR(v_pages);
+  MSA_CHECK_PTR(kv_indices);
+  MSA_CHECK_PTR(kv_block_indexes);
+  MSA_CHECK_PTR(out);
+  MSA_CHECK_PTR(lse);
+  MSA_CHECK_PTR(dout);
+  MSA_CHECK_PTR(dq);
+  MSA_CHECK_PTR(dk_pages);
+  MSA_CHECK_PTR(dv_pages);
+  msa_status_t st = check_ws(p, workspace, workspace_bytes);
+  if (st != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  for (int64_t w0 = 0; w0 < p->T; w0 += p->attn_window) {
+    const int32_t w1 = (int32_t)std::min<int64_t>(p->T, w0 + p->attn_window);
+    hipError_t e = msa::launch_prefill_backward_window(p, m, q, k_pages, v_pages, kv_indices, kv_block_indexes, out,
+                                                       lse, dout, dq, dk_pages, dv_pages,
+                                                       static_cast<char*>(workspace), (int32_t)w0, w1, w0 == 0, hs);
+    if (e != hipSuccess) return hip_status(e, __func__);
+  }
+  return ok();
 }
 
 msa_status_t msa_sparse_attn_decode(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,

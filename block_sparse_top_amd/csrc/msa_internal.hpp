@@ -89,6 +89,11 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
                                  const void* vp, const float* ks, const float* vs, const int32_t* kv_indices,
                                  const int32_t* sel, void* out, float* lse, char* ws, int32_t w0, int32_t w1,
                                  hipStream_t st);
+hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
+                                          const void* vp, const int32_t* kv_indices, const int32_t* sel,
+                                          const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                                          float* dv, char* ws, int32_t w0, int32_t w1, bool first_window,
+                                          hipStream_t st);
 hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
                          const float* ks, const float* vs, const int32_t* kv_indices, const int32_t* sel,
                          void* out, float* lse, char* ws, hipStream_t st);

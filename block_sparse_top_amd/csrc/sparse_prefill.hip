@@ -482,10 +482,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 }  // namespace
 
-hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
-                                 const void* vp, const float* ks, const float* vs, const int32_t* kv_indices,
-                                 const int32_t* sel, void* out, float* lse, char* ws, int32_t w0, int32_t w1,
-                                 hipStream_t st) {
+namespace {
+
+// Invert kv_block_indexes for rows [w0, w1) into per-(group, block) entry
+// lists (counts, offsets, entries) and the capped work items.
+void build_csr(const msa_plan_s* p, const DevMeta& m, const int32_t* sel, char* ws, int32_t w0, int32_t w1,
+               hipStream_t st) {
   const PlanLayout& L = p->lay;
   const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
   const int32_t nkey = Hkv * p->NB;
@@ -522,6 +524,22 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   if (lds_hist) hipExtLaunchKernelGGL((csr_pass_kernel<true, true>), cgrid, dim3(256), hist_bytes, st, nullptr, pe.stop, 0, c);
   else hipExtLaunchKernelGGL((csr_pass_kernel<true, false>), cgrid, dim3(256), 0, st, nullptr, pe.stop, 0, c);
   }
+
+}
+
+}  // namespace
+
+hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
+                                 const void* vp, const float* ks, const float* vs, const int32_t* kv_indices,
+                                 const int32_t* sel, void* out, float* lse, char* ws, int32_t w0, int32_t w1,
+                                 hipStream_t st) {
+  const PlanLayout& L = p->lay;
+  const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
+  const int32_t nkey = Hkv * p->NB;
+  const int32_t* entries = reinterpret_cast<const int32_t*>(ws + L.entries);
+  const int4* items = reinterpret_cast<const int4*>(ws + L.items);
+  const int32_t* nitems = reinterpret_cast<const int32_t*>(ws + L.nitems);
+  build_csr(p, m, sel, ws, w0, w1, st);
 
   PartialArgs a;
   a.q = static_cast<const uint8_t*>(q);
@@ -573,6 +591,495 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   {
     ProfEvents pe(p, "merge");
     hipExtLaunchKernelGGL(merge_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, pe.start, pe.stop, 0, mg);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Backward: gradients of the attention above for training, over the same
+// cached selection (the Flash-MSA article: block indexes are computed once in
+// the forward pass and reused, so everything but the proxy pass stays linear
+// in the cached blocks).  With P the softmax of a row over its keys, L its
+// log-sum-exp (from the forward) and dO the upstream gradient:
+//   D = <dO, O>;  dP = dO V^T;  dS = P (dP - D)
+//   dQ = scale dS K;  dK = scale dS^T Q;  dV = P^T dO
+// in two kernels that reuse the forward's layouts:
+//  * bwd_dq (row-centric, per work item): S^T = K Q^T, P^T = exp2(S^T
+//    scale_log2 - L log2 e), dP^T = V dO^T, dS^T, then dQ^T = K^T dS^T with
+//    K^T read transposed from LDS (the forward's V^T P^T step); a bf16 dQ
+//    partial per (row, head, slot), summed over slots by bwd_dq_sum;
+//  * bwd_dkv (key-centric, one workgroup per (group, block) over all its
+//    rows): wave w owns keys 32w..32w+31; S = Q K^T and dP = dO V^T put the
+//    keys on lanes, so P and dS are directly the A operands of
+//    dV += P^T dO and dK += dS^T Q, whose dO and Q operands are read
+//    transposed from LDS.
+// S and dP are computed in both kernels (7 products instead of 5): each
+// kernel then needs no layout exchange of P or dS between waves.
+namespace {
+
+struct PrepArgs {
+  const uint16_t* out;    // bf16 [T, Hq, 128]
+  const uint16_t* dout;
+  float* D;               // [W, Hq]
+  int32_t w0, w1, Hq;
+};
+
+// D = <dO, O> per (row, head): 16 lanes per pair, 8 columns each.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
+  const int sub = threadIdx.x & 15;
+  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = idx < (int64_t)(a.w1 - a.w0) * a.Hq;   // shuffles need every lane
+  const int64_t id = live ? idx : 0;
+  const int64_t off = ((int64_t)a.w0 * a.Hq + id) * 128 + 8 * sub;
+  const i32x4 o = *reinterpret_cast<const i32x4*>(a.out + off);
+  const i32x4 g = *reinterpret_cast<const i32x4*>(a.dout + off);
+  float acc = 0.f;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    acc += __builtin_bit_cast(float, (uint32_t)o[x] << 16) * __builtin_bit_cast(float, (uint32_t)g[x] << 16);
+    acc += __builtin_bit_cast(float, (uint32_t)o[x] & 0xffff0000u) * __builtin_bit_cast(float, (uint32_t)g[x] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) acc += __shfl_xor(acc, sh, 16);
+  if (live && sub == 0) a.D[id] = acc;
+}
+
+struct BwdDqArgs {
+  const uint8_t* q;       // bf16 [T, Hq, 128]
+  const uint8_t* dout;
+  const uint8_t* kp;      // bf16 [N, Hkv, 128, 128]
+  const uint8_t* vp;
+  const float* lse;       // [T, Hq], natural log
+  const float* D;         // [W, Hq]
+  const int32_t* kv_indices;
+  const int32_t* entries;
+  const int4* items;
+  const int32_t* nitems;
+  DevMeta m;
+  uint16_t* part;         // bf16 dQ partials [W, Hq, k, 128], then one trash slot
+  int64_t trash;
+  int32_t Hq, Hkv, G, k, w0;
+  float scale_log2, sm_scale;
+};
+
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz: S^T operand
+  __shared__ __attribute__((aligned(16))) uint8_t kt[128 * 256];   // K, v_swz: transposed reads (K^T)
+  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, k_swz: dP^T operand
+  __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
+  __shared__ int32_t ent_s[kMaxItemEntries];
+  const int item = blockIdx.x;
+  if (item >= *a.nitems) return;
+  const int4 it = a.items[item];
+  const int g = it.x, gb = it.y, e0 = it.z, e1 = it.w;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = upper_bound_i32(a.m.page_start, a.m.S + 1, gb) - 1;
+  const int b = gb - a.m.page_start[s];
+  const int32_t page = a.kv_indices[gb];
+  const int32_t first_pos = a.m.kv[s] - a.m.qo[s];
+  const int32_t rs = a.m.row_start[s];
+  const int n_ent = e1 - e0;
+  {  // K (twice) and V -> LDS; padding rows (past kv_len) zeroed: dS and P are 0 there but 0 * NaN is NaN
+    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * 32768;
+    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * 32768;
+    i32x4 kr[8], vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      kr[i] = *reinterpret_cast<const i32x4*>(kb + c * 16);
+      vr[i] = *reinterpret_cast<const i32x4*>(vb + c * 16);
+    }
+    for (int i = tid; i < n_ent; i += 256) ent_s[i] = a.entries[e0 + i];
+    const int kv_in_block = a.m.kv[s] - b * 128;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      const bool live_row = (c >> 4) < kv_in_block;
+      lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], kr[i]);
+      lds_store16<i32x4>(&kt[v_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
+      lds_store16<i32x4>(&vs[k_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
+    }
+  }
+  __syncthreads();
+
+  const int G = a.G;
+  const int MT = 128 / G;
+  const int qr = 32 * wave + (lane & 31);
+  const int half = lane >> 5;
+  const int q16 = lane >> 4, m16 = lane & 15;
+  const int hh = qr % G, tok = qr / G;
+  const int h = g * G + hh;
+  const int nchunks = (n_ent + MT - 1) / MT;
+  int kbase[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) kbase[st] = (lane & 31) * 256 + (((2 * st + half) ^ (lane & 15)) << 4);
+  int vbase[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
+                ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  uint8_t* ow = ost + wave * kOStage;
+
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    const int e = chunk * MT + tok;
+    const bool valid = e < n_ent;
+    const int ent = ent_s[valid ? e : n_ent - 1];   // padding rows repeat a real one; their output is discarded
+    const int rl = ent >> 6, slot = ent & 63;
+    const int32_t r = a.w0 + rl;
+    const int32_t pos = first_pos + (r - rs);
+    const float l2 = a.lse[(int64_t)r * a.Hq + h] * kLog2e;
+    const float dval = a.D[(int64_t)rl * a.Hq + h];
+    bf16x8 qf[8], df[8];
+    {
+      const uint8_t* qrow = a.q + ((int64_t)r * a.Hq + h) * 256 + half * 16;
+      const uint8_t* drow = a.dout + ((int64_t)r * a.Hq + h) * 256 + half * 16;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
+        df[st] = *reinterpret_cast<const bf16x8*>(drow + st * 32);
+      }
+    }
+    // S^T = K Q^T, then P^T in place (hidden keys: -inf -> 0)
+    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int kt_ = 0; kt_ < 4; ++kt_) acc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&ks[kbase[st] + 8192 * kt_]), qf[st], acc[kt_]);
+    const int lim = pos - b * 128 - 4 * half;
+#pragma unroll
+    for (int kt_ = 0; kt_ < 4; ++kt_)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        acc[kt_][i] = (32 * kt_ + 8 * (i >> 2) + (i & 3)) <= lim ? fast_exp2(__builtin_fmaf(acc[kt_][i], a.scale_log2, -l2))
+                                                                : 0.f;
+    // dP^T = V dO^T
+    f32x16 dacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int kt_ = 0; kt_ < 4; ++kt_) dacc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&vs[kbase[st] + 8192 * kt_]), df[st], dacc[kt_]);
+    // dS^T = P^T (dP^T - D) as bf16 B operands
+    bf16x8 sf[4][2];
+#pragma unroll
+    for (int kt_ = 0; kt_ < 4; ++kt_)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        i32x4 pw;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int i0 = 8 * u + 2 * t;
+          const bf16x2 two = {(__bf16)(acc[kt_][i0] * (dacc[kt_][i0] - dval)),
+                              (__bf16)(acc[kt_][i0 + 1] * (dacc[kt_][i0 + 1] - dval))};
+          pw[t] = __builtin_bit_cast(int, two);
+        }
+        sf[kt_][u] = __builtin_bit_cast(bf16x8, pw);
+      }
+    // dQ^T = K^T dS^T
+    f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kt_ = 0; kt_ < 4; ++kt_) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const s16x4 lo = lds_read_tr16(&kt[vbase[dt] + 256 * (32 * kt_ + 16 * u)]);
+          const s16x4 hi = lds_read_tr16(&kt[vbase[dt] + 256 * (32 * kt_ + 16 * u + 8)]);
+          oacc[dt] = mfma32x32x16(join_tr16(lo, hi), sf[kt_][u], oacc[dt]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // scaled bf16 partial through the wave's staging area (as the forward's output)
+    int64_t spi[2];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int srow = 32 * wave + 16 * pass + (lane >> 2);
+      const int se = chunk * MT + srow / G;
+      const bool sv = se < n_ent;
+      const int sent = ent_s[sv ? se : 0];
+      spi[pass] = sv ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
+    }
+    const int jrow = lane & 31;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const bf16x2 lo2 = {(__bf16)(oacc[dt][4 * gq] * a.sm_scale), (__bf16)(oacc[dt][4 * gq + 1] * a.sm_scale)};
+        const bf16x2 hi2 = {(__bf16)(oacc[dt][4 * gq + 2] * a.sm_scale), (__bf16)(oacc[dt][4 * gq + 3] * a.sm_scale)};
+        const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+        lds_store8(&ow[jrow * 64 + ((gq ^ ((jrow >> 2) & 3)) << 4) + 8 * half], pk);
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int rr = 16 * pass + (lane >> 2), c = lane & 3;
+        const i32x4 v = lds_load16<i32x4>(&ow[rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4)]);
+        *reinterpret_cast<i32x4*>(a.part + spi[pass] * 128 + 32 * dt + 8 * c) = v;
+      }
+      wave_lds_sync();
+    }
+    (void)slot;
+    (void)valid;
+  }
+}
+
+struct DqSumArgs {
+  const int32_t* sel;
+  DevMeta m;
+  const uint16_t* part;
+  float* dq;              // fp32 [T, Hq, 128]
+  int32_t Hq, Hkv, G, k, w0, w1;
+};
+
+// dQ of a (row, head) = the sum of its valid slots' partials; 16 lanes per
+// pair, 8 columns each.
+__global__ __launch_bounds__(256) void bwd_dq_sum_kernel(DqSumArgs a) {
+  const int sub = threadIdx.x & 15;
+  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (idx >= (int64_t)(a.w1 - a.w0) * a.Hq) return;
+  const int32_t rl = (int32_t)(idx / a.Hq);
+  const int h = (int)(idx % a.Hq);
+  const int g = h / a.G;
+  const int32_t r = a.w0 + rl;
+  const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
+  const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
+  const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
+  const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int slot = 0; slot < a.k; ++slot) {
+    const int bk = row[slot];
+    if (bk < 0 || bk > local) continue;
+    const i32x4 v = *reinterpret_cast<const i32x4*>(a.part + (base + slot) * 128 + 8 * sub);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      o[2 * x] += __builtin_bit_cast(float, (uint32_t)v[x] << 16);
+      o[2 * x + 1] += __builtin_bit_cast(float, (uint32_t)v[x] & 0xffff0000u);
+    }
+  }
+  float* dst = a.dq + ((int64_t)r * a.Hq + h) * 128 + 8 * sub;
+  *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+}
+
+struct BwdKvArgs {
+  const uint8_t* q;       // bf16 [T, Hq, 128]
+  const uint8_t* dout;
+  const uint8_t* kp;      // bf16 [N, Hkv, 128, 128]
+  const uint8_t* vp;
+  const float* lse;       // [T, Hq], natural log
+  const float* D;         // [W, Hq]
+  const int32_t* kv_indices;
+  const int32_t* entries;
+  const int32_t* offsets; // [Hkv * NB + 1]
+  DevMeta m;
+  float* dk;              // fp32 [N, Hkv, 128, 128]
+  float* dv;
+  int32_t Hq, Hkv, G, NB, w0, accumulate;
+  float scale_log2, sm_scale;
+};
+
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz
+  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, k_swz
+  __shared__ __attribute__((aligned(16))) uint8_t qt[32 * 256];    // the chunk's 32 q rows, v_swz
+  __shared__ __attribute__((aligned(16))) uint8_t dtile[32 * 256]; // the chunk's 32 dO rows, v_swz
+  __shared__ float l2_s[32], d_s[32];
+  __shared__ int32_t pos_s[32];
+  const int key = blockIdx.x;
+  const int g = key / a.NB, gb = key % a.NB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = upper_bound_i32(a.m.page_start, a.m.S + 1, gb) - 1;
+  const int b = gb - a.m.page_start[s];
+  const int32_t page = a.kv_indices[gb];
+  const int32_t first_pos = a.m.kv[s] - a.m.qo[s];
+  const int32_t rs = a.m.row_start[s];
+  const int e0 = a.offsets[key], n_ent = a.offsets[key + 1] - e0;
+  {
+    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * 32768;
+    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * 32768;
+    const int kv_in_block = a.m.kv[s] - b * 128;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      const bool live_row = (c >> 4) < kv_in_block;
+      const i32x4 kr = *reinterpret_cast<const i32x4*>(kb + c * 16);
+      const i32x4 vr = *reinterpret_cast<const i32x4*>(vb + c * 16);
+      lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], live_row ? kr : i32x4{});
+      lds_store16<i32x4>(&vs[k_swz(c >> 4, c & 15)], live_row ? vr : i32x4{});
+    }
+  }
+  const int G = a.G;
+  const int MT = 32 / G;                       // tokens per 32-row chunk
+  const int half = lane >> 5, j = lane & 31;
+  const int q16 = lane >> 4, m16 = lane & 15;
+  const int nchunks = (n_ent + MT - 1) / MT;
+  const int keypos = b * 128 + 32 * wave + j;  // this lane's key position
+  int vbase[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
+                ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  f32x16 dkacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  f32x16 dvacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    __syncthreads();  // K/V staged (first chunk); the previous chunk's tiles are no longer read
+    for (int x = tid; x < 32 * 16; x += 256) {   // gather the chunk's rows: row i = token (i / G), head (i % G)
+      const int ri = x >> 4, c = x & 15;
+      const int e = min(chunk * MT + ri / G, n_ent - 1);
+      const int32_t r = a.w0 + (a.entries[e0 + e] >> 6);
+      const int64_t off = ((int64_t)r * a.Hq + g * G + ri % G) * 256 + c * 16;
+      lds_store16<i32x4>(&qt[v_swz(ri, c)], *reinterpret_cast<const i32x4*>(a.q + off));
+      lds_store16<i32x4>(&dtile[v_swz(ri, c)], *reinterpret_cast<const i32x4*>(a.dout + off));
+    }
+    if (tid < 32) {
+      const int ri = tid;
+      const int ee = chunk * MT + ri / G;
+      const int e = min(ee, n_ent - 1);
+      const int rl = a.entries[e0 + e] >> 6;
+      const int32_t r = a.w0 + rl;
+      const int h = g * G + ri % G;
+      l2_s[ri] = a.lse[(int64_t)r * a.Hq + h] * kLog2e;
+      d_s[ri] = a.D[(int64_t)rl * a.Hq + h];
+      pos_s[ri] = ee < n_ent ? first_pos + (r - rs) : -1;   // padding rows see no key
+    }
+    __syncthreads();
+    // S = Q K^T and dP = dO V^T for this wave's 32 keys: C[row][key], key on lanes
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 aq = lds_load16<bf16x8>(&qt[v_swz(j, 2 * st + half)]);
+      const bf16x8 bk = lds_load16<bf16x8>(&ks[k_swz(32 * wave + j, 2 * st + half)]);
+      sacc = mfma32x32x16(aq, bk, sacc);
+      const bf16x8 ad = lds_load16<bf16x8>(&dtile[v_swz(j, 2 * st + half)]);
+      const bf16x8 bv = lds_load16<bf16x8>(&vs[k_swz(32 * wave + j, 2 * st + half)]);
+      pacc = mfma32x32x16(ad, bv, pacc);
+    }
+    // P and dS (register r holds row 8(r/4) + 4 half + r%4), as bf16 A operands
+    bf16x8 pf[2], sf[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      i32x4 pw, sw;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float pv[2], sv[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int rr = 8 * u + 2 * t + x;
+          const int row = 8 * (rr >> 2) + 4 * half + (rr & 3);
+          const float p = keypos <= pos_s[row] ? fast_exp2(__builtin_fmaf(sacc[rr], a.scale_log2, -l2_s[row])) : 0.f;
+          pv[x] = p;
+          sv[x] = p * (pacc[rr] - d_s[row]);
+        }
+        const bf16x2 p2 = {(__bf16)pv[0], (__bf16)pv[1]};
+        const bf16x2 s2 = {(__bf16)sv[0], (__bf16)sv[1]};
+        pw[t] = __builtin_bit_cast(int, p2);
+        sw[t] = __builtin_bit_cast(int, s2);
+      }
+      pf[u] = __builtin_bit_cast(bf16x8, pw);
+      sf[u] = __builtin_bit_cast(bf16x8, sw);
+    }
+    // dV += P^T dO, dK += dS^T Q: dO and Q read transposed, rows in the same order
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const s16x4 dlo = lds_read_tr16(&dtile[vbase[dt] + 256 * (16 * u)]);
+        const s16x4 dhi = lds_read_tr16(&dtile[vbase[dt] + 256 * (16 * u + 8)]);
+        dvacc[dt] = mfma32x32x16(pf[u], join_tr16(dlo, dhi), dvacc[dt]);
+        const s16x4 qlo = lds_read_tr16(&qt[vbase[dt] + 256 * (16 * u)]);
+        const s16x4 qhi = lds_read_tr16(&qt[vbase[dt] + 256 * (16 * u + 8)]);
+        dkacc[dt] = mfma32x32x16(sf[u], join_tr16(qlo, qhi), dkacc[dt]);
+      }
+    }
+  }
+  // C[key][d]: lane (d, half), register r -> key 32 wave + 8 (r/4) + 4 half + r%4
+  const int64_t pbase = ((int64_t)page * a.Hkv + g) * 128;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = 32 * wave + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int64_t o = (pbase + kk) * 128 + 32 * dt + j;
+      const float vk = dkacc[dt][r] * a.sm_scale, vv = dvacc[dt][r];
+      a.dk[o] = a.accumulate ? a.dk[o] + vk : vk;
+      a.dv[o] = a.accumulate ? a.dv[o] + vv : vv;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
+                                          const void* vp, const int32_t* kv_indices, const int32_t* sel,
+                                          const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                                          float* dv, char* ws, int32_t w0, int32_t w1, bool first_window,
+                                          hipStream_t st) {
+  const PlanLayout& L = p->lay;
+  const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
+  const int32_t nkey = Hkv * p->NB;
+  build_csr(p, m, sel, ws, w0, w1, st);
+  float* D = reinterpret_cast<float*>(ws + L.part_lse);
+  uint16_t* part = reinterpret_cast<uint16_t*>(ws + L.part_o);
+  const int64_t npairs = (int64_t)(w1 - w0) * Hq;
+  {
+    PrepArgs pa{static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), D, w0, w1, Hq};
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, pa);
+  }
+  BwdDqArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.dout = static_cast<const uint8_t*>(dout);
+  a.kp = static_cast<const uint8_t*>(kp);
+  a.vp = static_cast<const uint8_t*>(vp);
+  a.lse = lse;
+  a.D = D;
+  a.kv_indices = kv_indices;
+  a.entries = reinterpret_cast<const int32_t*>(ws + L.entries);
+  a.items = reinterpret_cast<const int4*>(ws + L.items);
+  a.nitems = reinterpret_cast<const int32_t*>(ws + L.nitems);
+  a.m = m;
+  a.part = part;
+  a.trash = p->attn_window * Hq * k;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = p->G;
+  a.k = k;
+  a.w0 = w0;
+  a.scale_log2 = p->d.sm_scale * kLog2e;
+  a.sm_scale = p->d.sm_scale;
+  const int64_t max_items = ((int64_t)(w1 - w0) * Hkv * k + p->entries_per_item - 1) / p->entries_per_item + nkey;
+  {
+    ProfEvents pe(p, "bwd_dq");
+    hipExtLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)max_items), dim3(256), 0, st, pe.start, pe.stop, 0, a);
+  }
+  {
+    DqSumArgs ds{sel, m, part, dq, Hq, Hkv, p->G, k, w0, w1};
+    ProfEvents pe(p, "bwd_dq_sum");
+    hipExtLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, pe.start,
+                          pe.stop, 0, ds);
+  }
+  BwdKvArgs kv;
+  kv.q = a.q;
+  kv.dout = a.dout;
+  kv.kp = a.kp;
+  kv.vp = a.vp;
+  kv.lse = lse;
+  kv.D = D;
+  kv.kv_indices = kv_indices;
+  kv.entries = a.entries;
+  kv.offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
+  kv.m = m;
+  kv.dk = dk;
+  kv.dv = dv;
+  kv.Hq = Hq;
+  kv.Hkv = Hkv;
+  kv.G = p->G;
+  kv.NB = p->NB;
+  kv.w0 = w0;
+  kv.accumulate = first_window ? 0 : 1;
+  kv.scale_log2 = a.scale_log2;
+  kv.sm_scale = a.sm_scale;
+  {
+    ProfEvents pe(p, "bwd_dkv");
+    hipExtLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)nkey), dim3(256), 0, st, pe.start, pe.stop, 0, kv);
   }
   return hipGetLastError();
 }

@@ -227,6 +227,31 @@ msa_status_t msa_sparse_attn_prefill_rows(msa_plan_t plan, const void* q, const 
                                           int64_t row_count, void* workspace, size_t workspace_bytes,
                                           msa_stream_t stream);
 
+/* Training backward of stage 3a (Flash-MSA article, backward paragraphs:
+ * the forward pass's block indexes are cached and reused, so the backward
+ * runs over the same selection).  With P the softmax of row r, head h over
+ * its keys K(r, g) and dout the upstream gradient:
+ *   dv[j] += P_j dout[r][h]
+ *   ds_j   = P_j (<dout[r][h], v_j> - <dout[r][h], out[r][h]>)
+ *   dq[r][h] = sm_scale sum_j ds_j k_j,   dk[j] += sm_scale ds_j q[r][h]
+ *
+ *   q, k_pages, v_pages, kv_indices, kv_block_indexes: as in the forward
+ *                     (bf16 K/V only)
+ *   out, lse          the forward's output (bf16) and log-sum-exp (fp32,
+ *                     natural log) for the same inputs
+ *   dout              bf16 [T, H_q, 128]
+ *   dq                fp32 [T, H_q, 128], fully written
+ *   dk_pages, dv_pages fp32 [num_pages, H_kv, 128, 128]: every (page, head)
+ *                     that holds a block of some sequence is written (0 where
+ *                     no row attends to it); other pages are not touched
+ * Errors: INVALID_ARG for null or misaligned pointers; UNSUPPORTED for a
+ * decode plan or non-bf16 K/V; WORKSPACE_TOO_SMALL. */
+msa_status_t msa_sparse_attn_prefill_backward(msa_plan_t plan, const void* q, const void* k_pages,
+                                              const void* v_pages, const int32_t* kv_indices,
+                                              const int32_t* kv_block_indexes, const void* out, const float* lse,
+                                              const void* dout, float* dq, float* dk_pages, float* dv_pages,
+                                              void* workspace, size_t workspace_bytes, msa_stream_t stream);
+
 /* Stage 3b: paged sparse decode (README "Stacks": paged FP8 decode).  Stage
  * 3a with qo_len = 1 for every sequence: the new token is already the last
  * key of its sequence (position kv_len - 1), so its local block is the last.
@@ -251,7 +276,7 @@ msa_status_t msa_plan_info(msa_plan_t plan, int64_t* total_rows, int32_t* nb_max
 
 /* Diagnostics, not part of the path.  When `kernel` names one of the
  * library's internal kernels ("proxy_maxscore", "topk_select", "proxy_topk", "csr",
- * "partial_attn", "merge", "decode", "decode_merge"), each later launch of it
+ * "partial_attn", "merge", "decode", "decode_merge", "bwd_dq", "bwd_dq_sum", "bwd_dkv"), each later launch of it
  * for this plan carries two HIP events that the runtime stamps with the
  * dispatch's begin and end (events are created on first use and reused; no
  * device memory).  NULL
