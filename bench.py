@@ -38,6 +38,7 @@ PEAK_FP4_TFLOPS = 10100.0
 PROXY_PEAK = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "mxfp4": PEAK_FP8_TFLOPS, "mxfp4_qk": PEAK_FP4_TFLOPS}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
+    "bwd_dq": "sparse_prefill.hip", "bwd_dkv": "sparse_prefill.hip", "bwd_dq_sum": "sparse_prefill.hip",
     "proxy_maxscore": "proxy_maxscore.hip", "topk_select": "topk_select.hip", "proxy_topk": "proxy_maxscore.hip",
     "csr": "sparse_prefill.hip",
     "partial_attn": "sparse_prefill.hip", "merge": "sparse_prefill.hip", "decode": "sparse_decode.hip",
@@ -361,6 +362,60 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
     return res, (w, inp, sel)
 
 
+def backward_bench(msa, n_cfg, steps, warmup):
+    """The training backward of the sparse prefill attention on one workload:
+    the forward runs once (selection, output, lse), then each step is
+    msa_sparse_attn_prefill_backward with a fixed upstream gradient."""
+    import torch
+    from synthetic.gen import workload, seed_of
+    from synthetic.device_gen import make_inputs_device
+    w = workload(n_cfg)
+    inp = make_inputs_device(w, seed_of(n_cfg))
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                        w.num_proxy_kv_heads, topk=w.topk, proxy_dtype=w.proxy_dtype)
+    T, Hq, Hkv = w.total_rows, w.num_qo_heads, w.num_kv_heads
+    sel = torch.empty((T, Hkv, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    msa.run_prefill(plan, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale, inp.q, inp.k_pages,
+                    inp.v_pages, inp.kv_indices, sel, out, lse)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed_of(n_cfg) + 77)
+    dout = torch.randn((T, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    dq = torch.empty((T, Hq, 128), dtype=torch.float32, device="cuda")
+    dk = torch.empty((inp.k_pages.shape[0], Hkv, 128, 128), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+
+    def step():
+        msa.msa_sparse_attn_prefill_backward(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, lse,
+                                             dout, dq, dk, dv)
+
+    step()
+    torch.cuda.synchronize()
+    stages = ["csr", "bwd_dq", "bwd_dq_sum", "bwd_dkv"]
+    per_kernel = kernel_profile(msa, plan, step, stages)
+    dominant = max(("bwd_dq", "bwd_dkv"), key=lambda n: per_kernel[n][0])
+    ms_step, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, dominant)
+    nvis = visible_keys_per_row(sel, w.qo_lens, w.kv_lens, "cuda")
+    G = Hq // Hkv
+    pairs = float(nvis.sum().item()) * G          # (selected visible key, query head) pairs
+    # algorithmic products, 2*128 FLOP per pair each: S, dP, dQ in bwd_dq; dV, dK in bwd_dkv
+    # (bwd_dkv's own recomputation of S and dP is not counted)
+    f_total = 5 * 2 * 128 * pairs
+    work = (3 if dominant == "bwd_dq" else 2) * 2 * 128 * pairs / (launches // steps)
+    achieved = work / (k_ms * 1e-3) / 1e12
+    roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_from_profiles(dominant, w.name),
+            "avg_launch_ms": k_ms, "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "FLOP"}
+    return {
+        "workload": w.name + "_backward", "tok_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
+        "tflops": f_total / (ms_step * 1e-3) / 1e12, "stage_ms": {n: v[0] for n, v in per_kernel.items()},
+        "roofline": roof,
+        "config": {"workload": w.name + "_backward", "total_rows": T, "num_qo_heads": Hq, "num_kv_heads": Hkv,
+                   "topk": w.topk, "head_dim": 128, "kv_dtype": "bf16", "grads": "dq, dk, dv (fp32)"},
+    }
+
+
 def decode_bench(msa, steps, warmup, sets=4):
     import torch
     from synthetic.gen import workload, seed_of, decode_picks
@@ -503,10 +558,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode entries")
-    ap.add_argument("--extra", default="prefill_128k,prefill_32k_mxfp4,decode_131k,decode_step_131k,"
-                                       "decode_step_mxfp4_131k",
-                    help="comma-separated extra entries: prefill_128k, prefill_32k_mxfp4, decode_131k, "
-                         "decode_step_131k, decode_step_mxfp4_131k (or none)")
+    ap.add_argument("--extra", default="prefill_128k,prefill_32k_mxfp4,prefill_32k_backward,decode_131k,"
+                                       "decode_step_131k,decode_step_mxfp4_131k",
+                    help="comma-separated extra entries: prefill_128k, prefill_32k_mxfp4, prefill_32k_backward, "
+                         "decode_131k, decode_step_131k, decode_step_mxfp4_131k (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -532,7 +587,8 @@ def main():
     torch.cuda.set_device(0)
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
-        if e not in ("prefill_128k", "prefill_32k_mxfp4", "decode_131k", "decode_step_131k", "decode_step_mxfp4_131k"):
+        if e not in ("prefill_128k", "prefill_32k_mxfp4", "prefill_32k_backward", "decode_131k", "decode_step_131k",
+                     "decode_step_mxfp4_131k"):
             ap.error(f"unknown extra entry {e}")
     if args.copy_calibration:
         print("[bench] calibration copy", file=sys.stderr, flush=True)
@@ -548,6 +604,9 @@ def main():
         print("[bench] prefill 32k, MXFP4 proxy q and K, MXFP4 K/V", file=sys.stderr, flush=True)
         r8, _ = prefill_bench(msa, 8, args.steps, args.warmup)
         extra["prefill_32k_mxfp4"] = r8
+    if "prefill_32k_backward" in extras:
+        print("[bench] prefill 32k backward", file=sys.stderr, flush=True)
+        extra["prefill_32k_backward"] = backward_bench(msa, 2, args.steps, args.warmup)
     if "decode_131k" in extras:
         print("[bench] decode 131k fp8", file=sys.stderr, flush=True)
         extra["decode_131k"] = decode_bench(msa, max(50, args.steps * 10), 10)

@@ -363,7 +363,7 @@ def sparse_attention(q, k_pages, v_pages, kv_indices, kv_block_indexes, qo_lens,
 
 
 def sparse_attention_backward(q, k_pages, v_pages, kv_indices, kv_block_indexes, qo_lens, kv_lens, page_size, sm_scale,
-                              dout):
+                              dout, rows=None, groups=None):
     """Gradients of the block-sparse attention above ([FLASH] the training
     kernels: the selection is computed once in the forward pass and reused,
     so the backward runs over the same cached blocks) for bf16 q, K, V and an
@@ -379,7 +379,10 @@ def sparse_attention_backward(q, k_pages, v_pages, kv_indices, kv_block_indexes,
     dk and dv are accumulated per (page, KV head, slot) of the paged pools.
 
     Returns (dq float64 [T, H_q, d], dk float64, dv float64 shaped like the
-    page pools); pool slots no row attends to stay 0.
+    page pools); pool slots no row attends to stay 0.  With `rows`, only those
+    rows are visited: their dq rows are exact, dk and dv then hold only their
+    contributions.  With `groups`, only those KV groups (and their G query
+    heads) are visited; the other heads' dq and the other groups' dk, dv stay 0.
     """
     lay = Layout(qo_lens, kv_lens, page_size)
     T, Hq, d = q.shape
@@ -390,13 +393,13 @@ def sparse_attention_backward(q, k_pages, v_pages, kv_indices, kv_block_indexes,
     dk = np.zeros(k_pages.shape[:2] + (B, d))
     dv = np.zeros(v_pages.shape[:2] + (B, d))
     kvi = np.asarray(kv_indices, dtype=np.int64)
-    for r in range(T):
+    for r in (range(T) if rows is None else [int(x) for x in rows]):
         s = lay.seq_of_row(r)
         pos = lay.pos(r)
         L = lay.kv[s]
         qv = bf16_to_f64(q[r])
         dov = bf16_to_f64(dout[r])
-        for g in range(Hkv):
+        for g in (range(Hkv) if groups is None else [int(x) for x in groups]):
             blocks = sorted(set(int(b) for b in kv_block_indexes[r, g] if b >= 0))
             keys = np.concatenate([np.arange(b * B, (b + 1) * B) for b in blocks]) if blocks else np.zeros(0, np.int64)
             keys = keys[(keys <= pos) & (keys < L)]

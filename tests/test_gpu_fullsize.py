@@ -99,6 +99,70 @@ def _prefill_case(n_cfg, n_even):
     assert np.abs(glse - ref_lse).max() < 1e-3, w.name
 
 
+def _backward_case(n_cfg, n_even):
+    """The training backward at full size, in the launch configuration the
+    benchmark times: dq on sampled rows against the oracle; dk and dv of two
+    (group, block) pairs exactly (the oracle visits every row that selected
+    the block); and over every sequence and group the identity
+    sum_j dv_j = sum of that group's dout rows (each row's P sums to 1)."""
+    from block_sparse_top_amd import msa
+    w = workload(n_cfg)
+    print(f"[fullsize] backward workload={w.name}", flush=True)
+    inp = make_inputs_device(w, seed_of(n_cfg))
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                        w.num_proxy_kv_heads, topk=w.topk, proxy_dtype=w.proxy_dtype)
+    T, Hq, Hkv = w.total_rows, w.num_qo_heads, w.num_kv_heads
+    sel = torch.empty((T, Hkv, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    msa.run_prefill(plan, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale, inp.q, inp.k_pages,
+                    inp.v_pages, inp.kv_indices, sel, out, lse)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed_of(n_cfg) + 77)
+    dout = torch.randn((T, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    dq = torch.empty((T, Hq, 128), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((inp.k_pages.shape[0], Hkv, 128, 128), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    msa.msa_sparse_attn_prefill_backward(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, lse, dout,
+                                         dq, dk, dv)
+    torch.cuda.synchronize()
+    from tests.test_gpu_backward import _check
+    h = {k: to_host(getattr(inp, k)) for k in ("q", "k_pages", "v_pages", "kv_indices")}
+    gsel = sel.cpu().numpy()
+    dob = to_host(dout)
+    rows = _sample_rows(w, n_even, seed_of(n_cfg))
+    print(f"[fullsize] oracle dq on {rows.size} rows", flush=True)
+    rq, _, _ = O.sparse_attention_backward(h["q"], h["k_pages"], h["v_pages"], h["kv_indices"], gsel, w.qo_lens,
+                                           w.kv_lens, 128, w.sm_scale, dob, rows=rows)
+    _check(f"{w.name} dq (sampled rows)", dq[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64), rq[rows])
+    lay = O.Layout(w.qo_lens, w.kv_lens, 128)
+    rng = np.random.default_rng(seed_of(n_cfg))
+    # late blocks of the first sequence: few rows select them, so the oracle stays cheap
+    nb0 = lay.nb[0]
+    for gg, b in ((0, nb0 - 2), (int(rng.integers(Hkv)), int(rng.integers(nb0 - 12, nb0 - 2)))):
+        sel_rows = np.nonzero((gsel[:, gg, :] == b).any(axis=1) & (np.arange(T) < lay.row_start[1]))[0]
+        print(f"[fullsize] oracle dk, dv of group {gg} block {b}: {sel_rows.size} rows", flush=True)
+        _, rk, rv = O.sparse_attention_backward(h["q"], h["k_pages"], h["v_pages"], h["kv_indices"], gsel, w.qo_lens,
+                                                w.kv_lens, 128, w.sm_scale, dob, rows=sel_rows, groups=[gg])
+        page = int(h["kv_indices"][lay.page_start[0] + b])
+        _check(f"{w.name} dk (group {gg}, block {b})", dk[page, gg].cpu().numpy().astype(np.float64), rk[page, gg])
+        _check(f"{w.name} dv (group {gg}, block {b})", dv[page, gg].cpu().numpy().astype(np.float64), rv[page, gg])
+    G = Hq // Hkv
+    kvi = torch.from_numpy(h["kv_indices"].astype(np.int64)).cuda()
+    for si in range(len(w.kv_lens)):
+        pages = kvi[int(lay.page_start[si]):int(lay.page_start[si + 1])]
+        r0, r1 = int(lay.row_start[si]), int(lay.row_start[si + 1])
+        for gg in range(Hkv):
+            got = dv[pages, gg].double().sum(dim=(0, 1))
+            ref = dout[r0:r1, gg * G:(gg + 1) * G].double().sum(dim=(0, 1))
+            scale = dout[r0:r1, gg * G:(gg + 1) * G].double().abs().sum(dim=(0, 1))
+            assert ((got - ref).abs() <= 2.0 ** -7 * scale + 1e-6).all(), (si, gg)
+
+
+def test_prefill_32k_backward():
+    _backward_case(2, 48)
+
+
 def test_prefill_32k_sampled_rows():
     _prefill_case(2, 48)
 

@@ -109,3 +109,24 @@ def test_backward_closed_forms():
     do = (dout.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
     assert np.allclose(dv[kvi[0], 0, 0], do[0, 0] + do[0, 1])
+
+
+def test_backward_row_and_group_restrictions_are_sums_of_parts():
+    """Visiting a subset of rows or groups only drops the other terms: the
+    restricted results add up to the unrestricted ones."""
+    B = 16
+    qo, kv = [20, 33], [50, 33]
+    q, kp, vp, kvi, sel, dout, lay = _case(11, qo, kv, 4, 2, 3, B)
+    full = sparse_attention_backward(q, kp, vp, kvi, sel, qo, kv, B, 0.3, dout)
+    T = sum(qo)
+    half = np.arange(0, T, 2)
+    rest = np.arange(1, T, 2)
+    a = sparse_attention_backward(q, kp, vp, kvi, sel, qo, kv, B, 0.3, dout, rows=half)
+    b = sparse_attention_backward(q, kp, vp, kvi, sel, qo, kv, B, 0.3, dout, rows=rest)
+    g0 = sparse_attention_backward(q, kp, vp, kvi, sel, qo, kv, B, 0.3, dout, groups=[0])
+    g1 = sparse_attention_backward(q, kp, vp, kvi, sel, qo, kv, B, 0.3, dout, groups=[1])
+    for i in range(3):
+        assert np.allclose(a[i] + b[i], full[i], atol=1e-12)
+        assert np.allclose(g0[i] + g1[i], full[i], atol=1e-12)
+    assert np.abs(g0[0][:, 2:]).max() == 0 and np.abs(g0[1][:, 1]).max() == 0
+    assert np.array_equal(a[0][half], full[0][half]) and np.abs(a[0][rest]).max() == 0
