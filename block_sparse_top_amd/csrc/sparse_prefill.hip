@@ -878,15 +878,21 @@ struct BwdKvArgs {
   float scale_log2, sm_scale;
 };
 
+// A workgroup barrier that waits only for this wave's LDS traffic, so global
+// loads issued before it (the next chunk's rows) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz
-  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, k_swz
-  __shared__ __attribute__((aligned(16))) uint8_t qt[32 * 256];    // the chunk's 32 q rows, v_swz
-  __shared__ __attribute__((aligned(16))) uint8_t dtile[32 * 256]; // the chunk's 32 dO rows, v_swz
-  __shared__ float l2_s[32], d_s[32];
-  __shared__ int32_t pos_s[32];
-  const int key = blockIdx.x;
-  const int g = key / a.NB, gb = key % a.NB;
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];      // K, k_swz
+  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];      // V, k_swz
+  __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];    // a chunk's 32 q rows, v_swz, two buffers
+  __shared__ __attribute__((aligned(16))) uint8_t dtile[2][32 * 256]; // a chunk's 32 dO rows, v_swz
+  __shared__ __attribute__((aligned(16))) float l2_s[2][32];
+  __shared__ __attribute__((aligned(16))) float d_s[2][32];
+  __shared__ __attribute__((aligned(16))) int32_t pos_s[2][32];
+  // block-major order: the early, most selected blocks of every group start first
+  const int gb = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
+  const int key = g * a.NB + gb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = upper_bound_i32(a.m.page_start, a.m.S + 1, gb) - 1;
   const int b = gb - a.m.page_start[s];
@@ -921,74 +927,120 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
   f32x16 dkacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   f32x16 dvacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    __syncthreads();  // K/V staged (first chunk); the previous chunk's tiles are no longer read
-    for (int x = tid; x < 32 * 16; x += 256) {   // gather the chunk's rows: row i = token (i / G), head (i % G)
-      const int ri = x >> 4, c = x & 15;
-      const int e = min(chunk * MT + ri / G, n_ent - 1);
-      const int32_t r = a.w0 + (a.entries[e0 + e] >> 6);
-      const int64_t off = ((int64_t)r * a.Hq + g * G + ri % G) * 256 + c * 16;
-      lds_store16<i32x4>(&qt[v_swz(ri, c)], *reinterpret_cast<const i32x4*>(a.q + off));
-      lds_store16<i32x4>(&dtile[v_swz(ri, c)], *reinterpret_cast<const i32x4*>(a.dout + off));
-    }
+  // Gather slots of this thread: rows ri0 and ri0 + 16 of a chunk (row i =
+  // token i / G, head i % G), 16-byte column cc; threads below 32 also fetch
+  // row tid's lse, D and position.  Rows of chunk c + 1 are loaded into
+  // registers while chunk c computes; their entry ids one chunk earlier.
+  const int ri0 = tid >> 4, cc = tid & 15;
+  const int ri1 = ri0 + 16;
+  // entries and lse stay raw in registers until used, so that no wait for a
+  // just-issued load lands before the barrier
+  auto entry_of = [&](int chunk, int ri) { return a.entries[e0 + min(chunk * MT + ri / G, n_ent - 1)]; };
+  auto row_ptr = [&](const uint8_t* base, int32_t ent, int ri) {
+    return reinterpret_cast<const i32x4*>(base + ((int64_t)(a.w0 + (ent >> 6)) * a.Hq + g * G + ri % G) * 256 +
+                                          cc * 16);
+  };
+  if (nchunks > 0) {
+    int32_t ea = entry_of(0, ri0), eb = entry_of(0, ri1), es = tid < 32 ? entry_of(0, tid) : 0;
+    i32x4 rq0 = *row_ptr(a.q, ea, ri0), rq1 = *row_ptr(a.q, eb, ri1);
+    i32x4 rd0 = *row_ptr(a.dout, ea, ri0), rd1 = *row_ptr(a.dout, eb, ri1);
+    float rlse = 0.f, rdd = 0.f;
+    int32_t rpos = 0;
     if (tid < 32) {
-      const int ri = tid;
-      const int ee = chunk * MT + ri / G;
-      const int e = min(ee, n_ent - 1);
-      const int rl = a.entries[e0 + e] >> 6;
-      const int32_t r = a.w0 + rl;
-      const int h = g * G + ri % G;
-      l2_s[ri] = a.lse[(int64_t)r * a.Hq + h] * kLog2e;
-      d_s[ri] = a.D[(int64_t)rl * a.Hq + h];
-      pos_s[ri] = ee < n_ent ? first_pos + (r - rs) : -1;   // padding rows see no key
+      const int h = g * G + tid % G;
+      rlse = a.lse[(int64_t)(a.w0 + (es >> 6)) * a.Hq + h];
+      rdd = a.D[(int64_t)(es >> 6) * a.Hq + h];
+      rpos = tid / G < n_ent ? first_pos + (a.w0 + (es >> 6) - rs) : -1;   // padding rows see no key
     }
-    __syncthreads();
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys: C[row][key], key on lanes
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const bf16x8 aq = lds_load16<bf16x8>(&qt[v_swz(j, 2 * st + half)]);
-      const bf16x8 bk = lds_load16<bf16x8>(&ks[k_swz(32 * wave + j, 2 * st + half)]);
-      sacc = mfma32x32x16(aq, bk, sacc);
-      const bf16x8 ad = lds_load16<bf16x8>(&dtile[v_swz(j, 2 * st + half)]);
-      const bf16x8 bv = lds_load16<bf16x8>(&vs[k_swz(32 * wave + j, 2 * st + half)]);
-      pacc = mfma32x32x16(ad, bv, pacc);
-    }
-    // P and dS (register r holds row 8(r/4) + 4 half + r%4), as bf16 A operands
-    bf16x8 pf[2], sf[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      i32x4 pw, sw;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float pv[2], sv[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int rr = 8 * u + 2 * t + x;
-          const int row = 8 * (rr >> 2) + 4 * half + (rr & 3);
-          const float p = keypos <= pos_s[row] ? fast_exp2(__builtin_fmaf(sacc[rr], a.scale_log2, -l2_s[row])) : 0.f;
-          pv[x] = p;
-          sv[x] = p * (pacc[rr] - d_s[row]);
-        }
-        const bf16x2 p2 = {(__bf16)pv[0], (__bf16)pv[1]};
-        const bf16x2 s2 = {(__bf16)sv[0], (__bf16)sv[1]};
-        pw[t] = __builtin_bit_cast(int, p2);
-        sw[t] = __builtin_bit_cast(int, s2);
+    ea = entry_of(1, ri0);
+    eb = entry_of(1, ri1);
+    es = tid < 32 ? entry_of(1, tid) : 0;
+    for (int chunk = 0; chunk < nchunks; ++chunk) {
+      const int buf = chunk & 1;
+      lds_store16<i32x4>(&qt[buf][v_swz(ri0, cc)], rq0);
+      lds_store16<i32x4>(&qt[buf][v_swz(ri1, cc)], rq1);
+      lds_store16<i32x4>(&dtile[buf][v_swz(ri0, cc)], rd0);
+      lds_store16<i32x4>(&dtile[buf][v_swz(ri1, cc)], rd1);
+      if (tid < 32) {
+        l2_s[buf][tid] = rlse * kLog2e;
+        d_s[buf][tid] = rdd;
+        pos_s[buf][tid] = rpos;
       }
-      pf[u] = __builtin_bit_cast(bf16x8, pw);
-      sf[u] = __builtin_bit_cast(bf16x8, sw);
-    }
-    // dV += P^T dO, dK += dS^T Q: dO and Q read transposed, rows in the same order
+      // prefetch chunk + 1 (clamped past the end), then the entry ids of chunk + 2
+      rq0 = *row_ptr(a.q, ea, ri0);
+      rq1 = *row_ptr(a.q, eb, ri1);
+      rd0 = *row_ptr(a.dout, ea, ri0);
+      rd1 = *row_ptr(a.dout, eb, ri1);
+      if (tid < 32) {
+        const int h = g * G + tid % G;
+        rlse = a.lse[(int64_t)(a.w0 + (es >> 6)) * a.Hq + h];
+        rdd = a.D[(int64_t)(es >> 6) * a.Hq + h];
+        rpos = (chunk + 1) * MT + tid / G < n_ent ? first_pos + (a.w0 + (es >> 6) - rs) : -1;
+      }
+      ea = entry_of(chunk + 2, ri0);
+      eb = entry_of(chunk + 2, ri1);
+      es = tid < 32 ? entry_of(chunk + 2, tid) : 0;
+      // the tiles of this chunk (and K/V, first chunk) are in LDS; every wave is
+      // done with chunk - 1, whose buffer chunk + 1 will overwrite
+      lds_barrier();
+      const uint8_t* qb = qt[buf];
+      const uint8_t* db = dtile[buf];
+      // S = Q K^T and dP = dO V^T for this wave's 32 keys: C[row][key], key on lanes
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+      for (int st = 0; st < 8; ++st) {
+        const bf16x8 aq = lds_load16<bf16x8>(&qb[v_swz(j, 2 * st + half)]);
+        const bf16x8 bk = lds_load16<bf16x8>(&ks[k_swz(32 * wave + j, 2 * st + half)]);
+        sacc = mfma32x32x16(aq, bk, sacc);
+        const bf16x8 ad = lds_load16<bf16x8>(&db[v_swz(j, 2 * st + half)]);
+        const bf16x8 bv = lds_load16<bf16x8>(&vs[k_swz(32 * wave + j, 2 * st + half)]);
+        pacc = mfma32x32x16(ad, bv, pacc);
+      }
+      // P and dS (register r holds row 8(r/4) + 4 half + r%4), as bf16 A operands;
+      // the rows' lse, D and positions come as four 4-row runs
+      f32x4 l2v[4], dv4[4];
+      i32x4 ps4[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const s16x4 dlo = lds_read_tr16(&dtile[vbase[dt] + 256 * (16 * u)]);
-        const s16x4 dhi = lds_read_tr16(&dtile[vbase[dt] + 256 * (16 * u + 8)]);
-        dvacc[dt] = mfma32x32x16(pf[u], join_tr16(dlo, dhi), dvacc[dt]);
-        const s16x4 qlo = lds_read_tr16(&qt[vbase[dt] + 256 * (16 * u)]);
-        const s16x4 qhi = lds_read_tr16(&qt[vbase[dt] + 256 * (16 * u + 8)]);
-        dkacc[dt] = mfma32x32x16(sf[u], join_tr16(qlo, qhi), dkacc[dt]);
+      for (int t4 = 0; t4 < 4; ++t4) {
+        l2v[t4] = *reinterpret_cast<const f32x4*>(&l2_s[buf][8 * t4 + 4 * half]);
+        dv4[t4] = *reinterpret_cast<const f32x4*>(&d_s[buf][8 * t4 + 4 * half]);
+        ps4[t4] = *reinterpret_cast<const i32x4*>(&pos_s[buf][8 * t4 + 4 * half]);
+      }
+      bf16x8 pf[2], sf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        i32x4 pw, sw;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float pv[2], sv[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int rr = 8 * u + 2 * t + x;
+            const float ex = fast_exp2(__builtin_fmaf(sacc[rr], a.scale_log2, -l2v[rr >> 2][rr & 3]));
+            const float p = keypos <= ps4[rr >> 2][rr & 3] ? ex : 0.f;
+            pv[x] = p;
+            sv[x] = p * (pacc[rr] - dv4[rr >> 2][rr & 3]);
+          }
+          const bf16x2 p2 = {(__bf16)pv[0], (__bf16)pv[1]};
+          const bf16x2 s2 = {(__bf16)sv[0], (__bf16)sv[1]};
+          pw[t] = __builtin_bit_cast(int, p2);
+          sw[t] = __builtin_bit_cast(int, s2);
+        }
+        pf[u] = __builtin_bit_cast(bf16x8, pw);
+        sf[u] = __builtin_bit_cast(bf16x8, sw);
+      }
+      // dV += P^T dO, dK += dS^T Q: dO and Q read transposed, rows in the same order
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const s16x4 dlo = lds_read_tr16(&db[vbase[dt] + 256 * (16 * u)]);
+          const s16x4 dhi = lds_read_tr16(&db[vbase[dt] + 256 * (16 * u + 8)]);
+          dvacc[dt] = mfma32x32x16(pf[u], join_tr16(dlo, dhi), dvacc[dt]);
+          const s16x4 qlo = lds_read_tr16(&qb[vbase[dt] + 256 * (16 * u)]);
+          const s16x4 qhi = lds_read_tr16(&qb[vbase[dt] + 256 * (16 * u + 8)]);
+          dkacc[dt] = mfma32x32x16(sf[u], join_tr16(qlo, qhi), dkacc[dt]);
+        }
       }
     }
   }
@@ -1079,7 +1131,7 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   kv.sm_scale = a.sm_scale;
   {
     ProfEvents pe(p, "bwd_dkv");
-    hipExtLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)nkey), dim3(256), 0, st, pe.start, pe.stop, 0, kv);
+    hipExtLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)nkey), dim3(256), 0, st, pe.start, pe.stop, 0, kv);  // NB x Hkv
   }
   return hipGetLastError();
 }
