@@ -420,6 +420,74 @@ def sparse_attention_backward(q, k_pages, v_pages, kv_indices, kv_block_indexes,
     return dq, dk, dv
 
 
+def proxy_kl_backward(proxy_q, proxy_k_pages, q, k_pages, kv_indices, kv_block_indexes, qo_lens, kv_lens, page_size,
+                      sm_scale, proxy_sm_scale, grad_scale=1.0, rows=None, groups=None):
+    """Gradient of the proxy's distillation loss with respect to the bf16
+    proxy q and proxy K ([FLASH] the backward paragraph: the KL divergence
+    between the proxy's and the main attention's distributions, whose gradient
+    with respect to a proxy score is the proxy probability minus the main
+    probability).
+
+    Readings where the pages are silent: for row r and group g (driven by
+    proxy head g, as in the forward)
+      p_proxy_j = softmax over the row's visible keys j (j <= pos, j < kv_len)
+                  of z_j = proxy_sm_scale <pq[r, g], pk[j, g]>   (dense proxy)
+      p_main_j  = mean over the group's G heads h of the main attention
+                  probability softmax_j(sm_scale <q[r, h], k[j, g]>) over the
+                  selected visible keys K(r, g), and 0 on every other key
+      loss      = grad_scale * sum over (r, g) of KL(p_main || p_proxy),
+    with p_main a fixed target (no gradient flows into the main attention).
+    Then dloss/dz_j = grad_scale (p_proxy_j - p_main_j) and
+      dpq[r, g]  = proxy_sm_scale sum_j dz_j pk[j, g]
+      dpk[j, g] += proxy_sm_scale dz_j pq[r, g].
+
+    Needs one proxy head and one proxy-K head per KV group.  Returns (dpq
+    float64 [T, P, d], dpk float64 shaped like the proxy pool, kl float64 [T, P]
+    (each (row, group)'s KL, without grad_scale)).  `rows` and `groups` visit
+    a subset as in sparse_attention_backward.
+    """
+    lay = Layout(qo_lens, kv_lens, page_size)
+    T, Hq, d = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    P, Pk = proxy_q.shape[1], proxy_k_pages.shape[1]
+    if P != Hkv or Pk != P:
+        raise ValueError("one proxy head and one proxy-K head per KV group")
+    B = lay.B
+    dpq = np.zeros((T, P, d))
+    dpk = np.zeros(proxy_k_pages.shape[:2] + (B, d))
+    kl = np.zeros((T, P))
+    kvi = np.asarray(kv_indices, dtype=np.int64)
+    for r in (range(T) if rows is None else [int(x) for x in rows]):
+        s = lay.seq_of_row(r)
+        pos = lay.pos(r)
+        L = lay.kv[s]
+        vis = np.arange(min(pos + 1, L))                      # the row's visible keys
+        pages = kvi[lay.page_start[s] + vis // B]
+        slots = vis % B
+        qv = bf16_to_f64(q[r])
+        for g in (range(Hkv) if groups is None else [int(x) for x in groups]):
+            pq = bf16_to_f64(proxy_q[r, g])
+            PK = gather_rows(proxy_k_pages, BF16, None, kv_indices, lay, s, g, vis)
+            z = proxy_sm_scale * (PK @ pq)
+            logpp = z - z.max() - np.log(np.sum(np.exp(z - z.max())))
+            pp = np.exp(logpp)
+            blocks = set(int(b) for b in kv_block_indexes[r, g] if b >= 0)
+            chosen = np.array([int(j) // B in blocks for j in vis], dtype=bool)
+            K = gather_rows(k_pages, BF16, None, kv_indices, lay, s, g, vis[chosen])
+            pm = np.zeros(vis.size)
+            for h in range(g * G, (g + 1) * G):
+                sc = sm_scale * (K @ qv[h])
+                w = np.exp(sc - sc.max())
+                pm[chosen] += w / w.sum() / G
+            dz = grad_scale * (pp - pm)
+            dpq[r, g] = proxy_sm_scale * (dz @ PK)
+            np.add.at(dpk, (pages, g, slots), proxy_sm_scale * dz[:, None] * pq[None, :])
+            on = pm > 0
+            kl[r, g] = float(np.sum(pm[on] * (np.log(pm[on]) - logpp[on])))
+    return dpq, dpk, kl
+
+
 def sparse_decode(q, k_pages, v_pages, kv_indices, kv_block_indexes, kv_lens, page_size, sm_scale,
                   kv_dtype=FP8, k_scale=None, v_scale=None, rows=None):
     """Paged sparse decode ([README] "Stacks": paged FP8 decode wrapper): one
