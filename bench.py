@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "partial_attn": "sparse_prefill.hip", "merge": "sparse_prefill.hip", "decode": "sparse_decode.hip",
     "decode_merge": "sparse_decode.hip", "proxy_onerow": "proxy_maxscore.hip",
     "proxy_onerow_mxfp4": "proxy_maxscore.hip", "topk_wave": "topk_select.hip",
+    "kl_dq_sum": "sparse_prefill.hip", "kl_dense_dq": "proxy_kl.hip", "kl_dense_dk": "proxy_kl.hip",
 }
 
 
@@ -167,6 +168,8 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
     # partial_attn dispatches -> workload: the prefill workloads run one after
     # another, so each run of partial_attn dispatches with one grid is the
     # next prefill workload in bench order
+    # (a training backward between two forwards also starts a new run)
+    backward = lambda k: k.startswith(("bwd_", "kl_"))
     pa_label = {}
     run, prev = -1, None
     for i, (k, grid, _) in enumerate(rows):
@@ -175,12 +178,20 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
                 run += 1
                 prev = grid
             pa_label[i] = prefill_names[run] if run < len(prefill_names) else f"prefill grid {grid}"
+        elif backward(k):
+            prev = None
+    # a dispatch belongs to a backward step when the next partial_attn or
+    # backward kernel after it is a backward kernel (its CSR build included)
     section = [None] * len(rows)
-    nxt = None
+    in_bwd = [False] * len(rows)
+    nxt, nxt_bwd = None, False
     for i in range(len(rows) - 1, -1, -1):
         if rows[i][0] == "partial_attn":
-            nxt = pa_label[i]
+            nxt, nxt_bwd = pa_label[i], False
+        elif backward(rows[i][0]):
+            nxt_bwd = True
         section[i] = nxt
+        in_bwd[i] = nxt_bwd
     last = None
     step_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow"), len(rows))
     mx_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow_mxfp4"), len(rows))
@@ -191,7 +202,7 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
             section[i] = DECODE_STEP_WORKLOAD
         elif k.startswith("decode"):
             section[i] = SECTION_OF_KERNEL["decode"]
-        elif k == "merge" or section[i] is None:
+        elif k == "merge" or in_bwd[i] or section[i] is None:
             section[i] = last
         if k == "partial_attn":
             last = pa_label[i]
@@ -362,10 +373,12 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
     return res, (w, inp, sel)
 
 
-def backward_bench(msa, n_cfg, steps, warmup):
+def backward_bench(msa, n_cfg, steps, warmup, kl=False):
     """The training backward of the sparse prefill attention on one workload:
     the forward runs once (selection, output, lse), then each step is
-    msa_sparse_attn_prefill_backward with a fixed upstream gradient."""
+    msa_sparse_attn_prefill_backward with a fixed upstream gradient (with `kl`,
+    msa_sparse_attn_prefill_backward_kl: the same plus the gradient of the
+    proxy's distillation loss)."""
     import torch
     from synthetic.gen import workload, seed_of
     from synthetic.device_gen import make_inputs_device
@@ -385,34 +398,57 @@ def backward_bench(msa, n_cfg, steps, warmup):
     dq = torch.empty((T, Hq, 128), dtype=torch.float32, device="cuda")
     dk = torch.empty((inp.k_pages.shape[0], Hkv, 128, 128), dtype=torch.float32, device="cuda")
     dv = torch.empty_like(dk)
+    if kl:
+        dpq = torch.empty((T, Hkv, 128), dtype=torch.float32, device="cuda")
+        dpk = torch.empty_like(dk)
+        plse = torch.empty((T, Hkv), dtype=torch.float32, device="cuda")
 
     def step():
-        msa.msa_sparse_attn_prefill_backward(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, lse,
-                                             dout, dq, dk, dv)
+        if kl:
+            msa.msa_sparse_attn_prefill_backward_kl(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out,
+                                                    lse, dout, inp.proxy_q, inp.proxy_k_pages, 1.0, dq, dk, dv, dpq,
+                                                    dpk, plse)
+        else:
+            msa.msa_sparse_attn_prefill_backward(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out,
+                                                 lse, dout, dq, dk, dv)
 
     step()
     torch.cuda.synchronize()
     stages = ["csr", "bwd_dq", "bwd_dq_sum", "bwd_dkv"]
+    if kl:
+        stages += ["kl_dq_sum", "kl_dense_dq", "kl_dense_dk"]
     per_kernel = kernel_profile(msa, plan, step, stages)
-    dominant = max(("bwd_dq", "bwd_dkv"), key=lambda n: per_kernel[n][0])
+    heavy = ("bwd_dq", "bwd_dkv", "kl_dense_dq", "kl_dense_dk") if kl else ("bwd_dq", "bwd_dkv")
+    dominant = max(heavy, key=lambda n: per_kernel[n][0])
     ms_step, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, dominant)
     nvis = visible_keys_per_row(sel, w.qo_lens, w.kv_lens, "cuda")
     G = Hq // Hkv
     pairs = float(nvis.sum().item()) * G          # (selected visible key, query head) pairs
-    # algorithmic products, 2*128 FLOP per pair each: S, dP, dQ in bwd_dq; dV, dK in bwd_dkv
-    # (bwd_dkv's own recomputation of S and dP is not counted)
-    f_total = 5 * 2 * 128 * pairs
-    work = (3 if dominant == "bwd_dq" else 2) * 2 * 128 * pairs / (launches // steps)
+    dense = 0.0                                   # (visible key, proxy head) pairs of the dense proxy
+    for qo, kv in zip(w.qo_lens, w.kv_lens):
+        first = kv - qo
+        dense += (qo * (first + 1) + qo * (qo - 1) / 2) * Hkv
+    # algorithmic products, 2*128 FLOP per pair each: S, dP, dQ in bwd_dq; dV, dK in
+    # bwd_dkv (its recomputation of S and dP is not counted); with the proxy term
+    # one more sparse product in each, and S, dQ, dK over the dense proxy pairs
+    # (kl_dense_dq's first sweep, which only finds the log-sum-exp, is not counted)
+    per_kernel_products = {"bwd_dq": (3 + kl) * pairs, "bwd_dkv": (2 + kl) * pairs,
+                           "kl_dense_dq": 2 * dense, "kl_dense_dk": dense}
+    f_total = (5 + 2 * kl) * 2 * 128 * pairs + (3 * 2 * 128 * dense if kl else 0.0)
+    work = 2 * 128 * per_kernel_products[dominant] / (launches // steps)
     achieved = work / (k_ms * 1e-3) / 1e12
     roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_from_profiles(dominant, w.name),
             "avg_launch_ms": k_ms, "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "FLOP"}
+    name = w.name + ("_backward_kl" if kl else "_backward")
+    grads = "dq, dk, dv, dproxy_q, dproxy_k (fp32)" if kl else "dq, dk, dv (fp32)"
     return {
-        "workload": w.name + "_backward", "tok_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
+        "workload": name, "tok_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
         "tflops": f_total / (ms_step * 1e-3) / 1e12, "stage_ms": {n: v[0] for n, v in per_kernel.items()},
         "roofline": roof,
-        "config": {"workload": w.name + "_backward", "total_rows": T, "num_qo_heads": Hq, "num_kv_heads": Hkv,
-                   "topk": w.topk, "head_dim": 128, "kv_dtype": "bf16", "grads": "dq, dk, dv (fp32)"},
+        "config": {"workload": name, "total_rows": T, "num_qo_heads": Hq, "num_kv_heads": Hkv,
+                   "num_proxy_heads": w.num_proxy_heads, "topk": w.topk, "head_dim": 128, "kv_dtype": "bf16",
+                   "grads": grads},
     }
 
 
@@ -558,10 +594,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode entries")
-    ap.add_argument("--extra", default="prefill_128k,prefill_32k_mxfp4,prefill_32k_backward,decode_131k,"
-                                       "decode_step_131k,decode_step_mxfp4_131k",
+    ap.add_argument("--extra", default="prefill_128k,prefill_32k_mxfp4,prefill_32k_backward,prefill_32k_backward_kl,"
+                                       "decode_131k,decode_step_131k,decode_step_mxfp4_131k",
                     help="comma-separated extra entries: prefill_128k, prefill_32k_mxfp4, prefill_32k_backward, "
-                         "decode_131k, decode_step_131k, decode_step_mxfp4_131k (or none)")
+                         "prefill_32k_backward_kl, decode_131k, decode_step_131k, decode_step_mxfp4_131k (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -587,8 +623,8 @@ def main():
     torch.cuda.set_device(0)
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
-        if e not in ("prefill_128k", "prefill_32k_mxfp4", "prefill_32k_backward", "decode_131k", "decode_step_131k",
-                     "decode_step_mxfp4_131k"):
+        if e not in ("prefill_128k", "prefill_32k_mxfp4", "prefill_32k_backward", "prefill_32k_backward_kl",
+                     "decode_131k", "decode_step_131k", "decode_step_mxfp4_131k"):
             ap.error(f"unknown extra entry {e}")
     if args.copy_calibration:
         print("[bench] calibration copy", file=sys.stderr, flush=True)
@@ -607,6 +643,9 @@ def main():
     if "prefill_32k_backward" in extras:
         print("[bench] prefill 32k backward", file=sys.stderr, flush=True)
         extra["prefill_32k_backward"] = backward_bench(msa, 2, args.steps, args.warmup)
+    if "prefill_32k_backward_kl" in extras:
+        print("[bench] prefill 32k backward with the proxy distillation gradient", file=sys.stderr, flush=True)
+        extra["prefill_32k_backward_kl"] = backward_bench(msa, 2, args.steps, args.warmup, kl=True)
     if "decode_131k" in extras:
         print("[bench] decode 131k fp8", file=sys.stderr, flush=True)
         extra["decode_131k"] = decode_bench(msa, max(50, args.steps * 10), 10)

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -119,7 +120,7 @@ hipEvent_t take_event(msa::Profiler& pr) {
 }
 const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "proxy_topk", "csr",        "partial_attn",
                                     "merge",          "decode",      "decode_merge", "bwd_dq", "bwd_dq_sum",
-                                    "bwd_dkv"};
+                                    "bwd_dkv",        "kl_dq_sum",   "kl_dense_dq",  "kl_dense_dk"};
 }  // namespace
 
 ProfEvents::ProfEvents(const msa_plan_s* p, const char* name) {
@@ -309,6 +310,12 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     // one extra slot at index W * Hq * K takes the stores of padding rows
     L.part_o = off; off = align_up(off + (W * Hq * K + 1) * 128 * 2, 256);
     L.part_lse = off; off = align_up(off + (W * Hq * K + 1) * 4, 256);
+    // the fused backward's proxy distillation term needs one bf16 proxy head
+    // and proxy-K head per KV group: its per-(token, group, slot) partials
+    if (d.proxy_dtype == MSA_BF16 && d.num_proxy_heads == Hkv && d.num_proxy_kv_heads == Hkv) {
+      L.kl_part = off;
+      off = align_up(off + W * Hkv * K * 128 * 2, 256);
+    }
     // one query row per sequence (a decode step's indexer pass): the proxy
     // pass uses the one-row kernel, and the fused selection keeps its block
     // scores here
@@ -509,11 +516,61 @@ msa_status_t msa_sparse_attn_prefill_backward(msa_plan_t p, const void* q, const
   for (int64_t w0 = 0; w0 < p->T; w0 += p->attn_window) {
     const int32_t w1 = (int32_t)std::min<int64_t>(p->T, w0 + p->attn_window);
     hipError_t e = msa::launch_prefill_backward_window(p, m, q, k_pages, v_pages, kv_indices, kv_block_indexes, out,
-                                                       lse, dout, dq, dk_pages, dv_pages,
+                                                       lse, dout, dq, dk_pages, dv_pages, nullptr,
                                                        static_cast<char*>(workspace), (int32_t)w0, w1, w0 == 0, hs);
     if (e != hipSuccess) return hip_status(e, __func__);
   }
   return ok();
+}
+
+msa_status_t msa_sparse_attn_prefill_backward_kl(msa_plan_t p, const void* q, const void* k_pages,
+                                                 const void* v_pages, const int32_t* kv_indices,
+                                                 const int32_t* kv_block_indexes, const void* out, const float* lse,
+                                                 const void* dout, const void* proxy_q, const void* proxy_k_pages,
+                                                 float kl_grad_scale, float* dq, float* dk_pages, float* dv_pages,
+                                                 float* dproxy_q, float* dproxy_k_pages, float* proxy_lse,
+                                                 void* workspace, size_t workspace_bytes, msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill_backward_kl: NULL plan");
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_prefill_backward_kl: decode plan");
+  if (p->d.kv_dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_prefill_backward_kl: the backward is built for bf16 K/V");
+  if (p->lay.kl_part == 0)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "msa_sparse_attn_prefill_backward_kl: needs a bf16 proxy with one proxy head and one proxy-K head "
+                "per KV group");
+  if (!std::isfinite(kl_grad_scale))
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_prefill_backward_kl: kl_grad_scale is not finite");
+  MSA_CHECK_PTR(q);
+  MSA_CHECK_PTR(k_pages);
+  MSA_CHECK_PTR(v_pages);
+  MSA_CHECK_PTR(kv_indices);
+  MSA_CHECK_PTR(kv_block_indexes);
+  MSA_CHECK_PTR(out);
+  MSA_CHECK_PTR(lse);
+  MSA_CHECK_PTR(dout);
+  MSA_CHECK_PTR(proxy_q);
+  MSA_CHECK_PTR(proxy_k_pages);
+  MSA_CHECK_PTR(dq);
+  MSA_CHECK_PTR(dk_pages);
+  MSA_CHECK_PTR(dv_pages);
+  MSA_CHECK_PTR(dproxy_q);
+  MSA_CHECK_PTR(dproxy_k_pages);
+  MSA_CHECK_PTR(proxy_lse);
+  msa_status_t st = check_ws(p, workspace, workspace_bytes);
+  if (st != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  const msa::KlOperands kl{proxy_q, proxy_k_pages, dproxy_q, dproxy_k_pages, proxy_lse, p->d.proxy_sm_scale,
+                           kl_grad_scale};
+  for (int64_t w0 = 0; w0 < p->T; w0 += p->attn_window) {
+    const int32_t w1 = (int32_t)std::min<int64_t>(p->T, w0 + p->attn_window);
+    hipError_t e = msa::launch_prefill_backward_window(p, m, q, k_pages, v_pages, kv_indices, kv_block_indexes, out,
+                                                       lse, dout, dq, dk_pages, dv_pages, &kl,
+                                                       static_cast<char*>(workspace), (int32_t)w0, w1, w0 == 0, hs);
+    if (e != hipSuccess) return hip_status(e, __func__);
+  }
+  return hip_status(msa::launch_proxy_kl_dense(p, m, kv_indices, kl, hs), __func__);
 }
 
 msa_status_t msa_sparse_attn_decode(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,

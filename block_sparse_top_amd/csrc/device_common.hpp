@@ -148,6 +148,27 @@ __device__ __forceinline__ bf16x8 join_tr16(const s16x4& lo, const s16x4& hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// The value of another lane, chosen by the DPP control CTRL (quad
+// permutations, row mirrors) within each 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// K and V sit in LDS as unpadded 256-byte rows whose 16-byte chunks are
+// XOR-swizzled by row.  K: chunk c of row r at c ^ (r & 15), so each 16 lanes
+// of an MFMA operand read (16 rows, one column chunk) hit 16 distinct chunk
+// positions.  V: chunk c at c ^ 4 (r & 3), so the 8 rows x 4 chunks of a
+// transposed read cover every bank exactly twice.  The per-lane part of each
+// read address is computed once (8 K bases, one per 32-byte column step; 4 V
+// bases, one per 32-column tile) and the row offsets become immediates.
+__device__ __forceinline__ int k_swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int v_swz(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 2)) << 4); }
+
+// A workgroup barrier that waits only for this wave's LDS traffic, so global
+// loads issued before it (the next chunk's rows) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int32_t x) {
   // first index i in [0, n) with a[i] > x (a ascending)
   int lo = 0, hi = n;

@@ -34,6 +34,9 @@ struct PlanLayout {
   size_t meta = 0, meta_bytes = 0;
   // prefill window scratch
   size_t counts = 0, cursor = 0, offsets = 0, items = 0, nitems = 0, entries = 0, part_o = 0, part_lse = 0;
+  // per-(token, group, slot) partials of the proxy distillation term (plans
+  // with one bf16 proxy head and proxy-K head per KV group)
+  size_t kl_part = 0;
   int64_t max_items = 0;
   // decode split scratch
   size_t dec_o = 0, dec_ml = 0;
@@ -89,11 +92,25 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
                                  const void* vp, const float* ks, const float* vs, const int32_t* kv_indices,
                                  const int32_t* sel, void* out, float* lse, char* ws, int32_t w0, int32_t w1,
                                  hipStream_t st);
+// Proxy distillation operands of the fused backward (bf16 proxy q [T, Hkv,
+// 128] and proxy K pool, fp32 gradients); null in the main-only backward.
+struct KlOperands {
+  const void* pq;
+  const void* pkp;
+  float* dpq;      // [T, Hkv, 128]
+  float* dpk;      // [N, Hkv, 128, 128]
+  float* plse;     // [T, Hkv] proxy log-sum-exp (natural log), written
+  float proxy_scale, grad_scale;
+};
 hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
                                           const void* vp, const int32_t* kv_indices, const int32_t* sel,
                                           const void* out, const float* lse, const void* dout, float* dq, float* dk,
-                                          float* dv, char* ws, int32_t w0, int32_t w1, bool first_window,
-                                          hipStream_t st);
+                                          float* dv, const KlOperands* kl, char* ws, int32_t w0, int32_t w1,
+                                          bool first_window, hipStream_t st);
+// The dense proxy part of the distillation gradient, after every window of
+// the fused backward has stored its sparse part in dpq and dpk.
+hipError_t launch_proxy_kl_dense(const msa_plan_s* p, const DevMeta& m, const int32_t* kv_indices,
+                                 const KlOperands& kl, hipStream_t st);
 hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
                          const float* ks, const float* vs, const int32_t* kv_indices, const int32_t* sel,
                          void* out, float* lse, char* ws, hipStream_t st);

@@ -20,21 +20,14 @@
 //     (row, head, slot);
 //  3. merge: per (row, head) the slot partials are combined with their
 //     log-sum-exp weights into the final output and lse.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "msa_internal.hpp"
 
 namespace msa {
 namespace {
 
-// K and V sit in LDS as unpadded 256-byte rows whose 16-byte chunks are
-// XOR-swizzled by row.  K: chunk c of row r at c ^ (r & 15), so each 16 lanes
-// of an MFMA operand read (16 rows, one column chunk) hit 16 distinct chunk
-// positions.  V: chunk c at c ^ 4 (r & 3), so the 8 rows x 4 chunks of a
-// transposed read cover every bank exactly twice.  The per-lane part of each
-// read address is computed once (8 K bases, one per 32-byte column step; 4 V
-// bases, one per 32-column tile) and the row offsets become immediates.
-__device__ __forceinline__ int k_swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
-__device__ __forceinline__ int v_swz(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 2)) << 4); }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
@@ -486,8 +479,60 @@ namespace {
 
 // Invert kv_block_indexes for rows [w0, w1) into per-(group, block) entry
 // lists (counts, offsets, entries) and the capped work items.
+// Canonical order within each (group, block) bin: ascending window row (a row
+// enters a bin at most once).  The fill pass places entries in the order its
+// atomics land; the forward does not care (one partial per entry), but the
+// backward's dk/dv sum a bin's rows in entry order, and this order makes those
+// gradients bit-reproducible.  Per bin: the rows go into an LDS bitmap over the
+// window (their slots into a byte per row), a prefix of the words' popcounts
+// ranks them, and each entry is written back at its rank.  Dynamic LDS:
+// W / 8 bytes of bitmap, then W slot bytes.
+constexpr int kOrderThreads = 256;
+constexpr int kOrderMaxRows = 65536;    // windows up to this many rows are ordered
+__global__ __launch_bounds__(kOrderThreads) void csr_order_kernel(const int32_t* offsets, int32_t* entries,
+                                                                 int32_t W) {
+  extern __shared__ uint32_t bits[];
+  __shared__ int32_t wsum[kOrderThreads / 64];
+  uint8_t* slot_of = reinterpret_cast<uint8_t*>(bits + (W + 31) / 32);
+  const int32_t e0 = offsets[blockIdx.x], n = offsets[blockIdx.x + 1] - e0;
+  if (n <= 1) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (W + 31) / 32;
+  for (int i = tid; i < nw; i += kOrderThreads) bits[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += kOrderThreads) {
+    const int32_t e = entries[e0 + i];
+    atomicOr(&bits[(e >> 6) >> 5], 1u << ((e >> 6) & 31));
+    slot_of[e >> 6] = (uint8_t)(e & 63);
+  }
+  __syncthreads();
+  // thread t owns words [t * per, (t + 1) * per); exclusive prefix of their popcounts
+  const int per = (nw + kOrderThreads - 1) / kOrderThreads;
+  const int w_lo = min(nw, tid * per), w_hi = min(nw, w_lo + per);
+  int cnt = 0;
+  for (int w = w_lo; w < w_hi; ++w) cnt += __popc(bits[w]);
+  int incl = cnt;   // inclusive scan within the wave
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = incl - cnt;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  for (int w = w_lo; w < w_hi; ++w) {
+    uint32_t m = bits[w];
+    while (m) {
+      const int b = __ffs(m) - 1;
+      m &= m - 1;
+      const int32_t rl = 32 * w + b;
+      entries[e0 + base++] = (rl << 6) | slot_of[rl];
+    }
+  }
+}
+
 void build_csr(const msa_plan_s* p, const DevMeta& m, const int32_t* sel, char* ws, int32_t w0, int32_t w1,
-               hipStream_t st) {
+               hipStream_t st, bool sorted = false) {
   const PlanLayout& L = p->lay;
   const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
   const int32_t nkey = Hkv * p->NB;
@@ -521,8 +566,16 @@ void build_csr(const msa_plan_s* p, const DevMeta& m, const int32_t* sel, char* 
   else hipLaunchKernelGGL((csr_pass_kernel<false, false>), cgrid, dim3(256), 0, st, c);
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, counts, offsets, items, nitems, nkey,
                      p->NB, p->entries_per_item);
-  if (lds_hist) hipExtLaunchKernelGGL((csr_pass_kernel<true, true>), cgrid, dim3(256), hist_bytes, st, nullptr, pe.stop, 0, c);
-  else hipExtLaunchKernelGGL((csr_pass_kernel<true, false>), cgrid, dim3(256), 0, st, nullptr, pe.stop, 0, c);
+  const bool order = sorted && w1 - w0 <= kOrderMaxRows;   // longer windows keep the fill order
+  hipEvent_t fill_stop = order ? nullptr : pe.stop;
+  if (lds_hist) hipExtLaunchKernelGGL((csr_pass_kernel<true, true>), cgrid, dim3(256), hist_bytes, st, nullptr, fill_stop, 0, c);
+  else hipExtLaunchKernelGGL((csr_pass_kernel<true, false>), cgrid, dim3(256), 0, st, nullptr, fill_stop, 0, c);
+  if (order) {
+    const int32_t W = w1 - w0;
+    const size_t lds = (size_t)(W + 31) / 32 * 4 + (size_t)W;
+    hipExtLaunchKernelGGL(csr_order_kernel, dim3((unsigned)nkey), dim3(kOrderThreads), lds, st, nullptr, pe.stop, 0,
+                          offsets, entries, W);
+  }
   }
 
 }
@@ -660,12 +713,20 @@ struct BwdDqArgs {
   int64_t trash;
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2, sm_scale;
+  // proxy distillation term (KL kernels only): proxy K pool bf16 [N, Hkv,
+  // 128, 128] and per-(token, group, slot) partials bf16 [W, Hkv, k, 128] of
+  // (1/G) sum over the group's heads h of sum_j P_hj pk_j
+  const uint8_t* pkp;
+  uint16_t* klpart;
+  float inv_g;
 };
 
+template <bool KL>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz: S^T operand
   __shared__ __attribute__((aligned(16))) uint8_t kt[128 * 256];   // K, v_swz: transposed reads (K^T)
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, k_swz: dP^T operand
+  __shared__ __attribute__((aligned(16))) uint8_t pkt[KL ? 128 * 256 : 16];   // proxy K, v_swz
   __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
   __shared__ int32_t ent_s[kMaxItemEntries];
   const int item = blockIdx.x;
@@ -699,6 +760,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
       lds_store16<i32x4>(&kt[v_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
       lds_store16<i32x4>(&vs[k_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
     }
+    if constexpr (KL) {
+      const uint8_t* pb = a.pkp + ((int64_t)page * a.Hkv + g) * 32768;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kr[i] = *reinterpret_cast<const i32x4*>(pb + (tid + 256 * i) * 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = tid + 256 * i;
+        lds_store16<i32x4>(&pkt[v_swz(c >> 4, c & 15)], (c >> 4) < kv_in_block ? kr[i] : i32x4{});
+      }
+    }
   }
   __syncthreads();
 
@@ -720,59 +791,80 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
   uint8_t* ow = ost + wave * kOStage;
 
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    const int e = chunk * MT + tok;
-    const bool valid = e < n_ent;
-    const int ent = ent_s[valid ? e : n_ent - 1];   // padding rows repeat a real one; their output is discarded
-    const int rl = ent >> 6, slot = ent & 63;
-    const int32_t r = a.w0 + rl;
-    const int32_t pos = first_pos + (r - rs);
-    const float l2 = a.lse[(int64_t)r * a.Hq + h] * kLog2e;
-    const float dval = a.D[(int64_t)rl * a.Hq + h];
-    bf16x8 qf[8], df[8];
-    {
-      const uint8_t* qrow = a.q + ((int64_t)r * a.Hq + h) * 256 + half * 16;
-      const uint8_t* drow = a.dout + ((int64_t)r * a.Hq + h) * 256 + half * 16;
+  // The row of a chunk: padding rows (past the item's entries) repeat a real
+  // one; their output is discarded.  Each wave's rows come from global memory
+  // straight into registers: the next chunk's q rows are loaded once this
+  // chunk's S^T is issued, its dO rows once dP^T is, its lse and D early.
+  auto entry_at = [&](int chunk) { return ent_s[min(chunk * MT + tok, max(n_ent - 1, 0))]; };
+  auto q_ptr = [&](const uint8_t* base, int ent) {
+    return base + ((int64_t)(a.w0 + (ent >> 6)) * a.Hq + h) * 256 + half * 16;
+  };
+  bf16x8 qf[8], df[8];
+  float l2 = 0.f, dval = 0.f;
+  int ent = 0;
+  // (lse and D are issued first, so that they are the oldest loads in flight
+  // wherever the loop waits for them)
+  if (nchunks > 0) {
+    ent = entry_at(0);
+    l2 = a.lse[(int64_t)(a.w0 + (ent >> 6)) * a.Hq + h];
+    dval = a.D[(int64_t)(ent >> 6) * a.Hq + h];
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
-        df[st] = *reinterpret_cast<const bf16x8*>(drow + st * 32);
-      }
+    for (int st = 0; st < 8; ++st) {
+      qf[st] = *reinterpret_cast<const bf16x8*>(q_ptr(a.q, ent) + st * 32);
+      df[st] = *reinterpret_cast<const bf16x8*>(q_ptr(a.dout, ent) + st * 32);
     }
+  }
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    const int32_t r = a.w0 + (ent >> 6);
+    const int32_t pos = first_pos + (r - rs);
+    const float l2c = l2 * kLog2e, dvc = dval;
+    const int ent_next = entry_at(chunk + 1);
+    l2 = a.lse[(int64_t)(a.w0 + (ent_next >> 6)) * a.Hq + h];
+    dval = a.D[(int64_t)(ent_next >> 6) * a.Hq + h];
     // S^T = K Q^T, then P^T in place (hidden keys: -inf -> 0)
     f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
 #pragma unroll
     for (int st = 0; st < 8; ++st)
 #pragma unroll
       for (int kt_ = 0; kt_ < 4; ++kt_) acc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&ks[kbase[st] + 8192 * kt_]), qf[st], acc[kt_]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(q_ptr(a.q, ent_next) + st * 32);
     const int lim = pos - b * 128 - 4 * half;
 #pragma unroll
     for (int kt_ = 0; kt_ < 4; ++kt_)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        acc[kt_][i] = (32 * kt_ + 8 * (i >> 2) + (i & 3)) <= lim ? fast_exp2(__builtin_fmaf(acc[kt_][i], a.scale_log2, -l2))
-                                                                : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const float ex = fast_exp2(__builtin_fmaf(acc[kt_][i], a.scale_log2, -l2c));
+        acc[kt_][i] = (32 * kt_ + 8 * (i >> 2) + (i & 3)) <= lim ? ex : 0.f;
+      }
     // dP^T = V dO^T
     f32x16 dacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
 #pragma unroll
     for (int st = 0; st < 8; ++st)
 #pragma unroll
       for (int kt_ = 0; kt_ < 4; ++kt_) dacc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&vs[kbase[st] + 8192 * kt_]), df[st], dacc[kt_]);
-    // dS^T = P^T (dP^T - D) as bf16 B operands
-    bf16x8 sf[4][2];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) df[st] = *reinterpret_cast<const bf16x8*>(q_ptr(a.dout, ent_next) + st * 32);
+    // dS^T = P^T (dP^T - D) as bf16 B operands (and P^T itself for the proxy term)
+    bf16x8 sf[4][2], pfk[KL ? 4 : 1][2];
 #pragma unroll
     for (int kt_ = 0; kt_ < 4; ++kt_)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        i32x4 pw;
+        i32x4 pw, qw;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int i0 = 8 * u + 2 * t;
-          const bf16x2 two = {(__bf16)(acc[kt_][i0] * (dacc[kt_][i0] - dval)),
-                              (__bf16)(acc[kt_][i0 + 1] * (dacc[kt_][i0 + 1] - dval))};
+          const bf16x2 two = {(__bf16)(acc[kt_][i0] * (dacc[kt_][i0] - dvc)),
+                              (__bf16)(acc[kt_][i0 + 1] * (dacc[kt_][i0 + 1] - dvc))};
           pw[t] = __builtin_bit_cast(int, two);
+          if constexpr (KL) {
+            const bf16x2 pp = {(__bf16)acc[kt_][i0], (__bf16)acc[kt_][i0 + 1]};
+            qw[t] = __builtin_bit_cast(int, pp);
+          }
         }
         sf[kt_][u] = __builtin_bit_cast(bf16x8, pw);
+        if constexpr (KL) pfk[kt_][u] = __builtin_bit_cast(bf16x8, qw);
       }
     // dQ^T = K^T dS^T
     f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
@@ -818,8 +910,61 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
       }
       wave_lds_sync();
     }
-    (void)slot;
-    (void)valid;
+    if constexpr (KL) {
+      // sum_j P_hj pk_j for this wave's rows: C[dim][row] = pk^T P^T, then the
+      // sum over a token's G heads (adjacent lanes) and one bf16 store per
+      // (token, slot) from the token's first lane
+      f32x16 kacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kt_ = 0; kt_ < 4; ++kt_) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const s16x4 lo = lds_read_tr16(&pkt[vbase[dt] + 256 * (32 * kt_ + 16 * u)]);
+            const s16x4 hi = lds_read_tr16(&pkt[vbase[dt] + 256 * (32 * kt_ + 16 * u + 8)]);
+            kacc[dt] = mfma32x32x16(join_tr16(lo, hi), pfk[kt_][u], kacc[dt]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // G is a power of two up to 16 and a token's heads sit in G aligned
+      // lanes of a 16-lane row: xor 1 and xor 2 (quad permutations) leave
+      // every lane its pair and then quad sum; once each quad holds one value,
+      // the half-row mirror (lane i <- 7 - i within 8) adds the other quad of
+      // the 8, and once each 8 holds one value, the row mirror (i <- 15 - i)
+      // adds the other 8
+      float kv[64];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kv[16 * dt + i] = kacc[dt][i];
+      if (G >= 2)
+#pragma unroll
+        for (int e = 0; e < 64; ++e) kv[e] += dpp_f32<0xB1>(kv[e]);
+      if (G >= 4)
+#pragma unroll
+        for (int e = 0; e < 64; ++e) kv[e] += dpp_f32<0x4E>(kv[e]);
+      if (G >= 8)
+#pragma unroll
+        for (int e = 0; e < 64; ++e) kv[e] += dpp_f32<0x141>(kv[e]);
+      if (G >= 16)
+#pragma unroll
+        for (int e = 0; e < 64; ++e) kv[e] += dpp_f32<0x140>(kv[e]);
+      if (hh == 0 && chunk * MT + tok < n_ent) {
+        uint16_t* dst = a.klpart + (((int64_t)(ent >> 6) * a.Hkv + g) * a.k + (ent & 63)) * 128 + 4 * half;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const float* k4 = &kv[16 * dt + 4 * r4];
+            const bf16x2 lo2 = {(__bf16)(k4[0] * a.inv_g), (__bf16)(k4[1] * a.inv_g)};
+            const bf16x2 hi2 = {(__bf16)(k4[2] * a.inv_g), (__bf16)(k4[3] * a.inv_g)};
+            *reinterpret_cast<i32x2*>(dst + 32 * dt + 8 * r4) = i32x2{__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+          }
+      }
+    }
+    ent = ent_next;
   }
 }
 
@@ -876,17 +1021,23 @@ struct BwdKvArgs {
   float* dv;
   int32_t Hq, Hkv, G, NB, w0, accumulate;
   float scale_log2, sm_scale;
+  // proxy distillation term (KL kernels only): proxy q bf16 [T, Hkv, 128];
+  // dpk fp32 [N, Hkv, 128, 128] receives (1/G) sum over rows and heads of
+  // P_hj pq[token]
+  const uint8_t* pq;
+  float* dpk;
+  float inv_g;
 };
 
-// A workgroup barrier that waits only for this wave's LDS traffic, so global
-// loads issued before it (the next chunk's rows) stay in flight across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+template <bool KL>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];      // K, k_swz
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];      // V, k_swz
   __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];    // a chunk's 32 q rows, v_swz, two buffers
   __shared__ __attribute__((aligned(16))) uint8_t dtile[2][32 * 256]; // a chunk's 32 dO rows, v_swz
+  // the chunk's proxy q rows (row i: token i / G), v_swz
+  __shared__ __attribute__((aligned(16))) uint8_t ptile[KL ? 2 : 1][KL ? 32 * 256 : 16];
   __shared__ __attribute__((aligned(16))) float l2_s[2][32];
   __shared__ __attribute__((aligned(16))) float d_s[2][32];
   __shared__ __attribute__((aligned(16))) int32_t pos_s[2][32];
@@ -927,6 +1078,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
   f32x16 dkacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   f32x16 dvacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  f32x16 pkacc[KL ? 4 : 1];
+#pragma unroll
+  for (int dt = 0; dt < (KL ? 4 : 1); ++dt) pkacc[dt] = f32x16{};
   // Gather slots of this thread: rows ri0 and ri0 + 16 of a chunk (row i =
   // token i / G, head i % G), 16-byte column cc; threads below 32 also fetch
   // row tid's lse, D and position.  Rows of chunk c + 1 are loaded into
@@ -940,10 +1094,18 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
     return reinterpret_cast<const i32x4*>(base + ((int64_t)(a.w0 + (ent >> 6)) * a.Hq + g * G + ri % G) * 256 +
                                           cc * 16);
   };
+  auto prow_ptr = [&](int32_t ent) {
+    return reinterpret_cast<const i32x4*>(a.pq + ((int64_t)(a.w0 + (ent >> 6)) * a.Hkv + g) * 256 + cc * 16);
+  };
   if (nchunks > 0) {
     int32_t ea = entry_of(0, ri0), eb = entry_of(0, ri1), es = tid < 32 ? entry_of(0, tid) : 0;
     i32x4 rq0 = *row_ptr(a.q, ea, ri0), rq1 = *row_ptr(a.q, eb, ri1);
     i32x4 rd0 = *row_ptr(a.dout, ea, ri0), rd1 = *row_ptr(a.dout, eb, ri1);
+    i32x4 rp0 = {}, rp1 = {};
+    if constexpr (KL) {
+      rp0 = *prow_ptr(ea);
+      rp1 = *prow_ptr(eb);
+    }
     float rlse = 0.f, rdd = 0.f;
     int32_t rpos = 0;
     if (tid < 32) {
@@ -961,6 +1123,10 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
       lds_store16<i32x4>(&qt[buf][v_swz(ri1, cc)], rq1);
       lds_store16<i32x4>(&dtile[buf][v_swz(ri0, cc)], rd0);
       lds_store16<i32x4>(&dtile[buf][v_swz(ri1, cc)], rd1);
+      if constexpr (KL) {
+        lds_store16<i32x4>(&ptile[buf][v_swz(ri0, cc)], rp0);
+        lds_store16<i32x4>(&ptile[buf][v_swz(ri1, cc)], rp1);
+      }
       if (tid < 32) {
         l2_s[buf][tid] = rlse * kLog2e;
         d_s[buf][tid] = rdd;
@@ -971,6 +1137,10 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
       rq1 = *row_ptr(a.q, eb, ri1);
       rd0 = *row_ptr(a.dout, ea, ri0);
       rd1 = *row_ptr(a.dout, eb, ri1);
+      if constexpr (KL) {
+        rp0 = *prow_ptr(ea);
+        rp1 = *prow_ptr(eb);
+      }
       if (tid < 32) {
         const int h = g * G + tid % G;
         rlse = a.lse[(int64_t)(a.w0 + (es >> 6)) * a.Hq + h];
@@ -1040,6 +1210,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
           const s16x4 qlo = lds_read_tr16(&qb[vbase[dt] + 256 * (16 * u)]);
           const s16x4 qhi = lds_read_tr16(&qb[vbase[dt] + 256 * (16 * u + 8)]);
           dkacc[dt] = mfma32x32x16(sf[u], join_tr16(qlo, qhi), dkacc[dt]);
+          if constexpr (KL) {   // P^T times the rows' proxy q
+            const s16x4 plo = lds_read_tr16(&ptile[buf][vbase[dt] + 256 * (16 * u)]);
+            const s16x4 phi = lds_read_tr16(&ptile[buf][vbase[dt] + 256 * (16 * u + 8)]);
+            pkacc[dt] = mfma32x32x16(pf[u], join_tr16(plo, phi), pkacc[dt]);
+          }
         }
       }
     }
@@ -1055,6 +1230,10 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
       const float vk = dkacc[dt][r] * a.sm_scale, vv = dvacc[dt][r];
       a.dk[o] = a.accumulate ? a.dk[o] + vk : vk;
       a.dv[o] = a.accumulate ? a.dv[o] + vv : vv;
+      if constexpr (KL) {
+        const float vp = pkacc[dt][r] * a.inv_g;
+        a.dpk[o] = a.accumulate ? a.dpk[o] + vp : vp;
+      }
     }
 }
 
@@ -1063,12 +1242,12 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
 hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
                                           const void* vp, const int32_t* kv_indices, const int32_t* sel,
                                           const void* out, const float* lse, const void* dout, float* dq, float* dk,
-                                          float* dv, char* ws, int32_t w0, int32_t w1, bool first_window,
-                                          hipStream_t st) {
+                                          float* dv, const KlOperands* kl, char* ws, int32_t w0, int32_t w1,
+                                          bool first_window, hipStream_t st) {
   const PlanLayout& L = p->lay;
   const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
   const int32_t nkey = Hkv * p->NB;
-  build_csr(p, m, sel, ws, w0, w1, st);
+  build_csr(p, m, sel, ws, w0, w1, st, /*sorted=*/true);
   float* D = reinterpret_cast<float*>(ws + L.part_lse);
   uint16_t* part = reinterpret_cast<uint16_t*>(ws + L.part_o);
   const int64_t npairs = (int64_t)(w1 - w0) * Hq;
@@ -1097,16 +1276,29 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   a.w0 = w0;
   a.scale_log2 = p->d.sm_scale * kLog2e;
   a.sm_scale = p->d.sm_scale;
+  a.pkp = kl ? static_cast<const uint8_t*>(kl->pkp) : nullptr;
+  a.klpart = kl ? reinterpret_cast<uint16_t*>(ws + L.kl_part) : nullptr;
+  a.inv_g = 1.f / (float)p->G;
   const int64_t max_items = ((int64_t)(w1 - w0) * Hkv * k + p->entries_per_item - 1) / p->entries_per_item + nkey;
   {
     ProfEvents pe(p, "bwd_dq");
-    hipExtLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)max_items), dim3(256), 0, st, pe.start, pe.stop, 0, a);
+    if (kl)
+      hipExtLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)max_items), dim3(256), 0, st, pe.start, pe.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)max_items), dim3(256), 0, st, pe.start, pe.stop, 0, a);
   }
   {
     DqSumArgs ds{sel, m, part, dq, Hq, Hkv, p->G, k, w0, w1};
     ProfEvents pe(p, "bwd_dq_sum");
     hipExtLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, pe.start,
                           pe.stop, 0, ds);
+  }
+  if (kl) {   // the sparse proxy term of each (row, group): sum of its slots, into dpq
+    DqSumArgs ds{sel, m, a.klpart, kl->dpq, Hkv, Hkv, 1, k, w0, w1};
+    const int64_t n = (int64_t)(w1 - w0) * Hkv;
+    ProfEvents pe(p, "kl_dq_sum");
+    hipExtLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((n + 15) / 16)), dim3(256), 0, st, pe.start, pe.stop,
+                          0, ds);
   }
   BwdKvArgs kv;
   kv.q = a.q;
@@ -1129,9 +1321,15 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   kv.accumulate = first_window ? 0 : 1;
   kv.scale_log2 = a.scale_log2;
   kv.sm_scale = a.sm_scale;
+  kv.pq = kl ? static_cast<const uint8_t*>(kl->pq) : nullptr;
+  kv.dpk = kl ? kl->dpk : nullptr;
+  kv.inv_g = a.inv_g;
   {
     ProfEvents pe(p, "bwd_dkv");
-    hipExtLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)nkey), dim3(256), 0, st, pe.start, pe.stop, 0, kv);  // NB x Hkv
+    if (kl)
+      hipExtLaunchKernelGGL(bwd_dkv_kernel<true>, dim3((unsigned)nkey), dim3(256), 0, st, pe.start, pe.stop, 0, kv);
+    else
+      hipExtLaunchKernelGGL(bwd_dkv_kernel<false>, dim3((unsigned)nkey), dim3(256), 0, st, pe.start, pe.stop, 0, kv);
   }
   return hipGetLastError();
 }

@@ -252,6 +252,45 @@ msa_status_t msa_sparse_attn_prefill_backward(msa_plan_t plan, const void* q, co
                                               const void* dout, float* dq, float* dk_pages, float* dv_pages,
                                               void* workspace, size_t workspace_bytes, msa_stream_t stream);
 
+/* Fused training backward of the main attention and of the proxy's
+ * distillation loss (Flash-MSA article, backward paragraph: the KL divergence
+ * between the proxy's and the main attention's distributions needs both at
+ * once, and its gradient with respect to a proxy score is the proxy
+ * probability minus the main probability).  Computes everything
+ * msa_sparse_attn_prefill_backward computes, plus, for row r and KV group g
+ * (driven by proxy head g) over the row's visible keys j (j <= pos, j < kv_len):
+ *   p_proxy_j = softmax_j(z_j),  z_j = proxy_sm_scale <proxy_q[r][g], proxy_k[j][g]>
+ *   p_main_j  = (1/G) sum over the group's heads h of the main attention
+ *               probability of key j (0 off the cached selection)
+ *   dz_j      = kl_grad_scale (p_proxy_j - p_main_j)
+ *   dproxy_q[r][g]  = proxy_sm_scale sum_j dz_j proxy_k[j][g]
+ *   dproxy_k[j][g] += proxy_sm_scale dz_j proxy_q[r][g]
+ * i.e. the gradient of kl_grad_scale * sum_(r,g) KL(p_main || p_proxy) with
+ * p_main held fixed.  The main probabilities use the forward's lse, as the
+ * main gradients do.
+ *
+ *   main operands as in msa_sparse_attn_prefill_backward
+ *   proxy_q           bf16 [T, H_kv, 128]
+ *   proxy_k_pages     bf16 [num_pages, H_kv, 128, 128] (same page table)
+ *   kl_grad_scale     upstream gradient of the summed KL (finite)
+ *   dproxy_q          fp32 [T, H_kv, 128], fully written
+ *   dproxy_k_pages    fp32 [num_pages, H_kv, 128, 128]: pages of sequences
+ *                     written, other pages not touched
+ *   proxy_lse         fp32 [T, H_kv]: log-sum-exp (natural log) of z over the
+ *                     row's visible keys, written
+ * The plan needs proxy_dtype BF16 and num_proxy_heads == num_proxy_kv_heads
+ * == num_kv_heads; its workspace then holds the proxy term's per-slot
+ * partials.  Errors: INVALID_ARG for null or misaligned pointers or a
+ * non-finite kl_grad_scale; UNSUPPORTED for a decode plan, non-bf16 K/V or a
+ * plan without that proxy shape; WORKSPACE_TOO_SMALL. */
+msa_status_t msa_sparse_attn_prefill_backward_kl(msa_plan_t plan, const void* q, const void* k_pages,
+                                                 const void* v_pages, const int32_t* kv_indices,
+                                                 const int32_t* kv_block_indexes, const void* out, const float* lse,
+                                                 const void* dout, const void* proxy_q, const void* proxy_k_pages,
+                                                 float kl_grad_scale, float* dq, float* dk_pages, float* dv_pages,
+                                                 float* dproxy_q, float* dproxy_k_pages, float* proxy_lse,
+                                                 void* workspace, size_t workspace_bytes, msa_stream_t stream);
+
 /* Stage 3b: paged sparse decode (README "Stacks": paged FP8 decode).  Stage
  * 3a with qo_len = 1 for every sequence: the new token is already the last
  * key of its sequence (position kv_len - 1), so its local block is the last.
@@ -276,7 +315,8 @@ msa_status_t msa_plan_info(msa_plan_t plan, int64_t* total_rows, int32_t* nb_max
 
 /* Diagnostics, not part of the path.  When `kernel` names one of the
  * library's internal kernels ("proxy_maxscore", "topk_select", "proxy_topk", "csr",
- * "partial_attn", "merge", "decode", "decode_merge", "bwd_dq", "bwd_dq_sum", "bwd_dkv"), each later launch of it
+ * "partial_attn", "merge", "decode", "decode_merge", "bwd_dq", "bwd_dq_sum", "bwd_dkv",
+ * "kl_dq_sum", "kl_dense_dq", "kl_dense_dk"), each later launch of it
  * for this plan carries two HIP events that the runtime stamps with the
  * dispatch's begin and end (events are created on first use and reused; no
  * device memory).  NULL

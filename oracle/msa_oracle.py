@@ -443,7 +443,8 @@ def proxy_kl_backward(proxy_q, proxy_k_pages, q, k_pages, kv_indices, kv_block_i
 
     Needs one proxy head and one proxy-K head per KV group.  Returns (dpq
     float64 [T, P, d], dpk float64 shaped like the proxy pool, kl float64 [T, P]
-    (each (row, group)'s KL, without grad_scale)).  `rows` and `groups` visit
+    (each (row, group)'s KL, without grad_scale), plse float64 [T, P] (natural
+    log-sum-exp of z over the row's visible keys)).  `rows` and `groups` visit
     a subset as in sparse_attention_backward.
     """
     lay = Layout(qo_lens, kv_lens, page_size)
@@ -457,6 +458,7 @@ def proxy_kl_backward(proxy_q, proxy_k_pages, q, k_pages, kv_indices, kv_block_i
     dpq = np.zeros((T, P, d))
     dpk = np.zeros(proxy_k_pages.shape[:2] + (B, d))
     kl = np.zeros((T, P))
+    plse = np.zeros((T, P))
     kvi = np.asarray(kv_indices, dtype=np.int64)
     for r in (range(T) if rows is None else [int(x) for x in rows]):
         s = lay.seq_of_row(r)
@@ -470,7 +472,8 @@ def proxy_kl_backward(proxy_q, proxy_k_pages, q, k_pages, kv_indices, kv_block_i
             pq = bf16_to_f64(proxy_q[r, g])
             PK = gather_rows(proxy_k_pages, BF16, None, kv_indices, lay, s, g, vis)
             z = proxy_sm_scale * (PK @ pq)
-            logpp = z - z.max() - np.log(np.sum(np.exp(z - z.max())))
+            plse[r, g] = z.max() + np.log(np.sum(np.exp(z - z.max())))
+            logpp = z - plse[r, g]
             pp = np.exp(logpp)
             blocks = set(int(b) for b in kv_block_indexes[r, g] if b >= 0)
             chosen = np.array([int(j) // B in blocks for j in vis], dtype=bool)
@@ -485,7 +488,7 @@ def proxy_kl_backward(proxy_q, proxy_k_pages, q, k_pages, kv_indices, kv_block_i
             np.add.at(dpk, (pages, g, slots), proxy_sm_scale * dz[:, None] * pq[None, :])
             on = pm > 0
             kl[r, g] = float(np.sum(pm[on] * (np.log(pm[on]) - logpp[on])))
-    return dpq, dpk, kl
+    return dpq, dpk, kl, plse
 
 
 def sparse_decode(q, k_pages, v_pages, kv_indices, kv_block_indexes, kv_lens, page_size, sm_scale,

@@ -40,7 +40,7 @@ def test_kl_gradient_matches_torch_autograd(qo, kv, Hq, Hkv, k):
     B = 16
     q, kp, pq, pk, kvi, sel, lay = _case(3, qo, kv, Hq, Hkv, k, B)
     scale, pscale, gs = 0.3, 0.2, 0.7
-    dpq, dpk, kl = proxy_kl_backward(pq, pk, q, kp, kvi, sel, qo, kv, B, scale, pscale, grad_scale=gs)
+    dpq, dpk, kl, _ = proxy_kl_backward(pq, pk, q, kp, kvi, sel, qo, kv, B, scale, pscale, grad_scale=gs)
     PQ, PK = _t(pq).requires_grad_(), _t(pk).requires_grad_()
     Q, K = _t(q), _t(kp)
     G = Hq // Hkv
@@ -74,14 +74,14 @@ def test_kl_gradient_matches_finite_differences_of_the_loss():
     qo, kv = [30], [30]
     q, kp, pq, pk, kvi, sel, lay = _case(5, qo, kv, 4, 2, 2, B)
     scale, pscale = 0.25, 0.3
-    dpq, dpk, _ = proxy_kl_backward(pq, pk, q, kp, kvi, sel, qo, kv, B, scale, pscale)
+    dpq, dpk, _, _ = proxy_kl_backward(pq, pk, q, kp, kvi, sel, qo, kv, B, scale, pscale)
     f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
     def loss(pqf, pkf):
         orig = om.bf16_to_f64
         om.bf16_to_f64 = lambda x: np.asarray(x, dtype=np.float64)
         try:
-            _, _, kl = proxy_kl_backward(pqf, pkf, f(q), f(kp), kvi, sel, qo, kv, B, scale, pscale)
+            _, _, kl, _ = proxy_kl_backward(pqf, pkf, f(q), f(kp), kvi, sel, qo, kv, B, scale, pscale)
         finally:
             om.bf16_to_f64 = orig
         return float(kl.sum())
@@ -109,9 +109,12 @@ def test_kl_vanishes_when_the_proxy_is_the_main_attention():
     for r in range(25):
         loc = lay.local(r)
         sel[r, :, :loc + 1] = np.arange(loc + 1)
-    dpq, dpk, kl = proxy_kl_backward(q, kp, q, kp, kvi, sel, qo, kv, B, 0.4, 0.4)
+    dpq, dpk, kl, plse = proxy_kl_backward(q, kp, q, kp, kvi, sel, qo, kv, B, 0.4, 0.4)
     assert np.abs(kl).max() < 1e-12
     assert np.abs(dpq).max() < 1e-12 and np.abs(dpk).max() < 1e-12
+    # the proxy's log-sum-exp is then the main attention's, from the oracle forward
+    _, lse = om.sparse_attention(q, kp, kp, kvi, sel, qo, kv, B, 0.4)
+    assert np.allclose(plse, lse, atol=1e-12)
 
 
 def test_kl_proxy_k_gradient_sums_to_zero_per_sequence_and_head():
@@ -120,7 +123,7 @@ def test_kl_proxy_k_gradient_sums_to_zero_per_sequence_and_head():
     B = 16
     qo, kv = [20, 33], [50, 33]
     q, kp, pq, pk, kvi, sel, lay = _case(11, qo, kv, 4, 2, 3, B)
-    _, dpk, kl = proxy_kl_backward(pq, pk, q, kp, kvi, sel, qo, kv, B, 0.3, 0.3)
+    _, dpk, kl, _ = proxy_kl_backward(pq, pk, q, kp, kvi, sel, qo, kv, B, 0.3, 0.3)
     assert (kl >= -1e-12).all()
     for s in range(2):
         pages = kvi[lay.page_start[s]:lay.page_start[s + 1]]
