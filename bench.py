@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "decode_merge": "sparse_decode.hip", "proxy_onerow": "proxy_maxscore.hip",
     "proxy_onerow_mxfp4": "proxy_maxscore.hip", "topk_wave": "topk_select.hip",
     "kl_dq_sum": "sparse_prefill.hip", "kl_dense_dq": "proxy_kl.hip", "kl_dense_dk": "proxy_kl.hip",
+    "dense_fwd": "dense_attn.hip", "dense_dq": "dense_attn.hip", "dense_dkv": "sparse_prefill.hip",
 }
 
 
@@ -192,6 +193,14 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
             nxt_bwd = True
         section[i] = nxt
         in_bwd[i] = nxt_bwd
+    # the warm-up workload (no partial_attn): from its first dense forward on,
+    # dense and proxy-distillation kernels and D's preparation are its own
+    warm = next((wl for wl, _ in ev if wl.endswith("_warmup")), None)
+    warm_from = next((i for i, (k, _, _) in enumerate(rows) if k == "dense_fwd"), len(rows))
+    for i in range(warm_from, len(rows)):
+        if rows[i][0].startswith(("dense_", "kl_")) or rows[i][0] == "bwd_prep":
+            section[i] = warm
+            in_bwd[i] = False
     last = None
     step_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow"), len(rows))
     mx_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow_mxfp4"), len(rows))
@@ -202,6 +211,8 @@ def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
             section[i] = DECODE_STEP_WORKLOAD
         elif k.startswith("decode"):
             section[i] = SECTION_OF_KERNEL["decode"]
+        elif i >= warm_from and section[i] == warm:
+            pass
         elif k == "merge" or in_bwd[i] or section[i] is None:
             section[i] = last
         if k == "partial_attn":
@@ -452,6 +463,71 @@ def backward_bench(msa, n_cfg, steps, warmup, kl=False):
     }
 
 
+def warmup_bench(msa, n_cfg, steps, warmup):
+    """The warm-up mode on one workload: one step = the dense causal forward
+    (msa_dense_attn_prefill) and its backward with the proxy distillation
+    gradient against the dense main distribution
+    (msa_dense_attn_prefill_backward)."""
+    import torch
+    from synthetic.gen import workload, seed_of
+    from synthetic.device_gen import make_inputs_device
+    w = workload(n_cfg)
+    inp = make_inputs_device(w, seed_of(n_cfg))
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                        w.num_proxy_kv_heads, topk=w.topk, proxy_dtype=w.proxy_dtype)
+    T, Hq, Hkv = w.total_rows, w.num_qo_heads, w.num_kv_heads
+    N = inp.k_pages.shape[0]
+    out = torch.empty((T, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed_of(n_cfg) + 78)
+    dout = torch.randn((T, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    dq = torch.empty((T, Hq, 128), dtype=torch.float32, device="cuda")
+    dk = torch.empty((N, Hkv, 128, 128), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    dpq = torch.empty((T, Hkv, 128), dtype=torch.float32, device="cuda")
+    dpk = torch.empty_like(dk)
+    plse = torch.empty((T, Hkv), dtype=torch.float32, device="cuda")
+
+    def step():
+        msa.msa_dense_attn_prefill(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, out, lse)
+        msa.msa_dense_attn_prefill_backward(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, out, lse, dout,
+                                            dq, dk, dv, inp.proxy_q, inp.proxy_k_pages, 1.0, dpq, dpk, plse)
+
+    step()
+    torch.cuda.synchronize()
+    stages = ["dense_fwd", "dense_dq", "dense_dkv", "kl_dense_dq", "kl_dense_dk"]
+    per_kernel = kernel_profile(msa, plan, step, stages)
+    dominant = max(stages, key=lambda n: per_kernel[n][0])
+    ms_step, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, dominant)
+    dense = 0.0                                   # causally visible (row, key) pairs per KV head
+    for qo, kv in zip(w.qo_lens, w.kv_lens):
+        dense += qo * (kv - qo + 1) + qo * (qo - 1) / 2
+    G = Hq // Hkv
+    main_pairs = dense * Hq                       # (row, query head, key)
+    proxy_pairs = dense * Hkv                     # (row, proxy head, key)
+    # products of 2*128 FLOP per pair: forward S, PV; backward S, dP, dQ (dense_dq), dV, dK (dense_dkv;
+    # its S, dP recomputation not counted); the proxy term's pk^T P and P^T pq over the main pairs;
+    # the dense proxy S, dQ (kl_dense_dq) and dK (kl_dense_dk) over the proxy pairs
+    products = {"dense_fwd": 2 * main_pairs, "dense_dq": 4 * main_pairs, "dense_dkv": 3 * main_pairs,
+                "kl_dense_dq": 2 * proxy_pairs, "kl_dense_dk": proxy_pairs}
+    f_total = 256 * sum(products.values())
+    work = 256 * products[dominant] / (launches // steps)
+    achieved = work / (k_ms * 1e-3) / 1e12
+    roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_from_profiles(dominant, w.name),
+            "avg_launch_ms": k_ms, "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "FLOP"}
+    name = w.name + "_warmup"
+    return {
+        "workload": name, "tok_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
+        "tflops": f_total / (ms_step * 1e-3) / 1e12, "stage_ms": {n: v[0] for n, v in per_kernel.items()},
+        "roofline": roof,
+        "config": {"workload": name, "total_rows": T, "num_qo_heads": Hq, "num_kv_heads": Hkv,
+                   "num_proxy_heads": w.num_proxy_heads, "head_dim": 128, "kv_dtype": "bf16",
+                   "step": "dense forward + backward (dq, dk, dv, dproxy_q, dproxy_k)", "G": G},
+    }
+
+
 def decode_bench(msa, steps, warmup, sets=4):
     import torch
     from synthetic.gen import workload, seed_of, decode_picks
@@ -595,9 +671,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode entries")
     ap.add_argument("--extra", default="prefill_128k,prefill_32k_mxfp4,prefill_32k_backward,prefill_32k_backward_kl,"
-                                       "decode_131k,decode_step_131k,decode_step_mxfp4_131k",
+                                       "warmup_32k,decode_131k,decode_step_131k,decode_step_mxfp4_131k",
                     help="comma-separated extra entries: prefill_128k, prefill_32k_mxfp4, prefill_32k_backward, "
-                         "prefill_32k_backward_kl, decode_131k, decode_step_131k, decode_step_mxfp4_131k (or none)")
+                         "prefill_32k_backward_kl, warmup_32k, decode_131k, decode_step_131k, decode_step_mxfp4_131k "
+                         "(or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -624,7 +701,7 @@ def main():
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
         if e not in ("prefill_128k", "prefill_32k_mxfp4", "prefill_32k_backward", "prefill_32k_backward_kl",
-                     "decode_131k", "decode_step_131k", "decode_step_mxfp4_131k"):
+                     "warmup_32k", "decode_131k", "decode_step_131k", "decode_step_mxfp4_131k"):
             ap.error(f"unknown extra entry {e}")
     if args.copy_calibration:
         print("[bench] calibration copy", file=sys.stderr, flush=True)
@@ -646,6 +723,10 @@ def main():
     if "prefill_32k_backward_kl" in extras:
         print("[bench] prefill 32k backward with the proxy distillation gradient", file=sys.stderr, flush=True)
         extra["prefill_32k_backward_kl"] = backward_bench(msa, 2, args.steps, args.warmup, kl=True)
+    if "warmup_32k" in extras:
+        print("[bench] warm-up mode 32k: dense forward and backward with the proxy gradient", file=sys.stderr,
+              flush=True)
+        extra["warmup_32k"] = warmup_bench(msa, 2, max(2, args.steps // 2), 1)
     if "decode_131k" in extras:
         print("[bench] decode 131k fp8", file=sys.stderr, flush=True)
         extra["decode_131k"] = decode_bench(msa, max(50, args.steps * 10), 10)

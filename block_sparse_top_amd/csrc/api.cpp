@@ -120,7 +120,8 @@ hipEvent_t take_event(msa::Profiler& pr) {
 }
 const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "proxy_topk", "csr",        "partial_attn",
                                     "merge",          "decode",      "decode_merge", "bwd_dq", "bwd_dq_sum",
-                                    "bwd_dkv",        "kl_dq_sum",   "kl_dense_dq",  "kl_dense_dk"};
+                                    "bwd_dkv",        "kl_dq_sum",   "kl_dense_dq",  "kl_dense_dk",
+                                    "dense_fwd",      "dense_dq",    "dense_dkv"};
 }  // namespace
 
 ProfEvents::ProfEvents(const msa_plan_s* p, const char* name) {
@@ -571,6 +572,84 @@ msa_status_t msa_sparse_attn_prefill_backward_kl(msa_plan_t p, const void* q, co
     if (e != hipSuccess) return hip_status(e, __func__);
   }
   return hip_status(msa::launch_proxy_kl_dense(p, m, kv_indices, kl, hs), __func__);
+}
+
+msa_status_t msa_dense_attn_prefill(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                    const int32_t* kv_indices, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_dense_attn_prefill: NULL plan");
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_dense_attn_prefill: decode plan");
+  if (p->d.kv_dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_dense_attn_prefill: the dense attention is built for bf16 K/V");
+  MSA_CHECK_PTR(q);
+  MSA_CHECK_PTR(k_pages);
+  MSA_CHECK_PTR(v_pages);
+  MSA_CHECK_PTR(kv_indices);
+  MSA_CHECK_PTR(out);
+  MSA_CHECK_PTR(lse);
+  msa_status_t st = check_ws(p, workspace, workspace_bytes);
+  if (st != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  return hip_status(msa::launch_dense_forward(p, m, q, k_pages, v_pages, kv_indices, out, lse, hs), __func__);
+}
+
+msa_status_t msa_dense_attn_prefill_backward(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                             const int32_t* kv_indices, const void* out, const float* lse,
+                                             const void* dout, const void* proxy_q, const void* proxy_k_pages,
+                                             float kl_grad_scale, float* dq, float* dk_pages, float* dv_pages,
+                                             float* dproxy_q, float* dproxy_k_pages, float* proxy_lse,
+                                             void* workspace, size_t workspace_bytes, msa_stream_t stream) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_dense_attn_prefill_backward: NULL plan");
+  if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_dense_attn_prefill_backward: decode plan");
+  if (p->d.kv_dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_dense_attn_prefill_backward: the dense attention is built for bf16 K/V");
+  MSA_CHECK_PTR(q);
+  MSA_CHECK_PTR(k_pages);
+  MSA_CHECK_PTR(v_pages);
+  MSA_CHECK_PTR(kv_indices);
+  MSA_CHECK_PTR(out);
+  MSA_CHECK_PTR(lse);
+  MSA_CHECK_PTR(dout);
+  MSA_CHECK_PTR(dq);
+  MSA_CHECK_PTR(dk_pages);
+  MSA_CHECK_PTR(dv_pages);
+  const bool with_kl = proxy_q != nullptr || proxy_k_pages != nullptr;
+  if (with_kl) {
+    if (p->d.proxy_dtype != MSA_BF16 || p->d.num_proxy_heads != p->d.num_kv_heads ||
+        p->d.num_proxy_kv_heads != p->d.num_kv_heads)
+      return fail(MSA_ERR_UNSUPPORTED,
+                  "msa_dense_attn_prefill_backward: the proxy term needs a bf16 proxy with one proxy head and one "
+                  "proxy-K head per KV group");
+    if (!std::isfinite(kl_grad_scale))
+      return fail(MSA_ERR_INVALID_ARG, "msa_dense_attn_prefill_backward: kl_grad_scale is not finite");
+    MSA_CHECK_PTR(proxy_q);
+    MSA_CHECK_PTR(proxy_k_pages);
+    MSA_CHECK_PTR(dproxy_q);
+    MSA_CHECK_PTR(dproxy_k_pages);
+    MSA_CHECK_PTR(proxy_lse);
+  }
+  // D = <dout, out> for every row lives in the partial-output area
+  if ((size_t)p->T * p->d.num_qo_heads * 4 > p->lay.part_lse - p->lay.part_o)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "msa_dense_attn_prefill_backward: the plan's attention window is too short for this many rows "
+                "(its partial area holds D = <dout, out> of every row)");
+  msa_status_t st = check_ws(p, workspace, workspace_bytes);
+  if (st != MSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
+  const msa::DevMeta m = msa::dev_meta(p, workspace);
+  float* D = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->lay.part_o);
+  const msa::KlOperands kl{proxy_q, proxy_k_pages, dproxy_q, dproxy_k_pages, proxy_lse, p->d.proxy_sm_scale,
+                           kl_grad_scale};
+  const msa::KlOperands* klp = with_kl ? &kl : nullptr;
+  hipError_t e = msa::launch_bwd_prep(p, out, dout, D, 0, p->T, hs);
+  if (e == hipSuccess) e = msa::launch_dense_dq(p, m, q, k_pages, v_pages, kv_indices, lse, D, dout, dq, klp, hs);
+  if (e == hipSuccess)
+    e = msa::launch_dense_dkv(p, m, q, k_pages, v_pages, kv_indices, lse, D, dout, dk_pages, dv_pages, klp, hs);
+  if (e == hipSuccess && with_kl) e = msa::launch_proxy_kl_dense(p, m, kv_indices, kl, hs);
+  return hip_status(e, __func__);
 }
 
 msa_status_t msa_sparse_attn_decode(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,

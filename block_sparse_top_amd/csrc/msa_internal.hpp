@@ -107,6 +107,19 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
                                           const void* out, const float* lse, const void* dout, float* dq, float* dk,
                                           float* dv, const KlOperands* kl, char* ws, int32_t w0, int32_t w1,
                                           bool first_window, hipStream_t st);
+// Dense causal attention (the warm-up mode): forward; the backward's dq (and
+// the proxy term's dense p_main part into kl->dpq) and dk, dv (and into
+// kl->dpk); D = <dout, out> for rows [w0, w1) into D[0 ..).
+hipError_t launch_dense_forward(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
+                                const int32_t* kv_indices, void* out, float* lse, hipStream_t st);
+hipError_t launch_dense_dq(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
+                           const int32_t* kv_indices, const float* lse, const float* D, const void* dout, float* dq,
+                           const KlOperands* kl, hipStream_t st);
+hipError_t launch_dense_dkv(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
+                            const int32_t* kv_indices, const float* lse, const float* D, const void* dout, float* dk,
+                            float* dv, const KlOperands* kl, hipStream_t st);
+hipError_t launch_bwd_prep(const msa_plan_s* p, const void* out, const void* dout, float* D, int32_t w0, int32_t w1,
+                           hipStream_t st);
 // The dense proxy part of the distillation gradient, after every window of
 // the fused backward has stored its sparse part in dpq and dpk.
 hipError_t launch_proxy_kl_dense(const msa_plan_s* p, const DevMeta& m, const int32_t* kv_indices,

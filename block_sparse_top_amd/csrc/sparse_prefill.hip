@@ -1019,7 +1019,7 @@ struct BwdKvArgs {
   DevMeta m;
   float* dk;              // fp32 [N, Hkv, 128, 128]
   float* dv;
-  int32_t Hq, Hkv, G, NB, w0, accumulate;
+  int32_t Hq, Hkv, G, NB, w0, w1, accumulate;
   float scale_log2, sm_scale;
   // proxy distillation term (KL kernels only): proxy q bf16 [T, Hkv, 128];
   // dpk fp32 [N, Hkv, 128, 128] receives (1/G) sum over rows and heads of
@@ -1030,7 +1030,9 @@ struct BwdKvArgs {
 };
 
 
-template <bool KL>
+// DENSE: every row of the window that sees the block (the warm-up mode's
+// dense main attention), in row order, instead of the bin's CSR entries.
+template <bool KL, bool DENSE = false>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];      // K, k_swz
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];      // V, k_swz
@@ -1050,7 +1052,16 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
   const int32_t page = a.kv_indices[gb];
   const int32_t first_pos = a.m.kv[s] - a.m.qo[s];
   const int32_t rs = a.m.row_start[s];
-  const int e0 = a.offsets[key], n_ent = a.offsets[key + 1] - e0;
+  int e0 = 0, n_ent = 0, dense_lo = 0;   // dense: window-relative first row
+  if constexpr (DENSE) {
+    const int32_t lo = max(max(0, b * 128 - first_pos), a.w0 - rs);
+    const int32_t hi = min(a.m.qo[s], a.w1 - rs);
+    n_ent = max(0, hi - lo);
+    dense_lo = rs + lo - a.w0;
+  } else {
+    e0 = a.offsets[key];
+    n_ent = a.offsets[key + 1] - e0;
+  }
   {
     const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * 32768;
     const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * 32768;
@@ -1089,7 +1100,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
   const int ri1 = ri0 + 16;
   // entries and lse stay raw in registers until used, so that no wait for a
   // just-issued load lands before the barrier
-  auto entry_of = [&](int chunk, int ri) { return a.entries[e0 + min(chunk * MT + ri / G, n_ent - 1)]; };
+  auto entry_of = [&](int chunk, int ri) {
+    const int e = min(chunk * MT + ri / G, n_ent - 1);
+    if constexpr (DENSE) return (dense_lo + e) << 6;
+    else return a.entries[e0 + e];
+  };
   auto row_ptr = [&](const uint8_t* base, int32_t ent, int ri) {
     return reinterpret_cast<const i32x4*>(base + ((int64_t)(a.w0 + (ent >> 6)) * a.Hq + g * G + ri % G) * 256 +
                                           cc * 16);
@@ -1239,6 +1254,49 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
 
 }  // namespace
 
+hipError_t launch_dense_dkv(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
+                            const int32_t* kv_indices, const float* lse, const float* D, const void* dout, float* dk,
+                            float* dv, const KlOperands* kl, hipStream_t st) {
+  BwdKvArgs kv{};
+  kv.q = static_cast<const uint8_t*>(q);
+  kv.dout = static_cast<const uint8_t*>(dout);
+  kv.kp = static_cast<const uint8_t*>(kp);
+  kv.vp = static_cast<const uint8_t*>(vp);
+  kv.lse = lse;
+  kv.D = D;
+  kv.kv_indices = kv_indices;
+  kv.m = m;
+  kv.dk = dk;
+  kv.dv = dv;
+  kv.Hq = p->d.num_qo_heads;
+  kv.Hkv = p->d.num_kv_heads;
+  kv.G = p->G;
+  kv.NB = p->NB;
+  kv.w0 = 0;
+  kv.w1 = p->T;
+  kv.accumulate = 0;
+  kv.scale_log2 = p->d.sm_scale * kLog2e;
+  kv.sm_scale = p->d.sm_scale;
+  kv.pq = kl ? static_cast<const uint8_t*>(kl->pq) : nullptr;
+  kv.dpk = kl ? kl->dpk : nullptr;
+  kv.inv_g = 1.f / (float)p->G;
+  const dim3 grid((unsigned)(p->d.num_kv_heads * p->NB));
+  ProfEvents pe(p, "dense_dkv");
+  if (kl)
+    hipExtLaunchKernelGGL((bwd_dkv_kernel<true, true>), grid, dim3(256), 0, st, pe.start, pe.stop, 0, kv);
+  else
+    hipExtLaunchKernelGGL((bwd_dkv_kernel<false, true>), grid, dim3(256), 0, st, pe.start, pe.stop, 0, kv);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const msa_plan_s* p, const void* out, const void* dout, float* D, int32_t w0, int32_t w1,
+                           hipStream_t st) {
+  const int64_t npairs = (int64_t)(w1 - w0) * p->d.num_qo_heads;
+  PrepArgs pa{static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), D, w0, w1, p->d.num_qo_heads};
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, pa);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
                                           const void* vp, const int32_t* kv_indices, const int32_t* sel,
                                           const void* out, const float* lse, const void* dout, float* dq, float* dk,
@@ -1318,6 +1376,7 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   kv.G = p->G;
   kv.NB = p->NB;
   kv.w0 = w0;
+  kv.w1 = w1;
   kv.accumulate = first_window ? 0 : 1;
   kv.scale_log2 = a.scale_log2;
   kv.sm_scale = a.sm_scale;

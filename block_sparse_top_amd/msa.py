@@ -25,6 +25,7 @@ MSA_PREFILL, MSA_DECODE = 0, 1
 ENTRY_POINTS = ("msa_plan", "msa_plan_destroy", "msa_plan_info", "msa_proxy_block_maxscore", "msa_topk_select",
                 "msa_proxy_topk_select", "msa_sparse_attn_prefill", "msa_sparse_attn_prefill_rows",
                 "msa_sparse_attn_prefill_backward", "msa_sparse_attn_prefill_backward_kl",
+                "msa_dense_attn_prefill", "msa_dense_attn_prefill_backward",
                 "msa_sparse_attn_decode", "msa_last_error", "msa_profile_kernel", "msa_profile_read")
 
 
@@ -75,6 +76,9 @@ def _load() -> ctypes.CDLL:
     lib.msa_sparse_attn_prefill_backward.argtypes = [P, VP, VP, VP, IP, IP, VP, FP, VP, FP, FP, FP, VP, SZ, P]
     lib.msa_sparse_attn_prefill_backward_kl.argtypes = [P, VP, VP, VP, IP, IP, VP, FP, VP, VP, VP, ctypes.c_float, FP,
                                                         FP, FP, FP, FP, FP, VP, SZ, P]
+    lib.msa_dense_attn_prefill.argtypes = [P, VP, VP, VP, IP, VP, FP, VP, SZ, P]
+    lib.msa_dense_attn_prefill_backward.argtypes = [P, VP, VP, VP, IP, VP, FP, VP, VP, VP, ctypes.c_float, FP, FP, FP,
+                                                    FP, FP, FP, VP, SZ, P]
     lib.msa_sparse_attn_decode.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
     lib.msa_profile_kernel.argtypes = [P, ctypes.c_char_p]
     lib.msa_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -219,6 +223,23 @@ def msa_sparse_attn_prefill_backward_kl(plan: Plan, q, k_pages, v_pages, kv_indi
         _ptr(lse), _ptr(dout), _ptr(proxy_q), _ptr(proxy_k_pages), float(kl_grad_scale), _ptr(dq), _ptr(dk_pages),
         _ptr(dv_pages), _ptr(dproxy_q), _ptr(dproxy_k_pages), _ptr(proxy_lse), _ptr(plan.workspace),
         plan.workspace_bytes, _stream()))
+    return dq, dk_pages, dv_pages, dproxy_q, dproxy_k_pages, proxy_lse
+
+
+def msa_dense_attn_prefill(plan: Plan, q, k_pages, v_pages, kv_indices, out, lse):
+    _check(_lib.msa_dense_attn_prefill(plan.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(kv_indices), _ptr(out),
+                                       _ptr(lse), _ptr(plan.workspace), plan.workspace_bytes, _stream()))
+    return out, lse
+
+
+def msa_dense_attn_prefill_backward(plan: Plan, q, k_pages, v_pages, kv_indices, out, lse, dout, dq, dk_pages,
+                                    dv_pages, proxy_q=None, proxy_k_pages=None, kl_grad_scale=1.0, dproxy_q=None,
+                                    dproxy_k_pages=None, proxy_lse=None):
+    _check(_lib.msa_dense_attn_prefill_backward(
+        plan.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(kv_indices), _ptr(out), _ptr(lse), _ptr(dout),
+        _ptr(proxy_q), _ptr(proxy_k_pages), float(kl_grad_scale), _ptr(dq), _ptr(dk_pages), _ptr(dv_pages),
+        _ptr(dproxy_q), _ptr(dproxy_k_pages), _ptr(proxy_lse), _ptr(plan.workspace), plan.workspace_bytes,
+        _stream()))
     return dq, dk_pages, dv_pages, dproxy_q, dproxy_k_pages, proxy_lse
 
 

@@ -291,6 +291,44 @@ msa_status_t msa_sparse_attn_prefill_backward_kl(msa_plan_t plan, const void* q,
                                                  float* dproxy_q, float* dproxy_k_pages, float* proxy_lse,
                                                  void* workspace, size_t workspace_bytes, msa_stream_t stream);
 
+/* Warm-up mode, forward (Flash-MSA article, backward paragraph: a warm-up in
+ * which the main attention runs densely, without block indexes, while the
+ * proxy learns only in the backward pass): causal GQA attention of every
+ * query row over all of its visible keys (j <= pos, j < kv_len),
+ *   out[r][h] = sum_j softmax_j(sm_scale * <q[r][h], k[j][g]>) v[j][g],
+ *   lse[r][h] = natural log of sum_j exp(sm_scale * <q[r][h], k[j][g]>).
+ * Operands and layouts as in msa_sparse_attn_prefill without the selection;
+ * bf16 K/V only.  Errors: INVALID_ARG for null or misaligned pointers;
+ * UNSUPPORTED for a decode plan or non-bf16 K/V; WORKSPACE_TOO_SMALL. */
+msa_status_t msa_dense_attn_prefill(msa_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
+                                    const int32_t* kv_indices, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, msa_stream_t stream);
+
+/* Warm-up mode, backward: the gradients of msa_dense_attn_prefill (the
+ * formulas of msa_sparse_attn_prefill_backward with every visible key), and,
+ * when proxy_q and proxy_k_pages are given, the proxy distillation gradient
+ * of msa_sparse_attn_prefill_backward_kl with p_main the group mean of this
+ * dense attention (nonzero on every visible key).  With proxy_q and
+ * proxy_k_pages NULL the proxy arguments are ignored and may be NULL.
+ *   out, lse          msa_dense_attn_prefill's results for the same inputs
+ *   dq                fp32 [T, H_q, 128], fully written
+ *   dk_pages, dv_pages fp32 [num_pages, H_kv, 128, 128]: pages of sequences
+ *                     written, other pages not touched
+ *   proxy operands and outputs as in msa_sparse_attn_prefill_backward_kl
+ * The plan's partial-output area holds D = <dout, out> of every row, so very
+ * long batches need an attention window of at least T / (64 topk) rows.
+ * Errors: INVALID_ARG for null or misaligned pointers or a non-finite
+ * kl_grad_scale; UNSUPPORTED for a decode plan, non-bf16 K/V, a proxy term on
+ * a plan without one bf16 proxy head and proxy-K head per KV group, or too
+ * short an attention window; WORKSPACE_TOO_SMALL. */
+msa_status_t msa_dense_attn_prefill_backward(msa_plan_t plan, const void* q, const void* k_pages,
+                                             const void* v_pages, const int32_t* kv_indices, const void* out,
+                                             const float* lse, const void* dout, const void* proxy_q,
+                                             const void* proxy_k_pages, float kl_grad_scale, float* dq,
+                                             float* dk_pages, float* dv_pages, float* dproxy_q,
+                                             float* dproxy_k_pages, float* proxy_lse, void* workspace,
+                                             size_t workspace_bytes, msa_stream_t stream);
+
 /* Stage 3b: paged sparse decode (README "Stacks": paged FP8 decode).  Stage
  * 3a with qo_len = 1 for every sequence: the new token is already the last
  * key of its sequence (position kv_len - 1), so its local block is the last.
@@ -316,7 +354,7 @@ msa_status_t msa_plan_info(msa_plan_t plan, int64_t* total_rows, int32_t* nb_max
 /* Diagnostics, not part of the path.  When `kernel` names one of the
  * library's internal kernels ("proxy_maxscore", "topk_select", "proxy_topk", "csr",
  * "partial_attn", "merge", "decode", "decode_merge", "bwd_dq", "bwd_dq_sum", "bwd_dkv",
- * "kl_dq_sum", "kl_dense_dq", "kl_dense_dk"), each later launch of it
+ * "kl_dq_sum", "kl_dense_dq", "kl_dense_dk", "dense_fwd", "dense_dq", "dense_dkv"), each later launch of it
  * for this plan carries two HIP events that the runtime stamps with the
  * dispatch's begin and end (events are created on first use and reused; no
  * device memory).  NULL
