@@ -75,7 +75,8 @@ def traffic_from_profiles(kernel: str, workload: str):
 # rocprofv3 summaries (run on the host from the CSV files rocprofv3 wrote)
 # ----------------------------------------------------------------------------
 COPY_BYTES = 1 << 30           # calibration copy: bytes read and bytes written per launch
-PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --extra decode_131k,decode_step_131k --copy-calibration"
+PMC_ARGS = ("--steps 2 --warmup 1 --no-cpu-baseline --extra prefill_32k_backward,decode_131k,decode_step_131k "
+            "--copy-calibration")
 PMC_CMDS = {
     "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o f -- python bench.py {PMC_ARGS}",
     "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o w -- python bench.py {PMC_ARGS}",
@@ -84,8 +85,6 @@ TRACE_CMD = "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/kt -o kt -- p
 SECTION_OF_KERNEL = {"decode": "decode_fp8_b32_131k", "decode_merge": "decode_fp8_b32_131k",
                      "proxy_onerow": "decode_step_b32_131k", "topk_wave": "decode_step_b32_131k",
                      "proxy_onerow_mxfp4": "decode_step_mxfp4_b32_131k"}
-DECODE_STEP_WORKLOAD = "decode_step_b32_131k"
-DECODE_STEP_MXFP4_WORKLOAD = "decode_step_mxfp4_b32_131k"
 
 
 def _short_kernel(name: str):
@@ -144,94 +143,61 @@ def summarize_counters(fetch_csv: str, write_csv: str):
     return written
 
 
-def summarize_trace(trace_csv: str, bench_json: str, out_name: str):
+def summarize_trace(trace_csv: str, bench_json: str, bench_err: str, out_name: str):
     """Kernel durations from a rocprofv3 kernel trace, per workload, next to
     the per-launch averages that bench.py measured with HIP events in the same
-    run.  The prefill workloads run one after another and every step ends
-    with the attention and merge kernels, so a prefill dispatch belongs to the
-    workload of the next partial_attn dispatch, a merge to that of the one
-    before it; workloads are named in the order bench.py runs them."""
+    run.  bench.py stamps the host's monotonic clock on stderr before each
+    workload ("[bench-mark] <entry> <ns>"); the trace's dispatch timestamps
+    count from the same origin, so a dispatch belongs to the last workload
+    marked before it started."""
+    import bisect
     import collections
     import csv
     line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
     b = json.loads(line)
     ev = [(b["config"]["workload"], b["roofline"])]
-    for name, r in (b.get("extra") or {}).items():
+    name_of = {"main": b["config"]["workload"]}
+    for key, r in (b.get("extra") or {}).items():
         ev.append((r["workload"], r["roofline"]))
-    prefill_names = [wl for wl, _ in ev if wl.startswith("prefill")]
+        name_of[key] = r["workload"]
+    marks = []
+    for ln in open(bench_err).read().splitlines():
+        if ln.startswith("[bench-mark] "):
+            _, key, ns = ln.split()
+            marks.append((int(ns), name_of.get(key, key)))
+    marks.sort()
+    mark_t = [t for t, _ in marks]
     rows = []
     for r in sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"])):
         k = _short_kernel(r["Kernel_Name"])
         if k is None or k == "copy":
             continue
         grid = "x".join(r[f"Grid_Size_{a}"] for a in "XYZ")
-        rows.append((k, grid, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6))
-    # partial_attn dispatches -> workload: the prefill workloads run one after
-    # another, so each run of partial_attn dispatches with one grid is the
-    # next prefill workload in bench order
-    # (a training backward between two forwards also starts a new run)
-    backward = lambda k: k.startswith(("bwd_", "kl_"))
-    pa_label = {}
-    run, prev = -1, None
-    for i, (k, grid, _) in enumerate(rows):
-        if k == "partial_attn":
-            if grid != prev:
-                run += 1
-                prev = grid
-            pa_label[i] = prefill_names[run] if run < len(prefill_names) else f"prefill grid {grid}"
-        elif backward(k):
-            prev = None
-    # a dispatch belongs to a backward step when the next partial_attn or
-    # backward kernel after it is a backward kernel (its CSR build included)
-    section = [None] * len(rows)
-    in_bwd = [False] * len(rows)
-    nxt, nxt_bwd = None, False
-    for i in range(len(rows) - 1, -1, -1):
-        if rows[i][0] == "partial_attn":
-            nxt, nxt_bwd = pa_label[i], False
-        elif backward(rows[i][0]):
-            nxt_bwd = True
-        section[i] = nxt
-        in_bwd[i] = nxt_bwd
-    # the warm-up workload (no partial_attn): from its first dense forward on,
-    # dense and proxy-distillation kernels and D's preparation are its own
-    warm = next((wl for wl, _ in ev if wl.endswith("_warmup")), None)
-    warm_from = next((i for i, (k, _, _) in enumerate(rows) if k == "dense_fwd"), len(rows))
-    for i in range(warm_from, len(rows)):
-        if rows[i][0].startswith(("dense_", "kl_")) or rows[i][0] == "bwd_prep":
-            section[i] = warm
-            in_bwd[i] = False
-    last = None
-    step_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow"), len(rows))
-    mx_from = next((i for i, (k, _, _) in enumerate(rows) if k == "proxy_onerow_mxfp4"), len(rows))
-    for i, (k, grid, _) in enumerate(rows):
-        if i >= mx_from:        # the decode-step workloads run last, fp8 then MXFP4
-            section[i] = DECODE_STEP_MXFP4_WORKLOAD
-        elif i >= step_from:
-            section[i] = DECODE_STEP_WORKLOAD
-        elif k.startswith("decode"):
-            section[i] = SECTION_OF_KERNEL["decode"]
-        elif i >= warm_from and section[i] == warm:
-            pass
-        elif k == "merge" or in_bwd[i] or section[i] is None:
-            section[i] = last
-        if k == "partial_attn":
-            last = pa_label[i]
+        t0 = int(r["Start_Timestamp"])
+        i = bisect.bisect_right(mark_t, t0) - 1
+        sec = marks[i][1] if i >= 0 else "before the first mark"
+        rows.append((k, grid, (int(r["End_Timestamp"]) - t0) * 1e-6, sec))
+    section = [sec for (_, _, _, sec) in rows]
+    rows = [(k, grid, ms) for (k, grid, ms, _) in rows]
     g = collections.OrderedDict()
     for (k, grid, ms), sec in zip(rows, section):
         g.setdefault((sec, k, grid), []).append(ms)
     out = [f"# Kernel durations, rocprofv3 kernel trace of the default benchmark run",
            f"# command: {TRACE_CMD}",
-           f"# summary: python bench.py --summarize-trace gpurun_out/kt/kt_kernel_trace.csv <bench stdout> {out_name}",
+           f"# summary: python bench.py --summarize-trace gpurun_out/kt/kt_kernel_trace.csv <bench stdout> "
+           f"<bench stderr> {out_name}",
            "", "| workload | kernel | grid | calls | avg ms | min ms | max ms | total ms |",
            "|---|---|---|---|---|---|---|---|"]
     for (sec, k, grid), v in sorted(g.items(), key=lambda kv: str(kv[0][0])):
         out.append(f"| {sec} | {k} | {grid} | {len(v)} | {np.mean(v):.4f} | {min(v):.4f} | {max(v):.4f} | "
                    f"{sum(v):.3f} |")
     out += ["", "HIP-event averages that bench.py reported for the dominant kernel of each workload in this run:", ""]
+    # profiling names that share a kernel symbol with another entry
+    symbol_of = {"dense_dkv": "bwd_dkv", "kl_dq_sum": "bwd_dq_sum", "proxy_topk": "proxy_maxscore",
+                 "topk_select": "topk"}
     for wl, r in ev:
-        tr = np.mean(g.get((wl, r["kernel"], next((gr for (s2, k2, gr) in g if s2 == wl and k2 == r["kernel"]), "")),
-                           [float("nan")]))
+        kk = symbol_of.get(r["kernel"], r["kernel"])
+        tr = np.mean(g.get((wl, kk, next((gr for (s2, k2, gr) in g if s2 == wl and k2 == kk), "")), [float("nan")]))
         out.append(f"- {wl}: {r['kernel']} {r['avg_launch_ms']:.4f} ms per launch by HIP events, {tr:.4f} ms in the "
                    f"trace ({r['launches_per_step']} launches per step); {r['achieved']:.1f} {r['unit']} "
                    f"= {100 * r['frac']:.1f}% of {r['peak']:.0f}")
@@ -681,7 +647,7 @@ def main():
                     help="first run a streaming copy of known size (for scaling HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: write profiles/<kernel>__<workload>__traffic.txt from two rocprofv3 --pmc runs")
-    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "BENCH_STDOUT", "OUT_NAME"),
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_CSV", "BENCH_STDOUT", "BENCH_STDERR", "OUT_NAME"),
                     help="host only: write a kernel-duration summary under profiles/ from a rocprofv3 kernel trace")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -706,35 +672,48 @@ def main():
     if args.copy_calibration:
         print("[bench] calibration copy", file=sys.stderr, flush=True)
         copy_calibration()
+    def mark(key):   # host monotonic clock before a workload's first launch (trace summaries split on it)
+        torch.cuda.synchronize()
+        print(f"[bench-mark] {key} {time.monotonic_ns()}", file=sys.stderr, flush=True)
+
     print("[bench] prefill 32k", file=sys.stderr, flush=True)
+    mark("main")
     main_res, (w, inp, sel) = prefill_bench(msa, 2, args.steps, args.warmup)
     extra = {}
     if "prefill_128k" in extras:
         print("[bench] prefill 128k varlen", file=sys.stderr, flush=True)
+        mark("prefill_128k")
         r3, _ = prefill_bench(msa, 3, max(2, args.steps // 2), 1)
         extra["prefill_128k"] = r3
     if "prefill_32k_mxfp4" in extras:
         print("[bench] prefill 32k, MXFP4 proxy q and K, MXFP4 K/V", file=sys.stderr, flush=True)
+        mark("prefill_32k_mxfp4")
         r8, _ = prefill_bench(msa, 8, args.steps, args.warmup)
         extra["prefill_32k_mxfp4"] = r8
     if "prefill_32k_backward" in extras:
         print("[bench] prefill 32k backward", file=sys.stderr, flush=True)
+        mark("prefill_32k_backward")
         extra["prefill_32k_backward"] = backward_bench(msa, 2, args.steps, args.warmup)
     if "prefill_32k_backward_kl" in extras:
         print("[bench] prefill 32k backward with the proxy distillation gradient", file=sys.stderr, flush=True)
+        mark("prefill_32k_backward_kl")
         extra["prefill_32k_backward_kl"] = backward_bench(msa, 2, args.steps, args.warmup, kl=True)
     if "warmup_32k" in extras:
         print("[bench] warm-up mode 32k: dense forward and backward with the proxy gradient", file=sys.stderr,
               flush=True)
+        mark("warmup_32k")
         extra["warmup_32k"] = warmup_bench(msa, 2, max(2, args.steps // 2), 1)
     if "decode_131k" in extras:
         print("[bench] decode 131k fp8", file=sys.stderr, flush=True)
+        mark("decode_131k")
         extra["decode_131k"] = decode_bench(msa, max(50, args.steps * 10), 10)
     if "decode_step_131k" in extras:
         print("[bench] decode step (indexer + decode) 131k fp8", file=sys.stderr, flush=True)
+        mark("decode_step_131k")
         extra["decode_step_131k"] = decode_step_bench(msa, max(50, args.steps * 10), 10)
     if "decode_step_mxfp4_131k" in extras:
         print("[bench] decode step (indexer + decode) 131k, MXFP4 proxy K", file=sys.stderr, flush=True)
+        mark("decode_step_mxfp4_131k")
         extra["decode_step_mxfp4_131k"] = decode_step_bench(msa, max(50, args.steps * 10), 10, wn=7)
     cpu = None
     if not args.no_cpu_baseline:
