@@ -202,7 +202,6 @@ struct KlDkArgs {
 };
 
 __global__ __launch_bounds__(256) void kl_dense_dk_kernel(KlDkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];     // proxy K, k_swz
   __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];   // a chunk's 32 proxy q rows, v_swz
   __shared__ __attribute__((aligned(16))) float l2_s[2][32];
   __shared__ __attribute__((aligned(16))) int32_t pos_s[2][32];
@@ -216,17 +215,17 @@ __global__ __launch_bounds__(256) void kl_dense_dk_kernel(KlDkArgs a) {
   const int32_t i0 = max(0, 128 * b - first_pos);          // first row that sees the block
   const int32_t nrows = a.m.qo[s] - i0;
   const int32_t r0 = a.m.row_start[s] + i0;
-  {
-    const uint8_t* kb = a.pk + ((int64_t)page * a.P + p) * 32768;
-    const int kv_in_block = a.m.kv[s] - b * 128;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      const i32x4 kr = *reinterpret_cast<const i32x4*>(kb + c * 16);
-      lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], (c >> 4) < kv_in_block ? kr : i32x4{});
-    }
-  }
   const int half = lane >> 5, j = lane & 31;
+  // this wave's 32 proxy K rows, the B operand of every chunk's S (rows past
+  // kv_len zeroed)
+  bf16x8 bk[8];
+  {
+    const int krow = 32 * wave + j;
+    const bool live_row = krow < a.m.kv[s] - b * 128;
+    const uint8_t* kb = a.pk + ((int64_t)page * a.P + p) * 32768 + krow * 256 + half * 16;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) bk[st] = live_row ? *reinterpret_cast<const bf16x8*>(kb + st * 32) : bf16x8{};
+  }
   const int q16 = lane >> 4, m16 = lane & 15;
   const int keypos = b * 128 + 32 * wave + j;
   int vbase[4];
@@ -266,8 +265,7 @@ __global__ __launch_bounds__(256) void kl_dense_dk_kernel(KlDkArgs a) {
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const bf16x8 aq = lds_load16<bf16x8>(&qb[v_swz(j, 2 * st + half)]);
-        const bf16x8 bk = lds_load16<bf16x8>(&ks[k_swz(32 * wave + j, 2 * st + half)]);
-        sacc = mfma32x32x16(aq, bk, sacc);
+        sacc = mfma32x32x16(aq, bk[st], sacc);
       }
       f32x4 l2v[4];
       i32x4 ps4[4];

@@ -1034,8 +1034,6 @@ struct BwdKvArgs {
 // dense main attention), in row order, instead of the bin's CSR entries.
 template <bool KL, bool DENSE = false>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];      // K, k_swz
-  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];      // V, k_swz
   __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];    // a chunk's 32 q rows, v_swz, two buffers
   __shared__ __attribute__((aligned(16))) uint8_t dtile[2][32 * 256]; // a chunk's 32 dO rows, v_swz
   // the chunk's proxy q rows (row i: token i / G), v_swz
@@ -1062,23 +1060,23 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
     e0 = a.offsets[key];
     n_ent = a.offsets[key + 1] - e0;
   }
-  {
-    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * 32768;
-    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * 32768;
-    const int kv_in_block = a.m.kv[s] - b * 128;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      const bool live_row = (c >> 4) < kv_in_block;
-      const i32x4 kr = *reinterpret_cast<const i32x4*>(kb + c * 16);
-      const i32x4 vr = *reinterpret_cast<const i32x4*>(vb + c * 16);
-      lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], live_row ? kr : i32x4{});
-      lds_store16<i32x4>(&vs[k_swz(c >> 4, c & 15)], live_row ? vr : i32x4{});
-    }
-  }
   const int G = a.G;
   const int MT = 32 / G;                       // tokens per 32-row chunk
   const int half = lane >> 5, j = lane & 31;
+  // This wave's 32 keys never change: their K and V rows are the B operands
+  // of every chunk's S and dP products, held in registers (lane (j, half),
+  // step st: key 32 wave + j, dims 16 st + 8 half ..); rows past kv_len zeroed.
+  bf16x8 bk[8], bv[8];
+  {
+    const int krow = 32 * wave + j;
+    const bool live_row = krow < a.m.kv[s] - b * 128;
+    const int64_t off = ((int64_t)page * a.Hkv + g) * 32768 + krow * 256 + half * 16;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      bk[st] = live_row ? *reinterpret_cast<const bf16x8*>(a.kp + off + st * 32) : bf16x8{};
+      bv[st] = live_row ? *reinterpret_cast<const bf16x8*>(a.vp + off + st * 32) : bf16x8{};
+    }
+  }
   const int q16 = lane >> 4, m16 = lane & 15;
   const int nchunks = (n_ent + MT - 1) / MT;
   const int keypos = b * 128 + 32 * wave + j;  // this lane's key position
@@ -1165,7 +1163,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
       ea = entry_of(chunk + 2, ri0);
       eb = entry_of(chunk + 2, ri1);
       es = tid < 32 ? entry_of(chunk + 2, tid) : 0;
-      // the tiles of this chunk (and K/V, first chunk) are in LDS; every wave is
+      // the tiles of this chunk are in LDS; every wave is
       // done with chunk - 1, whose buffer chunk + 1 will overwrite
       lds_barrier();
       const uint8_t* qb = qt[buf];
@@ -1175,11 +1173,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const bf16x8 aq = lds_load16<bf16x8>(&qb[v_swz(j, 2 * st + half)]);
-        const bf16x8 bk = lds_load16<bf16x8>(&ks[k_swz(32 * wave + j, 2 * st + half)]);
-        sacc = mfma32x32x16(aq, bk, sacc);
+        sacc = mfma32x32x16(aq, bk[st], sacc);
         const bf16x8 ad = lds_load16<bf16x8>(&db[v_swz(j, 2 * st + half)]);
-        const bf16x8 bv = lds_load16<bf16x8>(&vs[k_swz(32 * wave + j, 2 * st + half)]);
-        pacc = mfma32x32x16(ad, bv, pacc);
+        pacc = mfma32x32x16(ad, bv[st], pacc);
       }
       // P and dS (register r holds row 8(r/4) + 4 half + r%4), as bf16 A operands;
       // the rows' lse, D and positions come as four 4-row runs
