@@ -171,3 +171,48 @@ def test_mxfp4_proxy_rules():
             nb = pqk.workspace_bytes
             assert f(pqk.handle, a, a, a, none, a, 0, 2, a, ws, nb, none) == msa.MSA_ERR_INVALID_ARG   # q scale given
             assert f(pqk.handle, a, a, none, none, a, 0, 2, a, ws, nb - 1, none) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_training_entry_points_validate_before_touching_the_device():
+    """The backward, the fused distillation backward and the warm-up calls
+    reject bad arguments and unsupported plans before any launch."""
+    L = msa.lib()
+    a = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x20000)
+    none = None
+    p = _plan()
+    nb = p.workspace_bytes
+    f = ctypes.c_float
+    # main backward: null dout, decode plan, fp8 K/V
+    assert L.msa_sparse_attn_prefill_backward(p.handle, a, a, a, a, a, a, a, none, a, a, a, ws, nb, none) == \
+        msa.MSA_ERR_INVALID_ARG and b"dout" in L.msa_last_error()
+    d = msa.msa_plan(None, [1000] * 4, 16, 2, topk=17, kv_dtype="fp8", mode="decode", allocate=False)
+    assert L.msa_sparse_attn_prefill_backward(d.handle, a, a, a, a, a, a, a, a, a, a, a, ws, d.workspace_bytes,
+                                              none) == msa.MSA_ERR_UNSUPPORTED
+    p8 = _plan(kv_dtype="fp8")
+    assert L.msa_sparse_attn_prefill_backward(p8.handle, a, a, a, a, a, a, a, a, a, a, a, ws, p8.workspace_bytes,
+                                              none) == msa.MSA_ERR_UNSUPPORTED
+    # fused distillation backward: proxy shape, finite scale, every pointer
+    args = lambda plan, gs, last=a: (plan.handle, a, a, a, a, a, a, a, a, a, a, f(gs), a, a, a, a, a, last, ws,
+                                     plan.workspace_bytes, none)
+    assert L.msa_sparse_attn_prefill_backward_kl(*args(p, float("nan"))) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_sparse_attn_prefill_backward_kl(*args(p, 1.0, none)) == msa.MSA_ERR_INVALID_ARG
+    pf8 = msa.msa_plan([300], [300], 8, 2, 2, 2, topk=4, proxy_dtype="fp8", allocate=False)
+    assert L.msa_sparse_attn_prefill_backward_kl(*args(pf8, 1.0)) == msa.MSA_ERR_UNSUPPORTED
+    shared = msa.msa_plan([300], [300], 8, 2, 2, 1, topk=4, allocate=False)
+    assert L.msa_sparse_attn_prefill_backward_kl(*args(shared, 1.0)) == msa.MSA_ERR_UNSUPPORTED
+    # warm-up forward and backward
+    assert L.msa_dense_attn_prefill(p.handle, a, a, a, a, a, none, ws, nb, none) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_dense_attn_prefill(d.handle, a, a, a, a, a, a, ws, d.workspace_bytes, none) == \
+        msa.MSA_ERR_UNSUPPORTED
+    assert L.msa_dense_attn_prefill(p8.handle, a, a, a, a, a, a, ws, p8.workspace_bytes, none) == \
+        msa.MSA_ERR_UNSUPPORTED
+    dense = lambda plan, pq, gs=1.0: (plan.handle, a, a, a, a, a, a, a, pq, pq, f(gs), a, a, a, a, a, a, ws,
+                                      plan.workspace_bytes, none)
+    assert L.msa_dense_attn_prefill_backward(*dense(pf8, a)) == msa.MSA_ERR_UNSUPPORTED
+    assert L.msa_dense_attn_prefill_backward(*dense(shared, a)) == msa.MSA_ERR_UNSUPPORTED
+    assert L.msa_dense_attn_prefill_backward(*dense(p, a, float("inf"))) == msa.MSA_ERR_INVALID_ARG
+    # an attention window too short to hold D of every row
+    tiny = msa.msa_plan([4096], [4096], 8, 2, 2, 2, topk=1, attn_window_rows=32, allocate=False)
+    assert L.msa_dense_attn_prefill_backward(*dense(tiny, none)) == msa.MSA_ERR_UNSUPPORTED and \
+        b"window" in L.msa_last_error()
