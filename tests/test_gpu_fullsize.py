@@ -163,6 +163,168 @@ def test_prefill_32k_backward():
     _backward_case(2, 48)
 
 
+def _check_sum_zero(name, grad, kvi, lay, scale):
+    """Per sequence and head, the gradient rows of a sequence's keys sum to
+    zero (up to fp32 accumulation, relative to the sum of magnitudes)."""
+    for si in range(len(lay.kv)):
+        pages = kvi[int(lay.page_start[si]):int(lay.page_start[si + 1])]
+        got = grad[pages].double().sum(dim=(0, 2))              # [heads, d]
+        mag = grad[pages].double().abs().sum(dim=(0, 2))
+        assert ((got.abs() <= 1e-3 * mag + 1e-6 * scale)).all(), (name, si)
+
+
+def _late_blocks(lay, rng, Hkv):
+    """Two (group, block) pairs among the first sequence's last blocks: few
+    rows see them, so the oracle, which must visit every one, stays quick."""
+    nb0 = lay.nb[0]
+    return ((0, nb0 - 2), (int(rng.integers(1, Hkv)), nb0 - 3))
+
+
+def test_prefill_32k_backward_kl():
+    """The fused distillation backward at 32K in the benchmark's launch
+    configuration: main gradients equal the main-only backward bit for bit;
+    dproxy_q and the proxy lse on sampled rows and two groups; dproxy_k of two
+    (group, late block) pairs exactly (the oracle visits every row that sees
+    the block: the dense proxy term reaches all of them); every (sequence,
+    head)'s dproxy_k sums to zero."""
+    from block_sparse_top_amd import msa
+    w = workload(2)
+    print(f"[fullsize] fused distillation backward workload={w.name}", flush=True)
+    inp = make_inputs_device(w, seed_of(2))
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                        w.num_proxy_kv_heads, topk=w.topk, proxy_dtype=w.proxy_dtype)
+    T, Hq, Hkv = w.total_rows, w.num_qo_heads, w.num_kv_heads
+    N = inp.k_pages.shape[0]
+    sel = torch.empty((T, Hkv, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    msa.run_prefill(plan, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale, inp.q, inp.k_pages,
+                    inp.v_pages, inp.kv_indices, sel, out, lse)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed_of(2) + 79)
+    dout = torch.randn((T, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    main = [torch.empty((T, Hq, 128), device="cuda"), torch.zeros((N, Hkv, 128, 128), device="cuda"),
+            torch.zeros((N, Hkv, 128, 128), device="cuda")]
+    ref_main = [torch.empty_like(main[0]), torch.zeros_like(main[1]), torch.zeros_like(main[2])]
+    dpq = torch.empty((T, Hkv, 128), device="cuda")
+    dpk = torch.zeros((N, Hkv, 128, 128), device="cuda")
+    plse = torch.empty((T, Hkv), device="cuda")
+    msa.msa_sparse_attn_prefill_backward_kl(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, lse, dout,
+                                            inp.proxy_q, inp.proxy_k_pages, 1.0, *main, dpq, dpk, plse)
+    msa.msa_sparse_attn_prefill_backward(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, lse, dout,
+                                         *ref_main)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), main, ref_main):
+        assert torch.equal(a, b), f"{name}: fused backward differs from the main-only backward"
+    from tests.test_gpu_backward import _check
+    h = {k: to_host(getattr(inp, k)) for k in ("q", "k_pages", "proxy_q", "proxy_k_pages", "kv_indices")}
+    gsel = sel.cpu().numpy()
+    lay = O.Layout(w.qo_lens, w.kv_lens, 128)
+    rng = np.random.default_rng(seed_of(2) + 5)
+    rows = _sample_rows(w, 8, seed_of(2))
+    groups = sorted(set(rng.integers(Hkv, size=2).tolist()))
+    print(f"[fullsize] oracle dproxy_q on {rows.size} rows, groups {groups}", flush=True)
+    rq, _, _, rl = O.proxy_kl_backward(h["proxy_q"], h["proxy_k_pages"], h["q"], h["k_pages"], h["kv_indices"], gsel,
+                                       w.qo_lens, w.kv_lens, 128, w.sm_scale, w.proxy_sm_scale, rows=rows,
+                                       groups=groups)
+    got = dpq[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    _check(f"{w.name} dproxy_q (sampled rows)", got[:, groups], rq[rows][:, groups])
+    assert np.abs(plse.cpu().numpy()[rows][:, groups] - rl[rows][:, groups]).max() < 1e-3
+    for gg, b in _late_blocks(lay, rng, Hkv):
+        see = np.nonzero((np.arange(T) < lay.row_start[1]) &
+                         (np.array([lay.pos(int(r)) for r in range(T)]) >= 128 * b))[0]
+        print(f"[fullsize] oracle dproxy_k of group {gg} block {b}: {see.size} rows", flush=True)
+        _, rk, _, _ = O.proxy_kl_backward(h["proxy_q"], h["proxy_k_pages"], h["q"], h["k_pages"], h["kv_indices"],
+                                          gsel, w.qo_lens, w.kv_lens, 128, w.sm_scale, w.proxy_sm_scale, rows=see,
+                                          groups=[gg])
+        page = int(h["kv_indices"][lay.page_start[0] + b])
+        _check(f"{w.name} dproxy_k (group {gg}, block {b})", dpk[page, gg].cpu().numpy().astype(np.float64),
+               rk[page, gg])
+    kvi = torch.from_numpy(h["kv_indices"].astype(np.int64)).cuda()
+    _check_sum_zero("dproxy_k", dpk, kvi, lay, float(dpk.abs().max()))
+
+
+def test_warmup_32k():
+    """The warm-up mode at 32K: the dense forward on sampled rows; dq and
+    dproxy_q on sampled rows and two groups; dk, dv and dproxy_k of two
+    (group, late block) pairs exactly; per sequence and group sum_j dv_j =
+    the group's dout sum and sum_j dk_j = 0, and dproxy_k sums to zero."""
+    from block_sparse_top_amd import msa
+    from tests.test_gpu_backward import _check
+    w = workload(2)
+    print(f"[fullsize] warm-up workload={w.name}", flush=True)
+    inp = make_inputs_device(w, seed_of(2))
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                        w.num_proxy_kv_heads, topk=w.topk, proxy_dtype=w.proxy_dtype)
+    T, Hq, Hkv = w.total_rows, w.num_qo_heads, w.num_kv_heads
+    N = inp.k_pages.shape[0]
+    G = Hq // Hkv
+    out = torch.empty((T, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    msa.msa_dense_attn_prefill(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, out, lse)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed_of(2) + 80)
+    dout = torch.randn((T, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    dq = torch.empty((T, Hq, 128), device="cuda")
+    dk = torch.zeros((N, Hkv, 128, 128), device="cuda")
+    dv = torch.zeros_like(dk)
+    dpq = torch.empty((T, Hkv, 128), device="cuda")
+    dpk = torch.zeros_like(dk)
+    plse = torch.empty((T, Hkv), device="cuda")
+    msa.msa_dense_attn_prefill_backward(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, out, lse, dout, dq, dk,
+                                        dv, inp.proxy_q, inp.proxy_k_pages, 1.0, dpq, dpk, plse)
+    torch.cuda.synchronize()
+    h = {k: to_host(getattr(inp, k)) for k in ("q", "k_pages", "v_pages", "proxy_q", "proxy_k_pages", "kv_indices")}
+    lay = O.Layout(w.qo_lens, w.kv_lens, 128)
+    allsel = np.full((T, Hkv, max(lay.nb)), -1, np.int32)
+    for r in range(T):
+        allsel[r, :, :lay.local(r) + 1] = np.arange(lay.local(r) + 1)
+    rng = np.random.default_rng(seed_of(2) + 6)
+    rows = _sample_rows(w, 8, seed_of(2))
+    print(f"[fullsize] oracle dense forward on {rows.size} rows", flush=True)
+    ref, ref_lse = O.sparse_attention(h["q"], h["k_pages"], h["v_pages"], h["kv_indices"], allsel, w.qo_lens,
+                                      w.kv_lens, 128, w.sm_scale, rows=rows)
+    tr = torch.from_numpy(rows).cuda()
+    check_output(bf16_out_to_f64(out[tr]), ref, BF16_ATOL, BF16_COS, w.name + " warm-up forward")
+    assert np.abs(lse[tr].cpu().numpy() - ref_lse).max() < 1e-3
+    groups = sorted(set(rng.integers(Hkv, size=2).tolist()))
+    heads = [hh for gg in groups for hh in range(gg * G, (gg + 1) * G)]
+    dob = to_host(dout)
+    print(f"[fullsize] oracle dq, dproxy_q on {rows.size} rows, groups {groups}", flush=True)
+    rq, _, _ = O.sparse_attention_backward(h["q"], h["k_pages"], h["v_pages"], h["kv_indices"], allsel, w.qo_lens,
+                                           w.kv_lens, 128, w.sm_scale, dob, rows=rows, groups=groups)
+    _check(f"{w.name} warm-up dq", dq[tr].cpu().numpy().astype(np.float64)[:, heads], rq[rows][:, heads])
+    rpq, _, _, rpl = O.proxy_kl_backward(h["proxy_q"], h["proxy_k_pages"], h["q"], h["k_pages"], h["kv_indices"],
+                                         allsel, w.qo_lens, w.kv_lens, 128, w.sm_scale, w.proxy_sm_scale, rows=rows,
+                                         groups=groups)
+    _check(f"{w.name} warm-up dproxy_q", dpq[tr].cpu().numpy().astype(np.float64)[:, groups], rpq[rows][:, groups])
+    assert np.abs(plse[tr].cpu().numpy()[:, groups] - rpl[rows][:, groups]).max() < 1e-3
+    for gg, b in _late_blocks(lay, rng, Hkv):
+        see = np.nonzero((np.arange(T) < lay.row_start[1]) &
+                         (np.array([lay.pos(int(r)) for r in range(T)]) >= 128 * b))[0]
+        print(f"[fullsize] oracle dk, dv, dproxy_k of group {gg} block {b}: {see.size} rows", flush=True)
+        _, rk, rv = O.sparse_attention_backward(h["q"], h["k_pages"], h["v_pages"], h["kv_indices"], allsel,
+                                                w.qo_lens, w.kv_lens, 128, w.sm_scale, dob, rows=see, groups=[gg])
+        _, rpk, _, _ = O.proxy_kl_backward(h["proxy_q"], h["proxy_k_pages"], h["q"], h["k_pages"], h["kv_indices"],
+                                           allsel, w.qo_lens, w.kv_lens, 128, w.sm_scale, w.proxy_sm_scale,
+                                           rows=see, groups=[gg])
+        page = int(h["kv_indices"][lay.page_start[0] + b])
+        for name, got_t, want in (("dk", dk, rk), ("dv", dv, rv), ("dproxy_k", dpk, rpk)):
+            _check(f"{w.name} warm-up {name} (group {gg}, block {b})",
+                   got_t[page, gg].cpu().numpy().astype(np.float64), want[page, gg])
+    kvi = torch.from_numpy(h["kv_indices"].astype(np.int64)).cuda()
+    for si in range(len(w.kv_lens)):
+        pages = kvi[int(lay.page_start[si]):int(lay.page_start[si + 1])]
+        r0, r1 = int(lay.row_start[si]), int(lay.row_start[si + 1])
+        for gg in range(Hkv):
+            got = dv[pages, gg].double().sum(dim=(0, 1))
+            ref_sum = dout[r0:r1, gg * G:(gg + 1) * G].double().sum(dim=(0, 1))
+            scale = dout[r0:r1, gg * G:(gg + 1) * G].double().abs().sum(dim=(0, 1))
+            assert ((got - ref_sum).abs() <= 2.0 ** -7 * scale + 1e-6).all(), (si, gg)
+    _check_sum_zero("dk", dk, kvi, lay, float(dk.abs().max()))
+    _check_sum_zero("dproxy_k", dpk, kvi, lay, float(dpk.abs().max()))
+
+
 def test_prefill_32k_sampled_rows():
     _prefill_case(2, 48)
 
