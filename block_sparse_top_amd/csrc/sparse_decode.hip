@@ -79,6 +79,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   constexpr int kVBytes = kDecWaves * 2 * kVTile;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kVBytes > kRedBytes ? kVBytes : kRedBytes];
   __shared__ int32_t blist[64];
+  __shared__ int32_t plist[64];   // their pages, looked up once
   __shared__ int32_t s_nvalid;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -91,13 +92,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   const int32_t* selrow = a.sel + ((int64_t)seq * a.Hkv + g) * a.k;
   const int32_t* pages = a.kv_indices + a.m.page_start[seq];
 
-  // valid selected blocks, in slot order (k <= 64: one wave)
+  // valid selected blocks, in slot order (k <= 64: one wave), and their pages:
+  // the slices' K/V loads then depend on no further global load
   if (wave == 0) {
     const int b = lane < a.k ? selrow[lane] : -1;
     const bool ok = b >= 0 && b <= local;
     const uint64_t mask = __ballot(ok);
     const int before = __popcll(mask & ((1ull << lane) - 1ull));
-    if (ok) blist[before] = b;
+    if (ok) {
+      blist[before] = b;
+      plist[before] = pages[b];
+    }
     if (lane == 0) s_nvalid = __popcll(mask);
   }
   __syncthreads();
@@ -123,9 +128,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
   // global loads of one 32-key slice: this lane's two interleaved K rows and
   // half a V row (two lanes per V row)
   auto issue = [&](SliceRegs<FP8>& R, int sl) {
-    const int b = blist[sl >> 2];
     const int key0 = 32 * (sl & 3);
-    const int32_t page = pages[b];
+    const int32_t page = plist[sl >> 2];
     const int64_t blk = ((int64_t)page * a.Hkv + g) * (128 * Tr::kRow);
     const uint8_t* kb = a.kp + blk + (int64_t)key0 * Tr::kRow;
     const uint8_t* vb = a.vp + blk + (int64_t)key0 * Tr::kRow;
