@@ -639,8 +639,8 @@ def main():
     ap.add_argument("--extra", default="prefill_128k,prefill_32k_mxfp4,prefill_32k_backward,prefill_32k_backward_kl,"
                                        "warmup_32k,decode_131k,decode_step_131k,decode_step_mxfp4_131k",
                     help="comma-separated extra entries: prefill_128k, prefill_32k_mxfp4, prefill_32k_backward, "
-                         "prefill_32k_backward_kl, warmup_32k, decode_131k, decode_step_131k, decode_step_mxfp4_131k "
-                         "(or none)")
+                         "prefill_32k_backward_kl, prefill_128k_backward (not by default), warmup_32k, decode_131k, "
+                         "decode_step_131k, decode_step_mxfp4_131k (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -667,7 +667,8 @@ def main():
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
         if e not in ("prefill_128k", "prefill_32k_mxfp4", "prefill_32k_backward", "prefill_32k_backward_kl",
-                     "warmup_32k", "decode_131k", "decode_step_131k", "decode_step_mxfp4_131k"):
+                     "prefill_128k_backward", "warmup_32k", "decode_131k", "decode_step_131k",
+                     "decode_step_mxfp4_131k"):
             ap.error(f"unknown extra entry {e}")
     if args.copy_calibration:
         print("[bench] calibration copy", file=sys.stderr, flush=True)
@@ -698,6 +699,10 @@ def main():
         print("[bench] prefill 32k backward with the proxy distillation gradient", file=sys.stderr, flush=True)
         mark("prefill_32k_backward_kl")
         extra["prefill_32k_backward_kl"] = backward_bench(msa, 2, args.steps, args.warmup, kl=True)
+    if "prefill_128k_backward" in extras:
+        print("[bench] prefill 128k varlen backward", file=sys.stderr, flush=True)
+        mark("prefill_128k_backward")
+        extra["prefill_128k_backward"] = backward_bench(msa, 3, max(2, args.steps // 2), 1)
     if "warmup_32k" in extras:
         print("[bench] warm-up mode 32k: dense forward and backward with the proxy gradient", file=sys.stderr,
               flush=True)

@@ -163,6 +163,12 @@ def test_prefill_32k_backward():
     _backward_case(2, 48)
 
 
+def test_prefill_varlen_128k_backward():
+    """Four sequences, G = 8 and four 32768-row attention windows: dk and dv
+    accumulate across windows."""
+    _backward_case(3, 24)
+
+
 def _check_sum_zero(name, grad, kvi, lay, scale):
     """Per sequence and head, the gradient rows of a sequence's keys sum to
     zero (up to fp32 accumulation, relative to the sum of magnitudes)."""
