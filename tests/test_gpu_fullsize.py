@@ -286,7 +286,7 @@ def test_warmup_32k():
     for r in range(T):
         allsel[r, :, :lay.local(r) + 1] = np.arange(lay.local(r) + 1)
     rng = np.random.default_rng(seed_of(2) + 6)
-    rows = _sample_rows(w, 8, seed_of(2))
+    rows = _sample_rows(w, 4, seed_of(2))
     print(f"[fullsize] oracle dense forward on {rows.size} rows", flush=True)
     ref, ref_lse = O.sparse_attention(h["q"], h["k_pages"], h["v_pages"], h["kv_indices"], allsel, w.qo_lens,
                                       w.kv_lens, 128, w.sm_scale, rows=rows)
@@ -305,7 +305,10 @@ def test_warmup_32k():
                                          groups=groups)
     _check(f"{w.name} warm-up dproxy_q", dpq[tr].cpu().numpy().astype(np.float64)[:, groups], rpq[rows][:, groups])
     assert np.abs(plse[tr].cpu().numpy()[:, groups] - rpl[rows][:, groups]).max() < 1e-3
-    for gg, b in _late_blocks(lay, rng, Hkv):
+    # every visible row reaches a block here (dense), so the checked blocks are
+    # the last (the diagonal block alone) and the one before it
+    nb0 = lay.nb[0]
+    for gg, b in ((0, nb0 - 1), (int(rng.integers(1, Hkv)), nb0 - 2)):
         see = np.nonzero((np.arange(T) < lay.row_start[1]) &
                          (np.array([lay.pos(int(r)) for r in range(T)]) >= 128 * b))[0]
         print(f"[fullsize] oracle dk, dv, dproxy_k of group {gg} block {b}: {see.size} rows", flush=True)
