@@ -193,10 +193,14 @@ __device__ __forceinline__ f32x16 mma(const typename ProxyTraits<F>::AFrag& a,
   }
 }
 
-constexpr int kProxyWaves = 8;
+// 4 waves of 64 rows: a workgroup covers half of a 512-row plan tile, so two
+// workgroups (2 waves per SIMD each) share a CU and one's per-block barrier
+// or K fetch overlaps the other's MFMAs
+constexpr int kProxyWaves = 4;
+constexpr int kProxySubs = 512 / (64 * kProxyWaves);
 
 template <Fmt F, bool TOPK>
-__global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyArgs a) {
+__global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(ProxyArgs a) {
   using Tr = ProxyTraits<F>;
   using AFrag = typename Tr::AFrag;
   using BFrag = typename Tr::BFrag;
@@ -216,11 +220,14 @@ __global__ __launch_bounds__(64 * kProxyWaves) void proxy_maxscore_kernel(ProxyA
   const int hsel = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave branches stay scalar
   const int p = blockIdx.x % a.P;
-  const int t = a.tile_lo + (a.ntiles - 1 - (int)(blockIdx.x / a.P));
+  const int qi = (int)(blockIdx.x / a.P);
+  const int t = a.tile_lo + (a.ntiles - 1 - qi / kProxySubs);   // long tiles first
+  const int part = kProxySubs - 1 - qi % kProxySubs;            // and their later rows first
   const int seq = a.tiles[4 * t + 0];
-  const int row0 = a.tiles[4 * t + 1];
-  const int nrows = a.tiles[4 * t + 2];
-  const int pos0 = a.tiles[4 * t + 3];
+  const int row0 = a.tiles[4 * t + 1] + 64 * kProxyWaves * part;
+  const int nrows = min(64 * kProxyWaves, a.tiles[4 * t + 2] - 64 * kProxyWaves * part);
+  if (nrows <= 0) return;
+  const int pos0 = a.tiles[4 * t + 3] + 64 * kProxyWaves * part;
   const int ph = (a.Pk == a.P) ? p : 0;
   const int32_t* pages = a.kv_indices + a.page_start[seq];
   const int b_last = (pos0 + nrows - 1) >> 7;
@@ -703,7 +710,7 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
   a.sel = sel;
   a.k = p->d.topk;
   a.scale = p->d.proxy_sm_scale;
-  const dim3 grid((unsigned)(a.ntiles * a.P)), block(64 * kProxyWaves);
+  const dim3 grid((unsigned)(a.ntiles * kProxySubs * a.P)), block(64 * kProxyWaves);
   ProfEvents pe(p, sel ? "proxy_topk" : "proxy_maxscore");
   auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, grid, block, 0, st, pe.start, pe.stop, 0, a); };
   switch (p->d.proxy_dtype) {
