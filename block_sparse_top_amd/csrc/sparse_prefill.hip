@@ -406,10 +406,12 @@ struct MergeArgs {
   int32_t Hq, Hkv, G, k, w0, w1;
 };
 
-// 16 lanes per (row, head), 8 output columns per lane.  Lane j of the 16
-// reads slot j's block id and log-sum-exp (coalesced), the group's max and
-// weights move by shuffles, and every partial row is read as 16-byte loads
-// (one 256-byte segment per 16 lanes), 16 slots at a time.  topk <= 64.
+// 16 lanes per (row, head), 8 output columns per lane.  Every partial row is
+// read as 16-byte loads (one 256-byte segment per 16 lanes), 16 slots at a
+// time, the first 16 issued before anything else; lane j of the 16 reads
+// slot j's block id and log-sum-exp (coalesced), the row's local block then
+// says which slots count, and the group's max and weights move by shuffles.
+// topk <= 64.
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int sub = threadIdx.x & 15;
   const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -419,23 +421,33 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int h = (int)(id % a.Hq);
   const int g = h / a.G;
   const int32_t r = a.w0 + rl;
+  const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
+  // the first 16 slots' partials depend on nothing else: issued before the
+  // row's sequence, selection and log-sum-exps are looked up
+  i32x4 v0[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    v0[j] = *reinterpret_cast<const i32x4*>(a.part_o + (base + min(j, a.k - 1)) * 128 + 8 * sub);
+  const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
+  const int ngroups = (a.k + 15) >> 4;
+  // lane sub's slot of each group of 16: block id and log-sum-exp, loaded
+  // before the row's local block is known (a slot counts when 0 <= b <= local)
+  int b_g[4];
+  float lse_g[4];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const int slot = min(16 * gi + sub, a.k - 1);
+    const bool in = gi < ngroups && 16 * gi + sub < a.k;
+    b_g[gi] = in ? row[slot] : -1;
+    lse_g[gi] = in ? a.part_lse[base + slot] : kNegInf;
+  }
   const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
   const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
-  const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
-  const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
-  const int ngroups = (a.k + 15) >> 4;
-  float lse_g[4];
   float M = kNegInf;
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
-    const int slot = 16 * gi + sub;
-    float l = kNegInf;
-    if (gi < ngroups && slot < a.k) {
-      const int b = row[slot];
-      if (b >= 0 && b <= local) l = a.part_lse[base + slot];
-    }
-    lse_g[gi] = l;
-    M = fmaxf(M, l);
+    if (!(b_g[gi] >= 0 && b_g[gi] <= local)) lse_g[gi] = kNegInf;   // never written: not read into the result
+    M = fmaxf(M, lse_g[gi]);
   }
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
@@ -448,7 +460,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     for (int j = 0; j < 16; ++j) {
       w[j] = __shfl(wl, j, 16);
       const int slot = min(16 * gi + j, a.k - 1);
-      v[j] = *reinterpret_cast<const i32x4*>(a.part_o + (base + slot) * 128 + 8 * sub);
+      v[j] = gi == 0 ? v0[j] : *reinterpret_cast<const i32x4*>(a.part_o + (base + slot) * 128 + 8 * sub);
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -986,19 +998,29 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(DqSumArgs a) {
   const int h = (int)(idx % a.Hq);
   const int g = h / a.G;
   const int32_t r = a.w0 + rl;
-  const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
-  const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
-  const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
+  const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int slot = 0; slot < a.k; ++slot) {
-    const int bk = row[slot];
-    if (bk < 0 || bk > local) continue;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(a.part + (base + slot) * 128 + 8 * sub);
+  // 16 slots at a time: the partials are loaded before the selection says
+  // which of them count (slots past topk repeat the last one)
+  for (int s0 = 0; s0 < a.k; s0 += 16) {
+    i32x4 v[16];
+    int bk[16];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      o[2 * x] += __builtin_bit_cast(float, (uint32_t)v[x] << 16);
-      o[2 * x + 1] += __builtin_bit_cast(float, (uint32_t)v[x] & 0xffff0000u);
+    for (int j = 0; j < 16; ++j)
+      v[j] = *reinterpret_cast<const i32x4*>(a.part + (base + min(s0 + j, a.k - 1)) * 128 + 8 * sub);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bk[j] = s0 + j < a.k ? row[s0 + j] : -1;
+    const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
+    const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (bk[j] < 0 || bk[j] > local) continue;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        o[2 * x] += __builtin_bit_cast(float, (uint32_t)v[j][x] << 16);
+        o[2 * x + 1] += __builtin_bit_cast(float, (uint32_t)v[j][x] & 0xffff0000u);
+      }
     }
   }
   float* dst = a.dq + ((int64_t)r * a.Hq + h) * 128 + 8 * sub;
