@@ -152,7 +152,9 @@ __device__ __forceinline__ bf16x8 join_tr16(const s16x4& lo, const s16x4& hi) {
 // permutations, row mirrors) within each 16-lane row.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  // every lane's source exists for these controls; the update form (old 0,
+  // bound_ctrl) lets the compiler fold the move into the consuming add
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // K and V sit in LDS as unpadded 256-byte rows whose 16-byte chunks are
