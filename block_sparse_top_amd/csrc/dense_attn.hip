@@ -65,9 +65,11 @@ struct DenseFwdArgs {
   float scale_log2;
 };
 
-__global__ __launch_bounds__(256) void dense_fwd_kernel(DenseFwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2][128 * 256];   // K, k_swz: S^T operand
-  __shared__ __attribute__((aligned(16))) uint8_t vt[2][128 * 256];   // V, v_swz: transposed reads
+__global__ __launch_bounds__(256, 2) void dense_fwd_kernel(DenseFwdArgs a) {
+  // one K and one V tile (64 KB): two workgroups share a CU, and one's block
+  // loads overlap the other's MFMAs
+  __shared__ __attribute__((aligned(16))) uint8_t ks[1][128 * 256];   // K, k_swz: S^T operand
+  __shared__ __attribute__((aligned(16))) uint8_t vt[1][128 * 256];   // V, v_swz: transposed reads
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, j = lane & 31;
@@ -112,12 +114,12 @@ __global__ __launch_bounds__(256) void dense_fwd_kernel(DenseFwdArgs a) {
   };
   float mrun = -INFINITY, lrun = 0.f;
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  load_blk(0);
   for (int b = 0; b < nblk; ++b) {
-    const int buf = b & 1;
+    const int buf = 0;
+    load_blk(b);
+    __syncthreads();   // every wave is done with the previous block's tiles
     store_blk(b, buf);
-    if (b + 1 < nblk) load_blk(b + 1);
-    lds_barrier();
+    __syncthreads();
     // S^T = K Q^T: register i of tile kt_ holds key 32 kt_ + 8 (i / 4) + 4 half + i % 4
     f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
 #pragma unroll
