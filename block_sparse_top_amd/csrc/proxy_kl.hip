@@ -37,9 +37,11 @@ struct KlDqArgs {
   float scale_log2, out_scale;
 };
 
-__global__ __launch_bounds__(256) void kl_dense_dq_kernel(KlDqArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2][128 * 256];   // proxy K, k_swz: S^T operand
-  __shared__ __attribute__((aligned(16))) uint8_t kt[2][128 * 256];   // proxy K, v_swz: transposed reads
+__global__ __launch_bounds__(256, 2) void kl_dense_dq_kernel(KlDqArgs a) {
+  // one tile of each (64 KB): two workgroups share a CU, and one's block
+  // loads overlap the other's MFMAs
+  __shared__ __attribute__((aligned(16))) uint8_t ks[1][128 * 256];   // proxy K, k_swz: S^T operand
+  __shared__ __attribute__((aligned(16))) uint8_t kt[1][128 * 256];   // proxy K, v_swz: transposed reads
   const int p = blockIdx.y;
   const int qi = (int)gridDim.x - 1 - (int)blockIdx.x;   // later quarters (more keys) start first
   const int t = qi >> 2, sub = qi & 3;
@@ -114,12 +116,12 @@ __global__ __launch_bounds__(256) void kl_dense_dq_kernel(KlDqArgs a) {
   // and dQ^T += K^T P^T; the row's sum of P gives its log-sum-exp at the end.
   float mrun = -INFINITY, lrun = 0.f;   // lrun: this lane's half of the row
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  load_blk(0);
   for (int b = 0; b < nblk; ++b) {
-    const int buf = b & 1;
+    const int buf = 0;
+    load_blk(b);
+    __syncthreads();   // every wave is done with the previous block's tiles
     store_blk(b, buf, true);
-    if (b + 1 < nblk) load_blk(b + 1);
-    lds_barrier();
+    __syncthreads();
     f32x16 acc[4];
     scores(b, buf, acc);
     float bm = -INFINITY;
