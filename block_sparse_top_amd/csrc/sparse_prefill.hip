@@ -247,6 +247,19 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   for (int dt = 0; dt < 4; ++dt)
     vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  // transposed reads of the k_swz tile: lane (q16, m16) fetches dims
+  // 32 dt + 16 (q16 & 1) + 4 (m16 & 3) .. +3 of key row r0 (lo) or r0 + 8
+  // (hi), r0 = 4 (q16 >> 1) + m16 / 4 (+ the 16-row offsets of the reads)
+  int ktlo[4], kthi[4];
+  {
+    const int r0 = 4 * (q16 >> 1) + (m16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int c = 4 * dt + 2 * (q16 & 1) + ((m16 & 3) >> 1);
+      ktlo[dt] = r0 * 256 + ((c ^ r0) << 4) + 8 * (m16 & 1);
+      kthi[dt] = (r0 + 8) * 256 + ((c ^ (r0 + 8)) << 4) + 8 * (m16 & 1);
+    }
+  }
   uint8_t* ow = ost + wave * kOStage;
 
   // Q fragments (B operand) of a chunk's row for this lane: gathered rows
@@ -733,10 +746,13 @@ struct BwdDqArgs {
   float inv_g;
 };
 
+// K sits in LDS once (k_swz): read directly as the S^T operand and with
+// transposed reads (addresses ktlo / kthi below) as K^T; each 128-key block is
+// taken in two 64-key halves, so that the plain variant fits two workgroups
+// per CU (74 KB of LDS, 256 registers).
 template <bool KL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz: S^T operand
-  __shared__ __attribute__((aligned(16))) uint8_t kt[128 * 256];   // K, v_swz: transposed reads (K^T)
+__global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz: S^T operand and K^T reads
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, k_swz: dP^T operand
   __shared__ __attribute__((aligned(16))) uint8_t pkt[KL ? 128 * 256 : 16];   // proxy K, v_swz
   __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
@@ -752,7 +768,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
   const int32_t first_pos = a.m.kv[s] - a.m.qo[s];
   const int32_t rs = a.m.row_start[s];
   const int n_ent = e1 - e0;
-  {  // K (twice) and V -> LDS; padding rows (past kv_len) zeroed: dS and P are 0 there but 0 * NaN is NaN
+  {  // K and V -> LDS; padding rows (past kv_len) zeroed: dS and P are 0 there but 0 * NaN is NaN
     const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * 32768;
     const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * 32768;
     i32x4 kr[8], vr[8];
@@ -768,8 +784,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
     for (int i = 0; i < 8; ++i) {
       const int c = tid + 256 * i;
       const bool live_row = (c >> 4) < kv_in_block;
-      lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], kr[i]);
-      lds_store16<i32x4>(&kt[v_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
+      lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
       lds_store16<i32x4>(&vs[k_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
     }
     if constexpr (KL) {
@@ -801,6 +816,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
   for (int dt = 0; dt < 4; ++dt)
     vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  // transposed reads of the k_swz tile: lane (q16, m16) fetches dims
+  // 32 dt + 16 (q16 & 1) + 4 (m16 & 3) .. +3 of key row r0 (lo) or r0 + 8
+  // (hi), r0 = 4 (q16 >> 1) + m16 / 4 (+ the 16-row offsets of the reads)
+  int ktlo[4], kthi[4];
+  {
+    const int r0 = 4 * (q16 >> 1) + (m16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int c = 4 * dt + 2 * (q16 & 1) + ((m16 & 3) >> 1);
+      ktlo[dt] = r0 * 256 + ((c ^ r0) << 4) + 8 * (m16 & 1);
+      kthi[dt] = (r0 + 8) * 256 + ((c ^ (r0 + 8)) << 4) + 8 * (m16 & 1);
+    }
+  }
   uint8_t* ow = ost + wave * kOStage;
 
   // The row of a chunk: padding rows (past the item's entries) repeat a real
@@ -833,65 +861,83 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
     const int ent_next = entry_at(chunk + 1);
     l2 = a.lse[(int64_t)(a.w0 + (ent_next >> 6)) * a.Hq + h];
     dval = a.D[(int64_t)(ent_next >> 6) * a.Hq + h];
-    // S^T = K Q^T, then P^T in place (hidden keys: -inf -> 0)
-    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-#pragma unroll
-    for (int st = 0; st < 8; ++st)
-#pragma unroll
-      for (int kt_ = 0; kt_ < 4; ++kt_) acc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&ks[kbase[st] + 8192 * kt_]), qf[st], acc[kt_]);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(q_ptr(a.q, ent_next) + st * 32);
     const int lim = pos - b * 128 - 4 * half;
+    f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    f32x16 kacc[KL ? 4 : 1];
 #pragma unroll
-    for (int kt_ = 0; kt_ < 4; ++kt_)
+    for (int dt = 0; dt < (KL ? 4 : 1); ++dt) kacc[dt] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float ex = fast_exp2(__builtin_fmaf(acc[kt_][i], a.scale_log2, -l2c));
-        acc[kt_][i] = (32 * kt_ + 8 * (i >> 2) + (i & 3)) <= lim ? ex : 0.f;
+    for (int kh = 0; kh < 2; ++kh) {   // keys 64 kh .. 64 kh + 63
+      // S^T = K Q^T, then P^T in place (hidden keys: -inf -> 0)
+      f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t] = mfma32x32x16(lds_load16<bf16x8>(&ks[kbase[st] + 8192 * (2 * kh + t)]), qf[st], acc[t]);
+      if (kh == 1) {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(q_ptr(a.q, ent_next) + st * 32);
       }
-    // dP^T = V dO^T
-    f32x16 dacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kt_ = 0; kt_ < 4; ++kt_) dacc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&vs[kbase[st] + 8192 * kt_]), df[st], dacc[kt_]);
+        for (int i = 0; i < 16; ++i) {
+          const float ex = fast_exp2(__builtin_fmaf(acc[t][i], a.scale_log2, -l2c));
+          acc[t][i] = (32 * (2 * kh + t) + 8 * (i >> 2) + (i & 3)) <= lim ? ex : 0.f;
+        }
+      // dP^T = V dO^T
+      f32x16 dacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int st = 0; st < 8; ++st) df[st] = *reinterpret_cast<const bf16x8*>(q_ptr(a.dout, ent_next) + st * 32);
-    // dS^T = P^T (dP^T - D) as bf16 B operands (and P^T itself for the proxy term)
-    bf16x8 sf[4][2], pfk[KL ? 4 : 1][2];
+      for (int st = 0; st < 8; ++st)
 #pragma unroll
-    for (int kt_ = 0; kt_ < 4; ++kt_)
+        for (int t = 0; t < 2; ++t)
+          dacc[t] = mfma32x32x16(lds_load16<bf16x8>(&vs[kbase[st] + 8192 * (2 * kh + t)]), df[st], dacc[t]);
+      if (kh == 1) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        i32x4 pw, qw;
+        for (int st = 0; st < 8; ++st) df[st] = *reinterpret_cast<const bf16x8*>(q_ptr(a.dout, ent_next) + st * 32);
+      }
+      // dS^T = P^T (dP^T - D) as bf16 B operands (and P^T itself for the proxy term)
+      bf16x8 sf[2][2], pfk[KL ? 2 : 1][2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int i0 = 8 * u + 2 * t;
-          const bf16x2 two = {(__bf16)(acc[kt_][i0] * (dacc[kt_][i0] - dvc)),
-                              (__bf16)(acc[kt_][i0 + 1] * (dacc[kt_][i0 + 1] - dvc))};
-          pw[t] = __builtin_bit_cast(int, two);
-          if constexpr (KL) {
-            const bf16x2 pp = {(__bf16)acc[kt_][i0], (__bf16)acc[kt_][i0 + 1]};
-            qw[t] = __builtin_bit_cast(int, pp);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          i32x4 pw, qw;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int i0 = 8 * u + 2 * x;
+            const bf16x2 two = {(__bf16)(acc[t][i0] * (dacc[t][i0] - dvc)),
+                                (__bf16)(acc[t][i0 + 1] * (dacc[t][i0 + 1] - dvc))};
+            pw[x] = __builtin_bit_cast(int, two);
+            if constexpr (KL) {
+              const bf16x2 pp = {(__bf16)acc[t][i0], (__bf16)acc[t][i0 + 1]};
+              qw[x] = __builtin_bit_cast(int, pp);
+            }
+          }
+          sf[t][u] = __builtin_bit_cast(bf16x8, pw);
+          if constexpr (KL) pfk[t][u] = __builtin_bit_cast(bf16x8, qw);
+        }
+      // dQ^T += K^T dS^T (and pk^T P^T for the proxy term)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int ro = 256 * 32 * (2 * kh + t);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const s16x4 lo = lds_read_tr16(&ks[ktlo[dt] + ro + 256 * 16 * u]);
+            const s16x4 hi = lds_read_tr16(&ks[kthi[dt] + ro + 256 * 16 * u]);
+            oacc[dt] = mfma32x32x16(join_tr16(lo, hi), sf[t][u], oacc[dt]);
+            if constexpr (KL) {
+              const s16x4 plo = lds_read_tr16(&pkt[vbase[dt] + ro + 256 * 16 * u]);
+              const s16x4 phi = lds_read_tr16(&pkt[vbase[dt] + ro + 256 * (16 * u + 8)]);
+              kacc[dt] = mfma32x32x16(join_tr16(plo, phi), pfk[t][u], kacc[dt]);
+            }
           }
         }
-        sf[kt_][u] = __builtin_bit_cast(bf16x8, pw);
-        if constexpr (KL) pfk[kt_][u] = __builtin_bit_cast(bf16x8, qw);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    // dQ^T = K^T dS^T
-    f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kt_ = 0; kt_ < 4; ++kt_) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const s16x4 lo = lds_read_tr16(&kt[vbase[dt] + 256 * (32 * kt_ + 16 * u)]);
-          const s16x4 hi = lds_read_tr16(&kt[vbase[dt] + 256 * (32 * kt_ + 16 * u + 8)]);
-          oacc[dt] = mfma32x32x16(join_tr16(lo, hi), sf[kt_][u], oacc[dt]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
     // scaled bf16 partial through the wave's staging area (as the forward's output)
     int64_t spi[2];
@@ -923,23 +969,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdDqArgs a) {
       wave_lds_sync();
     }
     if constexpr (KL) {
-      // sum_j P_hj pk_j for this wave's rows: C[dim][row] = pk^T P^T, then the
-      // sum over a token's G heads (adjacent lanes) and one bf16 store per
-      // (token, slot) from the token's first lane
-      f32x16 kacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kt_ = 0; kt_ < 4; ++kt_) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const s16x4 lo = lds_read_tr16(&pkt[vbase[dt] + 256 * (32 * kt_ + 16 * u)]);
-            const s16x4 hi = lds_read_tr16(&pkt[vbase[dt] + 256 * (32 * kt_ + 16 * u + 8)]);
-            kacc[dt] = mfma32x32x16(join_tr16(lo, hi), pfk[kt_][u], kacc[dt]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      // sum_j P_hj pk_j for this wave's rows (kacc: C[dim][row] = pk^T P^T),
+      // summed over a token's G heads (adjacent lanes); one bf16 store per
+      // (token, slot) from the token's first lane.
       // G is a power of two up to 16 and a token's heads sit in G aligned
       // lanes of a 16-lane row: xor 1 and xor 2 (quad permutations) leave
       // every lane its pair and then quad sum; once each quad holds one value,
