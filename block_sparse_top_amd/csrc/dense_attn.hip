@@ -218,10 +218,14 @@ struct DenseDqArgs {
   float inv_g;
 };
 
+// K sits in LDS once (k_swz), read directly for S^T and transposed for K^T;
+// blocks are taken in two 64-key halves.  The plain variant loads each block
+// straight into LDS and fits two workgroups per CU (64 KB, 256 registers),
+// whose block loads overlap each other's MFMAs; with the proxy term (96 KB)
+// one workgroup per CU prefetches the next block into registers instead.
 template <bool KL>
-__global__ __launch_bounds__(256) void dense_dq_kernel(DenseDqArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz: S^T operand
-  __shared__ __attribute__((aligned(16))) uint8_t kt[128 * 256];   // K, v_swz: K^T reads
+__global__ __launch_bounds__(256, KL ? 1 : 2) void dense_dq_kernel(DenseDqArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz: S^T operand and K^T reads
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, k_swz: dP^T operand
   __shared__ __attribute__((aligned(16))) uint8_t pkt[KL ? 128 * 256 : 16];   // proxy K, v_swz
   const int g = blockIdx.y;
@@ -253,6 +257,18 @@ __global__ __launch_bounds__(256) void dense_dq_kernel(DenseDqArgs a) {
   for (int dt = 0; dt < 4; ++dt)
     vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  // transposed reads of the k_swz tile: lane (q16, m16) fetches dims
+  // 32 dt + 16 (q16 & 1) + 4 (m16 & 3) .. +3 of key row r0 (lo) or r0 + 8 (hi)
+  int ktlo[4], kthi[4];
+  {
+    const int r0 = 4 * (q16 >> 1) + (m16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int c = 4 * dt + 2 * (q16 & 1) + ((m16 & 3) >> 1);
+      ktlo[dt] = r0 * 256 + ((c ^ r0) << 4) + 8 * (m16 & 1);
+      kthi[dt] = (r0 + 8) * 256 + ((c ^ (r0 + 8)) << 4) + 8 * (m16 & 1);
+    }
+  }
   i32x4 kr[8], vr[8], pr[KL ? 8 : 1];
   auto load_blk = [&](int b) {
     const int64_t off = ((int64_t)pages[b] * a.Hkv + g) * 32768;
@@ -267,8 +283,9 @@ __global__ __launch_bounds__(256) void dense_dq_kernel(DenseDqArgs a) {
   f32x16 kacc[KL ? 4 : 1];
 #pragma unroll
   for (int dt = 0; dt < (KL ? 4 : 1); ++dt) kacc[dt] = f32x16{};
-  load_blk(0);
+  if constexpr (KL) load_blk(0);
   for (int b = 0; b < nblk; ++b) {
+    if constexpr (!KL) load_blk(b);
     __syncthreads();   // the previous block's tiles are no longer read
     {
       const int kv_in_block = kv_len - 128 * b;   // rows past kv_len zeroed
@@ -277,75 +294,82 @@ __global__ __launch_bounds__(256) void dense_dq_kernel(DenseDqArgs a) {
         const int c = tid + 256 * i;
         const bool live_row = (c >> 4) < kv_in_block;
         lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
-        lds_store16<i32x4>(&kt[v_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
         lds_store16<i32x4>(&vs[k_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
         if constexpr (KL) lds_store16<i32x4>(&pkt[v_swz(c >> 4, c & 15)], live_row ? pr[i] : i32x4{});
       }
     }
-    if (b + 1 < nblk) load_blk(b + 1);
-    lds_barrier();
-    // S^T = K Q^T, then P^T in place (hidden keys 0)
-    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-#pragma unroll
-    for (int st = 0; st < 8; ++st)
-#pragma unroll
-      for (int kt_ = 0; kt_ < 4; ++kt_)
-        acc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&ks[kbase[st] + 8192 * kt_]), qf[st], acc[kt_]);
+    if constexpr (KL) {
+      if (b + 1 < nblk) load_blk(b + 1);
+      lds_barrier();
+    } else {
+      __syncthreads();
+    }
     const int lim = d.pos - b * 128 - 4 * half;
     const bool all_visible = b * 128 + 127 <= d.pos0;
 #pragma unroll
-    for (int kt_ = 0; kt_ < 4; ++kt_)
+    for (int kh = 0; kh < 2; ++kh) {   // keys 64 kh .. 64 kh + 63
+      // S^T = K Q^T, then P^T in place (hidden keys 0)
+      f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float ex = fast_exp2(__builtin_fmaf(acc[kt_][i], a.scale_log2, -l2));
-        acc[kt_][i] = all_visible || (32 * kt_ + 8 * (i >> 2) + (i & 3)) <= lim ? ex : 0.f;
-      }
-    // dP^T = V dO^T
-    f32x16 dacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+      for (int st = 0; st < 8; ++st)
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+        for (int t = 0; t < 2; ++t)
+          acc[t] = mfma32x32x16(lds_load16<bf16x8>(&ks[kbase[st] + 8192 * (2 * kh + t)]), qf[st], acc[t]);
 #pragma unroll
-      for (int kt_ = 0; kt_ < 4; ++kt_)
-        dacc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&vs[kbase[st] + 8192 * kt_]), df[st], dacc[kt_]);
-    // dS^T = P^T (dP^T - D) as bf16 B operands (and P^T itself for the proxy term)
-    bf16x8 sf[4][2], pfk[KL ? 4 : 1][2];
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int kt_ = 0; kt_ < 4; ++kt_)
+        for (int i = 0; i < 16; ++i) {
+          const float ex = fast_exp2(__builtin_fmaf(acc[t][i], a.scale_log2, -l2));
+          acc[t][i] = all_visible || (32 * (2 * kh + t) + 8 * (i >> 2) + (i & 3)) <= lim ? ex : 0.f;
+        }
+      // dP^T = V dO^T
+      f32x16 dacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        i32x4 pw, qw;
+      for (int st = 0; st < 8; ++st)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int i0 = 8 * u + 2 * tt;
-          const bf16x2 two = {(__bf16)(acc[kt_][i0] * (dacc[kt_][i0] - dval)),
-                              (__bf16)(acc[kt_][i0 + 1] * (dacc[kt_][i0 + 1] - dval))};
-          pw[tt] = __builtin_bit_cast(int, two);
-          if constexpr (KL) {
-            const bf16x2 pp = {(__bf16)acc[kt_][i0], (__bf16)acc[kt_][i0 + 1]};
-            qw[tt] = __builtin_bit_cast(int, pp);
+        for (int t = 0; t < 2; ++t)
+          dacc[t] = mfma32x32x16(lds_load16<bf16x8>(&vs[kbase[st] + 8192 * (2 * kh + t)]), df[st], dacc[t]);
+      // dS^T = P^T (dP^T - D) as bf16 B operands (and P^T itself for the proxy term)
+      bf16x8 sf[2][2], pfk[KL ? 2 : 1][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          i32x4 pw, qw;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const int i0 = 8 * u + 2 * tt;
+            const bf16x2 two = {(__bf16)(acc[t][i0] * (dacc[t][i0] - dval)),
+                                (__bf16)(acc[t][i0 + 1] * (dacc[t][i0 + 1] - dval))};
+            pw[tt] = __builtin_bit_cast(int, two);
+            if constexpr (KL) {
+              const bf16x2 pp = {(__bf16)acc[t][i0], (__bf16)acc[t][i0 + 1]};
+              qw[tt] = __builtin_bit_cast(int, pp);
+            }
+          }
+          sf[t][u] = __builtin_bit_cast(bf16x8, pw);
+          if constexpr (KL) pfk[t][u] = __builtin_bit_cast(bf16x8, qw);
+        }
+      // dQ^T += K^T dS^T (and pk^T P^T)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int ro = 256 * 32 * (2 * kh + t);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const s16x4 lo4 = lds_read_tr16(&ks[ktlo[dt] + ro + 256 * 16 * u]);
+            const s16x4 hi4 = lds_read_tr16(&ks[kthi[dt] + ro + 256 * 16 * u]);
+            oacc[dt] = mfma32x32x16(join_tr16(lo4, hi4), sf[t][u], oacc[dt]);
+            if constexpr (KL) {
+              const s16x4 plo = lds_read_tr16(&pkt[vbase[dt] + ro + 256 * 16 * u]);
+              const s16x4 phi = lds_read_tr16(&pkt[vbase[dt] + ro + 256 * (16 * u + 8)]);
+              kacc[dt] = mfma32x32x16(join_tr16(plo, phi), pfk[t][u], kacc[dt]);
+            }
           }
         }
-        sf[kt_][u] = __builtin_bit_cast(bf16x8, pw);
-        if constexpr (KL) pfk[kt_][u] = __builtin_bit_cast(bf16x8, qw);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    // dQ^T += K^T dS^T (and pk^T P^T)
-#pragma unroll
-    for (int kt_ = 0; kt_ < 4; ++kt_) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const s16x4 lo4 = lds_read_tr16(&kt[vbase[dt] + 256 * (32 * kt_ + 16 * u)]);
-          const s16x4 hi4 = lds_read_tr16(&kt[vbase[dt] + 256 * (32 * kt_ + 16 * u + 8)]);
-          oacc[dt] = mfma32x32x16(join_tr16(lo4, hi4), sf[kt_][u], oacc[dt]);
-          if constexpr (KL) {
-            const s16x4 plo = lds_read_tr16(&pkt[vbase[dt] + 256 * (32 * kt_ + 16 * u)]);
-            const s16x4 phi = lds_read_tr16(&pkt[vbase[dt] + 256 * (32 * kt_ + 16 * u + 8)]);
-            kacc[dt] = mfma32x32x16(join_tr16(plo, phi), pfk[kt_][u], kacc[dt]);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (d.live) {
