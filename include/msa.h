@@ -244,6 +244,10 @@ msa_status_t msa_sparse_attn_prefill_rows(msa_plan_t plan, const void* q, const 
  *   dk_pages, dv_pages fp32 [num_pages, H_kv, 128, 128]: every (page, head)
  *                     that holds a block of some sequence is written (0 where
  *                     no row attends to it); other pages are not touched
+ * Results are bit-reproducible when the plan's attention window is at most
+ * 65536 rows (the default window is): the rows that selected a block are then
+ * summed in ascending row order for dk/dv, and the per-slot dq partials in
+ * slot order.
  * Errors: INVALID_ARG for null or misaligned pointers; UNSUPPORTED for a
  * decode plan or non-bf16 K/V; WORKSPACE_TOO_SMALL. */
 msa_status_t msa_sparse_attn_prefill_backward(msa_plan_t plan, const void* q, const void* k_pages,
