@@ -378,7 +378,8 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       for (int pass = 0; pass < 2; ++pass) {
         const int r = 16 * pass + (lane >> 2), c = lane & 3;
         const i32x4 v = lds_load16<i32x4>(&ow[r * 64 + ((c ^ ((r >> 2) & 3)) << 4)]);
-        *reinterpret_cast<i32x4*>(a.part_o + spi[pass] * 128 + 32 * dt + 8 * c) = v;
+        // streamed out, read once by the merge: non-temporal
+        __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(a.part_o + spi[pass] * 128 + 32 * dt + 8 * c));
       }
       wave_lds_sync();
     }
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   i32x4 v0[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    v0[j] = *reinterpret_cast<const i32x4*>(a.part_o + (base + min(j, a.k - 1)) * 128 + 8 * sub);
+    v0[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(a.part_o + (base + min(j, a.k - 1)) * 128 + 8 * sub));
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   const int ngroups = (a.k + 15) >> 4;
   // lane sub's slot of each group of 16: block id and log-sum-exp, loaded
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     for (int j = 0; j < 16; ++j) {
       w[j] = __shfl(wl, j, 16);
       const int slot = min(16 * gi + j, a.k - 1);
-      v[j] = gi == 0 ? v0[j] : *reinterpret_cast<const i32x4*>(a.part_o + (base + slot) * 128 + 8 * sub);
+      v[j] = gi == 0 ? v0[j] : __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(a.part_o + (base + slot) * 128 + 8 * sub));
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
