@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const bf16x2 t = {(__bf16)(o[2 * j] * inv), (__bf16)(o[2 * j + 1] * inv)};
     packed[j] = __builtin_bit_cast(int, t);
   }
-  *reinterpret_cast<i32x4*>(a.out + ((int64_t)r * a.Hq + h) * 128 + 8 * sub) = packed;
+  __builtin_nontemporal_store(packed, reinterpret_cast<i32x4*>(a.out + ((int64_t)r * a.Hq + h) * 128 + 8 * sub));
   if (a.lse && sub == 0) a.lse[(int64_t)r * a.Hq + h] = M + fast_log2(L) * kLn2;
 }
 
