@@ -254,18 +254,23 @@ def time_steps(step, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def kernel_profile(msa, plan, step, names):
-    """Per-kernel total ms over one step (each kernel in its own step)."""
+def kernel_profile(msa, plan, step, names, reps=3):
+    """Per-kernel total ms per step, averaged over `reps` steps.  Two
+    unprofiled steps are queued first so that the profiled ones start on a
+    busy GPU (after an idle gap the first kernel of a step runs slower)."""
     import torch
     out = {}
     for n in names:
-        msa.msa_profile_kernel(plan, n)
         step()
+        step()
+        msa.msa_profile_kernel(plan, n)
+        for _ in range(reps):
+            step()
         torch.cuda.synchronize()
         ms, cnt = msa.msa_profile_read(plan)
         msa.msa_profile_kernel(plan, None)
         if cnt:
-            out[n] = (ms, cnt)
+            out[n] = (ms / reps, cnt // reps)
     return out
 
 
