@@ -162,7 +162,7 @@ struct PartialArgs {
 };
 
 constexpr int kMaxItemEntries = 512;   // entries_per_item = min(512, 16 chunks of 128 / G tokens)
-constexpr int kOStage = 32 * 64;       // output staging per wave: 32 rows x 32 bf16 columns
+constexpr int kOStage = 32 * 64;       // output staging per wave, 2 KB: 32 rows x 64 B or 16 rows x 128 B
 
 // Eight K/V elements of key row `row`, dims 8 col .. 8 col + 7, as bf16
 // (exact) from a page of format F.
@@ -347,41 +347,56 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of transposed reads
     }
-    // Output: each 32 x 32 tile of O (this wave's rows, 32 columns) goes
-    // through the wave's LDS staging area so that every store instruction
-    // writes 16 rows x 64 contiguous bytes.  Staged row j holds its 4 16-byte
-    // chunks at c ^ ((j >> 2) & 3): the 8-byte writes of a tile land on every
-    // bank exactly twice.
+    // Output: O goes through the wave's LDS staging area 16 rows x 128 bytes
+    // at a time (two 32-column tiles, 16 of the wave's rows), so that every
+    // store instruction writes 8 partial rows x 128 contiguous bytes: whole
+    // 128-byte lines.  The stores are non-temporal (the merge reads each
+    // partial once), and a line written in pieces would leave memory as
+    // several partial writes.  Staged row r keeps its 16-byte chunk c at
+    // c ^ ((r >> 1) & 7): the 8-byte writes of 16 rows and the 16-byte reads
+    // of 8 rows each touch every bank once.
     const float inv = v_scale / sum;
-    int64_t spi[2];
-    bool sval[2];
+    int64_t spi[4];   // partial index of staged row 8 i + lane / 8 of round R: spi[2 R + i]
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int srow = 32 * wave + 16 * pass + (lane >> 2);
+    for (int x = 0; x < 4; ++x) {
+      const int srow = 32 * wave + 8 * x + (lane >> 3);
       const int se = chunk * MT + srow / G;
-      sval[pass] = se < n_ent;
-      const int sent = ent_s[sval[pass] ? se : 0];
-      spi[pass] = sval[pass] ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
+      const bool sv = se < n_ent;
+      const int sent = ent_s[sv ? se : 0];
+      spi[x] = sv ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
     }
-    const int jrow = lane & 31;
+    const int jrow = lane & 31, lr = jrow & 15;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int pr = 0; pr < 2; ++pr) {
+      i32x2 pk[2][4];
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const bf16x2 lo2 = {(__bf16)(oacc[dt][4 * gq] * inv), (__bf16)(oacc[dt][4 * gq + 1] * inv)};
-        const bf16x2 hi2 = {(__bf16)(oacc[dt][4 * gq + 2] * inv), (__bf16)(oacc[dt][4 * gq + 3] * inv)};
-        const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
-        lds_store8(&ow[jrow * 64 + ((gq ^ ((jrow >> 2) & 3)) << 4) + 8 * half], pk);
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x16& o = oacc[2 * pr + d];
+          const bf16x2 lo2 = {(__bf16)(o[4 * gq] * inv), (__bf16)(o[4 * gq + 1] * inv)};
+          const bf16x2 hi2 = {(__bf16)(o[4 * gq + 2] * inv), (__bf16)(o[4 * gq + 3] * inv)};
+          pk[d][gq] = i32x2{__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+        }
+#pragma unroll
+      for (int R = 0; R < 2; ++R) {
+        if ((jrow >> 4) == R) {
+          // dims 32 d + 8 gq + 4 half .. +3 of this lane's row: chunk 4 d + gq, half 8-byte
+#pragma unroll
+          for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+              lds_store8(&ow[lr * 128 + (((4 * d + gq) ^ ((lr >> 1) & 7)) << 4) + 8 * half], pk[d][gq]);
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 8 * i + (lane >> 3), c = lane & 7;
+          const i32x4 v = lds_load16<i32x4>(&ow[r * 128 + ((c ^ ((r >> 1) & 7)) << 4)]);
+          __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(a.part_o + spi[2 * R + i] * 128 + 64 * pr + 8 * c));
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        const int r = 16 * pass + (lane >> 2), c = lane & 3;
-        const i32x4 v = lds_load16<i32x4>(&ow[r * 64 + ((c ^ ((r >> 2) & 3)) << 4)]);
-        // streamed out, read once by the merge: non-temporal
-        __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(a.part_o + spi[pass] * 128 + 32 * dt + 8 * c));
-      }
-      wave_lds_sync();
     }
     {  // both halves hold the row's max and sum and store the same value
       const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : a.trash;
