@@ -184,6 +184,56 @@ __device__ __forceinline__ i32x4 load_kv8(const uint8_t* page, int row, int col)
   }
 }
 
+// A wave's 32 query rows x 128 dims of output, held as four O^T MFMA tiles
+// (oacc[dt]: C[dim][row], dims 32 dt ..), scaled by `mul` and stored as bf16
+// rows of 256 bytes at part + spi * 128.  The rows go through the wave's
+// 2 KB LDS staging area 16 rows x 128 bytes at a time (two dim tiles of 16
+// rows), so that every store instruction writes 8 rows x 128 contiguous
+// bytes: whole 128-byte lines.  With non-temporal stores a line written in
+// pieces would leave memory as several partial writes.  Staged row r keeps
+// its 16-byte chunk c at c ^ ((r >> 1) & 7): the 8-byte writes of 16 rows and
+// the 16-byte reads of 8 rows each touch every bank once.  spi[2 R + i] is
+// the destination of the wave's row 16 R + 8 i + lane / 8.
+template <bool kNonTemporal>
+__device__ __forceinline__ void store_rows_bf16(const f32x16 (&oacc)[4], float mul, uint8_t* ow, uint16_t* part,
+                                                const int64_t (&spi)[4], int lane) {
+  const int jrow = lane & 31, lr = jrow & 15, half = lane >> 5;
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr) {
+    i32x2 pk[2][4];
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x16& o = oacc[2 * pr + d];
+        const bf16x2 lo2 = {(__bf16)(o[4 * gq] * mul), (__bf16)(o[4 * gq + 1] * mul)};
+        const bf16x2 hi2 = {(__bf16)(o[4 * gq + 2] * mul), (__bf16)(o[4 * gq + 3] * mul)};
+        pk[d][gq] = i32x2{__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+      }
+#pragma unroll
+    for (int R = 0; R < 2; ++R) {
+      if ((jrow >> 4) == R) {
+        // dims 32 d + 8 gq + 4 half .. +3 of this lane's row: chunk 4 d + gq, 8-byte half
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            lds_store8(&ow[lr * 128 + (((4 * d + gq) ^ ((lr >> 1) & 7)) << 4) + 8 * half], pk[d][gq]);
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        const i32x4 v = lds_load16<i32x4>(&ow[r * 128 + ((c ^ ((r >> 1) & 7)) << 4)]);
+        i32x4* dst = reinterpret_cast<i32x4*>(part + spi[2 * R + i] * 128 + 64 * pr + 8 * c);
+        if constexpr (kNonTemporal) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
 template <KvFmt F>
 __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];
@@ -347,16 +397,9 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of transposed reads
     }
-    // Output: O goes through the wave's LDS staging area 16 rows x 128 bytes
-    // at a time (two 32-column tiles, 16 of the wave's rows), so that every
-    // store instruction writes 8 partial rows x 128 contiguous bytes: whole
-    // 128-byte lines.  The stores are non-temporal (the merge reads each
-    // partial once), and a line written in pieces would leave memory as
-    // several partial writes.  Staged row r keeps its 16-byte chunk c at
-    // c ^ ((r >> 1) & 7): the 8-byte writes of 16 rows and the 16-byte reads
-    // of 8 rows each touch every bank once.
-    const float inv = v_scale / sum;
-    int64_t spi[4];   // partial index of staged row 8 i + lane / 8 of round R: spi[2 R + i]
+    // Output: the normalised bf16 partials, with non-temporal stores (the
+    // merge reads each of them once)
+    int64_t spi[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int srow = 32 * wave + 8 * x + (lane >> 3);
@@ -365,39 +408,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       const int sent = ent_s[sv ? se : 0];
       spi[x] = sv ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
     }
-    const int jrow = lane & 31, lr = jrow & 15;
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      i32x2 pk[2][4];
-#pragma unroll
-      for (int d = 0; d < 2; ++d)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x16& o = oacc[2 * pr + d];
-          const bf16x2 lo2 = {(__bf16)(o[4 * gq] * inv), (__bf16)(o[4 * gq + 1] * inv)};
-          const bf16x2 hi2 = {(__bf16)(o[4 * gq + 2] * inv), (__bf16)(o[4 * gq + 3] * inv)};
-          pk[d][gq] = i32x2{__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
-        }
-#pragma unroll
-      for (int R = 0; R < 2; ++R) {
-        if ((jrow >> 4) == R) {
-          // dims 32 d + 8 gq + 4 half .. +3 of this lane's row: chunk 4 d + gq, half 8-byte
-#pragma unroll
-          for (int d = 0; d < 2; ++d)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-              lds_store8(&ow[lr * 128 + (((4 * d + gq) ^ ((lr >> 1) & 7)) << 4) + 8 * half], pk[d][gq]);
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = 8 * i + (lane >> 3), c = lane & 7;
-          const i32x4 v = lds_load16<i32x4>(&ow[r * 128 + ((c ^ ((r >> 1) & 7)) << 4)]);
-          __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(a.part_o + spi[2 * R + i] * 128 + 64 * pr + 8 * c));
-        }
-        wave_lds_sync();
-      }
-    }
+    store_rows_bf16<true>(oacc, v_scale / sum, ow, a.part_o, spi, lane);
     {  // both halves hold the row's max and sum and store the same value
       const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : a.trash;
       a.part_lse[pi] = (mx + fast_log2(sum)) * kLn2;  // mx is already scaled
@@ -956,34 +967,18 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
       }
     }
     // scaled bf16 partial through the wave's staging area (as the forward's output)
-    int64_t spi[2];
+    int64_t spi[4];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int srow = 32 * wave + 16 * pass + (lane >> 2);
+    for (int x = 0; x < 4; ++x) {
+      const int srow = 32 * wave + 8 * x + (lane >> 3);
       const int se = chunk * MT + srow / G;
       const bool sv = se < n_ent;
       const int sent = ent_s[sv ? se : 0];
-      spi[pass] = sv ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
+      spi[x] = sv ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
     }
-    const int jrow = lane & 31;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const bf16x2 lo2 = {(__bf16)(oacc[dt][4 * gq] * a.sm_scale), (__bf16)(oacc[dt][4 * gq + 1] * a.sm_scale)};
-        const bf16x2 hi2 = {(__bf16)(oacc[dt][4 * gq + 2] * a.sm_scale), (__bf16)(oacc[dt][4 * gq + 3] * a.sm_scale)};
-        const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
-        lds_store8(&ow[jrow * 64 + ((gq ^ ((jrow >> 2) & 3)) << 4) + 8 * half], pk);
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        const int rr = 16 * pass + (lane >> 2), c = lane & 3;
-        const i32x4 v = lds_load16<i32x4>(&ow[rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4)]);
-        *reinterpret_cast<i32x4*>(a.part + spi[pass] * 128 + 32 * dt + 8 * c) = v;
-      }
-      wave_lds_sync();
-    }
+    // non-temporal in the plain variant; the fused distillation variant (one
+    // workgroup per CU) measured slower with them
+    store_rows_bf16<!KL>(oacc, a.sm_scale, ow, a.part, spi, lane);
     if constexpr (KL) {
       // sum_j P_hj pk_j for this wave's rows (kacc: C[dim][row] = pk^T P^T),
       // summed over a token's G heads (adjacent lanes); one bf16 store per
@@ -1056,7 +1051,7 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(DqSumArgs a) {
     int bk[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      v[j] = *reinterpret_cast<const i32x4*>(a.part + (base + min(s0 + j, a.k - 1)) * 128 + 8 * sub);
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(a.part + (base + min(s0 + j, a.k - 1)) * 128 + 8 * sub));
 #pragma unroll
     for (int j = 0; j < 16; ++j) bk[j] = s0 + j < a.k ? row[s0 + j] : -1;
     const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
