@@ -364,8 +364,8 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     const float mx = mraw * scale_log2;  // scaled row max (log2 domain)
     float sum = 0.f;
     bf16x8 pf[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    // P for key tile kt: p = exp2(s * scale - max), bf16 pairs, fp32 row sum
+    auto make_p = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         i32x4 pw;
@@ -379,13 +379,16 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
         }
         pf[kt][u] = __builtin_bit_cast(bf16x8, pw);
       }
-    }
-    sum += wave_xor32(sum);
+    };
 
-    // O^T = V^T P^T
+    // O^T = V^T P^T, software-pipelined: the exponentials of key tile kt + 1
+    // are computed between the matrix products of tile kt, so that the vector
+    // unit and the matrix core work at once inside the wave
     f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    make_p(0);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
+      if (kt + 1 < 4) make_p(kt + 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -397,6 +400,8 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of transposed reads
     }
+    sum += wave_xor32(sum);
+
     // Output: the normalised bf16 partials, with non-temporal stores (the
     // merge reads each of them once)
     int64_t spi[4];
