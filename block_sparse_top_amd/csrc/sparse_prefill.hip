@@ -331,15 +331,20 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     const int32_t pos = first_pos + (a.w0 + rl - rs);
 
     // S^T = K Q^T: 4 key tiles of 32
+    // K fragments read one k-step ahead of the products that use them
     f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) kf[0][kt] = lds_load16<bf16x8>(&ks[kbase[0] + 8192 * kt]);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 af = lds_load16<bf16x8>(&ks[kbase[st] + 8192 * kt]);
-        acc[kt] = mfma32x32x16(af, qf[st], acc[kt]);
+        for (int kt = 0; kt < 4; ++kt) kf[(st + 1) & 1][kt] = lds_load16<bf16x8>(&ks[kbase[st + 1] + 8192 * kt]);
       }
-      if (st & 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) acc[kt] = mfma32x32x16(kf[st & 1][kt], qf[st], acc[kt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // Row max on the raw scores with v_max3 (two scores per instruction),
