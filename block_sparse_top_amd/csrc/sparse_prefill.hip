@@ -186,48 +186,78 @@ __device__ __forceinline__ i32x4 load_kv8(const uint8_t* page, int row, int col)
 
 // A wave's 32 query rows x 128 dims of output, held as four O^T MFMA tiles
 // (oacc[dt]: C[dim][row], dims 32 dt ..), scaled by `mul` and stored as bf16
-// rows of 256 bytes at part + spi * 128.  The rows go through the wave's
-// 2 KB LDS staging area 16 rows x 128 bytes at a time (two dim tiles of 16
-// rows), so that every store instruction writes 8 rows x 128 contiguous
-// bytes: whole 128-byte lines.  With non-temporal stores a line written in
-// pieces would leave memory as several partial writes.  Staged row r keeps
-// its 16-byte chunk c at c ^ ((r >> 1) & 7): the 8-byte writes of 16 rows and
-// the 16-byte reads of 8 rows each touch every bank once.  spi[2 R + i] is
-// the destination of the wave's row 16 R + 8 i + lane / 8.
-template <bool kNonTemporal>
+// rows of 256 bytes at part + row_index(r) * 128 for the wave's row r, through
+// the wave's 2 KB LDS staging area.
+//  * kWholeLines: 16 rows x 128 bytes at a time (two dim tiles of 16 rows),
+//    so that every store instruction writes 8 rows x 128 contiguous bytes,
+//    whole 128-byte lines, with non-temporal stores (a line written in
+//    pieces that way would leave memory as several partial writes).  Staged
+//    row r keeps its 16-byte chunk c at c ^ ((r >> 1) & 7): the 8-byte
+//    writes of 16 rows and the 16-byte reads of 8 rows touch every bank once.
+//  * otherwise: one 32-column tile of all 32 rows at a time, every store
+//    instruction 16 rows x 64 bytes, ordinary stores (the cache combines the
+//    pieces of a line); half the LDS writes of the mode above.  Staged row j
+//    keeps its chunk c at c ^ ((j >> 2) & 3).
+template <bool kWholeLines, typename RowIndex>
 __device__ __forceinline__ void store_rows_bf16(const f32x16 (&oacc)[4], float mul, uint8_t* ow, uint16_t* part,
-                                                const int64_t (&spi)[4], int lane) {
-  const int jrow = lane & 31, lr = jrow & 15, half = lane >> 5;
+                                                RowIndex row_index, int lane) {
+  const int jrow = lane & 31, half = lane >> 5;
+  if constexpr (kWholeLines) {
+    int64_t spi[4];  // row 16 R + 8 i + lane / 8: spi[2 R + i]
 #pragma unroll
-  for (int pr = 0; pr < 2; ++pr) {
-    i32x2 pk[2][4];
+    for (int x = 0; x < 4; ++x) spi[x] = row_index(8 * x + (lane >> 3));
+    const int lr = jrow & 15;
 #pragma unroll
-    for (int d = 0; d < 2; ++d)
+    for (int pr = 0; pr < 2; ++pr) {
+      i32x2 pk[2][4];
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x16& o = oacc[2 * pr + d];
+          const bf16x2 lo2 = {(__bf16)(o[4 * gq] * mul), (__bf16)(o[4 * gq + 1] * mul)};
+          const bf16x2 hi2 = {(__bf16)(o[4 * gq + 2] * mul), (__bf16)(o[4 * gq + 3] * mul)};
+          pk[d][gq] = i32x2{__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+        }
+#pragma unroll
+      for (int R = 0; R < 2; ++R) {
+        if ((jrow >> 4) == R) {
+          // dims 32 d + 8 gq + 4 half .. +3 of this lane's row: chunk 4 d + gq, 8-byte half
+#pragma unroll
+          for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+              lds_store8(&ow[lr * 128 + (((4 * d + gq) ^ ((lr >> 1) & 7)) << 4) + 8 * half], pk[d][gq]);
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 8 * i + (lane >> 3), c = lane & 7;
+          const i32x4 v = lds_load16<i32x4>(&ow[r * 128 + ((c ^ ((r >> 1) & 7)) << 4)]);
+          __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(part + spi[2 * R + i] * 128 + 64 * pr + 8 * c));
+        }
+        wave_lds_sync();
+      }
+    }
+  } else {
+    int64_t spi[2];  // row 16 pass + lane / 4
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) spi[pass] = row_index(16 * pass + (lane >> 2));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const f32x16& o = oacc[2 * pr + d];
-        const bf16x2 lo2 = {(__bf16)(o[4 * gq] * mul), (__bf16)(o[4 * gq + 1] * mul)};
-        const bf16x2 hi2 = {(__bf16)(o[4 * gq + 2] * mul), (__bf16)(o[4 * gq + 3] * mul)};
-        pk[d][gq] = i32x2{__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
-      }
-#pragma unroll
-    for (int R = 0; R < 2; ++R) {
-      if ((jrow >> 4) == R) {
-        // dims 32 d + 8 gq + 4 half .. +3 of this lane's row: chunk 4 d + gq, 8-byte half
-#pragma unroll
-        for (int d = 0; d < 2; ++d)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            lds_store8(&ow[lr * 128 + (((4 * d + gq) ^ ((lr >> 1) & 7)) << 4) + 8 * half], pk[d][gq]);
+        const bf16x2 lo2 = {(__bf16)(oacc[dt][4 * gq] * mul), (__bf16)(oacc[dt][4 * gq + 1] * mul)};
+        const bf16x2 hi2 = {(__bf16)(oacc[dt][4 * gq + 2] * mul), (__bf16)(oacc[dt][4 * gq + 3] * mul)};
+        const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
+        lds_store8(&ow[jrow * 64 + ((gq ^ ((jrow >> 2) & 3)) << 4) + 8 * half], pk);
       }
       wave_lds_sync();
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 8 * i + (lane >> 3), c = lane & 7;
-        const i32x4 v = lds_load16<i32x4>(&ow[r * 128 + ((c ^ ((r >> 1) & 7)) << 4)]);
-        i32x4* dst = reinterpret_cast<i32x4*>(part + spi[2 * R + i] * 128 + 64 * pr + 8 * c);
-        if constexpr (kNonTemporal) __builtin_nontemporal_store(v, dst);
-        else *dst = v;
+      for (int pass = 0; pass < 2; ++pass) {
+        const int r = 16 * pass + (lane >> 2), c = lane & 3;
+        const i32x4 v = lds_load16<i32x4>(&ow[r * 64 + ((c ^ ((r >> 2) & 3)) << 4)]);
+        *reinterpret_cast<i32x4*>(part + spi[pass] * 128 + 32 * dt + 8 * c) = v;
       }
       wave_lds_sync();
     }
@@ -407,18 +437,16 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     }
     sum += wave_xor32(sum);
 
-    // Output: the normalised bf16 partials, with non-temporal stores (the
+    // Output: the normalised bf16 partials in whole lines, non-temporal (the
     // merge reads each of them once)
-    int64_t spi[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int srow = 32 * wave + 8 * x + (lane >> 3);
+    auto row_index = [&](int wrow) -> int64_t {
+      const int srow = 32 * wave + wrow;
       const int se = chunk * MT + srow / G;
-      const bool sv = se < n_ent;
-      const int sent = ent_s[sv ? se : 0];
-      spi[x] = sv ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
-    }
-    store_rows_bf16<true>(oacc, v_scale / sum, ow, a.part_o, spi, lane);
+      if (se >= n_ent) return a.trash;
+      const int sent = ent_s[se];
+      return ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63);
+    };
+    store_rows_bf16<true>(oacc, v_scale / sum, ow, a.part_o, row_index, lane);
     {  // both halves hold the row's max and sum and store the same value
       const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : a.trash;
       a.part_lse[pi] = (mx + fast_log2(sum)) * kLn2;  // mx is already scaled
@@ -976,19 +1004,18 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // scaled bf16 partial through the wave's staging area (as the forward's output)
-    int64_t spi[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int srow = 32 * wave + 8 * x + (lane >> 3);
+    // scaled bf16 partial through the wave's staging area: whole lines with
+    // non-temporal stores in the plain variant; the fused distillation variant
+    // (one workgroup per CU, so one wave per SIMD to hide the extra LDS
+    // writes) measured faster with 64-byte pieces and ordinary stores
+    auto row_index = [&](int wrow) -> int64_t {
+      const int srow = 32 * wave + wrow;
       const int se = chunk * MT + srow / G;
-      const bool sv = se < n_ent;
-      const int sent = ent_s[sv ? se : 0];
-      spi[x] = sv ? ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63) : a.trash;
-    }
-    // non-temporal in the plain variant; the fused distillation variant (one
-    // workgroup per CU) measured slower with them
-    store_rows_bf16<!KL>(oacc, a.sm_scale, ow, a.part, spi, lane);
+      if (se >= n_ent) return a.trash;
+      const int sent = ent_s[se];
+      return ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63);
+    };
+    store_rows_bf16<!KL>(oacc, a.sm_scale, ow, a.part, row_index, lane);
     if constexpr (KL) {
       // sum_j P_hj pk_j for this wave's rows (kacc: C[dim][row] = pk^T P^T),
       // summed over a token's G heads (adjacent lanes); one bf16 store per
