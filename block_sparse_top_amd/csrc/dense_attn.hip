@@ -121,12 +121,21 @@ __global__ __launch_bounds__(256, 2) void dense_fwd_kernel(DenseFwdArgs a) {
     store_blk(b, buf);
     __syncthreads();
     // S^T = K Q^T: register i of tile kt_ holds key 32 kt_ + 8 (i / 4) + 4 half + i % 4
+    // (K fragments read one k-step ahead of their products)
     f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    bf16x8 kf[2][4];
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int kt_ = 0; kt_ < 4; ++kt_) kf[0][kt_] = lds_load16<bf16x8>(&ks[buf][kbase[0] + 8192 * kt_]);
 #pragma unroll
-      for (int kt_ = 0; kt_ < 4; ++kt_)
-        acc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&ks[buf][kbase[st] + 8192 * kt_]), qf[st], acc[kt_]);
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) {
+#pragma unroll
+        for (int kt_ = 0; kt_ < 4; ++kt_) kf[(st + 1) & 1][kt_] = lds_load16<bf16x8>(&ks[buf][kbase[st + 1] + 8192 * kt_]);
+      }
+#pragma unroll
+      for (int kt_ = 0; kt_ < 4; ++kt_) acc[kt_] = mfma32x32x16(kf[st & 1][kt_], qf[st], acc[kt_]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int lim = d.pos - b * 128 - 4 * half;
     const bool all_visible = b * 128 + 127 <= d.pos0;
     float bm = -INFINITY;
@@ -153,8 +162,7 @@ __global__ __launch_bounds__(256, 2) void dense_fwd_kernel(DenseFwdArgs a) {
       mrun = mnew;
     }
     bf16x8 pf[4][2];
-#pragma unroll
-    for (int kt_ = 0; kt_ < 4; ++kt_)
+    auto make_p = [&](int kt_) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         i32x4 pw;
@@ -168,9 +176,13 @@ __global__ __launch_bounds__(256, 2) void dense_fwd_kernel(DenseFwdArgs a) {
         }
         pf[kt_][u] = __builtin_bit_cast(bf16x8, pw);
       }
-    // O^T += V^T P^T
+    };
+    // O^T += V^T P^T, with the exponentials of key tile kt_ + 1 computed
+    // between the products of tile kt_
+    make_p(0);
 #pragma unroll
     for (int kt_ = 0; kt_ < 4; ++kt_) {
+      if (kt_ + 1 < 4) make_p(kt_ + 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
