@@ -94,11 +94,19 @@ __global__ __launch_bounds__(256, 2) void kl_dense_dq_kernel(KlDqArgs a) {
   auto scores = [&](int b, int buf, f32x16 (&acc)[4]) {
 #pragma unroll
     for (int kt_ = 0; kt_ < 4; ++kt_) acc[kt_] = f32x16{};
+    bf16x8 kf[2][4];   // K fragments read one k-step ahead of their products
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int kt_ = 0; kt_ < 4; ++kt_) kf[0][kt_] = lds_load16<bf16x8>(&ks[buf][kbase[0] + 8192 * kt_]);
 #pragma unroll
-      for (int kt_ = 0; kt_ < 4; ++kt_)
-        acc[kt_] = mfma32x32x16(lds_load16<bf16x8>(&ks[buf][kbase[st] + 8192 * kt_]), qf[st], acc[kt_]);
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) {
+#pragma unroll
+        for (int kt_ = 0; kt_ < 4; ++kt_) kf[(st + 1) & 1][kt_] = lds_load16<bf16x8>(&ks[buf][kbase[st + 1] + 8192 * kt_]);
+      }
+#pragma unroll
+      for (int kt_ = 0; kt_ < 4; ++kt_) acc[kt_] = mfma32x32x16(kf[st & 1][kt_], qf[st], acc[kt_]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int lim = pos - b * 128 - 4 * half;
     const bool all_visible = b * 128 + 127 <= pos0;
 #pragma unroll
