@@ -5,12 +5,15 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "msa_internal.hpp"
 
@@ -48,14 +51,46 @@ msa_status_t hip_status(hipError_t e, const char* where) {
   return fail(MSA_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
 }
 
-// Copy the plan metadata into the workspace unless this workspace already
-// holds it.  The copy is ordered on `st` before the kernels that read it.
+// Which plan's metadata each workspace holds.  A call uploads the plan's
+// metadata (one hipMemcpyAsync on its stream, ordered before its kernels)
+// unless the record says that this workspace already holds exactly this
+// plan's metadata, uploaded on the same stream.  Records are dropped when
+// their plan is destroyed, when another plan's call may have written over
+// their metadata (its workspace overlaps it), and by msa_workspace_reset.
+// Plans are identified by a serial number, never by their address.
+struct WsRecord {
+  const char* meta_begin;
+  const char* meta_end;
+  const void* ws;
+  uint64_t plan_uid;
+  hipStream_t stream;
+};
+std::mutex g_ws_mu;
+std::vector<WsRecord> g_ws;  // few entries: one per live workspace
+std::atomic<uint64_t> g_plan_serial{1};
+
+void forget_overlapping(const char* lo, const char* hi, uint64_t keep_uid, const void* keep_ws) {
+  g_ws.erase(std::remove_if(g_ws.begin(), g_ws.end(),
+                            [&](const WsRecord& r) {
+                              if (r.plan_uid == keep_uid && r.ws == keep_ws) return false;
+                              return r.meta_begin < hi && lo < r.meta_end;
+                            }),
+             g_ws.end());
+}
+
 msa_status_t upload_meta(msa_plan_s* p, void* ws, hipStream_t st) {
-  if (p->uploaded_to == ws) return MSA_OK;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  const char* base = static_cast<const char*>(ws);
+  // this call's kernels may write anywhere in [ws, ws + total): other plans'
+  // metadata there is no longer trusted
+  forget_overlapping(base, base + p->lay.total, p->uid, ws);
+  for (const WsRecord& r : g_ws)
+    if (r.ws == ws && r.plan_uid == p->uid && r.stream == st) return MSA_OK;
+  g_ws.erase(std::remove_if(g_ws.begin(), g_ws.end(), [&](const WsRecord& r) { return r.ws == ws; }), g_ws.end());
   hipError_t e = hipMemcpyAsync(static_cast<char*>(ws) + p->lay.meta, p->meta.data(),
                                 p->meta.size() * sizeof(int32_t), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_status(e, "metadata upload");
-  p->uploaded_to = ws;
+  g_ws.push_back({base + p->lay.meta, base + p->lay.meta + p->lay.meta_bytes, ws, p->uid, st});
   return MSA_OK;
 }
 
@@ -118,7 +153,7 @@ hipEvent_t take_event(msa::Profiler& pr) {
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
 }
-const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "proxy_topk", "csr",        "partial_attn",
+const char* const kKernelNames[] = {"proxy_maxscore", "topk_select", "proxy_topk", "topk_refine", "csr", "partial_attn",
                                     "merge",          "decode",      "decode_merge", "bwd_dq", "bwd_dq_sum",
                                     "bwd_dkv",        "kl_dq_sum",   "kl_dense_dq",  "kl_dense_dk",
                                     "dense_fwd",      "dense_dq",    "dense_dkv"};
@@ -176,6 +211,14 @@ msa_status_t msa_profile_read(msa_plan_t p, double* total_ms, int64_t* launches)
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
+msa_status_t msa_workspace_reset(const void* workspace, size_t bytes) {
+  if (!workspace) return fail(MSA_ERR_INVALID_ARG, "msa_workspace_reset: workspace is NULL");
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  const char* lo = static_cast<const char*>(workspace);
+  forget_overlapping(lo, lo + std::max<size_t>(bytes, 1), 0, nullptr);
+  return ok();
+}
+
 msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* workspace_bytes) {
   if (!desc || !out || !workspace_bytes) return fail(MSA_ERR_INVALID_ARG, "msa_plan: NULL argument");
   *out = nullptr;
@@ -211,9 +254,12 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
   }
   if (d.max_rows_per_call < 0) return fail(MSA_ERR_INVALID_ARG, "msa_plan: max_rows_per_call < 0");
   if (d.attn_window_rows < 0) return fail(MSA_ERR_INVALID_ARG, "msa_plan: attn_window_rows < 0");
+  if (d.decode_splits < 0 || d.decode_splits > 64)
+    return fail(MSA_ERR_INVALID_ARG, "msa_plan: decode_splits %d not in [0, 64]", d.decode_splits);
 
   msa_plan_s* p = new (std::nothrow) msa_plan_s();
   if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_plan: out of host memory");
+  p->uid = g_plan_serial.fetch_add(1);
   p->d = d;
   p->d.qo_lens_host = nullptr;
   p->d.kv_lens_host = nullptr;
@@ -253,6 +299,13 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     }
     p->row_start.push_back((int32_t)T);
     p->page_start.push_back((int32_t)NB);
+  }
+  // block ids are kept in 16 bits by the selection kernels' candidate lists
+  if (p->nb_max > 65536) {
+    const int32_t nbm = p->nb_max;
+    delete p;
+    return fail(MSA_ERR_UNSUPPORTED, "msa_plan: a sequence of %d blocks exceeds the limit of 65536 blocks (8388608 keys)",
+                nbm);
   }
   p->T = (int32_t)T;
   p->NB = (int32_t)NB;
@@ -321,9 +374,20 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     // pass uses the one-row kernel, and the fused selection keeps its block
     // scores here
     p->one_row = std::all_of(p->qo.begin(), p->qo.end(), [](int32_t q) { return q == 1; });
+    const bool lowp = d.proxy_dtype != MSA_BF16;
     if (p->one_row) {
       L.dms = off;
       off = align_up(off + (int64_t)d.num_proxy_heads * p->nb_max * T * 4, 256);
+      if (d.proxy_dtype == MSA_MXFP4 || d.proxy_dtype == MSA_MXFP4_QK) {
+        L.kmx = off;
+        off = align_up(off + (int64_t)d.num_proxy_kv_heads * p->nb_max * T * 4, 256);
+      }
+    } else if (lowp) {
+      // every (row, group) pair may need exact re-scoring: 64 bytes each
+      L.rq_count = off;
+      off = align_up(off + 4, 256);
+      L.rq = off;
+      off = align_up(off + (int64_t)T * d.num_proxy_heads * 64, 256);
     }
   } else {
     // one workgroup per (sequence, group) when that fills the GPU; otherwise
@@ -331,6 +395,7 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     const int64_t pairs = (int64_t)p->S * Hkv;
     p->dec_splits = (int)std::max<int64_t>(1, std::min<int64_t>(8, (512 + pairs - 1) / pairs));
     if (pairs >= 192) p->dec_splits = 1;
+    if (d.decode_splits > 0) p->dec_splits = d.decode_splits;
     L.dec_o = off; off = align_up(off + (size_t)p->S * Hq * p->dec_splits * 128 * 4, 256);
     L.dec_ml = off; off = align_up(off + (size_t)p->S * Hq * p->dec_splits * 2 * 4, 256);
   }
@@ -342,6 +407,12 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
 
 msa_status_t msa_plan_destroy(msa_plan_t plan) {
   if (plan) {
+    {
+      std::lock_guard<std::mutex> lk(g_ws_mu);
+      g_ws.erase(std::remove_if(g_ws.begin(), g_ws.end(),
+                                [&](const WsRecord& r) { return r.plan_uid == plan->uid; }),
+                 g_ws.end());
+    }
     for (auto& pr : plan->prof.pending) {
       (void)hipEventDestroy(pr.first);
       (void)hipEventDestroy(pr.second);
@@ -383,7 +454,8 @@ msa_status_t msa_proxy_block_maxscore(msa_plan_t p, const void* proxy_q, const v
   while (hi > lo && p->tiles[4 * (hi - 1) + 1] >= row_begin + row_count) --hi;
   const msa::DevMeta m = msa::dev_meta(p, workspace);
   return hip_status(msa::launch_proxy_maxscore(p, m, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale,
-                                               kv_indices, lo, hi, row_begin, row_count, max_score, nullptr, nullptr, hs),
+                                               kv_indices, lo, hi, row_begin, row_count, max_score, nullptr,
+                                               msa::SelScratch{}, hs),
                     __func__);
 }
 
@@ -394,9 +466,13 @@ msa_status_t msa_proxy_topk_select(msa_plan_t p, const void* proxy_q, const void
                                    msa_stream_t stream) {
   if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_proxy_topk_select: NULL plan");
   if (p->d.mode != MSA_PREFILL) return fail(MSA_ERR_UNSUPPORTED, "msa_proxy_topk_select: decode plan");
-  if (p->d.topk > 17)
+  if (p->d.topk > 17 && !p->one_row)
     return fail(MSA_ERR_UNSUPPORTED, "msa_proxy_topk_select: topk %d > 17; use msa_proxy_block_maxscore + msa_topk_select",
                 p->d.topk);
+  if (p->one_row && p->d.proxy_dtype != MSA_BF16 && p->nb_max > 2048)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "msa_proxy_topk_select: one-query-row plans with a low-precision proxy select over at most 2048 "
+                "blocks per sequence (got %d)", p->nb_max);
   MSA_CHECK_PTR(proxy_q);
   MSA_CHECK_PTR(proxy_k_pages);
   MSA_CHECK_PTR(kv_indices);
@@ -413,11 +489,17 @@ msa_status_t msa_proxy_topk_select(msa_plan_t p, const void* proxy_q, const void
   while (lo < p->ntiles && p->tiles[4 * lo + 1] + p->tiles[4 * lo + 2] <= row_begin) ++lo;
   while (hi > lo && p->tiles[4 * (hi - 1) + 1] >= row_begin + row_count) --hi;
   const msa::DevMeta m = msa::dev_meta(p, workspace);
+  char* ws = static_cast<char*>(workspace);
+  msa::SelScratch scr;
+  if (p->one_row) scr.dms = reinterpret_cast<float*>(ws + p->lay.dms);
+  if (p->lay.kmx) scr.kmx = reinterpret_cast<int32_t*>(ws + p->lay.kmx);
+  if (p->lay.rq) {
+    scr.rq = reinterpret_cast<int32_t*>(ws + p->lay.rq);
+    scr.rq_count = reinterpret_cast<int32_t*>(ws + p->lay.rq_count);
+  }
   return hip_status(msa::launch_proxy_maxscore(p, m, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale,
                                                kv_indices, lo, hi, row_begin, row_count, nullptr, kv_block_indexes,
-                                               p->one_row ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p->lay.dms)
-                                                          : nullptr,
-                                               hs),
+                                               scr, hs),
                     __func__);
 }
 

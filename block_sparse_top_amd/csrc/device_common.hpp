@@ -171,6 +171,11 @@ __device__ __forceinline__ int v_swz(int row, int chunk) { return row * 256 + ((
 // loads issued before it (the next chunk's rows) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Number of set bits of a wave mask below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int32_t x) {
   // first index i in [0, n) with a[i] > x (a ascending)
   int lo = 0, hi = n;

@@ -40,8 +40,11 @@ struct PlanLayout {
   int64_t max_items = 0;
   // decode split scratch
   size_t dec_o = 0, dec_ml = 0;
-  // block scores of the fused selection on one-query-row plans
-  size_t dms = 0;
+  // block scores of the fused selection on one-query-row plans (and, MXFP4
+  // K, each block's largest scale code)
+  size_t dms = 0, kmx = 0;
+  // low-precision proxies: queue of (row, group) pairs re-scored exactly
+  size_t rq = 0, rq_count = 0;
   size_t total = 0;
 };
 
@@ -64,7 +67,7 @@ struct msa_plan_s {
   int32_t dec_splits = 1;
   bool one_row = false;              // prefill plan whose every sequence has one query row
   int32_t num_cu = 256;              // compute units of the device the plan was made on
-  const void* uploaded_to = nullptr; // last workspace the metadata was copied into
+  uint64_t uid = 0;                  // serial number (workspace records name plans by it)
   mutable msa::Profiler prof;
 };
 
@@ -81,13 +84,27 @@ struct ProfEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 
+// Workspace areas of the fused selection (msa_proxy_topk_select).
+struct SelScratch {
+  float* dms = nullptr;        // one-query-row plans: block scores [P, nb_max, rows]
+  int32_t* kmx = nullptr;      // one-query-row plans, MXFP4 K: largest scale code per block
+  int32_t* rq = nullptr;       // low-precision proxies: queue of pairs to re-score exactly
+  int32_t* rq_count = nullptr;
+};
+
 // Kernel launchers (defined in the .hip files).  They assume validated inputs.
 hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const void* pq, const void* pk,
                                  const float* qs, const float* ks, const int32_t* kv_indices, int32_t tile_lo,
                                  int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
-                                 int32_t* sel, float* scratch, hipStream_t st);
+                                 int32_t* sel, const SelScratch& scr, hipStream_t st);
 hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, int64_t row_begin,
                        int64_t row_count, int32_t* sel, hipStream_t st);
+// Exact selection of one-query-row plans with low-precision proxies (band
+// blocks re-scored from the proxy operands).
+hipError_t launch_topk_exact(const msa_plan_s* p, const DevMeta& m, const float* max_score, const int32_t* kmx,
+                             const void* pq, const void* pk, const float* qs, const float* ks,
+                             const int32_t* kv_indices, int64_t row_begin, int64_t row_count, int32_t* sel,
+                             hipStream_t st);
 hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp,
                                  const void* vp, const float* ks, const float* vs, const int32_t* kv_indices,
                                  const int32_t* sel, void* out, float* lse, char* ws, int32_t w0, int32_t w1,

@@ -30,6 +30,7 @@
 
 #include "device_common.hpp"
 #include "msa_internal.hpp"
+#include "proxy_exact.hpp"
 
 namespace msa {
 namespace {
@@ -49,19 +50,30 @@ struct ProxyArgs {
   int32_t* sel;              // [T, P, k] selections when fused with top-k, else null
   int32_t k;                 // slots per (row, group), local block included (fused path)
   float scale;
+  // low-precision proxies, fused path: (row, group) pairs whose selection the
+  // score error bound cannot certify, queued for exact re-scoring
+  int32_t* rq;               // [row_count * P][kRqInts]
+  int32_t* rq_count;         // entries queued (zeroed before the pass)
 };
 
 // Fused selection: each lane keeps its row's best kSelCap (score, block)
 // pairs in descending score order.  Blocks arrive in ascending order and an
 // equal score never displaces a listed one, so ties go to the lower block,
-// exactly as in the separate top-k over the same fp32 scores.
+// exactly as in the separate top-k over the same fp32 scores.  The
+// low-precision formats keep kSelCapLowp pairs: the extra ones hold the
+// blocks just below the boundary, which the score error bound may leave
+// undecided (see the epilogue).
 constexpr int kSelCap = 16;
+constexpr int kSelCapLowp = 24;
 
-// Proxy (q, K) formats: bf16 x bf16, fp8 x fp8, fp8 q x MXFP4 K, MXFP4 q x
-// MXFP4 K.  MXFP4 K rows are 64 bytes of E2M1 codes; the block's 128 x 4
-// E8M0 scale bytes follow the codes (page record); an MXFP4 q row is 64 code
-// bytes then its 4 scale bytes.
-enum class Fmt : int { BF16 = 0, FP8 = 1, MX4K = 2, MX4QK = 3 };
+// A queued (row, group) pair: [0] row, [1] proxy head, [2] n_in | m << 8 |
+// overflow << 16, [3 .. 15) the list's 24 block ids as 16-bit pairs (in list
+// order: descending low-precision score).
+constexpr int kRqInts = 16;
+
+// MXFP4 K rows are 64 bytes of E2M1 codes; the block's 128 x 4 E8M0 scale
+// bytes follow the codes (page record); an MXFP4 q row is 64 code bytes then
+// its 4 scale bytes.
 
 template <Fmt F>
 struct ProxyTraits;
@@ -282,12 +294,36 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
   float* outp = a.out + (int64_t)p * a.nb_max * a.row_count + (my_grow - a.row_begin);
 
   const int my_local = (pos0 + my_row) >> 7;   // this lane's row's local block
-  float tv[TOPK ? kSelCap : 1];
-  int ti[TOPK ? kSelCap : 1];
+  constexpr bool LOWP = TOPK && F != Fmt::BF16;  // low-precision scores: selection certified or re-scored
+  constexpr int kCap = LOWP ? kSelCapLowp : (TOPK ? kSelCap : 1);
+  float tv[kCap];
+  int ti[kCap];
 #pragma unroll
-  for (int j = 0; j < (TOPK ? kSelCap : 1); ++j) {
+  for (int j = 0; j < kCap; ++j) {
     tv[j] = kNegInf;
     ti[j] = -1;
+  }
+  // largest |q_d| of the lane's row (code units; MXFP4 q: its largest block
+  // scale times 6) and, for MXFP4 K, the largest K scale code seen
+  float qinf = 0.f;
+  uint32_t kmaxe = 0;
+  if constexpr (LOWP) {
+    float pm[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      if constexpr (F == Fmt::MX4QK) {
+        pm[sub] = 6.0f * e8m0_value(max(qsc[sub] & 0xff, (qsc[sub] >> 16) & 0xff));
+      } else {
+        float m = 0.f;
+#pragma unroll
+        for (int st = 0; st < Tr::kSteps; ++st)
+#pragma unroll
+          for (int w = 0; w < (int)(sizeof(BFrag) / 4); ++w) m = fmaxf(m, e4m3_absmax4((uint32_t)qf[sub][st][w]));
+        pm[sub] = m;
+      }
+      pm[sub] = fmaxf(pm[sub], wave_xor32(pm[sub]));
+    }
+    qinf = lane < 32 ? pm[0] : pm[1];
   }
 
   // Fused selection: after each block, its score is inserted into the row's
@@ -305,10 +341,10 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
     cv = pend_ok ? pend_v : kNegInf;  // -inf changes nothing
     ci = pend_b;
   };
-  auto ins_steps = [&](int r) {  // slots 15 - 4r down to 12 - 4r
+  auto ins_steps = [&](int r) {  // slots kCap-1 - 4r down to kCap-4 - 4r
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int j = kSelCap - 1 - (4 * r + jj);
+      const int j = kCap - 1 - (4 * r + jj);
       const bool gj = cv > tv[j];
       const bool gp = j > 0 ? cv > tv[j > 0 ? j - 1 : 0] : false;
       const float up = j > 0 ? tv[j > 0 ? j - 1 : 0] : kPosInf;
@@ -328,9 +364,16 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
       int32_t ksc[2] = {0, 0};
       if constexpr (kMxK<F>) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
           ksc[j] = (int32_t)(lds_load16<uint32_t>(tile + kCodeBytes + 4 * (32 * (2 * hf + j) + (lane & 31))) >>
                              (8 * hsel));
+          // bytes 0 and 2 of the shifted word are the ones this lane's MFMAs
+          // use.  Only blocks before the tile's last local block can compete
+          // for any of its rows, and they are whole (a sequence's partial last
+          // block, whose slots past kv_len may hold anything, never competes).
+          if constexpr (LOWP)
+            if (b < b_last) kmaxe = max(kmaxe, max((uint32_t)ksc[j] & 0xffu, ((uint32_t)ksc[j] >> 16) & 0xffu));
+        }
       }
       AFrag fr[2][2];
 #pragma unroll
@@ -384,7 +427,7 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
       pend_ok = b < my_local;
       ins_begin();
 #pragma unroll
-      for (int r = 0; r < kSelCap / 4; ++r) ins_steps(r);
+      for (int r = 0; r < kCap / 4; ++r) ins_steps(r);
     } else {
       if (writes) outp[(int64_t)b * a.row_count] = v;
     }
@@ -435,15 +478,65 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
 
   if constexpr (TOPK) {
     // the R = min(k - 1, local) best earlier blocks and the local block, ascending, -1 padded
-    if (writes) {
-      const int R = min(a.k - 1, my_local);
+    const int R = min(a.k - 1, my_local);
+    bool queued = false;
+    if constexpr (LOWP) {
+      // Low-precision scores f are within delta of the exact scores s.  With
+      // theta = the R-th largest f: a listed block with f > theta + 2 delta
+      // beats every block with f <= theta exactly, so it is in the exact top
+      // R ("sure"); a block with f < theta - 2 delta is beaten by the R listed
+      // blocks with f >= theta, so it is out.  When exactly R blocks have
+      // f >= theta - 2 delta (and, if blocks were dropped from the list, the
+      // last listed one is below that too), the list's top R is the exact top
+      // R.  Otherwise the pair is queued: the blocks in the band are
+      // re-scored exactly (all competing blocks if the band may run past the
+      // list).
+      uint32_t ke = kmaxe;
+      if constexpr (kMxK<F>) {
+        // largest K scale code over every block the workgroup visited (each
+        // lane saw its rows' codes for every block)
+        ke = max(ke, (uint32_t)__shfl_xor((int)ke, 32));
 #pragma unroll
-      for (int j = 0; j < kSelCap; ++j)
+        for (int o = 1; o < 32; o <<= 1) ke = max(ke, (uint32_t)__shfl_xor((int)ke, o));
+      }
+      const float kinf = kMxK<F> ? 6.0f * e8m0_value(ke) : 448.0f;
+      // delta, rounded up a little against the fp32 products above
+      const float delta = ScoreBound<F>::kCoef * 1.0001f * scale * qinf * kinf;
+      const float theta = tv[R > 0 ? R - 1 : 0];
+      int n_in = 0, m = 0;
+#pragma unroll
+      for (int j = 0; j < kCap; ++j) {
+        // entries past the row's competing blocks were never filled
+        n_in += (j < R && tv[j] > theta + 2.f * delta) ? 1 : 0;
+        m += (j < my_local && tv[j] >= theta - 2.f * delta) ? 1 : 0;
+      }
+      const bool ovf = my_local > kCap && tv[kCap - 1] >= theta - 2.f * delta;
+      const bool unc = writes && R > 0 && R < my_local && n_in < R && (m > R || ovf);
+      const uint64_t mask = __ballot(unc);
+      if (mask) {
+        const int first = (int)__builtin_ctzll(mask);
+        int base = 0;
+        if (lane == first) base = atomicAdd(a.rq_count, __popcll(mask));
+        base = __builtin_amdgcn_readlane(base, first);
+        if (unc) {
+          int32_t* e = a.rq + (int64_t)(base + lanes_below(mask)) * kRqInts;
+          e[0] = (int32_t)my_grow;
+          e[1] = p;
+          e[2] = n_in | (m << 8) | ((ovf ? 1 : 0) << 16);
+#pragma unroll
+          for (int j = 0; j < kCap; j += 2) e[3 + j / 2] = (ti[j] & 0xffff) | (ti[j + 1] << 16);
+        }
+      }
+      queued = unc;
+    }
+    if (writes && !queued) {
+#pragma unroll
+      for (int j = 0; j < kCap; ++j)
         if (j >= R) ti[j] = 0x7fffffff;
 #pragma unroll
-      for (int rnd = 0; rnd < kSelCap; ++rnd)  // odd-even transposition sort by block id
+      for (int rnd = 0; rnd < kCap; ++rnd)  // odd-even transposition sort by block id
 #pragma unroll
-        for (int j = rnd & 1; j + 1 < kSelCap; j += 2) {
+        for (int j = rnd & 1; j + 1 < kCap; j += 2) {
           const int x = ti[j], y = ti[j + 1];
           ti[j] = min(x, y);
           ti[j + 1] = max(x, y);
@@ -452,10 +545,104 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
 #pragma unroll
       for (int j = 0; j <= kSelCap; ++j) {
         if (j >= a.k) break;
-        const int v = j < R ? ti[j < kSelCap ? j : 0] : (j == R ? my_local : -1);
+        const int v = j < R ? ti[j < kCap ? j : 0] : (j == R ? my_local : -1);
         dst[j] = v;
       }
     }
+  }
+}
+
+// Exact re-scoring of the queued (row, group) pairs of the fused
+// low-precision pass.  One wave per pair, looping over the queue: the band
+// blocks of the pair's list (or, if the band may run past the list, every
+// competing block not already sure) in ascending block order; each is scored
+// exactly (exact_block_dotmax), the need = R - n_in best are kept with ties to
+// the lower block, and the row is written like the fused pass writes it.
+template <Fmt F>
+__global__ __launch_bounds__(256) void topk_refine_kernel(ProxyArgs a, DevMeta mt) {
+  using Tr = ProxyTraits<F>;
+  __shared__ int32_t cand_lds[4][kSelCapLowp];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int count = __builtin_amdgcn_readfirstlane(*a.rq_count);
+  for (int e = blockIdx.x * 4 + wave; e < count; e += gridDim.x * 4) {
+    const int32_t* ent = a.rq + (int64_t)e * kRqInts;
+    const int r = __builtin_amdgcn_readfirstlane(ent[0]);
+    const int p = __builtin_amdgcn_readfirstlane(ent[1]);
+    const int hdr = __builtin_amdgcn_readfirstlane(ent[2]);
+    const int n_in = hdr & 0xff, m = (hdr >> 8) & 0xff;
+    const bool ovf = (hdr >> 16) & 1;
+    const int s = upper_bound_i32(mt.row_start, mt.S + 1, r) - 1;
+    const int pos = mt.kv[s] - mt.qo[s] + (r - mt.row_start[s]);
+    const int local = pos >> 7;
+    const int R = min(a.k - 1, local);
+    const int need = R - n_in;
+    // list ids: lane j < 24 holds entry j
+    const int lid = lane < kSelCapLowp ? (int)((uint32_t)ent[3 + lane / 2] >> (16 * (lane & 1))) & 0xffff : 0x7fffffff;
+    const bool sure = lane < n_in;
+    const int ph = a.Pk == a.P ? p : 0;
+    const uint8_t* qrow = a.pq + ((int64_t)r * a.P + p) * Tr::kQRowBytes;
+    const ExactQ q = exact_load_q<F>(qrow);
+    float sc = a.scale;
+    if constexpr (F == Fmt::FP8) sc *= a.qs[p] * a.ks[ph];
+    if constexpr (F == Fmt::MX4K) sc *= a.qs[p];
+    const int32_t* pages = a.kv_indices + mt.page_start[s];
+    // the uniform top-`need` list (every lane holds a copy)
+    float bv[kSelCap];
+    int bi[kSelCap];
+#pragma unroll
+    for (int j = 0; j < kSelCap; ++j) {
+      bv[j] = kNegInf;
+      bi[j] = 0x7fffffff;
+    }
+    auto consider = [&](int b) {
+      const uint8_t* blk = a.pk + ((int64_t)pages[b] * a.Pk + ph) * Tr::kKBlockBytes;
+      const float v = exact_block_dotmax<F>(q, blk, 128) * sc;
+      // insert before the first strictly smaller listed score (ascending block
+      // order: equal scores keep the lower block ahead)
+#pragma unroll
+      for (int j = kSelCap - 1; j >= 0; --j) {
+        const bool gj = j < need && v > bv[j];
+        const bool gp = j > 0 && v > bv[j > 0 ? j - 1 : 0];
+        if (gj) {
+          bv[j] = gp ? bv[j > 0 ? j - 1 : 0] : v;
+          bi[j] = gp ? bi[j > 0 ? j - 1 : 0] : b;
+        }
+      }
+    };
+    if (!ovf) {
+      // band entries n_in .. m-1, visited in ascending block order
+      const bool cand = lane >= n_in && lane < m && lid < local;
+      const uint64_t cm = __ballot(cand);
+      int rank = 0;
+      for (int j = n_in; j < m; ++j)
+        rank += ((cm >> j) & 1) && __builtin_amdgcn_readlane(lid, j) < lid ? 1 : 0;
+      if (cand) cand_lds[wave][rank] = lid;
+      wave_lds_sync();
+      const int nc = __popcll(cm);
+      for (int c = 0; c < nc; ++c) consider(__builtin_amdgcn_readfirstlane(cand_lds[wave][c]));
+      wave_lds_sync();
+    } else {
+      // every competing block except the sure ones
+      for (int b = 0; b < local; ++b) {
+        bool is_sure = false;
+        for (int j = 0; j < n_in; ++j) is_sure |= __builtin_amdgcn_readlane(lid, j) == b;
+        if (!is_sure) consider(b);
+      }
+    }
+    // the row: sure ids (lanes < n_in) and the kept ones, ascending, then the
+    // local block and -1 padding
+    int mine = 0x7fffffff;
+    if (lane < n_in) mine = lid;
+#pragma unroll
+    for (int j = 0; j < kSelCap; ++j)
+      if (lane == n_in + j && j < need) mine = bi[j];
+    int rank = 0;
+    for (int j = 0; j < R; ++j) rank += __builtin_amdgcn_readlane(mine, j) < mine ? 1 : 0;
+    int32_t* dst = a.sel + ((int64_t)r * a.P + p) * a.k;
+    if (lane < R) dst[rank] = mine;
+    if (lane == R) dst[R] = local;
+    if (lane > R && lane < a.k) dst[lane] = -1;
   }
 }
 
@@ -477,7 +664,8 @@ struct ProxyRowArgs {
   DevMeta m;
   int32_t P, Pk, nb_max, blocks_per_wg;
   int64_t row_begin, row_count;
-  float* out;  // [P, nb_max, row_count]
+  float* out;    // [P, nb_max, row_count]
+  int32_t* kmx;  // MXFP4 K, fused low-precision selection: largest scale code per block [Pk, nb_max, row_count]
   float scale;
 };
 
@@ -492,15 +680,18 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rl = blockIdx.z;              // row within the call's range
   const int seq = (int)(a.row_begin + rl);    // one row per sequence: row index = sequence index
-  const int kh = blockIdx.y;                  // K head
+  // blockIdx.y: the K head (P_k = P), or with one shared K head the group of
+  // 32 proxy heads (MFMA columns) this workgroup serves
+  const int kh = a.Pk == 1 ? 0 : (int)blockIdx.y;
+  const int head0 = a.Pk == 1 ? 32 * (int)blockIdx.y : kh;
   const int32_t kv_len = a.m.kv[seq];
   const int nb = (kv_len + 127) >> 7;
   const int b0 = blockIdx.x * a.blocks_per_wg, b1 = min(nb, b0 + a.blocks_per_wg);
   if (b0 >= nb) return;
-  const int ncols = a.Pk == 1 ? a.P : 1;      // query heads this K head serves
+  const int ncols = a.Pk == 1 ? min(32, a.P - head0) : 1;  // query heads this K head serves here
   const int j = lane & 31, hsel = lane >> 5;
   const bool col_ok = j < ncols;
-  const int head = a.Pk == 1 ? (col_ok ? j : 0) : kh;
+  const int head = head0 + (col_ok ? j : 0);
   // B operand: the served heads' proxy q rows (zero columns past ncols)
   Frag qf[Tr::kSteps];
   {
@@ -577,15 +768,16 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(Prox
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rl = blockIdx.z;
   const int seq = (int)(a.row_begin + rl);
-  const int kh = blockIdx.y;
+  const int kh = a.Pk == 1 ? 0 : (int)blockIdx.y;
+  const int head0 = a.Pk == 1 ? 32 * (int)blockIdx.y : kh;
   const int32_t kv_len = a.m.kv[seq];
   const int nb = (kv_len + 127) >> 7;
   const int b0 = blockIdx.x * a.blocks_per_wg, b1 = min(nb, b0 + a.blocks_per_wg);
   if (b0 >= nb) return;
-  const int ncols = a.Pk == 1 ? a.P : 1;
+  const int ncols = a.Pk == 1 ? min(32, a.P - head0) : 1;
   const int j = lane & 31, hsel = lane >> 5;
   const bool col_ok = j < ncols;
-  const int head = a.Pk == 1 ? (col_ok ? j : 0) : kh;
+  const int head = head0 + (col_ok ? j : 0);
   typename Tr::BFrag qf[2];
   int32_t qsc = 0x7f7f7f7f;
   {
@@ -631,6 +823,16 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(Prox
     }
     m = fmaxf(m, wave_xor32(m));
     if (lane < ncols) a.out[((int64_t)head * a.nb_max + b) * a.row_count + rl] = m * scale;
+    if (a.kmx) {
+      // the block's largest scale code (bounds its |k|); every key of the
+      // block is in some lane's four tiles, bytes 0 and 2 of each shifted word
+      uint32_t e = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) e = max(e, max((uint32_t)cur[t].sc & 0xffu, ((uint32_t)cur[t].sc >> 16) & 0xffu));
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) e = max(e, (uint32_t)__shfl_xor((int)e, o));
+      if (lane == 0) a.kmx[((int64_t)kh * a.nb_max + b) * a.row_count + rl] = (int32_t)e;
+    }
   };
   for (; b + kRowWaves < b1; b += 2 * kRowWaves) {
     step(fa, fb, b);
@@ -639,12 +841,17 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(Prox
   if (b < b1) step(fa, fb, b);
 }
 
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const void* pq, const void* pk,
                                  const float* qs, const float* ks, const int32_t* kv_indices, int32_t tile_lo,
                                  int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
-                                 int32_t* sel, float* scratch, hipStream_t st) {
+                                 int32_t* sel, const SelScratch& scr, hipStream_t st) {
+  const bool lowp = p->d.proxy_dtype != MSA_BF16;
   if (p->one_row) {
     // indexer pass of a decode step: block maxima by the one-row kernel (into
     // the workspace when the selection is fused), then the top-k kernel
@@ -660,9 +867,11 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
     r.nb_max = p->nb_max;
     r.row_begin = row_begin;
     r.row_count = row_count;
-    r.out = sel ? scratch : max_score;
+    r.out = sel ? scr.dms : max_score;
+    r.kmx = sel && lowp ? scr.kmx : nullptr;
     r.scale = p->d.proxy_sm_scale;
-    const int khs = r.Pk == 1 ? 1 : r.P;
+    // grid.y: K heads, or with one shared K head groups of 32 proxy heads
+    const int khs = r.Pk == 1 ? (r.P + 31) / 32 : r.P;
     // about one workgroup per CU over (sequence, K head, block chunk)
     const int64_t units = row_count * khs;
     const int64_t want = p->num_cu;
@@ -686,7 +895,9 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
           hipExtLaunchKernelGGL(proxy_onerow_kernel<Fmt::BF16>, grid, blk, 0, st, pe.start, pe.stop, 0, r);
       }
     }
-    if (sel) return launch_topk(p, m, scratch, row_begin, row_count, sel, st);
+    if (sel && lowp)
+      return launch_topk_exact(p, m, scr.dms, scr.kmx, pq, pk, qs, ks, kv_indices, row_begin, row_count, sel, st);
+    if (sel) return launch_topk(p, m, scr.dms, row_begin, row_count, sel, st);
     return hipGetLastError();
   }
   if (tile_hi <= tile_lo) return hipSuccess;
@@ -710,14 +921,30 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
   a.sel = sel;
   a.k = p->d.topk;
   a.scale = p->d.proxy_sm_scale;
+  a.rq = scr.rq;
+  a.rq_count = scr.rq_count;
+  const bool refine = sel && lowp;
+  if (refine) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, scr.rq_count, 1);
   const dim3 grid((unsigned)(a.ntiles * kProxySubs * a.P)), block(64 * kProxyWaves);
-  ProfEvents pe(p, sel ? "proxy_topk" : "proxy_maxscore");
-  auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, grid, block, 0, st, pe.start, pe.stop, 0, a); };
-  switch (p->d.proxy_dtype) {
-    case MSA_MXFP4_QK: sel ? go(proxy_maxscore_kernel<Fmt::MX4QK, true>) : go(proxy_maxscore_kernel<Fmt::MX4QK, false>); break;
-    case MSA_MXFP4: sel ? go(proxy_maxscore_kernel<Fmt::MX4K, true>) : go(proxy_maxscore_kernel<Fmt::MX4K, false>); break;
-    case MSA_FP8_E4M3: sel ? go(proxy_maxscore_kernel<Fmt::FP8, true>) : go(proxy_maxscore_kernel<Fmt::FP8, false>); break;
-    default: sel ? go(proxy_maxscore_kernel<Fmt::BF16, true>) : go(proxy_maxscore_kernel<Fmt::BF16, false>);
+  {
+    ProfEvents pe(p, sel ? "proxy_topk" : "proxy_maxscore");
+    auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, grid, block, 0, st, pe.start, pe.stop, 0, a); };
+    switch (p->d.proxy_dtype) {
+      case MSA_MXFP4_QK: sel ? go(proxy_maxscore_kernel<Fmt::MX4QK, true>) : go(proxy_maxscore_kernel<Fmt::MX4QK, false>); break;
+      case MSA_MXFP4: sel ? go(proxy_maxscore_kernel<Fmt::MX4K, true>) : go(proxy_maxscore_kernel<Fmt::MX4K, false>); break;
+      case MSA_FP8_E4M3: sel ? go(proxy_maxscore_kernel<Fmt::FP8, true>) : go(proxy_maxscore_kernel<Fmt::FP8, false>); break;
+      default: sel ? go(proxy_maxscore_kernel<Fmt::BF16, true>) : go(proxy_maxscore_kernel<Fmt::BF16, false>);
+    }
+  }
+  if (refine) {
+    // waves loop over the queued pairs; the queue length is read on the device
+    ProfEvents pe(p, "topk_refine");
+    const dim3 rg((unsigned)(2 * p->num_cu)), rb(256);
+    switch (p->d.proxy_dtype) {
+      case MSA_MXFP4_QK: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::MX4QK>, rg, rb, 0, st, pe.start, pe.stop, 0, a, m); break;
+      case MSA_MXFP4: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::MX4K>, rg, rb, 0, st, pe.start, pe.stop, 0, a, m); break;
+      default: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::FP8>, rg, rb, 0, st, pe.start, pe.stop, 0, a, m);
+    }
   }
   return hipGetLastError();
 }

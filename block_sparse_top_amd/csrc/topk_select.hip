@@ -26,6 +26,7 @@
 //    the list overflows (heavy exact ties), passes 3-4 stream the row.
 #include "device_common.hpp"
 #include "msa_internal.hpp"
+#include "proxy_exact.hpp"
 
 namespace msa {
 namespace {
@@ -175,10 +176,6 @@ __device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
              max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 // The largest t such that at least n lanes have v >= t, i.e. the n-th largest
 // v of the wave (n >= 1), built bit by bit from ballot counts.
 __device__ __forceinline__ uint32_t wave_nth_largest(uint32_t v, int n) {
@@ -296,7 +293,206 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
   if (lane < R) dst[rank] = mine;
 }
 
+// Order-preserving key of a float (larger float, larger key; -0 as +0) and back.
+__device__ __forceinline__ uint32_t f2key(float x) {
+  const uint32_t u = x == 0.f ? 0u : __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+struct ExactRowArgs {
+  const uint8_t* pq;
+  const uint8_t* pk;
+  const float* qs;
+  const float* ks;
+  const int32_t* kv_indices;
+  const int32_t* kmx;  // MXFP4 K: largest scale code of each block [Pk, nb_max, row_count]
+  int32_t Pk;
+  float scale;
+};
+
+// The decode-step indexer's selection for the low-precision proxy formats
+// (one query row per sequence, every block score of the row available): one
+// wave per (row, group), lane b % 64 / register b / 64 holding block b's key
+// as in topk_wave_kernel.  theta = the R-th largest score exactly (bit by bit
+// from ballot counts); delta = the format's score error bound for this row.
+// Blocks above theta + 2 delta are in the exact top R, blocks below theta -
+// 2 delta are out; if exactly R blocks reach theta - 2 delta they are the
+// answer, else the band blocks are re-scored exactly, in ascending block
+// order, and the best R - n_in kept (ties to the lower block).  The kept list
+// is distributed over the lanes (slot j in lane j).
+template <int VPL, Fmt F>
+__global__ __launch_bounds__(256) void topk_wave_exact_kernel(TopkArgs a, ExactRowArgs x) {
+  __shared__ int32_t sure_ids[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
+  if (pair >= a.row_count * a.P) return;
+  const int64_t rl = pair / a.P;
+  const int p = (int)(pair % a.P);
+  const int32_t r = (int32_t)(a.row_begin + rl);  // = its sequence: one query row each
+  const int local = __builtin_amdgcn_readfirstlane((a.m.kv[r] - 1) >> 7);
+  const int R = min(a.k - 1, local);
+  const int kh = x.Pk == a.P ? p : 0;
+  int32_t* dst = a.sel + ((int64_t)r * a.P + p) * a.k;
+  if (lane == 0) dst[R] = local;
+  if (lane > R && lane < a.k) dst[lane] = -1;
+  if (R == 0) return;
+  if (R == local) {  // every competing block is selected
+    for (int j = lane; j < R; j += 64) dst[j] = j;
+    return;
+  }
+  const float* col = a.ms + (int64_t)p * a.m.nb_max * a.row_count + rl;
+  uint32_t key[VPL];
+  const int last = max(local - 1, 0);
+  uint32_t kmaxe = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int b = 64 * i + lane;
+    key[i] = b < local ? f2key(col[(int64_t)min(b, last) * a.row_count]) : 0u;
+    if constexpr (F != Fmt::FP8) {
+      const uint32_t e = (uint32_t)x.kmx[((int64_t)kh * a.m.nb_max + min(b, last)) * a.row_count + rl];
+      kmaxe = b < local ? max(kmaxe, e) : kmaxe;
+    }
+  }
+  // theta: the R-th largest key
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    if (cnt >= R) t = c;
+  }
+  const float theta = key2f(t);
+  // delta: bound coefficient x scales x max|q| x max|k| (value units)
+  const uint8_t* qrow = x.pq + ((int64_t)r * a.P + p) * (F == Fmt::MX4QK ? 68 : 128);
+  float qinf;
+  if constexpr (F == Fmt::MX4QK) {
+    qinf = 6.0f * e8m0_value(max_byte4(*reinterpret_cast<const uint32_t*>(qrow + 64)));
+  } else {
+    const uint32_t w = lane < 32 ? *reinterpret_cast<const uint32_t*>(qrow + 4 * lane) : 0u;
+    qinf = e4m3_absmax4(w);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) qinf = fmaxf(qinf, __shfl_xor(qinf, o));
+  }
+  float kinf = 448.0f;
+  if constexpr (F != Fmt::FP8) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) kmaxe = max(kmaxe, (uint32_t)__shfl_xor((int)kmaxe, o));
+    kinf = 6.0f * e8m0_value(kmaxe);
+  }
+  float sc = x.scale;
+  if constexpr (F == Fmt::FP8) sc *= x.qs[p] * x.ks[kh];
+  if constexpr (F == Fmt::MX4K) sc *= x.qs[p];
+  const float delta = ScoreBound<F>::kCoef * 1.0001f * sc * qinf * kinf;
+  const uint32_t lo = f2key(theta - 2.f * delta), hi = f2key(theta + 2.f * delta);
+  int n_in = 0, nb = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    n_in += __popcll(__ballot(key[i] > hi));
+    nb += __popcll(__ballot(key[i] >= lo && key[i] <= hi));
+  }
+  if (nb == R - n_in) {
+    // certified: the R blocks reaching theta - 2 delta, ascending
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const bool c = key[i] >= lo;
+      const uint64_t m = __ballot(c);
+      if (c) dst[base + lanes_below(m)] = 64 * i + lane;
+      base += __popcll(m);
+    }
+    return;
+  }
+  // sure blocks, ascending, into LDS
+  {
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const bool c = key[i] > hi;
+      const uint64_t m = __ballot(c);
+      if (c) sure_ids[wave][base + lanes_below(m)] = 64 * i + lane;
+      base += __popcll(m);
+    }
+  }
+  const int need = R - n_in;
+  const ExactQ q = exact_load_q<F>(qrow);
+  const int32_t* pages = x.kv_indices + a.m.page_start[r];
+  float kv_ = kNegInf;  // the kept list: slot `lane`
+  int ki = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    uint64_t m = __ballot(key[i] >= lo && key[i] <= hi);
+    while (m) {
+      const int b = 64 * i + (int)__builtin_ctzll(m);
+      m &= m - 1;
+      const uint8_t* blk = x.pk + ((int64_t)pages[b] * x.Pk + kh) * (F == Fmt::FP8 ? 128 * 128 : 128 * 68);
+      const float v = exact_block_dotmax<F>(q, blk, 128) * sc;
+      // insert before the first strictly smaller kept score
+      const float up = __shfl_up(kv_, 1);
+      const int upi = __shfl_up(ki, 1);
+      const bool gj = lane < need && v > kv_;
+      const bool gp = lane > 0 && v > up;
+      if (gj) {
+        kv_ = gp ? up : v;
+        ki = gp ? upi : b;
+      }
+    }
+  }
+  wave_lds_sync();
+  // the row: sure ids and kept ids, ascending
+  int mine = 0x7fffffff;
+  if (lane < n_in) mine = sure_ids[wave][lane];
+  const int kept = __shfl(ki, max(lane - n_in, 0));
+  if (lane >= n_in && lane < R) mine = kept;
+  int rank = 0;
+  for (int j = 0; j < R; ++j) rank += __builtin_amdgcn_readlane(mine, j) < mine ? 1 : 0;
+  if (lane < R) dst[rank] = mine;
+}
+
 }  // namespace
+
+hipError_t launch_topk_exact(const msa_plan_s* p, const DevMeta& m, const float* max_score, const int32_t* kmx,
+                             const void* pq, const void* pk, const float* qs, const float* ks,
+                             const int32_t* kv_indices, int64_t row_begin, int64_t row_count, int32_t* sel,
+                             hipStream_t st) {
+  TopkArgs a;
+  a.ms = max_score;
+  a.sel = sel;
+  a.m = m;
+  a.row_begin = row_begin;
+  a.row_count = row_count;
+  a.P = p->d.num_proxy_heads;
+  a.k = p->d.topk;
+  ExactRowArgs x;
+  x.pq = static_cast<const uint8_t*>(pq);
+  x.pk = static_cast<const uint8_t*>(pk);
+  x.qs = qs;
+  x.ks = ks;
+  x.kv_indices = kv_indices;
+  x.kmx = kmx;
+  x.Pk = p->d.num_proxy_kv_heads;
+  x.scale = p->d.proxy_sm_scale;
+  const unsigned grid = (unsigned)((row_count * a.P + 3) / 4);
+  const int vpl = (p->nb_max + 63) / 64;
+  ProfEvents pe(p, "topk_select");
+  auto go = [&](auto kern) { hipExtLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, pe.start, pe.stop, 0, a, x); };
+#define MSA_EXACT_VPL(V)                                                               \
+  switch (p->d.proxy_dtype) {                                                          \
+    case MSA_FP8_E4M3: go(topk_wave_exact_kernel<V, Fmt::FP8>); break;                 \
+    case MSA_MXFP4: go(topk_wave_exact_kernel<V, Fmt::MX4K>); break;                   \
+    default: go(topk_wave_exact_kernel<V, Fmt::MX4QK>);                                \
+  }
+  if (vpl <= 4) { MSA_EXACT_VPL(4) }
+  else if (vpl <= 8) { MSA_EXACT_VPL(8) }
+  else if (vpl <= 16) { MSA_EXACT_VPL(16) }
+  else { MSA_EXACT_VPL(32) }
+#undef MSA_EXACT_VPL
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, int64_t row_begin,
                        int64_t row_count, int32_t* sel, hipStream_t st) {

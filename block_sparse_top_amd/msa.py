@@ -26,7 +26,8 @@ ENTRY_POINTS = ("msa_plan", "msa_plan_destroy", "msa_plan_info", "msa_proxy_bloc
                 "msa_proxy_topk_select", "msa_sparse_attn_prefill", "msa_sparse_attn_prefill_rows",
                 "msa_sparse_attn_prefill_backward", "msa_sparse_attn_prefill_backward_kl",
                 "msa_dense_attn_prefill", "msa_dense_attn_prefill_backward",
-                "msa_sparse_attn_decode", "msa_last_error", "msa_profile_kernel", "msa_profile_read")
+                "msa_sparse_attn_decode", "msa_workspace_reset", "msa_last_error", "msa_profile_kernel",
+                "msa_profile_read")
 
 
 class MsaError(RuntimeError):
@@ -54,6 +55,7 @@ class PlanDesc(ctypes.Structure):
         ("mode", ctypes.c_int),
         ("max_rows_per_call", ctypes.c_int64),
         ("attn_window_rows", ctypes.c_int64),
+        ("decode_splits", ctypes.c_int32),
     ]
 
 
@@ -80,6 +82,7 @@ def _load() -> ctypes.CDLL:
     lib.msa_dense_attn_prefill_backward.argtypes = [P, VP, VP, VP, IP, VP, FP, VP, VP, VP, ctypes.c_float, FP, FP, FP,
                                                     FP, FP, FP, VP, SZ, P]
     lib.msa_sparse_attn_decode.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
+    lib.msa_workspace_reset.argtypes = [VP, SZ]
     lib.msa_profile_kernel.argtypes = [P, ctypes.c_char_p]
     lib.msa_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.msa_last_error.restype = ctypes.c_char_p
@@ -131,9 +134,22 @@ class Plan:
         T, nbm, mr = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64()
         _check(_lib.msa_plan_info(h, ctypes.byref(T), ctypes.byref(nbm), ctypes.byref(mr)))
         self.total_rows, self.nb_max, self.max_rows_per_call = int(T.value), int(nbm.value), int(mr.value)
-        self.workspace = None
+        self._workspace = None
         if allocate:
             self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device or "cuda")
+
+    @property
+    def workspace(self):
+        return self._workspace
+
+    @workspace.setter
+    def workspace(self, t: Optional[torch.Tensor]):
+        # memory from torch's caching allocator may have held anything
+        # (another plan's metadata included): the library must copy this
+        # plan's metadata into it again on first use
+        if t is not None:
+            _check(_lib.msa_workspace_reset(ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size()))
+        self._workspace = t
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -147,7 +163,7 @@ def msa_plan(qo_lens: Sequence[int], kv_lens: Sequence[int], num_qo_heads: int, 
              num_proxy_heads: int = 0, num_proxy_kv_heads: int = 0, topk: int = 16, kv_dtype: str = "bf16",
              proxy_dtype: str = "bf16", sm_scale: Optional[float] = None, proxy_sm_scale: Optional[float] = None,
              mode: str = "prefill", max_rows_per_call: int = 0, head_dim: int = 128, page_size: int = 128,
-             device=None, allocate: bool = True, attn_window_rows: int = 0) -> Plan:
+             device=None, allocate: bool = True, attn_window_rows: int = 0, decode_splits: int = 0) -> Plan:
     n = len(kv_lens)
     qo = (ctypes.c_int32 * n)(*[int(x) for x in qo_lens]) if qo_lens is not None else None
     kv = (ctypes.c_int32 * n)(*[int(x) for x in kv_lens])
@@ -164,6 +180,7 @@ def msa_plan(qo_lens: Sequence[int], kv_lens: Sequence[int], num_qo_heads: int, 
     d.mode = {"prefill": MSA_PREFILL, "decode": MSA_DECODE}[mode]
     d.max_rows_per_call = max_rows_per_call
     d.attn_window_rows = attn_window_rows
+    d.decode_splits = decode_splits
     return Plan(d, qo, kv, device=device, allocate=allocate)
 
 

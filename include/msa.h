@@ -109,15 +109,36 @@ typedef struct {
   int64_t max_rows_per_call;   /* prefill: rows per proxy/top-k call; 0 = min(T, 32768) */
   int64_t attn_window_rows;    /* prefill: rows whose attention partials are live at
                                   once (workspace scales with it); 0 = automatic */
+  int32_t decode_splits;       /* decode: workgroups sharing one (sequence, group),
+                                  merged by log-sum-exp; 0 = automatic, else 1..64 */
 } msa_plan_desc_t;
 
 /* Build a host plan from `desc`.  Validates every field; touches no device.
  * *workspace_bytes receives the device workspace size the compute calls need
- * (the caller allocates it; a workspace belongs to one plan).  The plan is
- * released by msa_plan_destroy. */
+ * (the caller allocates it).  The plan is released by msa_plan_destroy.
+ *
+ * Workspace metadata: the first call that uses a workspace with a plan
+ * copies the plan's small metadata (row and page offsets, proxy row tiles)
+ * into it, enqueued on that call's stream.  The library records which plan's
+ * metadata each workspace holds and copies it again whenever that record does
+ * not match: another plan, another stream, or another plan's call whose
+ * workspace overlaps this metadata.  Memory written by anything outside the
+ * library must be announced with msa_workspace_reset before it is used as a
+ * workspace again.  Calls sharing one workspace must not overlap in time
+ * (their streams must be ordered).
+ * Errors: INVALID_ARG for bad fields; UNSUPPORTED for shapes that are valid
+ * but not built (head_dim or page_size != 128, G not in {1,2,4,8,16}, a
+ * sequence of more than 65536 blocks = 8388608 keys). */
 msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* plan, size_t* workspace_bytes);
 
 msa_status_t msa_plan_destroy(msa_plan_t plan);
+
+/* Forget the metadata records of every workspace whose metadata lies in
+ * [workspace, workspace + bytes) (host only, nothing is enqueued): the next
+ * call using such a workspace copies its plan's metadata again.  Call it when
+ * that memory was freed and reallocated, or written by anything other than
+ * this library.  Errors: INVALID_ARG for a NULL workspace. */
+msa_status_t msa_workspace_reset(const void* workspace, size_t bytes);
 
 /* Stage 1: proxy block max scores (README "Usage", proxy pass with
  * output_maxscore; Flash-MSA article, max-pooling of proxy scores over

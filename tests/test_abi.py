@@ -216,3 +216,34 @@ def test_training_entry_points_validate_before_touching_the_device():
     tiny = msa.msa_plan([4096], [4096], 8, 2, 2, 2, topk=1, attn_window_rows=32, allocate=False)
     assert L.msa_dense_attn_prefill_backward(*dense(tiny, none)) == msa.MSA_ERR_UNSUPPORTED and \
         b"window" in L.msa_last_error()
+
+
+def test_plan_limits_and_workspace_reset():
+    """Sequences beyond 65536 blocks are refused; the one-row low-precision
+    fused selection is bounded at 2048 blocks per sequence; the workspace
+    record reset is host only and rejects NULL."""
+    L = msa.lib()
+    with pytest.raises(msa.MsaError) as e:
+        msa.msa_plan([1], [65536 * 128 + 1], 8, 2, 2, 2, topk=4, allocate=False)
+    assert e.value.status == msa.MSA_ERR_UNSUPPORTED and "65536" in str(e.value)
+    ok = msa.msa_plan([1], [65536 * 128], 8, 2, 2, 2, topk=4, allocate=False)
+    assert ok.nb_max == 65536
+    a = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x20000)
+    none = None
+    long_row = msa.msa_plan([1, 1], [2049 * 128, 300], 8, 2, 2, 1, topk=17, proxy_dtype="fp8", allocate=False)
+    assert L.msa_proxy_topk_select(long_row.handle, a, a, a, a, a, 0, 2, a, ws, long_row.workspace_bytes, none) == \
+        msa.MSA_ERR_UNSUPPORTED and b"2048" in L.msa_last_error()
+    # one-row plans take topk above 17 (the wave-per-row selection)
+    k30 = msa.msa_plan([1, 1], [5000, 300], 8, 2, 2, 1, topk=30, allocate=False)
+    assert k30.nb_max == 40
+    assert L.msa_workspace_reset(none, 16) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_workspace_reset(ws, 1 << 20) == msa.MSA_OK
+
+
+def test_lowp_plans_reserve_the_refine_queue():
+    """A multi-row plan with a low-precision proxy reserves 64 bytes per
+    (row, group) for the exact re-scoring queue; a bf16 one does not."""
+    b = msa.msa_plan([4096], [4096], 32, 8, 8, 1, topk=16, allocate=False)
+    f = msa.msa_plan([4096], [4096], 32, 8, 8, 1, topk=16, proxy_dtype="fp8", allocate=False)
+    assert f.workspace_bytes - b.workspace_bytes >= 4096 * 8 * 64

@@ -17,13 +17,13 @@ import torch
 import oracle as O
 from synthetic.gen import workload, seed_of, FP8
 from synthetic.device_gen import make_inputs_device, to_host
-from tests._gpu import (bf16_out_to_f64, check_max_score, check_selection, check_output, fp8_score_bound,
+from tests._gpu import (bf16_out_to_f64, check_max_score, check_selection, check_output, lowp_score_bound, LOW_PRECISION_PROXY,
                         BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS)
 
 pytestmark = pytest.mark.gpu
 
 
-def _sample_rows(w, n_even, seed):
+def _sample_rows(w, n_even, seed, n_random=8):
     T = w.total_rows
     rows = set(np.linspace(0, T - 1, n_even).astype(np.int64).tolist())
     r0 = 0
@@ -33,11 +33,11 @@ def _sample_rows(w, n_even, seed):
                 rows.add(r0 + i)
         r0 += qo
     rng = np.random.default_rng(seed)
-    rows.update(rng.integers(0, T, size=8).tolist())
+    rows.update(rng.integers(0, T, size=n_random).tolist())
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def _prefill_case(n_cfg, n_even):
+def _prefill_case(n_cfg, n_even, n_random=8):
     from block_sparse_top_amd import msa
     w = workload(n_cfg)
     print(f"[fullsize] prefill workload={w.name} T={w.total_rows}", flush=True)
@@ -45,7 +45,8 @@ def _prefill_case(n_cfg, n_even):
     plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
                         w.num_proxy_kv_heads, topk=w.topk, kv_dtype=w.kv_dtype, proxy_dtype=w.proxy_dtype)
     T, R = w.total_rows, plan.max_rows_per_call
-    rows = _sample_rows(w, n_even, seed_of(n_cfg))
+    lowp = w.proxy_dtype in LOW_PRECISION_PROXY
+    rows = _sample_rows(w, n_even, seed_of(n_cfg), n_random)
     sel = torch.full((T, w.num_kv_heads, w.topk), -7, dtype=torch.int32, device="cuda")
     ms = msa.max_score_buffer(plan)
     got_ms = np.full((w.num_proxy_heads, plan.nb_max, rows.size), np.nan, np.float32)
@@ -57,12 +58,23 @@ def _prefill_case(n_cfg, n_even):
         here = np.nonzero((rows >= r0) & (rows < r0 + n))[0]
         if here.size:
             got_ms[:, :, here] = msa.max_score_rows(ms, plan, n)[:, :, torch.from_numpy(rows[here] - r0).cuda()].cpu().numpy()
-    if w.topk <= 17:  # the fused pass (what run_prefill uses) selects exactly the same blocks, every row
+    low_sel = None
+    if w.topk <= 17:
+        # the fused pass (what run_prefill uses): with a bf16 proxy the same
+        # blocks as the separate calls, every row; with a low-precision proxy
+        # the exact selection, which the checks below use
         fsel = torch.full_like(sel, -7)
         msa.msa_proxy_topk_select(plan, inp.proxy_q, inp.proxy_k_pages, inp.proxy_q_scale, inp.proxy_k_scale,
                                   inp.kv_indices, 0, T, fsel)
-        assert torch.equal(fsel, sel), f"{w.name}: fused selection differs in {int((fsel != sel).any(dim=2).sum())} rows"
-        del fsel
+        if lowp:
+            ndiff = int((fsel != sel).any(dim=2).sum())
+            print(f"[fullsize] {w.name}: exact selection differs from the low-precision top-k in {ndiff} of "
+                  f"{T * w.num_kv_heads} (row, group) pairs", flush=True)
+            low_sel = sel[torch.from_numpy(rows).cuda()].cpu().numpy()
+            sel = fsel
+        else:
+            assert torch.equal(fsel, sel), f"{w.name}: fused selection differs in {int((fsel != sel).any(dim=2).sum())} rows"
+            del fsel
     out = torch.empty((T, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((T, w.num_qo_heads), dtype=torch.float32, device="cuda")
     msa.msa_sparse_attn_prefill(plan, inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, out, lse)
@@ -78,15 +90,34 @@ def _prefill_case(n_cfg, n_even):
     ref_ms = O.proxy_block_maxscore(h["proxy_q"], h["proxy_k_pages"], h["kv_indices"], w.qo_lens, w.kv_lens, 128,
                                     w.proxy_sm_scale, w.proxy_dtype, h["proxy_q_scale"], h["proxy_k_scale"], rows=rows)
     extra = None
-    if w.proxy_dtype == FP8:
+    lay = O.Layout(w.qo_lens, w.kv_lens, 128)
+    if lowp:
         from synthetic.gen import Inputs
         hi = Inputs(w, h["kv_indices"], h["q"], h["k_pages"], h["v_pages"], proxy_q=h["proxy_q"],
                     proxy_k_pages=h["proxy_k_pages"], proxy_q_scale=h["proxy_q_scale"],
                     proxy_k_scale=h["proxy_k_scale"])
-        extra = fp8_score_bound(hi, rows, w.proxy_sm_scale)
+        extra = lowp_score_bound(hi, rows, w.proxy_sm_scale)
+        # the separate top-k call is exact on the low-precision scores it was given
+        g = np.transpose(got_ms, (2, 0, 1)).astype(np.float64)
+        for i, r in enumerate(rows):
+            for p in range(w.num_kv_heads):
+                exp = O.topk_select_row(g[i, p], lay.local(int(r)), w.topk)
+                assert np.array_equal(low_sel[i, p], exp), (int(r), p)
     check_max_score(got_ms, ref_ms, w.name, extra)
-    lay = O.Layout(w.qo_lens, w.kv_lens, 128)
-    check_selection(gsel[rows], ref_ms, np.array([lay.local(int(r)) for r in rows]), w.topk, w.name)
+    locs = np.array([lay.local(int(r)) for r in rows])
+    check_selection(gsel[rows], ref_ms, locs, w.topk, w.name)
+    # gaps at the boundary of the checked rows: how many sat in the band or
+    # just above it (where an inexact score could have moved the set)
+    gaps = []
+    for i in range(rows.size):
+        R = min(w.topk - 1, int(locs[i]))
+        if 0 < R < locs[i]:
+            cs = -np.sort(-ref_ms[i, :, :locs[i]], axis=1)
+            gaps.append(cs[:, R - 1] - cs[:, R])
+    if gaps:
+        gp = np.concatenate(gaps)
+        print(f"[fullsize] {w.name}: {gp.size} checked (row, group) pairs with a boundary; oracle gap <= 1e-3: "
+              f"{int((gp <= 1e-3).sum())}, in (1e-3, 1e-2]: {int(((gp > 1e-3) & (gp <= 1e-2)).sum())}", flush=True)
     # every row: local block present, ascending, valid padding
     loc_all = np.concatenate([(np.arange(kv - qo, kv) // 128) for qo, kv in zip(w.qo_lens, w.kv_lens)])
     valid = gsel >= 0
@@ -335,16 +366,17 @@ def test_warmup_32k():
 
 
 def test_prefill_32k_sampled_rows():
-    _prefill_case(2, 48)
+    _prefill_case(2, 1024)
 
 
 def test_prefill_varlen_128k_sampled_rows():
-    _prefill_case(3, 48)
+    _prefill_case(3, 1024)
 
 
 @pytest.mark.slow
 def test_prefill_1m_fp8_proxy_sampled_rows():
-    _prefill_case(5, 12)
+    """256 seeded rows (evenly spaced) plus the edge rows and 8 random rows."""
+    _prefill_case(5, 256)
 
 
 def test_decode_fp8_b32_131k_all_outputs():
@@ -405,17 +437,26 @@ def test_decode_step_indexer_and_decode_b32_131k(wn):
     msa.msa_sparse_attn_decode(dp, inp.q, inp.k_pages, inp.v_pages, inp.k_scale, inp.v_scale, inp.kv_indices, sel,
                                out, lse)
     torch.cuda.synchronize()
-    assert torch.equal(sel, sel2), "fused indexer selection differs from the separate calls"
     gms = msa.max_score_rows(ms, ip, S).cpu().numpy()
     gsel = sel.cpu().numpy()
     rows = np.arange(S)
+    # the separate top-k call is exact on the low-precision scores it was given;
+    # the fused call's selection is the exact one (checked against the oracle below)
+    g = np.transpose(gms, (2, 0, 1)).astype(np.float64)
+    lsel = sel2.cpu().numpy()
+    for s_ in range(S):
+        for p in range(w.num_kv_heads):
+            loc = (w.kv_lens[s_] - 1) // 128
+            assert np.array_equal(lsel[s_, p], O.topk_select_row(g[s_, p], loc, w.topk)), (s_, p)
+    print(f"[fullsize] {w.name}: exact selection differs from the low-precision top-k in "
+          f"{int((gsel != lsel).any(axis=2).sum())} of {S * w.num_kv_heads} pairs", flush=True)
     h = {k: to_host(getattr(inp, k)) for k in ("q", "kv_indices", "proxy_q", "proxy_k_pages", "proxy_q_scale",
                                                 "proxy_k_scale", "k_scale", "v_scale")}
     ref_ms = O.proxy_block_maxscore(h["proxy_q"], h["proxy_k_pages"], h["kv_indices"], [1] * S, w.kv_lens, 128,
                                     w.proxy_sm_scale, w.proxy_dtype, h["proxy_q_scale"], h["proxy_k_scale"])
     hi = Inputs(w, h["kv_indices"], h["q"], None, None, proxy_q=h["proxy_q"], proxy_k_pages=h["proxy_k_pages"],
                 proxy_q_scale=h["proxy_q_scale"], proxy_k_scale=h["proxy_k_scale"])
-    check_max_score(gms, ref_ms, w.name, fp8_score_bound(hi, rows, w.proxy_sm_scale))
+    check_max_score(gms, ref_ms, w.name, lowp_score_bound(hi, rows, w.proxy_sm_scale))
     lay = O.Layout([1] * S, w.kv_lens, 128)
     check_selection(gsel, ref_ms, np.array([lay.local(int(r)) for r in rows]), w.topk, w.name)
     # the decode on the indexer's selection: the oracle reads only the selected pages

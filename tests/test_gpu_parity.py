@@ -5,12 +5,14 @@ the attention is checked on the selection the GPU produced so that near-ties
 cannot move the output.
 
 Tolerances: max scores |gpu - oracle| <= 1e-4 + 1e-5 |oracle| (fp32
-accumulation of exact bf16 products), plus 2^-12 * scale * max_key sum_d |q_d k_d|
-for fp8 proxy scores (the fp8 matrix cores do not accumulate exactly: the
-measured worst case is 2^-12.5 of the absolute product sum); selections by the
-1e-3 band rule;
-outputs max-abs <= 2e-2 and cosine >= 0.999 (bf16 K/V) or <= 6e-2 and
->= 0.99 (fp8 K/V)."""
+accumulation of exact bf16 products), plus, for low-precision proxy scores
+(fp8, fp8 x MXFP4, MXFP4 x MXFP4 on the scaled matrix cores, which do not sum
+products exactly), the library's error bound coef * scale * max|q| * max|k|;
+selections by the 1e-3 band rule against the oracle's exact scores -- for
+low-precision proxies this is the fused call's claim (its undecided
+boundary blocks are re-scored exactly), while the separate top-k call is
+exact on the scores it is given; outputs max-abs <= 2e-2 and cosine >= 0.999
+(bf16 K/V) or <= 6e-2 and >= 0.99 (fp8 K/V)."""
 import dataclasses
 
 import numpy as np
@@ -20,7 +22,7 @@ import torch
 import oracle as O
 from synthetic.gen import Workload, make_inputs, workload, seed_of, FP8, BF16, MXFP4, MXFP4_QK
 from tests._gpu import (device_inputs, plan_for, bf16_out_to_f64, oracle_scores, check_max_score, check_selection,
-                        check_output, fp8_score_bound, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS, LOW_PRECISION_PROXY)
+                        check_output, lowp_score_bound, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS, LOW_PRECISION_PROXY)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,12 +102,20 @@ def test_prefill_stages_match_oracle(case):
     print(f"[parity] prefill case={case} T={w.total_rows} seed={seed}", flush=True)
     gms, gsel, gout, glse = run_prefill_stages(msa, inp, max_rows)
     ref_ms = oracle_scores(inp)
-    extra = (fp8_score_bound(inp, np.arange(w.total_rows), w.proxy_sm_scale) if w.proxy_dtype in LOW_PRECISION_PROXY
-             else None)
+    lowp = w.proxy_dtype in LOW_PRECISION_PROXY
+    extra = lowp_score_bound(inp, np.arange(w.total_rows), w.proxy_sm_scale) if lowp else None
     check_max_score(gms, ref_ms, case, extra)
     lay = O.Layout(w.qo_lens, w.kv_lens, w.page_size)
     locals_ = np.array([lay.local(r) for r in range(w.total_rows)])
-    check_selection(gsel, ref_ms, locals_, w.topk, case)
+    if lowp:
+        # the separate top-k call is exact on the (low-precision) scores it is given
+        g = np.transpose(gms, (2, 0, 1)).astype(np.float64)
+        for r in range(w.total_rows):
+            for p in range(w.num_kv_heads):
+                exp = O.topk_select_row(g[r, p], int(locals_[r]), w.topk)
+                assert np.array_equal(gsel[r, p], exp), (case, r, p, gsel[r, p], exp)
+    else:
+        check_selection(gsel, ref_ms, locals_, w.topk, case)
     ref_out, ref_lse = O.sparse_attention(inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, gsel, w.qo_lens,
                                           w.kv_lens, w.page_size, w.sm_scale, w.kv_dtype, inp.k_scale, inp.v_scale)
     check_output(gout, ref_out, BF16_ATOL, BF16_COS, case)
@@ -113,10 +123,12 @@ def test_prefill_stages_match_oracle(case):
 
 
 @pytest.mark.parametrize("case", list(PREFILL_CASES))
-def test_fused_proxy_topk_equals_separate_calls(case):
-    """msa_proxy_topk_select must give, bit for bit, the selection of
-    msa_proxy_block_maxscore + msa_topk_select (same fp32 scores, same tie
-    rule), and that selection passes the band rule against the oracle."""
+def test_fused_proxy_topk_selection(case):
+    """msa_proxy_topk_select: with a bf16 proxy it gives, bit for bit, the
+    selection of msa_proxy_block_maxscore + msa_topk_select (same fp32
+    scores, same tie rule); with a low-precision proxy its selection must be
+    exact under the band rule against the oracle's exact scores on every
+    row.  A sub-range call writes exactly its rows, equal to the whole call."""
     msa = _msa()
     w, seed, max_rows = PREFILL_CASES[case]
     inp = make_inputs(w, seed)
@@ -129,7 +141,15 @@ def test_fused_proxy_topk_equals_separate_calls(case):
     msa.msa_proxy_topk_select(plan, d["proxy_q"], d["proxy_k_pages"], d["proxy_q_scale"], d["proxy_k_scale"],
                               d["kv_indices"], 0, T, sel)
     fsel = sel.cpu().numpy()
-    assert np.array_equal(fsel, gsel), f"{case}: {int((fsel != gsel).any(axis=2).sum())} (row, group) differ"
+    if w.proxy_dtype in LOW_PRECISION_PROXY:
+        lay = O.Layout(w.qo_lens, w.kv_lens, w.page_size)
+        ref_ms = oracle_scores(inp)
+        check_selection(fsel, ref_ms, np.array([lay.local(r) for r in range(T)]), w.topk, case)
+        print(f"[parity] {case}: fused exact selection differs from the low-precision top-k in "
+              f"{int((fsel != gsel).any(axis=2).sum())} (row, group) pairs", flush=True)
+        gsel = fsel
+    else:
+        assert np.array_equal(fsel, gsel), f"{case}: {int((fsel != gsel).any(axis=2).sum())} (row, group) differ"
     # a sub-range writes only its rows
     if T > 3:
         r0, n = T // 3, max(1, T // 3)
