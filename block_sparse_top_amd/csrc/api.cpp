@@ -46,6 +46,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
     if (!aligned16(p)) return fail(MSA_ERR_INVALID_ARG, "%s: `%s` is not 16-byte aligned", __func__, #p); \
   } while (0)
 
+#define MSA_CHECK_PTR_FN(fn, p)                                                                  \
+  do {                                                                                           \
+    if ((p) == nullptr) return fail(MSA_ERR_INVALID_ARG, "%s: `%s` is NULL", fn, #p);            \
+    if (!aligned16(p)) return fail(MSA_ERR_INVALID_ARG, "%s: `%s` is not 16-byte aligned", fn, #p); \
+  } while (0)
+
 msa_status_t hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return ok();
   return fail(MSA_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
@@ -734,30 +740,71 @@ msa_status_t msa_dense_attn_prefill_backward(msa_plan_t p, const void* q, const 
   return hip_status(e, __func__);
 }
 
+static msa_status_t decode_args(const char* fn, msa_plan_t p, const void* q, const void* k_pages,
+                                const void* v_pages, const float* k_scale, const float* v_scale,
+                                const int32_t* kv_indices, const int32_t* kv_block_indexes, void* out, float* lse) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "%s: NULL plan", fn);
+  if (p->d.mode != MSA_DECODE) return fail(MSA_ERR_UNSUPPORTED, "%s: prefill plan", fn);
+  MSA_CHECK_PTR_FN(fn, q);
+  MSA_CHECK_PTR_FN(fn, k_pages);
+  MSA_CHECK_PTR_FN(fn, v_pages);
+  MSA_CHECK_PTR_FN(fn, kv_indices);
+  MSA_CHECK_PTR_FN(fn, kv_block_indexes);
+  MSA_CHECK_PTR_FN(fn, out);
+  if (lse && !aligned16(lse)) return fail(MSA_ERR_INVALID_ARG, "%s: lse not 16-byte aligned", fn);
+  const bool fp8 = p->d.kv_dtype == MSA_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "%s: scale pointers must be given iff K/V are fp8", fn);
+  return MSA_OK;
+}
+
+static msa_status_t decode_common(const char* fn, msa_plan_t p, const void* q, const void* k_pages,
+                                  const void* v_pages, const float* k_scale, const float* v_scale,
+                                  const int32_t* kv_indices, const int32_t* kv_block_indexes, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, msa_stream_t stream);
+
 msa_status_t msa_sparse_attn_decode(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
                                     const float* k_scale, const float* v_scale, const int32_t* kv_indices,
                                     const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
                                     size_t workspace_bytes, msa_stream_t stream) {
-  if (!p) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_decode: NULL plan");
-  if (p->d.mode != MSA_DECODE) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_decode: prefill plan");
-  MSA_CHECK_PTR(q);
-  MSA_CHECK_PTR(k_pages);
-  MSA_CHECK_PTR(v_pages);
-  MSA_CHECK_PTR(kv_indices);
-  MSA_CHECK_PTR(kv_block_indexes);
-  MSA_CHECK_PTR(out);
-  if (lse && !aligned16(lse)) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_decode: lse not 16-byte aligned");
-  const bool fp8 = p->d.kv_dtype == MSA_FP8_E4M3;
-  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr))
-    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attn_decode: scale pointers must be given iff K/V are fp8");
-  msa_status_t st = check_ws(p, workspace, workspace_bytes);
+  return decode_common(__func__, p, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes, out, lse,
+                       workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_sparse_attn_decode_noalloc(msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,
+                                            const float* k_scale, const float* v_scale, const int32_t* kv_indices,
+                                            const int32_t* kv_block_indexes, void* out, float* lse,
+                                            msa_stream_t stream) {
+  msa_status_t st = decode_args(__func__, p, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes,
+                                out, lse);
+  if (st != MSA_OK) return st;
+  void* scr = nullptr;
+  size_t scr_bytes = 0;
+  hipError_t e = msa::noalloc_scratch(&scr, &scr_bytes);
+  if (e != hipSuccess) return hip_status(e, "msa_sparse_attn_decode_noalloc: static scratch address");
+  if (p->lay.total > scr_bytes)
+    return fail(MSA_ERR_INVALID_ARG,
+                "msa_sparse_attn_decode_noalloc: the plan needs %zu bytes of scratch, above the static scratch of "
+                "%zu bytes; use msa_sparse_attn_decode with a workspace",
+                p->lay.total, scr_bytes);
+  return decode_common(__func__, p, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes, out, lse,
+                       scr, scr_bytes, stream);
+}
+
+static msa_status_t decode_common(const char* fn, msa_plan_t p, const void* q, const void* k_pages,
+                                  const void* v_pages, const float* k_scale, const float* v_scale,
+                                  const int32_t* kv_indices, const int32_t* kv_block_indexes, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, msa_stream_t stream) {
+  msa_status_t st = decode_args(fn, p, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes, out, lse);
+  if (st != MSA_OK) return st;
+  st = check_ws(p, workspace, workspace_bytes);
   if (st != MSA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
   const msa::DevMeta m = msa::dev_meta(p, workspace);
   return hip_status(msa::launch_decode(p, m, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes,
                                        out, lse, static_cast<char*>(workspace), hs),
-                    __func__);
+                    fn);
 }
 
 }  // extern "C"

@@ -141,6 +141,9 @@ hipError_t launch_bwd_prep(const msa_plan_s* p, const void* out, const void* dou
 // the fused backward has stored its sparse part in dpq and dpk.
 hipError_t launch_proxy_kl_dense(const msa_plan_s* p, const DevMeta& m, const int32_t* kv_indices,
                                  const KlOperands& kl, hipStream_t st);
+// The current device's static scratch of the allocation-free decode entry
+// point (address from hipGetSymbolAddress, looked up once per device).
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
                          const float* ks, const float* vs, const int32_t* kv_indices, const int32_t* sel,
                          void* out, float* lse, char* ws, hipStream_t st);

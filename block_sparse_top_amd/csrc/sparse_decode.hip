@@ -23,6 +23,8 @@
 //    ds_read_b64_tr_b16 for bf16); LDS operations of one wave execute in
 //    order, so the wave needs no barrier between its write and its reads;
 //  * online softmax per wave; the 8 waves merge through LDS at the end.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "msa_internal.hpp"
 
@@ -326,7 +328,35 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* part_o, 
   if (lse && lane == 0) lse[idx] = M + fast_log2(L) * kLn2;
 }
 
+// Scratch of msa_sparse_attn_decode_noalloc: the plan metadata and the split
+// partials live here instead of in a caller workspace.  Each device holds its
+// own copy (allocated with the code object, kept until the process ends);
+// host code uses only the per-device address from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
                          const float* ks, const float* vs, const int32_t* kv_indices, const int32_t* sel,

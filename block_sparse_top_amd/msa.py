@@ -26,7 +26,7 @@ ENTRY_POINTS = ("msa_plan", "msa_plan_destroy", "msa_plan_info", "msa_proxy_bloc
                 "msa_proxy_topk_select", "msa_sparse_attn_prefill", "msa_sparse_attn_prefill_rows",
                 "msa_sparse_attn_prefill_backward", "msa_sparse_attn_prefill_backward_kl",
                 "msa_dense_attn_prefill", "msa_dense_attn_prefill_backward",
-                "msa_sparse_attn_decode", "msa_workspace_reset", "msa_last_error", "msa_profile_kernel",
+                "msa_sparse_attn_decode", "msa_sparse_attn_decode_noalloc", "msa_workspace_reset", "msa_last_error", "msa_profile_kernel",
                 "msa_profile_read")
 
 
@@ -82,6 +82,7 @@ def _load() -> ctypes.CDLL:
     lib.msa_dense_attn_prefill_backward.argtypes = [P, VP, VP, VP, IP, VP, FP, VP, VP, VP, ctypes.c_float, FP, FP, FP,
                                                     FP, FP, FP, VP, SZ, P]
     lib.msa_sparse_attn_decode.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, VP, SZ, P]
+    lib.msa_sparse_attn_decode_noalloc.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, P]
     lib.msa_workspace_reset.argtypes = [VP, SZ]
     lib.msa_profile_kernel.argtypes = [P, ctypes.c_char_p]
     lib.msa_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -265,6 +266,17 @@ def msa_sparse_attn_decode(plan: Plan, q, k_pages, v_pages, k_scale, v_scale, kv
     _check(_lib.msa_sparse_attn_decode(plan.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
                                        _ptr(v_scale), _ptr(kv_indices), _ptr(kv_block_indexes), _ptr(out),
                                        _ptr(lse), _ptr(plan.workspace), plan.workspace_bytes, _stream()))
+    return out, lse
+
+
+def msa_sparse_attn_decode_noalloc(plan: Plan, q, k_pages, v_pages, k_scale, v_scale, kv_indices, kv_block_indexes,
+                                   out, lse=None):
+    """msa_sparse_attn_decode with the library's static per-device scratch
+    instead of the plan's workspace (no allocation; calls on one device must
+    not overlap)."""
+    _check(_lib.msa_sparse_attn_decode_noalloc(plan.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                               _ptr(v_scale), _ptr(kv_indices), _ptr(kv_block_indexes), _ptr(out),
+                                               _ptr(lse), _stream()))
     return out, lse
 
 

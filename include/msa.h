@@ -369,6 +369,22 @@ msa_status_t msa_sparse_attn_decode(msa_plan_t plan, const void* q, const void* 
                                     const int32_t* kv_block_indexes, void* out, float* lse, void* workspace,
                                     size_t workspace_bytes, msa_stream_t stream);
 
+/* Allocation-free form of msa_sparse_attn_decode, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments and results, without
+ * a workspace.  The plan metadata and split partials go to a static scratch
+ * array of 16 MiB per device, part of the library's code object (each device
+ * the library runs on holds its own copy until the process ends).  The call
+ * allocates nothing.  Every call on one device shares that device's scratch:
+ * calls that overlap in time on one device (different streams, or different
+ * host threads without stream ordering) race.  Nothing in the scratch needs
+ * to start at zero.  Errors: as msa_sparse_attn_decode, plus INVALID_ARG when
+ * the plan's workspace size (msa_plan's workspace_bytes) exceeds 16 MiB. */
+msa_status_t msa_sparse_attn_decode_noalloc(msa_plan_t plan, const void* q, const void* k_pages,
+                                            const void* v_pages, const float* k_scale, const float* v_scale,
+                                            const int32_t* kv_indices, const int32_t* kv_block_indexes, void* out,
+                                            float* lse, msa_stream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* msa_last_error(void);
 
