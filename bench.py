@@ -221,6 +221,117 @@ def copy_calibration(reps=3):
 
 
 # ----------------------------------------------------------------------------
+# peaks measured on this device, reported beside the published ones
+# ----------------------------------------------------------------------------
+MEASURED = {}
+
+
+def measure_peaks(msa):
+    """A plain streaming copy (int32 bitwise not over 2 GiB read + 2 GiB
+    written, HIP events) for HBM, and the library's matrix-core loop
+    (msa_diag_mfma_rate: register operands, two waves per SIMD) for bf16, fp8
+    and FP4."""
+    import torch
+    n = (2 << 30) // 4
+    src = torch.arange(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        torch.bitwise_not(src, out=dst)
+    e1.record()
+    e1.synchronize()
+    copy_ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    MEASURED.update({
+        "hbm_gbs": 2.0 * n * 4 / (copy_ms * 1e-3) / 1e9,
+        "bf16_tflops": msa.msa_diag_mfma_rate("bf16", 20000),
+        "fp8_tflops": msa.msa_diag_mfma_rate("fp8", 20000),
+        "fp4_tflops": msa.msa_diag_mfma_rate("mxfp4_qk", 20000),
+        "method": "HBM: int32 streaming copy of 2 GiB read + 2 GiB written (HIP events, 10 launches); matrix "
+                  "cores: msa_diag_mfma_rate, 2 waves per SIMD, 4 independent 32x32 MFMA chains on register "
+                  "operands, 20000 rounds",
+    })
+    return dict(MEASURED)
+
+
+MEASURED_KEY = {"GB/s": "hbm_gbs"}
+PEAK_KEY = {PEAK_BF16_TFLOPS: "bf16_tflops", PEAK_FP8_TFLOPS: "fp8_tflops", PEAK_FP4_TFLOPS: "fp4_tflops",
+            PEAK_HBM_GBS: "hbm_gbs"}
+
+
+def with_measured(roof: dict) -> dict:
+    """Add the fraction of the peak measured on this device to a roofline entry."""
+    key = PEAK_KEY.get(roof.get("peak"))
+    mp = MEASURED.get(key) if key else None
+    if mp and roof.get("achieved") is not None:
+        roof["measured_peak"] = mp
+        roof["frac_measured"] = roof["achieved"] / mp
+    return roof
+
+
+def time_by_duration(step, warm_ms=50.0, rep_ms=200.0):
+    """At least warm_ms of warm-up steps, then one timed block of steps sized
+    from the warm-up rate to last at least rep_ms, between a synchronize on
+    both sides.  Returns (ms per step, steps timed)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+                break
+    per = (time.perf_counter() - t0) * 1e3 / n
+    reps = max(16, int(math.ceil(rep_ms / per)))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / reps, reps
+
+
+def host_cost_us(step, n=200):
+    """Host time to enqueue one step (binding, argument checks, launches),
+    measured without waiting for the device."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        step()
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    return (t1 - t0) * 1e6 / n
+
+
+def graph_time(step, sets, warm_ms=50.0, rep_ms=200.0):
+    """The same steps captured once in a HIP graph (`sets` consecutive steps,
+    so the rotated input sets all appear) and replayed: device time per step
+    without the host's launch cost."""
+    import torch
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):       # metadata uploaded on the capture stream before capture
+        for _ in range(2 * sets):
+            step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(sets):
+            step()
+    ms, reps = time_by_duration(g.replay, warm_ms, rep_ms)
+    del g
+    return ms / sets, reps * sets
+
+
+# ----------------------------------------------------------------------------
 # algorithmic work
 # ----------------------------------------------------------------------------
 def visible_keys_per_row(sel, qo_lens, kv_lens, device):
@@ -292,7 +403,7 @@ def timed_with_kernel(msa, plan, step, steps, warmup, kernel):
     return ms_step, kms / max(1, launches), launches
 
 
-def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
+def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0, profile_reps=3):
     import torch
     from synthetic.gen import workload, seed_of
     from synthetic.device_gen import make_inputs_device
@@ -313,8 +424,10 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
 
     step()
     torch.cuda.synchronize()
-    stages = (["proxy_topk"] if w.topk <= 17 else ["proxy_maxscore", "topk_select"]) + ["csr", "partial_attn", "merge"]
-    per_kernel = kernel_profile(msa, plan, step, stages)
+    lowp = w.proxy_dtype != "bf16"
+    stages = ((["proxy_topk"] + (["topk_refine"] if lowp else [])) if w.topk <= 17
+              else ["proxy_maxscore", "topk_select"]) + ["csr", "partial_attn", "merge"]
+    per_kernel = kernel_profile(msa, plan, step, stages, reps=profile_reps)
     dominant = max(per_kernel, key=lambda n: per_kernel[n][0])
     ms_step, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, dominant)
     launches_per_step = launches // steps
@@ -331,20 +444,21 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0):
     else:  # bandwidth-bound helper kernels: count their compulsory bytes
         work, peak, unit, bound = None, PEAK_HBM_GBS, "GB/s", "hbm"
     achieved = (work / (k_ms * 1e-3) / 1e12) if (work is not None) else None
-    roof = {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": (achieved / peak) if achieved is not None else None,
-            "traffic": traffic_from_profiles(dominant, w.name), "avg_launch_ms": k_ms,
-            "launches_per_step": launches_per_step,
-            "work_per_launch": work, "work_unit": "FLOP" if unit == "TFLOP/s" else "B"}
+    roof = with_measured({"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                          "frac": (achieved / peak) if achieved is not None else None,
+                          "traffic": traffic_from_profiles(dominant, w.name), "avg_launch_ms": k_ms,
+                          "launches_per_step": launches_per_step,
+                          "work_per_launch": work, "work_unit": "FLOP" if unit == "TFLOP/s" else "B"})
     stage_ms = {n: v[0] for n, v in per_kernel.items()}
     pstage = "proxy_topk" if "proxy_topk" in stage_ms else "proxy_maxscore"
     p_ach = f_proxy / (stage_ms[pstage] * 1e-3) / 1e12
-    proxy_roof = {"kernel": pstage, "proxy_dtype": w.proxy_dtype, "achieved": p_ach, "peak": proxy_peak,
-                  "unit": "TFLOP/s", "frac": p_ach / proxy_peak}
+    proxy_roof = with_measured({"kernel": pstage, "proxy_dtype": w.proxy_dtype, "achieved": p_ach, "peak": proxy_peak,
+                                "unit": "TFLOP/s", "frac": p_ach / proxy_peak})
     tflops = (f_main + f_proxy) / (ms_step * 1e-3) / 1e12
     res = {
         "workload": w.name, "tok_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
         "tflops": tflops, "mfma_util": tflops / PEAK_BF16_TFLOPS,
+        "mfma_util_measured": tflops / MEASURED["bf16_tflops"] if MEASURED.get("bf16_tflops") else None,
         "flops": {"proxy": f_proxy, "main": f_main}, "stage_ms": stage_ms, "roofline": roof,
         "proxy_roofline": proxy_roof,
         "config": {"workload": w.name, "qo_lens": w.qo_lens if len(w.qo_lens) <= 8 else None, "total_rows": T,
@@ -422,6 +536,7 @@ def backward_bench(msa, n_cfg, steps, warmup, kl=False):
     roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_from_profiles(dominant, w.name),
             "avg_launch_ms": k_ms, "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "FLOP"}
+    roof = with_measured(roof)
     name = w.name + ("_backward_kl" if kl else "_backward")
     grads = "dq, dk, dv, dproxy_q, dproxy_k (fp32)" if kl else "dq, dk, dv (fp32)"
     return {
@@ -488,6 +603,7 @@ def warmup_bench(msa, n_cfg, steps, warmup):
     roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_from_profiles(dominant, w.name),
             "avg_launch_ms": k_ms, "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "FLOP"}
+    roof = with_measured(roof)
     name = w.name + "_warmup"
     return {
         "workload": name, "tok_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
@@ -526,7 +642,13 @@ def decode_bench(msa, steps, warmup, sets=4):
     step()
     torch.cuda.synchronize()
     per_kernel = kernel_profile(msa, plan, step, ["decode", "decode_merge"])
-    ms_step, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, "decode")
+    # the kernel by its own HIP events (a separate pass); the step by duration,
+    # eagerly and replayed from a HIP graph, with no profiling events attached
+    _, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, "decode")
+    launches_per_step = max(1, launches // steps)
+    ms_step, timed = time_by_duration(step)
+    host_us = host_cost_us(step)
+    g_ms, g_steps = graph_time(step, sets)
     # compulsory bytes of one decode launch: selected K and V pages (fp8) + q + scales + indices + partials out
     nsel = sum(int((s >= 0).sum().item()) for s in sels) / sets
     kv_bytes = nsel * 2 * 128 * 128
@@ -534,12 +656,18 @@ def decode_bench(msa, steps, warmup, sets=4):
     work = kv_bytes + q_bytes
     achieved = work / (k_ms * 1e-3) / 1e9
     step_bytes = work + w.num_seqs * w.num_qo_heads * 128 * 2
-    roof = {"kernel": "decode", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles("decode", w.name),
-            "avg_launch_ms": k_ms, "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "B"}
+    roof = with_measured({"kernel": "decode", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                          "traffic": traffic_from_profiles("decode", w.name), "avg_launch_ms": k_ms,
+                          "launches_per_step": launches_per_step, "work_per_launch": work, "work_unit": "B"})
     return {
         "workload": w.name, "tok_per_s": w.num_seqs / (ms_step * 1e-3), "ms_per_step": ms_step,
+        "timing": f"by duration: >= 50 ms warm-up, then {timed} steps (>= 200 ms) between synchronizes, no "
+                  f"profiling events",
         "step_gbs": step_bytes / (ms_step * 1e-3) / 1e9, "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "host_us_per_step": host_us,
+        "graph": {"ms_per_step": g_ms, "tok_per_s": w.num_seqs / (g_ms * 1e-3), "steps": g_steps,
+                  "hbm_frac_step": step_bytes / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "stage_ms": {n: v[0] for n, v in per_kernel.items()}, "roofline": roof,
         "config": {"workload": w.name, "batch": w.num_seqs, "kv_len": w.kv_lens[0], "num_qo_heads": w.num_qo_heads,
                    "num_kv_heads": w.num_kv_heads, "slots": w.topk, "kv_dtype": "fp8", "rotated_sets": sets},
@@ -585,7 +713,10 @@ def decode_step_bench(msa, steps, warmup, sets=4, wn=6):
     for plan, names in ((ip, ["proxy_topk", "topk_select"]), (dp, ["decode"])):
         for n, v in kernel_profile(msa, plan, step, names).items():
             stage[n] = v[0]
-    ms_step, k_ms, launches = timed_with_kernel(msa, ip, step, steps, warmup, "proxy_topk")
+    _, k_ms, launches = timed_with_kernel(msa, ip, step, steps, warmup, "proxy_topk")
+    ms_step, timed = time_by_duration(step)
+    host_us = host_cost_us(step)
+    g_ms, g_steps = graph_time(step, sets)
     # compulsory bytes of one indexer launch: every visible proxy-K block
     # (fp8: 128 x 128 B; MXFP4: 128 x (64 + 4) B) + the fp8 proxy q
     nb = sum(-(-L // 128) for L in w.kv_lens)
@@ -593,11 +724,16 @@ def decode_step_bench(msa, steps, warmup, sets=4, wn=6):
     work = nb * w.num_proxy_kv_heads * kblock + S * w.num_proxy_heads * 128
     achieved = work / (k_ms * 1e-3) / 1e9
     kname = "proxy_onerow" if w.proxy_dtype == "fp8" else "proxy_onerow_mxfp4"
-    roof = {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles(kname, w.name), "avg_launch_ms": k_ms,
-            "launches_per_step": launches // steps, "work_per_launch": work, "work_unit": "B"}
+    roof = with_measured({"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                          "traffic": traffic_from_profiles(kname, w.name), "avg_launch_ms": k_ms,
+                          "launches_per_step": max(1, launches // steps), "work_per_launch": work, "work_unit": "B"})
     return {
         "workload": w.name, "tok_per_s": S / (ms_step * 1e-3), "ms_per_step": ms_step, "stage_ms": stage,
+        "timing": f"by duration: >= 50 ms warm-up, then {timed} steps (>= 200 ms) between synchronizes, no "
+                  f"profiling events",
+        "host_us_per_step": host_us,
+        "graph": {"ms_per_step": g_ms, "tok_per_s": S / (g_ms * 1e-3), "steps": g_steps},
         "roofline": roof,
         "config": {"workload": w.name, "batch": S, "kv_len": w.kv_lens[0], "num_qo_heads": w.num_qo_heads,
                    "num_kv_heads": w.num_kv_heads, "num_proxy_heads": w.num_proxy_heads,
@@ -630,9 +766,33 @@ def cpu_baseline(w, inp, sel, rows=256):
     O.sparse_attention(h["q"], h["k_pages"], h["v_pages"], h["kv_indices"], full_sel, w.qo_lens, w.kv_lens, 128,
                        w.sm_scale, rows=sample)
     dt = time.perf_counter() - t0
+    model, physical = cpu_info()
     return {"value": len(sample) / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "physical_cores": physical, "logical_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{len(sample)} rows evenly spaced over the {T}-row {w.name} workload "
                       f"(proxy scores, top-k and attention for each), {dt:.1f} s wall"}
+
+
+def cpu_info():
+    """(model name, physical cores among the CPUs this process may run on)."""
+    model, cores = None, set()
+    allowed = os.sched_getaffinity(0)
+    try:
+        cpu = phys = None
+        for ln in open("/proc/cpuinfo"):
+            k, _, v = ln.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "processor":
+                cpu, phys = int(v), None
+            elif k == "model name" and model is None:
+                model = v
+            elif k == "physical id":
+                phys = v
+            elif k == "core id" and cpu in allowed:
+                cores.add((phys, v))
+    except OSError:
+        pass
+    return model, (len(cores) or None)
 
 
 def main():
@@ -641,11 +801,13 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode entries")
-    ap.add_argument("--extra", default="prefill_128k,prefill_32k_mxfp4,prefill_32k_backward,prefill_32k_backward_kl,"
-                                       "warmup_32k,decode_131k,decode_step_131k,decode_step_mxfp4_131k",
-                    help="comma-separated extra entries: prefill_128k, prefill_32k_mxfp4, prefill_32k_backward, "
-                         "prefill_32k_backward_kl, prefill_128k_backward (not by default), warmup_32k, decode_131k, "
-                         "decode_step_131k, decode_step_mxfp4_131k (or none)")
+    ap.add_argument("--extra", default="prefill_128k,prefill_1m_fp8proxy,prefill_32k_mxfp4,prefill_32k_backward,"
+                                       "prefill_32k_backward_kl,warmup_32k,decode_131k,decode_step_131k,"
+                                       "decode_step_mxfp4_131k",
+                    help="comma-separated extra entries: prefill_128k, prefill_1m_fp8proxy, prefill_32k_mxfp4, "
+                         "prefill_32k_backward, prefill_32k_backward_kl, prefill_128k_backward (not by default), "
+                         "warmup_32k, decode_131k, decode_step_131k, decode_step_mxfp4_131k (or none)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -671,7 +833,8 @@ def main():
     torch.cuda.set_device(0)
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
-        if e not in ("prefill_128k", "prefill_32k_mxfp4", "prefill_32k_backward", "prefill_32k_backward_kl",
+        if e not in ("prefill_128k", "prefill_1m_fp8proxy", "prefill_32k_mxfp4", "prefill_32k_backward",
+                     "prefill_32k_backward_kl",
                      "prefill_128k_backward", "warmup_32k", "decode_131k", "decode_step_131k",
                      "decode_step_mxfp4_131k"):
             ap.error(f"unknown extra entry {e}")
@@ -682,6 +845,10 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench-mark] {key} {time.monotonic_ns()}", file=sys.stderr, flush=True)
 
+    peaks = None
+    if not args.no_peaks:
+        print("[bench] measured peaks (streaming copy, matrix-core loops)", file=sys.stderr, flush=True)
+        peaks = measure_peaks(msa)
     print("[bench] prefill 32k", file=sys.stderr, flush=True)
     mark("main")
     main_res, (w, inp, sel) = prefill_bench(msa, 2, args.steps, args.warmup)
@@ -691,6 +858,13 @@ def main():
         mark("prefill_128k")
         r3, _ = prefill_bench(msa, 3, max(2, args.steps // 2), 1)
         extra["prefill_128k"] = r3
+    if "prefill_1m_fp8proxy" in extras:
+        print("[bench] prefill 1M tokens, fp8 proxy", file=sys.stderr, flush=True)
+        mark("prefill_1m_fp8proxy")
+        r5, _ = prefill_bench(msa, 5, 2, 1, profile_reps=1)
+        extra["prefill_1m_fp8proxy"] = r5
+        import torch as _t
+        _t.cuda.empty_cache()
     if "prefill_32k_mxfp4" in extras:
         print("[bench] prefill 32k, MXFP4 proxy q and K, MXFP4 K/V", file=sys.stderr, flush=True)
         mark("prefill_32k_mxfp4")
@@ -735,7 +909,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), device generator)",
         "config": main_res["config"], "roofline": main_res["roofline"], "cpu_baseline": cpu,
         "mfma_util": main_res["mfma_util"], "tflops": main_res["tflops"], "stage_ms": main_res["stage_ms"],
-        "flops": main_res["flops"], "proxy_roofline": main_res["proxy_roofline"], "extra": extra,
+        "flops": main_res["flops"], "proxy_roofline": main_res["proxy_roofline"],
+        "mfma_util_measured": main_res["mfma_util_measured"], "measured_peaks": peaks, "extra": extra,
     }
     print(json.dumps(line), flush=True)
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsa.so")
 SOURCES = ["api.cpp", "proxy_maxscore.hip", "topk_select.hip", "sparse_prefill.hip", "sparse_decode.hip",
-           "proxy_kl.hip", "dense_attn.hip"]
+           "proxy_kl.hip", "dense_attn.hip", "diag.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -102,21 +102,36 @@ template <Fmt F>
 __device__ __forceinline__ float exact_block_dotmax(const ExactQ& q, const uint8_t* blk, int nkeys) {
   const int lane = threadIdx.x & 63;
   const int dq = lane >> 4, kk = lane & 15;
+  // every load of the block is issued before any arithmetic (one round trip)
+  constexpr int kV = F == Fmt::FP8 ? 2 : 1;
+  i32x4 x[8][kV];
+  uint32_t ke[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int key = 16 * i + kk;
+    if constexpr (F == Fmt::FP8) {
+      const i32x4* src = reinterpret_cast<const i32x4*>(blk + key * 128 + 32 * dq);
+      x[i][0] = src[0];
+      x[i][kV - 1] = src[1];
+      ke[i] = 127;
+    } else {
+      x[i][0] = *reinterpret_cast<const i32x4*>(blk + key * 64 + 16 * dq);
+      ke[i] = blk[128 * 64 + key * 4 + dq];
+    }
+  }
   float best = kNegInf;
-#pragma unroll 2
+#pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int key = 16 * i + kk;
     float acc = 0.f;
     if constexpr (F == Fmt::FP8) {
-      const i32x4* src = reinterpret_cast<const i32x4*>(blk + key * 128 + 32 * dq);
-      const i32x4 x0 = src[0], x1 = src[1];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const i32x4 x = h ? x1 : x0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)x[w], 1.0f, false);
-          const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)x[w], 1.0f, true);
+          const uint32_t c = (uint32_t)x[i][h][w];
+          const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
+          const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, true);
           const int d = 16 * h + 4 * w;
           acc = __builtin_fmaf(q.v[d], a[0], acc);
           acc = __builtin_fmaf(q.v[d + 1], a[1], acc);
@@ -125,16 +140,14 @@ __device__ __forceinline__ float exact_block_dotmax(const ExactQ& q, const uint8
         }
       }
     } else {
-      const i32x4 x = *reinterpret_cast<const i32x4*>(blk + key * 64 + 16 * dq);
-      const uint32_t ke = blk[128 * 64 + key * 4 + dq];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t c = (uint32_t)x[w];
+        const uint32_t c = (uint32_t)x[i][0][w];
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc = __builtin_fmaf(q.v[8 * w + n], e2m1_value((c >> (4 * n)) & 15u), acc);
       }
       // the key's and (MXFP4 q) the row's block scales: exact powers of two
-      acc = __builtin_ldexpf(acc, (int)ke - 127 + (int)q.e - 127);
+      acc = __builtin_ldexpf(acc, (int)ke[i] - 127 + (int)q.e - 127);
     }
     // the four dim blocks of a key sit in lanes kk, kk + 16, kk + 32, kk + 48
     acc += __shfl_xor(acc, 16);

@@ -939,7 +939,7 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
   if (refine) {
     // waves loop over the queued pairs; the queue length is read on the device
     ProfEvents pe(p, "topk_refine");
-    const dim3 rg((unsigned)(2 * p->num_cu)), rb(256);
+    const dim3 rg((unsigned)(4 * p->num_cu)), rb(256);
     switch (p->d.proxy_dtype) {
       case MSA_MXFP4_QK: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::MX4QK>, rg, rb, 0, st, pe.start, pe.stop, 0, a, m); break;
       case MSA_MXFP4: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::MX4K>, rg, rb, 0, st, pe.start, pe.stop, 0, a, m); break;

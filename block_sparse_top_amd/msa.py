@@ -27,7 +27,7 @@ ENTRY_POINTS = ("msa_plan", "msa_plan_destroy", "msa_plan_info", "msa_proxy_bloc
                 "msa_sparse_attn_prefill_backward", "msa_sparse_attn_prefill_backward_kl",
                 "msa_dense_attn_prefill", "msa_dense_attn_prefill_backward",
                 "msa_sparse_attn_decode", "msa_sparse_attn_decode_noalloc", "msa_workspace_reset", "msa_last_error", "msa_profile_kernel",
-                "msa_profile_read")
+                "msa_profile_read", "msa_diag_mfma_rate")
 
 
 class MsaError(RuntimeError):
@@ -85,6 +85,7 @@ def _load() -> ctypes.CDLL:
     lib.msa_sparse_attn_decode_noalloc.argtypes = [P, VP, VP, VP, FP, FP, IP, IP, VP, FP, P]
     lib.msa_workspace_reset.argtypes = [VP, SZ]
     lib.msa_profile_kernel.argtypes = [P, ctypes.c_char_p]
+    lib.msa_diag_mfma_rate.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
     lib.msa_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.msa_last_error.restype = ctypes.c_char_p
     for name in ENTRY_POINTS:
@@ -290,6 +291,13 @@ def msa_profile_read(plan: Plan):
     ms, n = ctypes.c_double(), ctypes.c_int64()
     _check(_lib.msa_profile_read(plan.handle, ctypes.byref(ms), ctypes.byref(n)))
     return float(ms.value), int(n.value)
+
+
+def msa_diag_mfma_rate(dtype: str, iters: int = 20000) -> float:
+    """Dense matrix-core TFLOP/s this device sustains (diagnostic)."""
+    t = ctypes.c_double()
+    _check(_lib.msa_diag_mfma_rate(_dtype_code(dtype), iters, ctypes.byref(t)))
+    return float(t.value)
 
 
 def max_score_buffer(plan: Plan, device=None) -> torch.Tensor:

@@ -405,6 +405,15 @@ msa_status_t msa_plan_info(msa_plan_t plan, int64_t* total_rows, int32_t* nb_max
 msa_status_t msa_profile_kernel(msa_plan_t plan, const char* kernel);
 msa_status_t msa_profile_read(msa_plan_t plan, double* total_ms, int64_t* launches);
 
+/* Diagnostic, not part of the path: the matrix-core rate the current device
+ * sustains.  dtype MSA_BF16 (v_mfma_f32_32x32x16_bf16), MSA_FP8_E4M3 or
+ * MSA_MXFP4_QK (v_mfma_scale_f32_32x32x64_f8f6f4 on e4m3 or E2M1 operands,
+ * unit block scales); every SIMD runs two waves of `iters`
+ * rounds of four independent accumulations on register operands.  Runs on the
+ * null stream and waits for it; *tflops receives dense TFLOP/s.  Errors:
+ * INVALID_ARG (bad dtype, iters < 1, NULL), HIP. */
+msa_status_t msa_diag_mfma_rate(int32_t dtype, int32_t iters, double* tflops);
+
 #ifdef __cplusplus
 }
 #endif
