@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "partial_attn": "sparse_prefill.hip", "merge": "sparse_prefill.hip", "decode": "sparse_decode.hip",
     "decode_merge": "sparse_decode.hip", "proxy_onerow": "proxy_maxscore.hip",
     "proxy_onerow_mxfp4": "proxy_maxscore.hip", "topk_wave": "topk_select.hip",
+    "topk_wave_exact": "topk_select.hip", "topk_refine": "proxy_maxscore.hip",
     "kl_dq_sum": "sparse_prefill.hip", "kl_dense_dq": "proxy_kl.hip", "kl_dense_dk": "proxy_kl.hip",
     "dense_fwd": "dense_attn.hip", "dense_dq": "dense_attn.hip", "dense_dkv": "sparse_prefill.hip",
 }
@@ -75,15 +76,27 @@ def traffic_from_profiles(kernel: str, workload: str):
 # rocprofv3 summaries (run on the host from the CSV files rocprofv3 wrote)
 # ----------------------------------------------------------------------------
 COPY_BYTES = 1 << 30           # calibration copy: bytes read and bytes written per launch
-PMC_ARGS = ("--steps 2 --warmup 1 --no-cpu-baseline --extra prefill_32k_backward,decode_131k,decode_step_131k "
-            "--copy-calibration")
+PMC_ARGS = ("--steps 2 --warmup 1 --no-cpu-baseline --no-peaks --profile-run --extra "
+            "prefill_32k_backward,decode_131k,decode_step_131k,decode_step_mxfp4_131k --copy-calibration")
+# counters are collected on the library's kernels and the calibration copy only
+PMC_FILTER = '--kernel-include-regex "msa|bitwise_not"'
 PMC_CMDS = {
-    "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o f -- python bench.py {PMC_ARGS}",
-    "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o w -- python bench.py {PMC_ARGS}",
+    "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE {PMC_FILTER} -f csv -d gpurun_out/pmc_fetch -o f -- python bench.py "
+                  f"{PMC_ARGS}",
+    "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE {PMC_FILTER} -f csv -d gpurun_out/pmc_write -o w -- python bench.py "
+                  f"{PMC_ARGS}",
 }
 TRACE_CMD = "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/kt -o kt -- python bench.py"
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+                 "SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE")
+MFMA_PMC_ARGS = ("--steps 2 --warmup 1 --no-cpu-baseline --no-peaks --profile-run --extra "
+                 "prefill_128k,prefill_32k_mxfp4,prefill_32k_backward,warmup_32k,decode_131k,decode_step_131k")
+MFMA_CMD = (f"rocprofv3 --pmc {MFMA_COUNTERS} {PMC_FILTER} -f csv -d gpurun_out/pmc_mfma -o m -- python bench.py "
+            f"{MFMA_PMC_ARGS}")
+NUM_CU, SIMD_PER_CU, NUM_XCD = 256, 4, 8
 SECTION_OF_KERNEL = {"decode": "decode_fp8_b32_131k", "decode_merge": "decode_fp8_b32_131k",
                      "proxy_onerow": "decode_step_b32_131k", "topk_wave": "decode_step_b32_131k",
+                     "topk_wave_exact": "decode_step_b32_131k",
                      "proxy_onerow_mxfp4": "decode_step_mxfp4_b32_131k"}
 
 
@@ -141,6 +154,86 @@ def summarize_counters(fetch_csv: str, write_csv: str):
         open(path, "w").write(txt)
         written.append(path)
     return written
+
+
+def summarize_mfma(mfma_csv: str, bench_err: str, out_name: str):
+    """Matrix-core and LDS counters per library kernel and workload from one
+    rocprofv3 --pmc run (MFMA_CMD): MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE x 1024 SIMDs); counted matrix FLOPs = MOPS x 512 (the
+    counters count 512-FLOP units); LDS active = SQ_LDS_IDX_ACTIVE /
+    (GRBM_GUI_ACTIVE x 256 CUs); bank conflicts per LDS-active cycle.  A
+    dispatch belongs to the workload bench.py marked last before it."""
+    import collections
+    import csv
+    disp = collections.defaultdict(lambda: collections.defaultdict(float))
+    kname, grbm, start_ts, dur_ns = {}, collections.defaultdict(float), {}, {}
+    for r in csv.DictReader(open(mfma_csv)):
+        k = _short_kernel(r["Kernel_Name"])
+        if k is None:
+            continue
+        d = int(r["Dispatch_Id"])
+        kname[d] = k
+        start_ts[d] = int(r.get("Start_Timestamp") or 0)
+        c, v = r["Counter_Name"], float(r["Counter_Value"])
+        if c == "GRBM_GUI_ACTIVE":
+            # reported summed over the 8 XCDs: per-XCD busy cycles
+            grbm[d] = max(grbm[d], v / NUM_XCD)
+        else:
+            disp[d][c] += v
+        dur_ns[d] = int(r.get("End_Timestamp") or 0) - int(r.get("Start_Timestamp") or 0)
+    # workload of each dispatch: the last "[bench-mark] <entry> <ns>" line (the
+    # host's monotonic clock, the trace's time origin) before its start
+    import bisect
+    names = {"main": "prefill_32k_gqa4", "prefill_128k": "prefill_varlen_128k_gqa8",
+             "prefill_32k_mxfp4": "prefill_32k_gqa4_mxfp4", "prefill_32k_backward": "prefill_32k_gqa4_backward",
+             "warmup_32k": "prefill_32k_gqa4_warmup", "decode_131k": "decode_fp8_b32_131k",
+             "decode_step_131k": "decode_step_b32_131k", "decode_step_mxfp4_131k": "decode_step_mxfp4_b32_131k",
+             "prefill_1m_fp8proxy": "prefill_1m_fp8proxy"}
+    marks = sorted((int(ln.split()[2]), names.get(ln.split()[1], ln.split()[1]))
+                   for ln in open(bench_err).read().splitlines() if ln.startswith("[bench-mark] "))
+    mark_t = [t for t, _ in marks]
+    sec = {}
+    for d, t0 in start_ts.items():
+        if kname.get(d) in (None, "copy"):
+            continue
+        i = bisect.bisect_right(mark_t, t0) - 1
+        sec[d] = marks[i][1] if i >= 0 else "?"
+    g = collections.OrderedDict()
+    for d in sorted(sec):
+        g.setdefault((sec[d], kname[d]), []).append(d)
+    out = ["# Matrix-core and LDS counters per kernel (rocprofv3 --pmc, per dispatch, averaged)",
+           f"# command: {MFMA_CMD}",
+           f"# summary: python bench.py --summarize-mfma gpurun_out/pmc_mfma/m_counter_collection.csv <bench stderr> "
+           f"{out_name}",
+           "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs); counted matrix FLOPs = "
+           "(MOPS_BF16 + MOPS_F8 + MOPS_F6F4) x 512; LDS active = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE x 256 CUs); "
+           "conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+           "# GRBM_GUI_ACTIVE is reported summed over the 8 XCDs; per-XCD cycles / dispatch duration gives the "
+           "clock column",
+           "", "| workload | kernel | dispatches | avg us | clock GHz | MFMA busy | bf16 GFLOP | fp8 GFLOP | "
+               "fp4/fp6 GFLOP | counted TFLOP/s | LDS active | LDS conflicts |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    rows = []
+    for (wl, k), ds in g.items():
+        cyc = np.mean([grbm[d] for d in ds])
+        busy = np.mean([disp[d]["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, grbm[d] * NUM_CU * SIMD_PER_CU) for d in ds])
+        fb = np.mean([disp[d]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 for d in ds]) / 1e9
+        f8 = np.mean([disp[d]["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512 for d in ds]) / 1e9
+        f4 = np.mean([disp[d]["SQ_INSTS_VALU_MFMA_MOPS_F6F4"] * 512 for d in ds]) / 1e9
+        lds = np.mean([disp[d]["SQ_LDS_IDX_ACTIVE"] / max(1.0, grbm[d] * NUM_CU) for d in ds])
+        bc = np.mean([disp[d]["SQ_LDS_BANK_CONFLICT"] / max(1.0, disp[d]["SQ_LDS_IDX_ACTIVE"]) for d in ds])
+        us = np.mean([dur_ns[d] for d in ds]) / 1e3
+        ghz = cyc / max(1e-9, us * 1e3)
+        tfs = (fb + f8 + f4) * 1e9 / max(1e-12, us * 1e-6) / 1e12
+        out.append(f"| {wl} | {k} | {len(ds)} | {us:.1f} | {ghz:.2f} | {100 * busy:.1f}% | {fb:.1f} | {f8:.1f} | "
+                   f"{f4:.1f} | {tfs:.0f} | {100 * lds:.1f}% | {100 * bc:.2f}% |")
+        rows.append({"workload": wl, "kernel": k, "dispatches": len(ds), "avg_us": us, "clock_ghz": ghz,
+                     "mfma_busy": busy, "bf16_gflop": fb, "fp8_gflop": f8, "fp6f4_gflop": f4,
+                     "counted_tflops": tfs, "lds_active": lds, "lds_conflict": bc})
+    out += ["", json.dumps({"rows": rows}), ""]
+    path = os.path.join(ROOT, "profiles", out_name)
+    open(path, "w").write("\n".join(out))
+    return path
 
 
 def summarize_trace(trace_csv: str, bench_json: str, bench_err: str, out_name: str):
@@ -224,6 +317,7 @@ def copy_calibration(reps=3):
 # peaks measured on this device, reported beside the published ones
 # ----------------------------------------------------------------------------
 MEASURED = {}
+PROFILE_RUN = [False]   # set by --profile-run: legs take fixed small step counts
 
 
 def measure_peaks(msa):
@@ -455,10 +549,14 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0, profile_
     proxy_roof = with_measured({"kernel": pstage, "proxy_dtype": w.proxy_dtype, "achieved": p_ach, "peak": proxy_peak,
                                 "unit": "TFLOP/s", "frac": p_ach / proxy_peak})
     tflops = (f_main + f_proxy) / (ms_step * 1e-3) / 1e12
+    # matrix-core utilisation of the step: the time the step's FLOPs need at
+    # each dtype's peak (bf16 attention, proxy at its own dtype) over the step time
+    util = (f_main / PEAK_BF16_TFLOPS + f_proxy / proxy_peak) / 1e12 / (ms_step * 1e-3)
+    mb, mpx = MEASURED.get("bf16_tflops"), MEASURED.get(PEAK_KEY[proxy_peak])
+    util_m = (f_main / mb + f_proxy / mpx) / 1e12 / (ms_step * 1e-3) if (mb and mpx) else None
     res = {
         "workload": w.name, "tok_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
-        "tflops": tflops, "mfma_util": tflops / PEAK_BF16_TFLOPS,
-        "mfma_util_measured": tflops / MEASURED["bf16_tflops"] if MEASURED.get("bf16_tflops") else None,
+        "tflops": tflops, "mfma_util": util, "mfma_util_measured": util_m,
         "flops": {"proxy": f_proxy, "main": f_main}, "stage_ms": stage_ms, "roofline": roof,
         "proxy_roofline": proxy_roof,
         "config": {"workload": w.name, "qo_lens": w.qo_lens if len(w.qo_lens) <= 8 else None, "total_rows": T,
@@ -646,9 +744,13 @@ def decode_bench(msa, steps, warmup, sets=4):
     # eagerly and replayed from a HIP graph, with no profiling events attached
     _, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, "decode")
     launches_per_step = max(1, launches // steps)
-    ms_step, timed = time_by_duration(step)
-    host_us = host_cost_us(step)
-    g_ms, g_steps = graph_time(step, sets)
+    if PROFILE_RUN[0]:
+        ms_step, timed = time_steps(step, steps, warmup), steps
+        host_us, g_ms, g_steps = None, float("nan"), 0
+    else:
+        ms_step, timed = time_by_duration(step)
+        host_us = host_cost_us(step)
+        g_ms, g_steps = graph_time(step, sets)
     # compulsory bytes of one decode launch: selected K and V pages (fp8) + q + scales + indices + partials out
     nsel = sum(int((s >= 0).sum().item()) for s in sels) / sets
     kv_bytes = nsel * 2 * 128 * 128
@@ -714,9 +816,13 @@ def decode_step_bench(msa, steps, warmup, sets=4, wn=6):
         for n, v in kernel_profile(msa, plan, step, names).items():
             stage[n] = v[0]
     _, k_ms, launches = timed_with_kernel(msa, ip, step, steps, warmup, "proxy_topk")
-    ms_step, timed = time_by_duration(step)
-    host_us = host_cost_us(step)
-    g_ms, g_steps = graph_time(step, sets)
+    if PROFILE_RUN[0]:
+        ms_step, timed = time_steps(step, steps, warmup), steps
+        host_us, g_ms, g_steps = None, float("nan"), 0
+    else:
+        ms_step, timed = time_by_duration(step)
+        host_us = host_cost_us(step)
+        g_ms, g_steps = graph_time(step, sets)
     # compulsory bytes of one indexer launch: every visible proxy-K block
     # (fp8: 128 x 128 B; MXFP4: 128 x (64 + 4) B) + the fp8 proxy q
     nb = sum(-(-L // 128) for L in w.kv_lens)
@@ -808,6 +914,8 @@ def main():
                          "prefill_32k_backward, prefill_32k_backward_kl, prefill_128k_backward (not by default), "
                          "warmup_32k, decode_131k, decode_step_131k, decode_step_mxfp4_131k (or none)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="under a profiler: fixed small step counts, no duration-timed, host-cost or graph legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -816,6 +924,8 @@ def main():
                     help="host only: write profiles/<kernel>__<workload>__traffic.txt from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_CSV", "BENCH_STDOUT", "BENCH_STDERR", "OUT_NAME"),
                     help="host only: write a kernel-duration summary under profiles/ from a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("MFMA_CSV", "BENCH_STDERR", "OUT_NAME"),
+                    help="host only: write a matrix-core / LDS counter summary under profiles/")
     args = ap.parse_args()
     if args.summarize_counters:
         for p in summarize_counters(*args.summarize_counters):
@@ -824,6 +934,9 @@ def main():
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace))
         return
+    if args.summarize_mfma:
+        print(summarize_mfma(*args.summarize_mfma))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (see the design notes on "
               "sharding); run with --gpus 1", file=sys.stderr)
@@ -831,6 +944,7 @@ def main():
     import torch
     from block_sparse_top_amd import msa
     torch.cuda.set_device(0)
+    PROFILE_RUN[0] = args.profile_run
     extras = [] if args.no_extra or args.extra == "none" else [e for e in args.extra.split(",") if e]
     for e in extras:
         if e not in ("prefill_128k", "prefill_1m_fp8proxy", "prefill_32k_mxfp4", "prefill_32k_backward",
@@ -890,15 +1004,18 @@ def main():
     if "decode_131k" in extras:
         print("[bench] decode 131k fp8", file=sys.stderr, flush=True)
         mark("decode_131k")
-        extra["decode_131k"] = decode_bench(msa, max(50, args.steps * 10), 10)
+        extra["decode_131k"] = decode_bench(msa, args.steps if args.profile_run else max(50, args.steps * 10),
+                                            1 if args.profile_run else 10)
     if "decode_step_131k" in extras:
         print("[bench] decode step (indexer + decode) 131k fp8", file=sys.stderr, flush=True)
         mark("decode_step_131k")
-        extra["decode_step_131k"] = decode_step_bench(msa, max(50, args.steps * 10), 10)
+        extra["decode_step_131k"] = decode_step_bench(msa, args.steps if args.profile_run else max(50, args.steps * 10),
+                                                      1 if args.profile_run else 10)
     if "decode_step_mxfp4_131k" in extras:
         print("[bench] decode step (indexer + decode) 131k, MXFP4 proxy K", file=sys.stderr, flush=True)
         mark("decode_step_mxfp4_131k")
-        extra["decode_step_mxfp4_131k"] = decode_step_bench(msa, max(50, args.steps * 10), 10, wn=7)
+        extra["decode_step_mxfp4_131k"] = decode_step_bench(
+            msa, args.steps if args.profile_run else max(50, args.steps * 10), 1 if args.profile_run else 10, wn=7)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
