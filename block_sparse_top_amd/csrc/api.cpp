@@ -522,7 +522,7 @@ msa_status_t msa_topk_select(msa_plan_t p, const float* max_score, int64_t row_b
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if ((st = upload_meta(p, workspace, hs)) != MSA_OK) return st;
   const msa::DevMeta m = msa::dev_meta(p, workspace);
-  return hip_status(msa::launch_topk(p, m, max_score, row_begin, row_count, kv_block_indexes, hs), __func__);
+  return hip_status(msa::launch_topk(p, m, max_score, false, row_begin, row_count, kv_block_indexes, hs), __func__);
 }
 
 static msa_status_t prefill_rows(const char* fn, msa_plan_t p, const void* q, const void* k_pages, const void* v_pages,

@@ -97,10 +97,16 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
                                  const float* qs, const float* ks, const int32_t* kv_indices, int32_t tile_lo,
                                  int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
                                  int32_t* sel, const SelScratch& scr, hipStream_t st);
-hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, int64_t row_begin,
-                       int64_t row_count, int32_t* sel, hipStream_t st);
+// One-query-row plans whose rows fit the wave-per-row top-k kernels (at most
+// 32 registers of 64 block scores per lane, topk - 1 kept ids in the lanes).
+inline bool onerow_wave_topk(const msa_plan_s* p) { return p->one_row && p->nb_max <= 64 * 32 && p->d.topk <= 64; }
+// `row_major`: scores laid out [row_count, P, nb_max] (the workspace copy of
+// a one-query-row plan's fused selection) instead of max_score's [P, nb_max,
+// row_count].
+hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, bool row_major,
+                       int64_t row_begin, int64_t row_count, int32_t* sel, hipStream_t st);
 // Exact selection of one-query-row plans with low-precision proxies (band
-// blocks re-scored from the proxy operands).
+// blocks re-scored from the proxy operands); scores and scale codes row-major.
 hipError_t launch_topk_exact(const msa_plan_s* p, const DevMeta& m, const float* max_score, const int32_t* kmx,
                              const void* pq, const void* pk, const float* qs, const float* ks,
                              const int32_t* kv_indices, int64_t row_begin, int64_t row_count, int32_t* sel,

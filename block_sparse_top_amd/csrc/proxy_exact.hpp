@@ -33,7 +33,9 @@ struct ScoreBound {
   static constexpr float kCoef = F == Fmt::MX4QK ? 0x1p-17f : 0x1p-9f;
 };
 
-// E2M1 code (4 bits) -> value, exact: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives.
+// E2M1 code (4 bits) -> value, exact: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives
+// (the q row; key codes go through the hardware conversion, which gives the
+// same values).
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
   const uint32_t e = (c >> 1) & 3u, m = c & 1u;
   const float mag = e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
@@ -143,8 +145,19 @@ __device__ __forceinline__ float exact_block_dotmax(const ExactQ& q, const uint8
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t c = (uint32_t)x[i][0][w];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc = __builtin_fmaf(q.v[8 * w + n], e2m1_value((c >> (4 * n)) & 15u), acc);
+        // byte n of the word: element 2n in the low nibble, 2n + 1 in the high one
+        const f32x2 k0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+        const f32x2 k1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+        const f32x2 k2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+        const f32x2 k3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+        acc = __builtin_fmaf(q.v[8 * w], k0[0], acc);
+        acc = __builtin_fmaf(q.v[8 * w + 1], k0[1], acc);
+        acc = __builtin_fmaf(q.v[8 * w + 2], k1[0], acc);
+        acc = __builtin_fmaf(q.v[8 * w + 3], k1[1], acc);
+        acc = __builtin_fmaf(q.v[8 * w + 4], k2[0], acc);
+        acc = __builtin_fmaf(q.v[8 * w + 5], k2[1], acc);
+        acc = __builtin_fmaf(q.v[8 * w + 6], k3[0], acc);
+        acc = __builtin_fmaf(q.v[8 * w + 7], k3[1], acc);
       }
       // the key's and (MXFP4 q) the row's block scales: exact powers of two
       acc = __builtin_ldexpf(acc, (int)ke[i] - 127 + (int)q.e - 127);

@@ -66,9 +66,10 @@ struct ProxyArgs {
 constexpr int kSelCap = 16;
 constexpr int kSelCapLowp = 24;
 
-// A queued (row, group) pair: [0] row, [1] proxy head, [2] n_in | m << 8 |
-// overflow << 16, [3 .. 15) the list's 24 block ids as 16-bit pairs (in list
-// order: descending low-precision score).
+// A queued (row, group) pair: [0] row, [1] the row's first page-table entry
+// (offset into kv_indices), [2] n_in | m << 8 | overflow << 16, [3 .. 15) the
+// list's 24 block ids as 16-bit pairs (in list order: descending
+// low-precision score), [15] local block | proxy head << 16.
 constexpr int kRqInts = 16;
 
 // MXFP4 K rows are 64 bytes of E2M1 codes; the block's 128 x 4 E8M0 scale
@@ -521,10 +522,11 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
         if (unc) {
           int32_t* e = a.rq + (int64_t)(base + lanes_below(mask)) * kRqInts;
           e[0] = (int32_t)my_grow;
-          e[1] = p;
+          e[1] = a.page_start[seq];
           e[2] = n_in | (m << 8) | ((ovf ? 1 : 0) << 16);
 #pragma unroll
           for (int j = 0; j < kCap; j += 2) e[3 + j / 2] = (ti[j] & 0xffff) | (ti[j + 1] << 16);
+          e[15] = my_local | (p << 16);
         }
       }
       queued = unc;
@@ -557,36 +559,40 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
 // blocks of the pair's list (or, if the band may run past the list, every
 // competing block not already sure) in ascending block order; each is scored
 // exactly (exact_block_dotmax), the need = R - n_in best are kept with ties to
-// the lower block, and the row is written like the fused pass writes it.
+// the lower block, and the row is written like the fused pass writes it.  The
+// entry carries everything the pair needs (no plan metadata is read); the
+// band blocks' page ids are loaded lane-parallel before the first is scored.
 template <Fmt F>
-__global__ __launch_bounds__(256) void topk_refine_kernel(ProxyArgs a, DevMeta mt) {
+__global__ __launch_bounds__(256) void topk_refine_kernel(ProxyArgs a) {
   using Tr = ProxyTraits<F>;
   __shared__ int32_t cand_lds[4][kSelCapLowp];
+  __shared__ int32_t cand_pg[4][kSelCapLowp];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int count = __builtin_amdgcn_readfirstlane(*a.rq_count);
   for (int e = blockIdx.x * 4 + wave; e < count; e += gridDim.x * 4) {
     const int32_t* ent = a.rq + (int64_t)e * kRqInts;
-    const int r = __builtin_amdgcn_readfirstlane(ent[0]);
-    const int p = __builtin_amdgcn_readfirstlane(ent[1]);
-    const int hdr = __builtin_amdgcn_readfirstlane(ent[2]);
+    const int ev = lane < kRqInts ? ent[lane] : 0;  // the entry, one int per lane
+    const int r = __builtin_amdgcn_readlane(ev, 0);
+    const int32_t* pages = a.kv_indices + __builtin_amdgcn_readlane(ev, 1);
+    const int hdr = __builtin_amdgcn_readlane(ev, 2);
+    const int lp = __builtin_amdgcn_readlane(ev, 15);
     const int n_in = hdr & 0xff, m = (hdr >> 8) & 0xff;
     const bool ovf = (hdr >> 16) & 1;
-    const int s = upper_bound_i32(mt.row_start, mt.S + 1, r) - 1;
-    const int pos = mt.kv[s] - mt.qo[s] + (r - mt.row_start[s]);
-    const int local = pos >> 7;
+    const int local = lp & 0xffff, p = (int)((uint32_t)lp >> 16);
     const int R = min(a.k - 1, local);
     const int need = R - n_in;
     // list ids: lane j < 24 holds entry j
-    const int lid = lane < kSelCapLowp ? (int)((uint32_t)ent[3 + lane / 2] >> (16 * (lane & 1))) & 0xffff : 0x7fffffff;
-    const bool sure = lane < n_in;
+    const int lw = __shfl(ev, 3 + min(lane, kSelCapLowp - 1) / 2);
+    const int lid = lane < kSelCapLowp ? (int)((uint32_t)lw >> (16 * (lane & 1))) & 0xffff : 0x7fffffff;
+    const bool cand = !ovf && lane >= n_in && lane < m && lid < local;
+    const int32_t cpg = cand ? pages[lid] : 0;
     const int ph = a.Pk == a.P ? p : 0;
     const uint8_t* qrow = a.pq + ((int64_t)r * a.P + p) * Tr::kQRowBytes;
     const ExactQ q = exact_load_q<F>(qrow);
     float sc = a.scale;
     if constexpr (F == Fmt::FP8) sc *= a.qs[p] * a.ks[ph];
     if constexpr (F == Fmt::MX4K) sc *= a.qs[p];
-    const int32_t* pages = a.kv_indices + mt.page_start[s];
     // the uniform top-`need` list (every lane holds a copy)
     float bv[kSelCap];
     int bi[kSelCap];
@@ -595,8 +601,8 @@ __global__ __launch_bounds__(256) void topk_refine_kernel(ProxyArgs a, DevMeta m
       bv[j] = kNegInf;
       bi[j] = 0x7fffffff;
     }
-    auto consider = [&](int b) {
-      const uint8_t* blk = a.pk + ((int64_t)pages[b] * a.Pk + ph) * Tr::kKBlockBytes;
+    auto consider = [&](int b, int32_t page) {
+      const uint8_t* blk = a.pk + ((int64_t)page * a.Pk + ph) * Tr::kKBlockBytes;
       const float v = exact_block_dotmax<F>(q, blk, 128) * sc;
       // insert before the first strictly smaller listed score (ascending block
       // order: equal scores keep the lower block ahead)
@@ -612,22 +618,28 @@ __global__ __launch_bounds__(256) void topk_refine_kernel(ProxyArgs a, DevMeta m
     };
     if (!ovf) {
       // band entries n_in .. m-1, visited in ascending block order
-      const bool cand = lane >= n_in && lane < m && lid < local;
       const uint64_t cm = __ballot(cand);
       int rank = 0;
       for (int j = n_in; j < m; ++j)
         rank += ((cm >> j) & 1) && __builtin_amdgcn_readlane(lid, j) < lid ? 1 : 0;
-      if (cand) cand_lds[wave][rank] = lid;
+      if (cand) {
+        cand_lds[wave][rank] = lid;
+        cand_pg[wave][rank] = cpg;
+      }
       wave_lds_sync();
       const int nc = __popcll(cm);
-      for (int c = 0; c < nc; ++c) consider(__builtin_amdgcn_readfirstlane(cand_lds[wave][c]));
+      for (int c = 0; c < nc; ++c)
+        consider(__builtin_amdgcn_readfirstlane(cand_lds[wave][c]), __builtin_amdgcn_readfirstlane(cand_pg[wave][c]));
       wave_lds_sync();
     } else {
-      // every competing block except the sure ones
-      for (int b = 0; b < local; ++b) {
-        bool is_sure = false;
-        for (int j = 0; j < n_in; ++j) is_sure |= __builtin_amdgcn_readlane(lid, j) == b;
-        if (!is_sure) consider(b);
+      // every competing block except the sure ones, page ids 64 at a time
+      for (int b0 = 0; b0 < local; b0 += 64) {
+        const int32_t pw = b0 + lane < local ? pages[b0 + lane] : 0;
+        for (int b = b0; b < min(b0 + 64, local); ++b) {
+          bool is_sure = false;
+          for (int j = 0; j < n_in; ++j) is_sure |= __builtin_amdgcn_readlane(lid, j) == b;
+          if (!is_sure) consider(b, __builtin_amdgcn_readlane(pw, b - b0));
+        }
       }
     }
     // the row: sure ids (lanes < n_in) and the kept ones, ascending, then the
@@ -664,8 +676,9 @@ struct ProxyRowArgs {
   DevMeta m;
   int32_t P, Pk, nb_max, blocks_per_wg;
   int64_t row_begin, row_count;
-  float* out;    // [P, nb_max, row_count]
-  int32_t* kmx;  // MXFP4 K, fused low-precision selection: largest scale code per block [Pk, nb_max, row_count]
+  float* out;              // block maxima: out[head * o_h + block * o_b + row * o_r]
+  int64_t o_h, o_b, o_r;   // [P, nb_max, row_count] for max_score, [row_count, P, nb_max] in the workspace
+  int32_t* kmx;            // MXFP4 K, fused low-precision selection: largest scale code per block [row_count, Pk, nb_max]
   float scale;
 };
 
@@ -738,7 +751,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
                   (8 * (r >> 2) + (r & 3) + 1) <= lim ? acc[r + 1] : kNegInf);
     }
     m = fmaxf(m, wave_xor32(m));
-    if (lane < ncols) a.out[((int64_t)head * a.nb_max + b) * a.row_count + rl] = m * scale;
+    if (lane < ncols) a.out[head * a.o_h + b * a.o_b + rl * a.o_r] = m * scale;
   };
   for (; b + kRowWaves < b1; b += 2 * kRowWaves) {
     step(fa, fb, b);
@@ -822,7 +835,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(Prox
                   (8 * (r >> 2) + (r & 3) + 1) <= lim ? acc[r + 1] : kNegInf);
     }
     m = fmaxf(m, wave_xor32(m));
-    if (lane < ncols) a.out[((int64_t)head * a.nb_max + b) * a.row_count + rl] = m * scale;
+    if (lane < ncols) a.out[head * a.o_h + b * a.o_b + rl * a.o_r] = m * scale;
     if (a.kmx) {
       // the block's largest scale code (bounds its |k|); every key of the
       // block is in some lane's four tiles, bytes 0 and 2 of each shifted word
@@ -831,7 +844,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(Prox
       for (int t = 0; t < 4; ++t) e = max(e, max((uint32_t)cur[t].sc & 0xffu, ((uint32_t)cur[t].sc >> 16) & 0xffu));
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) e = max(e, (uint32_t)__shfl_xor((int)e, o));
-      if (lane == 0) a.kmx[((int64_t)kh * a.nb_max + b) * a.row_count + rl] = (int32_t)e;
+      if (lane == 0) a.kmx[(rl * a.Pk + kh) * a.nb_max + b] = (int32_t)e;
     }
   };
   for (; b + kRowWaves < b1; b += 2 * kRowWaves) {
@@ -868,6 +881,18 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
     r.row_begin = row_begin;
     r.row_count = row_count;
     r.out = sel ? scr.dms : max_score;
+    // the wave-per-row selection reads its row's scores contiguously:
+    // row-major in the workspace (low-precision one-row plans always qualify)
+    const bool rm = sel && onerow_wave_topk(p);
+    if (rm) {
+      r.o_r = (int64_t)r.P * r.nb_max;
+      r.o_h = r.nb_max;
+      r.o_b = 1;
+    } else {
+      r.o_h = (int64_t)r.nb_max * row_count;
+      r.o_b = row_count;
+      r.o_r = 1;
+    }
     r.kmx = sel && lowp ? scr.kmx : nullptr;
     r.scale = p->d.proxy_sm_scale;
     // grid.y: K heads, or with one shared K head groups of 32 proxy heads
@@ -897,7 +922,7 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
     }
     if (sel && lowp)
       return launch_topk_exact(p, m, scr.dms, scr.kmx, pq, pk, qs, ks, kv_indices, row_begin, row_count, sel, st);
-    if (sel) return launch_topk(p, m, scr.dms, row_begin, row_count, sel, st);
+    if (sel) return launch_topk(p, m, scr.dms, rm, row_begin, row_count, sel, st);
     return hipGetLastError();
   }
   if (tile_hi <= tile_lo) return hipSuccess;
@@ -939,11 +964,11 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
   if (refine) {
     // waves loop over the queued pairs; the queue length is read on the device
     ProfEvents pe(p, "topk_refine");
-    const dim3 rg((unsigned)(4 * p->num_cu)), rb(256);
+    const dim3 rg((unsigned)(3 * p->num_cu)), rb(256);  // three waves per SIMD fit its registers
     switch (p->d.proxy_dtype) {
-      case MSA_MXFP4_QK: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::MX4QK>, rg, rb, 0, st, pe.start, pe.stop, 0, a, m); break;
-      case MSA_MXFP4: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::MX4K>, rg, rb, 0, st, pe.start, pe.stop, 0, a, m); break;
-      default: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::FP8>, rg, rb, 0, st, pe.start, pe.stop, 0, a, m);
+      case MSA_MXFP4_QK: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::MX4QK>, rg, rb, 0, st, pe.start, pe.stop, 0, a); break;
+      case MSA_MXFP4: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::MX4K>, rg, rb, 0, st, pe.start, pe.stop, 0, a); break;
+      default: hipExtLaunchKernelGGL(topk_refine_kernel<Fmt::FP8>, rg, rb, 0, st, pe.start, pe.stop, 0, a);
     }
   }
   return hipGetLastError();

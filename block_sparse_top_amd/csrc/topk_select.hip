@@ -35,10 +35,11 @@ constexpr int kTopkThreads = 128;
 constexpr int kCap = 48;  // per-thread candidate list length
 
 struct TopkArgs {
-  const float* ms;          // [P, nb_max, row_count]
+  const float* ms;          // [P, nb_max, row_count] (the wave kernels: ms[p * s_p + b * s_b + row * s_r])
   int32_t* sel;             // [T, Hkv, k]
   DevMeta m;
   int64_t row_begin, row_count;
+  int64_t s_p, s_b, s_r;
   int32_t P, k;
 };
 
@@ -218,13 +219,13 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
   const int32_t r = (int32_t)(a.row_begin + rl);  // = its sequence: one query row each
   const int local = __builtin_amdgcn_readfirstlane((a.m.kv[r] - 1) >> 7);
   const int R = min(a.k - 1, local);
-  const float* col = a.ms + (int64_t)p * a.m.nb_max * a.row_count + rl;
+  const float* col = a.ms + p * a.s_p + rl * a.s_r;
   uint32_t key[VPL];
   const int last = max(local - 1, 0);  // clamped loads: issued back to back, always in bounds
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int b = 64 * i + lane;
-    const float x = col[(int64_t)min(b, last) * a.row_count];
+    const float x = col[min(b, last) * a.s_b];
     const uint32_t u = x == 0.f ? 0u : __float_as_uint(x);
     key[i] = b < local ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
   }
@@ -308,63 +309,107 @@ struct ExactRowArgs {
   const float* qs;
   const float* ks;
   const int32_t* kv_indices;
-  const int32_t* kmx;  // MXFP4 K: largest scale code of each block [Pk, nb_max, row_count]
+  const int32_t* kmx;  // MXFP4 K: largest scale code of each block [row_count, Pk, nb_max]
   int32_t Pk;
   float scale;
 };
 
+constexpr int kExWaves = 8;       // waves per (row, group): band blocks are re-scored in parallel
+constexpr int kExBand = 2048;     // band scores held in LDS (one-row low-precision plans have <= 2048 blocks)
+
 // The decode-step indexer's selection for the low-precision proxy formats
-// (one query row per sequence, every block score of the row available): one
-// wave per (row, group), lane b % 64 / register b / 64 holding block b's key
-// as in topk_wave_kernel.  theta = the R-th largest score exactly (bit by bit
-// from ballot counts); delta = the format's score error bound for this row.
-// Blocks above theta + 2 delta are in the exact top R, blocks below theta -
-// 2 delta are out; if exactly R blocks reach theta - 2 delta they are the
-// answer, else the band blocks are re-scored exactly, in ascending block
-// order, and the best R - n_in kept (ties to the lower block).  The kept list
-// is distributed over the lanes (slot j in lane j).
+// (one query row per sequence, every block score of the row available in the
+// workspace, row-major): one workgroup of kExWaves waves per (row, group);
+// each wave reads the row (block b at lane b % 64, register b / 64, as
+// order-preserving keys as in topk_wave_kernel) and takes the same branches.
+//  * theta = the R-th largest score: the R-th largest lane maximum t0 is a
+//    lower bound (R lanes hold a distinct score >= t0), the scores >= t0 are
+//    compacted to one per lane when they fit, and theta is found bit by bit
+//    from ballot counts over them (else over the whole row);
+//  * delta = the format's score error bound for this row: blocks above
+//    theta + 2 delta are in the exact top R, blocks below theta - 2 delta are
+//    out; if exactly R blocks reach theta - 2 delta they are the answer;
+//  * else the band blocks are scored exactly, band block c by wave c %
+//    kExWaves (page ids loaded up front, lane-parallel), the scores
+//    meet in LDS, and wave 0 keeps the best R - n_in in ascending block order
+//    (a later block displaces a kept one only with a strictly larger score:
+//    ties go to the lower block), the kept list distributed over the lanes.
 template <int VPL, Fmt F>
-__global__ __launch_bounds__(256) void topk_wave_exact_kernel(TopkArgs a, ExactRowArgs x) {
-  __shared__ int32_t sure_ids[4][64];
+__global__ __launch_bounds__(64 * kExWaves) void topk_wave_exact_kernel(TopkArgs a, ExactRowArgs x) {
+  __shared__ int32_t sure_ids[64];
+  __shared__ uint32_t top_keys[kExWaves][64];
+  __shared__ float band_v[kExBand];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
-  if (pair >= a.row_count * a.P) return;
-  const int64_t rl = pair / a.P;
-  const int p = (int)(pair % a.P);
+  const int64_t rl = blockIdx.x / a.P;
+  const int p = (int)(blockIdx.x % a.P);
   const int32_t r = (int32_t)(a.row_begin + rl);  // = its sequence: one query row each
   const int local = __builtin_amdgcn_readfirstlane((a.m.kv[r] - 1) >> 7);
   const int R = min(a.k - 1, local);
   const int kh = x.Pk == a.P ? p : 0;
   int32_t* dst = a.sel + ((int64_t)r * a.P + p) * a.k;
-  if (lane == 0) dst[R] = local;
-  if (lane > R && lane < a.k) dst[lane] = -1;
+  if (wave == 0) {
+    if (lane == 0) dst[R] = local;
+    if (lane > R && lane < a.k) dst[lane] = -1;
+  }
   if (R == 0) return;
   if (R == local) {  // every competing block is selected
-    for (int j = lane; j < R; j += 64) dst[j] = j;
+    if (wave == 0)
+      for (int j = lane; j < R; j += 64) dst[j] = j;
     return;
   }
-  const float* col = a.ms + (int64_t)p * a.m.nb_max * a.row_count + rl;
+  // the row's scores (and scale codes) are loaded up to nb_max, all in
+  // bounds, so the loads do not wait for the sequence length; the page ids of
+  // the competing blocks are loaded next, while theta is found
+  const float* row = a.ms + p * a.s_p + rl * a.s_r;  // s_b == 1
+  const int nbm1 = a.m.nb_max - 1;
   uint32_t key[VPL];
-  const int last = max(local - 1, 0);
   uint32_t kmaxe = 0;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int b = 64 * i + lane;
-    key[i] = b < local ? f2key(col[(int64_t)min(b, last) * a.row_count]) : 0u;
+    key[i] = f2key(row[min(b, nbm1)]);
     if constexpr (F != Fmt::FP8) {
-      const uint32_t e = (uint32_t)x.kmx[((int64_t)kh * a.m.nb_max + min(b, last)) * a.row_count + rl];
+      const uint32_t e = (uint32_t)x.kmx[(rl * x.Pk + kh) * a.m.nb_max + min(b, nbm1)];
       kmaxe = b < local ? max(kmaxe, e) : kmaxe;
     }
   }
-  // theta: the R-th largest key
-  uint32_t t = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = t | (1u << bit);
-    int cnt = 0;
+  const int last = max(local - 1, 0);
+  const int32_t* pages = x.kv_indices + a.m.page_start[r];
+  int32_t pg[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) cnt += __popcll(__ballot(key[i] >= c));
-    if (cnt >= R) t = c;
+  for (int i = 0; i < VPL; ++i) {
+    pg[i] = pages[min(64 * i + lane, last)];
+    key[i] = 64 * i + lane < local ? key[i] : 0u;
+  }
+  // theta: the R-th largest key
+  uint32_t lm = key[0];
+#pragma unroll
+  for (int i = 1; i < VPL; ++i) lm = max(lm, key[i]);
+  const uint32_t t0 = wave_nth_largest(lm, R);
+  int c0 = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) c0 += __popcll(__ballot(key[i] >= t0));
+  uint32_t t = 0;
+  if (c0 <= 64) {
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const bool c = key[i] >= t0;
+      const uint64_t m = __ballot(c);
+      if (c) top_keys[wave][base + lanes_below(m)] = key[i];
+      base += __popcll(m);
+    }
+    wave_lds_sync();
+    t = wave_nth_largest(lane < c0 ? top_keys[wave][lane] : 0u, R);
+  } else {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = t | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) cnt += __popcll(__ballot(key[i] >= c));
+      if (cnt >= R) t = c;
+    }
   }
   const float theta = key2f(t);
   // delta: bound coefficient x scales x max|q| x max|k| (value units)
@@ -397,40 +442,63 @@ __global__ __launch_bounds__(256) void topk_wave_exact_kernel(TopkArgs a, ExactR
   }
   if (nb == R - n_in) {
     // certified: the R blocks reaching theta - 2 delta, ascending
-    int base = 0;
+    if (wave == 0) {
+      int base = 0;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const bool c = key[i] >= lo;
-      const uint64_t m = __ballot(c);
-      if (c) dst[base + lanes_below(m)] = 64 * i + lane;
-      base += __popcll(m);
+      for (int i = 0; i < VPL; ++i) {
+        const bool c = key[i] >= lo;
+        const uint64_t m = __ballot(c);
+        if (c) dst[base + lanes_below(m)] = 64 * i + lane;
+        base += __popcll(m);
+      }
     }
     return;
   }
-  // sure blocks, ascending, into LDS
-  {
+  if (wave == 0) {
+    // sure blocks, ascending, into LDS
     int base = 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const bool c = key[i] > hi;
       const uint64_t m = __ballot(c);
-      if (c) sure_ids[wave][base + lanes_below(m)] = 64 * i + lane;
+      if (c) sure_ids[base + lanes_below(m)] = 64 * i + lane;
       base += __popcll(m);
     }
   }
+  if (nb > wave) {
+    // this wave's band blocks c = wave, wave + kExWaves, ...: exact scores
+    const ExactQ q = exact_load_q<F>(qrow);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      uint64_t m = __ballot(key[i] >= lo && key[i] <= hi);
+      while (m) {
+        const int l = (int)__builtin_ctzll(m);
+        m &= m - 1;
+        if (c % kExWaves == wave && c < kExBand) {
+          const int32_t page = __builtin_amdgcn_readlane(pg[i], l);
+          const uint8_t* blk = x.pk + ((int64_t)page * x.Pk + kh) * (F == Fmt::FP8 ? 128 * 128 : 128 * 68);
+          const float v = exact_block_dotmax<F>(q, blk, 128) * sc;
+          if (lane == 0) band_v[c] = v;
+        }
+        ++c;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
   const int need = R - n_in;
-  const ExactQ q = exact_load_q<F>(qrow);
-  const int32_t* pages = x.kv_indices + a.m.page_start[r];
   float kv_ = kNegInf;  // the kept list: slot `lane`
   int ki = 0x7fffffff;
+  int c = 0;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     uint64_t m = __ballot(key[i] >= lo && key[i] <= hi);
     while (m) {
       const int b = 64 * i + (int)__builtin_ctzll(m);
       m &= m - 1;
-      const uint8_t* blk = x.pk + ((int64_t)pages[b] * x.Pk + kh) * (F == Fmt::FP8 ? 128 * 128 : 128 * 68);
-      const float v = exact_block_dotmax<F>(q, blk, 128) * sc;
+      const float v = band_v[min(c, kExBand - 1)];
+      ++c;
       // insert before the first strictly smaller kept score
       const float up = __shfl_up(kv_, 1);
       const int upi = __shfl_up(ki, 1);
@@ -442,10 +510,9 @@ __global__ __launch_bounds__(256) void topk_wave_exact_kernel(TopkArgs a, ExactR
       }
     }
   }
-  wave_lds_sync();
   // the row: sure ids and kept ids, ascending
   int mine = 0x7fffffff;
-  if (lane < n_in) mine = sure_ids[wave][lane];
+  if (lane < n_in) mine = sure_ids[lane];
   const int kept = __shfl(ki, max(lane - n_in, 0));
   if (lane >= n_in && lane < R) mine = kept;
   int rank = 0;
@@ -476,10 +543,16 @@ hipError_t launch_topk_exact(const msa_plan_s* p, const DevMeta& m, const float*
   x.kmx = kmx;
   x.Pk = p->d.num_proxy_kv_heads;
   x.scale = p->d.proxy_sm_scale;
-  const unsigned grid = (unsigned)((row_count * a.P + 3) / 4);
+  // row-major scores [row_count, P, nb_max]
+  a.s_r = (int64_t)a.P * p->nb_max;
+  a.s_p = p->nb_max;
+  a.s_b = 1;
+  const unsigned grid = (unsigned)(row_count * a.P);
   const int vpl = (p->nb_max + 63) / 64;
   ProfEvents pe(p, "topk_select");
-  auto go = [&](auto kern) { hipExtLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, pe.start, pe.stop, 0, a, x); };
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(64 * kExWaves), 0, st, pe.start, pe.stop, 0, a, x);
+  };
 #define MSA_EXACT_VPL(V)                                                               \
   switch (p->d.proxy_dtype) {                                                          \
     case MSA_FP8_E4M3: go(topk_wave_exact_kernel<V, Fmt::FP8>); break;                 \
@@ -494,8 +567,8 @@ hipError_t launch_topk_exact(const msa_plan_s* p, const DevMeta& m, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, int64_t row_begin,
-                       int64_t row_count, int32_t* sel, hipStream_t st) {
+hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_score, bool row_major,
+                       int64_t row_begin, int64_t row_count, int32_t* sel, hipStream_t st) {
   TopkArgs a;
   a.ms = max_score;
   a.sel = sel;
@@ -504,7 +577,16 @@ hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_s
   a.row_count = row_count;
   a.P = p->d.num_proxy_heads;
   a.k = p->d.topk;
-  if (p->one_row && p->nb_max <= 64 * 32 && a.k <= 64) {
+  if (row_major) {
+    a.s_r = (int64_t)a.P * p->nb_max;
+    a.s_p = p->nb_max;
+    a.s_b = 1;
+  } else {
+    a.s_p = (int64_t)p->nb_max * row_count;
+    a.s_b = row_count;
+    a.s_r = 1;
+  }
+  if (onerow_wave_topk(p)) {
     // one wave per (row, group): these plans have few rows and long score rows
     const unsigned grid = (unsigned)((row_count * a.P + 3) / 4);
     const int vpl = (p->nb_max + 63) / 64;
@@ -515,6 +597,7 @@ hipError_t launch_topk(const msa_plan_s* p, const DevMeta& m, const float* max_s
     else hipExtLaunchKernelGGL(topk_wave_kernel<32>, dim3(grid), dim3(256), 0, st, pe.start, pe.stop, 0, a);
     return hipGetLastError();
   }
+  if (row_major) return hipErrorInvalidValue;  // the thread-per-row kernel reads max_score's layout
   const dim3 grid((unsigned)((row_count + kTopkThreads - 1) / kTopkThreads), (unsigned)a.P), block(kTopkThreads);
   const int need = a.k - 1;
   if (need <= 16) { ProfEvents pe(p, "topk_select"); hipExtLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, pe.start, pe.stop, 0, a); }
