@@ -154,9 +154,10 @@ struct PartialArgs {
   const int4* items;
   const int32_t* nitems;
   DevMeta m;
-  uint16_t* part_o;      // [rows, Hq, k, 128] bf16, then one trash slot
-  float* part_lse;       // [rows, Hq, k], then one trash slot
-  int64_t trash;         // index of the trash slot (rows * Hq * k)
+  uint8_t* part_hi;      // partial records, block floating point (see store_rows_bfp10):
+  uint8_t* part_lo;      //   planes of 128 and 32 bytes per record [rows, k, Hq], then one trash record
+  float2* part_st;       //   {log-sum-exp, step} [rows, Hq, k], then one trash entry
+  int64_t trash;         // index of the trash record (rows * Hq * k)
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2;      // sm_scale * log2(e)
 };
@@ -262,6 +263,87 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16 (&oacc)[4], float m
       wave_lds_sync();
     }
   }
+}
+
+// The partial outputs of the sparse prefill in block floating point.  A
+// record holds one (row, head, slot) partial O (128 values) as 10-bit signed
+// integers n with O_d ~ step * n_d, step = 2^(E - 9) * 1024 / 1023 for the
+// smallest E with max_d |O_d| < 2^E: |O_d| / step < 511.5, so |n_d| <= 511
+// and the rounding error |O_d - step n_d| <= step / 2 < 2^-9 max_d |O_d| (a
+// bf16 value carries up to 2^-8 of its own magnitude).  A record is 160 bytes
+// against 256 in bf16: the partials are written once and read once, so this
+// is 35% of the traffic of the partial attention's stores and of the merge.
+//  * byte plane (128 bytes): n >> 2 as an int8; dim d = 32 dt + 8 gq + 4 h + t
+//    at byte 64 h + 16 dt + 4 gq + t (h: the MFMA lane half holding d);
+//  * 2-bit plane (32 bytes): n & 3 of dim d at bits 2t of byte 16 h + 4 dt + gq;
+//  * step, beside the log-sum-exp (float2).
+// Planes are indexed by record (row * k + slot) * Hq + head, so the G heads of
+// one (row, slot) entry are adjacent: the 2-bit planes of an entry's G >= 4
+// heads fill whole 128-byte lines.
+constexpr float kBfpMagic = 12582912.0f;  // 1.5 * 2^23: x + magic keeps round(x) in the low mantissa bits
+
+// Encodes the wave's 32 rows (the O^T tiles of store_rows_bf16, scaled by
+// `mul`) and stores the planes: byte planes through the wave's 2 KB staging
+// area in whole 128-byte lines (16 rows at a time, chunk c of staged row r at
+// c ^ ((r >> 1) & 7)), 2-bit planes straight from the lanes.  Returns the
+// lane's row's step.
+template <typename RecIndex>
+__device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float mul, uint8_t* ow, uint8_t* hi_plane,
+                                                  uint8_t* lo_plane, RecIndex rec, int lane) {
+  const int jrow = lane & 31, half = lane >> 5;
+  float amax = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) amax = max3f(amax, __builtin_fabsf(oacc[dt][i]), __builtin_fabsf(oacc[dt][i + 1]));
+  amax = fmaxf(amax, wave_xor32(amax));
+  // E = e - 126 for the biased exponent e of max|O|; rows below 2^-118 keep zeros
+  const uint32_t e = __float_as_uint(amax * mul) >> 23;
+  const bool live = e >= 9;
+  const float f = live ? mul * __uint_as_float((262u - e) << 23) * (1023.f / 1024.f) : 0.f;   // 1 / step
+  const float step = live ? __uint_as_float((e - 8u) << 23) * (1024.f / 1023.f) : 0.f;      // 2^(E - 9) * 1024 / 1023
+  uint32_t hw[4][4], lw[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    lw[dt] = 0u;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      hw[dt][gq] = 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // low 10 bits: n in two's complement
+        const uint32_t u = __float_as_uint(__builtin_fmaf(oacc[dt][4 * gq + t], f, kBfpMagic));
+        hw[dt][gq] = __builtin_amdgcn_alignbit(u >> 2, hw[dt][gq], 8);  // bytes fill from the top
+        lw[dt] = __builtin_amdgcn_alignbit(u, lw[dt], 2);
+      }
+    }
+  }
+  int64_t rr[4];  // staged rows 16 R + 8 i + lane / 8: rr[2 R + i]
+#pragma unroll
+  for (int x = 0; x < 4; ++x) rr[x] = rec(8 * x + (lane >> 3));
+  const int lr = jrow & 15;
+#pragma unroll
+  for (int R = 0; R < 2; ++R) {
+    if ((jrow >> 4) == R) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int c = 4 * half + dt;
+        lds_store16<i32x4>(&ow[lr * 128 + ((c ^ ((lr >> 1) & 7)) << 4)],
+                           i32x4{(int)hw[dt][0], (int)hw[dt][1], (int)hw[dt][2], (int)hw[dt][3]});
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * i + (lane >> 3), c = lane & 7;
+      const i32x4 v = lds_load16<i32x4>(&ow[r * 128 + ((c ^ ((r >> 1) & 7)) << 4)]);
+      __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(hi_plane + rr[2 * R + i] * 128 + 16 * c));
+    }
+    wave_lds_sync();
+  }
+  __builtin_nontemporal_store(i32x4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]},
+                              reinterpret_cast<i32x4*>(lo_plane + rec(jrow) * 32 + 16 * half));
+  return step;
 }
 
 template <KvFmt F>
@@ -437,19 +519,19 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     }
     sum += wave_xor32(sum);
 
-    // Output: the normalised bf16 partials in whole lines, non-temporal (the
-    // merge reads each of them once)
-    auto row_index = [&](int wrow) -> int64_t {
+    // Output: the normalised partials in block floating point, non-temporal
+    // (the merge reads each of them once)
+    auto rec_index = [&](int wrow) -> int64_t {
       const int srow = 32 * wave + wrow;
       const int se = chunk * MT + srow / G;
       if (se >= n_ent) return a.trash;
       const int sent = ent_s[se];
-      return ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63);
+      return ((int64_t)(sent >> 6) * a.k + (sent & 63)) * a.Hq + g * G + (srow & (G - 1));
     };
-    store_rows_bf16<true>(oacc, v_scale / sum, ow, a.part_o, row_index, lane);
-    {  // both halves hold the row's max and sum and store the same value
+    const float step = store_rows_bfp10(oacc, v_scale / sum, ow, a.part_hi, a.part_lo, rec_index, lane);
+    {  // both halves hold the row's max, sum and step and store the same value
       const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : a.trash;
-      a.part_lse[pi] = (mx + fast_log2(sum)) * kLn2;  // mx is already scaled
+      a.part_st[pi] = float2{(mx + fast_log2(sum)) * kLn2, step};  // mx is already scaled
     }
   };
 
@@ -477,22 +559,43 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
 struct MergeArgs {
   const int32_t* sel;
   DevMeta m;
-  const uint16_t* part_o;
-  const float* part_lse;
+  const uint8_t* part_hi;
+  const uint8_t* part_lo;
+  const float2* part_st;
   uint16_t* out;   // bf16 [T, Hq, 128]
   float* lse;      // [T, Hq] or null
   int32_t Hq, Hkv, G, k, w0, w1;
 };
 
-// 16 lanes per (row, head), 8 output columns per lane.  Every partial row is
-// read as 16-byte loads (one 256-byte segment per 16 lanes), 16 slots at a
-// time, the first 16 issued before anything else; lane j of the 16 reads
-// slot j's block id and log-sum-exp (coalesced), the row's local block then
-// says which slots count, and the group's max and weights move by shuffles.
-// topk <= 64.
+// 8 lanes per (row, head): lane l takes a record's byte-plane run 16 l .. +15
+// and its 2-bit-plane bytes 4 l .. +3 (store_rows_bfp10): dims 32 dt + 8 gq +
+// 4 h + t for h = l / 4, dt = l % 4 and gq, t = 0..3.  Slots go 8 at a time,
+// the first 8 slots' records issued before anything else; lane l of the 8
+// reads slot l's block id and {log-sum-exp, step} (coalesced), the row's local
+// block then says which slots count, and the group's max and weights move by
+// shuffles.  Decoding: the signed byte converts to float in one instruction
+// (a byte-select conversion); the four 2-bit fields of a byte are spread to
+// the four bytes of a word (byte t keeps field t at bit 2 t, so it reads as
+// 4^t f_t) and 4^t n_t = 4^(t+1) * byte + that is exact, its 4^-t going into
+// the slot weight.  topk <= 64.
+constexpr int kMergeLanes = 8;
+
+struct BfpRec {
+  i32x4 h;     // byte plane, 16 bytes
+  uint32_t l;  // 2-bit plane, 4 bytes
+};
+
+__device__ __forceinline__ BfpRec load_bfp_rec(const uint8_t* hi_plane, const uint8_t* lo_plane, int64_t rec, int l) {
+  BfpRec r;
+  r.h = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(hi_plane + rec * 128 + 16 * l));
+  r.l = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(lo_plane + rec * 32 + 4 * l));
+  return r;
+}
+
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int sub = threadIdx.x & 15;
-  const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  constexpr int NL = kMergeLanes;
+  const int l = threadIdx.x & (NL - 1);
+  const int64_t idx = (int64_t)blockIdx.x * (256 / NL) + (threadIdx.x / NL);
   const bool live = idx < (int64_t)(a.w1 - a.w0) * a.Hq;   // shuffles need every lane
   const int64_t id = live ? idx : 0;
   const int32_t rl = (int32_t)(id / a.Hq);
@@ -500,67 +603,92 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int g = h / a.G;
   const int32_t r = a.w0 + rl;
   const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
-  // the first 16 slots' partials depend on nothing else: issued before the
-  // row's sequence, selection and log-sum-exps are looked up
-  i32x4 v0[16];
+  auto rec_of = [&](int slot) -> int64_t { return ((int64_t)rl * a.k + slot) * a.Hq + h; };
+  // the first 8 slots' records depend on nothing else
+  BfpRec v[NL];
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    v0[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(a.part_o + (base + min(j, a.k - 1)) * 128 + 8 * sub));
+  for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_hi, a.part_lo, rec_of(min(j, a.k - 1)), l);
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
-  const int ngroups = (a.k + 15) >> 4;
-  // lane sub's slot of each group of 16: block id and log-sum-exp, loaded
+  const int ngroups = (a.k + NL - 1) / NL;
+  // lane l's slot of each group of 8: block id, log-sum-exp and step, loaded
   // before the row's local block is known (a slot counts when 0 <= b <= local)
-  int b_g[4];
-  float lse_g[4];
+  int b_g[8];
+  float lse_g[8], st_g[8];
 #pragma unroll
-  for (int gi = 0; gi < 4; ++gi) {
-    const int slot = min(16 * gi + sub, a.k - 1);
-    const bool in = gi < ngroups && 16 * gi + sub < a.k;
+  for (int gi = 0; gi < 8; ++gi) {
+    const int slot = min(NL * gi + l, a.k - 1);
+    const bool in = gi < ngroups && NL * gi + l < a.k;
     b_g[gi] = in ? row[slot] : -1;
-    lse_g[gi] = in ? a.part_lse[base + slot] : kNegInf;
+    const float2 ls = in ? a.part_st[base + slot] : float2{kNegInf, 0.f};
+    lse_g[gi] = ls.x;
+    st_g[gi] = ls.y;
   }
   const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
   const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
   float M = kNegInf;
 #pragma unroll
-  for (int gi = 0; gi < 4; ++gi) {
-    if (!(b_g[gi] >= 0 && b_g[gi] <= local)) lse_g[gi] = kNegInf;   // never written: not read into the result
+  for (int gi = 0; gi < 8; ++gi) {
+    if (!(b_g[gi] >= 0 && b_g[gi] <= local)) {  // never written: neither is read into the result
+      lse_g[gi] = kNegInf;
+      st_g[gi] = 0.f;
+    }
     M = fmaxf(M, lse_g[gi]);
   }
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
-  float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int gi = 0; gi < ngroups; ++gi) {
-    const float wl = lse_g[gi] == kNegInf ? 0.f : fast_exp2((lse_g[gi] - M) * kLog2e);
-    i32x4 v[16];
-    float w[16];
+  for (int off = 1; off < NL; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, NL));
+  float Ll = 0.f;  // this lane's slots' weights
+  float o[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      w[j] = __shfl(wl, j, 16);
-      const int slot = min(16 * gi + j, a.k - 1);
-      v[j] = gi == 0 ? v0[j] : __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(a.part_o + (base + slot) * 128 + 8 * sub));
+  for (int x = 0; x < 16; ++x) o[x] = 0.f;
+  for (int gi = 0; gi < ngroups; ++gi) {
+    float wl = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q == gi) wl = lse_g[q] == kNegInf ? 0.f : fast_exp2((lse_g[q] - M) * kLog2e);
+    float stl = st_g[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) stl = q == gi ? st_g[q] : stl;
+    Ll += wl;
+    const float wsl = wl * stl;  // weight x step
+    if (gi > 0) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_hi, a.part_lo, rec_of(min(NL * gi + j, a.k - 1)), l);
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (w[j] == 0.f) continue;  // invalid slots: never written, never read into the result
-      L += w[j];
+    for (int j = 0; j < NL; ++j) {
+      const float ws = __shfl(wsl, j, NL);
+      if (ws == 0.f) continue;  // invalid slots: never written, never read into the result
+      const float wt[4] = {ws, ws * 0.25f, ws * 0.0625f, ws * 0.015625f};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        o[2 * x] += w[j] * __builtin_bit_cast(float, (uint32_t)v[j][x] << 16);
-        o[2 * x + 1] += w[j] * __builtin_bit_cast(float, (uint32_t)v[j][x] & 0xffff0000u);
+      for (int gq = 0; gq < 4; ++gq) {
+        const uint32_t hw = (uint32_t)v[j].h[gq];
+        const uint32_t spread = __builtin_amdgcn_perm(v[j].l, v[j].l, 0x01010101u * gq) & 0xC0300C03u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float hi = (float)(int)(int8_t)(hw >> (8 * t));
+          const float lo = (float)((spread >> (8 * t)) & 0xffu);  // 4^t f_t
+          const float n4 = __builtin_fmaf((float)(4 << (2 * t)), hi, lo);  // 4^t n_t
+          o[4 * gq + t] = __builtin_fmaf(wt[t], n4, o[4 * gq + t]);
+        }
       }
     }
   }
+  float L = Ll;
+#pragma unroll
+  for (int off = 1; off < NL; off <<= 1) L += __shfl_xor(L, off, NL);
   if (!live) return;
   const float inv = 1.f / L;
-  i32x4 packed;
+  // dims 32 dt + 8 gq + 4 h + t: four 8-byte runs of the output row
+  const int hh = l >> 2, dt = l & 3;
+  uint16_t* orow = a.out + ((int64_t)r * a.Hq + h) * 128;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bf16x2 t = {(__bf16)(o[2 * j] * inv), (__bf16)(o[2 * j + 1] * inv)};
-    packed[j] = __builtin_bit_cast(int, t);
+  for (int gq = 0; gq < 4; ++gq) {
+    const bf16x2 t0 = {(__bf16)(o[4 * gq] * inv), (__bf16)(o[4 * gq + 1] * inv)};
+    const bf16x2 t1 = {(__bf16)(o[4 * gq + 2] * inv), (__bf16)(o[4 * gq + 3] * inv)};
+    *reinterpret_cast<i32x2*>(orow + 32 * dt + 8 * gq + 4 * hh) =
+        i32x2{__builtin_bit_cast(int, t0), __builtin_bit_cast(int, t1)};
   }
-  __builtin_nontemporal_store(packed, reinterpret_cast<i32x4*>(a.out + ((int64_t)r * a.Hq + h) * 128 + 8 * sub));
-  if (a.lse && sub == 0) a.lse[(int64_t)r * a.Hq + h] = M + fast_log2(L) * kLn2;
+  if (a.lse && l == 0) a.lse[(int64_t)r * a.Hq + h] = M + fast_log2(L) * kLn2;
 }
 
 }  // namespace
@@ -695,9 +823,13 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   a.items = items;
   a.nitems = nitems;
   a.m = m;
-  a.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o);
-  a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  // the partial records' planes share the region the backward uses for its
+  // bf16 dq partials (256 bytes per record; the forward needs 168)
   a.trash = p->attn_window * Hq * k;
+  const int64_t nrec = a.trash + 1;
+  a.part_hi = reinterpret_cast<uint8_t*>(ws + L.part_o);
+  a.part_lo = a.part_hi + nrec * 128;
+  a.part_st = reinterpret_cast<float2*>(a.part_lo + nrec * 32);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = p->G;
@@ -720,8 +852,9 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   MergeArgs mg;
   mg.sel = sel;
   mg.m = m;
-  mg.part_o = a.part_o;
-  mg.part_lse = a.part_lse;
+  mg.part_hi = a.part_hi;
+  mg.part_lo = a.part_lo;
+  mg.part_st = a.part_st;
   mg.out = static_cast<uint16_t*>(out);
   mg.lse = lse;
   mg.Hq = Hq;
@@ -733,7 +866,9 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   const int64_t npairs = (int64_t)(w1 - w0) * Hq;
   {
     ProfEvents pe(p, "merge");
-    hipExtLaunchKernelGGL(merge_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, pe.start, pe.stop, 0, mg);
+    constexpr int kPairsPerBlock = 256 / kMergeLanes;
+    hipExtLaunchKernelGGL(merge_kernel, dim3((unsigned)((npairs + kPairsPerBlock - 1) / kPairsPerBlock)), dim3(256), 0,
+                          st, pe.start, pe.stop, 0, mg);
   }
   return hipGetLastError();
 }
