@@ -567,6 +567,96 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0, profile_
     return res, (w, inp, sel)
 
 
+WINDOWS = (0, 8192, 4096, 2048)   # 0: the whole call (the default window)
+
+
+def window_sweep(msa, n_cfg, steps, warmup, mark):
+    """The sparse prefill at attention windows of 32K (the default), 8K, 4K
+    and 2K rows, each without and with XCD pinning of the work items
+    (MSA_XCD_PIN, read when a plan is made).  One JSON line per setting."""
+    import torch
+    from synthetic.gen import workload
+    T = workload(n_cfg).total_rows
+    for W in WINDOWS:
+        for pin in ("0", "1"):
+            os.environ["MSA_XCD_PIN"] = pin
+            mark(f"sweep_{n_cfg}_{W or T}_{pin}")
+            r, _ = prefill_bench(msa, n_cfg, steps, warmup, attn_window=W, profile_reps=1)
+            print(json.dumps({"window_sweep": r["config"]["workload"], "window": W or T, "xcd_pin": pin == "1",
+                              "launches_per_step": (T + (W or T) - 1) // (W or T),
+                              "ms_per_step": r["ms_per_step"], "stage_ms": r["stage_ms"]}), flush=True)
+            torch.cuda.empty_cache()
+    os.environ.pop("MSA_XCD_PIN", None)
+
+
+SWEEP_CMDS = {c: f"rocprofv3 --pmc {c} {PMC_FILTER} -f csv -d gpurun_out/sweep_{c.lower()} -o s -- python bench.py "
+                 f"--window-sweep 2 --profile-run --copy-calibration"
+              for c in ("FETCH_SIZE", "WRITE_SIZE")}
+
+
+def summarize_window_sweep(fetch_csv: str, fetch_err: str, write_csv: str, write_err: str, sweep_stdout: str,
+                           out_name: str):
+    """partial_attn HBM bytes per step and stage times of each window-sweep
+    setting: a counter run's dispatches belong to the setting that run marked
+    last before them; bytes scaled by the calibration copy in the same run."""
+    import bisect
+    import collections
+    import csv
+
+    def per_setting(path, counter, err):
+        marks = sorted((int(ln.split()[2]), ln.split()[1]) for ln in open(err).read().splitlines()
+                       if ln.startswith("[bench-mark] sweep_"))
+        mark_t = [t for t, _ in marks]
+        disp, start, kn = collections.defaultdict(float), {}, {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _short_kernel(r["Kernel_Name"])
+            if k not in ("copy", "partial_attn"):
+                continue
+            d = int(r["Dispatch_Id"])
+            disp[d] += float(r["Counter_Value"])
+            start[d] = int(r.get("Start_Timestamp") or 0)
+            kn[d] = k
+        copy = [disp[d] for d in disp if kn[d] == "copy"]
+        fac = COPY_BYTES / (sum(copy) / len(copy) * 1024.0)
+        acc = collections.defaultdict(list)
+        for d in disp:
+            if kn[d] != "partial_attn":
+                continue
+            i = bisect.bisect_right(mark_t, start[d]) - 1
+            if i >= 0:
+                acc[marks[i][1]].append(disp[d] * 1024.0 * fac)
+        return {k: sum(v) / len(v) for k, v in acc.items()}, fac
+
+    fetch, ff = per_setting(fetch_csv, "FETCH_SIZE", fetch_err)
+    write, wf = per_setting(write_csv, "WRITE_SIZE", write_err)
+    timing = [json.loads(ln) for ln in open(sweep_stdout).read().splitlines() if ln.startswith('{"window_sweep"')]
+    out = ["# Sparse prefill (prefill_32k_gqa4): attention window x XCD pinning of the work items",
+           f"# timing: python bench.py --window-sweep 2",
+           f"# fetch: {SWEEP_CMDS['FETCH_SIZE']}",
+           f"# write: {SWEEP_CMDS['WRITE_SIZE']}",
+           f"# summary: python bench.py --summarize-window-sweep <fetch csv> <fetch run stderr> <write csv> "
+           f"<write run stderr> <timing stdout> {out_name}",
+           f"# counters per partial_attn dispatch x launches per step; calibration factors {ff:.4f} (fetch), "
+           f"{wf:.4f} (write)",
+           "",
+           "| window (rows) | XCD pinning | launches / step | step ms | partial_attn ms / step | merge ms | "
+           "partial_attn read GB / step | written GB / step |",
+           "|---|---|---|---|---|---|---|---|"]
+    for t in timing:
+        key = f"sweep_2_{t['window']}_{'1' if t['xcd_pin'] else '0'}"
+        n = t["launches_per_step"]
+        fb = fetch.get(key)
+        wb = write.get(key)
+        out.append(f"| {t['window']} | {'yes' if t['xcd_pin'] else 'no'} | {n} | {t['ms_per_step']:.3f} | "
+                   f"{t['stage_ms']['partial_attn']:.3f} | {t['stage_ms']['merge']:.3f} | "
+                   f"{'' if fb is None else f'{fb * n / 1e9:.3f}'} | {'' if wb is None else f'{wb * n / 1e9:.3f}'} |")
+    path = os.path.join(ROOT, "profiles", out_name)
+    open(path, "w").write("\n".join(out) + "\n")
+    return path
+
+
 def backward_bench(msa, n_cfg, steps, warmup, kl=False):
     """The training backward of the sparse prefill attention on one workload:
     the forward runs once (selection, output, lse), then each step is
@@ -926,6 +1016,12 @@ def main():
                     help="host only: write a kernel-duration summary under profiles/ from a rocprofv3 kernel trace")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("MFMA_CSV", "BENCH_STDERR", "OUT_NAME"),
                     help="host only: write a matrix-core / LDS counter summary under profiles/")
+    ap.add_argument("--window-sweep", type=int, metavar="CFG",
+                    help="only the sparse prefill of workload CFG at attention windows 32K/8K/4K/2K, without and with "
+                         "XCD pinning (one JSON line each)")
+    ap.add_argument("--summarize-window-sweep", nargs=6,
+                    metavar=("FETCH_CSV", "FETCH_STDERR", "WRITE_CSV", "WRITE_STDERR", "SWEEP_STDOUT", "OUT_NAME"),
+                    help="host only: write the window-sweep summary under profiles/")
     args = ap.parse_args()
     if args.summarize_counters:
         for p in summarize_counters(*args.summarize_counters):
@@ -936,6 +1032,9 @@ def main():
         return
     if args.summarize_mfma:
         print(summarize_mfma(*args.summarize_mfma))
+        return
+    if args.summarize_window_sweep:
+        print(summarize_window_sweep(*args.summarize_window_sweep))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (see the design notes on "
@@ -958,6 +1057,10 @@ def main():
     def mark(key):   # host monotonic clock before a workload's first launch (trace summaries split on it)
         torch.cuda.synchronize()
         print(f"[bench-mark] {key} {time.monotonic_ns()}", file=sys.stderr, flush=True)
+    if args.window_sweep:
+        steps, warm = (2, 1) if args.profile_run else (args.steps, args.warmup)
+        window_sweep(msa, args.window_sweep, steps, warm, mark)
+        return
 
     peaks = None
     if not args.no_peaks:

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -358,6 +359,10 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     const int64_t per_row = Hq * K * (128 * 2 + 4);
     const int64_t auto_w = std::max<int64_t>(256, std::min<int64_t>(32768, ((int64_t)16 << 30) / per_row));
     p->attn_window = std::min<int64_t>(T, d.attn_window_rows > 0 ? d.attn_window_rows : auto_w);
+    {
+      const char* pin = std::getenv("MSA_XCD_PIN");
+      p->xcd_pin = pin && pin[0] == '1';
+    }
     const int64_t W = p->attn_window;
     const int64_t nkey = Hkv * NB;
     L.counts = off; off = align_up(off + nkey * 4, 256);
@@ -366,6 +371,7 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     L.max_items = (W * Hkv * K + p->entries_per_item - 1) / p->entries_per_item + nkey;
     L.items = off; off = align_up(off + L.max_items * 16, 256);
     L.nitems = off; off = align_up(off + 16, 256);
+    L.gitems = off; off = align_up(off + (Hkv + 1) * 4, 256);  // first work item of each KV group
     L.entries = off; off = align_up(off + W * Hkv * K * 4, 256);
     // one extra slot at index W * Hq * K takes the stores of padding rows
     L.part_o = off; off = align_up(off + (W * Hq * K + 1) * 128 * 2, 256);

@@ -33,7 +33,7 @@ struct Profiler {
 struct PlanLayout {
   size_t meta = 0, meta_bytes = 0;
   // prefill window scratch
-  size_t counts = 0, cursor = 0, offsets = 0, items = 0, nitems = 0, entries = 0, part_o = 0, part_lse = 0;
+  size_t counts = 0, cursor = 0, offsets = 0, items = 0, nitems = 0, gitems = 0, entries = 0, part_o = 0, part_lse = 0;
   // per-(token, group, slot) partials of the proxy distillation term (plans
   // with one bf16 proxy head and proxy-K head per KV group)
   size_t kl_part = 0;
@@ -66,6 +66,7 @@ struct msa_plan_s {
   // decode schedule
   int32_t dec_splits = 1;
   bool one_row = false;              // prefill plan whose every sequence has one query row
+  bool xcd_pin = false;              // prefill attention: a KV group's work items stay on one XCD
   int32_t num_cu = 256;              // compute units of the device the plan was made on
   uint64_t uid = 0;                  // serial number (workspace records name plans by it)
   mutable msa::Profiler prof;

@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
 // item list (g, global block, first entry, end entry).
 constexpr int kScanThreads = 1024;
 __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* counts, int32_t* offsets, int4* items,
-                                                                int32_t* nitems, int32_t n, int32_t NB, int32_t epi) {
+                                                                int32_t* nitems, int32_t* gitems, int32_t n, int32_t NB,
+                                                                int32_t epi) {
   __shared__ int32_t s_e[kScanThreads], s_i[kScanThreads];
   const int t = threadIdx.x;
   const int per = (n + kScanThreads - 1) / kScanThreads;
@@ -129,12 +130,14 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* c
   for (int j = lo; j < hi; ++j) {
     const int32_t c = counts[j];
     offsets[j] = e;
+    if (j % NB == 0) gitems[j / NB] = it;  // keys are group-major: a group's items are contiguous
     for (int32_t x = 0; x < c; x += epi) items[it++] = make_int4(j / NB, j % NB, e + x, e + min(c, x + epi));
     e += c;
   }
   if (t == kScanThreads - 1) {
     offsets[n] = s_e[t];
     *nitems = s_i[t];
+    gitems[n / NB] = s_i[t];
   }
 }
 
@@ -153,6 +156,8 @@ struct PartialArgs {
   const int32_t* entries;
   const int4* items;
   const int32_t* nitems;
+  const int32_t* gitems;  // first item of each KV group, [Hkv + 1]
+  int32_t xcd_pin;        // 1: workgroup i runs an item of the groups assigned to XCD i % 8
   DevMeta m;
   uint8_t* part_hi;      // partial records, block floating point (see store_rows_bfp10):
   uint8_t* part_lo;      //   planes of 128 and 32 bytes per record [rows, k, Hq], then one trash record
@@ -352,8 +357,33 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];
   __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
   __shared__ int32_t ent_s[kMaxItemEntries];
-  const int item = blockIdx.x;
-  if (item >= *a.nitems) return;
+  int item = blockIdx.x;
+  if (a.xcd_pin) {
+    // workgroups are dealt to the 8 XCDs round-robin: XCD x = blockIdx % 8
+    // runs the items of groups g = x (mod 8) (Hkv >= 8), or every (8 / Hkv)-th
+    // item of group x % Hkv (Hkv < 8), so a group's gathered Q rows stay in
+    // one XCD's L2
+    const int x = (int)(blockIdx.x & 7), jj = (int)(blockIdx.x >> 3);
+    item = -1;
+    if (a.Hkv >= 8) {
+      int rem = jj;
+      for (int gg = x; gg < a.Hkv; gg += 8) {
+        const int lo = a.gitems[gg], n = a.gitems[gg + 1] - lo;
+        if (rem < n) {
+          item = lo + rem;
+          break;
+        }
+        rem -= n;
+      }
+    } else {
+      const int per = 8 / a.Hkv, gg = x % a.Hkv;
+      const int cand = a.gitems[gg] + jj * per + x / a.Hkv;
+      if (cand < a.gitems[gg + 1]) item = cand;
+    }
+    if (item < 0) return;
+  } else if (item >= *a.nitems) {
+    return;
+  }
   const int4 it = a.items[item];
   const int g = it.x, gb = it.y, e0 = it.z, e1 = it.w;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -782,7 +812,8 @@ void build_csr(const msa_plan_s* p, const DevMeta& m, const int32_t* sel, char* 
   const size_t hist_bytes = lds_hist ? (size_t)p->NB * 4 : 0;
   if (lds_hist) hipLaunchKernelGGL((csr_pass_kernel<false, true>), cgrid, dim3(256), hist_bytes, st, c);
   else hipLaunchKernelGGL((csr_pass_kernel<false, false>), cgrid, dim3(256), 0, st, c);
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, counts, offsets, items, nitems, nkey,
+  int32_t* gitems = reinterpret_cast<int32_t*>(ws + L.gitems);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, counts, offsets, items, nitems, gitems, nkey,
                      p->NB, p->entries_per_item);
   const bool order = sorted && w1 - w0 <= kOrderMaxRows;   // longer windows keep the fill order
   hipEvent_t fill_stop = order ? nullptr : pe.stop;
@@ -822,6 +853,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   a.entries = entries;
   a.items = items;
   a.nitems = nitems;
+  a.gitems = reinterpret_cast<const int32_t*>(ws + L.gitems);
+  a.xcd_pin = p->xcd_pin && (Hkv % 8 == 0 || 8 % Hkv == 0);
   a.m = m;
   // the partial records' planes share the region the backward uses for its
   // bf16 dq partials (256 bytes per record; the forward needs 168)
@@ -838,9 +871,14 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   a.scale_log2 = p->d.sm_scale * kLog2e;
   // upper bound on the number of work items of this window
   const int64_t max_items = ((int64_t)(w1 - w0) * Hkv * k + p->entries_per_item - 1) / p->entries_per_item + nkey;
+  // pinned: 8 x a bound on one XCD's items (a group has at most W k / epi + NB)
+  const int64_t group_items = ((int64_t)(w1 - w0) * k + p->entries_per_item - 1) / p->entries_per_item + p->NB;
+  const int64_t grid_items = !a.xcd_pin ? max_items
+                             : Hkv >= 8 ? 8 * (Hkv / 8) * group_items
+                                        : 8 * ((group_items + 8 / Hkv - 1) / (8 / Hkv));
   {
     ProfEvents pe(p, "partial_attn");
-    const dim3 grid((unsigned)max_items), blk(256);
+    const dim3 grid((unsigned)grid_items), blk(256);
     if (p->d.kv_dtype == MSA_MXFP4)
       hipExtLaunchKernelGGL(partial_attn_kernel<KvFmt::MX4>, grid, blk, 0, st, pe.start, pe.stop, 0, a);
     else if (p->d.kv_dtype == MSA_FP8_E4M3)

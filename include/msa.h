@@ -117,6 +117,13 @@ typedef struct {
  * *workspace_bytes receives the device workspace size the compute calls need
  * (the caller allocates it).  The plan is released by msa_plan_destroy.
  *
+ * Environment, read here: MSA_XCD_PIN=1 makes the plan's sparse attention
+ * deal each KV group's work items to one XCD (Hkv a multiple of 8) or to
+ * 8 / Hkv XCDs (Hkv dividing 8), so that with a small attn_window_rows the
+ * group's gathered query rows stay in that XCD's L2.  Results are
+ * bit-identical; with the default window it is slower (a tuning knob, off
+ * by default).
+ *
  * Workspace metadata: the first call that uses a workspace with a plan
  * copies the plan's small metadata (row and page offsets, proxy row tiles)
  * into it, enqueued on that call's stream.  The library records which plan's

@@ -179,3 +179,35 @@ def test_onerow_64_proxy_heads_one_proxy_k_head(dt):
     check_max_score(msa.max_score_rows(ms, plan, S).cpu().numpy(), ref, w.name, extra)
     lay = O.Layout(w.qo_lens, w.kv_lens, 128)
     check_selection(sel.cpu().numpy(), ref, np.array([lay.local(r) for r in range(S)]), w.topk, w.name)
+
+
+@pytest.mark.parametrize("hkv", [8, 2])
+def test_xcd_pinned_work_items_match(hkv):
+    """MSA_XCD_PIN=1 (read when a plan is made) deals a KV group's attention
+    work items to one XCD (Hkv >= 8) or to 8 / Hkv XCDs (Hkv < 8): the same
+    items in another order, so every output is bit-identical; with small
+    attention windows (several launches)."""
+    import os
+    msa = _msa()
+    w = Workload(f"pin{hkv}", [700, 300, 129], [700, 500, 129], 2 * hkv, hkv, hkv, hkv, topk=5, poison_tail=True)
+    print(f"[invariance] XCD pinning Hkv={hkv}", flush=True)
+    inp = make_inputs(w, 58)
+    d = device_inputs(inp)
+    res = []
+    old = os.environ.get("MSA_XCD_PIN")
+    try:
+        for pin in ("0", "1"):
+            os.environ["MSA_XCD_PIN"] = pin
+            plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                                w.num_proxy_kv_heads, topk=w.topk, attn_window_rows=256)
+            res.append(_forward(msa, plan, d, w))
+    finally:
+        if old is None:
+            os.environ.pop("MSA_XCD_PIN", None)
+        else:
+            os.environ["MSA_XCD_PIN"] = old
+    for x, y in zip(*res):
+        assert torch.equal(x, y), "pinned work items give other results"
+    ref, _ = O.sparse_attention(inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, res[1][0].cpu().numpy(), w.qo_lens,
+                                w.kv_lens, 128, w.sm_scale)
+    check_output(bf16_out_to_f64(res[1][1]), ref, BF16_ATOL, BF16_COS, "pinned")
