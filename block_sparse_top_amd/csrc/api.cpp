@@ -374,7 +374,11 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     L.gitems = off; off = align_up(off + (Hkv + 1) * 4, 256);  // first work item of each KV group
     L.entries = off; off = align_up(off + W * Hkv * K * 4, 256);
     // one extra slot at index W * Hq * K takes the stores of padding rows
-    L.part_o = off; off = align_up(off + (W * Hq * K + 1) * 128 * 2, 256);
+    // the forward's partial records (and their trash records), or the
+    // backward's bf16 dq partials (one trash slot), whichever is larger
+    L.part_o = off;
+    off = align_up(off + std::max<int64_t>((W * Hq * K + 1) * 128 * 2,
+                                           (W * Hq * K + msa::kTrashRecords) * msa::kPartRecordBytes), 256);
     L.part_lse = off; off = align_up(off + (W * Hq * K + 1) * 4, 256);
     // the fused backward's proxy distillation term needs one bf16 proxy head
     // and proxy-K head per KV group: its per-(token, group, slot) partials

@@ -98,6 +98,11 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
                                  const float* qs, const float* ks, const int32_t* kv_indices, int32_t tile_lo,
                                  int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
                                  int32_t* sel, const SelScratch& scr, hipStream_t st);
+// Sparse prefill partial records: padding rows of a work item write to one
+// of this many trash records (by workgroup) after the window's records; a
+// record takes 128 + 32 bytes of code planes and 8 of {lse, step}.
+constexpr int64_t kTrashRecords = 256;
+constexpr int64_t kPartRecordBytes = 168;
 // One-query-row plans whose rows fit the wave-per-row top-k kernels (at most
 // 32 registers of 64 block scores per lane, topk - 1 kept ids in the lanes).
 inline bool onerow_wave_topk(const msa_plan_s* p) { return p->one_row && p->nb_max <= 64 * 32 && p->d.topk <= 64; }

@@ -162,7 +162,7 @@ struct PartialArgs {
   uint8_t* part_hi;      // partial records, block floating point (see store_rows_bfp10):
   uint8_t* part_lo;      //   planes of 128 and 32 bytes per record [rows, k, Hq], then one trash record
   float2* part_st;       //   {log-sum-exp, step} [rows, Hq, k], then one trash entry
-  int64_t trash;         // index of the trash record (rows * Hq * k)
+  int64_t trash;         // index of the first of kTrashRecords trash records (rows * Hq * k)
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2;      // sm_scale * log2(e)
 };
@@ -550,17 +550,21 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     sum += wave_xor32(sum);
 
     // Output: the normalised partials in block floating point, non-temporal
-    // (the merge reads each of them once)
+    // (the merge reads each of them once).  Padding rows write to one of
+    // kTrashRecords records picked by the workgroup: with one shared record,
+    // every workgroup's padding stores hit the same lines from every XCD,
+    // which doubled the kernel's time on windows of many small work items.
+    const int64_t trash = a.trash + (int64_t)(blockIdx.x & (kTrashRecords - 1));
     auto rec_index = [&](int wrow) -> int64_t {
       const int srow = 32 * wave + wrow;
       const int se = chunk * MT + srow / G;
-      if (se >= n_ent) return a.trash;
+      if (se >= n_ent) return trash;
       const int sent = ent_s[se];
       return ((int64_t)(sent >> 6) * a.k + (sent & 63)) * a.Hq + g * G + (srow & (G - 1));
     };
     const float step = store_rows_bfp10(oacc, v_scale / sum, ow, a.part_hi, a.part_lo, rec_index, lane);
     {  // both halves hold the row's max, sum and step and store the same value
-      const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : a.trash;
+      const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : trash;
       a.part_st[pi] = float2{(mx + fast_log2(sum)) * kLn2, step};  // mx is already scaled
     }
   };
@@ -859,7 +863,7 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   // the partial records' planes share the region the backward uses for its
   // bf16 dq partials (256 bytes per record; the forward needs 168)
   a.trash = p->attn_window * Hq * k;
-  const int64_t nrec = a.trash + 1;
+  const int64_t nrec = a.trash + kTrashRecords;
   a.part_hi = reinterpret_cast<uint8_t*>(ws + L.part_o);
   a.part_lo = a.part_hi + nrec * 128;
   a.part_st = reinterpret_cast<float2*>(a.part_lo + nrec * 32);

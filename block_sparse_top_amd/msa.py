@@ -127,6 +127,7 @@ class Plan:
 
     def __init__(self, desc: PlanDesc, qo, kv, device=None, allocate=True):
         self._keep = (qo, kv)
+        self.one_row = qo is not None and len(qo) > 0 and all(int(x) == 1 for x in qo)  # one query row per sequence
         h = ctypes.c_void_p()
         nbytes = ctypes.c_size_t()
         _check(_lib.msa_plan(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(nbytes)))
@@ -322,6 +323,10 @@ def run_prefill(plan: Plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale
     T, R = plan.total_rows, plan.max_rows_per_call
     if fused is None:
         fused = plan.desc.topk <= 17
+    if not fused and plan.desc.proxy_dtype != MSA_BF16 and not plan.one_row:
+        # the separate top-k ranks the fp32 scores it is given; only the fused
+        # call re-scores the fp8 / MXFP4 proxies' boundary blocks exactly
+        raise ValueError("run_prefill: fp8 / MXFP4 proxies select exactly only through the fused call (topk <= 17)")
     if fused:
         msa_proxy_topk_select(plan, proxy_q, proxy_k_pages, proxy_q_scale, proxy_k_scale, kv_indices, 0, T,
                               kv_block_indexes)

@@ -247,3 +247,16 @@ def test_lowp_plans_reserve_the_refine_queue():
     b = msa.msa_plan([4096], [4096], 32, 8, 8, 1, topk=16, allocate=False)
     f = msa.msa_plan([4096], [4096], 32, 8, 8, 1, topk=16, proxy_dtype="fp8", allocate=False)
     assert f.workspace_bytes - b.workspace_bytes >= 4096 * 8 * 64
+
+
+def test_run_prefill_refuses_inexact_low_precision_selection():
+    """fp8 / MXFP4 proxies select exactly only through the fused call (the
+    separate top-k ranks the matrix-core scores as given): run_prefill
+    refuses the separate path for them on multi-row plans (before any
+    device call)."""
+    for dt in ("fp8", "mxfp4", "mxfp4_qk"):
+        p = msa.msa_plan([300], [300], 8, 2, 2, 2, topk=18, proxy_dtype=dt, allocate=False)
+        with pytest.raises(ValueError, match="fused"):
+            msa.run_prefill(p, *([None] * 9), None, None)
+    # bf16 proxies and one-query-row plans are not refused by this check
+    assert msa.msa_plan([1, 1], [3000, 300], 8, 2, 2, 1, topk=18, proxy_dtype="fp8", allocate=False).one_row
