@@ -350,7 +350,9 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
       const bool gp = j > 0 ? cv > tv[j > 0 ? j - 1 : 0] : false;
       const float up = j > 0 ? tv[j > 0 ? j - 1 : 0] : kPosInf;
       const int upi = j > 0 ? ti[j > 0 ? j - 1 : 0] : 0;
-      ti[j] = gj ? (gp ? upi : ci) : ti[j];
+      // selects, not branches (every lane updates its own list)
+      const int nv = __builtin_unpredictable(gp) ? upi : ci;
+      ti[j] = __builtin_unpredictable(gj) ? nv : ti[j];
       tv[j] = __builtin_amdgcn_fmed3f(up, cv, tv[j]);
     }
   };
