@@ -123,6 +123,17 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // Wait for every outstanding memory counter (vector memory, LDS, exports).
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (N < 64; loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+#if defined(__HIP_DEVICE_COMPILE__)
+  // simm16: vmcnt [3:0] and [15:14], expcnt [6:4] = 7 and lgkmcnt [11:8] = 15 (no wait on those)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+#endif
+}
+
 __device__ __forceinline__ void wait_all_mem() {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_s_waitcnt(0);

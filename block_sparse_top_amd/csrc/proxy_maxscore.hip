@@ -219,14 +219,23 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
   using BFrag = typename Tr::BFrag;
   constexpr int kBlockBytes = Tr::kKBlockBytes;           // one K block in global memory
   constexpr int kCodeBytes = 128 * Tr::kKRowBytes;        // its key rows (MXFP4: the scales follow)
-  constexpr int kLoads = kCodeBytes / 1024 / kProxyWaves;  // 1 KB direct-to-LDS loads per wave
+  constexpr int kStageLoads = kCodeBytes / (F == Fmt::BF16 ? 2 : 1) / 1024 / kProxyWaves;  // 1 KB loads per wave per stage
   constexpr int kChunksPerRow = Tr::kKRowBytes / 16;
   constexpr int kRowsPerKB = 1024 / Tr::kKRowBytes;
-  // two distinct tile objects (not one array indexed by a runtime buffer
-  // number): the loads in flight into one are then provably disjoint from
-  // the reads of the other
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBlockBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBlockBytes];
+  // K arrives in stages through a ring of four LDS tiles, each stage issued
+  // three stages before it is used: half blocks (64 key rows) for bf16,
+  // whole blocks for the smaller fp8 and MXFP4 blocks (an MXFP4 tile: the
+  // codes, then the rows' scales).  Four distinct tile objects (not one array
+  // indexed by a runtime buffer number): the loads in flight into three of
+  // them are then provably disjoint from the reads of the fourth.
+  constexpr int kParts = F == Fmt::BF16 ? 2 : 1;        // stages per block
+  constexpr int kStageBytes = kBlockBytes / kParts;
+  constexpr int kStageCodeBytes = kCodeBytes / kParts;
+  constexpr int kStageRows = 128 / kParts;
+  __shared__ __attribute__((aligned(1024))) uint8_t h0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t h1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t h2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t h3[kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,21 +274,24 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
     }
   }
 
-  // K block -> LDS without registers: each wave issues kLoads direct 1 KB
-  // loads (global_load_lds_dwordx4: lane i fills bytes 16i..16i+15 of the
-  // KB), fetching for each lane the global chunk its swizzled slot holds;
-  // an MXFP4 block's 512 scale bytes follow unswizzled (the last wave).
-  auto kload = [&](int32_t page, uint8_t* tile) {
+  // Stage `part` of a K block -> LDS without registers: each wave issues
+  // kStageLoads direct 1 KB loads (global_load_lds_dwordx4: lane i fills
+  // bytes 16i..16i+15 of the KB), fetching for each lane the global chunk its
+  // swizzled slot holds (the swizzle depends on the row modulo 16, so tile
+  // and block rows agree); an MXFP4 block's 512 scale bytes follow
+  // unswizzled (the last wave).
+  auto kload = [&](int32_t page, int part, uint8_t* tile) {
     const uint8_t* src = a.pk + ((int64_t)page * a.Pk + ph) * kBlockBytes;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
+    for (int i = 0; i < kStageLoads; ++i) {
       const int kb = wave + kProxyWaves * i;             // which KB of the tile
-      const int row = kb * kRowsPerKB + lane / kChunksPerRow;
+      const int row = kStageRows * part + kb * kRowsPerKB + lane / kChunksPerRow;
       const int pc = lane % kChunksPerRow;               // physical chunk written by this lane
       const int lc = pc ^ Tr::swz(row);                  // logical chunk it must hold
       global_load_lds16(src + row * Tr::kKRowBytes + lc * 16, (MSA_LDS void*)(tile + kb * 1024));
     }
     if constexpr (kMxK<F>) {
+      static_assert(kParts == 1, "MXFP4 K stages are whole blocks");
       if (wave == kProxyWaves - 1 && lane < 32)
         global_load_lds16(src + kCodeBytes + lane * 16, (MSA_LDS void*)(tile + kCodeBytes));
     }
@@ -357,10 +369,11 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
     }
   };
 
-  auto block_max = [&](const uint8_t* tile, int b, float (&m)[2]) {
-    m[0] = m[1] = kNegInf;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+  // keys 64 hf .. 64 hf + 63 of block b (their key rows from `tile`, their
+  // MXFP4 scale words from `scales`): m takes the max over them (rows `sub`
+  // of the lane's two row tiles)
+  auto half_max = [&](const uint8_t* tile, const uint8_t* scales, int b, int hf, float (&m)[2]) {
+    {
       f32x16 acc[2][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = f32x16{};
@@ -368,8 +381,7 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
       if constexpr (kMxK<F>) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          ksc[j] = (int32_t)(lds_load16<uint32_t>(tile + kCodeBytes + 4 * (32 * (2 * hf + j) + (lane & 31))) >>
-                             (8 * hsel));
+          ksc[j] = (int32_t)(lds_load16<uint32_t>(scales + 4 * (32 * j + (lane & 31))) >> (8 * hsel));
           // bytes 0 and 2 of the shifted word are the ones this lane's MFMAs
           // use.  Only blocks before the tile's last local block can compete
           // for any of its rows, and they are whole (a sequence's partial last
@@ -380,13 +392,13 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
       }
       AFrag fr[2][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fr[0][j] = load_k_frag<F>(tile, 32 * (2 * hf + j) + (lane & 31), 0, hsel);
+      for (int j = 0; j < 2; ++j) fr[0][j] = load_k_frag<F>(tile, 32 * j + (lane & 31), 0, hsel);
 #pragma unroll
       for (int st = 0; st < Tr::kSteps; ++st) {
         if (st + 1 < Tr::kSteps) {
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            fr[(st + 1) & 1][j] = load_k_frag<F>(tile, 32 * (2 * hf + j) + (lane & 31), st + 1, hsel);
+            fr[(st + 1) & 1][j] = load_k_frag<F>(tile, 32 * j + (lane & 31), st + 1, hsel);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -454,30 +466,59 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
     }
   };
 
-  // block loop unrolled by two over the two tiles: block b computes from one
-  // tile while block b+1 streams into the other; pairs run unconditionally
-  // and an odd last block follows the loop (no branch inside the loop body
-  // that the per-row selection state has to flow through)
-  auto step = [&](int b, const uint8_t* tile, uint8_t* next_tile) __attribute__((always_inline)) {
-    advance(b);
-    if (b + 1 <= b_last) kload(page_of(b + 1), next_tile);
-    float m[2];
-    if (wave_active) {
-      block_max(tile, b, m);
-      finish(b, m);
-    }
-    wait_all_mem();
-    __syncthreads();
+  // Stages s = 2 b + hf over the blocks' halves, loop unrolled by four over
+  // the four tiles: stage s waits for its own half (the two later halves may
+  // stay in flight), a barrier makes every wave's part of it visible and
+  // frees stage s - 1's tile, into which the half of stage s + 3 is issued
+  // before stage s computes.  Past the last stage the loads repeat it (in
+  // bounds, never read), so every stage issues the same loads and the wait
+  // count is exact; groups run unconditionally and the two stages of an odd
+  // last block follow the loop (no branch inside the loop body that the
+  // per-row selection state has to flow through).
+  const int S = kParts * (b_last + 1);
+  auto issue = [&](int s2, uint8_t* tile) {
+    const int ss = min(s2, S - 1);
+    kload(page_of(ss / kParts), ss % kParts, tile);
   };
-  kload(page_of(0), lds0);
-  wait_all_mem();
-  __syncthreads();
-  int b = 0;
-  for (; b + 1 <= b_last; b += 2) {
-    step(b, lds0, lds1);
-    step(b + 1, lds1, lds0);
+  float m[2] = {kNegInf, kNegInf};
+  // `part` is a constant at each call (stages s2 with s2 % kParts == part)
+  auto stage = [&](int s2, int part, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+    const int b = s2 / kParts;
+    // this wave's part of stage s2 has landed; after the barrier every wave's
+    // has, and every wave is done with stage s2 - 1's tile (its reads fed
+    // that stage's products).  No workgroup fence: it would wait for every
+    // load in flight, the ring included.
+    wait_vmcnt<2 * kStageLoads>();
+    lds_barrier();
+    if (part == 0) advance(b);
+    issue(s2 + 3, nxt);
+    if (wave_active) {
+      if (part == 0) m[0] = m[1] = kNegInf;
+      if constexpr (kParts == 2) {
+        half_max(cur, cur, b, part, m);
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) half_max(cur + 64 * hf * Tr::kKRowBytes, cur + kCodeBytes + 256 * hf, b, hf, m);
+      }
+      if (part == kParts - 1) finish(b, m);
+    }
+  };
+  issue(0, h0);
+  issue(1, h1);
+  issue(2, h2);
+  __syncthreads();  // the q fragments' loads above are long done; a plain barrier before the ring
+  int s2 = 0;
+  for (; s2 + 3 < S; s2 += 4) {
+    stage(s2, 0, h0, h3);
+    stage(s2 + 1, 1 % kParts, h1, h0);
+    stage(s2 + 2, 0, h2, h1);
+    stage(s2 + 3, 1 % kParts, h3, h2);
   }
-  if (b <= b_last) step(b, lds0, lds1);
+  // the last S % 4 stages (S % 4 is 0 or 2 for half-block stages)
+  if (s2 < S) stage(s2, 0, h0, h3);
+  if (s2 + 1 < S) stage(s2 + 1, 1 % kParts, h1, h0);
+  if (s2 + 2 < S) stage(s2 + 2, 0, h2, h1);
+  wait_all_mem();  // the repeated loads past the last stage land before the workgroup ends
 
   if constexpr (TOPK) {
     // the R = min(k - 1, local) best earlier blocks and the local block, ascending, -1 padded
