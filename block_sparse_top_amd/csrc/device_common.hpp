@@ -176,6 +176,14 @@ __device__ __forceinline__ float dpp_f32(float v) {
 // read address is computed once (8 K bases, one per 32-byte column step; 4 V
 // bases, one per 32-column tile) and the row offsets become immediates.
 __device__ __forceinline__ int k_swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+// Tiles read both row-wise (16 consecutive rows at one 16-byte chunk: the
+// A operands) and transposed (ds_read_b64_tr_b16 over groups of 4 rows): the
+// chunk is XORed with a bijection of the row's low 4 bits whose row & 3 part
+// moves chunk bits 2-3, so each 16-lane phase of either pattern touches every
+// bank once (k_swz: the transposed reads collide pairwise; v_swz: the
+// row-wise reads collide 4 ways).
+__device__ __forceinline__ int rt_swz_key(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int rt_swz(int row, int chunk) { return row * 256 + ((chunk ^ rt_swz_key(row)) << 4); }
 __device__ __forceinline__ int v_swz(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 2)) << 4); }
 
 // A workgroup barrier that waits only for this wave's LDS traffic, so global

@@ -1313,9 +1313,9 @@ struct BwdKvArgs {
 // dense main attention), in row order, instead of the bin's CSR entries.
 template <bool KL, bool DENSE = false>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];    // a chunk's 32 q rows, v_swz, two buffers
-  __shared__ __attribute__((aligned(16))) uint8_t dtile[2][32 * 256]; // a chunk's 32 dO rows, v_swz
-  // the chunk's proxy q rows (row i: token i / G), v_swz
+  __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];    // a chunk's 32 q rows, rt_swz, two buffers
+  __shared__ __attribute__((aligned(16))) uint8_t dtile[2][32 * 256]; // a chunk's 32 dO rows, rt_swz
+  // the chunk's proxy q rows (row i: token i / G), rt_swz
   __shared__ __attribute__((aligned(16))) uint8_t ptile[KL ? 2 : 1][KL ? 32 * 256 : 16];
   __shared__ __attribute__((aligned(16))) float l2_s[2][32];
   __shared__ __attribute__((aligned(16))) float d_s[2][32];
@@ -1359,11 +1359,19 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
   const int q16 = lane >> 4, m16 = lane & 15;
   const int nchunks = (n_ent + MT - 1) / MT;
   const int keypos = b * 128 + 32 * wave + j;  // this lane's key position
-  int vbase[4];
+  // transposed reads: lane (q16, m16) fetches dims 32 dt + 16 (q16 & 1) +
+  // 4 (m16 & 3) .. +3 of tile row r0 (lo) or r0 + 8 (hi), r0 = 4 (q16 >> 1) +
+  // m16 / 4 (+ 16 u)
+  int vlo[4], vhi[4];
+  {
+    const int r0 = 4 * (q16 >> 1) + (m16 >> 2);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-    vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
-                ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+    for (int dt = 0; dt < 4; ++dt) {
+      const int c = 4 * dt + 2 * (q16 & 1) + ((m16 & 3) >> 1);
+      vlo[dt] = rt_swz(r0, c) + 8 * (m16 & 1);
+      vhi[dt] = rt_swz(r0 + 8, c) + 8 * (m16 & 1);
+    }
+  }
   f32x16 dkacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   f32x16 dvacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   f32x16 pkacc[KL ? 4 : 1];
@@ -1411,13 +1419,13 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
     es = tid < 32 ? entry_of(1, tid) : 0;
     for (int chunk = 0; chunk < nchunks; ++chunk) {
       const int buf = chunk & 1;
-      lds_store16<i32x4>(&qt[buf][v_swz(ri0, cc)], rq0);
-      lds_store16<i32x4>(&qt[buf][v_swz(ri1, cc)], rq1);
-      lds_store16<i32x4>(&dtile[buf][v_swz(ri0, cc)], rd0);
-      lds_store16<i32x4>(&dtile[buf][v_swz(ri1, cc)], rd1);
+      lds_store16<i32x4>(&qt[buf][rt_swz(ri0, cc)], rq0);
+      lds_store16<i32x4>(&qt[buf][rt_swz(ri1, cc)], rq1);
+      lds_store16<i32x4>(&dtile[buf][rt_swz(ri0, cc)], rd0);
+      lds_store16<i32x4>(&dtile[buf][rt_swz(ri1, cc)], rd1);
       if constexpr (KL) {
-        lds_store16<i32x4>(&ptile[buf][v_swz(ri0, cc)], rp0);
-        lds_store16<i32x4>(&ptile[buf][v_swz(ri1, cc)], rp1);
+        lds_store16<i32x4>(&ptile[buf][rt_swz(ri0, cc)], rp0);
+        lds_store16<i32x4>(&ptile[buf][rt_swz(ri1, cc)], rp1);
       }
       if (tid < 32) {
         l2_s[buf][tid] = rlse * kLog2e;
@@ -1451,9 +1459,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const bf16x8 aq = lds_load16<bf16x8>(&qb[v_swz(j, 2 * st + half)]);
+        const bf16x8 aq = lds_load16<bf16x8>(&qb[rt_swz(j, 2 * st + half)]);
         sacc = mfma32x32x16(aq, bk[st], sacc);
-        const bf16x8 ad = lds_load16<bf16x8>(&db[v_swz(j, 2 * st + half)]);
+        const bf16x8 ad = lds_load16<bf16x8>(&db[rt_swz(j, 2 * st + half)]);
         pacc = mfma32x32x16(ad, bv[st], pacc);
       }
       // P and dS (register r holds row 8(r/4) + 4 half + r%4), as bf16 A operands;
@@ -1494,15 +1502,15 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const s16x4 dlo = lds_read_tr16(&db[vbase[dt] + 256 * (16 * u)]);
-          const s16x4 dhi = lds_read_tr16(&db[vbase[dt] + 256 * (16 * u + 8)]);
+          const s16x4 dlo = lds_read_tr16(&db[vlo[dt] + 256 * (16 * u)]);
+          const s16x4 dhi = lds_read_tr16(&db[vhi[dt] + 256 * (16 * u)]);
           dvacc[dt] = mfma32x32x16(pf[u], join_tr16(dlo, dhi), dvacc[dt]);
-          const s16x4 qlo = lds_read_tr16(&qb[vbase[dt] + 256 * (16 * u)]);
-          const s16x4 qhi = lds_read_tr16(&qb[vbase[dt] + 256 * (16 * u + 8)]);
+          const s16x4 qlo = lds_read_tr16(&qb[vlo[dt] + 256 * (16 * u)]);
+          const s16x4 qhi = lds_read_tr16(&qb[vhi[dt] + 256 * (16 * u)]);
           dkacc[dt] = mfma32x32x16(sf[u], join_tr16(qlo, qhi), dkacc[dt]);
           if constexpr (KL) {   // P^T times the rows' proxy q
-            const s16x4 plo = lds_read_tr16(&ptile[buf][vbase[dt] + 256 * (16 * u)]);
-            const s16x4 phi = lds_read_tr16(&ptile[buf][vbase[dt] + 256 * (16 * u + 8)]);
+            const s16x4 plo = lds_read_tr16(&ptile[buf][vlo[dt] + 256 * (16 * u)]);
+            const s16x4 phi = lds_read_tr16(&ptile[buf][vhi[dt] + 256 * (16 * u)]);
             pkacc[dt] = mfma32x32x16(pf[u], join_tr16(plo, phi), pkacc[dt]);
           }
         }
