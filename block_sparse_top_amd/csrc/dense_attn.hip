@@ -230,15 +230,15 @@ struct DenseDqArgs {
   float inv_g;
 };
 
-// K sits in LDS once (k_swz), read directly for S^T and transposed for K^T;
+// K sits in LDS once (rt_swz), read directly for S^T and transposed for K^T;
 // blocks are taken in two 64-key halves.  The plain variant loads each block
 // straight into LDS and fits two workgroups per CU (64 KB, 256 registers),
 // whose block loads overlap each other's MFMAs; with the proxy term (96 KB)
 // one workgroup per CU prefetches the next block into registers instead.
 template <bool KL>
 __global__ __launch_bounds__(256, KL ? 1 : 2) void dense_dq_kernel(DenseDqArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz: S^T operand and K^T reads
-  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, k_swz: dP^T operand
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, rt_swz: S^T operand and K^T reads
+  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, rt_swz: dP^T operand
   __shared__ __attribute__((aligned(16))) uint8_t pkt[KL ? 128 * 256 : 16];   // proxy K, v_swz
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -263,13 +263,13 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void dense_dq_kernel(DenseDqArgs a
   const float dval = a.D[(int64_t)d.r * a.Hq + d.h];
   int kbase[8];
 #pragma unroll
-  for (int st = 0; st < 8; ++st) kbase[st] = j * 256 + (((2 * st + half) ^ (lane & 15)) << 4);
+  for (int st = 0; st < 8; ++st) kbase[st] = rt_swz(j, 2 * st + half);
   int vbase[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
     vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
-  // transposed reads of the k_swz tile: lane (q16, m16) fetches dims
+  // transposed reads of the rt_swz tile: lane (q16, m16) fetches dims
   // 32 dt + 16 (q16 & 1) + 4 (m16 & 3) .. +3 of key row r0 (lo) or r0 + 8 (hi)
   int ktlo[4], kthi[4];
   {
@@ -277,8 +277,8 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void dense_dq_kernel(DenseDqArgs a
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const int c = 4 * dt + 2 * (q16 & 1) + ((m16 & 3) >> 1);
-      ktlo[dt] = r0 * 256 + ((c ^ r0) << 4) + 8 * (m16 & 1);
-      kthi[dt] = (r0 + 8) * 256 + ((c ^ (r0 + 8)) << 4) + 8 * (m16 & 1);
+      ktlo[dt] = rt_swz(r0, c) + 8 * (m16 & 1);
+      kthi[dt] = rt_swz(r0 + 8, c) + 8 * (m16 & 1);
     }
   }
   i32x4 kr[8], vr[8], pr[KL ? 8 : 1];
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void dense_dq_kernel(DenseDqArgs a
       for (int i = 0; i < 8; ++i) {
         const int c = tid + 256 * i;
         const bool live_row = (c >> 4) < kv_in_block;
-        lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
-        lds_store16<i32x4>(&vs[k_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
+        lds_store16<i32x4>(&ks[rt_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
+        lds_store16<i32x4>(&vs[rt_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
         if constexpr (KL) lds_store16<i32x4>(&pkt[v_swz(c >> 4, c & 15)], live_row ? pr[i] : i32x4{});
       }
     }

@@ -212,7 +212,7 @@ struct KlDkArgs {
 };
 
 __global__ __launch_bounds__(256) void kl_dense_dk_kernel(KlDkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];   // a chunk's 32 proxy q rows, v_swz
+  __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];   // a chunk's 32 proxy q rows, rt_swz
   __shared__ __attribute__((aligned(16))) float l2_s[2][32];
   __shared__ __attribute__((aligned(16))) int32_t pos_s[2][32];
   // block-major order: early blocks, seen by the most rows, start first
@@ -238,11 +238,19 @@ __global__ __launch_bounds__(256) void kl_dense_dk_kernel(KlDkArgs a) {
   }
   const int q16 = lane >> 4, m16 = lane & 15;
   const int keypos = b * 128 + 32 * wave + j;
-  int vbase[4];
+  // transposed reads: lane (q16, m16) fetches dims 32 dt + 16 (q16 & 1) +
+  // 4 (m16 & 3) .. +3 of tile row r0 (lo) or r0 + 8 (hi), r0 = 4 (q16 >> 1) +
+  // m16 / 4 (+ 16 u)
+  int vlo[4], vhi[4];
+  {
+    const int r0 = 4 * (q16 >> 1) + (m16 >> 2);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-    vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
-                ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+    for (int dt = 0; dt < 4; ++dt) {
+      const int c = 4 * dt + 2 * (q16 & 1) + ((m16 & 3) >> 1);
+      vlo[dt] = rt_swz(r0, c) + 8 * (m16 & 1);
+      vhi[dt] = rt_swz(r0 + 8, c) + 8 * (m16 & 1);
+    }
+  }
   f32x16 dkacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   const int nchunks = (nrows + 31) / 32;
   // gather slots: rows ri0 and ri0 + 16 of a chunk, 16-byte column cc; the
@@ -258,8 +266,8 @@ __global__ __launch_bounds__(256) void kl_dense_dk_kernel(KlDkArgs a) {
     if (tid < 32) rlse = a.plse[(int64_t)(r0 + min(tid, nrows - 1)) * a.P + p];
     for (int chunk = 0; chunk < nchunks; ++chunk) {
       const int buf = chunk & 1;
-      lds_store16<i32x4>(&qt[buf][v_swz(ri0, cc)], rq0);
-      lds_store16<i32x4>(&qt[buf][v_swz(ri1, cc)], rq1);
+      lds_store16<i32x4>(&qt[buf][rt_swz(ri0, cc)], rq0);
+      lds_store16<i32x4>(&qt[buf][rt_swz(ri1, cc)], rq1);
       if (tid < 32) {
         const int i = chunk * 32 + tid;
         l2_s[buf][tid] = rlse * kLog2e;
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(256) void kl_dense_dk_kernel(KlDkArgs a) {
       f32x16 sacc = f32x16{};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const bf16x8 aq = lds_load16<bf16x8>(&qb[v_swz(j, 2 * st + half)]);
+        const bf16x8 aq = lds_load16<bf16x8>(&qb[rt_swz(j, 2 * st + half)]);
         sacc = mfma32x32x16(aq, bk[st], sacc);
       }
       f32x4 l2v[4];
@@ -308,8 +316,8 @@ __global__ __launch_bounds__(256) void kl_dense_dk_kernel(KlDkArgs a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const s16x4 qlo = lds_read_tr16(&qb[vbase[dt] + 256 * (16 * u)]);
-          const s16x4 qhi = lds_read_tr16(&qb[vbase[dt] + 256 * (16 * u + 8)]);
+          const s16x4 qlo = lds_read_tr16(&qb[vlo[dt] + 256 * (16 * u)]);
+          const s16x4 qhi = lds_read_tr16(&qb[vhi[dt] + 256 * (16 * u)]);
           dkacc[dt] = mfma32x32x16(pf[u], join_tr16(qlo, qhi), dkacc[dt]);
         }
     }

@@ -439,19 +439,6 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   for (int dt = 0; dt < 4; ++dt)
     vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
-  // transposed reads of the k_swz tile: lane (q16, m16) fetches dims
-  // 32 dt + 16 (q16 & 1) + 4 (m16 & 3) .. +3 of key row r0 (lo) or r0 + 8
-  // (hi), r0 = 4 (q16 >> 1) + m16 / 4 (+ the 16-row offsets of the reads)
-  int ktlo[4], kthi[4];
-  {
-    const int r0 = 4 * (q16 >> 1) + (m16 >> 2);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int c = 4 * dt + 2 * (q16 & 1) + ((m16 & 3) >> 1);
-      ktlo[dt] = r0 * 256 + ((c ^ r0) << 4) + 8 * (m16 & 1);
-      kthi[dt] = (r0 + 8) * 256 + ((c ^ (r0 + 8)) << 4) + 8 * (m16 & 1);
-    }
-  }
   uint8_t* ow = ost + wave * kOStage;
 
   // Q fragments (B operand) of a chunk's row for this lane: gathered rows
@@ -988,14 +975,14 @@ struct BwdDqArgs {
   float inv_g;
 };
 
-// K sits in LDS once (k_swz): read directly as the S^T operand and with
+// K sits in LDS once (rt_swz): read directly as the S^T operand and with
 // transposed reads (addresses ktlo / kthi below) as K^T; each 128-key block is
 // taken in two 64-key halves, so that the plain variant fits two workgroups
 // per CU (74 KB of LDS, 256 registers).
 template <bool KL>
 __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, k_swz: S^T operand and K^T reads
-  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, k_swz: dP^T operand
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, rt_swz: S^T operand and K^T reads
+  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, rt_swz: dP^T operand
   __shared__ __attribute__((aligned(16))) uint8_t pkt[KL ? 128 * 256 : 16];   // proxy K, v_swz
   __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
   __shared__ int32_t ent_s[kMaxItemEntries];
@@ -1026,8 +1013,8 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
     for (int i = 0; i < 8; ++i) {
       const int c = tid + 256 * i;
       const bool live_row = (c >> 4) < kv_in_block;
-      lds_store16<i32x4>(&ks[k_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
-      lds_store16<i32x4>(&vs[k_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
+      lds_store16<i32x4>(&ks[rt_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
+      lds_store16<i32x4>(&vs[rt_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
     }
     if constexpr (KL) {
       const uint8_t* pb = a.pkp + ((int64_t)page * a.Hkv + g) * 32768;
@@ -1052,13 +1039,13 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
   const int nchunks = (n_ent + MT - 1) / MT;
   int kbase[8];
 #pragma unroll
-  for (int st = 0; st < 8; ++st) kbase[st] = (lane & 31) * 256 + (((2 * st + half) ^ (lane & 15)) << 4);
+  for (int st = 0; st < 8; ++st) kbase[st] = rt_swz((lane & 31), 2 * st + half);
   int vbase[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
     vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
-  // transposed reads of the k_swz tile: lane (q16, m16) fetches dims
+  // transposed reads of the rt_swz tile: lane (q16, m16) fetches dims
   // 32 dt + 16 (q16 & 1) + 4 (m16 & 3) .. +3 of key row r0 (lo) or r0 + 8
   // (hi), r0 = 4 (q16 >> 1) + m16 / 4 (+ the 16-row offsets of the reads)
   int ktlo[4], kthi[4];
@@ -1067,8 +1054,8 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const int c = 4 * dt + 2 * (q16 & 1) + ((m16 & 3) >> 1);
-      ktlo[dt] = r0 * 256 + ((c ^ r0) << 4) + 8 * (m16 & 1);
-      kthi[dt] = (r0 + 8) * 256 + ((c ^ (r0 + 8)) << 4) + 8 * (m16 & 1);
+      ktlo[dt] = rt_swz(r0, c) + 8 * (m16 & 1);
+      kthi[dt] = rt_swz(r0 + 8, c) + 8 * (m16 & 1);
     }
   }
   uint8_t* ow = ost + wave * kOStage;
