@@ -441,8 +441,13 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
       pend_b = b;
       pend_ok = b < my_local;
       ins_begin();
+      // a score not above the list's last entry changes nothing: skip the
+      // insertion when that holds for every row of the wave (on long rows,
+      // most blocks once the lists have filled)
+      if (__builtin_amdgcn_ballot_w64(cv > tv[kCap - 1]) != 0) {
 #pragma unroll
-      for (int r = 0; r < kCap / 4; ++r) ins_steps(r);
+        for (int r = 0; r < kCap / 4; ++r) ins_steps(r);
+      }
     } else {
       if (writes) outp[(int64_t)b * a.row_count] = v;
     }
