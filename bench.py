@@ -93,6 +93,14 @@ MFMA_PMC_ARGS = ("--steps 2 --warmup 1 --no-cpu-baseline --no-peaks --profile-ru
                  "prefill_128k,prefill_32k_mxfp4,prefill_32k_backward,warmup_32k,decode_131k,decode_step_131k")
 MFMA_CMD = (f"rocprofv3 --pmc {MFMA_COUNTERS} {PMC_FILTER} -f csv -d gpurun_out/pmc_mfma -o m -- python bench.py "
             f"{MFMA_PMC_ARGS}")
+STALL_COUNTERS = {
+    "a": "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+         "SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_ANY",
+    "b": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_INSTS_SALU "
+         "SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU_TRANS_F32"}
+STALL_PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --no-peaks --profile-run --extra prefill_32k_backward"
+STALL_CMDS = {k: f"rocprofv3 --pmc {v} --kernel-include-regex \"msa\" -f csv -d gpurun_out/stall_{k} -o s -- python "
+                 f"bench.py {STALL_PMC_ARGS}" for k, v in STALL_COUNTERS.items()}
 NUM_CU, SIMD_PER_CU, NUM_XCD = 256, 4, 8
 SECTION_OF_KERNEL = {"decode": "decode_fp8_b32_131k", "decode_merge": "decode_fp8_b32_131k",
                      "proxy_onerow": "decode_step_b32_131k", "topk_wave": "decode_step_b32_131k",
@@ -233,6 +241,67 @@ def summarize_mfma(mfma_csv: str, bench_err: str, out_name: str):
     out += ["", json.dumps({"rows": rows}), ""]
     path = os.path.join(ROOT, "profiles", out_name)
     open(path, "w").write("\n".join(out))
+    return path
+
+
+def summarize_stalls(a_csv: str, b_csv: str, out_name: str):
+    """Where the waves of each library kernel spend their cycles (two
+    rocprofv3 --pmc passes over the 32K prefill and backward, STALL_CMDS),
+    as fractions of SQ_WAVE_CYCLES: waiting at s_waitcnt (memory or LDS),
+    waiting for an issue slot or a dependency, and issuing VALU, LDS, VMEM or
+    any instruction; plus instruction counts per MFMA."""
+    import collections
+    import csv
+
+    def load(path):
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        kn = {}
+        for r in csv.DictReader(open(path)):
+            k = _short_kernel(r["Kernel_Name"])
+            if k is None or k == "copy":
+                continue
+            d = int(r["Dispatch_Id"])
+            kn[d] = k
+            per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        agg = collections.defaultdict(lambda: collections.defaultdict(float))
+        n = collections.Counter()
+        for d, c in per.items():
+            n[kn[d]] += 1
+            for name, v in c.items():
+                agg[kn[d]][name] += v
+        return agg, n
+
+    a, na = load(a_csv)
+    b, _ = load(b_csv)
+    out = ["# Wave cycles and instruction mix per kernel (rocprofv3 --pmc, 32K prefill and backward, summed over "
+           "dispatches)",
+           f"# pass a: {STALL_CMDS['a']}", f"# pass b: {STALL_CMDS['b']}",
+           f"# summary: python bench.py --summarize-stalls <pass a csv> <pass b csv> {out_name}",
+           "# fractions of SQ_WAVE_CYCLES (cycles summed over resident waves): wait = at s_waitcnt, dep = waiting "
+           "for an issue slot or an operand, valu / lds / vmem / any = issuing that kind",
+           "", "| kernel | dispatches | wait | dep | valu | lds | vmem | any issue | VALU / MFMA | LDS / MFMA | "
+           "transcendental / MFMA | MFMA-VALU co-issue / wave cycle |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    rows = []
+    for k in sorted(a, key=lambda x: -a[x]["SQ_WAVE_CYCLES"]):
+        x, y = a[k], b.get(k, {})
+        wc = x["SQ_WAVE_CYCLES"] or 1.0
+        mf = y.get("SQ_INSTS_MFMA", 0.0)
+        per = (lambda c: f"{y.get(c, 0.0) / mf:.1f}" if mf else "")
+        row = {"kernel": k, "dispatches": na[k]}
+        row.update({c: x[c] / wc for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                                           "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_ANY")})
+        row.update({c: y.get(c, 0.0) for c in STALL_COUNTERS["b"].split()})
+        rows.append(row)
+        out.append(f"| {k} | {na[k]} | {row['SQ_WAIT_ANY']:.2f} | {row['SQ_WAIT_INST_ANY']:.2f} | "
+                   f"{row['SQ_ACTIVE_INST_VALU']:.2f} | {row['SQ_ACTIVE_INST_LDS']:.2f} | "
+                   f"{row['SQ_ACTIVE_INST_VMEM']:.2f} | {row['SQ_ACTIVE_INST_ANY']:.2f} | {per('SQ_INSTS_VALU')} | "
+                   f"{per('SQ_INSTS_LDS')} | {per('SQ_INSTS_VALU_TRANS_F32')} | "
+                   f"{y.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0.0) / wc:.3f} |")
+    out.append("")
+    out.append(json.dumps({"rows": rows}))
+    path = os.path.join(ROOT, "profiles", out_name)
+    open(path, "w").write("\n".join(out) + "\n")
     return path
 
 
@@ -391,6 +460,25 @@ def time_by_duration(step, warm_ms=50.0, rep_ms=200.0):
         step()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / reps, reps
+
+
+def stream_event_ms(step, warm_ms=50.0, rep_ms=200.0):
+    """Per-step time from one pair of HIP events recorded on the launch stream
+    around a block of back-to-back steps (no per-dispatch events): for a
+    step that is a single kernel launch, that kernel's average duration
+    including the gaps between launches."""
+    import torch
+    per, _ = time_by_duration(step, warm_ms, 20.0)   # warm-up, and the step time the block is sized from
+    n = max(16, int(math.ceil(rep_ms / per)))
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(n):
+        step()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n, n
 
 
 def host_cost_us(step, n=200):
@@ -834,6 +922,13 @@ def decode_bench(msa, steps, warmup, sets=4):
     # eagerly and replayed from a HIP graph, with no profiling events attached
     _, k_ms, launches = timed_with_kernel(msa, plan, step, steps, warmup, "decode")
     launches_per_step = max(1, launches // steps)
+    k_timing = "per-dispatch HIP events"
+    if "decode_merge" not in per_kernel and launches_per_step == 1 and not PROFILE_RUN[0]:
+        # the step is this one kernel: a pair of events around a block of
+        # back-to-back launches on the launch stream times it without the
+        # per-dispatch events' own cost (a few microseconds a launch)
+        k_ms, _ = stream_event_ms(step)
+        k_timing = "HIP events on the launch stream around a block of back-to-back launches (one launch per step)"
     if PROFILE_RUN[0]:
         ms_step, timed = time_steps(step, steps, warmup), steps
         host_us, g_ms, g_steps = None, float("nan"), 0
@@ -851,6 +946,7 @@ def decode_bench(msa, steps, warmup, sets=4):
     roof = with_measured({"kernel": "decode", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                           "traffic": traffic_from_profiles("decode", w.name), "avg_launch_ms": k_ms,
+                          "launch_timing": k_timing,
                           "launches_per_step": launches_per_step, "work_per_launch": work, "work_unit": "B"})
     return {
         "workload": w.name, "tok_per_s": w.num_seqs / (ms_step * 1e-3), "ms_per_step": ms_step,
@@ -1016,6 +1112,8 @@ def main():
                     help="host only: write a kernel-duration summary under profiles/ from a rocprofv3 kernel trace")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("MFMA_CSV", "BENCH_STDERR", "OUT_NAME"),
                     help="host only: write a matrix-core / LDS counter summary under profiles/")
+    ap.add_argument("--summarize-stalls", nargs=3, metavar=("PASS_A_CSV", "PASS_B_CSV", "OUT_NAME"),
+                    help="host only: write the wave-cycle / instruction-mix summary under profiles/")
     ap.add_argument("--window-sweep", type=int, metavar="CFG",
                     help="only the sparse prefill of workload CFG at attention windows 32K/8K/4K/2K, without and with "
                          "XCD pinning (one JSON line each)")
@@ -1032,6 +1130,9 @@ def main():
         return
     if args.summarize_mfma:
         print(summarize_mfma(*args.summarize_mfma))
+        return
+    if args.summarize_stalls:
+        print(summarize_stalls(*args.summarize_stalls))
         return
     if args.summarize_window_sweep:
         print(summarize_window_sweep(*args.summarize_window_sweep))
