@@ -29,7 +29,14 @@
  *    row-major and 16-byte aligned.  The caller owns every buffer.
  *  - The library allocates no device memory.  Each call is enqueued on the
  *    caller's `stream` and returns without synchronising; results are ready
- *    when the stream reaches that point.
+ *    when the stream reaches that point.  Every compute call therefore takes
+ *    the plan's device workspace (workspace, workspace_bytes: at least what
+ *    msa_plan returned) for its scratch: CSR lists, partial outputs, the
+ *    plan's metadata.
+ *  - max_score (stage 1's output, stage 2's input) is [P, nb_max, row_count]
+ *    with rows fastest, not [rows, P, nb_max]: the proxy kernel writes 64
+ *    consecutive rows per wave per block and the top-k kernel reads 64
+ *    consecutive rows per load, both as whole 256-byte lines.
  *  - Rows: the query rows of all sequences are concatenated, T = sum(qo_len).
  *    Row i of sequence s sits at KV position kv_len[s] - qo_len[s] + i
  *    (causal, bottom-right aligned).  Key j is visible to it iff j <= that
