@@ -83,6 +83,18 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 #endif
 }
 
+// max(a, |b|, |c|) as one v_max3_f32 with absolute-value source modifiers
+// (through max3f the compiler clears each sign bit with a v_and first).
+__device__ __forceinline__ float absmax3f(float a, float b, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+#else
+  return fmaxf(a, fmaxf(fabsf(b), fabsf(c)));
+#endif
+}
+
 // Read 16 bytes from LDS.
 template <typename T>
 __device__ __forceinline__ T lds_load16(const void* p) {

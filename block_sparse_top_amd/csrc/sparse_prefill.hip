@@ -300,7 +300,7 @@ __device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) amax = max3f(amax, __builtin_fabsf(oacc[dt][i]), __builtin_fabsf(oacc[dt][i + 1]));
+    for (int i = 0; i < 16; i += 2) amax = absmax3f(amax, oacc[dt][i], oacc[dt][i + 1]);
   amax = fmaxf(amax, wave_xor32(amax));
   // E = e - 126 for the biased exponent e of max|O|; rows below 2^-118 keep zeros
   const uint32_t e = __float_as_uint(amax * mul) >> 23;
@@ -357,6 +357,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];
   __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
   __shared__ int32_t ent_s[kMaxItemEntries];
+  __shared__ int32_t rk_s[kMaxItemEntries];  // entry row * k + slot (< T * 64 < 2^31): record index / Hq
   int item = blockIdx.x;
   if (a.xcd_pin) {
     // workgroups are dealt to the 8 XCDs round-robin: XCD x = blockIdx % 8
@@ -405,7 +406,11 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       kr[i] = load_kv8<F>(kb, c >> 4, c & 15);
       vr[i] = load_kv8<F>(vb, c >> 4, c & 15);
     }
-    for (int i = tid; i < n_ent; i += 256) ent_s[i] = a.entries[e0 + i];
+    for (int i = tid; i < n_ent; i += 256) {
+      const int32_t ent = a.entries[e0 + i];
+      ent_s[i] = ent;
+      rk_s[i] = (ent >> 6) * a.k + (ent & 63);
+    }
     const int kv_in_block = a.m.kv[s] - b * 128;  // V rows at or past this are page padding
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -545,11 +550,13 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     auto rec_index = [&](int wrow) -> int64_t {
       const int srow = 32 * wave + wrow;
       const int se = chunk * MT + srow / G;
-      if (se >= n_ent) return trash;
-      const int sent = ent_s[se];
-      return ((int64_t)(sent >> 6) * a.k + (sent & 63)) * a.Hq + g * G + (srow & (G - 1));
+      const int64_t rec = (int64_t)(uint32_t)rk_s[min(se, n_ent - 1)] * (uint32_t)a.Hq +
+                          (uint32_t)(g * G + (srow & (G - 1)));
+      return se < n_ent ? rec : trash;
     };
-    const float step = store_rows_bfp10(oacc, v_scale / sum, ow, a.part_hi, a.part_lo, rec_index, lane);
+    // sum >= 1 (the row max contributes exp2(0)): the hardware reciprocal's
+    // 1-ulp error is far below the encoding's step
+    const float step = store_rows_bfp10(oacc, v_scale * __builtin_amdgcn_rcpf(sum), ow, a.part_hi, a.part_lo, rec_index, lane);
     {  // both halves hold the row's max, sum and step and store the same value
       const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : trash;
       a.part_st[pi] = float2{(mx + fast_log2(sum)) * kLn2, step};  // mx is already scaled
