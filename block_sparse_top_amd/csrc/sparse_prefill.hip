@@ -159,9 +159,9 @@ struct PartialArgs {
   const int32_t* gitems;  // first item of each KV group, [Hkv + 1]
   int32_t xcd_pin;        // 1: workgroup i runs an item of the groups assigned to XCD i % 8
   DevMeta m;
-  uint8_t* part_hi;      // partial records, block floating point (see store_rows_bfp10):
-  uint8_t* part_lo;      //   planes of 128 and 32 bytes per record [rows, k, Hq], then one trash record
-  float2* part_st;       //   {log-sum-exp, step} [rows, Hq, k], then one trash entry
+  uint8_t* part_pk;      // partial records, block floating point (see store_rows_bfp10): five
+  int64_t plane_stride;  //   planes of 32 bytes per record [rows, k, Hq] + trash records, this far apart
+  float2* part_st;       //   {log-sum-exp, step} [rows, Hq, k], then the trash entries
   int64_t trash;         // index of the first of kTrashRecords trash records (rows * Hq * k)
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2;      // sm_scale * log2(e)
@@ -278,23 +278,22 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16 (&oacc)[4], float m
 // bf16 value carries up to 2^-8 of its own magnitude).  A record is 160 bytes
 // against 256 in bf16: the partials are written once and read once, so this
 // is 35% of the traffic of the partial attention's stores and of the merge.
-//  * byte plane (128 bytes): n >> 2 as an int8; dim d = 32 dt + 8 gq + 4 h + t
-//    at byte 64 h + 16 dt + 4 gq + t (h: the MFMA lane half holding d);
-//  * 2-bit plane (32 bytes): n & 3 of dim d at bits 2t of byte 16 h + 4 dt + gq;
-//  * step, beside the log-sum-exp (float2).
-// Planes are indexed by record (row * k + slot) * Hq + head, so the G heads of
-// one (row, slot) entry are adjacent: the 2-bit planes of an entry's G >= 4
-// heads fill whole 128-byte lines.
+// The lane holding dims d = 32 dt + 8 gq + 4 h + t (h: its MFMA lane half)
+// for gq, t = 0..3 packs their 16 values, j = 4 gq + t, into one 160-bit
+// group (field j at bits 10 j .. 10 j + 9, two's complement), five words;
+// word w of group c = 4 h + dt is dword c of the record's 32 bytes in plane
+// w.  Planes are indexed by record (row * k + slot) * Hq + head, so the G
+// heads of one (row, slot) entry are adjacent: for G >= 4 every store
+// instruction of a plane writes whole 128-byte lines.  The step sits beside
+// the log-sum-exp (float2).
 constexpr float kBfpMagic = 12582912.0f;  // 1.5 * 2^23: x + magic keeps round(x) in the low mantissa bits
 
 // Encodes the wave's 32 rows (the O^T tiles of store_rows_bf16, scaled by
-// `mul`) and stores the planes: byte planes through the wave's 2 KB staging
-// area in whole 128-byte lines (16 rows at a time, chunk c of staged row r at
-// c ^ ((r >> 1) & 7)), 2-bit planes straight from the lanes.  Returns the
-// lane's row's step.
+// `mul`) and stores the five plane words of each lane's group straight from
+// the lanes (16 bytes per lane and plane).  Returns the lane's row's step.
 template <typename RecIndex>
-__device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float mul, uint8_t* ow, uint8_t* hi_plane,
-                                                  uint8_t* lo_plane, RecIndex rec, int lane) {
+__device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float mul, uint8_t* planes,
+                                                  int64_t plane_stride, RecIndex rec, int lane) {
   const int jrow = lane & 31, half = lane >> 5;
   float amax = 0.f;
 #pragma unroll
@@ -307,47 +306,28 @@ __device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float
   const bool live = e >= 9;
   const float f = live ? mul * __uint_as_float((262u - e) << 23) * (1023.f / 1024.f) : 0.f;   // 1 / step
   const float step = live ? __uint_as_float((e - 8u) << 23) * (1024.f / 1023.f) : 0.f;      // 2^(E - 9) * 1024 / 1023
-  uint32_t hw[4][4], lw[4];
+  uint32_t wd[5][4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    lw[dt] = 0u;
+    uint32_t n[16];  // low 10 bits: n in two's complement
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      hw[dt][gq] = 0u;
+    for (int j = 0; j < 16; ++j) n[j] = __float_as_uint(__builtin_fmaf(oacc[dt][j], f, kBfpMagic));
+    // word w = group bits 32 w .. 32 w + 31: fields 3 w (from its bit 2 w) to
+    // 3 w + 3 (up to its bit 9 - 2 w); each alignbit shifts the word being
+    // built down and brings the next field in at the top
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // low 10 bits: n in two's complement
-        const uint32_t u = __float_as_uint(__builtin_fmaf(oacc[dt][4 * gq + t], f, kBfpMagic));
-        hw[dt][gq] = __builtin_amdgcn_alignbit(u >> 2, hw[dt][gq], 8);  // bytes fill from the top
-        lw[dt] = __builtin_amdgcn_alignbit(u, lw[dt], 2);
-      }
+    for (int w = 0; w < 5; ++w) {
+      const uint32_t x0 = n[3 * w] << 22;
+      const uint32_t x1 = __builtin_amdgcn_alignbit(n[3 * w + 1], x0, 10);
+      const uint32_t x2 = __builtin_amdgcn_alignbit(n[3 * w + 2], x1, 10);
+      wd[w][dt] = __builtin_amdgcn_alignbit(n[3 * w + 3], x2, 2 + 2 * w);
     }
   }
-  int64_t rr[4];  // staged rows 16 R + 8 i + lane / 8: rr[2 R + i]
+  uint8_t* dst = planes + rec(jrow) * 32 + 16 * half;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) rr[x] = rec(8 * x + (lane >> 3));
-  const int lr = jrow & 15;
-#pragma unroll
-  for (int R = 0; R < 2; ++R) {
-    if ((jrow >> 4) == R) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int c = 4 * half + dt;
-        lds_store16<i32x4>(&ow[lr * 128 + ((c ^ ((lr >> 1) & 7)) << 4)],
-                           i32x4{(int)hw[dt][0], (int)hw[dt][1], (int)hw[dt][2], (int)hw[dt][3]});
-      }
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * i + (lane >> 3), c = lane & 7;
-      const i32x4 v = lds_load16<i32x4>(&ow[r * 128 + ((c ^ ((r >> 1) & 7)) << 4)]);
-      __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(hi_plane + rr[2 * R + i] * 128 + 16 * c));
-    }
-    wave_lds_sync();
-  }
-  __builtin_nontemporal_store(i32x4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]},
-                              reinterpret_cast<i32x4*>(lo_plane + rec(jrow) * 32 + 16 * half));
+  for (int w = 0; w < 5; ++w)
+    __builtin_nontemporal_store(i32x4{(int)wd[w][0], (int)wd[w][1], (int)wd[w][2], (int)wd[w][3]},
+                                reinterpret_cast<i32x4*>(dst + w * plane_stride));
   return step;
 }
 
@@ -355,7 +335,6 @@ template <KvFmt F>
 __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
   __shared__ int32_t ent_s[kMaxItemEntries];
   __shared__ int32_t rk_s[kMaxItemEntries];  // entry row * k + slot (< T * 64 < 2^31): record index / Hq
   int item = blockIdx.x;
@@ -444,7 +423,6 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   for (int dt = 0; dt < 4; ++dt)
     vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
                 ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
-  uint8_t* ow = ost + wave * kOStage;
 
   // Q fragments (B operand) of a chunk's row for this lane: gathered rows
   auto load_q = [&](bf16x8 (&qf)[8], int chunk) {
@@ -556,7 +534,8 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     };
     // sum >= 1 (the row max contributes exp2(0)): the hardware reciprocal's
     // 1-ulp error is far below the encoding's step
-    const float step = store_rows_bfp10(oacc, v_scale * __builtin_amdgcn_rcpf(sum), ow, a.part_hi, a.part_lo, rec_index, lane);
+    const float step = store_rows_bfp10(oacc, v_scale * __builtin_amdgcn_rcpf(sum), a.part_pk, a.plane_stride,
+                                       rec_index, lane);
     {  // both halves hold the row's max, sum and step and store the same value
       const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : trash;
       a.part_st[pi] = float2{(mx + fast_log2(sum)) * kLn2, step};  // mx is already scaled
@@ -587,37 +566,41 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
 struct MergeArgs {
   const int32_t* sel;
   DevMeta m;
-  const uint8_t* part_hi;
-  const uint8_t* part_lo;
+  const uint8_t* part_pk;
+  int64_t plane_stride;
   const float2* part_st;
   uint16_t* out;   // bf16 [T, Hq, 128]
   float* lse;      // [T, Hq] or null
   int32_t Hq, Hkv, G, k, w0, w1;
 };
 
-// 8 lanes per (row, head): lane l takes a record's byte-plane run 16 l .. +15
-// and its 2-bit-plane bytes 4 l .. +3 (store_rows_bfp10): dims 32 dt + 8 gq +
-// 4 h + t for h = l / 4, dt = l % 4 and gq, t = 0..3.  Slots go 8 at a time,
-// the first 8 slots' records issued before anything else; lane l of the 8
-// reads slot l's block id and {log-sum-exp, step} (coalesced), the row's local
-// block then says which slots count, and the group's max and weights move by
-// shuffles.  Decoding: the signed byte converts to float in one instruction
-// (a byte-select conversion); the four 2-bit fields of a byte are spread to
-// the four bytes of a word (byte t keeps field t at bit 2 t, so it reads as
-// 4^t f_t) and 4^t n_t = 4^(t+1) * byte + that is exact, its 4^-t going into
-// the slot weight.  topk <= 64.
+// 8 lanes per (row, head): lane l takes dword l of each of a record's five
+// planes, group l of store_rows_bfp10: dims 32 dt + 8 gq + 4 h + t for
+// h = l / 4, dt = l % 4 and gq, t = 0..3.  Slots go 8 at a time, the first 8
+// slots' records issued before anything else; lane l of the 8 reads slot l's
+// block id and {log-sum-exp, step} (coalesced), the row's local block then
+// says which slots count, and the group's max and weights move by shuffles.
+// Decoding: a field inside one word is a signed bit-field extract, the four
+// that straddle two words first join them with one alignbit.  topk <= 64.
 constexpr int kMergeLanes = 8;
 
 struct BfpRec {
-  i32x4 h;     // byte plane, 16 bytes
-  uint32_t l;  // 2-bit plane, 4 bytes
+  uint32_t w[5];
 };
 
-__device__ __forceinline__ BfpRec load_bfp_rec(const uint8_t* hi_plane, const uint8_t* lo_plane, int64_t rec, int l) {
+__device__ __forceinline__ BfpRec load_bfp_rec(const uint8_t* planes, int64_t plane_stride, int64_t rec, int l) {
   BfpRec r;
-  r.h = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(hi_plane + rec * 128 + 16 * l));
-  r.l = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(lo_plane + rec * 32 + 4 * l));
+  const uint8_t* src = planes + rec * 32 + 4 * l;
+#pragma unroll
+  for (int w = 0; w < 5; ++w) r.w[w] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src + w * plane_stride));
   return r;
+}
+
+// field j (0..15) of a group: n, from its bits 10 j .. 10 j + 9
+__device__ __forceinline__ float bfp_field(const BfpRec& r, int j) {
+  const int bit = 10 * j, q = bit >> 5, o = bit & 31;
+  if (o <= 22) return (float)((int)(r.w[q] << (22 - o)) >> 22);
+  return (float)((int)(__builtin_amdgcn_alignbit(r.w[q + 1], r.w[q], o) << 22) >> 22);
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
@@ -635,7 +618,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   // the first 8 slots' records depend on nothing else
   BfpRec v[NL];
 #pragma unroll
-  for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_hi, a.part_lo, rec_of(min(j, a.k - 1)), l);
+  for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_pk, a.plane_stride, rec_of(min(j, a.k - 1)), l);
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   const int ngroups = (a.k + NL - 1) / NL;
   // lane l's slot of each group of 8: block id, log-sum-exp and step, loaded
@@ -680,25 +663,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const float wsl = wl * stl;  // weight x step
     if (gi > 0) {
 #pragma unroll
-      for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_hi, a.part_lo, rec_of(min(NL * gi + j, a.k - 1)), l);
+      for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_pk, a.plane_stride, rec_of(min(NL * gi + j, a.k - 1)), l);
     }
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       const float ws = __shfl(wsl, j, NL);
       if (ws == 0.f) continue;  // invalid slots: never written, never read into the result
-      const float wt[4] = {ws, ws * 0.25f, ws * 0.0625f, ws * 0.015625f};
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const uint32_t hw = (uint32_t)v[j].h[gq];
-        const uint32_t spread = __builtin_amdgcn_perm(v[j].l, v[j].l, 0x01010101u * gq) & 0xC0300C03u;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float hi = (float)(int)(int8_t)(hw >> (8 * t));
-          const float lo = (float)((spread >> (8 * t)) & 0xffu);  // 4^t f_t
-          const float n4 = __builtin_fmaf((float)(4 << (2 * t)), hi, lo);  // 4^t n_t
-          o[4 * gq + t] = __builtin_fmaf(wt[t], n4, o[4 * gq + t]);
-        }
-      }
+      for (int x = 0; x < 16; ++x) o[x] = __builtin_fmaf(ws, bfp_field(v[j], x), o[x]);
     }
   }
   float L = Ll;
@@ -858,9 +830,9 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   // bf16 dq partials (256 bytes per record; the forward needs 168)
   a.trash = p->attn_window * Hq * k;
   const int64_t nrec = a.trash + kTrashRecords;
-  a.part_hi = reinterpret_cast<uint8_t*>(ws + L.part_o);
-  a.part_lo = a.part_hi + nrec * 128;
-  a.part_st = reinterpret_cast<float2*>(a.part_lo + nrec * 32);
+  a.part_pk = reinterpret_cast<uint8_t*>(ws + L.part_o);
+  a.plane_stride = nrec * 32;
+  a.part_st = reinterpret_cast<float2*>(a.part_pk + 5 * a.plane_stride);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = p->G;
@@ -888,8 +860,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   MergeArgs mg;
   mg.sel = sel;
   mg.m = m;
-  mg.part_hi = a.part_hi;
-  mg.part_lo = a.part_lo;
+  mg.part_pk = a.part_pk;
+  mg.plane_stride = a.plane_stride;
   mg.part_st = a.part_st;
   mg.out = static_cast<uint16_t*>(out);
   mg.lse = lse;
