@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void dense_fwd_kernel(DenseFwdArgs a) {
     for (int kt_ = 0; kt_ < 4; ++kt_)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) bm = max3f(bm, acc[kt_][i], acc[kt_][i + 1]);
-    bm = fmaxf(bm, wave_xor32(bm));
+    bm = wave_max32(bm);
     const float mnew = fmaxf(mrun, bm);   // finite: key 0 is visible to every row
     if (mnew > mrun) {
       const float alpha = fast_exp2(mrun - mnew);
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void dense_fwd_kernel(DenseFwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  const float lt = lrun + wave_xor32(lrun);
+  const float lt = wave_sum32(lrun);
   if (!d.live) return;
   if (half == 0) a.lse[(int64_t)d.r * a.Hq + d.h] = (mrun + fast_log2(lt)) * kLn2d;
   const float inv_l = 1.f / lt;

@@ -68,8 +68,6 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32); }
-
 // max(a, b, c) as one v_max3_f32.  Written as an instruction because the
 // compiler otherwise quiets every operand it cannot prove canonical (one
 // extra v_max per matrix-core result); the operands here are finite or -inf.
@@ -93,6 +91,24 @@ __device__ __forceinline__ float absmax3f(float a, float b, float c) {
 #else
   return fmaxf(a, fmaxf(fabsf(b), fabsf(c)));
 #endif
+}
+
+// The values of v in lanes lane % 32 (.x) and 32 + lane % 32 (.y): the two
+// half-waves swapped in registers by v_permlane32_swap, with no LDS round
+// trip (a shuffle through ds_bpermute sits on the critical path of every
+// cross-half reduction).
+__device__ __forceinline__ f32x2 wave_halves32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// max(v, v of lane ^ 32) and v + v of lane ^ 32, the same in both lanes
+__device__ __forceinline__ float wave_max32(float v) {
+  const f32x2 h = wave_halves32(v);
+  return max3f(h[0], h[1], h[1]);
+}
+__device__ __forceinline__ float wave_sum32(float v) {
+  const f32x2 h = wave_halves32(v);
+  return h[0] + h[1];
 }
 
 // Read 16 bytes from LDS.

@@ -164,7 +164,7 @@ __device__ __forceinline__ float exact_block_dotmax(const ExactQ& q, const uint8
     }
     // the four dim blocks of a key sit in lanes kk, kk + 16, kk + 32, kk + 48
     acc += __shfl_xor(acc, 16);
-    acc += __shfl_xor(acc, 32);
+    acc = wave_sum32(acc);
     best = key < nkeys ? fmaxf(best, acc) : best;
   }
   // max over the 16 key lanes of a row

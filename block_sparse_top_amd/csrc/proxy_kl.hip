@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void kl_dense_dq_kernel(KlDqArgs a) {
     for (int kt_ = 0; kt_ < 4; ++kt_)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) bm = max3f(bm, acc[kt_][i], acc[kt_][i + 1]);
-    bm = fmaxf(bm, wave_xor32(bm));
+    bm = wave_max32(bm);
     const float mnew = fmaxf(mrun, bm);   // finite: key 0 of block 0 is visible to every row
     if (mnew > mrun) {
       const float alpha = fast_exp2(mrun - mnew);
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void kl_dense_dq_kernel(KlDqArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  const float lt = lrun + wave_xor32(lrun);
+  const float lt = wave_sum32(lrun);
   if (live && half == 0) a.plse[(int64_t)r * a.P + p] = (mrun + fast_log2(lt)) * kLn2;
   const float inv_l = 1.f / lt;
 #pragma unroll

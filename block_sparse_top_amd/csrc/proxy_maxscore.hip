@@ -334,7 +334,7 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
           for (int w = 0; w < (int)(sizeof(BFrag) / 4); ++w) m = fmaxf(m, e4m3_absmax4((uint32_t)qf[sub][st][w]));
         pm[sub] = m;
       }
-      pm[sub] = fmaxf(pm[sub], wave_xor32(pm[sub]));
+      pm[sub] = wave_max32(pm[sub]);
     }
     qinf = lane < 32 ? pm[0] : pm[1];
   }
@@ -431,8 +431,8 @@ __global__ __launch_bounds__(64 * kProxyWaves, 2) void proxy_maxscore_kernel(Pro
     }
   };
   auto finish = [&](int b, float (&m)[2]) {
-    m[0] = fmaxf(m[0], wave_xor32(m[0]));
-    m[1] = fmaxf(m[1], wave_xor32(m[1]));
+    m[0] = wave_max32(m[0]);
+    m[1] = wave_max32(m[1]);
     const float v = (lane < 32 ? m[0] : m[1]) * scale;
     if constexpr (TOPK) {
       // blocks before the local one compete (the local block is forced);
@@ -798,7 +798,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_kernel(ProxyRowAr
         m = max3f(m, (8 * (r >> 2) + (r & 3)) <= lim ? acc[r] : kNegInf,
                   (8 * (r >> 2) + (r & 3) + 1) <= lim ? acc[r + 1] : kNegInf);
     }
-    m = fmaxf(m, wave_xor32(m));
+    m = wave_max32(m);
     if (lane < ncols) a.out[head * a.o_h + b * a.o_b + rl * a.o_r] = m * scale;
   };
   for (; b + kRowWaves < b1; b += 2 * kRowWaves) {
@@ -882,7 +882,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void proxy_onerow_mxfp4_kernel(Prox
         m = max3f(m, (8 * (r >> 2) + (r & 3)) <= lim ? acc[r] : kNegInf,
                   (8 * (r >> 2) + (r & 3) + 1) <= lim ? acc[r + 1] : kNegInf);
     }
-    m = fmaxf(m, wave_xor32(m));
+    m = wave_max32(m);
     if (lane < ncols) a.out[head * a.o_h + b * a.o_b + rl * a.o_r] = m * scale;
     if (a.kmx) {
       // the block's largest scale code (bounds its |k|); every key of the

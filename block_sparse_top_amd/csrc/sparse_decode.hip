@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
       }
     }
     cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    cm = wave_max32(cm);
     const float m_new = fmaxf(m_run, cm);
     // a wave whose keys so far are all masked keeps m = -inf; use 0 as the
     // reference then so that no (-inf) - (-inf) appears
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
 
   // waves -> LDS: running max, lane-group sums, O^T (lane holds d = 16dt + 4q16 + e of head m16)
   l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = wave_sum32(l_run);
   __syncthreads();  // every wave is done with its V tiles; reuse smem
   float* red = reinterpret_cast<float*>(smem);  // [wave][head][131]: o[128], m, l
   float* mine = red + (wave * 16 + m16) * 131;

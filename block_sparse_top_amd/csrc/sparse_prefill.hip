@@ -300,7 +300,7 @@ __device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; i += 2) amax = absmax3f(amax, oacc[dt][i], oacc[dt][i + 1]);
-  amax = fmaxf(amax, wave_xor32(amax));
+  amax = wave_max32(amax);
   // E = e - 126 for the biased exponent e of max|O|; rows below 2^-118 keep zeros
   const uint32_t e = __float_as_uint(amax * mul) >> 23;
   const bool live = e >= 9;
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mraw = max3f(mraw, acc[kt][i], acc[kt][i + 1]);
-    mraw = fmaxf(mraw, wave_xor32(mraw));
+    mraw = wave_max32(mraw);
     const float mx = mraw * scale_log2;  // scaled row max (log2 domain)
     float sum = 0.f;
     bf16x8 pf[4][2];
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of transposed reads
     }
-    sum += wave_xor32(sum);
+    sum = wave_sum32(sum);
 
     // Output: the normalised partials in block floating point, non-temporal
     // (the merge reads each of them once).  Padding rows write to one of
