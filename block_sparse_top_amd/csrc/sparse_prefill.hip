@@ -1275,21 +1275,45 @@ struct BwdKvArgs {
 };
 
 
+// Workgroup shape.  Without the proxy term: two groups of four waves take
+// alternate chunks of the block's rows (each wave of a group owns 32 keys)
+// and sum their dK / dV partials through LDS at the end; two waves per SIMD,
+// at most 256 registers each, so the products accumulate in ordinary
+// registers that the vector unit reads directly.  With it (a third set of
+// 32x128 accumulators): one group, one wave per SIMD.
+template <bool KL>
+constexpr int bwd_dkv_groups() { return KL ? 1 : 2; }
+template <bool KL>
+constexpr int bwd_dkv_threads() { return 256 * bwd_dkv_groups<KL>(); }
+
 // DENSE: every row of the window that sees the block (the warm-up mode's
 // dense main attention), in row order, instead of the bin's CSR entries.
 template <bool KL, bool DENSE = false>
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t qt[2][32 * 256];    // a chunk's 32 q rows, rt_swz, two buffers
-  __shared__ __attribute__((aligned(16))) uint8_t dtile[2][32 * 256]; // a chunk's 32 dO rows, rt_swz
-  // the chunk's proxy q rows (row i: token i / G), rt_swz
-  __shared__ __attribute__((aligned(16))) uint8_t ptile[KL ? 2 : 1][KL ? 32 * 256 : 16];
-  __shared__ __attribute__((aligned(16))) float l2_s[2][32];
-  __shared__ __attribute__((aligned(16))) float d_s[2][32];
-  __shared__ __attribute__((aligned(16))) int32_t pos_s[2][32];
+__global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArgs a) {
+  constexpr int kGroups = bwd_dkv_groups<KL>();
+  constexpr int kTile = 32 * 256;  // a chunk's 32 rows of 128 bf16
+  // K and V of the block (rt_swz; rows past kv_len zeroed), the B operands of
+  // every chunk's S and dP products (with the proxy term, one wave per SIMD
+  // has the registers to hold its keys' K and V rows instead).  Then per
+  // group and buffer: the chunk's q rows, dO rows and (KL) proxy q rows (row
+  // i: token i / G), rt_swz.  The first 128 KB hold the second group's
+  // partials for the final sum.
+  constexpr int kKvBytes = KL ? 0 : 2 * 128 * 256;
+  constexpr int kGroupBytes = 2 * (KL ? 3 : 2) * kTile;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kKvBytes + kGroups * kGroupBytes];
+  __shared__ __attribute__((aligned(16))) float l2_s[kGroups][2][32];
+  __shared__ __attribute__((aligned(16))) float d_s[kGroups][2][32];
+  __shared__ __attribute__((aligned(16))) int32_t pos_s[kGroups][2][32];
+  static_assert(KL || kKvBytes + kGroups * kGroupBytes >= 4 * 8 * 16 * 64 * 4, "partials fit the tiles' space");
+  uint8_t* const kv_k = smem;
+  uint8_t* const kv_v = smem + (KL ? 0 : 128 * 256);
   // block-major order: the early, most selected blocks of every group start first
   const int gb = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
   const int key = g * a.NB + gb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int grp = kGroups == 1 ? 0 : tid >> 8;   // chunk group
+  const int gtid = tid & 255, wave = gtid >> 6;  // wave within the group: keys 32 wave ..
+  uint8_t* const gsm = smem + kKvBytes + grp * kGroupBytes;
   const int s = upper_bound_i32(a.m.page_start, a.m.S + 1, gb) - 1;
   const int b = gb - a.m.page_start[s];
   const int32_t page = a.kv_indices[gb];
@@ -1308,23 +1332,41 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
   const int G = a.G;
   const int MT = 32 / G;                       // tokens per 32-row chunk
   const int half = lane >> 5, j = lane & 31;
-  // This wave's 32 keys never change: their K and V rows are the B operands
-  // of every chunk's S and dP products, held in registers (lane (j, half),
-  // step st: key 32 wave + j, dims 16 st + 8 half ..); rows past kv_len zeroed.
-  bf16x8 bk[8], bv[8];
-  {
+  bf16x8 bk_r[KL ? 8 : 1], bv_r[KL ? 8 : 1];
+  if constexpr (KL) {
+    // lane (j, half), step st: key 32 wave + j, dims 16 st + 8 half ..
     const int krow = 32 * wave + j;
     const bool live_row = krow < a.m.kv[s] - b * 128;
     const int64_t off = ((int64_t)page * a.Hkv + g) * 32768 + krow * 256 + half * 16;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      bk[st] = live_row ? *reinterpret_cast<const bf16x8*>(a.kp + off + st * 32) : bf16x8{};
-      bv[st] = live_row ? *reinterpret_cast<const bf16x8*>(a.vp + off + st * 32) : bf16x8{};
+      bk_r[st] = live_row ? *reinterpret_cast<const bf16x8*>(a.kp + off + st * 32) : bf16x8{};
+      bv_r[st] = live_row ? *reinterpret_cast<const bf16x8*>(a.vp + off + st * 32) : bf16x8{};
+    }
+  } else {  // K and V -> LDS (16-byte pieces; rows past kv_len zeroed)
+    const int kv_rows = a.m.kv[s] - b * 128;
+    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * 32768;
+    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * 32768;
+    constexpr int kRounds = 2048 / bwd_dkv_threads<KL>();
+    i32x4 kr[kRounds], vr[kRounds];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int c = tid + bwd_dkv_threads<KL>() * i;
+      kr[i] = *reinterpret_cast<const i32x4*>(kb + c * 16);
+      vr[i] = *reinterpret_cast<const i32x4*>(vb + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int c = tid + bwd_dkv_threads<KL>() * i;
+      const bool live_row = (c >> 4) < kv_rows;
+      lds_store16<i32x4>(&kv_k[rt_swz(c >> 4, c & 15)], live_row ? kr[i] : i32x4{});
+      lds_store16<i32x4>(&kv_v[rt_swz(c >> 4, c & 15)], live_row ? vr[i] : i32x4{});
     }
   }
   const int q16 = lane >> 4, m16 = lane & 15;
   const int nchunks = (n_ent + MT - 1) / MT;
   const int keypos = b * 128 + 32 * wave + j;  // this lane's key position
+  const int krow = 32 * wave + j;              // its K / V row
   // transposed reads: lane (q16, m16) fetches dims 32 dt + 16 (q16 & 1) +
   // 4 (m16 & 3) .. +3 of tile row r0 (lo) or r0 + 8 (hi), r0 = 4 (q16 >> 1) +
   // m16 / 4 (+ 16 u)
@@ -1343,107 +1385,163 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
   f32x16 pkacc[KL ? 4 : 1];
 #pragma unroll
   for (int dt = 0; dt < (KL ? 4 : 1); ++dt) pkacc[dt] = f32x16{};
-  // Gather slots of this thread: rows ri0 and ri0 + 16 of a chunk (row i =
-  // token i / G, head i % G), 16-byte column cc; threads below 32 also fetch
-  // row tid's lse, D and position.  Rows of chunk c + 1 are loaded into
-  // registers while chunk c computes; their entry ids one chunk earlier.
-  const int ri0 = tid >> 4, cc = tid & 15;
-  const int ri1 = ri0 + 16;
-  // entries and lse stay raw in registers until used, so that no wait for a
-  // just-issued load lands before the barrier
+  // Gathered rows (row i of a chunk: token i / G, head i % G).  Two waves
+  // per SIMD (no proxy term): straight from global memory to LDS
+  // (global_load_lds_dwordx4), so that no register holds them: instruction
+  // i of wave w of a group fills bytes 1024 (2 w + i) .. +1023 of the chunk's
+  // tile, lane l its 16-byte slot, i.e. row ri_i = 8 w + 4 i + l / 16 at
+  // physical chunk l % 16, so the lane fetches that row's logical chunk
+  // (rt_swz); the next chunk is issued once every wave is past the barrier
+  // that retires the buffer it overwrites.  One wave per SIMD (proxy term):
+  // through registers, the next chunk's loads issued before the barrier (a
+  // wave alone on its SIMD has nothing else to hide them behind), stored to
+  // LDS at the start of the next chunk.  Threads below 32 of the group also
+  // fetch row gtid's lse, D and position into registers; entry ids one chunk
+  // earlier.  Past the last chunk a group runs a chunk whose rows are all
+  // padding (position -1: no key visible).
+  const int ri0 = 8 * wave + (lane >> 4), ri1 = ri0 + 4;
+  const int lc0 = (lane & 15) ^ rt_swz_key(ri0), lc1 = (lane & 15) ^ rt_swz_key(ri1);
+  const int niter = (nchunks + kGroups - 1) / kGroups;
+  auto chunk_of = [&](int it) { return it * kGroups + grp; };
+  // entries and lse stay raw in registers until used
   auto entry_of = [&](int chunk, int ri) {
     const int e = min(chunk * MT + ri / G, n_ent - 1);
     if constexpr (DENSE) return (dense_lo + e) << 6;
     else return a.entries[e0 + e];
   };
-  auto row_ptr = [&](const uint8_t* base, int32_t ent, int ri) {
-    return reinterpret_cast<const i32x4*>(base + ((int64_t)(a.w0 + (ent >> 6)) * a.Hq + g * G + ri % G) * 256 +
-                                          cc * 16);
+  auto row_src = [&](const uint8_t* base, int32_t ent, int ri, int lc) {
+    return base + ((int64_t)(a.w0 + (ent >> 6)) * a.Hq + g * G + ri % G) * 256 + lc * 16;
   };
-  auto prow_ptr = [&](int32_t ent) {
-    return reinterpret_cast<const i32x4*>(a.pq + ((int64_t)(a.w0 + (ent >> 6)) * a.Hkv + g) * 256 + cc * 16);
+  auto prow_src = [&](int32_t ent, int lc) {
+    return a.pq + ((int64_t)(a.w0 + (ent >> 6)) * a.Hkv + g) * 256 + lc * 16;
   };
-  if (nchunks > 0) {
-    int32_t ea = entry_of(0, ri0), eb = entry_of(0, ri1), es = tid < 32 ? entry_of(0, tid) : 0;
-    i32x4 rq0 = *row_ptr(a.q, ea, ri0), rq1 = *row_ptr(a.q, eb, ri1);
-    i32x4 rd0 = *row_ptr(a.dout, ea, ri0), rd1 = *row_ptr(a.dout, eb, ri1);
-    i32x4 rp0 = {}, rp1 = {};
+  // tiles of buffer `buf`: q, dO, (KL) proxy q
+  auto tile = [&](int kind, int buf) { return gsm + (2 * kind + buf) * kTile; };
+  auto issue_rows = [&](int32_t ea, int32_t eb, int buf) {
+    uint8_t* const w0b = tile(0, buf) + 2048 * wave;
+    uint8_t* const w1b = tile(1, buf) + 2048 * wave;
+    global_load_lds16(row_src(a.q, ea, ri0, lc0), (MSA_LDS void*)w0b);
+    global_load_lds16(row_src(a.q, eb, ri1, lc1), (MSA_LDS void*)(w0b + 1024));
+    global_load_lds16(row_src(a.dout, ea, ri0, lc0), (MSA_LDS void*)w1b);
+    global_load_lds16(row_src(a.dout, eb, ri1, lc1), (MSA_LDS void*)(w1b + 1024));
     if constexpr (KL) {
-      rp0 = *prow_ptr(ea);
-      rp1 = *prow_ptr(eb);
+      uint8_t* const w2b = tile(2, buf) + 2048 * wave;
+      global_load_lds16(prow_src(ea, lc0), (MSA_LDS void*)w2b);
+      global_load_lds16(prow_src(eb, lc1), (MSA_LDS void*)(w2b + 1024));
     }
+  };
+  i32x4 rr[KL ? 6 : 1];  // KL: the next chunk's q, dO and proxy q pieces of rows ri0, ri1
+  auto load_rows = [&](int32_t ea, int32_t eb) {
+    if constexpr (KL) {
+      rr[0] = *reinterpret_cast<const i32x4*>(row_src(a.q, ea, ri0, lane & 15));
+      rr[1] = *reinterpret_cast<const i32x4*>(row_src(a.q, eb, ri1, lane & 15));
+      rr[2] = *reinterpret_cast<const i32x4*>(row_src(a.dout, ea, ri0, lane & 15));
+      rr[3] = *reinterpret_cast<const i32x4*>(row_src(a.dout, eb, ri1, lane & 15));
+      rr[4] = *reinterpret_cast<const i32x4*>(prow_src(ea, lane & 15));
+      rr[5] = *reinterpret_cast<const i32x4*>(prow_src(eb, lane & 15));
+    }
+  };
+  auto store_rows = [&](int buf) {
+    if constexpr (KL) {
+#pragma unroll
+      for (int kind = 0; kind < 3; ++kind) {
+        lds_store16<i32x4>(tile(kind, buf) + rt_swz(ri0, lane & 15), rr[2 * kind]);
+        lds_store16<i32x4>(tile(kind, buf) + rt_swz(ri1, lane & 15), rr[2 * kind + 1]);
+      }
+    }
+  };
+  if (niter > 0) {
+    int32_t ea = entry_of(chunk_of(0), ri0), eb = entry_of(chunk_of(0), ri1);
+    int32_t es = gtid < 32 ? entry_of(chunk_of(0), gtid) : 0;
+    if constexpr (KL) load_rows(ea, eb);
+    else issue_rows(ea, eb, 0);
     float rlse = 0.f, rdd = 0.f;
     int32_t rpos = 0;
-    if (tid < 32) {
-      const int h = g * G + tid % G;
+    if (gtid < 32) {
+      const int h = g * G + gtid % G;
       rlse = a.lse[(int64_t)(a.w0 + (es >> 6)) * a.Hq + h];
       rdd = a.D[(int64_t)(es >> 6) * a.Hq + h];
-      rpos = tid / G < n_ent ? first_pos + (a.w0 + (es >> 6) - rs) : -1;   // padding rows see no key
+      rpos = chunk_of(0) * MT + gtid / G < n_ent ? first_pos + (a.w0 + (es >> 6) - rs) : -1;  // padding rows see no key
     }
-    ea = entry_of(1, ri0);
-    eb = entry_of(1, ri1);
-    es = tid < 32 ? entry_of(1, tid) : 0;
-    for (int chunk = 0; chunk < nchunks; ++chunk) {
-      const int buf = chunk & 1;
-      lds_store16<i32x4>(&qt[buf][rt_swz(ri0, cc)], rq0);
-      lds_store16<i32x4>(&qt[buf][rt_swz(ri1, cc)], rq1);
-      lds_store16<i32x4>(&dtile[buf][rt_swz(ri0, cc)], rd0);
-      lds_store16<i32x4>(&dtile[buf][rt_swz(ri1, cc)], rd1);
-      if constexpr (KL) {
-        lds_store16<i32x4>(&ptile[buf][rt_swz(ri0, cc)], rp0);
-        lds_store16<i32x4>(&ptile[buf][rt_swz(ri1, cc)], rp1);
+    ea = entry_of(chunk_of(1), ri0);
+    eb = entry_of(chunk_of(1), ri1);
+    es = gtid < 32 ? entry_of(chunk_of(1), gtid) : 0;
+    for (int it = 0; it < niter; ++it) {
+      const int buf = it & 1;
+      const uint8_t* const qb = tile(0, buf);
+      const uint8_t* const db = tile(1, buf);
+      const uint8_t* const pb = tile(2, buf);  // KL only
+      store_rows(buf);
+      if (gtid < 32) {
+        l2_s[grp][buf][gtid] = rlse * kLog2e;
+        d_s[grp][buf][gtid] = rdd;
+        pos_s[grp][buf][gtid] = rpos;
       }
-      if (tid < 32) {
-        l2_s[buf][tid] = rlse * kLog2e;
-        d_s[buf][tid] = rdd;
-        pos_s[buf][tid] = rpos;
-      }
-      // prefetch chunk + 1 (clamped past the end), then the entry ids of chunk + 2
-      rq0 = *row_ptr(a.q, ea, ri0);
-      rq1 = *row_ptr(a.q, eb, ri1);
-      rd0 = *row_ptr(a.dout, ea, ri0);
-      rd1 = *row_ptr(a.dout, eb, ri1);
-      if constexpr (KL) {
-        rp0 = *prow_ptr(ea);
-        rp1 = *prow_ptr(eb);
-      }
-      if (tid < 32) {
-        const int h = g * G + tid % G;
+      const int cn = chunk_of(it + 1);
+      if constexpr (KL) load_rows(ea, eb);
+      // this chunk's rows are in LDS (each wave waits for its own direct
+      // loads, the barrier for everyone's; K and V the first time); every
+      // wave is done with the previous chunk, whose buffer the next one fills
+      if constexpr (!KL) wait_vmem();
+      lds_barrier();
+      if constexpr (!KL) issue_rows(ea, eb, buf ^ 1);
+      if (gtid < 32) {
+        const int h = g * G + gtid % G;
         rlse = a.lse[(int64_t)(a.w0 + (es >> 6)) * a.Hq + h];
         rdd = a.D[(int64_t)(es >> 6) * a.Hq + h];
-        rpos = (chunk + 1) * MT + tid / G < n_ent ? first_pos + (a.w0 + (es >> 6) - rs) : -1;
+        rpos = cn * MT + gtid / G < n_ent ? first_pos + (a.w0 + (es >> 6) - rs) : -1;
       }
-      ea = entry_of(chunk + 2, ri0);
-      eb = entry_of(chunk + 2, ri1);
-      es = tid < 32 ? entry_of(chunk + 2, tid) : 0;
-      // the tiles of this chunk are in LDS; every wave is
-      // done with chunk - 1, whose buffer chunk + 1 will overwrite
-      lds_barrier();
-      const uint8_t* qb = qt[buf];
-      const uint8_t* db = dtile[buf];
-      // S = Q K^T and dP = dO V^T for this wave's 32 keys: C[row][key], key on lanes
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const bf16x8 aq = lds_load16<bf16x8>(&qb[rt_swz(j, 2 * st + half)]);
-        sacc = mfma32x32x16(aq, bk[st], sacc);
-        const bf16x8 ad = lds_load16<bf16x8>(&db[rt_swz(j, 2 * st + half)]);
-        pacc = mfma32x32x16(ad, bv[st], pacc);
-      }
-      // P and dS (register r holds row 8(r/4) + 4 half + r%4), as bf16 A operands;
-      // the rows' lse, D and positions come as four 4-row runs
+      ea = entry_of(chunk_of(it + 2), ri0);
+      eb = entry_of(chunk_of(it + 2), ri1);
+      es = gtid < 32 ? entry_of(chunk_of(it + 2), gtid) : 0;
+      // the rows' lse, D and positions as 4-row runs (register r of the
+      // products below holds row 8(r/4) + 4 half + r%4): with the proxy term
+      // (registers to spare, one wave per SIMD) read before the products,
+      // whose latency then covers theirs, else read where used
       f32x4 l2v[4], dv4[4];
       i32x4 ps4[4];
+      auto read_rows = [&](int t4) {
+        l2v[t4] = *reinterpret_cast<const f32x4*>(&l2_s[grp][buf][8 * t4 + 4 * half]);
+        dv4[t4] = *reinterpret_cast<const f32x4*>(&d_s[grp][buf][8 * t4 + 4 * half]);
+        ps4[t4] = *reinterpret_cast<const i32x4*>(&pos_s[grp][buf][8 * t4 + 4 * half]);
+      };
+      if constexpr (KL) {
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        l2v[t4] = *reinterpret_cast<const f32x4*>(&l2_s[buf][8 * t4 + 4 * half]);
-        dv4[t4] = *reinterpret_cast<const f32x4*>(&d_s[buf][8 * t4 + 4 * half]);
-        ps4[t4] = *reinterpret_cast<const i32x4*>(&pos_s[buf][8 * t4 + 4 * half]);
+        for (int t4 = 0; t4 < 4; ++t4) read_rows(t4);
       }
+      // S = Q K^T and dP = dO V^T for this wave's 32 keys: C[row][key], key on lanes
+      // fragments from LDS read one k-step ahead of their products
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      bf16x8 aq[2], ad[2], bkl[KL ? 1 : 2], bvl[KL ? 1 : 2];
+      auto frags = [&](int st, int x) {
+        aq[x] = lds_load16<bf16x8>(&qb[rt_swz(j, 2 * st + half)]);
+        ad[x] = lds_load16<bf16x8>(&db[rt_swz(j, 2 * st + half)]);
+        if constexpr (!KL) {
+          bkl[x] = lds_load16<bf16x8>(&kv_k[rt_swz(krow, 2 * st + half)]);
+          bvl[x] = lds_load16<bf16x8>(&kv_v[rt_swz(krow, 2 * st + half)]);
+        }
+      };
+      frags(0, 0);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (st + 1 < 8) frags(st + 1, (st + 1) & 1);
+        if constexpr (KL) {
+          sacc = mfma32x32x16(aq[st & 1], bk_r[st], sacc);
+          pacc = mfma32x32x16(ad[st & 1], bv_r[st], pacc);
+        } else {
+          sacc = mfma32x32x16(aq[st & 1], bkl[st & 1], sacc);
+          pacc = mfma32x32x16(ad[st & 1], bvl[st & 1], pacc);
+        }
+      }
+      // P and dS as bf16 A operands
       bf16x8 pf[2], sf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         i32x4 pw, sw;
+        if constexpr (!KL) {
+          read_rows(2 * u);
+          read_rows(2 * u + 1);
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           float pv[2], sv[2];
@@ -1475,13 +1573,37 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdKvArgs a) {
           const s16x4 qhi = lds_read_tr16(&qb[vhi[dt] + 256 * (16 * u)]);
           dkacc[dt] = mfma32x32x16(sf[u], join_tr16(qlo, qhi), dkacc[dt]);
           if constexpr (KL) {   // P^T times the rows' proxy q
-            const s16x4 plo = lds_read_tr16(&ptile[buf][vlo[dt] + 256 * (16 * u)]);
-            const s16x4 phi = lds_read_tr16(&ptile[buf][vhi[dt] + 256 * (16 * u)]);
+            const s16x4 plo = lds_read_tr16(&pb[vlo[dt] + 256 * (16 * u)]);
+            const s16x4 phi = lds_read_tr16(&pb[vhi[dt] + 256 * (16 * u)]);
             pkacc[dt] = mfma32x32x16(pf[u], join_tr16(plo, phi), pkacc[dt]);
           }
         }
       }
     }
+  }
+  if constexpr (kGroups == 2) {
+    // the second group's partials -> LDS (over the tiles), added by the first
+    // group in a fixed order: [wave][tile: dK 0-3, dV 0-3][register][lane]
+    float* const red = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every wave is done with the tiles
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          red[((wave * 8 + dt) * 16 + r) * 64 + lane] = dkacc[dt][r];
+          red[((wave * 8 + 4 + dt) * 16 + r) * 64 + lane] = dvacc[dt][r];
+        }
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkacc[dt][r] += red[((wave * 8 + dt) * 16 + r) * 64 + lane];
+        dvacc[dt][r] += red[((wave * 8 + 4 + dt) * 16 + r) * 64 + lane];
+      }
   }
   // C[key][d]: lane (d, half), register r -> key 32 wave + 8 (r/4) + 4 half + r%4
   const int64_t pbase = ((int64_t)page * a.Hkv + g) * 128;
@@ -1532,9 +1654,11 @@ hipError_t launch_dense_dkv(const msa_plan_s* p, const DevMeta& m, const void* q
   const dim3 grid((unsigned)(p->d.num_kv_heads * p->NB));
   ProfEvents pe(p, "dense_dkv");
   if (kl)
-    hipExtLaunchKernelGGL((bwd_dkv_kernel<true, true>), grid, dim3(256), 0, st, pe.start, pe.stop, 0, kv);
+    hipExtLaunchKernelGGL((bwd_dkv_kernel<true, true>), grid, dim3(bwd_dkv_threads<true>()), 0, st, pe.start,
+                          pe.stop, 0, kv);
   else
-    hipExtLaunchKernelGGL((bwd_dkv_kernel<false, true>), grid, dim3(256), 0, st, pe.start, pe.stop, 0, kv);
+    hipExtLaunchKernelGGL((bwd_dkv_kernel<false, true>), grid, dim3(bwd_dkv_threads<false>()), 0, st, pe.start,
+                          pe.stop, 0, kv);
   return hipGetLastError();
 }
 
@@ -1635,9 +1759,11 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   {
     ProfEvents pe(p, "bwd_dkv");
     if (kl)
-      hipExtLaunchKernelGGL(bwd_dkv_kernel<true>, dim3((unsigned)nkey), dim3(256), 0, st, pe.start, pe.stop, 0, kv);
+      hipExtLaunchKernelGGL(bwd_dkv_kernel<true>, dim3((unsigned)nkey), dim3(bwd_dkv_threads<true>()), 0, st,
+                            pe.start, pe.stop, 0, kv);
     else
-      hipExtLaunchKernelGGL(bwd_dkv_kernel<false>, dim3((unsigned)nkey), dim3(256), 0, st, pe.start, pe.stop, 0, kv);
+      hipExtLaunchKernelGGL(bwd_dkv_kernel<false>, dim3((unsigned)nkey), dim3(bwd_dkv_threads<false>()), 0, st,
+                            pe.start, pe.stop, 0, kv);
   }
   return hipGetLastError();
 }

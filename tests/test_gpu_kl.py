@@ -62,10 +62,11 @@ def test_fused_kl_backward_matches_oracle(case):
                                          dout, *ref_main)
     torch.cuda.synchronize()
     used = torch.from_numpy(np.asarray(inp.kv_indices, dtype=np.int64)).cuda()
+    from tests.test_gpu_backward import assert_same_main_grads
     for name, a, b in zip(("dq", "dk", "dv"), grads, ref_main):
         if name != "dq":
             a, b = a[used], b[used]
-        assert torch.equal(a, b), f"{case} {name}: fused backward differs from the main-only backward"
+        assert_same_main_grads(case, name, a, b)
     rq, rk, _, rl = O.proxy_kl_backward(inp.proxy_q, inp.proxy_k_pages, inp.q, inp.k_pages, inp.kv_indices,
                                         sel.cpu().numpy(), w.qo_lens, w.kv_lens, w.page_size, w.sm_scale,
                                         w.proxy_sm_scale, grad_scale=gs)
