@@ -385,6 +385,8 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     if (d.proxy_dtype == MSA_BF16 && d.num_proxy_heads == Hkv && d.num_proxy_kv_heads == Hkv) {
       L.kl_part = off;
       off = align_up(off + W * Hkv * K * 128 * 2, 256);
+      L.kl_stash = off;
+      off = align_up(off + nkey * 128 * 128 * 2 * 4, 256);
     }
     // one query row per sequence (a decode step's indexer pass): the proxy
     // pass uses the one-row kernel, and the fused selection keeps its block
@@ -745,7 +747,8 @@ msa_status_t msa_dense_attn_prefill_backward(msa_plan_t p, const void* q, const 
   hipError_t e = msa::launch_bwd_prep(p, out, dout, D, 0, p->T, hs);
   if (e == hipSuccess) e = msa::launch_dense_dq(p, m, q, k_pages, v_pages, kv_indices, lse, D, dout, dq, klp, hs);
   if (e == hipSuccess)
-    e = msa::launch_dense_dkv(p, m, q, k_pages, v_pages, kv_indices, lse, D, dout, dk_pages, dv_pages, klp, hs);
+    e = msa::launch_dense_dkv(p, m, q, k_pages, v_pages, kv_indices, lse, D, dout, dk_pages, dv_pages, klp,
+                              static_cast<char*>(workspace), hs);
   if (e == hipSuccess && with_kl) e = msa::launch_proxy_kl_dense(p, m, kv_indices, kl, hs);
   return hip_status(e, __func__);
 }

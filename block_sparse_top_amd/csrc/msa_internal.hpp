@@ -35,8 +35,9 @@ struct PlanLayout {
   // prefill window scratch
   size_t counts = 0, cursor = 0, offsets = 0, items = 0, nitems = 0, gitems = 0, entries = 0, part_o = 0, part_lse = 0;
   // per-(token, group, slot) partials of the proxy distillation term (plans
-  // with one bf16 proxy head and proxy-K head per KV group)
-  size_t kl_part = 0;
+  // with one bf16 proxy head and proxy-K head per KV group), and the fused
+  // key-side backward's even-chunk dK / dV partials (128 KB per (group, block))
+  size_t kl_part = 0, kl_stash = 0;
   int64_t max_items = 0;
   // decode split scratch
   size_t dec_o = 0, dec_ml = 0;
@@ -146,7 +147,7 @@ hipError_t launch_dense_dq(const msa_plan_s* p, const DevMeta& m, const void* q,
                            const KlOperands* kl, hipStream_t st);
 hipError_t launch_dense_dkv(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
                             const int32_t* kv_indices, const float* lse, const float* D, const void* dout, float* dk,
-                            float* dv, const KlOperands* kl, hipStream_t st);
+                            float* dv, const KlOperands* kl, char* ws, hipStream_t st);
 hipError_t launch_bwd_prep(const msa_plan_s* p, const void* out, const void* dout, float* D, int32_t w0, int32_t w1,
                            hipStream_t st);
 // The dense proxy part of the distillation gradient, after every window of

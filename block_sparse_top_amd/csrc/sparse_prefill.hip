@@ -1272,6 +1272,9 @@ struct BwdKvArgs {
   const uint8_t* pq;
   float* dpk;
   float inv_g;
+  // KL kernels: the even chunks' dK / dV partials of each (group, block),
+  // [key][wave][tile][register][lane] fp32 (see bwd_dkv_kernel)
+  float* stash;
 };
 
 
@@ -1401,8 +1404,16 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
   // padding (position -1: no key visible).
   const int ri0 = 8 * wave + (lane >> 4), ri1 = ri0 + 4;
   const int lc0 = (lane & 15) ^ rt_swz_key(ri0), lc1 = (lane & 15) ^ rt_swz_key(ri1);
-  const int niter = (nchunks + kGroups - 1) / kGroups;
-  auto chunk_of = [&](int it) { return it * kGroups + grp; };
+  // Chunk order.  Two groups: group grp takes chunks grp, grp + 2, ..., and
+  // the final dK / dV is (even chunks' sum) + (odd chunks' sum).  One group
+  // (KL): the even chunks in order, then the odd ones; the even chunks'
+  // partials are parked in `stash` in between and added at the end, so that
+  // the result is the same fp32 sum bit for bit (a group's padding chunk
+  // adds exact zeros).
+  const int n_even = (nchunks + 1) / 2;
+  const int niter = kGroups == 2 ? n_even : nchunks;
+  auto chunk_of = [&](int it) { return kGroups == 2 ? 2 * it + grp : it < n_even ? 2 * it : 2 * (it - n_even) + 1; };
+  float* const stash = KL ? a.stash + (int64_t)(key * 4 + wave) * (8 * 16 * 64) + lane : nullptr;
   // entries and lse stay raw in registers until used
   auto entry_of = [&](int chunk, int ri) {
     const int e = min(chunk * MT + ri / G, n_ent - 1);
@@ -1466,7 +1477,7 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
     ea = entry_of(chunk_of(1), ri0);
     eb = entry_of(chunk_of(1), ri1);
     es = gtid < 32 ? entry_of(chunk_of(1), gtid) : 0;
-    for (int it = 0; it < niter; ++it) {
+    auto step = [&](int it) __attribute__((always_inline)) {
       const int buf = it & 1;
       const uint8_t* const qb = tile(0, buf);
       const uint8_t* const db = tile(1, buf);
@@ -1579,6 +1590,22 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
           }
         }
       }
+    };
+    const int it_split = KL ? n_even : niter;
+    for (int it = 0; it < it_split; ++it) step(it);
+    if constexpr (KL) {
+      if (n_even < nchunks) {  // the even chunks are done: park their dK / dV partials
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            stash[(dt * 16 + r) * 64] = dkacc[dt][r];
+            stash[((4 + dt) * 16 + r) * 64] = dvacc[dt][r];
+          }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
+      }
+      for (int it = it_split; it < niter; ++it) step(it);
     }
   }
   if constexpr (kGroups == 2) {
@@ -1605,6 +1632,18 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
         dvacc[dt][r] += red[((wave * 8 + 4 + dt) * 16 + r) * 64 + lane];
       }
   }
+  if constexpr (KL) {
+    if (n_even < nchunks) {  // even chunks' partials + odd chunks' (this lane's own stores, read back)
+      wait_vmem();
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dkacc[dt][r] = stash[(dt * 16 + r) * 64] + dkacc[dt][r];
+          dvacc[dt][r] = stash[((4 + dt) * 16 + r) * 64] + dvacc[dt][r];
+        }
+    }
+  }
   // C[key][d]: lane (d, half), register r -> key 32 wave + 8 (r/4) + 4 half + r%4
   const int64_t pbase = ((int64_t)page * a.Hkv + g) * 128;
 #pragma unroll
@@ -1627,7 +1666,7 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
 
 hipError_t launch_dense_dkv(const msa_plan_s* p, const DevMeta& m, const void* q, const void* kp, const void* vp,
                             const int32_t* kv_indices, const float* lse, const float* D, const void* dout, float* dk,
-                            float* dv, const KlOperands* kl, hipStream_t st) {
+                            float* dv, const KlOperands* kl, char* ws, hipStream_t st) {
   BwdKvArgs kv{};
   kv.q = static_cast<const uint8_t*>(q);
   kv.dout = static_cast<const uint8_t*>(dout);
@@ -1651,6 +1690,7 @@ hipError_t launch_dense_dkv(const msa_plan_s* p, const DevMeta& m, const void* q
   kv.pq = kl ? static_cast<const uint8_t*>(kl->pq) : nullptr;
   kv.dpk = kl ? kl->dpk : nullptr;
   kv.inv_g = 1.f / (float)p->G;
+  kv.stash = kl ? reinterpret_cast<float*>(ws + p->lay.kl_stash) : nullptr;
   const dim3 grid((unsigned)(p->d.num_kv_heads * p->NB));
   ProfEvents pe(p, "dense_dkv");
   if (kl)
@@ -1756,6 +1796,7 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   kv.pq = kl ? static_cast<const uint8_t*>(kl->pq) : nullptr;
   kv.dpk = kl ? kl->dpk : nullptr;
   kv.inv_g = a.inv_g;
+  kv.stash = kl ? reinterpret_cast<float*>(ws + L.kl_stash) : nullptr;
   {
     ProfEvents pe(p, "bwd_dkv");
     if (kl)
