@@ -168,7 +168,6 @@ struct PartialArgs {
 };
 
 constexpr int kMaxItemEntries = 512;   // entries_per_item = min(512, 16 chunks of 128 / G tokens)
-constexpr int kOStage = 32 * 64;       // output staging per wave, 2 KB: 32 rows x 64 B or 16 rows x 128 B
 
 // Eight K/V elements of key row `row`, dims 8 col .. 8 col + 7, as bf16
 // (exact) from a page of format F.
@@ -190,86 +189,6 @@ __device__ __forceinline__ i32x4 load_kv8(const uint8_t* page, int row, int col)
   }
 }
 
-// A wave's 32 query rows x 128 dims of output, held as four O^T MFMA tiles
-// (oacc[dt]: C[dim][row], dims 32 dt ..), scaled by `mul` and stored as bf16
-// rows of 256 bytes at part + row_index(r) * 128 for the wave's row r, through
-// the wave's 2 KB LDS staging area.
-//  * kWholeLines: 16 rows x 128 bytes at a time (two dim tiles of 16 rows),
-//    so that every store instruction writes 8 rows x 128 contiguous bytes,
-//    whole 128-byte lines, with non-temporal stores (a line written in
-//    pieces that way would leave memory as several partial writes).  Staged
-//    row r keeps its 16-byte chunk c at c ^ ((r >> 1) & 7): the 8-byte
-//    writes of 16 rows and the 16-byte reads of 8 rows touch every bank once.
-//  * otherwise: one 32-column tile of all 32 rows at a time, every store
-//    instruction 16 rows x 64 bytes, ordinary stores (the cache combines the
-//    pieces of a line); half the LDS writes of the mode above.  Staged row j
-//    keeps its chunk c at c ^ ((j >> 2) & 3).
-template <bool kWholeLines, typename RowIndex>
-__device__ __forceinline__ void store_rows_bf16(const f32x16 (&oacc)[4], float mul, uint8_t* ow, uint16_t* part,
-                                                RowIndex row_index, int lane) {
-  const int jrow = lane & 31, half = lane >> 5;
-  if constexpr (kWholeLines) {
-    int64_t spi[4];  // row 16 R + 8 i + lane / 8: spi[2 R + i]
-#pragma unroll
-    for (int x = 0; x < 4; ++x) spi[x] = row_index(8 * x + (lane >> 3));
-    const int lr = jrow & 15;
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      i32x2 pk[2][4];
-#pragma unroll
-      for (int d = 0; d < 2; ++d)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x16& o = oacc[2 * pr + d];
-          const bf16x2 lo2 = {(__bf16)(o[4 * gq] * mul), (__bf16)(o[4 * gq + 1] * mul)};
-          const bf16x2 hi2 = {(__bf16)(o[4 * gq + 2] * mul), (__bf16)(o[4 * gq + 3] * mul)};
-          pk[d][gq] = i32x2{__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
-        }
-#pragma unroll
-      for (int R = 0; R < 2; ++R) {
-        if ((jrow >> 4) == R) {
-          // dims 32 d + 8 gq + 4 half .. +3 of this lane's row: chunk 4 d + gq, 8-byte half
-#pragma unroll
-          for (int d = 0; d < 2; ++d)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-              lds_store8(&ow[lr * 128 + (((4 * d + gq) ^ ((lr >> 1) & 7)) << 4) + 8 * half], pk[d][gq]);
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = 8 * i + (lane >> 3), c = lane & 7;
-          const i32x4 v = lds_load16<i32x4>(&ow[r * 128 + ((c ^ ((r >> 1) & 7)) << 4)]);
-          __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(part + spi[2 * R + i] * 128 + 64 * pr + 8 * c));
-        }
-        wave_lds_sync();
-      }
-    }
-  } else {
-    int64_t spi[2];  // row 16 pass + lane / 4
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) spi[pass] = row_index(16 * pass + (lane >> 2));
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const bf16x2 lo2 = {(__bf16)(oacc[dt][4 * gq] * mul), (__bf16)(oacc[dt][4 * gq + 1] * mul)};
-        const bf16x2 hi2 = {(__bf16)(oacc[dt][4 * gq + 2] * mul), (__bf16)(oacc[dt][4 * gq + 3] * mul)};
-        const i32x2 pk = {__builtin_bit_cast(int, lo2), __builtin_bit_cast(int, hi2)};
-        lds_store8(&ow[jrow * 64 + ((gq ^ ((jrow >> 2) & 3)) << 4) + 8 * half], pk);
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        const int r = 16 * pass + (lane >> 2), c = lane & 3;
-        const i32x4 v = lds_load16<i32x4>(&ow[r * 64 + ((c ^ ((r >> 2) & 3)) << 4)]);
-        *reinterpret_cast<i32x4*>(part + spi[pass] * 128 + 32 * dt + 8 * c) = v;
-      }
-      wave_lds_sync();
-    }
-  }
-}
-
 // The partial outputs of the sparse prefill in block floating point.  A
 // record holds one (row, head, slot) partial O (128 values) as 10-bit signed
 // integers n with O_d ~ step * n_d, step = 2^(E - 9) * 1024 / 1023 for the
@@ -288,9 +207,11 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16 (&oacc)[4], float m
 // the log-sum-exp (float2).
 constexpr float kBfpMagic = 12582912.0f;  // 1.5 * 2^23: x + magic keeps round(x) in the low mantissa bits
 
-// Encodes the wave's 32 rows (the O^T tiles of store_rows_bf16, scaled by
-// `mul`) and stores the five plane words of each lane's group straight from
-// the lanes (16 bytes per lane and plane).  Returns the lane's row's step.
+// Encodes a wave's 32 rows x 128 dims of output, held as four O^T MFMA tiles
+// (oacc[dt]: C[dim][row], dims 32 dt ..; lane (row, h) holds dims 32 dt +
+// 8 gq + 4 h + t in register 4 gq + t), scaled by `mul`, and stores the five
+// plane words of each lane's group straight from the lanes (16 bytes per
+// lane and plane) at record rec(row).  Returns the lane's row's step.
 template <typename RecIndex>
 __device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float mul, uint8_t* planes,
                                                   int64_t plane_stride, RecIndex rec, int lane) {
@@ -942,8 +863,10 @@ struct BwdDqArgs {
   const int4* items;
   const int32_t* nitems;
   DevMeta m;
-  uint16_t* part;         // bf16 dQ partials [W, Hq, k, 128], then one trash slot
-  int64_t trash;
+  uint8_t* part_pk;       // dQ partials, block floating point (store_rows_bfp10): five planes of
+  int64_t plane_stride;   //   32 bytes per record [W, k, Hq] + trash records, this far apart
+  float* part_step;       //   each record's step [W, Hq, k] + trash entries
+  int64_t trash;          // index of the first of kTrashRecords trash records
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2, sm_scale;
   // proxy distillation term (KL kernels only): proxy K pool bf16 [N, Hkv,
@@ -963,7 +886,6 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];   // K, rt_swz: S^T operand and K^T reads
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];   // V, rt_swz: dP^T operand
   __shared__ __attribute__((aligned(16))) uint8_t pkt[KL ? 128 * 256 : 16];   // proxy K, v_swz
-  __shared__ __attribute__((aligned(16))) uint8_t ost[4 * kOStage];
   __shared__ int32_t ent_s[kMaxItemEntries];
   const int item = blockIdx.x;
   if (item >= *a.nitems) return;
@@ -1037,7 +959,6 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
       kthi[dt] = rt_swz(r0 + 8, c) + 8 * (m16 & 1);
     }
   }
-  uint8_t* ow = ost + wave * kOStage;
 
   // The row of a chunk: padding rows (past the item's entries) repeat a real
   // one; their output is discarded.  Each wave's rows come from global memory
@@ -1147,18 +1068,22 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // scaled bf16 partial through the wave's staging area: whole lines with
-    // non-temporal stores in the plain variant; the fused distillation variant
-    // (one workgroup per CU, so one wave per SIMD to hide the extra LDS
-    // writes) measured faster with 64-byte pieces and ordinary stores
-    auto row_index = [&](int wrow) -> int64_t {
-      const int srow = 32 * wave + wrow;
+    // the scaled partial in block floating point, straight from the lanes
+    // (records (row * k + slot) * Hq + head: the G heads of an entry share
+    // lines); padding rows go to one of kTrashRecords trash records
+    {
+      const int srow = 32 * wave + (lane & 31);
       const int se = chunk * MT + srow / G;
-      if (se >= n_ent) return a.trash;
-      const int sent = ent_s[se];
-      return ((int64_t)(sent >> 6) * a.Hq + g * G + (srow & (G - 1))) * a.k + (sent & 63);
-    };
-    store_rows_bf16<!KL>(oacc, a.sm_scale, ow, a.part, row_index, lane);
+      const int64_t trash = a.trash + (int64_t)(blockIdx.x & (kTrashRecords - 1));
+      const int sent = ent_s[min(se, n_ent - 1)];
+      const int head = g * G + (srow & (G - 1));
+      auto rec_index = [&](int) -> int64_t {  // the lane's own row
+        return se < n_ent ? ((int64_t)(sent >> 6) * a.k + (sent & 63)) * a.Hq + head : trash;
+      };
+      const float step = store_rows_bfp10(oacc, a.sm_scale, a.part_pk, a.plane_stride, rec_index, lane);
+      // both halves hold the row's step and store the same value
+      a.part_step[se < n_ent ? ((int64_t)(sent >> 6) * a.Hq + head) * a.k + (sent & 63) : trash] = step;
+    }
     if constexpr (KL) {
       // sum_j P_hj pk_j for this wave's rows (kacc: C[dim][row] = pk^T P^T),
       // summed over a token's G heads (adjacent lanes); one bf16 store per
@@ -1249,6 +1174,79 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(DqSumArgs a) {
   float* dst = a.dq + ((int64_t)r * a.Hq + h) * 128 + 8 * sub;
   *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
   *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+}
+
+// dq = the sum over a row's slots of its block-floating-point partials
+// (bwd_dq): 8 lanes per (row, head), laid out like the forward merge's (lane
+// l: dword l of each plane, dims 32 dt + 8 gq + 4 h + t for h = l / 4,
+// dt = l % 4), slots 8 at a time; a slot counts when its block is at most
+// the row's local block (bwd_dq wrote nothing for the others: their step
+// is taken as 0).  topk <= 64.
+struct DqBfpSumArgs {
+  const int32_t* sel;
+  DevMeta m;
+  const uint8_t* part_pk;
+  int64_t plane_stride;
+  const float* part_step;
+  float* dq;              // fp32 [T, Hq, 128]
+  int32_t Hq, Hkv, G, k, w0, w1;
+};
+__global__ __launch_bounds__(256) void bwd_dq_sum_bfp_kernel(DqBfpSumArgs a) {
+  constexpr int NL = kMergeLanes;
+  const int l = threadIdx.x & (NL - 1);
+  const int64_t idx = (int64_t)blockIdx.x * (256 / NL) + (threadIdx.x / NL);
+  const bool live = idx < (int64_t)(a.w1 - a.w0) * a.Hq;   // shuffles need every lane
+  const int64_t id = live ? idx : 0;
+  const int32_t rl = (int32_t)(id / a.Hq);
+  const int h = (int)(id % a.Hq);
+  const int g = h / a.G;
+  const int32_t r = a.w0 + rl;
+  const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
+  auto rec_of = [&](int slot) -> int64_t { return ((int64_t)rl * a.k + slot) * a.Hq + h; };
+  BfpRec v[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_pk, a.plane_stride, rec_of(min(j, a.k - 1)), l);
+  const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
+  const int ngroups = (a.k + NL - 1) / NL;
+  int b_g[8];
+  float st_g[8];
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) {
+    const int slot = min(NL * gi + l, a.k - 1);
+    const bool in = gi < ngroups && NL * gi + l < a.k;
+    b_g[gi] = in ? row[slot] : -1;
+    st_g[gi] = in ? a.part_step[base + slot] : 0.f;
+  }
+  const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
+  const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi)
+    if (!(b_g[gi] >= 0 && b_g[gi] <= local)) st_g[gi] = 0.f;  // never written: never read into the sum
+  float o[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) o[x] = 0.f;
+  for (int gi = 0; gi < ngroups; ++gi) {
+    float stl = st_g[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) stl = q == gi ? st_g[q] : stl;
+    if (gi > 0) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_pk, a.plane_stride, rec_of(min(NL * gi + j, a.k - 1)), l);
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const float step = __shfl(stl, j, NL);
+      if (step == 0.f) continue;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) o[x] = __builtin_fmaf(step, bfp_field(v[j], x), o[x]);
+    }
+  }
+  if (!live) return;
+  const int hh = l >> 2, dt = l & 3;
+  float* drow = a.dq + ((int64_t)r * a.Hq + h) * 128;
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq)
+    *reinterpret_cast<f32x4*>(drow + 32 * dt + 8 * gq + 4 * hh) = f32x4{o[4 * gq], o[4 * gq + 1], o[4 * gq + 2], o[4 * gq + 3]};
 }
 
 struct BwdKvArgs {
@@ -1720,7 +1718,6 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   const int32_t nkey = Hkv * p->NB;
   build_csr(p, m, sel, ws, w0, w1, st, /*sorted=*/true);
   float* D = reinterpret_cast<float*>(ws + L.part_lse);
-  uint16_t* part = reinterpret_cast<uint16_t*>(ws + L.part_o);
   const int64_t npairs = (int64_t)(w1 - w0) * Hq;
   {
     PrepArgs pa{static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), D, w0, w1, Hq};
@@ -1738,8 +1735,13 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   a.items = reinterpret_cast<const int4*>(ws + L.items);
   a.nitems = reinterpret_cast<const int32_t*>(ws + L.nitems);
   a.m = m;
-  a.part = part;
+  // the dQ partial records' planes and steps share the region the forward's
+  // partial records use (160 + 4 bytes per record of its 168)
   a.trash = p->attn_window * Hq * k;
+  const int64_t nrec = a.trash + kTrashRecords;
+  a.part_pk = reinterpret_cast<uint8_t*>(ws + L.part_o);
+  a.plane_stride = nrec * 32;
+  a.part_step = reinterpret_cast<float*>(a.part_pk + 5 * a.plane_stride);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = p->G;
@@ -1759,10 +1761,11 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
       hipExtLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)max_items), dim3(256), 0, st, pe.start, pe.stop, 0, a);
   }
   {
-    DqSumArgs ds{sel, m, part, dq, Hq, Hkv, p->G, k, w0, w1};
+    DqBfpSumArgs ds{sel, m, a.part_pk, a.plane_stride, a.part_step, dq, Hq, Hkv, p->G, k, w0, w1};
+    constexpr int kPairsPerBlock = 256 / kMergeLanes;
     ProfEvents pe(p, "bwd_dq_sum");
-    hipExtLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((npairs + 15) / 16)), dim3(256), 0, st, pe.start,
-                          pe.stop, 0, ds);
+    hipExtLaunchKernelGGL(bwd_dq_sum_bfp_kernel, dim3((unsigned)((npairs + kPairsPerBlock - 1) / kPairsPerBlock)),
+                          dim3(256), 0, st, pe.start, pe.stop, 0, ds);
   }
   if (kl) {   // the sparse proxy term of each (row, group): sum of its slots, into dpq
     DqSumArgs ds{sel, m, a.klpart, kl->dpq, Hkv, Hkv, 1, k, w0, w1};
