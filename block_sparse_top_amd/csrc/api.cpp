@@ -373,13 +373,12 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     L.nitems = off; off = align_up(off + 16, 256);
     L.gitems = off; off = align_up(off + (Hkv + 1) * 4, 256);  // first work item of each KV group
     L.entries = off; off = align_up(off + W * Hkv * K * 4, 256);
-    // one extra slot at index W * Hq * K takes the stores of padding rows
-    // the forward's partial records (and their trash records), or the
-    // backward's bf16 dq partials (one trash slot), whichever is larger
+    // the forward's partial records and the backward's dQ partial records
+    // (block floating point, 168 and 164 bytes), each followed by
+    // kTrashRecords records that take the stores of padding rows
     L.part_o = off;
-    off = align_up(off + std::max<int64_t>((W * Hq * K + 1) * 128 * 2,
-                                           (W * Hq * K + msa::kTrashRecords) * msa::kPartRecordBytes), 256);
-    L.part_lse = off; off = align_up(off + (W * Hq * K + 1) * 4, 256);
+    off = align_up(off + (W * Hq * K + msa::kTrashRecords) * msa::kPartRecordBytes, 256);
+    L.bwd_d = off; off = align_up(off + W * Hq * 4, 256);  // the sparse backward's D = <dout, out> [W, Hq]
     // the fused backward's proxy distillation term needs one bf16 proxy head
     // and proxy-K head per KV group: its per-(token, group, slot) partials
     if (d.proxy_dtype == MSA_BF16 && d.num_proxy_heads == Hkv && d.num_proxy_kv_heads == Hkv) {
@@ -731,7 +730,7 @@ msa_status_t msa_dense_attn_prefill_backward(msa_plan_t p, const void* q, const 
     MSA_CHECK_PTR(proxy_lse);
   }
   // D = <dout, out> for every row lives in the partial-output area
-  if ((size_t)p->T * p->d.num_qo_heads * 4 > p->lay.part_lse - p->lay.part_o)
+  if ((size_t)p->T * p->d.num_qo_heads * 4 > p->lay.bwd_d - p->lay.part_o)
     return fail(MSA_ERR_UNSUPPORTED,
                 "msa_dense_attn_prefill_backward: the plan's attention window is too short for this many rows "
                 "(its partial area holds D = <dout, out> of every row)");

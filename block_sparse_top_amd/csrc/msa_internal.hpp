@@ -33,7 +33,7 @@ struct Profiler {
 struct PlanLayout {
   size_t meta = 0, meta_bytes = 0;
   // prefill window scratch
-  size_t counts = 0, cursor = 0, offsets = 0, items = 0, nitems = 0, gitems = 0, entries = 0, part_o = 0, part_lse = 0;
+  size_t counts = 0, cursor = 0, offsets = 0, items = 0, nitems = 0, gitems = 0, entries = 0, part_o = 0, bwd_d = 0;
   // per-(token, group, slot) partials of the proxy distillation term (plans
   // with one bf16 proxy head and proxy-K head per KV group), and the fused
   // key-side backward's even-chunk dK / dV partials (128 KB per (group, block))

@@ -1717,7 +1717,7 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
   const int32_t nkey = Hkv * p->NB;
   build_csr(p, m, sel, ws, w0, w1, st, /*sorted=*/true);
-  float* D = reinterpret_cast<float*>(ws + L.part_lse);
+  float* D = reinterpret_cast<float*>(ws + L.bwd_d);
   const int64_t npairs = (int64_t)(w1 - w0) * Hq;
   {
     PrepArgs pa{static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), D, w0, w1, Hq};

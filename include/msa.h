@@ -281,8 +281,8 @@ msa_status_t msa_sparse_attn_prefill_rows(msa_plan_t plan, const void* q, const 
  *                     no row attends to it); other pages are not touched
  * Results are bit-reproducible when the plan's attention window is at most
  * 65536 rows (the default window is): the rows that selected a block are then
- * summed in ascending row order for dk/dv, and the per-slot dq partials in
- * slot order.
+ * summed in a fixed order for dk/dv (ascending rows, in two interleaved chunk
+ * groups added at the end), and the per-slot dq partials in slot order.
  * Errors: INVALID_ARG for null or misaligned pointers; UNSUPPORTED for a
  * decode plan or non-bf16 K/V; WORKSPACE_TOO_SMALL. */
 msa_status_t msa_sparse_attn_prefill_backward(msa_plan_t plan, const void* q, const void* k_pages,
