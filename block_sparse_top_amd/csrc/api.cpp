@@ -359,6 +359,9 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     const int64_t per_row = Hq * K * (128 * 2 + 4);
     const int64_t auto_w = std::max<int64_t>(256, std::min<int64_t>(32768, ((int64_t)16 << 30) / per_row));
     p->attn_window = std::min<int64_t>(T, d.attn_window_rows > 0 ? d.attn_window_rows : auto_w);
+    // each of the five planes of partial records (32 bytes a record) stays
+    // under 2^32 bytes: the merge addresses a plane with a 32-bit offset
+    p->attn_window = std::min<int64_t>(p->attn_window, (((int64_t)1 << 27) - msa::kTrashRecords) / (Hq * K));
     {
       const char* pin = std::getenv("MSA_XCD_PIN");
       p->xcd_pin = pin && pin[0] == '1';

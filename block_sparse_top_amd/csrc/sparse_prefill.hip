@@ -20,6 +20,7 @@
 //     (row, head, slot);
 //  3. merge: per (row, head) the slot partials are combined with their
 //     log-sum-exp weights into the final output and lse.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -41,10 +42,11 @@ struct CsrArgs {
   const int32_t* offsets;
   int32_t* entries;
   int32_t w0, w1, Hkv, k;
+  int32_t with_local;  // 1: a row's own block is an entry too (the backward); 0: it is not (the forward)
 };
 
 // One thread per row of one group (grid.y = group); a row's valid slots are
-// those with 0 <= b <= local.  With LDS_HIST the workgroup first histograms
+// those with 0 <= b <= local (b < local without the row's own block).  With LDS_HIST the workgroup first histograms
 // its 256 rows' blocks in LDS, so global memory sees one atomic per touched
 // (group, block) bin per workgroup instead of one per entry.
 constexpr int kMaxLdsBins = 16384;
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
   const int32_t r = a.w0 + (valid ? rl : 0);
   const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
   const int32_t pos = a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s]);
-  const int local = pos >> 7;
+  const int bend = (pos >> 7) + a.with_local;  // entries: blocks 0 <= b < bend
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   const int32_t pb = a.m.page_start[s];
   const int NB = a.m.NB;
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
     if (!valid) return;
     for (int slot = 0; slot < a.k; ++slot) {
       const int b = row[slot];
-      if (b < 0 || b > local) continue;
+      if (b < 0 || b >= bend) continue;
       if (!FILL) atomicAdd(&counts[pb + b], 1);
       else a.entries[offsets[pb + b] + atomicAdd(&cursor[pb + b], 1)] = (rl << 6) | slot;
     }
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
     if (valid)
       for (int slot = 0; slot < a.k; ++slot) {
         const int b = row[slot];
-        if (b >= 0 && b <= local) atomicAdd(&hist[pb + b], 1);
+        if (b >= 0 && b < bend) atomicAdd(&hist[pb + b], 1);
       }
     __syncthreads();
     for (int i = tid; i < NB; i += 256) {
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
     if (valid)
       for (int slot = 0; slot < a.k; ++slot) {
         const int b = row[slot];
-        if (b >= 0 && b <= local) a.entries[atomicAdd(&hist[pb + b], 1)] = (rl << 6) | slot;
+        if (b >= 0 && b < bend) a.entries[atomicAdd(&hist[pb + b], 1)] = (rl << 6) | slot;
       }
   }
 }
@@ -484,25 +486,346 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   }
 }
 
-struct MergeArgs {
-  const int32_t* sel;
+// The local block of every row inside the merge.  Each row's own
+// (diagonal) block is computed here rather than as a slot of partial_attn:
+// one workgroup per (KV group, block, 128 rows of the block's own query rows
+// x G heads), whose Q rows are contiguous (no gather), whose key tiles past
+// a wave's last row are skipped, and whose result stays in registers: the
+// row's other slots' partial records (bfp) are then added to it with the
+// usual log-sum-exp weights, and the output row is written.  A lane holds
+// the dims of its row that store_rows_bfp10 packed from the same lane
+// position, so a slot's record is one 16-byte load per plane.
+struct LocalMergeArgs {
+  const uint8_t* q;      // bf16 [T, Hq, 128]
+  const uint8_t* kp;     // K / V pages (format F)
+  const uint8_t* vp;
+  const float* ks;       // fp8: [Hkv] scales, else null
+  const float* vs;
+  const int32_t* kv_indices;
+  const int32_t* sel;    // [T, Hkv, k]
   DevMeta m;
-  const uint8_t* part_pk;
+  const uint8_t* part_pk;  // partial_attn's records and their {lse, step}
   int64_t plane_stride;
   const float2* part_st;
-  uint16_t* out;   // bf16 [T, Hq, 128]
-  float* lse;      // [T, Hq] or null
+  uint16_t* out;         // bf16 [T, Hq, 128]
+  float* lse;            // [T, Hq] or null
   int32_t Hq, Hkv, G, k, w0, w1;
+  int32_t key0;          // first (block, group) key of the launch: block * Hkv
+  float scale_log2;      // sm_scale * log2(e)
 };
 
-// 8 lanes per (row, head): lane l takes dword l of each of a record's five
-// planes, group l of store_rows_bfp10: dims 32 dt + 8 gq + 4 h + t for
-// h = l / 4, dt = l % 4 and gq, t = 0..3.  Slots go 8 at a time, the first 8
-// slots' records issued before anything else; lane l of the 8 reads slot l's
-// block id and {log-sum-exp, step} (coalesced), the row's local block then
-// says which slots count, and the group's max and weights move by shuffles.
-// Decoding: a field inside one word is a signed bit-field extract, the four
-// that straddle two words first join them with one alignbit.  topk <= 64.
+template <KvFmt F>
+__global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];
+  const int G = a.G;
+  // workgroups are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8):
+  // XCD x takes the x-th eighth of the launch's (block, group) keys, so that
+  // the G workgroups of a key share its K/V in one L2 and each XCD streams
+  // a contiguous range of records, query rows and output rows
+  const uint32_t nwg = gridDim.x, bid = blockIdx.x;
+  const int wid = (int)(nwg % 8 == 0 ? (bid % 8) * (nwg / 8) + bid / 8 : bid);
+  const int c = wid % G;                         // which 128 of the block's rows x G heads
+  const int key = a.key0 + wid / G;
+  const int gb = key / a.Hkv, g = key % a.Hkv;
+  const int s = upper_bound_i32(a.m.page_start, a.m.S + 1, gb) - 1;
+  const int b = gb - a.m.page_start[s];
+  const int32_t first_pos = a.m.kv[s] - a.m.qo[s];
+  const int32_t rs = a.m.row_start[s];
+  // the block's keys b*128 + t that are query rows of this window
+  const int32_t p_lo = max(max(b * 128, first_pos), first_pos + (a.w0 - rs));
+  const int32_t p_hi = min(min(b * 128 + 128, a.m.kv[s]), first_pos + (a.w1 - rs));
+  const int MT = 128 / G;                        // tokens per 128 rows
+  const int32_t t0 = p_lo - b * 128 + c * MT;    // this workgroup's first token
+  const int32_t t_hi = p_hi - b * 128;
+  if (t0 >= t_hi) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t page = a.kv_indices[gb];
+  {  // K and V block -> LDS as bf16 (as partial_attn): the 32-key tiles
+     // that the workgroup's last row sees, 16 keys per pass
+    constexpr int64_t kPageBytes = F == KvFmt::BF16 ? 32768 : F == KvFmt::FP8 ? 16384 : 128 * 64 + 128 * 4;
+    const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * kPageBytes;
+    const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * kPageBytes;
+    const int passes = 2 * ((min(t0 + MT, t_hi) - 1) / 32 + 1);
+    i32x4 kr[8], vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < passes) {
+        const int cc = tid + 256 * i;
+        kr[i] = load_kv8<F>(kb, cc >> 4, cc & 15);
+        vr[i] = load_kv8<F>(vb, cc >> 4, cc & 15);
+      }
+    }
+    const int kv_in_block = a.m.kv[s] - b * 128;  // rows at or past this are page padding
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < passes) {
+        const int cc = tid + 256 * i;
+        lds_store16<i32x4>(&ks[k_swz(cc >> 4, cc & 15)], kr[i]);
+        lds_store16<i32x4>(&vs[v_swz(cc >> 4, cc & 15)], (cc >> 4) < kv_in_block ? vr[i] : i32x4{});
+      }
+    }
+  }
+  const int half = lane >> 5;
+  const int qr = 32 * wave + (lane & 31);        // this lane's row within the 128
+  const int hh = qr % G;
+  const int32_t t = t0 + qr / G;
+  const bool row_ok = t < t_hi;
+  const int32_t tt = row_ok ? t : t_hi - 1;     // padding lanes repeat the last row (nothing stored)
+  const int32_t r = rs + (b * 128 + tt - first_pos);
+  const int h = g * G + hh;
+  const float scale_log2 = F == KvFmt::FP8 ? a.scale_log2 * a.ks[g] : a.scale_log2;
+  const float v_scale = F == KvFmt::FP8 ? a.vs[g] : 1.f;
+  const int q16 = lane >> 4, m16 = lane & 15;
+  int kbase[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) kbase[st] = (lane & 31) * 256 + (((2 * st + half) ^ (lane & 15)) << 4);
+  int vbase[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
+                ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  bf16x8 qf[8];
+  {
+    const uint8_t* qrow = a.q + ((int64_t)r * a.Hq + h) * 256 + half * 16;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
+  }
+  // The row's other slots (blocks 0 <= blk < b; the local block is b): the
+  // first 16 slots' block ids and {lse, step} are requested now and arrive
+  // while the local block is computed.
+  constexpr int kBatch = 16;
+  const int32_t rl = r - a.w0;
+  const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
+  const float2* st_row = a.part_st + ((int64_t)rl * a.Hq + h) * a.k;
+  // with k a multiple of 4 (and the selection 16-byte aligned) the rows of
+  // block ids and of {lse, step} go in 16-byte pieces
+  const bool vec_stats = (a.k & 3) == 0 && (reinterpret_cast<uintptr_t>(a.sel) & 15) == 0;
+  auto load_stats = [&](int s0, int (&blk)[kBatch], float2 (&ls)[kBatch]) {
+    if (vec_stats) {
+#pragma unroll
+      for (int j = 0; j < kBatch; j += 4) {
+        const int slot = min(s0 + j, a.k - 4);
+        const i32x4 bv = *reinterpret_cast<const i32x4*>(row + slot);
+        const f32x4 l01 = *reinterpret_cast<const f32x4*>(st_row + slot);
+        const f32x4 l23 = *reinterpret_cast<const f32x4*>(st_row + slot + 2);
+        const bool in = s0 + j < a.k;  // then all four are
+#pragma unroll
+        for (int q = 0; q < 4; ++q) blk[j + q] = in ? bv[q] : -1;
+        ls[j] = float2{l01[0], l01[1]};
+        ls[j + 1] = float2{l01[2], l01[3]};
+        ls[j + 2] = float2{l23[0], l23[1]};
+        ls[j + 3] = float2{l23[2], l23[3]};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int slot = min(s0 + j, a.k - 1);
+        blk[j] = s0 + j < a.k ? row[slot] : -1;
+        ls[j] = st_row[slot];
+      }
+    }
+  };
+  // a plane holds under 2^32 bytes (the plan caps the window): one 32-bit
+  // offset per slot serves the five planes' uniform bases
+  const uint8_t* const plane0 = a.part_pk;
+  const uint8_t* const plane1 = plane0 + a.plane_stride;
+  const uint8_t* const plane2 = plane1 + a.plane_stride;
+  const uint8_t* const plane3 = plane2 + a.plane_stride;
+  const uint8_t* const plane4 = plane3 + a.plane_stride;
+  auto rec_load = [&](int slot, i32x4 (&w)[5]) {
+    const uint32_t off = (((uint32_t)rl * (uint32_t)a.k + (uint32_t)slot) * (uint32_t)a.Hq + (uint32_t)h) * 32u + 16u * half;
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane0 + off));
+    w[1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane1 + off));
+    w[2] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane2 + off));
+    w[3] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane3 + off));
+    w[4] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane4 + off));
+  };
+  int blk0[kBatch];
+  float2 ls0[kBatch];
+  load_stats(0, blk0, ls0);
+  // key tiles holding a visible key of some row of the wave: its rows are
+  // consecutive tokens, the last one sees keys 0 .. its t
+  int tmax = tt;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) tmax = max(tmax, __shfl_xor(tmax, o));
+  const int nkt = __builtin_amdgcn_readfirstlane(min(4, (tmax >> 5) + 1));  // the same in every lane
+  const int lim = tt - 4 * half;                 // last visible key offset, minus the lane's 4-key shift
+  __syncthreads();
+
+  // S^T = K Q^T on the live tiles; K fragments one k-step ahead
+  f32x16 acc[4];
+  {
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      if (kt < nkt) kf[0][kt] = lds_load16<bf16x8>(&ks[kbase[0] + 8192 * kt]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          if (kt < nkt) kf[(st + 1) & 1][kt] = lds_load16<bf16x8>(&ks[kbase[st + 1] + 8192 * kt]);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        if (kt < nkt) acc[kt] = mfma32x32x16(kf[st & 1][kt], qf[st], st == 0 ? f32x16{} : acc[kt]);
+    }
+  }
+  // causal mask (hidden scores -inf), row max, p = exp2(s * scale - max)
+  float mraw = kNegInf;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+    if (kt < nkt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) acc[kt][i] = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mraw = max3f(mraw, acc[kt][i], acc[kt][i + 1]);
+    }
+  mraw = wave_max32(mraw);
+  const float mx = mraw * scale_log2;
+  float sum = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    if (kt < nkt) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        i32x4 pw;
+#pragma unroll
+        for (int tq = 0; tq < 4; ++tq) {
+          const float p0 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * tq], scale_log2, -mx));
+          const float p1 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * tq + 1], scale_log2, -mx));
+          sum += p0 + p1;
+          const bf16x2 two = {(__bf16)p0, (__bf16)p1};
+          pw[tq] = __builtin_bit_cast(int, two);
+        }
+        pf[u] = __builtin_bit_cast(bf16x8, pw);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const s16x4 lo = lds_read_tr16(&vs[vbase[dt] + 256 * (32 * kt + 16 * u)]);
+          const s16x4 hi = lds_read_tr16(&vs[vbase[dt] + 256 * (32 * kt + 16 * u + 8)]);
+          oacc[dt] = mfma32x32x16(join_tr16(lo, hi), pf[u], kt == 0 && u == 0 ? f32x16{} : oacc[dt]);
+        }
+      }
+    }
+  }
+  sum = wave_sum32(sum);  // >= 1: the row max contributes exp2(0)
+
+  // The slots' max M over the local block and the counted slots, then per
+  // batch of 16 slots each one's weight exp(lse - M) * step goes to LDS (the
+  // K/V tiles are no longer needed; [slot][thread], conflict-free) and the
+  // records are added one slot after another, each loaded three slots ahead
+  // (one workgroup's waves alone keep the memory system busy while the other
+  // workgroup on the compute unit is in its local block).
+  // A slot that holds no record weighs 0: its stats may hold anything, NaN
+  // too, and are not read into the result; its (unwritten) record is
+  // integers, always finite, and adds exactly 0.
+  const float lse_loc = (mx + fast_log2(sum)) * kLn2;  // natural log
+  float M = lse_loc;
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    if (blk0[j] >= 0 && blk0[j] < b) M = fmaxf(M, ls0[j].x);
+  for (int s0 = kBatch; s0 < a.k; s0 += kBatch) {
+    int blk[kBatch];
+    float2 ls[kBatch];
+    load_stats(s0, blk, ls);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (blk[j] >= 0 && blk[j] < b) M = fmaxf(M, ls[j].x);
+  }
+  const float w_loc = fast_exp2((lse_loc - M) * kLog2e);
+  float L = w_loc;
+  const float f_loc = v_scale * w_loc / sum;   // oacc holds sum_j p_j v_j (unscaled V for fp8)
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] *= f_loc;
+  // field j of group dt: bits 10 j .. of the 160-bit group made of plane
+  // words w[0..4][dt] (as bfp_field)
+  auto field = [&](const i32x4 (&w)[5], int dt, int j) -> float {
+    const int bit = 10 * j, qw = bit >> 5, o = bit & 31;
+    const uint32_t x0 = (uint32_t)w[qw][dt];
+    if (o <= 22) return (float)((int)(x0 << (22 - o)) >> 22);
+    return (float)((int)(__builtin_amdgcn_alignbit((uint32_t)w[qw + 1][dt], x0, o) << 22) >> 22);
+  };
+  auto add_rec = [&](const i32x4 (&w)[5], float ws) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[dt][j] = __builtin_fmaf(ws, field(w, dt, j), oacc[dt][j]);
+  };
+  auto put_weights = [&](const int (&blk)[kBatch], const float2 (&ls)[kBatch], float* ws_s) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool in = blk[j] >= 0 && blk[j] < b;
+      const float w = in ? fast_exp2((ls[j].x - M) * kLog2e) : 0.f;
+      L += w;
+      ws_s[j * 256 + tid] = in ? w * ls[j].y : 0.f;  // this lane's own slot weights
+    }
+  };
+  __syncthreads();  // every wave is done with the K/V tiles
+  float* const ws_s = reinterpret_cast<float*>(ks);   // [kBatch][256]
+  i32x4 rb[4][5];  // records of four consecutive slots, slot j in rb[j % 4]
+  rec_load(0, rb[0]);
+  put_weights(blk0, ls0, ws_s);
+  for (int s0 = 0; s0 < a.k; s0 += kBatch) {
+    if (s0 > 0) {
+      int blk[kBatch];
+      float2 ls[kBatch];
+      load_stats(s0, blk, ls);
+      put_weights(blk, ls, ws_s);
+      rec_load(s0, rb[0]);
+    }
+    // the batch's slots padded to a multiple of 4: a padding slot re-reads
+    // slot k - 1's record and weighs 0 (put_weights), so every load of the
+    // ring is unconditional and stays in flight across the loop
+    const int n4 = (min(kBatch, a.k - s0) + 3) & ~3;  // the same in every lane
+#pragma unroll
+    for (int u = 1; u < 4; ++u) rec_load(min(s0 + u, a.k - 1), rb[u]);
+    // (the scheduler would otherwise hoist later slots' decoding, and with it
+    // their waits, above the earlier slots' adds)
+    int j = 0;
+    for (; j + 4 < n4; j += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        add_rec(rb[u], ws_s[(j + u) * 256 + tid]);
+        rec_load(min(s0 + j + u + 4, a.k - 1), rb[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      add_rec(rb[u], ws_s[(j + u) * 256 + tid]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (!row_ok) return;
+  const float inv = 1.f / L;
+  // lane (row, half): dims 32 dt + 8 gq + 4 half + tq in register 4 gq + tq
+  uint16_t* orow = a.out + ((int64_t)r * a.Hq + h) * 128;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const bf16x2 t0v = {(__bf16)(oacc[dt][4 * gq] * inv), (__bf16)(oacc[dt][4 * gq + 1] * inv)};
+      const bf16x2 t1v = {(__bf16)(oacc[dt][4 * gq + 2] * inv), (__bf16)(oacc[dt][4 * gq + 3] * inv)};
+      *reinterpret_cast<i32x2*>(orow + 32 * dt + 8 * gq + 4 * half) =
+          i32x2{__builtin_bit_cast(int, t0v), __builtin_bit_cast(int, t1v)};
+    }
+  if (a.lse && half == 0) a.lse[(int64_t)r * a.Hq + h] = M + fast_log2(L) * kLn2;
+}
+
+// Reading a record 8 lanes at a time: lane l takes dword l of each of the
+// record's five planes, group l of store_rows_bfp10: dims 32 dt + 8 gq + 4 h
+// + t for h = l / 4, dt = l % 4 and gq, t = 0..3.  Decoding: a field inside
+// one word is a signed bit-field extract, the four that straddle two words
+// first join them with one alignbit.
 constexpr int kMergeLanes = 8;
 
 struct BfpRec {
@@ -524,93 +847,6 @@ __device__ __forceinline__ float bfp_field(const BfpRec& r, int j) {
   return (float)((int)(__builtin_amdgcn_alignbit(r.w[q + 1], r.w[q], o) << 22) >> 22);
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int NL = kMergeLanes;
-  const int l = threadIdx.x & (NL - 1);
-  const int64_t idx = (int64_t)blockIdx.x * (256 / NL) + (threadIdx.x / NL);
-  const bool live = idx < (int64_t)(a.w1 - a.w0) * a.Hq;   // shuffles need every lane
-  const int64_t id = live ? idx : 0;
-  const int32_t rl = (int32_t)(id / a.Hq);
-  const int h = (int)(id % a.Hq);
-  const int g = h / a.G;
-  const int32_t r = a.w0 + rl;
-  const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
-  auto rec_of = [&](int slot) -> int64_t { return ((int64_t)rl * a.k + slot) * a.Hq + h; };
-  // the first 8 slots' records depend on nothing else
-  BfpRec v[NL];
-#pragma unroll
-  for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_pk, a.plane_stride, rec_of(min(j, a.k - 1)), l);
-  const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
-  const int ngroups = (a.k + NL - 1) / NL;
-  // lane l's slot of each group of 8: block id, log-sum-exp and step, loaded
-  // before the row's local block is known (a slot counts when 0 <= b <= local)
-  int b_g[8];
-  float lse_g[8], st_g[8];
-#pragma unroll
-  for (int gi = 0; gi < 8; ++gi) {
-    const int slot = min(NL * gi + l, a.k - 1);
-    const bool in = gi < ngroups && NL * gi + l < a.k;
-    b_g[gi] = in ? row[slot] : -1;
-    const float2 ls = in ? a.part_st[base + slot] : float2{kNegInf, 0.f};
-    lse_g[gi] = ls.x;
-    st_g[gi] = ls.y;
-  }
-  const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
-  const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
-  float M = kNegInf;
-#pragma unroll
-  for (int gi = 0; gi < 8; ++gi) {
-    if (!(b_g[gi] >= 0 && b_g[gi] <= local)) {  // never written: neither is read into the result
-      lse_g[gi] = kNegInf;
-      st_g[gi] = 0.f;
-    }
-    M = fmaxf(M, lse_g[gi]);
-  }
-#pragma unroll
-  for (int off = 1; off < NL; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, NL));
-  float Ll = 0.f;  // this lane's slots' weights
-  float o[16];
-#pragma unroll
-  for (int x = 0; x < 16; ++x) o[x] = 0.f;
-  for (int gi = 0; gi < ngroups; ++gi) {
-    float wl = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q == gi) wl = lse_g[q] == kNegInf ? 0.f : fast_exp2((lse_g[q] - M) * kLog2e);
-    float stl = st_g[0];
-#pragma unroll
-    for (int q = 1; q < 8; ++q) stl = q == gi ? st_g[q] : stl;
-    Ll += wl;
-    const float wsl = wl * stl;  // weight x step
-    if (gi > 0) {
-#pragma unroll
-      for (int j = 0; j < NL; ++j) v[j] = load_bfp_rec(a.part_pk, a.plane_stride, rec_of(min(NL * gi + j, a.k - 1)), l);
-    }
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const float ws = __shfl(wsl, j, NL);
-      if (ws == 0.f) continue;  // invalid slots: never written, never read into the result
-#pragma unroll
-      for (int x = 0; x < 16; ++x) o[x] = __builtin_fmaf(ws, bfp_field(v[j], x), o[x]);
-    }
-  }
-  float L = Ll;
-#pragma unroll
-  for (int off = 1; off < NL; off <<= 1) L += __shfl_xor(L, off, NL);
-  if (!live) return;
-  const float inv = 1.f / L;
-  // dims 32 dt + 8 gq + 4 h + t: four 8-byte runs of the output row
-  const int hh = l >> 2, dt = l & 3;
-  uint16_t* orow = a.out + ((int64_t)r * a.Hq + h) * 128;
-#pragma unroll
-  for (int gq = 0; gq < 4; ++gq) {
-    const bf16x2 t0 = {(__bf16)(o[4 * gq] * inv), (__bf16)(o[4 * gq + 1] * inv)};
-    const bf16x2 t1 = {(__bf16)(o[4 * gq + 2] * inv), (__bf16)(o[4 * gq + 3] * inv)};
-    *reinterpret_cast<i32x2*>(orow + 32 * dt + 8 * gq + 4 * hh) =
-        i32x2{__builtin_bit_cast(int, t0), __builtin_bit_cast(int, t1)};
-  }
-  if (a.lse && l == 0) a.lse[(int64_t)r * a.Hq + h] = M + fast_log2(L) * kLn2;
-}
 
 }  // namespace
 
@@ -671,7 +907,7 @@ __global__ __launch_bounds__(kOrderThreads) void csr_order_kernel(const int32_t*
 }
 
 void build_csr(const msa_plan_s* p, const DevMeta& m, const int32_t* sel, char* ws, int32_t w0, int32_t w1,
-               hipStream_t st, bool sorted = false) {
+               hipStream_t st, bool sorted, bool with_local) {
   const PlanLayout& L = p->lay;
   const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
   const int32_t nkey = Hkv * p->NB;
@@ -698,6 +934,7 @@ void build_csr(const msa_plan_s* p, const DevMeta& m, const int32_t* sel, char* 
   c.w1 = w1;
   c.Hkv = Hkv;
   c.k = k;
+  c.with_local = with_local ? 1 : 0;
   const dim3 cgrid((unsigned)((w1 - w0 + 255) / 256), (unsigned)Hkv);
   const bool lds_hist = p->NB <= kMaxLdsBins;
   const size_t hist_bytes = lds_hist ? (size_t)p->NB * 4 : 0;
@@ -732,7 +969,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   const int32_t* entries = reinterpret_cast<const int32_t*>(ws + L.entries);
   const int4* items = reinterpret_cast<const int4*>(ws + L.items);
   const int32_t* nitems = reinterpret_cast<const int32_t*>(ws + L.nitems);
-  build_csr(p, m, sel, ws, w0, w1, st);
+  // a row's own block is computed by local_merge_kernel, not as an entry
+  build_csr(p, m, sel, ws, w0, w1, st, /*sorted=*/false, /*with_local=*/false);
 
   PartialArgs a;
   a.q = static_cast<const uint8_t*>(q);
@@ -778,7 +1016,13 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
       hipExtLaunchKernelGGL(partial_attn_kernel<KvFmt::BF16>, grid, blk, 0, st, pe.start, pe.stop, 0, a);
   }
 
-  MergeArgs mg;
+  LocalMergeArgs mg;
+  mg.q = a.q;
+  mg.kp = a.kp;
+  mg.vp = a.vp;
+  mg.ks = ks;
+  mg.vs = vs;
+  mg.kv_indices = kv_indices;
   mg.sel = sel;
   mg.m = m;
   mg.part_pk = a.part_pk;
@@ -792,12 +1036,26 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   mg.k = k;
   mg.w0 = w0;
   mg.w1 = w1;
-  const int64_t npairs = (int64_t)(w1 - w0) * Hq;
+  mg.scale_log2 = a.scale_log2;
   {
+    // one workgroup per (block, group, 128 of the block's rows x G heads)
+    // over the blocks that hold the window's rows: rows go sequence by
+    // sequence and position by position, so those blocks are the global
+    // blocks gb(w0) .. gb(w1 - 1)
+    auto gb_of_row = [&](int32_t r) {
+      const int sq = (int)(std::upper_bound(p->row_start.begin(), p->row_start.end(), r) - p->row_start.begin()) - 1;
+      return p->page_start[sq] + (p->kv[sq] - p->qo[sq] + (r - p->row_start[sq])) / 128;
+    };
+    const int32_t gb_lo = gb_of_row(w0), gb_hi = gb_of_row(w1 - 1);
+    mg.key0 = gb_lo * Hkv;
     ProfEvents pe(p, "merge");
-    constexpr int kPairsPerBlock = 256 / kMergeLanes;
-    hipExtLaunchKernelGGL(merge_kernel, dim3((unsigned)((npairs + kPairsPerBlock - 1) / kPairsPerBlock)), dim3(256), 0,
-                          st, pe.start, pe.stop, 0, mg);
+    const dim3 grid((unsigned)((int64_t)(gb_hi - gb_lo + 1) * Hkv * p->G)), blk(256);
+    if (p->d.kv_dtype == MSA_MXFP4)
+      hipExtLaunchKernelGGL(local_merge_kernel<KvFmt::MX4>, grid, blk, 0, st, pe.start, pe.stop, 0, mg);
+    else if (p->d.kv_dtype == MSA_FP8_E4M3)
+      hipExtLaunchKernelGGL(local_merge_kernel<KvFmt::FP8>, grid, blk, 0, st, pe.start, pe.stop, 0, mg);
+    else
+      hipExtLaunchKernelGGL(local_merge_kernel<KvFmt::BF16>, grid, blk, 0, st, pe.start, pe.stop, 0, mg);
   }
   return hipGetLastError();
 }
@@ -1177,11 +1435,11 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(DqSumArgs a) {
 }
 
 // dq = the sum over a row's slots of its block-floating-point partials
-// (bwd_dq): 8 lanes per (row, head), laid out like the forward merge's (lane
-// l: dword l of each plane, dims 32 dt + 8 gq + 4 h + t for h = l / 4,
-// dt = l % 4), slots 8 at a time; a slot counts when its block is at most
-// the row's local block (bwd_dq wrote nothing for the others: their step
-// is taken as 0).  topk <= 64.
+// (bwd_dq): 8 lanes per (row, head), each reading its dword of the planes
+// (load_bfp_rec), slots 8 at a time, the first 8 slots' records issued before
+// anything else; lane l of the 8 reads slot l's block id (coalesced) and a
+// slot counts when its block is at most the row's local block (bwd_dq wrote
+// nothing for the others: their step is taken as 0).  topk <= 64.
 struct DqBfpSumArgs {
   const int32_t* sel;
   DevMeta m;
@@ -1716,7 +1974,7 @@ hipError_t launch_prefill_backward_window(const msa_plan_s* p, const DevMeta& m,
   const PlanLayout& L = p->lay;
   const int Hkv = p->d.num_kv_heads, Hq = p->d.num_qo_heads, k = p->d.topk;
   const int32_t nkey = Hkv * p->NB;
-  build_csr(p, m, sel, ws, w0, w1, st, /*sorted=*/true);
+  build_csr(p, m, sel, ws, w0, w1, st, /*sorted=*/true, /*with_local=*/true);
   float* D = reinterpret_cast<float*>(ws + L.bwd_d);
   const int64_t npairs = (int64_t)(w1 - w0) * Hq;
   {

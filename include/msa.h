@@ -115,7 +115,8 @@ typedef struct {
   msa_mode_t mode;             /* which entry points the plan serves */
   int64_t max_rows_per_call;   /* prefill: rows per proxy/top-k call; 0 = min(T, 32768) */
   int64_t attn_window_rows;    /* prefill: rows whose attention partials are live at
-                                  once (workspace scales with it); 0 = automatic */
+                                  once (workspace scales with it); 0 = automatic.
+                                  Capped at (2^27 - 256) / (num_qo_heads * topk) */
   int32_t decode_splits;       /* decode: workgroups sharing one (sequence, group),
                                   merged by log-sum-exp; 0 = automatic, else 1..64 */
 } msa_plan_desc_t;

@@ -51,6 +51,17 @@ def test_plan_info_and_workspace():
     assert d.total_rows == 4 and d.nb_max == 8
 
 
+def test_window_capped_to_32bit_planes():
+    # a plane of partial records (32 bytes each, rows x heads x topk plus 256
+    # spare records) stays under 2^32 bytes: 64 heads, topk 64 -> 32767 rows
+    def ws(w):
+        return msa.msa_plan([40000], [40000], 64, 8, 8, 8, topk=64, attn_window_rows=w,
+                            allocate=False).workspace_bytes
+    cap = ((1 << 27) - 256) // (64 * 64)
+    assert cap == 32767
+    assert ws(40000) == ws(cap) > ws(cap - 1)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), msa.MSA_ERR_UNSUPPORTED),
     (dict(page_size=64), msa.MSA_ERR_UNSUPPORTED),
