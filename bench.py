@@ -39,9 +39,10 @@ PROXY_PEAK = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "mxfp4": PEAK_FP
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "bwd_dq": "sparse_prefill.hip", "bwd_dkv": "sparse_prefill.hip", "bwd_dq_sum": "sparse_prefill.hip",
+    "bwd_dq_sum_bfp": "sparse_prefill.hip",
     "proxy_maxscore": "proxy_maxscore.hip", "topk_select": "topk_select.hip", "proxy_topk": "proxy_maxscore.hip",
     "csr": "sparse_prefill.hip",
-    "partial_attn": "sparse_prefill.hip", "merge": "sparse_prefill.hip", "decode": "sparse_decode.hip",
+    "partial_attn": "sparse_prefill.hip", "local_merge": "sparse_prefill.hip", "decode": "sparse_decode.hip",
     "decode_merge": "sparse_decode.hip", "proxy_onerow": "proxy_maxscore.hip",
     "proxy_onerow_mxfp4": "proxy_maxscore.hip", "topk_wave": "topk_select.hip",
     "topk_wave_exact": "topk_select.hip", "topk_refine": "proxy_maxscore.hip",
