@@ -141,6 +141,20 @@ __device__ __forceinline__ void global_load_lds16(const void* g, MSA_LDS void* l
 #endif
 }
 
+// The same load issued from inline assembly, so that the compiler does not
+// track it: it then puts no wait for it before the following LDS reads,
+// which it cannot tell apart from the load's destination (and would make
+// wait for the load right after its issue).  No register receives data; M0
+// is set in the same block (one wait state before the load reads it).  The
+// caller orders the load before every read of its destination itself: a
+// vmcnt wait for it, then a barrier.
+__device__ __forceinline__ void global_load_lds16_untracked(const void* g, MSA_LDS void* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(g) : "memory", "m0");
+#endif
+}
+
 // Wait for all outstanding vector memory operations only (loads and stores;
 // on this architecture one counter covers both, in issue order).
 __device__ __forceinline__ void wait_vmem() {

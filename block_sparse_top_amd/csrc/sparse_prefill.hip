@@ -1684,17 +1684,19 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
   };
   // tiles of buffer `buf`: q, dO, (KL) proxy q
   auto tile = [&](int kind, int buf) { return gsm + (2 * kind + buf) * kTile; };
+  // (untracked by the compiler: it would wait for them before the current
+  // chunk's first LDS read; the wait before the next barrier orders them)
   auto issue_rows = [&](int32_t ea, int32_t eb, int buf) {
     uint8_t* const w0b = tile(0, buf) + 2048 * wave;
     uint8_t* const w1b = tile(1, buf) + 2048 * wave;
-    global_load_lds16(row_src(a.q, ea, ri0, lc0), (MSA_LDS void*)w0b);
-    global_load_lds16(row_src(a.q, eb, ri1, lc1), (MSA_LDS void*)(w0b + 1024));
-    global_load_lds16(row_src(a.dout, ea, ri0, lc0), (MSA_LDS void*)w1b);
-    global_load_lds16(row_src(a.dout, eb, ri1, lc1), (MSA_LDS void*)(w1b + 1024));
+    global_load_lds16_untracked(row_src(a.q, ea, ri0, lc0), (MSA_LDS void*)w0b);
+    global_load_lds16_untracked(row_src(a.q, eb, ri1, lc1), (MSA_LDS void*)(w0b + 1024));
+    global_load_lds16_untracked(row_src(a.dout, ea, ri0, lc0), (MSA_LDS void*)w1b);
+    global_load_lds16_untracked(row_src(a.dout, eb, ri1, lc1), (MSA_LDS void*)(w1b + 1024));
     if constexpr (KL) {
       uint8_t* const w2b = tile(2, buf) + 2048 * wave;
-      global_load_lds16(prow_src(ea, lc0), (MSA_LDS void*)w2b);
-      global_load_lds16(prow_src(eb, lc1), (MSA_LDS void*)(w2b + 1024));
+      global_load_lds16_untracked(prow_src(ea, lc0), (MSA_LDS void*)w2b);
+      global_load_lds16_untracked(prow_src(eb, lc1), (MSA_LDS void*)(w2b + 1024));
     }
   };
   i32x4 rr[KL ? 6 : 1];  // KL: the next chunk's q, dO and proxy q pieces of rows ri0, ri1
