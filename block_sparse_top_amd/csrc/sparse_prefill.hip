@@ -1555,15 +1555,19 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
   // every chunk's S and dP products (with the proxy term, one wave per SIMD
   // has the registers to hold its keys' K and V rows instead).  Then per
   // group and buffer: the chunk's q rows, dO rows and (KL) proxy q rows (row
-  // i: token i / G), rt_swz.  The first 128 KB hold the second group's
-  // partials for the final sum.
+  // i: token i / G), rt_swz; two buffers, three for the second group (its
+  // dV / dK products of a chunk run one iteration late, below).  The first
+  // 128 KB hold the second group's partials for the final sum.
+  constexpr int kKinds = KL ? 3 : 2;
   constexpr int kKvBytes = KL ? 0 : 2 * 128 * 256;
-  constexpr int kGroupBytes = 2 * (KL ? 3 : 2) * kTile;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kKvBytes + kGroups * kGroupBytes];
+  constexpr int kGroupBytes = 2 * kKinds * kTile;   // the first group's
+  constexpr int kBufs1 = 3;                          // the second group's buffers
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kKvBytes + kGroupBytes + (kGroups - 1) * kBufs1 * kKinds * kTile];
   __shared__ __attribute__((aligned(16))) float l2_s[kGroups][2][32];
   __shared__ __attribute__((aligned(16))) float d_s[kGroups][2][32];
   __shared__ __attribute__((aligned(16))) int32_t pos_s[kGroups][2][32];
-  static_assert(KL || kKvBytes + kGroups * kGroupBytes >= 4 * 8 * 16 * 64 * 4, "partials fit the tiles' space");
+  static_assert(KL || kKvBytes + kGroupBytes + kBufs1 * kKinds * kTile >= 4 * 8 * 16 * 64 * 4,
+                "partials fit the tiles' space");
   uint8_t* const kv_k = smem;
   uint8_t* const kv_v = smem + (KL ? 0 : 128 * 256);
   // block-major order: the early, most selected blocks of every group start first
@@ -1683,7 +1687,8 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
     return a.pq + ((int64_t)(a.w0 + (ent >> 6)) * a.Hkv + g) * 256 + lc * 16;
   };
   // tiles of buffer `buf`: q, dO, (KL) proxy q
-  auto tile = [&](int kind, int buf) { return gsm + (2 * kind + buf) * kTile; };
+  const int nbufs = grp == 1 ? kBufs1 : 2;
+  auto tile = [&](int kind, int buf) { return gsm + (nbufs * kind + buf) * kTile; };
   // (untracked by the compiler: it would wait for them before the current
   // chunk's first LDS read; the wait before the next barrier orders them)
   auto issue_rows = [&](int32_t ea, int32_t eb, int buf) {
@@ -1735,16 +1740,18 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
     ea = entry_of(chunk_of(1), ri0);
     eb = entry_of(chunk_of(1), ri1);
     es = gtid < 32 ? entry_of(chunk_of(1), gtid) : 0;
-    auto step = [&](int it) __attribute__((always_inline)) {
-      const int buf = it & 1;
-      const uint8_t* const qb = tile(0, buf);
-      const uint8_t* const db = tile(1, buf);
-      const uint8_t* const pb = tile(2, buf);  // KL only
-      store_rows(buf);
+    // One chunk in phases.  head: the chunk's row values to LDS, the barrier
+    // after which its rows are in LDS (and every wave is done with the buffer
+    // the next chunk fills), the next chunk's loads; products: S, dP, then P
+    // and dS as bf16 A operands; update: dV += P^T dO, dK += dS^T Q.  tb is
+    // the chunk's tile buffer, the row values' buffer is it & 1.
+    auto head = [&](int it, int tb, int tb_next) __attribute__((always_inline)) {
+      const int rb = it & 1;
+      store_rows(tb);
       if (gtid < 32) {
-        l2_s[grp][buf][gtid] = rlse * kLog2e;
-        d_s[grp][buf][gtid] = rdd;
-        pos_s[grp][buf][gtid] = rpos;
+        l2_s[grp][rb][gtid] = rlse * kLog2e;
+        d_s[grp][rb][gtid] = rdd;
+        pos_s[grp][rb][gtid] = rpos;
       }
       const int cn = chunk_of(it + 1);
       if constexpr (KL) load_rows(ea, eb);
@@ -1753,7 +1760,7 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
       // wave is done with the previous chunk, whose buffer the next one fills
       if constexpr (!KL) wait_vmem();
       lds_barrier();
-      if constexpr (!KL) issue_rows(ea, eb, buf ^ 1);
+      if constexpr (!KL) issue_rows(ea, eb, tb_next);
       if (gtid < 32) {
         const int h = g * G + gtid % G;
         rlse = a.lse[(int64_t)(a.w0 + (es >> 6)) * a.Hq + h];
@@ -1763,6 +1770,11 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
       ea = entry_of(chunk_of(it + 2), ri0);
       eb = entry_of(chunk_of(it + 2), ri1);
       es = gtid < 32 ? entry_of(chunk_of(it + 2), gtid) : 0;
+    };
+    auto products = [&](int it, int tb, bf16x8 (&pf)[2], bf16x8 (&sf)[2]) __attribute__((always_inline)) {
+      const int buf = it & 1;
+      const uint8_t* const qb = tile(0, tb);
+      const uint8_t* const db = tile(1, tb);
       // the rows' lse, D and positions as 4-row runs (register r of the
       // products below holds row 8(r/4) + 4 half + r%4): with the proxy term
       // (registers to spare, one wave per SIMD) read before the products,
@@ -1803,7 +1815,6 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
         }
       }
       // P and dS as bf16 A operands
-      bf16x8 pf[2], sf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         i32x4 pw, sw;
@@ -1830,6 +1841,11 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
         pf[u] = __builtin_bit_cast(bf16x8, pw);
         sf[u] = __builtin_bit_cast(bf16x8, sw);
       }
+    };
+    auto update = [&](int tb, const bf16x8 (&pf)[2], const bf16x8 (&sf)[2]) __attribute__((always_inline)) {
+      const uint8_t* const qb = tile(0, tb);
+      const uint8_t* const db = tile(1, tb);
+      const uint8_t* const pb = tile(2, tb);  // KL only
       // dV += P^T dO, dK += dS^T Q: dO and Q read transposed, rows in the same order
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -1849,27 +1865,61 @@ __global__ __launch_bounds__(bwd_dkv_threads<KL>()) void bwd_dkv_kernel(BwdKvArg
         }
       }
     };
-    const int it_split = KL ? n_even : niter;
-    for (int it = 0; it < it_split; ++it) step(it);
-    if constexpr (KL) {
-      if (n_even < nchunks) {  // the even chunks are done: park their dK / dV partials
+    bool late = false;   // the second group: each chunk's update one iteration late
+    if constexpr (kGroups == 2) late = grp == 1;
+    if (!late) {
+      auto step = [&](int it) __attribute__((always_inline)) {
+        const int tb = it & 1;
+        head(it, tb, tb ^ 1);
+        bf16x8 pf[2], sf[2];
+        products(it, tb, pf, sf);
+        update(tb, pf, sf);
+      };
+      const int it_split = KL ? n_even : niter;
+      for (int it = 0; it < it_split; ++it) step(it);
+      if constexpr (KL) {
+        if (n_even < nchunks) {  // the even chunks are done: park their dK / dV partials
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+          for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            stash[(dt * 16 + r) * 64] = dkacc[dt][r];
-            stash[((4 + dt) * 16 + r) * 64] = dvacc[dt][r];
-          }
+            for (int r = 0; r < 16; ++r) {
+              stash[(dt * 16 + r) * 64] = dkacc[dt][r];
+              stash[((4 + dt) * 16 + r) * 64] = dvacc[dt][r];
+            }
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
+          for (int dt = 0; dt < 4; ++dt) dkacc[dt] = dvacc[dt] = f32x16{};
+        }
+        for (int it = it_split; it < niter; ++it) step(it);
       }
-      for (int it = it_split; it < niter; ++it) step(it);
+    } else if constexpr (kGroups == 2) {
+      // Both groups pass the same barrier every chunk; with the same order of
+      // phases the two waves of a SIMD (one per group) would run their
+      // products and their vector work at the same time.  This group runs a
+      // chunk's update after the next chunk's barrier, while the first group
+      // runs its S and dP products, and its P / dS work while the first group
+      // runs its update.  Three tile buffers: chunk it in it % 3 (the update
+      // of chunk it - 1 reads its buffer while chunk it + 1's rows land).
+      // The sums are the same, chunk by chunk in the same order.
+      bf16x8 pf[2], sf[2];
+      int tb = 0;
+      for (int it = 0; it < niter; ++it) {
+        const int tb_next = tb == kBufs1 - 1 ? 0 : tb + 1;
+        head(it, tb, tb_next);
+        if (it > 0) update(tb == 0 ? kBufs1 - 1 : tb - 1, pf, sf);
+        products(it, tb, pf, sf);
+        tb = tb_next;
+      }
+      update(tb == 0 ? kBufs1 - 1 : tb - 1, pf, sf);
     }
   }
   if constexpr (kGroups == 2) {
     // the second group's partials -> LDS (over the tiles), added by the first
     // group in a fixed order: [wave][tile: dK 0-3, dV 0-3][register][lane]
     float* const red = reinterpret_cast<float*>(smem);
+    // the last chunk's loads of the next (padding) rows may still be in
+    // flight into the tiles' space: every wave waits for its own, then the
+    // barrier for everyone's
+    wait_vmem();
     __syncthreads();  // every wave is done with the tiles
     if (grp == 1) {
 #pragma unroll
