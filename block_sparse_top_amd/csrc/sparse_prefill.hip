@@ -489,12 +489,13 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
 // The local block of every row inside the merge.  Each row's own
 // (diagonal) block is computed here rather than as a slot of partial_attn:
 // one workgroup per (KV group, block, 128 rows of the block's own query rows
-// x G heads), whose Q rows are contiguous (no gather), whose key tiles past
-// a wave's last row are skipped, and whose result stays in registers: the
-// row's other slots' partial records (bfp) are then added to it with the
-// usual log-sum-exp weights, and the output row is written.  A lane holds
-// the dims of its row that store_rows_bfp10 packed from the same lane
-// position, so a slot's record is one 16-byte load per plane.
+// x G heads), whose Q rows are contiguous (no gather) and whose key tiles
+// past a wave's last row are skipped.  The row's other slots' partial
+// records (bfp) are summed first, against their own maximum log-sum-exp,
+// while the block's K and V rows land in LDS; the local block comes last,
+// its weight folded into its P, and its products add onto the slots' sum.
+// A lane holds the dims of its row that store_rows_bfp10 packed from the
+// same lane position, so a slot's record is one 16-byte load per plane.
 struct LocalMergeArgs {
   const uint8_t* q;      // bf16 [T, Hq, 128]
   const uint8_t* kp;     // K / V pages (format F)
@@ -518,6 +519,8 @@ template <KvFmt F>
 __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];
+  constexpr int kBatch = 16;
+  __shared__ float ws_s[kBatch * 256];           // slot weights, [slot][thread]: each lane its own
   const int G = a.G;
   // workgroups are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8):
   // XCD x takes the x-th eighth of the launch's (block, group) keys, so that
@@ -541,28 +544,44 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
   if (t0 >= t_hi) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t page = a.kv_indices[gb];
-  {  // K and V block -> LDS as bf16 (as partial_attn): the 32-key tiles
-     // that the workgroup's last row sees, 16 keys per pass
+  // K and V of the block -> LDS as bf16 (as partial_attn): the 16-key passes
+  // that the workgroup's last row sees
+  {
     constexpr int64_t kPageBytes = F == KvFmt::BF16 ? 32768 : F == KvFmt::FP8 ? 16384 : 128 * 64 + 128 * 4;
     const uint8_t* kb = a.kp + ((int64_t)page * a.Hkv + g) * kPageBytes;
     const uint8_t* vb = a.vp + ((int64_t)page * a.Hkv + g) * kPageBytes;
     const int passes = 2 * ((min(t0 + MT, t_hi) - 1) / 32 + 1);
-    i32x4 kr[8], vr[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < passes) {
-        const int cc = tid + 256 * i;
-        kr[i] = load_kv8<F>(kb, cc >> 4, cc & 15);
-        vr[i] = load_kv8<F>(vb, cc >> 4, cc & 15);
-      }
-    }
     const int kv_in_block = a.m.kv[s] - b * 128;  // rows at or past this are page padding
+    if constexpr (F == KvFmt::BF16) {
+      // straight from global memory (untracked direct loads, waited for
+      // before the local block's products, after the merge): one wave
+      // instruction fills 4 rows; lane l physical chunk l % 16 of row
+      // 4 i + l / 16, i.e. fetches the logical chunk the swizzle puts there.
+      // Page padding rows fetch the block's last key row instead (finite;
+      // every query row's mask hides them).
+      for (int i = wave; i < 4 * passes; i += 4) {
+        const int krow = 4 * i + (lane >> 4), pc = lane & 15;
+        const int srow = min(krow, kv_in_block - 1);
+        global_load_lds16_untracked(kb + srow * 256 + ((pc ^ (krow & 15)) << 4), (MSA_LDS void*)(ks + 1024 * i));
+        global_load_lds16_untracked(vb + srow * 256 + ((pc ^ ((krow & 3) << 2)) << 4), (MSA_LDS void*)(vs + 1024 * i));
+      }
+    } else {  // widened to bf16 on the way (through registers)
+      i32x4 kr[8], vr[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < passes) {
-        const int cc = tid + 256 * i;
-        lds_store16<i32x4>(&ks[k_swz(cc >> 4, cc & 15)], kr[i]);
-        lds_store16<i32x4>(&vs[v_swz(cc >> 4, cc & 15)], (cc >> 4) < kv_in_block ? vr[i] : i32x4{});
+      for (int i = 0; i < 8; ++i) {
+        if (i < passes) {
+          const int cc = tid + 256 * i;
+          kr[i] = load_kv8<F>(kb, cc >> 4, cc & 15);
+          vr[i] = load_kv8<F>(vb, cc >> 4, cc & 15);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < passes) {
+          const int cc = tid + 256 * i;
+          lds_store16<i32x4>(&ks[k_swz(cc >> 4, cc & 15)], kr[i]);
+          lds_store16<i32x4>(&vs[v_swz(cc >> 4, cc & 15)], (cc >> 4) < kv_in_block ? vr[i] : i32x4{});
+        }
       }
     }
   }
@@ -576,25 +595,22 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
   const int h = g * G + hh;
   const float scale_log2 = F == KvFmt::FP8 ? a.scale_log2 * a.ks[g] : a.scale_log2;
   const float v_scale = F == KvFmt::FP8 ? a.vs[g] : 1.f;
-  const int q16 = lane >> 4, m16 = lane & 15;
-  int kbase[8];
-#pragma unroll
-  for (int st = 0; st < 8; ++st) kbase[st] = (lane & 31) * 256 + (((2 * st + half) ^ (lane & 15)) << 4);
-  int vbase[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-    vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
-                ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  // Q fragments: requested now, used by the local block's products last
   bf16x8 qf[8];
   {
     const uint8_t* qrow = a.q + ((int64_t)r * a.Hq + h) * 256 + half * 16;
 #pragma unroll
     for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + st * 32);
   }
-  // The row's other slots (blocks 0 <= blk < b; the local block is b): the
-  // first 16 slots' block ids and {lse, step} are requested now and arrive
-  // while the local block is computed.
-  constexpr int kBatch = 16;
+
+  // The row's other slots first (blocks 0 <= blk < b; the local block is b),
+  // against their own maximum Ms: oacc = sum_s w_s rec_s step_s with
+  // w_s = exp(lse_s - Ms), Ls = sum_s w_s.  Their {lse, step}, 16 slots per
+  // batch of loads; each slot's weight goes to LDS ([slot][thread]) and the
+  // records are added one slot after another, each loaded three slots ahead.
+  // A slot that holds no record weighs 0: its stats may hold anything, NaN
+  // too, and are not read into the result; its (unwritten) record is
+  // integers, always finite, and adds exactly 0.
   const int32_t rl = r - a.w0;
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   const float2* st_row = a.part_st + ((int64_t)rl * a.Hq + h) * a.k;
@@ -641,111 +657,23 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
     w[3] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane3 + off));
     w[4] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane4 + off));
   };
+  float Ms = kNegInf;
   int blk0[kBatch];
   float2 ls0[kBatch];
   load_stats(0, blk0, ls0);
-  // key tiles holding a visible key of some row of the wave: its rows are
-  // consecutive tokens, the last one sees keys 0 .. its t
-  int tmax = tt;
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) tmax = max(tmax, __shfl_xor(tmax, o));
-  const int nkt = __builtin_amdgcn_readfirstlane(min(4, (tmax >> 5) + 1));  // the same in every lane
-  const int lim = tt - 4 * half;                 // last visible key offset, minus the lane's 4-key shift
-  __syncthreads();
-
-  // S^T = K Q^T on the live tiles; K fragments one k-step ahead
-  f32x16 acc[4];
-  {
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      if (kt < nkt) kf[0][kt] = lds_load16<bf16x8>(&ks[kbase[0] + 8192 * kt]);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (st + 1 < 8) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          if (kt < nkt) kf[(st + 1) & 1][kt] = lds_load16<bf16x8>(&ks[kbase[st + 1] + 8192 * kt]);
-      }
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        if (kt < nkt) acc[kt] = mfma32x32x16(kf[st & 1][kt], qf[st], st == 0 ? f32x16{} : acc[kt]);
-    }
-  }
-  // causal mask (hidden scores -inf), row max, p = exp2(s * scale - max)
-  float mraw = kNegInf;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-    if (kt < nkt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) acc[kt][i] = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mraw = max3f(mraw, acc[kt][i], acc[kt][i + 1]);
-    }
-  mraw = wave_max32(mraw);
-  const float mx = mraw * scale_log2;
-  float sum = 0.f;
-  f32x16 oacc[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    if (kt < nkt) {
-      bf16x8 pf[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        i32x4 pw;
-#pragma unroll
-        for (int tq = 0; tq < 4; ++tq) {
-          const float p0 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * tq], scale_log2, -mx));
-          const float p1 = fast_exp2(__builtin_fmaf(acc[kt][8 * u + 2 * tq + 1], scale_log2, -mx));
-          sum += p0 + p1;
-          const bf16x2 two = {(__bf16)p0, (__bf16)p1};
-          pw[tq] = __builtin_bit_cast(int, two);
-        }
-        pf[u] = __builtin_bit_cast(bf16x8, pw);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const s16x4 lo = lds_read_tr16(&vs[vbase[dt] + 256 * (32 * kt + 16 * u)]);
-          const s16x4 hi = lds_read_tr16(&vs[vbase[dt] + 256 * (32 * kt + 16 * u + 8)]);
-          oacc[dt] = mfma32x32x16(join_tr16(lo, hi), pf[u], kt == 0 && u == 0 ? f32x16{} : oacc[dt]);
-        }
-      }
-    }
-  }
-  sum = wave_sum32(sum);  // >= 1: the row max contributes exp2(0)
-
-  // The slots' max M over the local block and the counted slots, then per
-  // batch of 16 slots each one's weight exp(lse - M) * step goes to LDS (the
-  // K/V tiles are no longer needed; [slot][thread], conflict-free) and the
-  // records are added one slot after another, each loaded three slots ahead
-  // (one workgroup's waves alone keep the memory system busy while the other
-  // workgroup on the compute unit is in its local block).
-  // A slot that holds no record weighs 0: its stats may hold anything, NaN
-  // too, and are not read into the result; its (unwritten) record is
-  // integers, always finite, and adds exactly 0.
-  const float lse_loc = (mx + fast_log2(sum)) * kLn2;  // natural log
-  float M = lse_loc;
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    if (blk0[j] >= 0 && blk0[j] < b) M = fmaxf(M, ls0[j].x);
+    if (blk0[j] >= 0 && blk0[j] < b) Ms = fmaxf(Ms, ls0[j].x);
   for (int s0 = kBatch; s0 < a.k; s0 += kBatch) {
     int blk[kBatch];
     float2 ls[kBatch];
     load_stats(s0, blk, ls);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
-      if (blk[j] >= 0 && blk[j] < b) M = fmaxf(M, ls[j].x);
+      if (blk[j] >= 0 && blk[j] < b) Ms = fmaxf(Ms, ls[j].x);
   }
-  const float w_loc = fast_exp2((lse_loc - M) * kLog2e);
-  float L = w_loc;
-  const float f_loc = v_scale * w_loc / sum;   // oacc holds sum_j p_j v_j (unscaled V for fp8)
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[dt][i] *= f_loc;
+  float Ls = 0.f;
+  f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   // field j of group dt: bits 10 j .. of the 160-bit group made of plane
   // words w[0..4][dt] (as bfp_field)
   auto field = [&](const i32x4 (&w)[5], int dt, int j) -> float {
@@ -760,26 +688,24 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) oacc[dt][j] = __builtin_fmaf(ws, field(w, dt, j), oacc[dt][j]);
   };
-  auto put_weights = [&](const int (&blk)[kBatch], const float2 (&ls)[kBatch], float* ws_s) {
+  auto put_weights = [&](const int (&blk)[kBatch], const float2 (&ls)[kBatch]) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const bool in = blk[j] >= 0 && blk[j] < b;
-      const float w = in ? fast_exp2((ls[j].x - M) * kLog2e) : 0.f;
-      L += w;
+      const float w = in ? fast_exp2((ls[j].x - Ms) * kLog2e) : 0.f;
+      Ls += w;
       ws_s[j * 256 + tid] = in ? w * ls[j].y : 0.f;  // this lane's own slot weights
     }
   };
-  __syncthreads();  // every wave is done with the K/V tiles
-  float* const ws_s = reinterpret_cast<float*>(ks);   // [kBatch][256]
   i32x4 rb[4][5];  // records of four consecutive slots, slot j in rb[j % 4]
   rec_load(0, rb[0]);
-  put_weights(blk0, ls0, ws_s);
+  put_weights(blk0, ls0);
   for (int s0 = 0; s0 < a.k; s0 += kBatch) {
     if (s0 > 0) {
       int blk[kBatch];
       float2 ls[kBatch];
       load_stats(s0, blk, ls);
-      put_weights(blk, ls, ws_s);
+      put_weights(blk, ls);
       rec_load(s0, rb[0]);
     }
     // the batch's slots padded to a multiple of 4: a padding slot re-reads
@@ -803,6 +729,110 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
     for (int u = 0; u < 4; ++u) {
       add_rec(rb[u], ws_s[(j + u) * 256 + tid]);
       __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // The local block, into the same accumulators.  Its K and V rows are in
+  // LDS (each wave waits for its own direct loads, the barrier for
+  // everyone's; for the register path the barrier orders the stores).
+  if constexpr (F == KvFmt::BF16) wait_vmem();
+  __syncthreads();
+  const int q16 = lane >> 4, m16 = lane & 15;
+  int kbase[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) kbase[st] = (lane & 31) * 256 + (((2 * st + half) ^ (lane & 15)) << 4);
+  int vbase[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    vbase[dt] = (4 * (q16 >> 1) + (m16 >> 2)) * 256 +
+                ((4 * (dt ^ (m16 >> 2)) + 2 * (q16 & 1) + ((m16 & 3) >> 1)) << 4) + 8 * (m16 & 1);
+  // key tiles holding a visible key of some row of the wave: its rows are
+  // consecutive tokens, the last one sees keys 0 .. its t
+  int tmax = tt;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) tmax = max(tmax, __shfl_xor(tmax, o));
+  const int nkt = __builtin_amdgcn_readfirstlane(min(4, (tmax >> 5) + 1));  // the same in every lane
+  const int lim = tt - 4 * half;                 // last visible key offset, minus the lane's 4-key shift
+
+  // S^T = K Q^T on the live tiles; K fragments one k-step ahead
+  f32x16 acc[4];
+  {
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      if (kt < nkt) kf[0][kt] = lds_load16<bf16x8>(&ks[kbase[0] + 8192 * kt]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          if (kt < nkt) kf[(st + 1) & 1][kt] = lds_load16<bf16x8>(&ks[kbase[st + 1] + 8192 * kt]);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        if (kt < nkt) acc[kt] = mfma32x32x16(kf[st & 1][kt], qf[st], st == 0 ? f32x16{} : acc[kt]);
+    }
+  }
+  // causal mask (hidden scores -inf), row max, p = exp2(s * scale - max) in place
+  float mraw = kNegInf;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+    if (kt < nkt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) acc[kt][i] = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mraw = max3f(mraw, acc[kt][i], acc[kt][i + 1]);
+    }
+  mraw = wave_max32(mraw);
+  const float mx = mraw * scale_log2;
+  float sum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+    if (kt < nkt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc[kt][i] = fast_exp2(__builtin_fmaf(acc[kt][i], scale_log2, -mx));
+        sum += acc[kt][i];
+      }
+    }
+  sum = wave_sum32(sum);  // >= 1: the row max contributes exp2(0)
+  // weights: the slots' exp(Ms - M), the local block's exp(lse_loc - M) / sum
+  // (folded into its P before the bf16 rounding, with fp8's V scale)
+  const float lse_loc = (mx + fast_log2(sum)) * kLn2;  // natural log
+  const float M = fmaxf(Ms, lse_loc);
+  const float alpha = fast_exp2((Ms - M) * kLog2e);    // 0 without a counted slot
+  const float beta = fast_exp2((lse_loc - M) * kLog2e);
+  const float L = Ls * alpha + beta;
+  const float f_loc = v_scale * beta / sum;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+  // O^T += V^T P^T on the live tiles
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    if (kt < nkt) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        i32x4 pw;
+#pragma unroll
+        for (int tq = 0; tq < 4; ++tq) {
+          const bf16x2 two = {(__bf16)(acc[kt][8 * u + 2 * tq] * f_loc), (__bf16)(acc[kt][8 * u + 2 * tq + 1] * f_loc)};
+          pw[tq] = __builtin_bit_cast(int, two);
+        }
+        pf[u] = __builtin_bit_cast(bf16x8, pw);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const s16x4 lo = lds_read_tr16(&vs[vbase[dt] + 256 * (32 * kt + 16 * u)]);
+          const s16x4 hi = lds_read_tr16(&vs[vbase[dt] + 256 * (32 * kt + 16 * u + 8)]);
+          oacc[dt] = mfma32x32x16(join_tr16(lo, hi), pf[u], oacc[dt]);
+        }
+      }
     }
   }
   if (!row_ok) return;
