@@ -163,7 +163,7 @@ struct PartialArgs {
   DevMeta m;
   uint8_t* part_pk;      // partial records, block floating point (see store_rows_bfp10): five
   int64_t plane_stride;  //   planes of 32 bytes per record [rows, k, Hq] + trash records, this far apart
-  float2* part_st;       //   {log-sum-exp, step} [rows, Hq, k], then the trash entries
+  float2* part_st;       //   {log-sum-exp, step} per record, indexed as the records (then the trash entries)
   int64_t trash;         // index of the first of kTrashRecords trash records (rows * Hq * k)
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2;      // sm_scale * log2(e)
@@ -460,7 +460,10 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     const float step = store_rows_bfp10(oacc, v_scale * __builtin_amdgcn_rcpf(sum), a.part_pk, a.plane_stride,
                                        rec_index, lane);
     {  // both halves hold the row's max, sum and step and store the same value
-      const int64_t pi = valid ? ((int64_t)rl * a.Hq + h) * a.k + slot : trash;
+      // indexed as the records: a token's G heads are adjacent, so one store
+      // instruction writes G * 8 contiguous bytes per token (scattered 8-byte
+      // pieces, one per line, had cost the kernel an eighth of its time)
+      const int64_t pi = valid ? ((int64_t)rl * a.k + slot) * a.Hq + h : trash;
       a.part_st[pi] = float2{(mx + fast_log2(sum)) * kLn2, step};  // mx is already scaled
     }
   };
@@ -613,34 +616,26 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
   // integers, always finite, and adds exactly 0.
   const int32_t rl = r - a.w0;
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
-  const float2* st_row = a.part_st + ((int64_t)rl * a.Hq + h) * a.k;
-  // with k a multiple of 4 (and the selection 16-byte aligned) the rows of
-  // block ids and of {lse, step} go in 16-byte pieces
-  const bool vec_stats = (a.k & 3) == 0 && (reinterpret_cast<uintptr_t>(a.sel) & 15) == 0;
+  // {lse, step} of slot j: indexed as the records, Hq apart
+  const float2* st_row = a.part_st + (int64_t)rl * a.k * a.Hq + h;
+  // with k a multiple of 4 (and the selection 16-byte aligned) the row of
+  // block ids goes in 16-byte pieces
+  const bool vec_blk = (a.k & 3) == 0 && (reinterpret_cast<uintptr_t>(a.sel) & 15) == 0;
   auto load_stats = [&](int s0, int (&blk)[kBatch], float2 (&ls)[kBatch]) {
-    if (vec_stats) {
+    if (vec_blk) {
 #pragma unroll
       for (int j = 0; j < kBatch; j += 4) {
-        const int slot = min(s0 + j, a.k - 4);
-        const i32x4 bv = *reinterpret_cast<const i32x4*>(row + slot);
-        const f32x4 l01 = *reinterpret_cast<const f32x4*>(st_row + slot);
-        const f32x4 l23 = *reinterpret_cast<const f32x4*>(st_row + slot + 2);
+        const i32x4 bv = *reinterpret_cast<const i32x4*>(row + min(s0 + j, a.k - 4));
         const bool in = s0 + j < a.k;  // then all four are
 #pragma unroll
         for (int q = 0; q < 4; ++q) blk[j + q] = in ? bv[q] : -1;
-        ls[j] = float2{l01[0], l01[1]};
-        ls[j + 1] = float2{l01[2], l01[3]};
-        ls[j + 2] = float2{l23[0], l23[1]};
-        ls[j + 3] = float2{l23[2], l23[3]};
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int slot = min(s0 + j, a.k - 1);
-        blk[j] = s0 + j < a.k ? row[slot] : -1;
-        ls[j] = st_row[slot];
-      }
+      for (int j = 0; j < kBatch; ++j) blk[j] = s0 + j < a.k ? row[min(s0 + j, a.k - 1)] : -1;
     }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) ls[j] = st_row[(int64_t)min(s0 + j, a.k - 1) * a.Hq];
   };
   // a plane holds under 2^32 bytes (the plan caps the window): one 32-bit
   // offset per slot serves the five planes' uniform bases
