@@ -1148,7 +1148,7 @@ struct BwdDqArgs {
   DevMeta m;
   uint8_t* part_pk;       // dQ partials, block floating point (store_rows_bfp10): five planes of
   int64_t plane_stride;   //   32 bytes per record [W, k, Hq] + trash records, this far apart
-  float* part_step;       //   each record's step [W, Hq, k] + trash entries
+  float* part_step;       //   each record's step, indexed as the records (then the trash entries)
   int64_t trash;          // index of the first of kTrashRecords trash records
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2, sm_scale;
@@ -1364,8 +1364,10 @@ __global__ __launch_bounds__(256, KL ? 1 : 2) void bwd_dq_kernel(BwdDqArgs a) {
         return se < n_ent ? ((int64_t)(sent >> 6) * a.k + (sent & 63)) * a.Hq + head : trash;
       };
       const float step = store_rows_bfp10(oacc, a.sm_scale, a.part_pk, a.plane_stride, rec_index, lane);
-      // both halves hold the row's step and store the same value
-      a.part_step[se < n_ent ? ((int64_t)(sent >> 6) * a.Hq + head) * a.k + (sent & 63) : trash] = step;
+      // both halves hold the row's step and store the same value, at the
+      // record's index (a token's heads adjacent: one contiguous piece per
+      // token and store instruction)
+      a.part_step[rec_index(0)] = step;
     }
     if constexpr (KL) {
       // sum_j P_hj pk_j for this wave's rows (kacc: C[dim][row] = pk^T P^T),
@@ -1484,7 +1486,6 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_bfp_kernel(DqBfpSumArgs a) {
   const int h = (int)(id % a.Hq);
   const int g = h / a.G;
   const int32_t r = a.w0 + rl;
-  const int64_t base = ((int64_t)rl * a.Hq + h) * a.k;
   auto rec_of = [&](int slot) -> int64_t { return ((int64_t)rl * a.k + slot) * a.Hq + h; };
   BfpRec v[NL];
 #pragma unroll
@@ -1498,7 +1499,7 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_bfp_kernel(DqBfpSumArgs a) {
     const int slot = min(NL * gi + l, a.k - 1);
     const bool in = gi < ngroups && NL * gi + l < a.k;
     b_g[gi] = in ? row[slot] : -1;
-    st_g[gi] = in ? a.part_step[base + slot] : 0.f;
+    st_g[gi] = in ? a.part_step[rec_of(slot)] : 0.f;
   }
   const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
   const int local = (a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s])) >> 7;
