@@ -254,6 +254,47 @@ __device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float
   return step;
 }
 
+// The forward's partial records: 8-bit fields, n = round(O / step) in
+// [-127, 127] with step = 2^(E-7) * 128/127 for the smallest E with max|O| <
+// 2^E (|O| / step < 127), stored offset-binary (n + 128, one byte; the merge
+// converts a byte with one instruction and takes the 128 off once per row).
+// Encoding is one FMA per value (adding 1.5 * 2^23 + 128 leaves 128 + n in
+// the low byte).  A lane's 64 bytes: group dt (16 values) in plane dt, 16
+// bytes per lane (value j in byte j % 4 of word j / 4).  Returns the step.
+constexpr float kBfp8Magic = 12582912.0f + 128.0f;
+constexpr int kFwdPlanes = 4;
+template <typename RecIndex>
+__device__ __forceinline__ float store_rows_bfp8(const f32x16 (&oacc)[4], float mul, uint8_t* planes,
+                                                 int64_t plane_stride, RecIndex rec, int lane) {
+  const int jrow = lane & 31, half = lane >> 5;
+  float amax = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) amax = absmax3f(amax, oacc[dt][i], oacc[dt][i + 1]);
+  amax = wave_max32(amax);
+  // E = e - 126 for the biased exponent e of max|O|; rows below 2^-120 keep zeros
+  const uint32_t e = __float_as_uint(amax * mul) >> 23;
+  const bool live = e >= 7;
+  const float f = live ? mul * __uint_as_float((260u - e) << 23) * (127.f / 128.f) : 0.f;   // 1 / step
+  const float step = live ? __uint_as_float((e - 6u) << 23) * (128.f / 127.f) : 0.f;       // 2^(E - 7) * 128 / 127
+  uint8_t* dst = planes + rec(jrow) * 32 + 16 * half;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    uint32_t wd[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t t[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) t[b] = __float_as_uint(__builtin_fmaf(oacc[dt][4 * q + b], f, kBfp8Magic)) & 0xffu;
+      wd[q] = t[0] | (t[1] << 8) | (t[2] << 16) | (t[3] << 24);
+    }
+    __builtin_nontemporal_store(i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]},
+                                reinterpret_cast<i32x4*>(dst + dt * plane_stride));
+  }
+  return step;
+}
+
 template <KvFmt F>
 __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];
@@ -457,8 +498,8 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     };
     // sum >= 1 (the row max contributes exp2(0)): the hardware reciprocal's
     // 1-ulp error is far below the encoding's step
-    const float step = store_rows_bfp10(oacc, v_scale * __builtin_amdgcn_rcpf(sum), a.part_pk, a.plane_stride,
-                                       rec_index, lane);
+    const float step = store_rows_bfp8(oacc, v_scale * __builtin_amdgcn_rcpf(sum), a.part_pk, a.plane_stride,
+                                      rec_index, lane);
     {  // both halves hold the row's max, sum and step and store the same value
       // indexed as the records: a token's G heads are adjacent, so one store
       // instruction writes G * 8 contiguous bytes per token (scattered 8-byte
@@ -607,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
   }
 
   // The row's other slots first (blocks 0 <= blk < b; the local block is b),
-  // against their own maximum Ms: oacc = sum_s w_s rec_s step_s with
+  // against their own maximum Ms: oacc = sum_s w_s n_s step_s with
   // w_s = exp(lse_s - Ms), Ls = sum_s w_s.  Their {lse, step}, 16 slots per
   // batch of loads; each slot's weight goes to LDS ([slot][thread]) and the
   // records are added one slot after another, each loaded three slots ahead.
@@ -638,19 +679,17 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
     for (int j = 0; j < kBatch; ++j) ls[j] = st_row[(int64_t)min(s0 + j, a.k - 1) * a.Hq];
   };
   // a plane holds under 2^32 bytes (the plan caps the window): one 32-bit
-  // offset per slot serves the five planes' uniform bases
+  // offset per slot serves the four planes' uniform bases
   const uint8_t* const plane0 = a.part_pk;
   const uint8_t* const plane1 = plane0 + a.plane_stride;
   const uint8_t* const plane2 = plane1 + a.plane_stride;
   const uint8_t* const plane3 = plane2 + a.plane_stride;
-  const uint8_t* const plane4 = plane3 + a.plane_stride;
-  auto rec_load = [&](int slot, i32x4 (&w)[5]) {
+  auto rec_load = [&](int slot, i32x4 (&w)[kFwdPlanes]) {
     const uint32_t off = (((uint32_t)rl * (uint32_t)a.k + (uint32_t)slot) * (uint32_t)a.Hq + (uint32_t)h) * 32u + 16u * half;
     w[0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane0 + off));
     w[1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane1 + off));
     w[2] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane2 + off));
     w[3] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane3 + off));
-    w[4] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane4 + off));
   };
   float Ms = kNegInf;
   int blk0[kBatch];
@@ -667,17 +706,14 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
     for (int j = 0; j < kBatch; ++j)
       if (blk[j] >= 0 && blk[j] < b) Ms = fmaxf(Ms, ls[j].x);
   }
-  float Ls = 0.f;
+  float Ls = 0.f, Ws = 0.f;   // sum of the slots' weights, and of weight * step
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  // field j of group dt: bits 10 j .. of the 160-bit group made of plane
-  // words w[0..4][dt] (as bfp_field)
-  auto field = [&](const i32x4 (&w)[5], int dt, int j) -> float {
-    const int bit = 10 * j, qw = bit >> 5, o = bit & 31;
-    const uint32_t x0 = (uint32_t)w[qw][dt];
-    if (o <= 22) return (float)((int)(x0 << (22 - o)) >> 22);
-    return (float)((int)(__builtin_amdgcn_alignbit((uint32_t)w[qw + 1][dt], x0, o) << 22) >> 22);
+  // value j of group dt, offset-binary: byte j % 4 of word j / 4 of plane dt
+  // (128 + n: the 128 comes off once per row, below)
+  auto field = [&](const i32x4 (&w)[kFwdPlanes], int dt, int j) -> float {
+    return (float)(((uint32_t)w[dt][j >> 2] >> (8 * (j & 3))) & 0xffu);
   };
-  auto add_rec = [&](const i32x4 (&w)[5], float ws) __attribute__((always_inline)) {
+  auto add_rec = [&](const i32x4 (&w)[kFwdPlanes], float ws) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -689,10 +725,12 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
       const bool in = blk[j] >= 0 && blk[j] < b;
       const float w = in ? fast_exp2((ls[j].x - Ms) * kLog2e) : 0.f;
       Ls += w;
-      ws_s[j * 256 + tid] = in ? w * ls[j].y : 0.f;  // this lane's own slot weights
+      const float ws = in ? w * ls[j].y : 0.f;
+      Ws += ws;
+      ws_s[j * 256 + tid] = ws;  // this lane's own slot weights
     }
   };
-  i32x4 rb[4][5];  // records of four consecutive slots, slot j in rb[j % 4]
+  i32x4 rb[4][kFwdPlanes];  // records of four consecutive slots, slot j in rb[j % 4]
   rec_load(0, rb[0]);
   put_weights(blk0, ls0);
   for (int s0 = 0; s0 < a.k; s0 += kBatch) {
@@ -726,6 +764,12 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+
+  // the offset of the stored bytes: sum_s ws_s * 128 off every value
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] -= 128.f * Ws;
 
   // The local block, into the same accumulators.  Its K and V rows are in
   // LDS (each wave waits for its own direct loads, the barrier for
@@ -1016,7 +1060,7 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   const int64_t nrec = a.trash + kTrashRecords;
   a.part_pk = reinterpret_cast<uint8_t*>(ws + L.part_o);
   a.plane_stride = nrec * 32;
-  a.part_st = reinterpret_cast<float2*>(a.part_pk + 5 * a.plane_stride);
+  a.part_st = reinterpret_cast<float2*>(a.part_pk + kFwdPlanes * a.plane_stride);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = p->G;
