@@ -100,8 +100,10 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
                                  int32_t tile_hi, int64_t row_begin, int64_t row_count, float* max_score,
                                  int32_t* sel, const SelScratch& scr, hipStream_t st);
 // Sparse prefill partial records: padding rows of a work item write to one
-// of this many trash records (by workgroup) after the window's records; a
-// record takes 128 + 32 bytes of code planes and 8 of {lse, step}.
+// of this many trash records (by workgroup) after the window's records.  The
+// region holds, per record, the larger of the forward's record (4 planes of
+// 32 bytes and 8 of {lse, step}: 136) and the backward's dQ partial record
+// (5 planes and a 4-byte step: 164).
 constexpr int64_t kTrashRecords = 256;
 constexpr int64_t kPartRecordBytes = 168;
 // One-query-row plans whose rows fit the wave-per-row top-k kernels (at most

@@ -1055,7 +1055,7 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   a.xcd_pin = p->xcd_pin && (Hkv % 8 == 0 || 8 % Hkv == 0);
   a.m = m;
   // the partial records' planes share the region the backward uses for its
-  // bf16 dq partials (256 bytes per record; the forward needs 168)
+  // dQ partials (168 bytes per record; the forward needs 136)
   a.trash = p->attn_window * Hq * k;
   const int64_t nrec = a.trash + kTrashRecords;
   a.part_pk = reinterpret_cast<uint8_t*>(ws + L.part_o);
