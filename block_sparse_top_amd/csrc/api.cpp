@@ -377,7 +377,7 @@ msa_status_t msa_plan(const msa_plan_desc_t* desc, msa_plan_t* out, size_t* work
     L.gitems = off; off = align_up(off + (Hkv + 1) * 4, 256);  // first work item of each KV group
     L.entries = off; off = align_up(off + W * Hkv * K * 4, 256);
     // the forward's partial records and the backward's dQ partial records
-    // (block floating point, 136 and 164 bytes), each followed by
+    // (block floating point, 152 and 164 bytes), each followed by
     // kTrashRecords records that take the stores of padding rows
     L.part_o = off;
     off = align_up(off + (W * Hq * K + msa::kTrashRecords) * msa::kPartRecordBytes, 256);

@@ -102,7 +102,7 @@ hipError_t launch_proxy_maxscore(const msa_plan_s* p, const DevMeta& m, const vo
 // Sparse prefill partial records: padding rows of a work item write to one
 // of this many trash records (by workgroup) after the window's records.  The
 // region holds, per record, the larger of the forward's record (4 planes of
-// 32 bytes and 8 of {lse, step}: 136) and the backward's dQ partial record
+// 32 bytes, one of 16 and 8 of {lse, step}: 152) and the backward's dQ partial record
 // (5 planes and a 4-byte step: 164).
 constexpr int64_t kTrashRecords = 256;
 constexpr int64_t kPartRecordBytes = 168;

@@ -254,17 +254,35 @@ __device__ __forceinline__ float store_rows_bfp10(const f32x16 (&oacc)[4], float
   return step;
 }
 
-// The forward's partial records: 8-bit fields, n = round(O / step) in
-// [-127, 127] with step = 2^(E-7) * 128/127 for the smallest E with max|O| <
-// 2^E (|O| / step < 127), stored offset-binary (n + 128, one byte; the merge
-// converts a byte with one instruction and takes the 128 off once per row).
-// Encoding is one FMA per value (adding 1.5 * 2^23 + 128 leaves 128 + n in
-// the low byte).  A lane's 64 bytes: group dt (16 values) in plane dt, 16
-// bytes per lane (value j in byte j % 4 of word j / 4).  Returns the step.
-constexpr float kBfp8Magic = 12582912.0f + 128.0f;
-constexpr int kFwdPlanes = 4;
+// The forward's partial records: 9-bit signed fields, n = round(O / step) in
+// [-255, 255] with step = 2^(E-8) * 256/255 for the smallest E with max|O| <
+// 2^E (|O| / step < 255).  The error, at most step / 2 < 2^-8 * max|O|, and
+// the output's bf16 rounding stay inside the output tolerance even when one
+// value row of size 4 carries a row's whole output (8-bit fields would not).
+// Encoding is one FMA per value (adding 1.5 * 2^23 leaves n in the low
+// bits).  A lane's 64 values (value j of group dt is value 16 dt + j) form
+// one stream of 576 bits, value f at bits 9 f .. 9 f + 8, i.e. 18 words:
+// words 0-15 in planes 0-3 (plane p: words 4 p .. 4 p + 3, 16 bytes per lane,
+// 32 per record as the 10-bit form), words 16-17 in a fifth, half-width
+// plane (8 bytes per lane, 16 per record) after them.  Returns the step.
+constexpr int kFwdFullPlanes = 4;
+// word Q of the stream: the fields that cover it, inserted at the top and
+// shifted down (alignbit), the last one by the bits it has in the word
+template <int Q>
+__device__ __forceinline__ uint32_t bfp9_word(const uint32_t (&t)[64]) {
+  constexpr int lo = 32 * Q, hi = lo + 32;
+  constexpr int f0 = lo / 9, f1 = (hi - 1) / 9;
+  uint32_t w = 0;
+#pragma unroll
+  for (int f = f0; f < f1; ++f) w = __builtin_amdgcn_alignbit(t[f], w, 9);
+  return __builtin_amdgcn_alignbit(t[f1], w, hi - 9 * f1);
+}
+struct Rec9 {       // one record's planes as a lane of the merge holds them
+  i32x4 p[4];       // words 0-15
+  i32x2 x;          // words 16-17
+};
 template <typename RecIndex>
-__device__ __forceinline__ float store_rows_bfp8(const f32x16 (&oacc)[4], float mul, uint8_t* planes,
+__device__ __forceinline__ float store_rows_bfp9(const f32x16 (&oacc)[4], float mul, uint8_t* planes,
                                                  int64_t plane_stride, RecIndex rec, int lane) {
   const int jrow = lane & 31, half = lane >> 5;
   float amax = 0.f;
@@ -273,25 +291,28 @@ __device__ __forceinline__ float store_rows_bfp8(const f32x16 (&oacc)[4], float 
 #pragma unroll
     for (int i = 0; i < 16; i += 2) amax = absmax3f(amax, oacc[dt][i], oacc[dt][i + 1]);
   amax = wave_max32(amax);
-  // E = e - 126 for the biased exponent e of max|O|; rows below 2^-120 keep zeros
+  // E = e - 126 for the biased exponent e of max|O|; rows below 2^-119 keep zeros
   const uint32_t e = __float_as_uint(amax * mul) >> 23;
-  const bool live = e >= 7;
-  const float f = live ? mul * __uint_as_float((260u - e) << 23) * (127.f / 128.f) : 0.f;   // 1 / step
-  const float step = live ? __uint_as_float((e - 6u) << 23) * (128.f / 127.f) : 0.f;       // 2^(E - 7) * 128 / 127
-  uint8_t* dst = planes + rec(jrow) * 32 + 16 * half;
+  const bool live = e >= 8;
+  const float f = live ? mul * __uint_as_float((261u - e) << 23) * (255.f / 256.f) : 0.f;   // 1 / step
+  const float step = live ? __uint_as_float((e - 7u) << 23) * (256.f / 255.f) : 0.f;       // 2^(E - 8) * 256 / 255
+  uint32_t t[64];  // low 9 bits: n in two's complement
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    uint32_t wd[4];
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t t[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) t[b] = __float_as_uint(__builtin_fmaf(oacc[dt][4 * q + b], f, kBfp8Magic)) & 0xffu;
-      wd[q] = t[0] | (t[1] << 8) | (t[2] << 16) | (t[3] << 24);
-    }
-    __builtin_nontemporal_store(i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]},
-                                reinterpret_cast<i32x4*>(dst + dt * plane_stride));
-  }
+    for (int j = 0; j < 16; ++j) t[16 * dt + j] = __float_as_uint(__builtin_fmaf(oacc[dt][j], f, kBfpMagic));
+  const int64_t r = rec(jrow);
+  uint8_t* dst = planes + r * 32 + 16 * half;
+  __builtin_nontemporal_store(i32x4{(int)bfp9_word<0>(t), (int)bfp9_word<1>(t), (int)bfp9_word<2>(t), (int)bfp9_word<3>(t)},
+                              reinterpret_cast<i32x4*>(dst));
+  __builtin_nontemporal_store(i32x4{(int)bfp9_word<4>(t), (int)bfp9_word<5>(t), (int)bfp9_word<6>(t), (int)bfp9_word<7>(t)},
+                              reinterpret_cast<i32x4*>(dst + plane_stride));
+  __builtin_nontemporal_store(i32x4{(int)bfp9_word<8>(t), (int)bfp9_word<9>(t), (int)bfp9_word<10>(t), (int)bfp9_word<11>(t)},
+                              reinterpret_cast<i32x4*>(dst + 2 * plane_stride));
+  __builtin_nontemporal_store(i32x4{(int)bfp9_word<12>(t), (int)bfp9_word<13>(t), (int)bfp9_word<14>(t), (int)bfp9_word<15>(t)},
+                              reinterpret_cast<i32x4*>(dst + 3 * plane_stride));
+  __builtin_nontemporal_store(i32x2{(int)bfp9_word<16>(t), (int)bfp9_word<17>(t)},
+                              reinterpret_cast<i32x2*>(planes + kFwdFullPlanes * plane_stride + r * 16 + 8 * half));
   return step;
 }
 
@@ -498,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     };
     // sum >= 1 (the row max contributes exp2(0)): the hardware reciprocal's
     // 1-ulp error is far below the encoding's step
-    const float step = store_rows_bfp8(oacc, v_scale * __builtin_amdgcn_rcpf(sum), a.part_pk, a.plane_stride,
+    const float step = store_rows_bfp9(oacc, v_scale * __builtin_amdgcn_rcpf(sum), a.part_pk, a.plane_stride,
                                       rec_index, lane);
     {  // both halves hold the row's max, sum and step and store the same value
       // indexed as the records: a token's G heads are adjacent, so one store
@@ -679,17 +700,21 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
     for (int j = 0; j < kBatch; ++j) ls[j] = st_row[(int64_t)min(s0 + j, a.k - 1) * a.Hq];
   };
   // a plane holds under 2^32 bytes (the plan caps the window): one 32-bit
-  // offset per slot serves the four planes' uniform bases
+  // offset per slot serves the planes' uniform bases (the fifth, half-width
+  // plane at half the offset)
   const uint8_t* const plane0 = a.part_pk;
   const uint8_t* const plane1 = plane0 + a.plane_stride;
   const uint8_t* const plane2 = plane1 + a.plane_stride;
   const uint8_t* const plane3 = plane2 + a.plane_stride;
-  auto rec_load = [&](int slot, i32x4 (&w)[kFwdPlanes]) {
-    const uint32_t off = (((uint32_t)rl * (uint32_t)a.k + (uint32_t)slot) * (uint32_t)a.Hq + (uint32_t)h) * 32u + 16u * half;
-    w[0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane0 + off));
-    w[1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane1 + off));
-    w[2] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane2 + off));
-    w[3] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane3 + off));
+  const uint8_t* const plane4 = plane3 + a.plane_stride;
+  auto rec_load = [&](int slot, Rec9& w) {
+    const uint32_t rec = ((uint32_t)rl * (uint32_t)a.k + (uint32_t)slot) * (uint32_t)a.Hq + (uint32_t)h;
+    const uint32_t off = rec * 32u + 16u * half;
+    w.p[0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane0 + off));
+    w.p[1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane1 + off));
+    w.p[2] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane2 + off));
+    w.p[3] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane3 + off));
+    w.x = __builtin_nontemporal_load(reinterpret_cast<const i32x2*>(plane4 + (off >> 1)));
   };
   float Ms = kNegInf;
   int blk0[kBatch];
@@ -706,14 +731,19 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
     for (int j = 0; j < kBatch; ++j)
       if (blk[j] >= 0 && blk[j] < b) Ms = fmaxf(Ms, ls[j].x);
   }
-  float Ls = 0.f, Ws = 0.f;   // sum of the slots' weights, and of weight * step
+  float Ls = 0.f;
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  // value j of group dt, offset-binary: byte j % 4 of word j / 4 of plane dt
-  // (128 + n: the 128 comes off once per row, below)
-  auto field = [&](const i32x4 (&w)[kFwdPlanes], int dt, int j) -> float {
-    return (float)(((uint32_t)w[dt][j >> 2] >> (8 * (j & 3))) & 0xffu);
+  // value j of group dt: bits 9 f .. of the lane's 576-bit stream, f = 16 dt
+  // + j (store_rows_bfp9); a signed bit-field extract, after one alignbit
+  // for the values that straddle two words
+  auto word = [&](const Rec9& w, int q) -> uint32_t { return q < 16 ? (uint32_t)w.p[q >> 2][q & 3] : (uint32_t)w.x[q - 16]; };
+  auto field = [&](const Rec9& w, int dt, int j) -> float {
+    const int bit = 9 * (16 * dt + j), q = bit >> 5, o = bit & 31;
+    const uint32_t x0 = word(w, q);
+    if (o <= 23) return (float)((int)(x0 << (23 - o)) >> 23);
+    return (float)((int)(__builtin_amdgcn_alignbit(word(w, q + 1), x0, o) << 23) >> 23);
   };
-  auto add_rec = [&](const i32x4 (&w)[kFwdPlanes], float ws) __attribute__((always_inline)) {
+  auto add_rec = [&](const Rec9& w, float ws) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -725,12 +755,10 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
       const bool in = blk[j] >= 0 && blk[j] < b;
       const float w = in ? fast_exp2((ls[j].x - Ms) * kLog2e) : 0.f;
       Ls += w;
-      const float ws = in ? w * ls[j].y : 0.f;
-      Ws += ws;
-      ws_s[j * 256 + tid] = ws;  // this lane's own slot weights
+      ws_s[j * 256 + tid] = in ? w * ls[j].y : 0.f;  // this lane's own slot weights
     }
   };
-  i32x4 rb[4][kFwdPlanes];  // records of four consecutive slots, slot j in rb[j % 4]
+  Rec9 rb[4];  // records of four consecutive slots, slot j in rb[j % 4]
   rec_load(0, rb[0]);
   put_weights(blk0, ls0);
   for (int s0 = 0; s0 < a.k; s0 += kBatch) {
@@ -764,12 +792,6 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-
-  // the offset of the stored bytes: sum_s ws_s * 128 off every value
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[dt][i] -= 128.f * Ws;
 
   // The local block, into the same accumulators.  Its K and V rows are in
   // LDS (each wave waits for its own direct loads, the barrier for
@@ -1055,12 +1077,13 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   a.xcd_pin = p->xcd_pin && (Hkv % 8 == 0 || 8 % Hkv == 0);
   a.m = m;
   // the partial records' planes share the region the backward uses for its
-  // dQ partials (168 bytes per record; the forward needs 136)
+  // dQ partials (168 bytes per record; the forward needs 152)
   a.trash = p->attn_window * Hq * k;
   const int64_t nrec = a.trash + kTrashRecords;
   a.part_pk = reinterpret_cast<uint8_t*>(ws + L.part_o);
   a.plane_stride = nrec * 32;
-  a.part_st = reinterpret_cast<float2*>(a.part_pk + kFwdPlanes * a.plane_stride);
+  // after the four full planes, the half-width fifth (16 bytes per record)
+  a.part_st = reinterpret_cast<float2*>(a.part_pk + kFwdFullPlanes * a.plane_stride + nrec * 16);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = p->G;

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle as O
-from synthetic.gen import Workload, make_inputs, workload, seed_of, FP8, BF16, MXFP4, MXFP4_QK
+from synthetic.gen import Workload, make_inputs, workload, seed_of, to_bf16_bits, FP8, BF16, MXFP4, MXFP4_QK
 from tests._gpu import (device_inputs, plan_for, bf16_out_to_f64, oracle_scores, check_max_score, check_selection,
                         check_output, lowp_score_bound, BF16_ATOL, BF16_COS, FP8_ATOL, FP8_COS, LOW_PRECISION_PROXY)
 
@@ -120,6 +120,53 @@ def test_prefill_stages_match_oracle(case):
                                           w.kv_lens, w.page_size, w.sm_scale, w.kv_dtype, inp.k_scale, inp.v_scale)
     check_output(gout, ref_out, BF16_ATOL, BF16_COS, case)
     assert np.abs(glse - ref_lse).max() < 1e-3, case
+
+
+def test_prefill_one_nonlocal_key_carries_each_row():
+    """The stored partials' precision at its limit: every row of blocks 1..7
+    selects block 0 besides its own block, and one key of block 0 takes most
+    of every row's softmax (score about 12 against about 0 for the rest),
+    with a value row of magnitudes between 2 and 4.  Each output row is then
+    mostly that slot's partial as stored (block floating point, a step of
+    about 2^-6 at these magnitudes; off the bf16 grid, as the other keys mix
+    in) and rounded to bf16: the two roundings together must still meet the
+    output tolerance against the oracle (8-bit fields would not: 0.0235)."""
+    msa = _msa()
+    w = Workload("peak", [1024], [1024], 8, 2, 2, 2, topk=2)
+    inp = make_inputs(w, 90)
+    g = np.random.default_rng(90)
+    widen = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)
+    u = g.standard_normal(128).astype(np.float32)
+    u /= np.linalg.norm(u)
+    q = 0.3 * widen(inp.q) + 4.0 * u            # every row and head leans on u
+    k_pages = widen(inp.k_pages).copy()
+    v_pages = widen(inp.v_pages).copy()
+    page0 = int(inp.kv_indices[0])
+    k_pages[page0, :, 5, :] = 34.0 * u          # key 5 of block 0: q.k / sqrt(128) ~ 12
+    mag = g.uniform(2.0, 4.0, size=(w.num_kv_heads, 128))
+    v_pages[page0, :, 5, :] = (mag * np.where(g.random(mag.shape) < 0.5, -1.0, 1.0)).astype(np.float32)
+    inp = dataclasses.replace(inp, q=to_bf16_bits(q), k_pages=to_bf16_bits(k_pages), v_pages=to_bf16_bits(v_pages))
+    T = w.total_rows
+    blk = np.arange(T) // 128
+    sel = np.full((T, w.num_kv_heads, 2), -1, np.int32)
+    sel[:, :, 0] = 0
+    sel[blk > 0, :, 1] = blk[blk > 0, None]
+    print("[parity] prefill with one dominant non-local key per row", flush=True)
+    d = device_inputs(inp)
+    plan = plan_for(msa, inp)
+    out = torch.full((T, w.num_qo_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, w.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_prefill(plan, d["q"], d["k_pages"], d["v_pages"], d["kv_indices"],
+                                torch.from_numpy(sel).cuda(), out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = O.sparse_attention(inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, sel, w.qo_lens,
+                                          w.kv_lens, w.page_size, w.sm_scale)
+    gout = bf16_out_to_f64(out)
+    # the premise: rows past block 0 are carried by the one key (|out| near 2..4)
+    assert np.abs(ref_out[128:]).min() > 1.5
+    err, c = check_output(gout, ref_out, BF16_ATOL, BF16_COS, "dominant key")
+    print(f"[parity] dominant key: max|err| {err:.4g}, cos {c:.7f}", flush=True)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-3
 
 
 @pytest.mark.parametrize("case", list(PREFILL_CASES))
