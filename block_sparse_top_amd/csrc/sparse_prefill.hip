@@ -51,6 +51,27 @@ struct CsrArgs {
 // (group, block) bin per workgroup instead of one per entry.
 constexpr int kMaxLdsBins = 16384;
 
+// A row's slots, kSlotChunk at a time: the loads of a chunk are issued
+// together, so a row waits for one memory latency per chunk rather than one
+// per slot.  A row is 16-byte aligned when k is a multiple of 4 (sel is), and
+// then loads as int4.  Slots past k read as -1 (not an entry).
+constexpr int kSlotChunk = 16;
+__device__ __forceinline__ void load_slots(const int32_t* row, int s0, int k, int32_t (&v)[kSlotChunk]) {
+  if ((k & 3) == 0) {
+#pragma unroll
+    for (int j = 0; j < kSlotChunk; j += 4) {
+      const i32x4 x = s0 + j < k ? *reinterpret_cast<const i32x4*>(row + s0 + j) : i32x4{-1, -1, -1, -1};
+      v[j] = x[0];
+      v[j + 1] = x[1];
+      v[j + 2] = x[2];
+      v[j + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSlotChunk; ++j) v[j] = s0 + j < k ? row[s0 + j] : -1;
+  }
+}
+
 template <bool FILL, bool LDS_HIST>
 __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
   extern __shared__ int32_t hist[];
@@ -62,30 +83,37 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
   const int32_t r = a.w0 + (valid ? rl : 0);
   const int s = upper_bound_i32(a.m.row_start, a.m.S + 1, r) - 1;
   const int32_t pos = a.m.kv[s] - a.m.qo[s] + (r - a.m.row_start[s]);
-  const int bend = (pos >> 7) + a.with_local;  // entries: blocks 0 <= b < bend
+  // entries: blocks 0 <= b < bend; an invalid lane has none
+  const int bend = valid ? (pos >> 7) + a.with_local : 0;
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
   const int32_t pb = a.m.page_start[s];
   const int NB = a.m.NB;
   int32_t* counts = a.counts + (int64_t)g * NB;
   int32_t* cursor = a.cursor + (int64_t)g * NB;
   const int32_t* offsets = a.offsets + (int64_t)g * NB;
+  int32_t v[kSlotChunk];
   if constexpr (!LDS_HIST) {
     if (!valid) return;
-    for (int slot = 0; slot < a.k; ++slot) {
-      const int b = row[slot];
-      if (b < 0 || b >= bend) continue;
-      if (!FILL) atomicAdd(&counts[pb + b], 1);
-      else a.entries[offsets[pb + b] + atomicAdd(&cursor[pb + b], 1)] = (rl << 6) | slot;
+    for (int s0 = 0; s0 < a.k; s0 += kSlotChunk) {
+      load_slots(row, s0, a.k, v);
+#pragma unroll
+      for (int j = 0; j < kSlotChunk; ++j) {
+        const int b = v[j];
+        if (b < 0 || b >= bend) continue;
+        if (!FILL) atomicAdd(&counts[pb + b], 1);
+        else a.entries[offsets[pb + b] + atomicAdd(&cursor[pb + b], 1)] = (rl << 6) | (s0 + j);
+      }
     }
     return;
   } else {
     for (int i = tid; i < NB; i += 256) hist[i] = 0;
     __syncthreads();
-    if (valid)
-      for (int slot = 0; slot < a.k; ++slot) {
-        const int b = row[slot];
-        if (b >= 0 && b < bend) atomicAdd(&hist[pb + b], 1);
-      }
+    for (int s0 = 0; s0 < a.k; s0 += kSlotChunk) {
+      load_slots(row, s0, a.k, v);
+#pragma unroll
+      for (int j = 0; j < kSlotChunk; ++j)
+        if (v[j] >= 0 && v[j] < bend) atomicAdd(&hist[pb + v[j]], 1);
+    }
     __syncthreads();
     for (int i = tid; i < NB; i += 256) {
       const int c = hist[i];
@@ -95,11 +123,12 @@ __global__ __launch_bounds__(256) void csr_pass_kernel(CsrArgs a) {
     }
     if (!FILL) return;
     __syncthreads();
-    if (valid)
-      for (int slot = 0; slot < a.k; ++slot) {
-        const int b = row[slot];
-        if (b >= 0 && b < bend) a.entries[atomicAdd(&hist[pb + b], 1)] = (rl << 6) | slot;
-      }
+    for (int s0 = 0; s0 < a.k; s0 += kSlotChunk) {
+      load_slots(row, s0, a.k, v);
+#pragma unroll
+      for (int j = 0; j < kSlotChunk; ++j)
+        if (v[j] >= 0 && v[j] < bend) a.entries[atomicAdd(&hist[pb + v[j]], 1)] = (rl << 6) | (s0 + j);
+    }
   }
 }
 
@@ -113,10 +142,17 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* c
   const int t = threadIdx.x;
   const int per = (n + kScanThreads - 1) / kScanThreads;
   const int lo = min(n, t * per), hi = min(n, lo + per);
+  // a thread's counts are read 8 at a time (loads issued together)
   int32_t se = 0, si = 0;
-  for (int j = lo; j < hi; ++j) {
-    se += counts[j];
-    si += (counts[j] + epi - 1) / epi;
+  for (int j0 = lo; j0 < hi; j0 += 8) {
+    int32_t c8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c8[u] = j0 + u < hi ? counts[j0 + u] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      se += c8[u];
+      si += (c8[u] + epi - 1) / epi;
+    }
   }
   s_e[t] = se;
   s_i[t] = si;
@@ -129,12 +165,20 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* c
     __syncthreads();
   }
   int32_t e = s_e[t] - se, it = s_i[t] - si;
-  for (int j = lo; j < hi; ++j) {
-    const int32_t c = counts[j];
-    offsets[j] = e;
-    if (j % NB == 0) gitems[j / NB] = it;  // keys are group-major: a group's items are contiguous
-    for (int32_t x = 0; x < c; x += epi) items[it++] = make_int4(j / NB, j % NB, e + x, e + min(c, x + epi));
-    e += c;
+  for (int j0 = lo; j0 < hi; j0 += 8) {
+    int32_t c8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c8[u] = j0 + u < hi ? counts[j0 + u] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      if (j >= hi) break;
+      const int32_t c = c8[u];
+      offsets[j] = e;
+      if (j % NB == 0) gitems[j / NB] = it;  // keys are group-major: a group's items are contiguous
+      for (int32_t x = 0; x < c; x += epi) items[it++] = make_int4(j / NB, j % NB, e + x, e + min(c, x + epi));
+      e += c;
+    }
   }
   if (t == kScanThreads - 1) {
     offsets[n] = s_e[t];
