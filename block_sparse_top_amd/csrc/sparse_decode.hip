@@ -8,7 +8,7 @@
 //    selected blocks are listed once per workgroup (one ballot), and each
 //    block is cut into four 32-key slices dealt round-robin to the waves, so
 //    the waves stay balanced (17 blocks = 68 slices over 8 waves) and each
-//    wave streams its slices independently, with the next slice's loads in
+//    wave streams its slices independently, with the next slices' loads in
 //    flight while the current one is computed (no workgroup barrier in the
 //    loop).  Splits are only used when (sequence, group) pairs are too few to
 //    fill the GPU; a small kernel then merges them by log-sum-exp;
@@ -234,21 +234,35 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  // this wave's slices: s_lo + wave, + 8, ...; two register buffers, two LDS tiles
+  // this wave's slices: s_lo + wave, + 8, ...; kBufs register buffers (the
+  // next kBufs - 1 slices' loads in flight while one is computed), two LDS
+  // tiles.  The loop runs whole rounds of kBufs steps, and every step issues
+  // its loads: past the last slice they repeat it (in bounds, never
+  // computed) and its compute is skipped by a wave-uniform branch.  The loads
+  // in flight are then the same on every path, each buffer keeps its
+  // registers, and the compiler's wait before each slice is exact.
+  constexpr int kBufs = FP8 ? 3 : 2;   // bf16 slices take twice the registers
   uint8_t* vt0 = smem + (2 * wave) * kVTile;
   uint8_t* vt1 = vt0 + kVTile;
-  SliceRegs<FP8> r0, r1;
-  int sl = s_lo + wave;
-  if (sl < s_hi) issue(r0, sl);
-  while (sl < s_hi) {
-    const int sl1 = sl + kDecWaves;
-    if (sl1 < s_hi) issue(r1, sl1);
-    compute(r0, sl, vt0);
-    if (sl1 >= s_hi) break;
-    const int sl2 = sl1 + kDecWaves;
-    if (sl2 < s_hi) issue(r0, sl2);
-    compute(r1, sl1, vt1);
-    sl = sl2;
+  SliceRegs<FP8> rb[kBufs];
+  const int sl0 = s_lo + wave;
+  const int nsteps = sl0 < s_hi ? (s_hi - sl0 + kDecWaves - 1) / kDecWaves : 0;
+  if (nsteps > 0) {
+    const int last = s_hi - 1;
+    // in buffer order (the loop's waits count on rb[0]'s loads being the oldest)
+#pragma unroll
+    for (int i = 0; i < kBufs - 1; ++i) {
+      issue(rb[i], min(sl0 + kDecWaves * i, last));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int it = 0; it < nsteps; it += kBufs) {
+#pragma unroll
+      for (int i = 0; i < kBufs; ++i) {
+        const int sl = sl0 + kDecWaves * (it + i);
+        issue(rb[(i + kBufs - 1) % kBufs], min(sl + kDecWaves * (kBufs - 1), last));
+        if (it + i < nsteps) compute(rb[i], sl, (i & 1) ? vt1 : vt0);
+      }
+    }
   }
 
   // waves -> LDS: running max, lane-group sums, O^T (lane holds d = 16dt + 4q16 + e of head m16)
