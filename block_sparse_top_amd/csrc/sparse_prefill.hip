@@ -192,6 +192,23 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* c
 // output); MXFP4 records (codes widen with their E8M0 block scale, exactly).
 enum class KvFmt : int { BF16 = 0, FP8 = 1, MX4 = 2 };
 
+// Forward partial records: the window's rows in tiles of 2^rec_shift = 128 / G
+// rows (the rows of one merge workgroup), tile after tile; inside a tile of
+// tr rows starting at row t0, slot-major: window row rl, slot `slot`, query
+// head g * G + hh is record t0 k Hq + ((slot Hkv + g) tr + rl - t0) G + hh
+// (the last tile of the rec_rows-row index may be shorter).  A token's G
+// heads are adjacent (for G = 4 one 128-byte line per plane), and one slot
+// of a tile's rows for one group is contiguous: the merge, which takes one
+// slot of a block's consecutive rows at a time, reads 4 KB pieces of one
+// tile's region.  Below 2^32: the plan caps the window.
+__device__ __forceinline__ uint32_t fwd_rec(int slot, int g, int rl, int hh, int Hkv, int G, int k, int rec_rows,
+                                            int rec_shift) {
+  const uint32_t t0 = ((uint32_t)rl >> rec_shift) << rec_shift;
+  const uint32_t tr = min(1u << rec_shift, (uint32_t)rec_rows - t0);
+  return t0 * (uint32_t)k * (uint32_t)(Hkv * G) +
+         (((uint32_t)slot * (uint32_t)Hkv + (uint32_t)g) * tr + ((uint32_t)rl - t0)) * (uint32_t)G + (uint32_t)hh;
+}
+
 struct PartialArgs {
   const uint8_t* q;      // bf16 [T, Hq, 128]
   const uint8_t* kp;     // [N, Hkv, 128, 128] bf16 / fp8, or [N, Hkv, 8704 B] MXFP4 records
@@ -205,10 +222,11 @@ struct PartialArgs {
   const int32_t* gitems;  // first item of each KV group, [Hkv + 1]
   int32_t xcd_pin;        // 1: workgroup i runs an item of the groups assigned to XCD i % 8
   DevMeta m;
-  uint8_t* part_pk;      // partial records, block floating point (see store_rows_bfp10): five
-  int64_t plane_stride;  //   planes of 32 bytes per record [rows, k, Hq] + trash records, this far apart
+  uint8_t* part_pk;      // partial records, block floating point (see store_rows_bfp9): planes of
+  int64_t plane_stride;  //   32 bytes per record (fwd_rec order) + trash records, this far apart
   float2* part_st;       //   {log-sum-exp, step} per record, indexed as the records (then the trash entries)
   int64_t trash;         // index of the first of kTrashRecords trash records (rows * Hq * k)
+  int32_t rec_rows, rec_shift;  // record index (fwd_rec): the plan's window rows, log2(128 / G)
   int32_t Hq, Hkv, G, k, w0;
   float scale_log2;      // sm_scale * log2(e)
 };
@@ -247,10 +265,10 @@ __device__ __forceinline__ i32x4 load_kv8(const uint8_t* page, int row, int col)
 // for gq, t = 0..3 packs their 16 values, j = 4 gq + t, into one 160-bit
 // group (field j at bits 10 j .. 10 j + 9, two's complement), five words;
 // word w of group c = 4 h + dt is dword c of the record's 32 bytes in plane
-// w.  Planes are indexed by record (row * k + slot) * Hq + head, so the G
-// heads of one (row, slot) entry are adjacent: for G >= 4 every store
-// instruction of a plane writes whole 128-byte lines.  The step sits beside
-// the log-sum-exp (float2).
+// w.  The backward's dQ records are indexed (row * k + slot) * Hq + head and
+// the forward's in fwd_rec order; in both the G heads of one (row, slot)
+// entry are adjacent: for G >= 4 every store instruction of a plane writes
+// whole 128-byte lines.  The step sits beside the log-sum-exp (float2).
 constexpr float kBfpMagic = 12582912.0f;  // 1.5 * 2^23: x + magic keeps round(x) in the low mantissa bits
 
 // Encodes a wave's 32 rows x 128 dims of output, held as four O^T MFMA tiles
@@ -365,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[128 * 256];
   __shared__ __attribute__((aligned(16))) uint8_t vs[128 * 256];
   __shared__ int32_t ent_s[kMaxItemEntries];
-  __shared__ int32_t rk_s[kMaxItemEntries];  // entry row * k + slot (< T * 64 < 2^31): record index / Hq
+  __shared__ int32_t rk_s[kMaxItemEntries];  // an entry's record, head 0 of the group (fwd_rec)
   int item = blockIdx.x;
   if (a.xcd_pin) {
     // workgroups are dealt to the 8 XCDs round-robin: XCD x = blockIdx % 8
@@ -417,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     for (int i = tid; i < n_ent; i += 256) {
       const int32_t ent = a.entries[e0 + i];
       ent_s[i] = ent;
-      rk_s[i] = (ent >> 6) * a.k + (ent & 63);
+      rk_s[i] = (int32_t)fwd_rec(ent & 63, g, ent >> 6, 0, a.Hkv, a.G, a.k, a.rec_rows, a.rec_shift);
     }
     const int kv_in_block = a.m.kv[s] - b * 128;  // V rows at or past this are page padding
 #pragma unroll
@@ -557,8 +575,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
     auto rec_index = [&](int wrow) -> int64_t {
       const int srow = 32 * wave + wrow;
       const int se = chunk * MT + srow / G;
-      const int64_t rec = (int64_t)(uint32_t)rk_s[min(se, n_ent - 1)] * (uint32_t)a.Hq +
-                          (uint32_t)(g * G + (srow & (G - 1)));
+      const int64_t rec = (int64_t)((uint32_t)rk_s[min(se, n_ent - 1)] + (uint32_t)(srow & (G - 1)));
       return se < n_ent ? rec : trash;
     };
     // sum >= 1 (the row max contributes exp2(0)): the hardware reciprocal's
@@ -569,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void partial_attn_kernel(PartialArgs a) {
       // indexed as the records: a token's G heads are adjacent, so one store
       // instruction writes G * 8 contiguous bytes per token (scattered 8-byte
       // pieces, one per line, had cost the kernel an eighth of its time)
-      const int64_t pi = valid ? ((int64_t)rl * a.k + slot) * a.Hq + h : trash;
+      const int64_t pi = valid ? (int64_t)fwd_rec(slot, g, rl, hh, a.Hkv, G, a.k, a.rec_rows, a.rec_shift) : trash;
       a.part_st[pi] = float2{(mx + fast_log2(sum)) * kLn2, step};  // mx is already scaled
     }
   };
@@ -617,6 +634,7 @@ struct LocalMergeArgs {
   const uint8_t* part_pk;  // partial_attn's records and their {lse, step}
   int64_t plane_stride;
   const float2* part_st;
+  int32_t rec_rows, rec_shift;  // record index (fwd_rec)
   uint16_t* out;         // bf16 [T, Hq, 128]
   float* lse;            // [T, Hq] or null
   int32_t Hq, Hkv, G, k, w0, w1;
@@ -722,8 +740,11 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
   // integers, always finite, and adds exactly 0.
   const int32_t rl = r - a.w0;
   const int32_t* row = a.sel + ((int64_t)r * a.Hkv + g) * a.k;
-  // {lse, step} of slot j: indexed as the records, Hq apart
-  const float2* st_row = a.part_st + (int64_t)rl * a.k * a.Hq + h;
+  // {lse, step} of slot j: indexed as the records, Hkv tr G records apart
+  // (tr: the rows of the row's record tile)
+  const uint32_t rec0 = fwd_rec(0, g, rl, hh, a.Hkv, G, a.k, a.rec_rows, a.rec_shift);
+  const uint32_t rec_slot = fwd_rec(1, g, rl, hh, a.Hkv, G, a.k, a.rec_rows, a.rec_shift) - rec0;
+  const float2* st_row = a.part_st + rec0;
   // with k a multiple of 4 (and the selection 16-byte aligned) the row of
   // block ids goes in 16-byte pieces
   const bool vec_blk = (a.k & 3) == 0 && (reinterpret_cast<uintptr_t>(a.sel) & 15) == 0;
@@ -741,7 +762,7 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
       for (int j = 0; j < kBatch; ++j) blk[j] = s0 + j < a.k ? row[min(s0 + j, a.k - 1)] : -1;
     }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) ls[j] = st_row[(int64_t)min(s0 + j, a.k - 1) * a.Hq];
+    for (int j = 0; j < kBatch; ++j) ls[j] = st_row[(uint32_t)min(s0 + j, a.k - 1) * rec_slot];
   };
   // a plane holds under 2^32 bytes (the plan caps the window): one 32-bit
   // offset per slot serves the planes' uniform bases (the fifth, half-width
@@ -752,7 +773,7 @@ __global__ __launch_bounds__(256, 2) void local_merge_kernel(LocalMergeArgs a) {
   const uint8_t* const plane3 = plane2 + a.plane_stride;
   const uint8_t* const plane4 = plane3 + a.plane_stride;
   auto rec_load = [&](int slot, Rec9& w) {
-    const uint32_t rec = ((uint32_t)rl * (uint32_t)a.k + (uint32_t)slot) * (uint32_t)a.Hq + (uint32_t)h;
+    const uint32_t rec = rec0 + (uint32_t)slot * rec_slot;
     const uint32_t off = rec * 32u + 16u * half;
     w.p[0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane0 + off));
     w.p[1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(plane1 + off));
@@ -1123,6 +1144,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   // the partial records' planes share the region the backward uses for its
   // dQ partials (168 bytes per record; the forward needs 152)
   a.trash = p->attn_window * Hq * k;
+  a.rec_rows = (int32_t)p->attn_window;
+  a.rec_shift = __builtin_ctz((unsigned)(128 / p->G));
   const int64_t nrec = a.trash + kTrashRecords;
   a.part_pk = reinterpret_cast<uint8_t*>(ws + L.part_o);
   a.plane_stride = nrec * 32;
@@ -1164,6 +1187,8 @@ hipError_t launch_prefill_window(const msa_plan_s* p, const DevMeta& m, const vo
   mg.part_pk = a.part_pk;
   mg.plane_stride = a.plane_stride;
   mg.part_st = a.part_st;
+  mg.rec_rows = a.rec_rows;
+  mg.rec_shift = a.rec_shift;
   mg.out = static_cast<uint16_t*>(out);
   mg.lse = lse;
   mg.Hq = Hq;
