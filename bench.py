@@ -528,6 +528,32 @@ def visible_keys_per_row(sel, qo_lens, kv_lens, device):
     return torch.where(valid, n, torch.zeros_like(n)).sum(dim=2)   # [T, Hkv]
 
 
+FWD_RECORD_BYTES = 152   # one forward partial record: 144 B of 9-bit values + {lse, step}
+KV_PAGE_PAIR_BYTES = {"bf16": 2 * 128 * 128 * 2, "fp8": 2 * 128 * 128, "mxfp4": 2 * 8704}
+
+
+def partial_attn_bytes(sel, qo_lens, kv_lens, G, kv_dtype, device):
+    """HBM bytes the partial attention moves in its formulation: per (row,
+    group) slot other than the row's own block, the G heads' gathered q rows
+    (G x 256 B read) and their partial records (G x 152 B written), plus each
+    selected (group, block) K/V page pair once."""
+    import torch
+    T, Hkv, k = sel.shape
+    pos = torch.cat([torch.arange(kv - qo, kv, device=device) for qo, kv in zip(qo_lens, kv_lens)])
+    base, acc = [], 0
+    for qo, kv in zip(qo_lens, kv_lens):   # first global block of each row's sequence
+        base.append(torch.full((qo,), acc, dtype=torch.long, device=device))
+        acc += (kv + 127) // 128
+    base = torch.cat(base)
+    b = sel.long()
+    ent = (b >= 0) & (b < (pos // 128)[:, None, None])
+    n_e = int(ent.sum().item())
+    g = torch.arange(Hkv, device=device)[None, :, None].expand_as(b)
+    keys = (g * acc + base[:, None, None] + b)[ent]
+    n_pages = int(torch.unique(keys).numel())
+    return n_e * G * (256 + FWD_RECORD_BYTES) + n_pages * KV_PAGE_PAIR_BYTES[kv_dtype]
+
+
 def proxy_flops(qo_lens, kv_lens, P, d=128):
     pairs = sum(sum(range(kv - qo + 1, kv + 1)) for qo, kv in zip(qo_lens, kv_lens))
     return 2.0 * d * pairs * P
@@ -632,6 +658,16 @@ def prefill_bench(msa, n_cfg, steps, warmup, max_rows=0, attn_window=0, profile_
                           "traffic": traffic_from_profiles(dominant, w.name), "avg_launch_ms": k_ms,
                           "launches_per_step": launches_per_step,
                           "work_per_launch": work, "work_unit": "FLOP" if unit == "TFLOP/s" else "B"})
+    if dominant == "partial_attn":
+        # the same launch against the HBM roof: the bytes this formulation
+        # moves (gathered q, records, K/V pages), counted from the selection
+        fb = partial_attn_bytes(sel, w.qo_lens, w.kv_lens, G, w.kv_dtype, "cuda") / launches_per_step
+        gbs = fb / (k_ms * 1e-3) / 1e9
+        mh = MEASURED.get("hbm_gbs")
+        roof["hbm_view"] = {"bytes_per_launch": fb, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": gbs / PEAK_HBM_GBS, "frac_measured": (gbs / mh) if mh else None,
+                            "basis": "gathered q (G x 256 B) + partial records (G x 152 B) per non-local "
+                                     "(row, group) slot, + each selected K/V page pair once"}
     stage_ms = {n: v[0] for n, v in per_kernel.items()}
     pstage = "proxy_topk" if "proxy_topk" in stage_ms else "proxy_maxscore"
     p_ach = f_proxy / (stage_ms[pstage] * 1e-3) / 1e12
