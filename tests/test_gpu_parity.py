@@ -122,6 +122,36 @@ def test_prefill_stages_match_oracle(case):
     assert np.abs(glse - ref_lse).max() < 1e-3, case
 
 
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_prefill_windows_cut_record_tiles(G):
+    """Attention windows of 204 rows over three sequences of ragged lengths:
+    neither a window nor a sequence's first row falls on a multiple of a
+    merge workgroup's 128 / G rows, so the partial records' row tiles are
+    cut short at the end of the record index and workgroups straddle two
+    tiles.  Output and LSE against the oracle on the selection made."""
+    msa = _msa()
+    w = Workload(f"win{G}", [700, 77, 333], [700, 300, 400], 2 * G, 2, 2, 2, topk=5, poison_tail=True)
+    inp = make_inputs(w, 70 + G)
+    print(f"[parity] prefill windows of 204 rows G={G} T={w.total_rows}", flush=True)
+    d = device_inputs(inp)
+    plan = msa.msa_plan(w.qo_lens, w.kv_lens, w.num_qo_heads, w.num_kv_heads, w.num_proxy_heads,
+                        w.num_proxy_kv_heads, topk=w.topk, attn_window_rows=204)
+    T = w.total_rows
+    sel = torch.full((T, w.num_kv_heads, w.topk), -7, dtype=torch.int32, device="cuda")
+    msa.msa_proxy_topk_select(plan, d["proxy_q"], d["proxy_k_pages"], d["proxy_q_scale"], d["proxy_k_scale"],
+                              d["kv_indices"], 0, T, sel)
+    out = torch.full((T, w.num_qo_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, w.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_prefill(plan, d["q"], d["k_pages"], d["v_pages"], d["kv_indices"], sel, out, lse,
+                                d["k_scale"], d["v_scale"])
+    torch.cuda.synchronize()
+    gsel = sel.cpu().numpy()
+    ref_out, ref_lse = O.sparse_attention(inp.q, inp.k_pages, inp.v_pages, inp.kv_indices, gsel, w.qo_lens,
+                                          w.kv_lens, w.page_size, w.sm_scale, w.kv_dtype, inp.k_scale, inp.v_scale)
+    check_output(bf16_out_to_f64(out), ref_out, BF16_ATOL, BF16_COS, f"win{G}")
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-3, G
+
+
 def test_prefill_one_nonlocal_key_carries_each_row():
     """The stored partials' precision at its limit: every row of blocks 1..7
     selects block 0 besides its own block, and one key of block 0 takes most
